@@ -1,0 +1,13 @@
+"""contextual_sparsity_ffn_amd -- the contextual-sparsity sparse FFN step on AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libcsf.so`` (C ABI: ``include/csf.h``).  This package holds
+its sources (``csrc/``), the in-tree build (``build.py``), a thin ctypes binding (``_lib``) whose
+functions carry the C entry points' names, and the seeded synthetic workloads (``workloads``).
+"""
+from ._lib import (BF16, F16, F32, REGLU, RELU, CsfError, dense_ffn, k_from_ratio, lib,
+                   predict_active, select_threshold, select_topk, sparse_ffn, sparse_ffn_layer,
+                   workspace_size)
+
+__all__ = ["BF16", "F16", "F32", "REGLU", "RELU", "CsfError", "dense_ffn", "k_from_ratio", "lib",
+           "predict_active", "select_threshold", "select_topk", "sparse_ffn", "sparse_ffn_layer",
+           "workspace_size"]

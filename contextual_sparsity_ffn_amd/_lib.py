@@ -1,0 +1,289 @@
+"""Thin ctypes binding of ``libcsf.so`` (the C ABI in ``include/csf.h``).
+
+Argument marshalling only: each function checks the tensors it is given (device, dtype, shape,
+contiguity), sizes and allocates the workspace with torch, passes raw device pointers and the
+current HIP stream to the library, and raises on a non-zero status.  Every step of the path runs
+in the library's HIP kernels; there is no fallback of any kind.  If ``libcsf.so`` has not been
+built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsf.so")
+
+F32, F16, BF16 = 0, 1, 2
+RELU, REGLU = 0, 1
+OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER = range(6)
+
+_STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
+           3: "CSF_ERR_MISALIGNED", 4: "CSF_ERR_WORKSPACE_TOO_SMALL", 5: "CSF_ERR_HIP"}
+
+EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
+           "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
+           "csf_dense_ffn", "csf_sparse_ffn_layer")
+
+
+class CsfError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m contextual_sparsity_ffn_amd.build` "
+            "(hipcc, gfx950).  The library has no non-HIP fallback.")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, flt = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L.csf_abi_version.restype = i32
+    L.csf_abi_version.argtypes = []
+    L.csf_status_string.restype = ctypes.c_char_p
+    L.csf_status_string.argtypes = [i32]
+    L.csf_last_error.restype = ctypes.c_char_p
+    L.csf_last_error.argtypes = []
+    L.csf_workspace_size.restype = sz
+    L.csf_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.csf_predict_active.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
+    L.csf_select_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.csf_select_threshold.argtypes = [vp, i32, i32, flt, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32,
+                                 vp, vp, vp, sz, vp]
+    L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
+                                       flt, vp, vp, vp, vp, vp, sz, vp]
+    for name in EXPORTS[4:]:
+        getattr(L, name).restype = i32
+    return L
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------------
+def dtype_code(dt: torch.dtype) -> int:
+    try:
+        return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}[dt]
+    except KeyError:
+        raise ValueError(f"unsupported weight dtype {dt}; use float32, float16 or bfloat16") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise CsfError(status, lib.csf_last_error().decode())
+
+
+def _tensor(t, name, dtype=None, shape=None, device=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def workspace_size(op, B, d, f, r=0, max_count=0, dtype=F16) -> int:
+    return int(lib.csf_workspace_size(op, B, d, f, r, max_count, dtype))
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        _tensor(ws, "ws", dtype=torch.uint8, device=device)
+        if ws.numel() < nbytes:
+            raise ValueError(f"workspace has {ws.numel()} bytes, needs {nbytes}")
+        return ws, ws.numel()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def k_from_ratio(f: int, ratio: float) -> int:
+    """Active-set size for a fraction of f neurons: nearest integer, halves rounded up."""
+    import math
+    return int(math.floor(f * ratio + 0.5))
+
+
+# ------------------------------------------------------------------------------------------------
+# entry points (same names as the C ABI without the csf_ prefix)
+# ------------------------------------------------------------------------------------------------
+def predict_active(x, V, U, scores=None, ws=None):
+    """Sigmoid scores [B, f] (float32) of the low-rank predictor for x [B, d] (or [d])."""
+    squeeze = x.dim() == 1
+    X = x.unsqueeze(0) if squeeze else x
+    _tensor(X, "x")
+    dev, dt = X.device, X.dtype
+    B, d = X.shape
+    _tensor(V, "V", dtype=dt, device=dev)
+    r = V.shape[0]
+    _tensor(V, "V", shape=(r, d))
+    f = U.shape[0]
+    _tensor(U, "U", dtype=dt, shape=(f, r), device=dev)
+    if scores is None:
+        scores = torch.empty(B, f, dtype=torch.float32, device=dev)
+    _tensor(scores, "scores", dtype=torch.float32, device=dev)
+    if scores.numel() != B * f:
+        raise ValueError(f"scores must hold {B}x{f} values")
+    code = dtype_code(dt)
+    w, wb = _workspace(workspace_size(OP_PREDICT, B, d, f, r, 0, code), dev, ws)
+    _check(lib.csf_predict_active(_ptr(X), B, d, _ptr(V), r, _ptr(U), f, code, _ptr(scores),
+                                  _ptr(w), wb, _stream(dev)))
+    return scores.view(f) if squeeze else scores.view(B, f)
+
+
+def select_topk(scores, k, idx=None, count=None, bitmap=None):
+    """Ascending top-k neuron lists [B, k] (int32); lower index wins ties."""
+    squeeze = scores.dim() == 1
+    S = scores.unsqueeze(0) if squeeze else scores
+    _tensor(S, "scores", dtype=torch.float32)
+    dev = S.device
+    B, f = S.shape
+    k = int(k)
+    if idx is None:
+        idx = torch.empty(B, max(k, 1), dtype=torch.int32, device=dev)
+    _tensor(idx, "idx", dtype=torch.int32, device=dev)
+    if idx.numel() < B * max(k, 1):
+        raise ValueError("idx is too small")
+    _tensor(count, "count", dtype=torch.int32, device=dev, optional=True)
+    _tensor(bitmap, "bitmap", dtype=torch.int32, device=dev, optional=True)
+    _check(lib.csf_select_topk(_ptr(S), B, f, k, _ptr(idx), _ptr(count), _ptr(bitmap), None, 0,
+                               _stream(dev)))
+    out = idx.view(B, -1)[:, :k]
+    return out[0] if squeeze else out
+
+
+def select_threshold(scores, tau, idx=None, count=None, bitmap=None):
+    """Every neuron with score >= tau: returns (idx [B, f] int32, count [B] int32), both on device."""
+    squeeze = scores.dim() == 1
+    S = scores.unsqueeze(0) if squeeze else scores
+    _tensor(S, "scores", dtype=torch.float32)
+    dev = S.device
+    B, f = S.shape
+    if idx is None:
+        idx = torch.empty(B, f, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, dtype=torch.int32, device=dev)
+    _tensor(idx, "idx", dtype=torch.int32, shape=(B, f), device=dev)
+    _tensor(count, "count", dtype=torch.int32, shape=(B,), device=dev)
+    _tensor(bitmap, "bitmap", dtype=torch.int32, device=dev, optional=True)
+    _check(lib.csf_select_threshold(_ptr(S), B, f, float(tau), _ptr(idx), _ptr(count),
+                                    _ptr(bitmap), None, 0, _stream(dev)))
+    return (idx[0], count[0:1]) if squeeze else (idx, count)
+
+
+def _ffn_weights(x, W1, b1, Wup, W2T, act):
+    dev, dt = x.device, x.dtype
+    f, d = W1.shape
+    _tensor(W1, "W1", dtype=dt, device=dev)
+    _tensor(W2T, "W2T", dtype=dt, shape=(f, d), device=dev)
+    _tensor(b1, "b1", dtype=torch.float32, shape=(f,), device=dev, optional=True)
+    if act == REGLU:
+        _tensor(Wup, "Wup", dtype=dt, shape=(f, d), device=dev)
+    elif Wup is not None:
+        raise ValueError("Wup is only used with the gated (REGLU) activation")
+    return dev, dt, f, d
+
+
+def sparse_ffn(x, W1, b1, Wup, W2T, idx, act=RELU, count=None, max_count=None, h=None, y=None,
+               ws=None):
+    """y [B, d] float32 over each token's active list idx [B, stride] (int32, ascending)."""
+    squeeze = x.dim() == 1
+    X = x.unsqueeze(0) if squeeze else x
+    I = idx.unsqueeze(0) if idx.dim() == 1 else idx
+    _tensor(X, "x")
+    dev, dt, f, d = _ffn_weights(X, W1, b1, Wup, W2T, act)
+    B = X.shape[0]
+    _tensor(X, "x", shape=(B, d))
+    _tensor(I, "idx", dtype=torch.int32, device=dev)
+    if I.shape[0] != B:
+        raise ValueError("idx must have one row per token")
+    stride = I.shape[1]
+    max_count = stride if max_count is None else int(max_count)
+    _tensor(count, "count", dtype=torch.int32, shape=(B,), device=dev, optional=True)
+    if h is not None:
+        _tensor(h, "h", dtype=torch.float32, shape=(B, stride), device=dev)
+    if y is None:
+        y = torch.empty(B, d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, device=dev)
+    code = dtype_code(dt)
+    w, wb = _workspace(workspace_size(OP_SPARSE_FFN, B, d, f, 0, max_count, code), dev, ws)
+    _check(lib.csf_sparse_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
+                              _ptr(W2T), _ptr(I), stride, _ptr(count), max_count, _ptr(h), _ptr(y),
+                              _ptr(w), wb, _stream(dev)))
+    return y.view(d) if squeeze else y.view(B, d)
+
+
+def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, ws=None):
+    """y [B, d] float32 over every neuron."""
+    squeeze = x.dim() == 1
+    X = x.unsqueeze(0) if squeeze else x
+    _tensor(X, "x")
+    dev, dt, f, d = _ffn_weights(X, W1, b1, Wup, W2T, act)
+    B = X.shape[0]
+    _tensor(X, "x", shape=(B, d))
+    if y is None:
+        y = torch.empty(B, d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, device=dev)
+    code = dtype_code(dt)
+    w, wb = _workspace(workspace_size(OP_DENSE_FFN, B, d, f, 0, f, code), dev, ws)
+    _check(lib.csf_dense_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
+                             _ptr(W2T), _ptr(y), _ptr(w), wb, _stream(dev)))
+    return y.view(d) if squeeze else y.view(B, d)
+
+
+def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=None, scores=None,
+                     idx=None, count=None, ws=None):
+    """Predict, select (top-k if k is given, else threshold tau) and the sparse FFN for one token."""
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k (top-k) or tau (threshold)")
+    _tensor(x, "x")
+    if x.dim() != 1:
+        raise ValueError("x must be one token, shape [d]")
+    dev, dt, f, d = _ffn_weights(x, W1, b1, Wup, W2T, act)
+    _tensor(x, "x", shape=(d,))
+    r = V.shape[0]
+    _tensor(V, "V", dtype=dt, shape=(r, d), device=dev)
+    _tensor(U, "U", dtype=dt, shape=(f, r), device=dev)
+    kk = -1 if k is None else int(k)
+    if y is None:
+        y = torch.empty(d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, shape=(d,), device=dev)
+    _tensor(scores, "scores", dtype=torch.float32, shape=(f,), device=dev, optional=True)
+    if idx is not None:
+        _tensor(idx, "idx", dtype=torch.int32, device=dev)
+        if idx.numel() < (f if kk < 0 else max(kk, 1)):
+            raise ValueError("idx is too small")
+    _tensor(count, "count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    code = dtype_code(dt)
+    max_count = f if kk < 0 else kk
+    w, wb = _workspace(workspace_size(OP_LAYER, 1, d, f, r, max_count, code), dev, ws)
+    _check(lib.csf_sparse_ffn_layer(_ptr(x), d, f, r, act, code, _ptr(V), _ptr(U), _ptr(W1),
+                                    _ptr(b1), _ptr(Wup), _ptr(W2T), kk,
+                                    float(tau if tau is not None else 0.0), _ptr(y), _ptr(scores),
+                                    _ptr(idx), _ptr(count), _ptr(w), wb, _stream(dev)))
+    return y

@@ -1,0 +1,433 @@
+// api.cpp -- the C ABI of the contextual-sparsity FFN library (declared in include/csf.h):
+// host-side argument validation, workspace carving and kernel dispatch.
+//
+// Every entry point checks all of its arguments before it enqueues anything, so a rejected call
+// leaves the stream untouched.  Nothing here allocates device memory or synchronises the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/csf.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return CSF_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return ok();
+    return fail(CSF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) { return dtype == CSF_F32 ? 4 : 2; }
+bool valid_dtype(int dtype) { return dtype == CSF_F32 || dtype == CSF_F16 || dtype == CSF_BF16; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Limits of the kernels in this build (rows held in registers per thread).
+constexpr long kMaxRowChunks = 16 * 256;   // d: 16-byte chunks per row for the gathered kernels
+constexpr long kMaxPredChunks = 512;       // r: 16-byte chunks per row of U
+
+#define REQUIRE(cond, status, ...)                 \
+    do {                                           \
+        if (!(cond))                               \
+            return fail(status, __VA_ARGS__);      \
+    } while (0)
+
+int check_ptr(const void *p, const char *name, bool required)
+{
+    if (!p) {
+        if (required)
+            return fail(CSF_ERR_INVALID_ARG, "%s must not be NULL", name);
+        return CSF_OK;
+    }
+    if (!aligned16(p))
+        return fail(CSF_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+    return CSF_OK;
+}
+
+#define CHECK_PTR(p, req)                                  \
+    do {                                                   \
+        int _s = check_ptr((p), #p, (req));                \
+        if (_s != CSF_OK)                                  \
+            return _s;                                     \
+    } while (0)
+
+int check_row(int n, int dtype, const char *name, long max_chunks)
+{
+    if (n <= 0)
+        return fail(CSF_ERR_INVALID_ARG, "%s must be positive (got %d)", name, n);
+    long bytes = (long)n * elem_bytes(dtype);
+    if (bytes % 16 != 0)
+        return fail(CSF_ERR_UNSUPPORTED,
+                    "%s = %d: a row must be a multiple of 16 bytes (%s of 8 for 16-bit types, 4 for float32)",
+                    name, n, name);
+    if (bytes / 16 > max_chunks)
+        return fail(CSF_ERR_UNSUPPORTED, "%s = %d exceeds this build's limit of %ld elements", name,
+                    n, max_chunks * 16 / elem_bytes(dtype));
+    return CSF_OK;
+}
+
+#define CHECK_ROW(n, dtype, maxc)                          \
+    do {                                                   \
+        int _s = check_row((n), (dtype), #n, (maxc));      \
+        if (_s != CSF_OK)                                  \
+            return _s;                                     \
+    } while (0)
+
+// ---- workspace layouts -------------------------------------------------------------------------
+struct PredictWs {
+    size_t a, total;
+};
+PredictWs predict_ws(int B, int r)
+{
+    PredictWs w;
+    w.a = 0;
+    w.total = round_up((size_t)B * r * sizeof(float));
+    return w;
+}
+
+struct FfnWs {
+    size_t h, partials, total;
+};
+FfnWs ffn_ws(int B, int d, int dtype, int max_count)
+{
+    FfnWs w;
+    w.h = 0;
+    w.partials = round_up((size_t)B * (max_count > 0 ? max_count : 1) * sizeof(float));
+    const int nchunk = csf::ffn_num_chunks(B, d, dtype, max_count);
+    w.total = w.partials + round_up((size_t)B * nchunk * d * sizeof(float));
+    return w;
+}
+
+struct LayerWs {
+    size_t a, scores, idx, count, ffn, total;
+};
+LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
+{
+    LayerWs w;
+    w.a = 0;
+    w.scores = w.a + round_up((size_t)r * sizeof(float));
+    w.idx = w.scores + round_up((size_t)f * sizeof(float));
+    w.count = w.idx + round_up((size_t)f * sizeof(int32_t));
+    w.ffn = w.count + round_up(sizeof(int32_t));
+    w.total = w.ffn + ffn_ws(1, d, dtype, max_count).total;
+    return w;
+}
+
+char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+int check_ws(void *ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0)
+        return CSF_OK;
+    if (ws_bytes < need)
+        return fail(CSF_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes,
+                    need);
+    return check_ptr(ws, "ws", true);
+}
+
+#define CHECK_WS(ws, bytes, need)                          \
+    do {                                                   \
+        int _s = check_ws((ws), (bytes), (need));          \
+        if (_s != CSF_OK)                                  \
+            return _s;                                     \
+    } while (0)
+
+int validate_ffn(const void *x, int B, int d, int f, int act, int dtype, const void *W1,
+                 const float *b1, const void *Wup, const void *W2T)
+{
+    REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
+    REQUIRE(valid_dtype(dtype), CSF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    REQUIRE(act == CSF_ACT_RELU || act == CSF_ACT_REGLU, CSF_ERR_INVALID_ARG,
+            "unknown activation %d", act);
+    CHECK_ROW(d, dtype, kMaxRowChunks);
+    CHECK_PTR(x, B > 0);
+    CHECK_PTR(W1, true);
+    CHECK_PTR(W2T, true);
+    CHECK_PTR(b1, false);
+    if (act == CSF_ACT_REGLU) {
+        CHECK_PTR(Wup, true);
+    } else {
+        REQUIRE(Wup == nullptr, CSF_ERR_INVALID_ARG, "Wup must be NULL for CSF_ACT_RELU");
+    }
+    return CSF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csf_abi_version(void) { return CSF_ABI_VERSION; }
+
+const char *csf_status_string(int status)
+{
+    switch (status) {
+    case CSF_OK: return "CSF_OK";
+    case CSF_ERR_INVALID_ARG: return "CSF_ERR_INVALID_ARG";
+    case CSF_ERR_UNSUPPORTED: return "CSF_ERR_UNSUPPORTED";
+    case CSF_ERR_MISALIGNED: return "CSF_ERR_MISALIGNED";
+    case CSF_ERR_WORKSPACE_TOO_SMALL: return "CSF_ERR_WORKSPACE_TOO_SMALL";
+    case CSF_ERR_HIP: return "CSF_ERR_HIP";
+    default: return "CSF_ERR_UNKNOWN";
+    }
+}
+
+const char *csf_last_error(void) { return g_last_error.c_str(); }
+
+size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype)
+{
+    if (B < 0 || d <= 0 || f <= 0 || !valid_dtype(dtype) || max_count < 0)
+        return 0;
+    switch (op) {
+    case CSF_OP_PREDICT:
+        return r > 0 ? predict_ws(B, r).total : 0;
+    case CSF_OP_SELECT_TOPK:
+    case CSF_OP_SELECT_THRESHOLD:
+        return 0;
+    case CSF_OP_SPARSE_FFN:
+        return ffn_ws(B, d, dtype, max_count).total;
+    case CSF_OP_DENSE_FFN:
+        return ffn_ws(B, d, dtype, f).total;
+    case CSF_OP_LAYER:
+        return r > 0 ? layer_ws(d, f, r, max_count, dtype).total : 0;
+    default:
+        return 0;
+    }
+}
+
+int csf_predict_active(const void *x, int B, int d, const void *V, int r, const void *U, int f,
+                       int dtype, float *scores, void *ws, size_t ws_bytes, void *stream)
+{
+    REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
+    REQUIRE(valid_dtype(dtype), CSF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    CHECK_ROW(d, dtype, kMaxRowChunks);
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(x, B > 0);
+    CHECK_PTR(V, true);
+    CHECK_PTR(U, true);
+    CHECK_PTR(scores, B > 0);
+    if (B == 0)
+        return ok();
+    PredictWs w = predict_ws(B, r);
+    CHECK_WS(ws, ws_bytes, w.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, a, st);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor down-projection launch");
+    return hip_status(csf::launch_pred_up(dtype, a, B, r, U, f, scores, st),
+                      "predictor up-projection launch");
+}
+
+int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
+                    uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
+    REQUIRE(k >= 0 && k <= f, CSF_ERR_INVALID_ARG, "k = %d is outside [0, f = %d]", k, f);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    CHECK_PTR(scores, B > 0);
+    CHECK_PTR(idx, B > 0 && k > 0);
+    CHECK_PTR(count, false);
+    CHECK_PTR(bitmap, false);
+    if (B == 0)
+        return ok();
+    return hip_status(csf::launch_select_topk(scores, B, f, k, idx, k > 0 ? k : 1, count, bitmap,
+                                              static_cast<hipStream_t>(stream)),
+                      "top-k selection launch");
+}
+
+int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
+                         int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    CHECK_PTR(scores, B > 0);
+    CHECK_PTR(idx, B > 0);
+    CHECK_PTR(count, B > 0);
+    CHECK_PTR(bitmap, false);
+    if (B == 0)
+        return ok();
+    return hip_status(csf::launch_select_threshold(scores, B, f, tau, idx, f, count, bitmap,
+                                                   static_cast<hipStream_t>(stream)),
+                      "threshold selection launch");
+}
+
+int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const void *W1,
+                   const float *b1, const void *Wup, const void *W2T, const int32_t *idx,
+                   int idx_stride, const int32_t *count, int max_count, float *h, float *y,
+                   void *ws, size_t ws_bytes, void *stream)
+{
+    int s = validate_ffn(x, B, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    REQUIRE(max_count >= 0 && max_count <= idx_stride, CSF_ERR_INVALID_ARG,
+            "max_count = %d must be in [0, idx_stride = %d]", max_count, idx_stride);
+    CHECK_PTR(idx, B > 0 && max_count > 0);
+    CHECK_PTR(count, false);
+    CHECK_PTR(h, false);
+    CHECK_PTR(y, B > 0);
+    if (B == 0)
+        return ok();
+    FfnWs w = ffn_ws(B, d, dtype, max_count);
+    CHECK_WS(ws, ws_bytes, w.total);
+    csf::FfnArgs a;
+    a.dtype = dtype;
+    a.act = act;
+    a.x = x;
+    a.B = B;
+    a.d = d;
+    a.f = f;
+    a.W1 = W1;
+    a.Wup = Wup;
+    a.W2T = W2T;
+    a.b1 = b1;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.count = count;
+    a.max_count = max_count;
+    a.h = h ? h : reinterpret_cast<float *>(at(ws, w.h));
+    a.h_stride = h ? idx_stride : (max_count > 0 ? max_count : 1);
+    a.y = y;
+    a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "sparse FFN launch");
+}
+
+int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
+                  const float *b1, const void *Wup, const void *W2T, float *Y, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    CHECK_PTR(Y, B > 0);
+    if (B == 0)
+        return ok();
+    FfnWs w = ffn_ws(B, d, dtype, f);
+    CHECK_WS(ws, ws_bytes, w.total);
+    csf::FfnArgs a;
+    a.dtype = dtype;
+    a.act = act;
+    a.x = X;
+    a.B = B;
+    a.d = d;
+    a.f = f;
+    a.W1 = W1;
+    a.Wup = Wup;
+    a.W2T = W2T;
+    a.b1 = b1;
+    a.idx = nullptr;
+    a.idx_stride = f;
+    a.count = nullptr;
+    a.max_count = f;
+    a.h = reinterpret_cast<float *>(at(ws, w.h));
+    a.h_stride = f;
+    a.y = Y;
+    a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "dense FFN launch");
+}
+
+int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,
+                         const void *U, const void *W1, const float *b1, const void *Wup,
+                         const void *W2T, int k, float tau, float *y, float *scores_out,
+                         int32_t *idx_out, int32_t *count_out, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    int s = validate_ffn(x, 1, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(V, true);
+    CHECK_PTR(U, true);
+    CHECK_PTR(y, true);
+    CHECK_PTR(scores_out, false);
+    CHECK_PTR(idx_out, false);
+    CHECK_PTR(count_out, false);
+    REQUIRE(k >= -1 && k <= f, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, f = %d]",
+            k, f);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    const int max_count = k >= 0 ? k : f;
+    LayerWs w = layer_ws(d, f, r, max_count, dtype);
+    CHECK_WS(ws, ws_bytes, w.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
+    int32_t *ix = idx_out ? idx_out : reinterpret_cast<int32_t *>(at(ws, w.idx));
+    int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
+
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor down-projection launch");
+    e = csf::launch_pred_up(dtype, a, 1, r, U, f, sc, st);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor up-projection launch");
+    if (k >= 0)
+        e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st);
+    else
+        e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st);
+    if (e != hipSuccess)
+        return hip_status(e, "selection launch");
+
+    FfnWs fw = ffn_ws(1, d, dtype, max_count);
+    csf::FfnArgs fa;
+    fa.dtype = dtype;
+    fa.act = act;
+    fa.x = x;
+    fa.B = 1;
+    fa.d = d;
+    fa.f = f;
+    fa.W1 = W1;
+    fa.Wup = Wup;
+    fa.W2T = W2T;
+    fa.b1 = b1;
+    fa.idx = ix;
+    fa.idx_stride = max_count > 0 ? max_count : 1;
+    fa.count = k >= 0 ? nullptr : cn;
+    fa.max_count = max_count;
+    fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+    fa.h_stride = max_count > 0 ? max_count : 1;
+    fa.y = y;
+    fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+    return hip_status(csf::launch_ffn(fa, st), "sparse FFN launch");
+}
+
+}  // extern "C"

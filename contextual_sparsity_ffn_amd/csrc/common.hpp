@@ -1,0 +1,137 @@
+// common.hpp -- storage-type traits, 16-byte vector loads and wavefront/block reductions shared by
+// the gfx950 kernels of the contextual-sparsity FFN library.
+//
+// Every weight row is streamed in 16-byte chunks (one global_load_dwordx4 per lane, 1 KiB per
+// 64-lane wavefront instruction).  A chunk holds E elements of the storage type: 4 float32 or 8
+// binary16 / bfloat16 values.  Dot products accumulate in float32: binary16 and bfloat16 pairs go
+// through the packed dot2 instructions (products of 16-bit values are exact in float32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csf {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Streaming load of a weight chunk that is read once per call: non-temporal so that it does not
+// evict the small, reused operands (x, a, h, index lists) from the caches.
+__device__ __forceinline__ u32x4 ld_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+struct F32T {
+    static constexpr int E = 4;
+    __device__ static __forceinline__ float dot(u32x4 w, u32x4 x, float acc)
+    {
+        acc = fmaf(u2f(w.x), u2f(x.x), acc);
+        acc = fmaf(u2f(w.y), u2f(x.y), acc);
+        acc = fmaf(u2f(w.z), u2f(x.z), acc);
+        acc = fmaf(u2f(w.w), u2f(x.w), acc);
+        return acc;
+    }
+    __device__ static __forceinline__ void unpack(u32x4 w, float *o)
+    {
+        o[0] = u2f(w.x); o[1] = u2f(w.y); o[2] = u2f(w.z); o[3] = u2f(w.w);
+    }
+};
+
+struct F16T {
+    static constexpr int E = 8;
+    __device__ static __forceinline__ float dot(u32x4 w, u32x4 x, float acc)
+    {
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w.x), as_f16x2(x.x), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w.y), as_f16x2(x.y), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w.z), as_f16x2(x.z), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w.w), as_f16x2(x.w), acc, false);
+        return acc;
+    }
+    __device__ static __forceinline__ void unpack(u32x4 w, float *o)
+    {
+        f16x2 p;
+        p = as_f16x2(w.x); o[0] = (float)p.x; o[1] = (float)p.y;
+        p = as_f16x2(w.y); o[2] = (float)p.x; o[3] = (float)p.y;
+        p = as_f16x2(w.z); o[4] = (float)p.x; o[5] = (float)p.y;
+        p = as_f16x2(w.w); o[6] = (float)p.x; o[7] = (float)p.y;
+    }
+};
+
+struct BF16T {
+    static constexpr int E = 8;
+    __device__ static __forceinline__ float dot(u32x4 w, u32x4 x, float acc)
+    {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), acc, false);
+        return acc;
+    }
+    // a bfloat16 value is the upper half of the binary32 pattern with the same value
+    __device__ static __forceinline__ void unpack(u32x4 w, float *o)
+    {
+        o[0] = u2f(w.x << 16); o[1] = u2f(w.x & 0xffff0000u);
+        o[2] = u2f(w.y << 16); o[3] = u2f(w.y & 0xffff0000u);
+        o[4] = u2f(w.z << 16); o[5] = u2f(w.z & 0xffff0000u);
+        o[6] = u2f(w.w << 16); o[7] = u2f(w.w & 0xffff0000u);
+    }
+};
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.  The butterfly order is
+// fixed, so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64); every lane of a group receives its
+// group's total.
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Exclusive prefix sum over a workgroup of NW wavefronts (blockDim.x == 64 * NW).  `scratch` is
+// LDS of at least NW words; the call contains two barriers and must be reached by every thread.
+template <int NW>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t *total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t n = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += n;
+    }
+    if (lane == kWave - 1)
+        scratch[w] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        uint32_t s = scratch[i];
+        before += (i < w) ? s : 0u;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+}  // namespace csf

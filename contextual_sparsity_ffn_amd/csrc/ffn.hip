@@ -1,0 +1,298 @@
+// ffn.hip -- the gathered FFN on gfx950: active gate/up rows, activation, and the neuron-major
+// down projection with a deterministic two-phase float32 reduction.
+//
+// "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm":
+//   "The Prediction Problem" (sparse_mlp_forward) -- gather the active gate rows and the matching
+//   down weights and compute only those;
+//   "Kernel-Level Implementation" -- one dot product per selected neuron with float32 accumulation,
+//   then max(acc, 0); plain indexing must not break coalescing;
+//   "The SiLU/GELU Challenge: TurboSparse" -- the ReLU-fied gated form relu(gate x) * (up x).
+//
+// The page's sketch gives one thread per neuron, so a wavefront's lanes walk 64 different rows and
+// no load is coalesced.  Here every row is read whole by a full workgroup in 16-byte chunks (1 KiB
+// per wavefront instruction, contiguous), and the down projection is stored neuron-major so that
+// the weights of an active neuron are one contiguous row as well:
+//   k_gather_up    workgroup of 256 threads per RPW active rows: h_n = act(W1[j_n].x + b1, Wup[j_n].x)
+//   k_gather_down  grid (d-slice of 64 chunks) x (neuron chunk) x token; each of the 4 wavefronts
+//                  of a workgroup accumulates every 4th neuron of its chunk into float32 registers;
+//                  the 4 wavefronts are summed in a fixed order through LDS and written as a
+//                  partial row;
+//   k_reduce       y = sum of the partial rows in chunk order (fixed order, so deterministic).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csf {
+
+namespace {
+
+constexpr int kDownUnroll = 8;    // neurons whose 16-byte chunks are in flight per wavefront
+constexpr int kSliceChunks = 64;  // one 16-byte chunk per lane: a d-slice is 1 KiB of a row
+
+__device__ __forceinline__ int token_count(const int32_t *count, int token, int max_count)
+{
+    if (!count)
+        return max_count;
+    int c = count[token];
+    return c < 0 ? 0 : (c > max_count ? max_count : c);
+}
+
+template <int MX, bool GATED>
+struct UpShape {
+    // rows in flight per workgroup: about 24 chunk loads per thread, at most 4 rows
+    static constexpr int loads = MX * (GATED ? 2 : 1);
+    static constexpr int RPW = loads >= 24 ? 1 : (loads >= 12 ? 2 : 4);
+};
+
+template <class T, int MX, bool GATED>
+__global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
+                                                   const u32x4 *__restrict__ W1,
+                                                   const u32x4 *__restrict__ Wup,
+                                                   const float *__restrict__ b1,
+                                                   const int32_t *__restrict__ idx,
+                                                   int idx_stride,
+                                                   const int32_t *__restrict__ count,
+                                                   int max_count, int f, int C,
+                                                   float *__restrict__ h, int h_stride)
+{
+    constexpr int RPW = UpShape<MX, GATED>::RPW;
+    __shared__ float red[4][RPW][GATED ? 2 : 1];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int token = blockIdx.y;
+    const int n0 = blockIdx.x * RPW;
+    const int cnt = token_count(count, token, max_count);
+    if (n0 >= cnt)
+        return;                                   // uniform across the workgroup
+
+    const u32x4 *xt = x + (size_t)token * C;
+    u32x4 xv[MX];
+#pragma unroll
+    for (int m = 0; m < MX; ++m) {
+        const int c = t + 256 * m;
+        xv[m] = c < C ? xt[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // jr = neuron of list entry n0+i; -1 past the list end; -2 for an index outside [0, f), which
+    // contributes nothing (its h is written as 0 and the down projection skips it)
+    int jr[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int n = n0 + i;
+        int j = n < cnt ? (idx ? idx[(size_t)token * idx_stride + n] : n) : -1;
+        if (n < cnt && (j < 0 || j >= f))
+            j = -2;
+        jr[i] = j;
+    }
+
+    u32x4 wv[RPW][MX];
+    u32x4 uv[GATED ? RPW : 1][GATED ? MX : 1];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const u32x4 *row = W1 + (size_t)(jr[i] < 0 ? 0 : jr[i]) * C;
+#pragma unroll
+        for (int m = 0; m < MX; ++m) {
+            const int c = t + 256 * m;
+            wv[i][m] = (jr[i] >= 0 && c < C) ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (GATED) {
+            const u32x4 *urow = Wup + (size_t)(jr[i] < 0 ? 0 : jr[i]) * C;
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const int c = t + 256 * m;
+                uv[i][m] = (jr[i] >= 0 && c < C) ? ld_stream(urow + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MX; ++m)
+            acc = T::dot(wv[i][m], xv[m], acc);
+        acc = wave_sum(acc);
+        if (lane == 0)
+            red[w][i][0] = acc;
+        if constexpr (GATED) {
+            float au = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MX; ++m)
+                au = T::dot(uv[i][m], xv[m], au);
+            au = wave_sum(au);
+            if (lane == 0)
+                red[w][i][GATED ? 1 : 0] = au;
+        }
+    }
+    __syncthreads();
+    if (t < RPW && jr[t] == -2)
+        h[(size_t)token * h_stride + n0 + t] = 0.0f;
+    if (t < RPW && jr[t] >= 0) {
+        const int i = t;
+        float p = (red[0][i][0] + red[1][i][0]) + (red[2][i][0] + red[3][i][0]);
+        if (b1)
+            p += b1[jr[i]];
+        float hv = p > 0.0f ? p : 0.0f;
+        if constexpr (GATED) {
+            const int g = GATED ? 1 : 0;
+            const float u = (red[0][i][g] + red[1][i][g]) + (red[2][i][g] + red[3][i][g]);
+            hv *= u;
+        }
+        h[(size_t)token * h_stride + n0 + i] = hv;
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W2T,
+                                                     const float *__restrict__ h, int h_stride,
+                                                     const int32_t *__restrict__ idx,
+                                                     int idx_stride,
+                                                     const int32_t *__restrict__ count,
+                                                     int max_count, int f, int C, int nchunk,
+                                                     float *__restrict__ part)
+{
+    constexpr int E = T::E;
+    __shared__ float red[3][kSliceChunks * E];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int slice = blockIdx.x, chunk = blockIdx.y, token = blockIdx.z;
+    const int c = slice * kSliceChunks + lane;
+    const int cnt = token_count(count, token, max_count);
+    const int per = (cnt + nchunk - 1) / nchunk;
+    const int nb = chunk * per;
+    const int ne = nb + per < cnt ? nb + per : cnt;
+    const int32_t *it = idx ? idx + (size_t)token * idx_stride : nullptr;
+    const float *ht = h + (size_t)token * h_stride;
+
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        acc[e] = 0.0f;
+
+    for (int n = nb + w; n < ne; n += 4 * kDownUnroll) {
+        u32x4 wv[kDownUnroll];
+        float hv[kDownUnroll];
+#pragma unroll
+        for (int u = 0; u < kDownUnroll; ++u) {
+            const int nn = n + 4 * u;
+            int j = nn < ne ? (it ? it[nn] : nn) : 0;
+            const bool ok = nn < ne && j >= 0 && j < f;
+            j = ok ? j : 0;
+            hv[u] = ok ? ht[nn] : 0.0f;
+            wv[u] = (ok && c < C) ? ld_stream(W2T + (size_t)j * C + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kDownUnroll; ++u) {
+            float wf[E];
+            T::unpack(wv[u], wf);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[e] = fmaf(hv[u], wf[e], acc[e]);
+        }
+    }
+
+    // fixed-order sum of the 4 wavefronts: wave 0 + wave 1 + wave 2 + wave 3
+    if (w > 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            red[w - 1][lane * E + e] = acc[e];
+    }
+    __syncthreads();
+    if (w == 0 && c < C) {
+        float *out = part + ((size_t)token * nchunk + chunk) * ((size_t)C * E) + (size_t)c * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out[e] = ((acc[e] + red[0][lane * E + e]) + red[1][lane * E + e]) + red[2][lane * E + e];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ part, int nchunk, int D,
+                                                float *__restrict__ y)
+{
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    const int token = blockIdx.y;
+    if (col >= D)
+        return;
+    const float *p = part + (size_t)token * nchunk * D + col;
+    float s = 0.0f;
+    for (int q = 0; q < nchunk; ++q)
+        s += p[(size_t)q * D];
+    y[(size_t)token * D + col] = s;
+}
+
+template <class T, int MX, bool GATED>
+hipError_t up_launch(const FfnArgs &a, int C, hipStream_t st)
+{
+    constexpr int RPW = UpShape<MX, GATED>::RPW;
+    const int blocks = (a.max_count + RPW - 1) / RPW;
+    if (blocks == 0)
+        return hipSuccess;
+    dim3 grid(blocks, a.B);
+    k_gather_up<T, MX, GATED><<<grid, 256, 0, st>>>(
+        static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
+        static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count, a.max_count, a.f,
+        C, a.h, a.h_stride);
+    return hipGetLastError();
+}
+
+template <class T, bool GATED>
+hipError_t up_gated(const FfnArgs &a, int C, hipStream_t st)
+{
+    const int mx = (C + 255) / 256;
+    if (mx <= 1) return up_launch<T, 1, GATED>(a, C, st);
+    if (mx <= 2) return up_launch<T, 2, GATED>(a, C, st);
+    if (mx <= 4) return up_launch<T, 4, GATED>(a, C, st);
+    if (mx <= 6) return up_launch<T, 6, GATED>(a, C, st);
+    if (mx <= 8) return up_launch<T, 8, GATED>(a, C, st);
+    if (mx <= 12) return up_launch<T, 12, GATED>(a, C, st);
+    if (mx <= 16) return up_launch<T, 16, GATED>(a, C, st);
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t ffn_t(const FfnArgs &a, hipStream_t st)
+{
+    const int C = a.d / T::E;
+    hipError_t e = a.act == 1 ? up_gated<T, true>(a, C, st) : up_gated<T, false>(a, C, st);
+    if (e != hipSuccess)
+        return e;
+    const int nchunk = ffn_num_chunks(a.B, a.d, a.dtype, a.max_count);
+    dim3 grid((C + kSliceChunks - 1) / kSliceChunks, nchunk, a.B);
+    k_gather_down<T><<<grid, 256, 0, st>>>(static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride,
+                                           a.idx, a.idx_stride, a.count, a.max_count, a.f, C,
+                                           nchunk, a.partials);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    dim3 rgrid((a.d + 255) / 256, a.B);
+    k_reduce<<<rgrid, 256, 0, st>>>(a.partials, nchunk, a.d, a.y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int ffn_num_chunks(int B, int d, int dtype, int max_count)
+{
+    const int E = dtype == 0 ? 4 : 8;
+    const int C = d / E;
+    const int slices = (C + kSliceChunks - 1) / kSliceChunks;
+    // aim for about 1024 workgroups per token in the down projection, with at least 16 neurons
+    // per chunk.  The split depends on neither B nor the data, so a token's summation order (and
+    // its bits) are the same in every batch.
+    (void)B;
+    long want = (1024 + (long)slices - 1) / (long)slices;
+    long cap = max_count / 16;
+    if (want > cap)
+        want = cap;
+    if (want < 1)
+        want = 1;
+    if (want > 256)
+        want = 256;
+    return (int)want;
+}
+
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t st)
+{
+    if (a.dtype == 0) return ffn_t<F32T>(a, st);
+    if (a.dtype == 1) return ffn_t<F16T>(a, st);
+    return ffn_t<BF16T>(a, st);
+}
+
+}  // namespace csf

@@ -1,0 +1,51 @@
+// launch.hpp -- internal launchers of the gfx950 kernels (not part of the C ABI).
+//
+// Each launcher takes validated arguments (the C-ABI layer in api.cpp checks every size, pointer
+// and alignment first), picks the template instance and grid, enqueues on `stream` and returns the
+// launch status.  Sizes are in elements unless named *_chunks (16-byte units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csf {
+
+// ---- predictor (predict.hip) ----------------------------------------------------------------
+// a[B][r] = relu(V x_t) in float32.
+hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
+                            float *a, hipStream_t stream);
+// s[B][f] = sigmoid(U a_t) in float32.
+hipError_t launch_pred_up(int dtype, const float *a, int B, int r, const void *U, int f,
+                          float *s, hipStream_t stream);
+
+// ---- selection (select.hip) -----------------------------------------------------------------
+hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
+                              int idx_stride, int32_t *count, uint32_t *bitmap,
+                              hipStream_t stream);
+hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
+                                   int idx_stride, int32_t *count, uint32_t *bitmap,
+                                   hipStream_t stream);
+int select_max_f();   // largest f the selection kernels accept
+
+// ---- FFN (ffn.hip) --------------------------------------------------------------------------
+struct FfnArgs {
+    int dtype, act;
+    const void *x;          // [B][d]
+    int B, d, f;
+    const void *W1, *Wup, *W2T;
+    const float *b1;        // may be null
+    const int32_t *idx;     // [B][idx_stride]; null = identity list (dense)
+    int idx_stride;
+    const int32_t *count;   // [B] device; null = max_count for every token
+    int max_count;
+    float *h;               // [B][h_stride]
+    int h_stride;
+    float *y;               // [B][d]
+    float *partials;        // workspace for the two-phase down-projection reduction
+};
+// Number of neuron chunks the down projection is split into (sizes the partials workspace).
+int ffn_num_chunks(int B, int d, int dtype, int max_count);
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream);
+
+}  // namespace csf

@@ -1,0 +1,203 @@
+// predict.hip -- the low-rank activation predictor on gfx950.
+//
+// "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm", section "The
+// Prediction Problem": a bias-free two-layer network per layer scores every FFN neuron,
+// scores = sigmoid(up(relu(down(x)))), with down: d -> r and up: r -> f.
+//
+// Both halves are skinny GEMVs bound by HBM bandwidth (2 flops per weight element read), so they
+// are written as streaming dot-product kernels, not as MFMA tiles:
+//   k_pred_down  one 256-thread workgroup per row of V; each thread keeps its 16-byte chunks of the
+//                row in registers and reuses them for every token; ReLU in the epilogue.
+//   k_pred_up    groups of LPR lanes per row of U (LPR = 16/32/64 so short rows still use whole
+//                128-byte lines); the hidden activation a (float32) of the lane's chunk positions
+//                sits in registers; sigmoid in the epilogue.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csf {
+
+namespace {
+
+template <class T, int MX>
+__global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
+                                                   const u32x4 *__restrict__ x, int C, int r,
+                                                   int B, float *__restrict__ a)
+{
+    __shared__ float red[4][8];
+    const int i = blockIdx.x;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const u32x4 *row = V + (size_t)i * C;
+    u32x4 wv[MX];
+#pragma unroll
+    for (int m = 0; m < MX; ++m) {
+        const int c = t + 256 * m;
+        wv[m] = c < C ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int t0 = 0; t0 < B; t0 += 8) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            acc[q] = 0.0f;
+            const int tok = t0 + q;
+            if (tok < B) {
+                const u32x4 *xt = x + (size_t)tok * C;
+#pragma unroll
+                for (int m = 0; m < MX; ++m) {
+                    const int c = t + 256 * m;
+                    if (c < C)
+                        acc[q] = T::dot(wv[m], xt[c], acc[q]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[q] = wave_sum(acc[q]);
+        if (lane == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                red[w][q] = acc[q];
+        }
+        __syncthreads();
+        if (t < 8 && t0 + t < B) {
+            const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+            a[(size_t)(t0 + t) * r + i] = s > 0.0f ? s : 0.0f;
+        }
+        __syncthreads();
+    }
+}
+
+template <class T, int LPR, int MM, int RW>
+__global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
+                                                 const float *__restrict__ a, int C, int r, int f,
+                                                 int B, float *__restrict__ s)
+{
+    constexpr int G = kWave / LPR;   // rows handled side by side by one wavefront
+    constexpr int E = T::E;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane / LPR, li = lane % LPR;
+    const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int row0 = wave * (RW * G);
+    u32x4 wv[RW][MM];
+#pragma unroll
+    for (int st = 0; st < RW; ++st) {
+        const int j = row0 + st * G + g;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int c = li + LPR * m;
+            wv[st][m] = (j < f && c < C) ? ld_stream(U + (size_t)j * C + c)
+                                         : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    for (int tok = 0; tok < B; ++tok) {
+        const float *at = a + (size_t)tok * r;
+        float av[MM][E];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int c = li + LPR * m;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                float4 v = c < C ? *reinterpret_cast<const float4 *>(at + c * E + e)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                av[m][e] = v.x; av[m][e + 1] = v.y; av[m][e + 2] = v.z; av[m][e + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < RW; ++st) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                float wf[E];
+                T::unpack(wv[st][m], wf);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc = fmaf(wf[e], av[m][e], acc);
+            }
+            acc = group_sum<LPR>(acc);
+            const int j = row0 + st * G + g;
+            if (li == 0 && j < f)
+                s[(size_t)tok * f + j] = 1.0f / (1.0f + expf(-acc));
+        }
+    }
+}
+
+template <class T, int MX>
+hipError_t down_mx(const void *x, int B, int C, const void *V, int r, float *a, hipStream_t st)
+{
+    k_pred_down<T, MX><<<r, 256, 0, st>>>(static_cast<const u32x4 *>(V),
+                                          static_cast<const u32x4 *>(x), C, r, B, a);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t down_t(const void *x, int B, int C, const void *V, int r, float *a, hipStream_t st)
+{
+    const int mx = (C + 255) / 256;
+    if (mx <= 1) return down_mx<T, 1>(x, B, C, V, r, a, st);
+    if (mx <= 2) return down_mx<T, 2>(x, B, C, V, r, a, st);
+    if (mx <= 4) return down_mx<T, 4>(x, B, C, V, r, a, st);
+    if (mx <= 6) return down_mx<T, 6>(x, B, C, V, r, a, st);
+    if (mx <= 8) return down_mx<T, 8>(x, B, C, V, r, a, st);
+    if (mx <= 12) return down_mx<T, 12>(x, B, C, V, r, a, st);
+    if (mx <= 16) return down_mx<T, 16>(x, B, C, V, r, a, st);
+    return hipErrorInvalidValue;
+}
+
+template <class T, int LPR, int MM, int RW>
+hipError_t up_launch(const float *a, int B, int r, int C, const void *U, int f, float *s,
+                     hipStream_t st)
+{
+    constexpr int rows_per_wave = RW * (kWave / LPR);
+    const int waves = (f + rows_per_wave - 1) / rows_per_wave;
+    const int blocks = (waves + 3) / 4;
+    k_pred_up<T, LPR, MM, RW><<<blocks, 256, 0, st>>>(static_cast<const u32x4 *>(U), a, C, r, f,
+                                                       B, s);
+    return hipGetLastError();
+}
+
+// Rows in flight per lane group: enough 16-byte loads per lane (about 8) to cover HBM latency,
+// fewer when the matrix is too short to give every CU several workgroups.
+template <class T, int LPR, int MM>
+hipError_t up_rw(const float *a, int B, int r, int C, const void *U, int f, float *s,
+                 hipStream_t st)
+{
+    constexpr int G = kWave / LPR;
+    int rw = 8 / MM > 4 ? 4 : (8 / MM < 1 ? 1 : 8 / MM);
+    while (rw > 1 && (long)f / (rw * G) < 4096)   // keep >= 1024 workgroups when f allows
+        rw /= 2;
+    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, r, C, U, f, s, st);
+    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, r, C, U, f, s, st);
+    return up_launch<T, LPR, MM, 1>(a, B, r, C, U, f, s, st);
+}
+
+template <class T>
+hipError_t up_t(const float *a, int B, int r, int C, const void *U, int f, float *s,
+                hipStream_t st)
+{
+    if (C <= 16) return up_rw<T, 16, 1>(a, B, r, C, U, f, s, st);
+    if (C <= 32) return up_rw<T, 32, 1>(a, B, r, C, U, f, s, st);
+    if (C <= 64) return up_rw<T, 64, 1>(a, B, r, C, U, f, s, st);
+    if (C <= 128) return up_rw<T, 64, 2>(a, B, r, C, U, f, s, st);
+    if (C <= 256) return up_rw<T, 64, 4>(a, B, r, C, U, f, s, st);
+    if (C <= 512) return up_rw<T, 64, 8>(a, B, r, C, U, f, s, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
+                            float *a, hipStream_t st)
+{
+    if (dtype == 0) return down_t<F32T>(x, B, d / 4, V, r, a, st);
+    if (dtype == 1) return down_t<F16T>(x, B, d / 8, V, r, a, st);
+    return down_t<BF16T>(x, B, d / 8, V, r, a, st);
+}
+
+hipError_t launch_pred_up(int dtype, const float *a, int B, int r, const void *U, int f,
+                          float *s, hipStream_t st)
+{
+    if (dtype == 0) return up_t<F32T>(a, B, r, r / 4, U, f, s, st);
+    if (dtype == 1) return up_t<F16T>(a, B, r, r / 8, U, f, s, st);
+    return up_t<BF16T>(a, B, r, r / 8, U, f, s, st);
+}
+
+}  // namespace csf

@@ -1,0 +1,178 @@
+"""Seeded synthetic workloads for the contextual-sparsity FFN step.
+
+Input generation only: this module draws weights and tokens and holds none of the method's
+arithmetic.  The pages measure on trained models (OPT-175B, OPT-30B, LLaMA/Mistral-class) that
+are not available here; these stand-ins copy their shapes and the structure the method relies on:
+
+  * W1 = U V + small noise, so the active set is predictable from a cheap low-rank projection
+    ("Contextual Sparsity and Activation Predictors": the set is predictable from the layer input
+    by something far cheaper than the layer);
+  * a bias calibrated so a chosen fraction of pre-activations is positive (the sparsity level);
+  * clustered tokens, so that the active sets of a batch overlap ("When it breaks").
+
+Normal draws N(0, s) use s as the standard deviation.  Every tensor is drawn from its own
+torch.Generator seeded with seed(config, role, layer) = 1_000_000*config + 1_000*role + layer,
+in float32, and rounded once (nearest-even) to the storage type.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+ROLE_U, ROLE_V, ROLE_W1_NOISE, ROLE_W2T, ROLE_WUP, ROLE_TOKENS = 1, 2, 3, 4, 5, 6
+ROLE_CALIB, ROLE_CENTROIDS, ROLE_CLUSTER_IDS, ROLE_CLUSTER_NOISE = 7, 8, 9, 10
+
+RELU, REGLU = 0, 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    index: int
+    name: str
+    d: int
+    f: int
+    r: int
+    dtype: torch.dtype
+    act: int
+    k: Optional[int]                 # top-k size, or None for threshold mode
+    tau: Optional[float]             # threshold on the sigmoid score
+    uv_std: float                    # std of the low-rank factors U, V
+    noise_std: float                 # std of the W1 noise elements
+    w2t_std: float
+    wup_std: float
+    bias: Optional[float]            # fixed bias, or None to calibrate
+    positive_frac: Optional[float]   # calibrated fraction of positive pre-activations
+    tokens: int
+    layers: int = 1
+
+    def scaled(self, d: int, f: int, r: int, k: Optional[int] = None, tokens: int = 4) -> "Config":
+        """The same recipe at another shape (parity tests); k defaults to the same fraction of f."""
+        if k is None and self.k is not None:
+            k = int(math.floor(f * self.k / self.f + 0.5))
+        gated = self.act == REGLU
+        return dataclasses.replace(self, d=d, f=f, r=r, k=k, tokens=tokens,
+                                   uv_std=1.0 / math.sqrt(r), noise_std=0.1 / d,
+                                   w2t_std=1.0 / math.sqrt(d if gated else f),
+                                   wup_std=1.0 / math.sqrt(d) if gated else 0.0)
+
+
+# The five workloads: a tiny float32 layer; the OPT-175B FFN shape at 5% (the headline case); a
+# LLaMA-class gated (ReGLU) layer in bfloat16 with a sigmoid >= 0.5 threshold; the OPT-30B FFN shape
+# at 20% for batch-union studies; and a 48-layer stack of that shape.
+CONFIGS = {
+    0: Config(0, "tiny-relu-f32", 256, 1024, 64, torch.float32, RELU, 102, None,
+              uv_std=1 / 8, noise_std=0.1 / 256, w2t_std=1 / 32, wup_std=0.0, bias=-0.5,
+              positive_frac=None, tokens=64),
+    1: Config(1, "opt175b-relu-f16", 12288, 49152, 1024, torch.float16, RELU, 2458, None,
+              uv_std=1 / 32, noise_std=0.1 / 12288, w2t_std=1 / math.sqrt(49152), wup_std=0.0,
+              bias=None, positive_frac=0.05, tokens=256),
+    2: Config(2, "llama-reglu-bf16", 4096, 14336, 256, torch.bfloat16, REGLU, None, 0.5,
+              uv_std=1 / 16, noise_std=0.1 / 4096, w2t_std=1 / 64, wup_std=1 / 64, bias=None,
+              positive_frac=0.10, tokens=256),
+    3: Config(3, "opt30b-relu-f16", 7168, 28672, 512, torch.float16, RELU, 5734, None,
+              uv_std=1 / math.sqrt(512), noise_std=0.1 / 7168, w2t_std=1 / math.sqrt(28672),
+              wup_std=0.0, bias=None, positive_frac=0.20, tokens=256),
+    4: Config(4, "opt30b-relu-f16-stack48", 7168, 28672, 512, torch.float16, RELU, 5734, None,
+              uv_std=1 / math.sqrt(512), noise_std=0.1 / 7168, w2t_std=1 / math.sqrt(28672),
+              wup_std=0.0, bias=None, positive_frac=0.20, tokens=128, layers=48),
+}
+
+
+def seed(config: int, role: int, layer: int = 0) -> int:
+    return 1_000_000 * config + 1_000 * role + layer
+
+
+def _gen(device, s: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    return g
+
+
+def normal(shape, std, device, s) -> torch.Tensor:
+    return torch.randn(*shape, generator=_gen(device, s), device=device, dtype=torch.float32) * std
+
+
+@dataclasses.dataclass
+class Layer:
+    cfg: Config
+    V: torch.Tensor         # [r, d]  predictor down projection
+    U: torch.Tensor         # [f, r]  predictor up projection
+    W1: torch.Tensor        # [f, d]  gate (or up) projection
+    b1: torch.Tensor        # [f]     float32
+    Wup: Optional[torch.Tensor]  # [f, d] for the gated form
+    W2T: torch.Tensor       # [f, d]  down projection, neuron-major
+
+    @property
+    def weight_bytes(self) -> int:
+        n = self.W1.numel() + self.W2T.numel() + (self.Wup.numel() if self.Wup is not None else 0)
+        return n * self.W1.element_size()
+
+
+def make_layer(cfg: Config, device="cpu", layer: int = 0, config_id: Optional[int] = None) -> Layer:
+    """Draw one layer's predictor and FFN weights on `device` (float32 draws, one rounding)."""
+    c = cfg.index if config_id is None else config_id
+    d, f, r, dt = cfg.d, cfg.f, cfg.r, cfg.dtype
+    U32 = normal((f, r), cfg.uv_std, device, seed(c, ROLE_U, layer))
+    V32 = normal((r, d), cfg.uv_std, device, seed(c, ROLE_V, layer))
+    W1_32 = normal((f, d), cfg.noise_std, device, seed(c, ROLE_W1_NOISE, layer))
+    W1_32.addmm_(U32, V32)
+    W1 = W1_32.to(dt)
+    del W1_32
+    W2T = normal((f, d), cfg.w2t_std, device, seed(c, ROLE_W2T, layer)).to(dt)
+    Wup = None
+    if cfg.act == REGLU:
+        Wup = normal((f, d), cfg.wup_std, device, seed(c, ROLE_WUP, layer)).to(dt)
+    V, U = V32.to(dt), U32.to(dt)
+    del U32, V32
+    if cfg.bias is not None:
+        b = cfg.bias
+    else:
+        b = calibrate_bias(cfg, W1, device, c, layer)
+    b1 = torch.full((f,), b, dtype=torch.float32, device=device)
+    return Layer(cfg, V, U, W1, b1, Wup, W2T)
+
+
+def calibrate_bias(cfg: Config, W1: torch.Tensor, device, c: int, layer: int,
+                   n_tokens: int = 64) -> float:
+    """Scalar bias -q with q the (1 - positive_frac) quantile of W1 x over calibration tokens, so
+    that about positive_frac of the pre-activations are positive."""
+    X = normal((n_tokens, cfg.d), 1.0, device, seed(c, ROLE_CALIB, layer)).to(cfg.dtype)
+    P = (X.float() @ W1.float().t()).reshape(-1)
+    kth = int(math.ceil((1.0 - cfg.positive_frac) * P.numel()))
+    kth = min(max(kth, 1), P.numel())
+    q = torch.kthvalue(P.cpu(), kth).values.item()
+    return float(-q)
+
+
+def make_tokens(cfg: Config, n: int, device="cpu", config_id: Optional[int] = None) -> torch.Tensor:
+    """n tokens x ~ N(0, 1), rounded to the storage type: [n, d]."""
+    c = cfg.index if config_id is None else config_id
+    return normal((n, cfg.d), 1.0, device, seed(c, ROLE_TOKENS)).to(cfg.dtype)
+
+
+def make_clustered_tokens(cfg: Config, n: int, device="cpu", n_centroids: int = 8,
+                          noise: float = 0.3, config_id: Optional[int] = None) -> torch.Tensor:
+    """n tokens drawn as centroid[Uniform{0..n_centroids-1}] + N(0, noise): [n, d]."""
+    c = cfg.index if config_id is None else config_id
+    cent = normal((n_centroids, cfg.d), 1.0, device, seed(c, ROLE_CENTROIDS))
+    ids = torch.randint(0, n_centroids, (n,), generator=_gen(device, seed(c, ROLE_CLUSTER_IDS)),
+                        device=device)
+    X = cent[ids] + normal((n, cfg.d), noise, device, seed(c, ROLE_CLUSTER_NOISE))
+    return X.to(cfg.dtype)
+
+
+def touched_bytes(cfg: Config, count: int) -> int:
+    """Algorithmic bytes one batch-1 layer step reads: predictor V and U, `count` active rows of W1
+    (and W_up) and W2T, and x."""
+    es = torch.tensor([], dtype=cfg.dtype).element_size()
+    rows = 3 if cfg.act == REGLU else 2
+    return es * (cfg.r * cfg.d + cfg.f * cfg.r + count * rows * cfg.d + cfg.d)
+
+
+def dense_bytes(cfg: Config) -> int:
+    es = torch.tensor([], dtype=cfg.dtype).element_size()
+    rows = 3 if cfg.act == REGLU else 2
+    return es * rows * cfg.f * cfg.d

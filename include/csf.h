@@ -1,0 +1,192 @@
+/*
+ * csf.h -- C ABI of the contextual-sparsity sparse FFN library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one feed-forward block the contextual-sparsity way: a small low-rank
+ * predictor scores every FFN neuron from the layer input, the top-k (or thresholded) scores
+ * name the active neurons, and only the active rows of the gate/up projection and the matching
+ * rows of the neuron-major down projection are read and computed.
+ *
+ * Sources (three web pages on the method):
+ *   [DV] "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm"
+ *   [CP] "Contextual Sparsity and Activation Predictors"
+ *   [AS] "Activation sparsity" (wiki page)
+ *
+ * Conventions shared by every entry point
+ *   Pointers      All tensor pointers are DEVICE pointers (hipMalloc or equivalent) unless a
+ *                 comment says "host".  The caller allocates and frees every buffer, including
+ *                 the workspace; the library never allocates device memory.
+ *   Streams       `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
+ *                 only enqueues work on it and returns; nothing synchronises the device.
+ *                 Data-dependent sizes (threshold counts, union sizes) stay in device memory.
+ *   Layouts       Row-major, contiguous.  x[B][d], V[r][d], U[f][r], W1[f][d], Wup[f][d] and
+ *                 W2T[f][d] (the down projection stored neuron-major: row j holds the d output
+ *                 weights of neuron j).  Weights and x share one storage type (csf_dtype);
+ *                 scores, the hidden activations h, biases and outputs y are float32.
+ *   Alignment     Every pointer must be 16-byte aligned, and each weight row must be a multiple of
+ *                 16 bytes long (d and r multiples of 8 for 16-bit types, of 4 for float32);
+ *                 otherwise CSF_ERR_MISALIGNED / CSF_ERR_UNSUPPORTED.
+ *   Index lists   Active lists are int32, ascending, one row of `idx_stride` entries per token.
+ *   Errors        Every entry point validates all of its arguments on the host BEFORE it
+ *                 enqueues anything: a non-zero status means nothing was enqueued, except
+ *                 CSF_ERR_HIP, which reports a failed launch.  Device faults surface at the
+ *                 caller's next synchronisation.  csf_last_error() gives a message (per thread).
+ *                 Inputs must be finite; NaN/Inf are not checked.
+ *   Determinism   The same inputs give bitwise-identical outputs: no floating-point atomics, every
+ *                 reduction runs in a fixed order.
+ */
+#ifndef CSF_H
+#define CSF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSF_OK = 0,
+    CSF_ERR_INVALID_ARG = 1,          /* a size, k, pointer or enum value is out of range       */
+    CSF_ERR_UNSUPPORTED = 2,          /* a valid request this build does not implement           */
+    CSF_ERR_MISALIGNED = 3,           /* a pointer or a row length breaks the 16-byte rule       */
+    CSF_ERR_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes < csf_workspace_size(...)                      */
+    CSF_ERR_HIP = 5                   /* the HIP runtime reported an error at launch             */
+} csf_status;
+
+typedef enum { CSF_F32 = 0, CSF_F16 = 1, CSF_BF16 = 2 } csf_dtype;
+
+/* CSF_ACT_RELU:  h_j = max(0, W1[j].x + b1_j)                       ([DV] "Kernel-Level
+ *                Implementation": dot product then max(acc, 0)).
+ * CSF_ACT_REGLU: h_j = max(0, W1[j].x + b1_j) * (Wup[j].x), with W1 the gate projection
+ *                ([DV] "The SiLU/GELU Challenge: TurboSparse", the ReLU-fied gated form). */
+typedef enum { CSF_ACT_RELU = 0, CSF_ACT_REGLU = 1 } csf_act;
+
+/* Operation codes for csf_workspace_size. */
+typedef enum {
+    CSF_OP_PREDICT = 0,
+    CSF_OP_SELECT_TOPK = 1,
+    CSF_OP_SELECT_THRESHOLD = 2,
+    CSF_OP_SPARSE_FFN = 3,
+    CSF_OP_DENSE_FFN = 4,
+    CSF_OP_LAYER = 5,
+    CSF_OP_BATCHED_UNION = 6
+} csf_op;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define CSF_ABI_VERSION 1
+int csf_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *csf_status_string(int status);
+
+/* Message describing the last failure on the calling thread ("" if none).  Host memory owned by
+ * the library, valid until the next call on this thread. */
+const char *csf_last_error(void);
+
+/* Bytes of device workspace the operation needs for these sizes (0 if none).  `d`, `f`, `r`, `B`
+ * are the sizes passed to the entry point; `max_count` is the longest active list (k for top-k,
+ * f for threshold or dense).  Returns 0 for invalid sizes. */
+size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_predict_active -- predictor scores for every neuron of every token.
+ * [DV] "The Prediction Problem": a bias-free two-layer network per layer,
+ *      scores = sigmoid(up(relu(down(x)))), down: d -> r (the bottleneck), up: r -> f.
+ * [AS] "Implementation sketch", predict_active: the scores feed a threshold (or top-k) test.
+ *
+ *   x       [B][d]  dtype      layer input of B tokens
+ *   V       [r][d]  dtype      predictor down projection
+ *   U       [f][r]  dtype      predictor up projection
+ *   scores  [B][f]  float32    out: sigmoid scores in [0, 1]
+ * The hidden activation relu(V x) is kept in float32; all sums accumulate in float32.
+ * Workspace: csf_workspace_size(CSF_OP_PREDICT, B, d, f, r, 0, dtype) bytes.
+ * ------------------------------------------------------------------------------------------- */
+int csf_predict_active(const void *x, int B, int d, const void *V, int r, const void *U, int f,
+                       int dtype, float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_select_topk -- the k highest scores of each token.
+ * [DV] "The Prediction Problem": the k largest predictor scores form the active set.
+ * Ties go to the lower neuron index; -0.0 and +0.0 are equal; the list is ascending.
+ *
+ *   scores  [B][f]       float32   finite scores
+ *   k       0 <= k <= f            (f <= 65536 in this build)
+ *   idx     [B][k]       int32     out: ascending active list per token
+ *   count   [B]          int32     out, optional (NULL): set to k
+ *   bitmap  [B][(f+31)/32] uint32  out, optional (NULL): bit j%32 of word j/32 set iff j selected
+ * Workspace: none (pass NULL, 0).
+ * ------------------------------------------------------------------------------------------- */
+int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
+                    uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_select_threshold -- every neuron with score >= tau.
+ * [AS] "Implementation sketch", predict_active: active = scores >= threshold.
+ *
+ *   idx     [B][f]       int32     out: ascending active list; entries past count[t] undefined
+ *   count   [B]          int32     out (required): list length per token, in device memory
+ *   bitmap  optional, as for csf_select_topk
+ * Workspace: none.
+ * ------------------------------------------------------------------------------------------- */
+int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
+                         int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_sparse_ffn -- the FFN restricted to each token's active list.
+ * [DV] "The Prediction Problem" (sparse_mlp_forward): gather the active gate rows and the
+ *      matching down weights, compute only those; "Kernel-Level Implementation": one dot
+ *      product per selected neuron with float32 accumulation, then the activation.
+ *
+ *   x        [B][d]  dtype
+ *   W1       [f][d]  dtype     gate (ReLU: the up) projection
+ *   b1       [f]     float32   optional (NULL = no bias)
+ *   Wup      [f][d]  dtype     CSF_ACT_REGLU only, else NULL
+ *   W2T      [f][d]  dtype     down projection, neuron-major
+ *   idx      [B][idx_stride] int32  active lists (ascending, values in [0, f))
+ *   count    [B]     int32     optional device lengths; NULL = every list has max_count entries
+ *   max_count                  0 <= max_count <= idx_stride; device counts are clamped to it
+ *   h        [B][idx_stride] float32  out, optional: activation of each listed neuron
+ *   y        [B][d]  float32   out: y_t = sum over the list of h_j * W2T[j]
+ * Tokens are independent (each reads its own rows).  For one read of shared rows across a
+ * batch use csf_sparse_ffn_batched_union.
+ * Workspace: csf_workspace_size(CSF_OP_SPARSE_FFN, B, d, f, 0, max_count, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const void *W1,
+                   const float *b1, const void *Wup, const void *W2T, const int32_t *idx,
+                   int idx_stride, const int32_t *count, int max_count, float *h, float *y,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_dense_ffn -- the same FFN over every neuron; the reference the sparse step must beat
+ * ([CP] "The predictor and its budget": the dense layer's bytes are the budget).
+ *   X [B][d] dtype, Y [B][d] float32; other arguments as csf_sparse_ffn.
+ * Workspace: csf_workspace_size(CSF_OP_DENSE_FFN, B, d, f, 0, f, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
+                  const float *b1, const void *Wup, const void *W2T, float *Y, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_sparse_ffn_layer -- predict, select and the sparse FFN for one token in one enqueue.
+ * [DV] "The Prediction Problem" (the whole sparse_mlp_forward path).
+ *
+ *   x [d], predictor V [r][d] / U [f][r], FFN W1, b1, Wup, W2T as above.
+ *   k >= 0        top-k selection with this k
+ *   k == -1       threshold selection with tau
+ *   y [d] float32 out
+ *   scores_out [f] float32, idx_out [k or f] int32, count_out [1] int32: optional outputs (NULL =
+ *   kept in the workspace only).
+ * Workspace: csf_workspace_size(CSF_OP_LAYER, 1, d, f, r, k >= 0 ? k : f, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,
+                         const void *U, const void *W1, const float *b1, const void *Wup,
+                         const void *W2T, int k, float tau, float *y, float *scores_out,
+                         int32_t *idx_out, int32_t *count_out, void *ws, size_t ws_bytes,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSF_H */

@@ -1,0 +1,150 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented status before anything is enqueued.
+
+No call here passes validation, so no kernel is launched and no GPU is needed.  Device pointers
+are stand-in addresses that the host code never dereferences.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import contextual_sparsity_ffn_amd as csf
+from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL, HIP = range(6)
+P = ctypes.c_void_p(0x7F0000001000)        # aligned stand-in device address (never dereferenced)
+Q = ctypes.c_void_p(0x7F0000002008)        # 8-byte aligned only
+NULL = None
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "csf.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(csf_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert L.csf_abi_version() == 1
+    assert L.csf_status_string(0) == b"CSF_OK"
+    assert L.csf_status_string(4) == b"CSF_ERR_WORKSPACE_TOO_SMALL"
+    assert L.csf_status_string(99) == b"CSF_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    assert csf.workspace_size(_lib.OP_SELECT_TOPK, 1, 12288, 49152) == 0
+    assert csf.workspace_size(_lib.OP_PREDICT, 1, 12288, 49152, 1024, 0, csf.F16) >= 1024 * 4
+    ffn = csf.workspace_size(_lib.OP_SPARSE_FFN, 1, 12288, 49152, 0, 2458, csf.F16)
+    assert ffn >= (2458 + 12288) * 4
+    layer = csf.workspace_size(_lib.OP_LAYER, 1, 12288, 49152, 1024, 2458, csf.F16)
+    assert layer >= ffn + 49152 * 8
+    assert csf.workspace_size(_lib.OP_SPARSE_FFN, 1, 0, 10) == 0      # invalid sizes -> 0
+    assert csf.workspace_size(99, 1, 8, 8) == 0
+
+
+def predict(x=P, B=1, d=64, V=P, r=16, U=P, f=100, dt=csf.F16, s=P, ws=P, wsb=1 << 20):
+    return L.csf_predict_active(x, B, d, V, r, U, f, dt, s, ws, wsb, NULL)
+
+
+def test_predict_validation():
+    assert predict(d=60) == UNSUPPORTED                    # row not a multiple of 16 bytes
+    assert predict(d=0) == INVALID
+    assert predict(r=12) == UNSUPPORTED
+    assert predict(r=8192) == UNSUPPORTED                  # beyond the kernel limit
+    assert predict(f=0) == INVALID
+    assert predict(dt=7) == INVALID
+    assert predict(V=NULL) == INVALID
+    assert predict(U=Q) == MISALIGNED
+    assert predict(wsb=16) == WS_SMALL
+    assert predict(ws=NULL) == INVALID
+    assert predict(B=-1) == INVALID
+    assert predict(B=0, x=NULL, s=NULL) == OK              # nothing to do, nothing enqueued
+    assert predict(d=60) == UNSUPPORTED
+    assert b"multiple of 16 bytes" in L.csf_last_error()
+
+
+def test_select_validation():
+    assert L.csf_select_topk(P, 1, 100, 101, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(P, 1, 100, -1, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(P, 1, 70000, 5, P, NULL, NULL, NULL, 0, NULL) == UNSUPPORTED
+    assert L.csf_select_topk(P, 1, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(P, 1, 100, 5, P, Q, NULL, NULL, 0, NULL) == MISALIGNED
+    assert L.csf_select_threshold(P, 1, 100, ctypes.c_float(float("nan")), P, P, NULL, NULL, 0,
+                                  NULL) == INVALID
+    assert L.csf_select_threshold(P, 1, 100, ctypes.c_float(0.5), P, NULL, NULL, NULL, 0,
+                                  NULL) == INVALID                       # count is required
+    assert L.csf_select_topk(NULL, 0, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == OK
+
+
+def sparse(x=P, B=1, d=64, f=100, act=csf.RELU, dt=csf.F16, W1=P, b1=NULL, Wup=NULL, W2T=P,
+           idx=P, stride=10, count=NULL, maxc=10, h=NULL, y=P, ws=P, wsb=1 << 24):
+    return L.csf_sparse_ffn(x, B, d, f, act, dt, W1, b1, Wup, W2T, idx, stride, count, maxc, h,
+                            y, ws, wsb, NULL)
+
+
+def test_sparse_ffn_validation():
+    assert sparse(maxc=11) == INVALID                      # max_count > idx_stride
+    assert sparse(maxc=-1) == INVALID
+    assert sparse(act=2) == INVALID
+    assert sparse(act=csf.REGLU) == INVALID                # gated form needs Wup
+    assert sparse(Wup=P) == INVALID                        # ... and ReLU must not get one
+    assert sparse(W2T=NULL) == INVALID
+    assert sparse(b1=Q) == MISALIGNED
+    assert sparse(d=12) == UNSUPPORTED
+    assert sparse(d=64, dt=csf.F32, wsb=8) == WS_SMALL
+    assert sparse(idx=NULL) == INVALID
+
+
+def test_layer_validation():
+    def layer(k=5, tau=0.5, r=16, **kw):
+        a = dict(x=P, d=64, f=100, act=csf.RELU, dt=csf.F16, V=P, U=P, W1=P, b1=NULL, Wup=NULL,
+                 W2T=P, y=P, ws=P, wsb=1 << 24)
+        a.update(kw)
+        return L.csf_sparse_ffn_layer(a["x"], a["d"], a["f"], r, a["act"], a["dt"], a["V"], a["U"],
+                                      a["W1"], a["b1"], a["Wup"], a["W2T"], k, ctypes.c_float(tau),
+                                      a["y"], NULL, NULL, NULL, a["ws"], a["wsb"], NULL)
+    assert layer(k=-2) == INVALID
+    assert layer(k=101) == INVALID
+    assert layer(k=-1, tau=float("nan")) == INVALID
+    assert layer(r=10) == UNSUPPORTED
+    assert layer(V=NULL) == INVALID
+    assert layer(wsb=100) == WS_SMALL
+
+
+def test_k_from_ratio_matches_the_printed_figures():
+    figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    for case in figs["k_from_ratio"]:
+        assert csf.k_from_ratio(case["f"], case["ratio"]) == case["k"]
+    # the workload sizes: 10% of 1024, 5% of 49152, 20% of 28672
+    assert csf.k_from_ratio(1024, 0.10) == wl.CONFIGS[0].k == 102
+    assert csf.k_from_ratio(49152, 0.05) == wl.CONFIGS[1].k == 2458
+    assert csf.k_from_ratio(28672, 0.20) == wl.CONFIGS[3].k == 5734
+
+
+def test_budget_figure_arithmetic():
+    """An 11 GB FFN stack at 90% predicted sparsity leaves about 10 GB for the predictor."""
+    b = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))["predictor_budget"]
+    assert abs(b["dense_bytes_GB"] * b["predicted_sparsity"] - b["headroom_GB_approx"]) < 0.15
+    # the headline workload's predictor is far inside that budget: (V + U) < s * dense bytes
+    cfg = wl.CONFIGS[1]
+    pred = 2 * (cfg.r * cfg.d + cfg.f * cfg.r)
+    assert pred < 0.95 * wl.dense_bytes(cfg)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        csf.predict_active(x, torch.zeros(16, 64, dtype=torch.float16),
+                           torch.zeros(100, 16, dtype=torch.float16))

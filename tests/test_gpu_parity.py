@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bars: predictor scores within 1e-5 absolute; selection bit-exact when the oracle is fed the same
+scores; FFN outputs within the normwise bars of csf_testutil (1e-5 float32, 2e-2 16-bit, plus the
+tighter 1e-4 accumulation bound); integer-valued inputs bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import contextual_sparsity_ffn_amd as csf
+from contextual_sparsity_ffn_amd import workloads as wl
+from csf_testutil import (ORC_DT, announce, assert_ffn_close, layer_to_orc, to_orc)
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _dev(t):
+    return t.to(DEV)
+
+
+def _layer(cfg):
+    return wl.make_layer(cfg, device="cpu")
+
+
+def _to_dev_layer(L):
+    return wl.Layer(L.cfg, _dev(L.V), _dev(L.U), _dev(L.W1), _dev(L.b1),
+                    None if L.Wup is None else _dev(L.Wup), _dev(L.W2T))
+
+
+# shapes that span several workgroup tiles and end in ragged tails
+PRED_CASES = [
+    ("c0", wl.CONFIGS[0], 3),
+    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 2),
+    ("bf16", wl.CONFIGS[2].scaled(4096, 1433, 256), 2),
+    ("f16-r1024", wl.CONFIGS[1].scaled(1024, 2050, 1024), 1),
+]
+
+
+@pytest.mark.parametrize("name,cfg,B", PRED_CASES, ids=[c[0] for c in PRED_CASES])
+def test_predict_scores(name, cfg, B):
+    announce(f"predict {name}")
+    L = _layer(cfg)
+    X = wl.make_tokens(cfg, B)
+    s = csf.predict_active(_dev(X), _dev(L.V), _dev(L.U))
+    torch.cuda.synchronize()
+    o = layer_to_orc(L)
+    for t in range(B):
+        _, _, s_ref = orc.predict(to_orc(X[t]), o["V"], o["U"], o["dt"])
+        diff = np.abs(s[t].cpu().numpy().astype(np.float64) - s_ref.astype(np.float64)).max()
+        assert diff <= 1e-5, (name, t, diff)
+
+
+def _score_patterns(f, g):
+    u = torch.rand(f, generator=g)
+    q = torch.round(torch.rand(f, generator=g) * 16) / 16            # heavy ties
+    eq = torch.full((f,), 0.5)
+    z = torch.where(torch.rand(f, generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
+    sat = torch.where(torch.rand(f, generator=g) < 0.3, torch.tensor(1.0), torch.rand(f, generator=g))
+    sig = torch.sigmoid(torch.randn(f, generator=g) * 2.45)
+    return {"uniform": u, "ties": q, "all-equal": eq, "signed-zero": z, "saturated": sat,
+            "sigmoid": sig}
+
+
+SELECT_F = [1, 7, 1000, 1024, 1025, 3001, 49152, 65536]
+
+
+@pytest.mark.parametrize("f", SELECT_F)
+def test_select_topk_bit_exact(f):
+    g = torch.Generator().manual_seed(f)
+    pats = _score_patterns(f, g)
+    for pname, s in pats.items():
+        for k in sorted({0, 1, max(f // 20, 1), f // 2, max(f - 1, 0), f}):
+            if k > f:
+                continue
+            announce(f"select_topk f={f} k={k} pattern={pname}")
+            S = torch.stack([s, s.flip(0)]).float().contiguous()
+            words = (f + 31) // 32
+            bm = torch.empty(2, words, dtype=torch.int32, device=DEV)
+            cnt = torch.empty(2, dtype=torch.int32, device=DEV)
+            idx = csf.select_topk(_dev(S), k, count=cnt, bitmap=bm)
+            torch.cuda.synchronize()
+            for t in range(2):
+                ref = orc.select_topk(S[t].numpy(), k)
+                got = idx[t].cpu().numpy()
+                assert np.array_equal(got, ref), (f, k, pname, t)
+                assert cnt[t].item() == k
+                want_bm = orc.to_bitmap(ref, f).view(np.int32)
+                assert np.array_equal(bm[t].cpu().numpy(), want_bm), (f, k, pname, t)
+
+
+@pytest.mark.parametrize("f", SELECT_F)
+def test_select_threshold_bit_exact(f):
+    g = torch.Generator().manual_seed(1000 + f)
+    pats = _score_patterns(f, g)
+    for pname, s in pats.items():
+        for tau in (0.0, 0.25, 0.5, 0.9375, 1.0, 2.0):
+            announce(f"select_threshold f={f} tau={tau} pattern={pname}")
+            S = torch.stack([s, s.flip(0)]).float().contiguous()
+            words = (f + 31) // 32
+            bm = torch.empty(2, words, dtype=torch.int32, device=DEV)
+            idx, cnt = csf.select_threshold(_dev(S), tau, bitmap=bm)
+            torch.cuda.synchronize()
+            for t in range(2):
+                ref = orc.select_threshold(S[t].numpy(), tau)
+                n = cnt[t].item()
+                assert n == len(ref), (f, tau, pname, t)
+                assert np.array_equal(idx[t, :n].cpu().numpy(), ref)
+                assert np.array_equal(bm[t].cpu().numpy(), orc.to_bitmap(ref, f).view(np.int32))
+
+
+FFN_CASES = [
+    ("c0-f32", wl.CONFIGS[0], 102),
+    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 150),
+    ("f16-reglu", wl.dataclasses.replace(wl.CONFIGS[2].scaled(2600, 3001, 136), dtype=torch.float16), 301),
+    ("bf16-reglu", wl.CONFIGS[2].scaled(4096, 1433, 256), 400),
+    ("f16-wide", wl.CONFIGS[1].scaled(12288, 700, 64), 333),
+]
+
+
+@pytest.mark.parametrize("name,cfg,count", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_sparse_ffn(name, cfg, count):
+    announce(f"sparse_ffn {name}")
+    L = _layer(cfg)
+    Ld = _to_dev_layer(L)
+    B = 3
+    X = wl.make_tokens(cfg, B)
+    g = torch.Generator().manual_seed(count)
+    idx = torch.stack([torch.sort(torch.randperm(cfg.f, generator=g)[:count]).values
+                       for _ in range(B)]).int()
+    h = torch.empty(B, count, dtype=torch.float32, device=DEV)
+    y = csf.sparse_ffn(_dev(X), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, _dev(idx), act=cfg.act, h=h)
+    torch.cuda.synchronize()
+    o = layer_to_orc(L)
+    for t in range(B):
+        h_ref, y_ref = orc.sparse_ffn(to_orc(X[t]), o["W1"], o["b1"], o["Wup"], o["W2T"],
+                                      idx[t].numpy(), o["act"], o["dt"])
+        assert_ffn_close(y[t], y_ref, cfg.dtype, f"{name} token {t}")
+        hs = np.abs(h_ref).max()
+        assert np.abs(h[t].cpu().double().numpy() - h_ref).max() <= 1e-4 * max(hs, 1e-30)
+    # each token alone gives the same bits as the batch
+    for t in range(B):
+        y1 = csf.sparse_ffn(_dev(X[t]), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, _dev(idx[t]), act=cfg.act)
+        assert torch.equal(y1, y[t])
+    # a second run gives the same bits
+    y2 = csf.sparse_ffn(_dev(X), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, _dev(idx), act=cfg.act)
+    assert torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("act", [csf.RELU, csf.REGLU])
+def test_sparse_ffn_integer_inputs_bit_exact(act):
+    announce(f"sparse_ffn integer act={act}")
+    g = torch.Generator().manual_seed(77)
+    d, f, count, B = 2048 + 64, 1500, 200, 2
+    x = torch.randint(-3, 4, (B, d), generator=g).half()
+    W1 = torch.randint(-2, 3, (f, d), generator=g).half()
+    Wup = torch.randint(-2, 3, (f, d), generator=g).half() if act == csf.REGLU else None
+    W2T = torch.randint(-2, 3, (f, d), generator=g).half()
+    b1 = torch.randint(-3, 4, (f,), generator=g).float()
+    idx = torch.stack([torch.sort(torch.randperm(f, generator=g)[:count]).values for _ in range(B)]).int()
+    y = csf.sparse_ffn(_dev(x), _dev(W1), _dev(b1), None if Wup is None else _dev(Wup), _dev(W2T),
+                       _dev(idx), act=act)
+    torch.cuda.synchronize()
+    for t in range(B):
+        _, y_ref = orc.sparse_ffn(to_orc(x[t]), to_orc(W1), to_orc(b1),
+                                  None if Wup is None else to_orc(Wup), to_orc(W2T),
+                                  idx[t].numpy(), act, orc.F16)
+        # every partial sum is an integer below 2^24, so float32 accumulation is exact
+        assert np.abs(y_ref).max() < 2 ** 24
+        assert np.array_equal(y[t].cpu().double().numpy(), y_ref)
+
+
+def test_sparse_ffn_device_counts_empty_and_bad_index():
+    announce("sparse_ffn device counts / empty / bad index")
+    cfg = wl.CONFIGS[1].scaled(1024, 900, 64)
+    L = _to_dev_layer(_layer(cfg))
+    B, stride = 3, 64
+    X = _dev(wl.make_tokens(cfg, B))
+    g = torch.Generator().manual_seed(5)
+    idx = torch.stack([torch.sort(torch.randperm(cfg.f, generator=g)[:stride]).values for _ in range(B)]).int()
+    counts = torch.tensor([0, 17, 64], dtype=torch.int32)
+    y = csf.sparse_ffn(X, L.W1, L.b1, None, L.W2T, _dev(idx), count=_dev(counts))
+    torch.cuda.synchronize()
+    assert not y[0].any()                                  # empty active set -> y = 0
+    y17 = csf.sparse_ffn(X[1], L.W1, L.b1, None, L.W2T, _dev(idx[1, :17].contiguous()))
+    y64 = csf.sparse_ffn(X[2], L.W1, L.b1, None, L.W2T, _dev(idx[2]))
+    torch.cuda.synchronize()
+    o = layer_to_orc(L)
+    _, r17 = orc.sparse_ffn(to_orc(X[1]), o["W1"], o["b1"], None, o["W2T"], idx[1, :17].numpy(),
+                            orc.RELU, orc.F16)
+    assert_ffn_close(y[1], r17, cfg.dtype, "count 17")
+    assert_ffn_close(y17, r17, cfg.dtype, "list of 17")
+    assert torch.equal(y[2], y64)
+    # an index outside [0, f) contributes nothing
+    bad = idx[2].clone()
+    bad[10] = cfg.f + 5
+    bad[20] = -1
+    yb = csf.sparse_ffn(X[2], L.W1, L.b1, None, L.W2T, _dev(bad))
+    keep = np.delete(idx[2].numpy(), [10, 20])
+    _, rb = orc.sparse_ffn(to_orc(X[2]), o["W1"], o["b1"], None, o["W2T"], keep, orc.RELU, orc.F16)
+    torch.cuda.synchronize()
+    assert_ffn_close(yb, rb, cfg.dtype, "bad index skipped")
+
+
+DENSE_CASES = [
+    ("c0-f32", wl.CONFIGS[0]),
+    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136)),
+    ("bf16-reglu", wl.CONFIGS[2].scaled(4096, 1433, 256)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_ffn_and_full_list(name, cfg):
+    announce(f"dense_ffn {name}")
+    L = _layer(cfg)
+    Ld = _to_dev_layer(L)
+    X = wl.make_tokens(cfg, 2)
+    y = csf.dense_ffn(_dev(X), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, act=cfg.act)
+    full = torch.arange(cfg.f, dtype=torch.int32, device=DEV).repeat(2, 1).contiguous()
+    ys = csf.sparse_ffn(_dev(X), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, full, act=cfg.act)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ys)                              # the full list is the dense layer
+    o = layer_to_orc(L)
+    for t in range(2):
+        _, y_ref = orc.dense_ffn(to_orc(X[t]), o["W1"], o["b1"], o["Wup"], o["W2T"], o["act"], o["dt"])
+        assert_ffn_close(y[t], y_ref, cfg.dtype, f"dense {name} token {t}")
+
+
+def test_relu_true_set_matches_dense():
+    """For ReLU, the sparse step over the true active set gives the dense output (up to order)."""
+    announce("true set vs dense")
+    cfg = wl.CONFIGS[1].scaled(2048, 4000, 128)
+    L = _layer(cfg)
+    Ld = _to_dev_layer(L)
+    x = wl.make_tokens(cfg, 1)[0]
+    o = layer_to_orc(L)
+    T = orc.true_set(to_orc(x), o["W1"], o["b1"], o["dt"])
+    y_sparse = csf.sparse_ffn(_dev(x), Ld.W1, Ld.b1, None, Ld.W2T, _dev(torch.from_numpy(T)))
+    y_dense = csf.dense_ffn(_dev(x), Ld.W1, Ld.b1, None, Ld.W2T)
+    torch.cuda.synchronize()
+    _, y_ref = orc.dense_ffn(to_orc(x), o["W1"], o["b1"], None, o["W2T"], orc.RELU, o["dt"])
+    assert_ffn_close(y_sparse, y_ref, cfg.dtype, "true set")
+    assert_ffn_close(y_dense, y_ref, cfg.dtype, "dense")
+
+
+LAYER_CASES = [
+    ("c0", wl.CONFIGS[0], 6),
+    ("f16-ragged-topk", wl.CONFIGS[1].scaled(2600, 3001, 136), 3),
+    ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(4096, 1433, 256), 3),
+]
+
+
+def _check_layer_token(L, o, x, k, tau, what):
+    f = L.cfg.f
+    scores = torch.empty(f, dtype=torch.float32, device=DEV)
+    idx = torch.empty(f, dtype=torch.int32, device=DEV)
+    count = torch.empty(1, dtype=torch.int32, device=DEV)
+    y = csf.sparse_ffn_layer(_dev(x), L.V, L.U, L.W1, L.b1, L.Wup, L.W2T, k=k, tau=tau,
+                             act=L.cfg.act, scores=scores, idx=idx, count=count)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()
+    _, _, s_ref = orc.predict(to_orc(x), o["V"], o["U"], o["dt"])
+    assert np.abs(s_gpu.astype(np.float64) - s_ref).max() <= 1e-5, what
+    n = count.item()
+    ix = idx[:n].cpu().numpy()
+    # selection is bit-exact when the oracle is fed the GPU's scores
+    ref_sel = orc.select_topk(s_gpu, k) if k is not None else orc.select_threshold(s_gpu, tau)
+    assert np.array_equal(ix, ref_sel), what
+    # against the oracle's own scores, every disagreement sits within 1e-5 of the boundary
+    own = orc.select_topk(s_ref, k) if k is not None else orc.select_threshold(s_ref, tau)
+    theta = np.sort(s_ref)[::-1][k - 1] if (k is not None and k > 0) else tau
+    for j in np.setxor1d(own, ix):
+        assert abs(float(s_ref[j]) - float(theta)) < 1e-5, (what, j)
+    _, y_ref = orc.sparse_ffn(to_orc(x), o["W1"], o["b1"], o["Wup"], o["W2T"], ix, o["act"], o["dt"])
+    assert_ffn_close(y, y_ref, L.cfg.dtype, what)
+    return ix
+
+
+@pytest.mark.parametrize("name,cfg,ntok", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_end_to_end(name, cfg, ntok):
+    L = _layer(cfg)
+    Ld = _to_dev_layer(L)
+    o = layer_to_orc(L)
+    X = wl.make_tokens(cfg, ntok)
+    for t in range(ntok):
+        announce(f"layer {name} token {t}")
+        _check_layer_token(Ld, o, X[t], cfg.k, cfg.tau if cfg.k is None else None, f"{name}/{t}")
+
+
+def test_layer_full_size_opt175b_shape():
+    """The headline workload at full size (d=12288, f=49152, r=1024, f16, k=2458), one token,
+    in the same launch configuration the benchmark times."""
+    announce("layer full size c1")
+    cfg = wl.CONFIGS[1]
+    Ld = wl.make_layer(cfg, device=DEV)
+    x = wl.make_tokens(cfg, 1, device=DEV)[0]
+    o = layer_to_orc(Ld)
+    ix = _check_layer_token(Ld, o, x, cfg.k, None, "c1 full")
+    assert len(ix) == cfg.k
