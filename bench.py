@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the contextual-sparsity FFN step on one MI355X.
+
+Workload: the OPT-175B FFN shape at batch 1 (d = 12288, f = 49152, predictor rank 1024, float16
+weights with float32 accumulation, top-k = 2458 = 5% of f).  One step is one call of
+csf_sparse_ffn_layer for one token: predictor, top-k selection and the gathered FFN.  Steps
+rotate over several independently seeded layer instances (so the touched set is not served
+from the 256 MB last-level cache) and over seeded tokens.
+
+Printed: one JSON line.  `value` is the achieved bandwidth in GB/s on the bytes one step must
+touch (V + U + the active rows of W1 and W2T + x), the metric's bandwidth form; the same line
+gives microseconds per layer, the per-kernel times, the roofline of the dominant kernel, the
+speed-up over the library's dense FFN, predictor recall/precision against the true active set,
+and the CPU oracle's rate on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN µs/layer + HBM GB/s on touched bytes, batch 1, OPT-175B shape @5%"
+PEAK_HBM_GBS = 8000.0
+KERNELS = ["pred_down", "pred_up", "select_topk", "gather_up", "gather_down", "reduce_partials"]
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer instances rotated")
+    ap.add_argument("--tokens", type=int, default=256)
+    ap.add_argument("--trace-steps", type=int, default=400)
+    ap.add_argument("--quality-tokens", type=int, default=32)
+    ap.add_argument("--dense-steps", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (to scale HBM byte counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU path only: this build has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = wl.CONFIGS[1]
+    d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
+    code = _lib.dtype_code(cfg.dtype)
+    log(f"building {args.layers} layer instances of d={d} f={f} r={r} ({cfg.dtype})")
+    layers = [wl.make_layer(cfg, device=dev, layer=l) for l in range(args.layers)]
+    X = wl.make_tokens(cfg, args.tokens, device=dev)
+    torch.cuda.synchronize()
+
+    ws_bytes = csf.workspace_size(_lib.OP_LAYER, 1, d, f, r, k, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    scores = torch.empty(f, dtype=torch.float32, device=dev)
+    idx = torch.empty(k, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+
+    def call_args(l, t, y_out=y, scores_out=None, idx_out=None):
+        L = layers[l]
+        return (vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(L.V.data_ptr()),
+                vp(L.U.data_ptr()), vp(L.W1.data_ptr()), vp(L.b1.data_ptr()), None,
+                vp(L.W2T.data_ptr()), k, ctypes.c_float(0.0), vp(y_out.data_ptr()),
+                None if scores_out is None else vp(scores_out.data_ptr()),
+                None if idx_out is None else vp(idx_out.data_ptr()), None,
+                vp(ws.data_ptr()), ws_bytes, vp(stream.cuda_stream))
+
+    plan = [call_args(s % args.layers, (s * 7) % args.tokens) for s in range(args.layers * args.tokens)]
+    fn = _lib.lib.csf_sparse_ffn_layer
+
+    def run(n, offset=0):
+        for s in range(n):
+            rc = fn(*plan[(offset + s) % len(plan)])
+            if rc:
+                raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+
+    log(f"warmup {args.warmup} steps")
+    run(args.warmup)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    run(args.steps, offset=args.warmup)
+    e1.record(stream)
+    enqueue = time.perf_counter() - wall0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    us_layer = ms_per_step * 1e3
+    touched = wl.touched_bytes(cfg, k)
+    value = touched / (ms_per_step * 1e-3) / 1e9
+    log(f"{us_layer:.2f} us/layer, {value:.1f} GB/s on touched bytes (wall {wall:.3f}s, "
+        f"host enqueue {enqueue / args.steps * 1e6:.1f} us/step)")
+
+    # ---- per-kernel times from the library's trace hook (a separate pass) -------------------
+    log(f"tracing {args.trace_steps} steps")
+    nev = len(KERNELS) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.trace_steps)]
+    for row in evs:                      # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for s in range(args.trace_steps):
+        csf.set_trace_events(evs[s])
+        rc = fn(*plan[(args.warmup + args.steps + s) % len(plan)])
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+    csf.set_trace_events([])
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for i, name in enumerate(KERNELS):
+        ts = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.trace_steps))
+        per_kernel[name] = {"avg_us": sum(ts) / len(ts), "p50_us": ts[len(ts) // 2]}
+    es = 2  # float16
+    kernel_bytes = {
+        "pred_down": r * d * es + d * es + r * 4,
+        "pred_up": f * r * es + r * 4 + f * 4,
+        "select_topk": f * 4 + k * 4,
+        "gather_up": k * d * es + d * es + k * 4 + k * 4,
+        "gather_down": k * d * es + k * 8,
+        "reduce_partials": 0,
+    }
+    dom = max(KERNELS, key=lambda n: per_kernel[n]["avg_us"])
+    dom_gbs = kernel_bytes[dom] / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": kernel_bytes[dom],
+                "avg_launch_us": round(per_kernel[dom]["avg_us"], 3)}
+    for n in KERNELS:
+        b = kernel_bytes[n]
+        per_kernel[n]["GBps"] = round(b / (per_kernel[n]["avg_us"] * 1e-6) / 1e9, 1) if b else None
+        per_kernel[n]["avg_us"] = round(per_kernel[n]["avg_us"], 3)
+        per_kernel[n]["p50_us"] = round(per_kernel[n]["p50_us"], 3)
+
+    # ---- dense FFN over the same layers ----------------------------------------------------
+    log(f"dense FFN {args.dense_steps} steps")
+    dws_bytes = csf.workspace_size(_lib.OP_DENSE_FFN, 1, d, f, 0, f, code)
+    dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+    hd = torch.empty(f, dtype=torch.float32, device=dev)
+    dfn = _lib.lib.csf_dense_ffn
+
+    def dense_call(l, t, h_out=None):
+        L = layers[l]
+        return dfn(vp(X[t].data_ptr()), 1, d, f, cfg.act, code, vp(L.W1.data_ptr()),
+                   vp(L.b1.data_ptr()), None, vp(L.W2T.data_ptr()),
+                   None if h_out is None else vp(h_out.data_ptr()), vp(y.data_ptr()),
+                   vp(dws.data_ptr()), dws_bytes, vp(stream.cuda_stream))
+
+    for s in range(4):
+        dense_call(s % args.layers, s)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(args.dense_steps):
+        dense_call(s % args.layers, s % args.tokens)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_us = e0.elapsed_time(e1) * 1e3 / args.dense_steps
+
+    # ---- predictor quality: recall / precision against the true active set -------------------
+    log(f"quality on {args.quality_tokens} tokens")
+    rec, prec, tfrac = [], [], []
+    for t in range(args.quality_tokens):
+        l = t % args.layers
+        rc = fn(*call_args(l, t, scores_out=scores, idx_out=idx))
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+        dense_call(l, t, h_out=hd)
+        torch.cuda.synchronize()
+        true = torch.nonzero(hd != 0).flatten()
+        pred = idx.long()
+        hit = torch.isin(pred, true).sum().item()
+        nt = true.numel()
+        rec.append(hit / nt if nt else 1.0)
+        prec.append(hit / k if k else 1.0)
+        tfrac.append(nt / f)
+
+    # ---- optional plain copy for counter calibration -----------------------------------------
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- CPU oracle baseline (rank 0, bounded sample) ----------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, layers[0], X, args.cpu_tokens, touched)
+
+    dense_b = wl.dense_bytes(cfg)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "OPT-175B-shape sparse FFN layer, batch 1: predict + top-k + gathered FFN",
+                   "d": d, "f": f, "r": r, "k": k, "batch": 1, "act": "relu",
+                   "weights": "float16, float32 accumulation", "layers_rotated": args.layers,
+                   "tokens": args.tokens, "parallelism": "single GPU"},
+        "us_per_layer": round(us_layer, 3),
+        "host_enqueue_us_per_step": round(enqueue / args.steps * 1e6, 2),
+        "tokens_per_s_per_layer": round(1e6 / us_layer, 1),
+        "touched_bytes": touched,
+        "frac_of_peak_hbm": round(value / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+        "kernels": per_kernel,
+        "dense_us_per_layer": round(dense_us, 3),
+        "dense_GBps": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
+        "speedup_vs_dense": round(dense_us / us_layer, 3),
+        "speedup_bound_bytes": round(dense_b / touched, 3),
+        "speedup_bound_active_frac": round(f / k, 3),
+        "recall": round(sum(rec) / len(rec), 4) if rec else None,
+        "precision": round(sum(prec) / len(prec), 4) if prec else None,
+        "true_frac": round(sum(tfrac) / len(tfrac), 4) if tfrac else None,
+        "pred_frac": round(k / f, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, L, X, ntok, touched):
+    """The oracle as it stands, single-threaded on the host, on `ntok` tokens of layer 0."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    log(f"CPU oracle baseline on {ntok} tokens")
+
+    def host(t):
+        return t.detach().cpu().numpy()
+
+    V, U, W1, W2T, b1 = host(L.V), host(L.U), host(L.W1), host(L.W2T), host(L.b1)
+    xs = [host(X[t]) for t in range(ntok)]
+    orc.lib()
+    t0 = time.perf_counter()
+    for x in xs:
+        _, _, s = orc.predict(x, V, U, orc.F16)
+        sel = orc.select_topk(s, cfg.k)
+        orc.sparse_ffn(x, W1, b1, None, W2T, sel, orc.RELU, orc.F16)
+    dt = time.perf_counter() - t0
+    gbs = touched * ntok / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_layer": round(dt / ntok * 1e6, 1),
+            "sample": f"{ntok} tokens of one layer of the same shape (predict + top-k + sparse FFN), "
+                      f"single-threaded C oracle with double accumulation, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -5,9 +5,9 @@ its sources (``csrc/``), the in-tree build (``build.py``), a thin ctypes binding
 functions carry the C entry points' names, and the seeded synthetic workloads (``workloads``).
 """
 from ._lib import (BF16, F16, F32, REGLU, RELU, CsfError, dense_ffn, k_from_ratio, lib,
-                   predict_active, select_threshold, select_topk, sparse_ffn, sparse_ffn_layer,
-                   workspace_size)
+                   predict_active, select_threshold, select_topk, set_trace_events, sparse_ffn,
+                   sparse_ffn_layer, workspace_size)
 
 __all__ = ["BF16", "F16", "F32", "REGLU", "RELU", "CsfError", "dense_ffn", "k_from_ratio", "lib",
-           "predict_active", "select_threshold", "select_topk", "sparse_ffn", "sparse_ffn_layer",
-           "workspace_size"]
+           "predict_active", "select_threshold", "select_topk", "set_trace_events", "sparse_ffn",
+           "sparse_ffn_layer", "workspace_size"]

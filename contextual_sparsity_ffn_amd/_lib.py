@@ -25,7 +25,7 @@ _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
 
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
            "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
-           "csf_dense_ffn", "csf_sparse_ffn_layer")
+           "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_set_trace_events")
 
 
 class CsfError(RuntimeError):
@@ -37,7 +37,7 @@ class CsfError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m contextual_sparsity_ffn_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python contextual_sparsity_ffn_amd/build.py` "
             "(hipcc, gfx950).  The library has no non-HIP fallback.")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz, flt = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
@@ -54,7 +54,8 @@ def _load():
     L.csf_select_threshold.argtypes = [vp, i32, i32, flt, vp, vp, vp, vp, sz, vp]
     L.csf_sparse_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32,
                                  vp, vp, vp, sz, vp]
-    L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_set_trace_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
                                        flt, vp, vp, vp, vp, vp, sz, vp]
     for name in EXPORTS[4:]:
@@ -238,8 +239,8 @@ def sparse_ffn(x, W1, b1, Wup, W2T, idx, act=RELU, count=None, max_count=None, h
     return y.view(d) if squeeze else y.view(B, d)
 
 
-def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, ws=None):
-    """y [B, d] float32 over every neuron."""
+def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
+    """y [B, d] float32 over every neuron; h [B, f] (optional) receives every activation."""
     squeeze = x.dim() == 1
     X = x.unsqueeze(0) if squeeze else x
     _tensor(X, "x")
@@ -249,11 +250,24 @@ def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, ws=None):
     if y is None:
         y = torch.empty(B, d, dtype=torch.float32, device=dev)
     _tensor(y, "y", dtype=torch.float32, device=dev)
+    if h is not None:
+        _tensor(h, "h", dtype=torch.float32, device=dev)
+        if h.numel() != B * f:
+            raise ValueError(f"h must hold {B}x{f} values")
     code = dtype_code(dt)
     w, wb = _workspace(workspace_size(OP_DENSE_FFN, B, d, f, 0, f, code), dev, ws)
     _check(lib.csf_dense_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
-                             _ptr(W2T), _ptr(y), _ptr(w), wb, _stream(dev)))
+                             _ptr(W2T), _ptr(h), _ptr(y), _ptr(w), wb, _stream(dev)))
     return y.view(d) if squeeze else y.view(B, d)
+
+
+def set_trace_events(events):
+    """Profiling hook: a list of >= 7 torch.cuda.Event(enable_timing=True) (or [] to switch off)
+    that csf_sparse_ffn_layer records around each of its kernels on its stream.  torch creates
+    the underlying HIP event on its first record(), so record each event once beforehand."""
+    n = len(events)
+    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib.csf_set_trace_events(arr, n))
 
 
 def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=None, scores=None,

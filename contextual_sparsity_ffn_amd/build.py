@@ -1,7 +1,8 @@
 """Build the HIP library ``libcsf.so`` in-tree for gfx950 with hipcc.
 
 Each source compiles to an object of its own (in parallel), then one shared-object link.
-Run as ``python -m contextual_sparsity_ffn_amd.build`` or through ``__graft_entry__.build()``.
+Run as ``python contextual_sparsity_ffn_amd/build.py`` or through ``__graft_entry__.build()``
+(not as ``-m``: importing the package loads the library this script builds).
 """
 from __future__ import annotations
 

@@ -11,11 +11,14 @@
 #include <string>
 
 #include "../../include/csf.h"
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_trace_events[16];
+thread_local int g_trace_n = 0;
 
 int fail(int status, const char *fmt, ...)
 {
@@ -119,7 +122,7 @@ FfnWs ffn_ws(int B, int d, int dtype, int max_count)
     FfnWs w;
     w.h = 0;
     w.partials = round_up((size_t)B * (max_count > 0 ? max_count : 1) * sizeof(float));
-    const int nchunk = csf::ffn_num_chunks(B, d, dtype, max_count);
+    const size_t nchunk = (size_t)csf::ffn_num_chunks(d, dtype, max_count);
     w.total = w.partials + round_up((size_t)B * nchunk * d * sizeof(float));
     return w;
 }
@@ -199,6 +202,18 @@ const char *csf_status_string(int status)
 }
 
 const char *csf_last_error(void) { return g_last_error.c_str(); }
+
+int csf_set_trace_events(void *const *events, int n)
+{
+    REQUIRE(n >= 0 && n <= 16, CSF_ERR_INVALID_ARG, "n = %d must be in [0, 16]", n);
+    REQUIRE(n == 0 || events, CSF_ERR_INVALID_ARG, "events must not be NULL when n > 0");
+    for (int i = 0; i < n; ++i)
+        REQUIRE(events[i], CSF_ERR_INVALID_ARG, "events[%d] is NULL", i);
+    for (int i = 0; i < n; ++i)
+        g_trace_events[i] = static_cast<hipEvent_t>(events[i]);
+    g_trace_n = n;
+    return ok();
+}
 
 size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype)
 {
@@ -330,12 +345,13 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
 }
 
 int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
-                  const float *b1, const void *Wup, const void *W2T, float *Y, void *ws,
+                  const float *b1, const void *Wup, const void *W2T, float *H, float *Y, void *ws,
                   size_t ws_bytes, void *stream)
 {
     int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
         return s;
+    CHECK_PTR(H, false);
     CHECK_PTR(Y, B > 0);
     if (B == 0)
         return ok();
@@ -356,7 +372,7 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     a.idx_stride = f;
     a.count = nullptr;
     a.max_count = f;
-    a.h = reinterpret_cast<float *>(at(ws, w.h));
+    a.h = H ? H : reinterpret_cast<float *>(at(ws, w.h));
     a.h_stride = f;
     a.y = Y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
@@ -388,6 +404,12 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     LayerWs w = layer_ws(d, f, r, max_count, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    csf::Trace tr;
+    if (g_trace_n >= 7) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    tr.mark(st);
 
     float *a = reinterpret_cast<float *>(at(ws, w.a));
     float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
@@ -397,15 +419,18 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
+    tr.mark(st);
     e = csf::launch_pred_up(dtype, a, 1, r, U, f, sc, st);
     if (e != hipSuccess)
         return hip_status(e, "predictor up-projection launch");
+    tr.mark(st);
     if (k >= 0)
         e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st);
     else
         e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st);
     if (e != hipSuccess)
         return hip_status(e, "selection launch");
+    tr.mark(st);
 
     FfnWs fw = ffn_ws(1, d, dtype, max_count);
     csf::FfnArgs fa;
@@ -427,7 +452,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     fa.h_stride = max_count > 0 ? max_count : 1;
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
-    return hip_status(csf::launch_ffn(fa, st), "sparse FFN launch");
+    return hip_status(csf::launch_ffn(fa, st, tr.ev ? &tr : nullptr), "sparse FFN launch");
 }
 
 }  // extern "C"

@@ -18,6 +18,19 @@ typedef short bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Buckets of the score histogram that top-k selection starts from.
+constexpr int kScoreBuckets = 2048;
+
+// Monotone, non-decreasing map of a score to a bucket in [0, NB): uniform buckets over [0, 1]
+// (the range of a sigmoid); values below 0 (and NaN) land in bucket 0, values >= 1 in NB - 1.
+// Scaling by NB is exact (a power of two) and truncation of a non-negative float is its floor.
+template <int NB>
+__device__ __forceinline__ int score_bucket(float s)
+{
+    const float v = fminf(fmaxf(s * (float)NB, 0.0f), (float)(NB - 1));
+    return (int)v;
+}
+
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }

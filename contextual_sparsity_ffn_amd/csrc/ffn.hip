@@ -13,11 +13,9 @@
 // per wavefront instruction, contiguous), and the down projection is stored neuron-major so that
 // the weights of an active neuron are one contiguous row as well:
 //   k_gather_up    workgroup of 256 threads per RPW active rows: h_n = act(W1[j_n].x + b1, Wup[j_n].x)
-//   k_gather_down  grid (d-slice of 64 chunks) x (neuron chunk) x token; each of the 4 wavefronts
-//                  of a workgroup accumulates every 4th neuron of its chunk into float32 registers;
-//                  the 4 wavefronts are summed in a fixed order through LDS and written as a
-//                  partial row;
-//   k_reduce       y = sum of the partial rows in chunk order (fixed order, so deterministic).
+//   k_gather_down  grid (d-slice of 1 KiB per row) x (chunk of the active list) x token; a partial
+//                  row per chunk;
+//   k_reduce_partials  sums the partial rows in chunk order (fixed order, so deterministic).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,8 +23,9 @@ namespace csf {
 
 namespace {
 
-constexpr int kDownUnroll = 8;    // neurons whose 16-byte chunks are in flight per wavefront
+constexpr int kDownUnroll = 4;    // list entries whose 16-byte chunks are in flight per lane
 constexpr int kSliceChunks = 64;  // one 16-byte chunk per lane: a d-slice is 1 KiB of a row
+constexpr int kMaxChunks = 64;    // most neuron chunks (partial rows) per slice
 
 __device__ __forceinline__ int token_count(const int32_t *count, int token, int max_count)
 {
@@ -140,6 +139,15 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
     }
 }
 
+// Down projection.  Grid: (d-slice of 64 chunks, neuron chunk, token).  Each lane owns one
+// 16-byte chunk column of the slice, so a wavefront instruction reads 1 KiB of one row, contiguous;
+// the 4 wavefronts of a workgroup take every 4th list entry of the chunk, kDownUnroll rows in
+// flight each (few rows per wavefront and many workgroups measured faster than deep unrolling:
+// occupancy, not per-wavefront queue depth, sets the gather rate).  The wavefronts are summed in
+// a fixed order and the chunk's partial row is stored; k_reduce_partials then sums the partial
+// rows in chunk order.  Handing the partials to another workgroup inside this kernel would need a
+// device-coherent write-back of each XCD's L2 per workgroup, which costs more than the kernel
+// boundary.  No float atomics anywhere, so y is deterministic.
 template <class T>
 __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W2T,
                                                      const float *__restrict__ h, int h_stride,
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
     __shared__ float red[3][kSliceChunks * E];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int slice = blockIdx.x, chunk = blockIdx.y, token = blockIdx.z;
+    const int D = C * E;
     const int c = slice * kSliceChunks + lane;
     const int cnt = token_count(count, token, max_count);
     const int per = (cnt + nchunk - 1) / nchunk;
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
         }
     }
 
-    // fixed-order sum of the 4 wavefronts: wave 0 + wave 1 + wave 2 + wave 3
+    // fixed-order sum of the 4 wavefronts: ((wave 0 + wave 1) + wave 2) + wave 3
     if (w > 0) {
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -196,25 +205,32 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
     }
     __syncthreads();
     if (w == 0 && c < C) {
-        float *out = part + ((size_t)token * nchunk + chunk) * ((size_t)C * E) + (size_t)c * E;
+        float *out = part + ((size_t)token * nchunk + chunk) * (size_t)D + (size_t)c * E;
 #pragma unroll
         for (int e = 0; e < E; ++e)
             out[e] = ((acc[e] + red[0][lane * E + e]) + red[1][lane * E + e]) + red[2][lane * E + e];
     }
 }
 
-__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ part, int nchunk, int D,
-                                                float *__restrict__ y)
+// y[token][col] = sum over chunks q (in order) of part[token][q][col]; one thread per column with
+// every partial load issued before the first add.
+__global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict__ part, int nchunk,
+                                                         int D, float *__restrict__ y)
 {
     const int col = blockIdx.x * 256 + threadIdx.x;
     const int token = blockIdx.y;
     if (col >= D)
         return;
-    const float *p = part + (size_t)token * nchunk * D + col;
-    float s = 0.0f;
-    for (int q = 0; q < nchunk; ++q)
-        s += p[(size_t)q * D];
-    y[(size_t)token * D + col] = s;
+    const float *p = part + (size_t)token * nchunk * (size_t)D + col;
+    float pv[kMaxChunks];
+#pragma unroll
+    for (int q = 0; q < kMaxChunks; ++q)
+        pv[q] = q < nchunk ? p[(size_t)q * D] : 0.0f;
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxChunks; ++q)
+        sum += pv[q];
+    y[(size_t)token * D + col] = sum;
 }
 
 template <class T, int MX, bool GATED>
@@ -247,52 +263,62 @@ hipError_t up_gated(const FfnArgs &a, int C, hipStream_t st)
 }
 
 template <class T>
-hipError_t ffn_t(const FfnArgs &a, hipStream_t st)
+hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / T::E;
     hipError_t e = a.act == 1 ? up_gated<T, true>(a, C, st) : up_gated<T, false>(a, C, st);
     if (e != hipSuccess)
         return e;
-    const int nchunk = ffn_num_chunks(a.B, a.d, a.dtype, a.max_count);
-    dim3 grid((C + kSliceChunks - 1) / kSliceChunks, nchunk, a.B);
+    if (tr)
+        tr->mark(st);
+    const int nchunk = ffn_num_chunks(a.d, a.dtype, a.max_count);
+    dim3 grid(ffn_num_slices(a.d, a.dtype), nchunk, a.B);
     k_gather_down<T><<<grid, 256, 0, st>>>(static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride,
                                            a.idx, a.idx_stride, a.count, a.max_count, a.f, C,
                                            nchunk, a.partials);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    if (tr)
+        tr->mark(st);
     dim3 rgrid((a.d + 255) / 256, a.B);
-    k_reduce<<<rgrid, 256, 0, st>>>(a.partials, nchunk, a.d, a.y);
-    return hipGetLastError();
+    k_reduce_partials<<<rgrid, 256, 0, st>>>(a.partials, nchunk, a.d, a.y);
+    e = hipGetLastError();
+    if (tr)
+        tr->mark(st);
+    return e;
 }
 
 }  // namespace
 
-int ffn_num_chunks(int B, int d, int dtype, int max_count)
+int ffn_num_slices(int d, int dtype)
 {
-    const int E = dtype == 0 ? 4 : 8;
-    const int C = d / E;
-    const int slices = (C + kSliceChunks - 1) / kSliceChunks;
-    // aim for about 1024 workgroups per token in the down projection, with at least 16 neurons
-    // per chunk.  The split depends on neither B nor the data, so a token's summation order (and
-    // its bits) are the same in every batch.
-    (void)B;
-    long want = (1024 + (long)slices - 1) / (long)slices;
-    long cap = max_count / 16;
-    if (want > cap)
-        want = cap;
-    if (want < 1)
-        want = 1;
-    if (want > 256)
-        want = 256;
-    return (int)want;
+    const int C = d / (dtype == 0 ? 4 : 8);
+    return (C + kSliceChunks - 1) / kSliceChunks;
 }
 
-hipError_t launch_ffn(const FfnArgs &a, hipStream_t st)
+int ffn_num_chunks(int d, int dtype, int max_count)
 {
-    if (a.dtype == 0) return ffn_t<F32T>(a, st);
-    if (a.dtype == 1) return ffn_t<F16T>(a, st);
-    return ffn_t<BF16T>(a, st);
+    // about 1536 workgroups per token in the down projection, at least 16 list entries per chunk.
+    // The split depends on neither the batch size nor the data, so a token's summation order
+    // (and its bits) are the same in every batch.
+    const int slices = ffn_num_slices(d, dtype);
+    int want = (1536 + slices - 1) / slices;
+    const int cap = max_count / 16;
+    if (want > cap)
+        want = cap;
+    if (want > kMaxChunks)
+        want = kMaxChunks;
+    if (want < 1)
+        want = 1;
+    return want;
+}
+
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t st, Trace *tr)
+{
+    if (a.dtype == 0) return ffn_t<F32T>(a, st, tr);
+    if (a.dtype == 1) return ffn_t<F16T>(a, st, tr);
+    return ffn_t<BF16T>(a, st, tr);
 }
 
 }  // namespace csf

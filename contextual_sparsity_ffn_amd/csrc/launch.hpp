@@ -11,6 +11,18 @@
 
 namespace csf {
 
+// Optional profiling marks: when set, mark() records the next caller-owned event on the stream.
+struct Trace {
+    hipEvent_t *ev = nullptr;
+    int n = 0;
+    int pos = 0;
+    void mark(hipStream_t st)
+    {
+        if (ev && pos < n)
+            (void)hipEventRecord(ev[pos++], st);
+    }
+};
+
 // ---- predictor (predict.hip) ----------------------------------------------------------------
 // a[B][r] = relu(V x_t) in float32.
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
@@ -42,10 +54,11 @@ struct FfnArgs {
     float *h;               // [B][h_stride]
     int h_stride;
     float *y;               // [B][d]
-    float *partials;        // workspace for the two-phase down-projection reduction
+    float *partials;        // [B][ffn_num_chunks][d] workspace
 };
-// Number of neuron chunks the down projection is split into (sizes the partials workspace).
-int ffn_num_chunks(int B, int d, int dtype, int max_count);
-hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream);
+// Shape of the down projection's two-phase reduction (sizes its workspace).
+int ffn_num_slices(int d, int dtype);
+int ffn_num_chunks(int d, int dtype, int max_count);
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 
 }  // namespace csf

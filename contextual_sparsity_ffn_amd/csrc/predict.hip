@@ -120,25 +120,33 @@ __global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
     }
 }
 
+struct DownArgs {
+    const void *x;
+    int B, C;
+    const void *V;
+    int r;
+    float *a;
+};
+
 template <class T, int MX>
-hipError_t down_mx(const void *x, int B, int C, const void *V, int r, float *a, hipStream_t st)
+hipError_t down_mx(const DownArgs &g, hipStream_t st)
 {
-    k_pred_down<T, MX><<<r, 256, 0, st>>>(static_cast<const u32x4 *>(V),
-                                          static_cast<const u32x4 *>(x), C, r, B, a);
+    k_pred_down<T, MX><<<g.r, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
+                                            static_cast<const u32x4 *>(g.x), g.C, g.r, g.B, g.a);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t down_t(const void *x, int B, int C, const void *V, int r, float *a, hipStream_t st)
+hipError_t down_t(const DownArgs &g, hipStream_t st)
 {
-    const int mx = (C + 255) / 256;
-    if (mx <= 1) return down_mx<T, 1>(x, B, C, V, r, a, st);
-    if (mx <= 2) return down_mx<T, 2>(x, B, C, V, r, a, st);
-    if (mx <= 4) return down_mx<T, 4>(x, B, C, V, r, a, st);
-    if (mx <= 6) return down_mx<T, 6>(x, B, C, V, r, a, st);
-    if (mx <= 8) return down_mx<T, 8>(x, B, C, V, r, a, st);
-    if (mx <= 12) return down_mx<T, 12>(x, B, C, V, r, a, st);
-    if (mx <= 16) return down_mx<T, 16>(x, B, C, V, r, a, st);
+    const int mx = (g.C + 255) / 256;
+    if (mx <= 1) return down_mx<T, 1>(g, st);
+    if (mx <= 2) return down_mx<T, 2>(g, st);
+    if (mx <= 4) return down_mx<T, 4>(g, st);
+    if (mx <= 6) return down_mx<T, 6>(g, st);
+    if (mx <= 8) return down_mx<T, 8>(g, st);
+    if (mx <= 12) return down_mx<T, 12>(g, st);
+    if (mx <= 16) return down_mx<T, 16>(g, st);
     return hipErrorInvalidValue;
 }
 
@@ -187,9 +195,10 @@ hipError_t up_t(const float *a, int B, int r, int C, const void *U, int f, float
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
                             float *a, hipStream_t st)
 {
-    if (dtype == 0) return down_t<F32T>(x, B, d / 4, V, r, a, st);
-    if (dtype == 1) return down_t<F16T>(x, B, d / 8, V, r, a, st);
-    return down_t<BF16T>(x, B, d / 8, V, r, a, st);
+    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, a};
+    if (dtype == 0) return down_t<F32T>(g, st);
+    if (dtype == 1) return down_t<F16T>(g, st);
+    return down_t<BF16T>(g, st);
 }
 
 hipError_t launch_pred_up(int dtype, const float *a, int B, int r, const void *U, int f,

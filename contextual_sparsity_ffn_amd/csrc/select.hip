@@ -5,16 +5,22 @@
 // scores the lower neuron index wins; -0.0 equals +0.0; the list is written in ascending order.
 // Threshold: "Activation sparsity", section "Implementation sketch" -- active = scores >= threshold.
 //
-// One 1024-thread workgroup per token.  Thread t owns the contiguous index range
-// [t*J, t*J + J) (J = ceil(f/1024)) and keeps those scores in registers, so every pass after the
-// first load runs out of registers and LDS:
-//   1. scores -> order-preserving 32-bit keys (binary32 sign/magnitude mapped onto unsigned order,
-//      -0.0 folded onto +0.0);
-//   2. radix select, 8 bits per pass, LDS histogram: finds T, the k-th largest key, and `need`,
-//      how many keys equal to T belong in the set (the lowest-indexed ones);
-//   3. one block-wide exclusive scan of the per-thread count of keys equal to T gives each
-//      thread its tie rank; a second scan of the per-thread selection count gives each thread
-//      its output position, so the list comes out in ascending index order with no sort.
+// Top-k runs as a bucket select.  Every score falls in one of kScoreBuckets buckets by a monotone
+// map of its value (uniform over [0, 1], the range of a sigmoid score; values outside clamp), so
+// all neurons in buckets above the bucket B* that holds the k-th score are selected, all below are
+// not, and only the candidates inside B* need ranking.  One 1024-thread workgroup per token holds
+// the scores in registers -- thread t takes scores 4t..4t+3 of every sweep of 4096, one coalesced
+// 16-byte load each, all issued before any is used -- and:
+//   1. builds the bucket histogram in LDS and finds B* and `need` (how many of B*'s candidates to
+//      take) with one block scan of the histogram, top bucket first;
+//   2. classifies its scores into 4-bit nibbles, ORs the nibbles of 8 neighbouring lanes into a
+//      bitmap word (lane shuffles, then one LDS store; no ballots or branches, so the CU's single
+//      scalar unit, shared by all 16 wavefronts, stays out of the loop); candidates go to an LDS
+//      list;
+//   3. ranks the candidates by (score desc, index asc) -- a direct count when there are at most
+//      kMaxDirect of them, else a radix select over the bucket's 32-bit order keys with an
+//      index-ordered pass for exact ties -- and sets their bits;
+//   4. compacts the bitmap into the ascending index list (popcounts + one block scan).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,7 +30,9 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kQuad = 4 * kSelThreads;     // scores per sweep: four consecutive per thread
 constexpr int kMaxWords = 2048;            // bitmap words held in LDS: f <= 65536
+constexpr int kMaxDirect = 512;            // candidates ranked by direct counting
 
 __device__ __forceinline__ uint32_t order_key(float s)
 {
@@ -34,239 +42,357 @@ __device__ __forceinline__ uint32_t order_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ void clear_words(uint32_t *bm, int words)
+// Rank of a (score, index) pair as one integer: larger ranks first (score desc, index asc).
+__device__ __forceinline__ uint64_t composite(uint32_t key, int j)
 {
-    for (int w = threadIdx.x; w < words; w += kSelThreads)
-        bm[w] = 0u;
+    return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
 }
 
-__device__ __forceinline__ void store_words(const uint32_t *bm, int words, uint32_t *out)
+// Four consecutive scores j0..j0+3 of one row; positions past f read as NaN.  VEC: the row is
+// 16-byte aligned (f % 4 == 0), so a full quad is one 16-byte load.
+template <bool VEC>
+__device__ __forceinline__ float4 load_quad(const float *s, int j0, int f)
 {
-    for (int w = threadIdx.x; w < words; w += kSelThreads)
-        out[w] = bm[w];
+    const float nan = __builtin_nanf("");
+    if (VEC && j0 + 3 < f)
+        return *reinterpret_cast<const float4 *>(s + j0);
+    float4 q;
+    q.x = j0 < f ? s[j0] : nan;
+    q.y = j0 + 1 < f ? s[j0 + 1] : nan;
+    q.z = j0 + 2 < f ? s[j0 + 2] : nan;
+    q.w = j0 + 3 < f ? s[j0 + 3] : nan;
+    return q;
 }
 
-template <int J>
+// Lane l holds a 4-bit nibble for scores 4l..4l+3 of a 256-score block; OR it across each group of
+// 8 lanes into the block's 32-bit words and store word l/8 from the group's first lane.  Other
+// lanes store into a per-lane trash slot, so no branch (and no scalar work) is needed.
+__device__ __forceinline__ void store_nibbles(uint32_t nib, uint32_t *bm, int word0, int words,
+                                              uint32_t *trash)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t x = nib << (4 * (lane & 7));
+    x |= __shfl_xor(x, 1, kWave);
+    x |= __shfl_xor(x, 2, kWave);
+    x |= __shfl_xor(x, 4, kWave);
+    const int widx = word0 + (lane >> 3);
+    uint32_t *dst = ((lane & 7) == 0 && widx < words) ? &bm[widx] : &trash[threadIdx.x];
+    *dst = x;
+}
+
+// Compaction of an LDS bitmap into the ascending index list; also copies the bitmap out.
+__device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int out_cap,
+                               uint32_t *bitmap_out, uint32_t *scan_tmp, uint32_t *total_out)
+{
+    const int t = threadIdx.x;
+    const int wpt = (words + kSelThreads - 1) / kSelThreads;   // <= 2 for f <= 65536
+    const int w0 = t * wpt;
+    uint32_t n = 0;
+    for (int q = 0; q < wpt; ++q)
+        if (w0 + q < words)
+            n += __popc(bm[w0 + q]);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kSelWaves>(n, scan_tmp, &total);
+    if (total_out)
+        *total_out = total;
+    for (int q = 0; q < wpt; ++q) {
+        const int w = w0 + q;
+        if (w >= words)
+            break;
+        uint32_t bits = bm[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (pos < (uint32_t)out_cap)
+                out[pos] = w * 32 + b;
+            ++pos;
+        }
+    }
+    if (bitmap_out)
+        for (int w = t; w < words; w += kSelThreads)
+            bitmap_out[w] = bm[w];
+}
+
+template <int NB, int J, bool VEC>
 __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__restrict__ scores,
-                                                             int f, int Jr, int k,
+                                                             int f, int k,
                                                              int32_t *__restrict__ idx,
                                                              int idx_stride,
                                                              int32_t *__restrict__ count,
                                                              uint32_t *__restrict__ bitmap)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t scan_tmp[kSelWaves];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t hist[NB];
     __shared__ uint32_t bm[kMaxWords];
+    __shared__ uint32_t trash[kSelThreads];
+    __shared__ uint64_t cand[kMaxDirect];
+    __shared__ uint32_t scan_tmp[kSelWaves];
+    __shared__ uint32_t rhist[256];
+    __shared__ uint32_t misc[8];   // 0: B*, 1: need, 2: candidate count, 3: digit, 4: krem
 
     const int t = threadIdx.x;
     const int token = blockIdx.x;
     const float *s = scores + (size_t)token * f;
     const int words = (f + 31) / 32;
-    const int base = t * Jr;
-    int nvalid = f - base;
-    nvalid = nvalid < 0 ? 0 : (nvalid > Jr ? Jr : nvalid);
+    int32_t *out = idx + (size_t)token * idx_stride;
+    uint32_t *bm_out = bitmap ? bitmap + (size_t)token * words : nullptr;
 
-    if (bitmap)
-        clear_words(bm, words);
-    if (t == 0 && count)
-        count[token] = k;
+    if (t == 0) {
+        misc[2] = 0u;
+        if (count)
+            count[token] = k;
+    }
+    if (k == 0) {                                     // uniform: nothing is selected
+        if (bm_out)
+            for (int q = t; q < words; q += kSelThreads)
+                bm_out[q] = 0u;
+        return;
+    }
 
-    uint32_t key[J];
+    // scores 4t..4t+3 of each sweep of 4096, held in registers; every load is issued first
+    float4 v[J];
 #pragma unroll
-    for (int q = 0; q < J; ++q)
-        key[q] = q < nvalid ? order_key(s[base + q]) : 0u;
+    for (int i = 0; i < J; ++i)
+        v[i] = load_quad<VEC>(s, i * kQuad + 4 * t, f);
 
-    uint32_t T = 0u, need = 0u;
-    if (k > 0) {
-        uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
+    // ---- 1. the bucket histogram and the boundary bucket B* ------------------------------------
+    for (int b = t; b < NB; b += kSelThreads)
+        hist[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < J; ++i) {
+        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (e[q] == e[q])
+                atomicAdd(&hist[score_bucket<NB>(e[q])], 1u);
+    }
+    __syncthreads();
+
+    // thread t owns buckets NB-1-BPT*t-q, q < BPT (thread 0 holds the top buckets)
+    constexpr int BPT = NB / kSelThreads;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q)
+        mine += hist[NB - 1 - (BPT * t + q)];
+    uint32_t total;
+    uint32_t above = block_exclusive_scan<kSelWaves>(mine, scan_tmp, &total);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const int b = NB - 1 - (BPT * t + q);
+        const uint32_t c = hist[b];
+        if (above < (uint32_t)k && above + c >= (uint32_t)k) {
+            misc[0] = (uint32_t)b;
+            misc[1] = (uint32_t)k - above;
+        }
+        above += c;
+    }
+    __syncthreads();
+    const int bstar = (int)misc[0];
+    const uint32_t need = misc[1];
+    const bool direct = hist[bstar] <= (uint32_t)kMaxDirect;
+
+    // ---- 2. certain members into the bitmap, candidates into LDS --------------------------------
+#pragma unroll
+    for (int i = 0; i < J; ++i) {
+        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t nib = 0u, cmask = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = e[q] == e[q] ? score_bucket<NB>(e[q]) : -1;
+            nib |= (b > bstar ? 1u : 0u) << q;
+            cmask |= (b == bstar ? 1u : 0u) << q;
+        }
+        const int j0 = i * kQuad + 4 * t;
+        store_nibbles(nib, bm, j0 >> 5 & ~7, words, trash);
+        if (direct && cmask) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cmask & (1u << q)) {
+                    const uint32_t p = atomicAdd(&misc[2], 1u);
+                    if (p < (uint32_t)kMaxDirect)
+                        cand[p] = composite(order_key(e[q]), j0 + q);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. rank the candidates of bucket B* -------------------------------------------------------
+    if (direct) {
+        const uint32_t nc = misc[2] < (uint32_t)kMaxDirect ? misc[2] : (uint32_t)kMaxDirect;
+        for (uint32_t i = t; i < nc; i += kSelThreads) {
+            const uint64_t me = cand[i];
+            uint32_t rank = 0;
+#pragma unroll 8
+            for (uint32_t q = 0; q < nc; ++q)
+                rank += cand[q] > me ? 1u : 0u;
+            if (rank < need) {
+                const int j = (int)(0xffffffffu - (uint32_t)me);
+                atomicOr(&bm[j >> 5], 1u << (j & 31));
+            }
+        }
+    } else {
+        // many candidates (heavy ties or a concentrated distribution): radix select over the
+        // 32-bit order keys of bucket B*, 8 bits per pass.  This rare path re-reads the scores
+        // from memory so that the common path keeps its registers.
+        uint32_t prefix = 0u, pmask = 0u, krem = need;
 #pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
             if (t < 256)
-                hist[t] = 0u;
+                rhist[t] = 0u;
             __syncthreads();
-#pragma unroll
-            for (int q = 0; q < J; ++q)
-                if (q < nvalid && (key[q] & pmask) == prefix)
-                    atomicAdd(&hist[(key[q] >> shift) & 0xffu], 1u);
+            for (int j = t; j < f; j += kSelThreads) {
+                const float x = s[j];
+                const uint32_t key = order_key(x);
+                if (score_bucket<NB>(x) == bstar && (key & pmask) == prefix)
+                    atomicAdd(&rhist[(key >> shift) & 0xffu], 1u);
+            }
             __syncthreads();
             if (t < kWave) {
-                // lane l holds digits 4l..4l+3; find the digit where the count of keys with a
-                // larger digit is < krem and including this digit's keys reaches krem
-                const uint32_t c0 = hist[4 * t], c1 = hist[4 * t + 1];
-                const uint32_t c2 = hist[4 * t + 2], c3 = hist[4 * t + 3];
+                const uint32_t c0 = rhist[4 * t], c1 = rhist[4 * t + 1];
+                const uint32_t c2 = rhist[4 * t + 2], c3 = rhist[4 * t + 3];
                 const uint32_t local = c0 + c1 + c2 + c3;
-                uint32_t suffix = local;               // sum over lanes >= t
+                uint32_t suffix = local;
 #pragma unroll
                 for (int o = 1; o < kWave; o <<= 1) {
-                    uint32_t n = __shfl_down(suffix, o, kWave);
+                    const uint32_t n = __shfl_down(suffix, o, kWave);
                     if (t + o < kWave)
                         suffix += n;
                 }
-                uint32_t above = suffix - local;       // keys in digits > 4t+3
+                uint32_t ab = suffix - local;
                 const uint32_t cs[4] = {c0, c1, c2, c3};
 #pragma unroll
                 for (int b = 3; b >= 0; --b) {
-                    if (above < krem && above + cs[b] >= krem) {
-                        pick[0] = (uint32_t)(4 * t + b);
-                        pick[1] = krem - above;
+                    if (ab < krem && ab + cs[b] >= krem) {
+                        misc[3] = (uint32_t)(4 * t + b);
+                        misc[4] = krem - ab;
                     }
-                    above += cs[b];
+                    ab += cs[b];
                 }
             }
             __syncthreads();
-            const uint32_t digit = pick[0];
-            krem = pick[1];
-            prefix |= digit << shift;
+            prefix |= misc[3] << shift;
             pmask |= 0xffu << shift;
+            krem = misc[4];
             __syncthreads();
         }
-        T = prefix;
-        need = krem;
-    }
-
-    // per-thread counts of keys above T and equal to T
-    uint32_t cgt = 0u, ceq = 0u;
-    if (k > 0) {
-#pragma unroll
-        for (int q = 0; q < J; ++q) {
-            if (q < nvalid) {
-                cgt += key[q] > T ? 1u : 0u;
-                ceq += key[q] == T ? 1u : 0u;
-            }
-        }
-    }
-    uint32_t total;
-    const uint32_t eq_before = block_exclusive_scan<kSelWaves>(ceq, scan_tmp, &total);
-    uint32_t take_eq = 0u;
-    if (need > eq_before)
-        take_eq = (need - eq_before) < ceq ? (need - eq_before) : ceq;
-    const uint32_t nsel = cgt + take_eq;
-    uint32_t pos = block_exclusive_scan<kSelWaves>(nsel, scan_tmp, &total);
-
-    if (nsel) {
-        int32_t *out = idx + (size_t)token * idx_stride;
-        uint32_t er = eq_before;
-#pragma unroll
-        for (int q = 0; q < J; ++q) {
-            if (q < nvalid) {
-                bool sel = key[q] > T;
-                if (key[q] == T) {
-                    sel = er < need;
-                    ++er;
-                }
-                if (sel) {
-                    const int j = base + q;
-                    if (pos < (uint32_t)idx_stride)
-                        out[pos] = j;
-                    ++pos;
-                    if (bitmap)
-                        atomicOr(&bm[j >> 5], 1u << (j & 31));
+        // keys above T are in; of the keys equal to T the krem lowest-indexed are in (blocks of
+        // 1024 indices in ascending order, a block scan ranks the equal keys inside each block)
+        const uint32_t T = prefix;
+        uint32_t taken = 0;
+#pragma unroll 1
+        for (int base = 0; base < f; base += kSelThreads) {
+            const int j = base + t;
+            bool gt = false, eq = false;
+            if (j < f) {
+                const float x = s[j];
+                if (score_bucket<NB>(x) == bstar) {
+                    const uint32_t key = order_key(x);
+                    gt = key > T;
+                    eq = key == T;
                 }
             }
+            uint32_t eq_total;
+            const uint32_t eq_before =
+                block_exclusive_scan<kSelWaves>(eq ? 1u : 0u, scan_tmp, &eq_total);
+            if (gt || (eq && taken + eq_before < krem))
+                atomicOr(&bm[j >> 5], 1u << (j & 31));
+            taken += eq_total;
         }
     }
-    if (bitmap) {
-        __syncthreads();
-        store_words(bm, words, bitmap + (size_t)token * words);
-    }
+    __syncthreads();
+
+    // ---- 4. ascending list ------------------------------------------------------------------------
+    bitmap_to_list(bm, words, out, idx_stride, bm_out, scan_tmp, nullptr);
 }
 
-template <int J>
+template <int J, bool VEC>
 __global__ __launch_bounds__(kSelThreads) void k_select_threshold(
-    const float *__restrict__ scores, int f, int Jr, float tau, int32_t *__restrict__ idx,
-    int idx_stride, int32_t *__restrict__ count, uint32_t *__restrict__ bitmap)
+    const float *__restrict__ scores, int f, float tau, int32_t *__restrict__ idx, int idx_stride,
+    int32_t *__restrict__ count, uint32_t *__restrict__ bitmap)
 {
-    __shared__ uint32_t scan_tmp[kSelWaves];
     __shared__ uint32_t bm[kMaxWords];
-
+    __shared__ uint32_t trash[kSelThreads];
+    __shared__ uint32_t scan_tmp[kSelWaves];
     const int t = threadIdx.x;
     const int token = blockIdx.x;
     const float *s = scores + (size_t)token * f;
     const int words = (f + 31) / 32;
-    const int base = t * Jr;
-    int nvalid = f - base;
-    nvalid = nvalid < 0 ? 0 : (nvalid > Jr ? Jr : nvalid);
-
-    if (bitmap)
-        clear_words(bm, words);
-
-    float v[J];
+    float4 v[J];
 #pragma unroll
-    for (int q = 0; q < J; ++q)
-        v[q] = q < nvalid ? s[base + q] : 0.0f;
-    uint32_t nsel = 0u;
+    for (int i = 0; i < J; ++i)
+        v[i] = load_quad<VEC>(s, i * kQuad + 4 * t, f);
 #pragma unroll
-    for (int q = 0; q < J; ++q)
-        nsel += (q < nvalid && v[q] >= tau) ? 1u : 0u;
+    for (int i = 0; i < J; ++i) {
+        // NaN (positions past f) never compares >= tau
+        const uint32_t nib = (v[i].x >= tau ? 1u : 0u) | (v[i].y >= tau ? 2u : 0u) |
+                             (v[i].z >= tau ? 4u : 0u) | (v[i].w >= tau ? 8u : 0u);
+        store_nibbles(nib, bm, (i * kQuad + 4 * t) >> 5 & ~7, words, trash);
+    }
+    __syncthreads();
     uint32_t total;
-    uint32_t pos = block_exclusive_scan<kSelWaves>(nsel, scan_tmp, &total);
+    bitmap_to_list(bm, words, idx + (size_t)token * idx_stride, idx_stride,
+                   bitmap ? bitmap + (size_t)token * words : nullptr, scan_tmp, &total);
     if (t == 0)
         count[token] = (int32_t)total;
-    if (nsel) {
-        int32_t *out = idx + (size_t)token * idx_stride;
-#pragma unroll
-        for (int q = 0; q < J; ++q) {
-            if (q < nvalid && v[q] >= tau) {
-                const int j = base + q;
-                if (pos < (uint32_t)idx_stride)
-                    out[pos] = j;
-                ++pos;
-                if (bitmap)
-                    atomicOr(&bm[j >> 5], 1u << (j & 31));
-            }
-        }
-    }
-    if (bitmap) {
-        __syncthreads();
-        store_words(bm, words, bitmap + (size_t)token * words);
-    }
 }
 
-int per_thread(int f) { return (f + kSelThreads - 1) / kSelThreads; }
+
+template <int J>
+hipError_t topk_j(const float *scores, int B, int f, int k, int32_t *idx, int idx_stride,
+                  int32_t *count, uint32_t *bitmap, hipStream_t st)
+{
+    if (f % 4 == 0)
+        k_select_topk<kScoreBuckets, J, true><<<B, kSelThreads, 0, st>>>(scores, f, k, idx,
+                                                                         idx_stride, count, bitmap);
+    else
+        k_select_topk<kScoreBuckets, J, false><<<B, kSelThreads, 0, st>>>(scores, f, k, idx,
+                                                                          idx_stride, count, bitmap);
+    return hipGetLastError();
+}
+
+template <int J>
+hipError_t threshold_j(const float *scores, int B, int f, float tau, int32_t *idx, int idx_stride,
+                       int32_t *count, uint32_t *bitmap, hipStream_t st)
+{
+    if (f % 4 == 0)
+        k_select_threshold<J, true><<<B, kSelThreads, 0, st>>>(scores, f, tau, idx, idx_stride,
+                                                               count, bitmap);
+    else
+        k_select_threshold<J, false><<<B, kSelThreads, 0, st>>>(scores, f, tau, idx, idx_stride,
+                                                                count, bitmap);
+    return hipGetLastError();
+}
 
 }  // namespace
 
-int select_max_f() { return 64 * kSelThreads; }
+int select_max_f() { return 32 * kMaxWords; }
 
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap, hipStream_t st)
 {
-    const int Jr = per_thread(f);
-    dim3 grid(B), block(kSelThreads);
-#define CSF_TOPK(JJ) \
-    k_select_topk<JJ><<<grid, block, 0, st>>>(scores, f, Jr, k, idx, idx_stride, count, bitmap)
-    if (Jr <= 1) CSF_TOPK(1);
-    else if (Jr <= 2) CSF_TOPK(2);
-    else if (Jr <= 4) CSF_TOPK(4);
-    else if (Jr <= 8) CSF_TOPK(8);
-    else if (Jr <= 16) CSF_TOPK(16);
-    else if (Jr <= 32) CSF_TOPK(32);
-    else if (Jr <= 64) CSF_TOPK(64);
-    else return hipErrorInvalidValue;
-#undef CSF_TOPK
-    return hipGetLastError();
+    const int J = (f + kQuad - 1) / kQuad;     // sweeps of 4096 scores
+    if (J <= 1) return topk_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 2) return topk_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 4) return topk_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 8) return topk_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 12) return topk_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 16) return topk_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
                                    hipStream_t st)
 {
-    const int Jr = per_thread(f);
-    dim3 grid(B), block(kSelThreads);
-#define CSF_THR(JJ) \
-    k_select_threshold<JJ><<<grid, block, 0, st>>>(scores, f, Jr, tau, idx, idx_stride, count, \
-                                                   bitmap)
-    if (Jr <= 1) CSF_THR(1);
-    else if (Jr <= 2) CSF_THR(2);
-    else if (Jr <= 4) CSF_THR(4);
-    else if (Jr <= 8) CSF_THR(8);
-    else if (Jr <= 16) CSF_THR(16);
-    else if (Jr <= 32) CSF_THR(32);
-    else if (Jr <= 64) CSF_THR(64);
-    else return hipErrorInvalidValue;
-#undef CSF_THR
-    return hipGetLastError();
+    const int J = (f + kQuad - 1) / kQuad;
+    if (J <= 1) return threshold_j<1>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 2) return threshold_j<2>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 4) return threshold_j<4>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 8) return threshold_j<8>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 12) return threshold_j<12>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 16) return threshold_j<16>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace csf

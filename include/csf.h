@@ -161,10 +161,14 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
  * csf_dense_ffn -- the same FFN over every neuron; the reference the sparse step must beat
  * ([CP] "The predictor and its budget": the dense layer's bytes are the budget).
  *   X [B][d] dtype, Y [B][d] float32; other arguments as csf_sparse_ffn.
+ *   H [B][f] float32, optional (NULL): the activation of every neuron.  Its non-zero entries are
+ *   the true active set ([DV] "The Empirical Foundation": a ReLU neuron is either exactly zero
+ *   or contributes), against which a predicted set's recall and precision are measured
+ *   ([CP] "Precision, recall, and which error hurts").
  * Workspace: csf_workspace_size(CSF_OP_DENSE_FFN, B, d, f, 0, f, dtype).
  * ------------------------------------------------------------------------------------------- */
 int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
-                  const float *b1, const void *Wup, const void *W2T, float *Y, void *ws,
+                  const float *b1, const void *Wup, const void *W2T, float *H, float *Y, void *ws,
                   size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
@@ -184,6 +188,16 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
                          const void *W2T, int k, float tau, float *y, float *scores_out,
                          int32_t *idx_out, int32_t *count_out, void *ws, size_t ws_bytes,
                          void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_set_trace_events -- profiling hook for csf_sparse_ffn_layer (per calling thread).
+ * While n >= 7 events are set, each csf_sparse_ffn_layer call records, on its stream,
+ * events[0] before its first kernel and events[i] after its i-th kernel: 1 predictor
+ * down-projection, 2 predictor up-projection, 3 selection, 4 gathered up/gate rows, 5 gathered
+ * down rows (partial sums), 6 reduction of the partial sums.  Differences of consecutive events time each kernel.  The events are
+ * hipEvent_t handles (as void*) created and owned by the caller; n = 0 switches tracing off.
+ * ------------------------------------------------------------------------------------------- */
+int csf_set_trace_events(void *const *events, int n);
 
 #ifdef __cplusplus
 }
