@@ -110,7 +110,7 @@ PredictWs predict_ws(int B, int r)
 {
     PredictWs w;
     w.a = 0;
-    w.total = round_up((size_t)B * r * sizeof(float));
+    w.total = round_up((size_t)csf::kMaxPredSplit * B * r * sizeof(float));
     return w;
 }
 
@@ -134,7 +134,7 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
 {
     LayerWs w;
     w.a = 0;
-    w.scores = w.a + round_up((size_t)r * sizeof(float));
+    w.scores = w.a + round_up((size_t)csf::kMaxPredSplit * r * sizeof(float));
     w.idx = w.scores + round_up((size_t)f * sizeof(float));
     w.count = w.idx + round_up((size_t)f * sizeof(int32_t));
     w.ffn = w.count + round_up(sizeof(int32_t));
@@ -257,7 +257,7 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
     hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, a, st);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
-    return hip_status(csf::launch_pred_up(dtype, a, B, r, U, f, scores, st),
+    return hip_status(csf::launch_pred_up(dtype, a, B, d, r, U, f, scores, st),
                       "predictor up-projection launch");
 }
 
@@ -420,7 +420,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
     tr.mark(st);
-    e = csf::launch_pred_up(dtype, a, 1, r, U, f, sc, st);
+    e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st);
     if (e != hipSuccess)
         return hip_status(e, "predictor up-projection launch");
     tr.mark(st);

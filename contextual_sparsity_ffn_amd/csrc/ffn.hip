@@ -37,12 +37,13 @@ __device__ __forceinline__ int token_count(const int32_t *count, int token, int 
 
 template <int MX, bool GATED>
 struct UpShape {
-    // rows in flight per workgroup: about 24 chunk loads per thread, at most 4 rows
+    // rows per workgroup: about 12 chunk loads in flight per thread, at most 4 rows (measured:
+    // deeper queues per thread with fewer workgroups gather more slowly)
     static constexpr int loads = MX * (GATED ? 2 : 1);
-    static constexpr int RPW = loads >= 24 ? 1 : (loads >= 12 ? 2 : 4);
+    static constexpr int RPW = loads >= 12 ? 1 : (loads >= 6 ? 2 : 4);
 };
 
-template <class T, int MX, bool GATED>
+template <class T, int MX, bool GATED, int RPW = UpShape<MX, GATED>::RPW>
 __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
                                                    const u32x4 *__restrict__ W1,
                                                    const u32x4 *__restrict__ Wup,
@@ -53,7 +54,6 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
                                                    int max_count, int f, int C,
                                                    float *__restrict__ h, int h_stride)
 {
-    constexpr int RPW = UpShape<MX, GATED>::RPW;
     __shared__ float red[4][RPW][GATED ? 2 : 1];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int token = blockIdx.y;

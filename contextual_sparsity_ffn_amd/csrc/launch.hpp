@@ -24,11 +24,14 @@ struct Trace {
 };
 
 // ---- predictor (predict.hip) ----------------------------------------------------------------
-// a[B][r] = relu(V x_t) in float32.
+// Split-K factor of the predictor's down projection (rows of V split over S workgroups).
+constexpr int kMaxPredSplit = 4;
+int pred_split(int r, int d, int dtype);
+// part[S][B][r] = split-K partial sums of V x_t (float32), S = pred_split(r, d, dtype).
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *a, hipStream_t stream);
-// s[B][f] = sigmoid(U a_t) in float32.
-hipError_t launch_pred_up(int dtype, const float *a, int B, int r, const void *U, int f,
+                            float *part, hipStream_t stream);
+// s[B][f] = sigmoid(U relu(sum of the partials)) in float32.
+hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
                           float *s, hipStream_t stream);
 
 // ---- selection (select.hip) -----------------------------------------------------------------

@@ -6,11 +6,12 @@
 //
 // Both halves are skinny GEMVs bound by HBM bandwidth (2 flops per weight element read), so they
 // are written as streaming dot-product kernels, not as MFMA tiles:
-//   k_pred_down  one 256-thread workgroup per row of V; each thread keeps its 16-byte chunks of the
-//                row in registers and reuses them for every token; ReLU in the epilogue.
+//   k_pred_down  S 256-thread workgroups per row of V (split-K); each thread keeps its 16-byte
+//                chunks in registers and reuses them for every token; partial sums out.
 //   k_pred_up    groups of LPR lanes per row of U (LPR = 16/32/64 so short rows still use whole
-//                128-byte lines); the hidden activation a (float32) of the lane's chunk positions
-//                sits in registers; sigmoid in the epilogue.
+//                128-byte lines); the prologue adds the split-K partials and applies ReLU, and
+//                the hidden activation a (float32) of the lane's chunk positions sits in
+//                registers; sigmoid in the epilogue.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,50 +19,55 @@ namespace csf {
 
 namespace {
 
-template <class T, int MX>
+// Split-K down projection: S workgroups per row of V, each over a contiguous 1/S of the row's
+// 16-byte chunks (more, shorter workgroups keep more of HBM busy than one workgroup per row).  The
+// partial sums go to part[S][B][r]; the up-projection kernel adds them in order and applies ReLU.
+template <class T, int MX, int TG>
 __global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
                                                    const u32x4 *__restrict__ x, int C, int r,
-                                                   int B, float *__restrict__ a)
+                                                   int B, int S, float *__restrict__ part)
 {
-    __shared__ float red[4][8];
-    const int i = blockIdx.x;
+    __shared__ float red[4][TG];
+    const int i = blockIdx.x / S, sp = blockIdx.x % S;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int cper = (C + S - 1) / S;
+    const int c0 = sp * cper;
+    const int c1 = c0 + cper < C ? c0 + cper : C;
     const u32x4 *row = V + (size_t)i * C;
     u32x4 wv[MX];
 #pragma unroll
     for (int m = 0; m < MX; ++m) {
-        const int c = t + 256 * m;
-        wv[m] = c < C ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
+        const int c = c0 + t + 256 * m;
+        wv[m] = c < c1 ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
     }
-    for (int t0 = 0; t0 < B; t0 += 8) {
-        float acc[8];
+    // tokens in groups of TG (TG = 1 for a single token: one accumulator, one reduction)
+    for (int t0 = 0; t0 < B; t0 += TG) {
+        float acc[TG];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < TG; ++q) {
             acc[q] = 0.0f;
             const int tok = t0 + q;
             if (tok < B) {
                 const u32x4 *xt = x + (size_t)tok * C;
 #pragma unroll
                 for (int m = 0; m < MX; ++m) {
-                    const int c = t + 256 * m;
-                    if (c < C)
+                    const int c = c0 + t + 256 * m;
+                    if (c < c1)
                         acc[q] = T::dot(wv[m], xt[c], acc[q]);
                 }
             }
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < TG; ++q)
             acc[q] = wave_sum(acc[q]);
         if (lane == 0) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < TG; ++q)
                 red[w][q] = acc[q];
         }
         __syncthreads();
-        if (t < 8 && t0 + t < B) {
-            const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
-            a[(size_t)(t0 + t) * r + i] = s > 0.0f ? s : 0.0f;
-        }
+        if (t < TG && t0 + t < B)
+            part[((size_t)sp * B + t0 + t) * r + i] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
         __syncthreads();
     }
 }
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
 template <class T, int LPR, int MM, int RW>
 __global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
                                                  const float *__restrict__ a, int C, int r, int f,
-                                                 int B, float *__restrict__ s)
+                                                 int B, int S, float *__restrict__ s)
 {
     constexpr int G = kWave / LPR;   // rows handled side by side by one wavefront
     constexpr int E = T::E;
@@ -89,18 +95,31 @@ __global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
         }
     }
     for (int tok = 0; tok < B; ++tok) {
-        const float *at = a + (size_t)tok * r;
+        // hidden activation a = relu(sum of the S split-K partial sums, in order)
         float av[MM][E];
 #pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            const int c = li + LPR * m;
+        for (int m = 0; m < MM; ++m)
 #pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                float4 v = c < C ? *reinterpret_cast<const float4 *>(at + c * E + e)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-                av[m][e] = v.x; av[m][e + 1] = v.y; av[m][e + 2] = v.z; av[m][e + 3] = v.w;
+            for (int e = 0; e < E; ++e)
+                av[m][e] = 0.0f;
+        for (int sp = 0; sp < S; ++sp) {
+            const float *at = a + ((size_t)sp * B + tok) * r;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int c = li + LPR * m;
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    float4 v = c < C ? *reinterpret_cast<const float4 *>(at + c * E + e)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                    av[m][e] += v.x; av[m][e + 1] += v.y; av[m][e + 2] += v.z; av[m][e + 3] += v.w;
+                }
             }
         }
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                av[m][e] = av[m][e] > 0.0f ? av[m][e] : 0.0f;
 #pragma unroll
         for (int st = 0; st < RW; ++st) {
             float acc = 0.0f;
@@ -124,22 +143,28 @@ struct DownArgs {
     const void *x;
     int B, C;
     const void *V;
-    int r;
+    int r, S;
     float *a;
 };
 
 template <class T, int MX>
 hipError_t down_mx(const DownArgs &g, hipStream_t st)
 {
-    k_pred_down<T, MX><<<g.r, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
-                                            static_cast<const u32x4 *>(g.x), g.C, g.r, g.B, g.a);
+    if (g.B == 1)
+        k_pred_down<T, MX, 1><<<g.r * g.S, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
+                                                         static_cast<const u32x4 *>(g.x), g.C, g.r,
+                                                         g.B, g.S, g.a);
+    else
+        k_pred_down<T, MX, 8><<<g.r * g.S, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
+                                                         static_cast<const u32x4 *>(g.x), g.C, g.r,
+                                                         g.B, g.S, g.a);
     return hipGetLastError();
 }
 
 template <class T>
 hipError_t down_t(const DownArgs &g, hipStream_t st)
 {
-    const int mx = (g.C + 255) / 256;
+    const int mx = ((g.C + g.S - 1) / g.S + 255) / 256;
     if (mx <= 1) return down_mx<T, 1>(g, st);
     if (mx <= 2) return down_mx<T, 2>(g, st);
     if (mx <= 4) return down_mx<T, 4>(g, st);
@@ -151,62 +176,78 @@ hipError_t down_t(const DownArgs &g, hipStream_t st)
 }
 
 template <class T, int LPR, int MM, int RW>
-hipError_t up_launch(const float *a, int B, int r, int C, const void *U, int f, float *s,
+hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
                      hipStream_t st)
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
     const int blocks = (waves + 3) / 4;
     k_pred_up<T, LPR, MM, RW><<<blocks, 256, 0, st>>>(static_cast<const u32x4 *>(U), a, C, r, f,
-                                                       B, s);
+                                                       B, S, s);
     return hipGetLastError();
 }
 
-// Rows in flight per lane group: enough 16-byte loads per lane (about 8) to cover HBM latency,
-// fewer when the matrix is too short to give every CU several workgroups.
+// Rows per lane group: up to 4, so that each wavefront's read of the hidden activation (S partial
+// vectors, from L2) is amortized over several rows; fewer when the matrix is too short to give
+// every CU several workgroups.
 template <class T, int LPR, int MM>
-hipError_t up_rw(const float *a, int B, int r, int C, const void *U, int f, float *s,
+hipError_t up_rw(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
                  hipStream_t st)
 {
     constexpr int G = kWave / LPR;
-    int rw = 8 / MM > 4 ? 4 : (8 / MM < 1 ? 1 : 8 / MM);
+    int rw = 4;
     while (rw > 1 && (long)f / (rw * G) < 4096)   // keep >= 1024 workgroups when f allows
         rw /= 2;
-    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, r, C, U, f, s, st);
-    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, r, C, U, f, s, st);
-    return up_launch<T, LPR, MM, 1>(a, B, r, C, U, f, s, st);
+    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st);
+    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, S, r, C, U, f, s, st);
+    return up_launch<T, LPR, MM, 1>(a, B, S, r, C, U, f, s, st);
 }
 
 template <class T>
-hipError_t up_t(const float *a, int B, int r, int C, const void *U, int f, float *s,
+hipError_t up_t(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
                 hipStream_t st)
 {
-    if (C <= 16) return up_rw<T, 16, 1>(a, B, r, C, U, f, s, st);
-    if (C <= 32) return up_rw<T, 32, 1>(a, B, r, C, U, f, s, st);
-    if (C <= 64) return up_rw<T, 64, 1>(a, B, r, C, U, f, s, st);
-    if (C <= 128) return up_rw<T, 64, 2>(a, B, r, C, U, f, s, st);
-    if (C <= 256) return up_rw<T, 64, 4>(a, B, r, C, U, f, s, st);
-    if (C <= 512) return up_rw<T, 64, 8>(a, B, r, C, U, f, s, st);
+    if (C <= 16) return up_rw<T, 16, 1>(a, B, S, r, C, U, f, s, st);
+    if (C <= 32) return up_rw<T, 32, 1>(a, B, S, r, C, U, f, s, st);
+    if (C <= 64) return up_rw<T, 64, 1>(a, B, S, r, C, U, f, s, st);
+    if (C <= 128) return up_rw<T, 64, 2>(a, B, S, r, C, U, f, s, st);
+    if (C <= 256) return up_rw<T, 64, 4>(a, B, S, r, C, U, f, s, st);
+    if (C <= 512) return up_rw<T, 64, 8>(a, B, S, r, C, U, f, s, st);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+int pred_split(int r, int d, int dtype)
+{
+    // Split only short predictors (r < 1024): every wavefront of the up projection re-reads all S
+    // partial vectors, which costs more than the split gains once r is large.  Each workgroup
+    // keeps at least 256 16-byte chunks of its row.
+    const int C = d / (dtype == 0 ? 4 : 8);
+    int S = 1024 / r;
+    if (S > kMaxPredSplit)
+        S = kMaxPredSplit;
+    while (S > 1 && C / S < 256)
+        --S;
+    return S < 1 ? 1 : S;
+}
+
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
                             float *a, hipStream_t st)
 {
-    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, a};
+    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a};
     if (dtype == 0) return down_t<F32T>(g, st);
     if (dtype == 1) return down_t<F16T>(g, st);
     return down_t<BF16T>(g, st);
 }
 
-hipError_t launch_pred_up(int dtype, const float *a, int B, int r, const void *U, int f,
+hipError_t launch_pred_up(int dtype, const float *a, int B, int d, int r, const void *U, int f,
                           float *s, hipStream_t st)
 {
-    if (dtype == 0) return up_t<F32T>(a, B, r, r / 4, U, f, s, st);
-    if (dtype == 1) return up_t<F16T>(a, B, r, r / 8, U, f, s, st);
-    return up_t<BF16T>(a, B, r, r / 8, U, f, s, st);
+    const int S = pred_split(r, d, dtype);
+    if (dtype == 0) return up_t<F32T>(a, B, S, r, r / 4, U, f, s, st);
+    if (dtype == 1) return up_t<F16T>(a, B, S, r, r / 8, U, f, s, st);
+    return up_t<BF16T>(a, B, S, r, r / 8, U, f, s, st);
 }
 
 }  // namespace csf
