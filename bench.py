@@ -123,8 +123,8 @@ def main():
         f"host enqueue {enqueue / args.steps * 1e6:.1f} us/step)")
 
     # ---- per-kernel times from the library's trace hook (a separate pass) -------------------
-    log(f"tracing {args.trace_steps} steps")
-    nev = len(KERNELS) + 1
+    log(f"timing each kernel over {args.trace_steps} steps")
+    nev = 2 * len(KERNELS)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.trace_steps)]
     for row in evs:                      # torch creates the HIP event on first record
         for e in row:
@@ -139,7 +139,8 @@ def main():
     torch.cuda.synchronize()
     per_kernel = {}
     for i, name in enumerate(KERNELS):
-        ts = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.trace_steps))
+        # the runtime records these at the kernel's own start and end
+        ts = sorted(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) * 1e3 for s in range(args.trace_steps))
         per_kernel[name] = {"avg_us": sum(ts) / len(ts), "p50_us": ts[len(ts) // 2]}
     es = 2  # float16
     kernel_bytes = {
@@ -152,8 +153,16 @@ def main():
     }
     dom = max(KERNELS, key=lambda n: per_kernel[n]["avg_us"])
     dom_gbs = kernel_bytes[dom] / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
+    # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated), valid only
+    # while the kernel sources are the ones the counters were taken from
+    from contextual_sparsity_ffn_amd import profiling
+    counters = profiling.load_counters(os.path.join(ROOT, "profiles", "layer_opt175b_hbm_counters.json"))
+    traffic = None
+    if counters and dom in counters["kernels"]:
+        kc = counters["kernels"][dom]
+        traffic = int(round(kc["fetch_bytes"] + kc["write_bytes"]))
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": kernel_bytes[dom],
                 "avg_launch_us": round(per_kernel[dom]["avg_us"], 3)}
     for n in KERNELS:
@@ -176,15 +185,17 @@ def main():
                    None if h_out is None else vp(h_out.data_ptr()), vp(y.data_ptr()),
                    vp(dws.data_ptr()), dws_bytes, vp(stream.cuda_stream))
 
-    for s in range(4):
-        dense_call(s % args.layers, s)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for s in range(args.dense_steps):
-        dense_call(s % args.layers, s % args.tokens)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dense_us = e0.elapsed_time(e1) * 1e3 / args.dense_steps
+    dense_us = None
+    if args.dense_steps > 0:
+        for s in range(4):
+            dense_call(s % args.layers, s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(args.dense_steps):
+            dense_call(s % args.layers, s % args.tokens)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_us = e0.elapsed_time(e1) * 1e3 / args.dense_steps
 
     # ---- predictor quality: recall / precision against the true active set -------------------
     log(f"quality on {args.quality_tokens} tokens")
@@ -242,9 +253,9 @@ def main():
         "frac_of_peak_hbm": round(value / PEAK_HBM_GBS, 4),
         "roofline": roofline,
         "kernels": per_kernel,
-        "dense_us_per_layer": round(dense_us, 3),
-        "dense_GBps": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
-        "speedup_vs_dense": round(dense_us / us_layer, 3),
+        "dense_us_per_layer": round(dense_us, 3) if dense_us else None,
+        "dense_GBps": round(dense_b / (dense_us * 1e-6) / 1e9, 1) if dense_us else None,
+        "speedup_vs_dense": round(dense_us / us_layer, 3) if dense_us else None,
         "speedup_bound_bytes": round(dense_b / touched, 3),
         "speedup_bound_active_frac": round(f / k, 3),
         "recall": round(sum(rec) / len(rec), 4) if rec else None,

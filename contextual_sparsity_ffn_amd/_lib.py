@@ -262,9 +262,10 @@ def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
 
 
 def set_trace_events(events):
-    """Profiling hook: a list of >= 7 torch.cuda.Event(enable_timing=True) (or [] to switch off)
-    that csf_sparse_ffn_layer records around each of its kernels on its stream.  torch creates
-    the underlying HIP event on its first record(), so record each event once beforehand."""
+    """Per-kernel timing hook: a list of up to 16 torch.cuda.Event(enable_timing=True) (or [] to
+    switch off); the i-th kernel of csf_sparse_ffn_layer gets events 2i (start) and 2i+1 (end),
+    recorded by the runtime at the kernel's own start and end.  torch creates the underlying HIP
+    event on its first record(), so record each event once beforehand."""
     n = len(events)
     arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     _check(lib.csf_set_trace_events(arr, n))

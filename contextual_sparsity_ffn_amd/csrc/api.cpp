@@ -405,32 +405,30 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     CHECK_WS(ws, ws_bytes, w.total);
     hipStream_t st = static_cast<hipStream_t>(stream);
     csf::Trace tr;
-    if (g_trace_n >= 7) {
+    if (g_trace_n > 0) {
         tr.ev = g_trace_events;
         tr.n = g_trace_n;
     }
-    tr.mark(st);
 
     float *a = reinterpret_cast<float *>(at(ws, w.a));
     float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
     int32_t *ix = idx_out ? idx_out : reinterpret_cast<int32_t *>(at(ws, w.idx));
     int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
 
-    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st);
+    csf::Trace *trp = tr.ev ? &tr : nullptr;
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
-    tr.mark(st);
-    e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st);
+    e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "predictor up-projection launch");
-    tr.mark(st);
     if (k >= 0)
-        e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st);
+        e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st,
+                                    trp);
     else
-        e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st);
+        e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "selection launch");
-    tr.mark(st);
 
     FfnWs fw = ffn_ws(1, d, dtype, max_count);
     csf::FfnArgs fa;
@@ -452,7 +450,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     fa.h_stride = max_count > 0 ? max_count : 1;
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
-    return hip_status(csf::launch_ffn(fa, st, tr.ev ? &tr : nullptr), "sparse FFN launch");
+    return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 
 }  // extern "C"

@@ -234,31 +234,29 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict
 }
 
 template <class T, int MX, bool GATED>
-hipError_t up_launch(const FfnArgs &a, int C, hipStream_t st)
+hipError_t up_launch(const FfnArgs &a, int C, hipStream_t st, Trace *tr)
 {
     constexpr int RPW = UpShape<MX, GATED>::RPW;
     const int blocks = (a.max_count + RPW - 1) / RPW;
     if (blocks == 0)
         return hipSuccess;
-    dim3 grid(blocks, a.B);
-    k_gather_up<T, MX, GATED><<<grid, 256, 0, st>>>(
-        static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
-        static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count, a.max_count, a.f,
-        C, a.h, a.h_stride);
-    return hipGetLastError();
+    return launch(k_gather_up<T, MX, GATED>, dim3(blocks, a.B), dim3(256), st, tr,
+                  static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
+                  static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count,
+                  a.max_count, a.f, C, a.h, a.h_stride);
 }
 
 template <class T, bool GATED>
-hipError_t up_gated(const FfnArgs &a, int C, hipStream_t st)
+hipError_t up_gated(const FfnArgs &a, int C, hipStream_t st, Trace *tr)
 {
     const int mx = (C + 255) / 256;
-    if (mx <= 1) return up_launch<T, 1, GATED>(a, C, st);
-    if (mx <= 2) return up_launch<T, 2, GATED>(a, C, st);
-    if (mx <= 4) return up_launch<T, 4, GATED>(a, C, st);
-    if (mx <= 6) return up_launch<T, 6, GATED>(a, C, st);
-    if (mx <= 8) return up_launch<T, 8, GATED>(a, C, st);
-    if (mx <= 12) return up_launch<T, 12, GATED>(a, C, st);
-    if (mx <= 16) return up_launch<T, 16, GATED>(a, C, st);
+    if (mx <= 1) return up_launch<T, 1, GATED>(a, C, st, tr);
+    if (mx <= 2) return up_launch<T, 2, GATED>(a, C, st, tr);
+    if (mx <= 4) return up_launch<T, 4, GATED>(a, C, st, tr);
+    if (mx <= 6) return up_launch<T, 6, GATED>(a, C, st, tr);
+    if (mx <= 8) return up_launch<T, 8, GATED>(a, C, st, tr);
+    if (mx <= 12) return up_launch<T, 12, GATED>(a, C, st, tr);
+    if (mx <= 16) return up_launch<T, 16, GATED>(a, C, st, tr);
     return hipErrorInvalidValue;
 }
 
@@ -266,27 +264,17 @@ template <class T>
 hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / T::E;
-    hipError_t e = a.act == 1 ? up_gated<T, true>(a, C, st) : up_gated<T, false>(a, C, st);
+    hipError_t e = a.act == 1 ? up_gated<T, true>(a, C, st, tr) : up_gated<T, false>(a, C, st, tr);
     if (e != hipSuccess)
         return e;
-    if (tr)
-        tr->mark(st);
     const int nchunk = ffn_num_chunks(a.d, a.dtype, a.max_count);
-    dim3 grid(ffn_num_slices(a.d, a.dtype), nchunk, a.B);
-    k_gather_down<T><<<grid, 256, 0, st>>>(static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride,
-                                           a.idx, a.idx_stride, a.count, a.max_count, a.f, C,
-                                           nchunk, a.partials);
-    e = hipGetLastError();
+    e = launch(k_gather_down<T>, dim3(ffn_num_slices(a.d, a.dtype), nchunk, a.B), dim3(256), st,
+               tr, static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride, a.idx, a.idx_stride, a.count,
+               a.max_count, a.f, C, nchunk, a.partials);
     if (e != hipSuccess)
         return e;
-    if (tr)
-        tr->mark(st);
-    dim3 rgrid((a.d + 255) / 256, a.B);
-    k_reduce_partials<<<rgrid, 256, 0, st>>>(a.partials, nchunk, a.d, a.y);
-    e = hipGetLastError();
-    if (tr)
-        tr->mark(st);
-    return e;
+    return launch(k_reduce_partials, dim3((a.d + 255) / 256, a.B), dim3(256), st, tr, a.partials,
+                  nchunk, a.d, a.y);
 }
 
 }  // namespace

@@ -5,23 +5,42 @@
 // launch status.  Sizes are in elements unless named *_chunks (16-byte units).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace csf {
 
-// Optional profiling marks: when set, mark() records the next caller-owned event on the stream.
+// Optional per-kernel timing: while set, each launch takes the next two caller-owned events and
+// has the runtime record them at the kernel's start and end (hipExtLaunchKernel), so their
+// difference is the kernel's own duration.
 struct Trace {
     hipEvent_t *ev = nullptr;
     int n = 0;
     int pos = 0;
-    void mark(hipStream_t st)
+    bool next(hipEvent_t *start, hipEvent_t *stop)
     {
-        if (ev && pos < n)
-            (void)hipEventRecord(ev[pos++], st);
+        if (!ev || pos + 1 >= n)
+            return false;
+        *start = ev[pos];
+        *stop = ev[pos + 1];
+        pos += 2;
+        return true;
     }
 };
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                         Trace *tr, Args... args)
+{
+    hipEvent_t start, stop;
+    if (tr && tr->next(&start, &stop))
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, start, stop, 0, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, 0, st>>>(static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
 
 // ---- predictor (predict.hip) ----------------------------------------------------------------
 // Split-K factor of the predictor's down projection (rows of V split over S workgroups).
@@ -29,18 +48,18 @@ constexpr int kMaxPredSplit = 4;
 int pred_split(int r, int d, int dtype);
 // part[S][B][r] = split-K partial sums of V x_t (float32), S = pred_split(r, d, dtype).
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *part, hipStream_t stream);
+                            float *part, hipStream_t stream, Trace *trace = nullptr);
 // s[B][f] = sigmoid(U relu(sum of the partials)) in float32.
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
-                          float *s, hipStream_t stream);
+                          float *s, hipStream_t stream, Trace *trace = nullptr);
 
 // ---- selection (select.hip) -----------------------------------------------------------------
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap,
-                              hipStream_t stream);
+                              hipStream_t stream, Trace *trace = nullptr);
 hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
-                                   hipStream_t stream);
+                                   hipStream_t stream, Trace *trace = nullptr);
 int select_max_f();   // largest f the selection kernels accept
 
 // ---- FFN (ffn.hip) --------------------------------------------------------------------------

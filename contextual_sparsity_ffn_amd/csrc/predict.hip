@@ -148,43 +148,39 @@ struct DownArgs {
 };
 
 template <class T, int MX>
-hipError_t down_mx(const DownArgs &g, hipStream_t st)
+hipError_t down_mx(const DownArgs &g, hipStream_t st, Trace *tr)
 {
+    const u32x4 *V = static_cast<const u32x4 *>(g.V), *x = static_cast<const u32x4 *>(g.x);
     if (g.B == 1)
-        k_pred_down<T, MX, 1><<<g.r * g.S, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
-                                                         static_cast<const u32x4 *>(g.x), g.C, g.r,
-                                                         g.B, g.S, g.a);
-    else
-        k_pred_down<T, MX, 8><<<g.r * g.S, 256, 0, st>>>(static_cast<const u32x4 *>(g.V),
-                                                         static_cast<const u32x4 *>(g.x), g.C, g.r,
-                                                         g.B, g.S, g.a);
-    return hipGetLastError();
+        return launch(k_pred_down<T, MX, 1>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r,
+                      g.B, g.S, g.a);
+    return launch(k_pred_down<T, MX, 8>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r, g.B,
+                  g.S, g.a);
 }
 
 template <class T>
-hipError_t down_t(const DownArgs &g, hipStream_t st)
+hipError_t down_t(const DownArgs &g, hipStream_t st, Trace *tr)
 {
     const int mx = ((g.C + g.S - 1) / g.S + 255) / 256;
-    if (mx <= 1) return down_mx<T, 1>(g, st);
-    if (mx <= 2) return down_mx<T, 2>(g, st);
-    if (mx <= 4) return down_mx<T, 4>(g, st);
-    if (mx <= 6) return down_mx<T, 6>(g, st);
-    if (mx <= 8) return down_mx<T, 8>(g, st);
-    if (mx <= 12) return down_mx<T, 12>(g, st);
-    if (mx <= 16) return down_mx<T, 16>(g, st);
+    if (mx <= 1) return down_mx<T, 1>(g, st, tr);
+    if (mx <= 2) return down_mx<T, 2>(g, st, tr);
+    if (mx <= 4) return down_mx<T, 4>(g, st, tr);
+    if (mx <= 6) return down_mx<T, 6>(g, st, tr);
+    if (mx <= 8) return down_mx<T, 8>(g, st, tr);
+    if (mx <= 12) return down_mx<T, 12>(g, st, tr);
+    if (mx <= 16) return down_mx<T, 16>(g, st, tr);
     return hipErrorInvalidValue;
 }
 
 template <class T, int LPR, int MM, int RW>
 hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                     hipStream_t st)
+                     hipStream_t st, Trace *tr)
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
     const int blocks = (waves + 3) / 4;
-    k_pred_up<T, LPR, MM, RW><<<blocks, 256, 0, st>>>(static_cast<const u32x4 *>(U), a, C, r, f,
-                                                       B, S, s);
-    return hipGetLastError();
+    return launch(k_pred_up<T, LPR, MM, RW>, dim3(blocks), dim3(256), st, tr,
+                  static_cast<const u32x4 *>(U), a, C, r, f, B, S, s);
 }
 
 // Rows per lane group: up to 4, so that each wavefront's read of the hidden activation (S partial
@@ -192,27 +188,27 @@ hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, 
 // every CU several workgroups.
 template <class T, int LPR, int MM>
 hipError_t up_rw(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                 hipStream_t st)
+                 hipStream_t st, Trace *tr)
 {
     constexpr int G = kWave / LPR;
     int rw = 4;
     while (rw > 1 && (long)f / (rw * G) < 4096)   // keep >= 1024 workgroups when f allows
         rw /= 2;
-    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st);
-    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, S, r, C, U, f, s, st);
-    return up_launch<T, LPR, MM, 1>(a, B, S, r, C, U, f, s, st);
+    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st, tr);
+    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, S, r, C, U, f, s, st, tr);
+    return up_launch<T, LPR, MM, 1>(a, B, S, r, C, U, f, s, st, tr);
 }
 
 template <class T>
 hipError_t up_t(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                hipStream_t st)
+                hipStream_t st, Trace *tr)
 {
-    if (C <= 16) return up_rw<T, 16, 1>(a, B, S, r, C, U, f, s, st);
-    if (C <= 32) return up_rw<T, 32, 1>(a, B, S, r, C, U, f, s, st);
-    if (C <= 64) return up_rw<T, 64, 1>(a, B, S, r, C, U, f, s, st);
-    if (C <= 128) return up_rw<T, 64, 2>(a, B, S, r, C, U, f, s, st);
-    if (C <= 256) return up_rw<T, 64, 4>(a, B, S, r, C, U, f, s, st);
-    if (C <= 512) return up_rw<T, 64, 8>(a, B, S, r, C, U, f, s, st);
+    if (C <= 16) return up_rw<T, 16, 1>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 32) return up_rw<T, 32, 1>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 64) return up_rw<T, 64, 1>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 128) return up_rw<T, 64, 2>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 256) return up_rw<T, 64, 4>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 512) return up_rw<T, 64, 8>(a, B, S, r, C, U, f, s, st, tr);
     return hipErrorInvalidValue;
 }
 
@@ -233,21 +229,21 @@ int pred_split(int r, int d, int dtype)
 }
 
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *a, hipStream_t st)
+                            float *a, hipStream_t st, Trace *tr)
 {
     DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a};
-    if (dtype == 0) return down_t<F32T>(g, st);
-    if (dtype == 1) return down_t<F16T>(g, st);
-    return down_t<BF16T>(g, st);
+    if (dtype == 0) return down_t<F32T>(g, st, tr);
+    if (dtype == 1) return down_t<F16T>(g, st, tr);
+    return down_t<BF16T>(g, st, tr);
 }
 
 hipError_t launch_pred_up(int dtype, const float *a, int B, int d, int r, const void *U, int f,
-                          float *s, hipStream_t st)
+                          float *s, hipStream_t st, Trace *tr)
 {
     const int S = pred_split(r, d, dtype);
-    if (dtype == 0) return up_t<F32T>(a, B, S, r, r / 4, U, f, s, st);
-    if (dtype == 1) return up_t<F16T>(a, B, S, r, r / 8, U, f, s, st);
-    return up_t<BF16T>(a, B, S, r, r / 8, U, f, s, st);
+    if (dtype == 0) return up_t<F32T>(a, B, S, r, r / 4, U, f, s, st, tr);
+    if (dtype == 1) return up_t<F16T>(a, B, S, r, r / 8, U, f, s, st, tr);
+    return up_t<BF16T>(a, B, S, r, r / 8, U, f, s, st, tr);
 }
 
 }  // namespace csf

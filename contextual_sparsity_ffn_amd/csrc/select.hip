@@ -340,28 +340,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select_threshold(
 
 template <int J>
 hipError_t topk_j(const float *scores, int B, int f, int k, int32_t *idx, int idx_stride,
-                  int32_t *count, uint32_t *bitmap, hipStream_t st)
+                  int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr)
 {
     if (f % 4 == 0)
-        k_select_topk<kScoreBuckets, J, true><<<B, kSelThreads, 0, st>>>(scores, f, k, idx,
-                                                                         idx_stride, count, bitmap);
-    else
-        k_select_topk<kScoreBuckets, J, false><<<B, kSelThreads, 0, st>>>(scores, f, k, idx,
-                                                                          idx_stride, count, bitmap);
-    return hipGetLastError();
+        return launch(k_select_topk<kScoreBuckets, J, true>, dim3(B), dim3(kSelThreads), st, tr,
+                      scores, f, k, idx, idx_stride, count, bitmap);
+    return launch(k_select_topk<kScoreBuckets, J, false>, dim3(B), dim3(kSelThreads), st, tr,
+                  scores, f, k, idx, idx_stride, count, bitmap);
 }
 
 template <int J>
 hipError_t threshold_j(const float *scores, int B, int f, float tau, int32_t *idx, int idx_stride,
-                       int32_t *count, uint32_t *bitmap, hipStream_t st)
+                       int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr)
 {
     if (f % 4 == 0)
-        k_select_threshold<J, true><<<B, kSelThreads, 0, st>>>(scores, f, tau, idx, idx_stride,
-                                                               count, bitmap);
-    else
-        k_select_threshold<J, false><<<B, kSelThreads, 0, st>>>(scores, f, tau, idx, idx_stride,
-                                                                count, bitmap);
-    return hipGetLastError();
+        return launch(k_select_threshold<J, true>, dim3(B), dim3(kSelThreads), st, tr, scores, f,
+                      tau, idx, idx_stride, count, bitmap);
+    return launch(k_select_threshold<J, false>, dim3(B), dim3(kSelThreads), st, tr, scores, f,
+                  tau, idx, idx_stride, count, bitmap);
 }
 
 }  // namespace
@@ -369,29 +365,30 @@ hipError_t threshold_j(const float *scores, int B, int f, float tau, int32_t *id
 int select_max_f() { return 32 * kMaxWords; }
 
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
-                              int idx_stride, int32_t *count, uint32_t *bitmap, hipStream_t st)
+                              int idx_stride, int32_t *count, uint32_t *bitmap, hipStream_t st,
+                              Trace *tr)
 {
     const int J = (f + kQuad - 1) / kQuad;     // sweeps of 4096 scores
-    if (J <= 1) return topk_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
-    if (J <= 2) return topk_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
-    if (J <= 4) return topk_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
-    if (J <= 8) return topk_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
-    if (J <= 12) return topk_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
-    if (J <= 16) return topk_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, st);
+    if (J <= 1) return topk_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 2) return topk_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 4) return topk_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 8) return topk_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 12) return topk_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 16) return topk_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
-                                   hipStream_t st)
+                                   hipStream_t st, Trace *tr)
 {
     const int J = (f + kQuad - 1) / kQuad;
-    if (J <= 1) return threshold_j<1>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
-    if (J <= 2) return threshold_j<2>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
-    if (J <= 4) return threshold_j<4>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
-    if (J <= 8) return threshold_j<8>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
-    if (J <= 12) return threshold_j<12>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
-    if (J <= 16) return threshold_j<16>(scores, B, f, tau, idx, idx_stride, count, bitmap, st);
+    if (J <= 1) return threshold_j<1>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 2) return threshold_j<2>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 4) return threshold_j<4>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 8) return threshold_j<8>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 12) return threshold_j<12>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 16) return threshold_j<16>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
     return hipErrorInvalidValue;
 }
 

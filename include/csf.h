@@ -190,12 +190,14 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
                          void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * csf_set_trace_events -- profiling hook for csf_sparse_ffn_layer (per calling thread).
- * While n >= 7 events are set, each csf_sparse_ffn_layer call records, on its stream,
- * events[0] before its first kernel and events[i] after its i-th kernel: 1 predictor
- * down-projection, 2 predictor up-projection, 3 selection, 4 gathered up/gate rows, 5 gathered
- * down rows (partial sums), 6 reduction of the partial sums.  Differences of consecutive events time each kernel.  The events are
- * hipEvent_t handles (as void*) created and owned by the caller; n = 0 switches tracing off.
+ * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer (per calling thread).
+ * While n > 0 events are set, the i-th kernel a csf_sparse_ffn_layer call launches has the HIP
+ * runtime record events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
+ * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
+ * order: predictor down-projection, predictor up-projection, selection, gathered up/gate rows,
+ * gathered down rows (partial sums), reduction of the partial sums -- 12 events cover them all.
+ * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
+ * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */
 int csf_set_trace_events(void *const *events, int n);
 
