@@ -18,14 +18,19 @@ LIB_PATH = os.path.join(_HERE, "libcsf.so")
 
 F32, F16, BF16 = 0, 1, 2
 RELU, REGLU = 0, 1
-OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER = range(6)
+OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
+    OP_BATCHED_UNION = range(7)
+SEM_PER_TOKEN, SEM_UNION = 0, 1
+PATH_AUTO, PATH_GATHER, PATH_MFMA = 0, 1, 2
+MAX_UNION_BATCH = 32
 
 _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
            3: "CSF_ERR_MISALIGNED", 4: "CSF_ERR_WORKSPACE_TOO_SMALL", 5: "CSF_ERR_HIP"}
 
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
            "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
-           "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_set_trace_events")
+           "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_batched_union",
+           "csf_set_trace_events")
 
 
 class CsfError(RuntimeError):
@@ -58,6 +63,8 @@ def _load():
     L.csf_set_trace_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
                                        flt, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn_batched_union.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                               i32, i32, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
     for name in EXPORTS[4:]:
         getattr(L, name).restype = i32
     return L
@@ -302,3 +309,31 @@ def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=No
                                     float(tau if tau is not None else 0.0), _ptr(y), _ptr(scores),
                                     _ptr(idx), _ptr(count), _ptr(w), wb, _stream(dev)))
     return y
+
+
+def sparse_ffn_batched_union(X, W1, b1, Wup, W2T, bitmaps, act=RELU, semantics=SEM_PER_TOKEN,
+                             path=PATH_AUTO, Y=None, union_count=None, ws=None):
+    """Sparse FFN of the B tokens X [B, d] reading the union of their sets once.
+
+    bitmaps [B, ceil(f/32)] int32 (the bit patterns of csf_select_*'s bitmap output).  Returns
+    (Y [B, d] float32, path taken: PATH_GATHER or PATH_MFMA); union_count ([1] int32, optional)
+    receives the union size on the device."""
+    _tensor(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be [B, d]")
+    dev, dt, f, d = _ffn_weights(X, W1, b1, Wup, W2T, act)
+    B = X.shape[0]
+    _tensor(X, "X", shape=(B, d))
+    _tensor(bitmaps, "bitmaps", dtype=torch.int32, shape=(B, (f + 31) // 32), device=dev)
+    if Y is None:
+        Y = torch.empty(B, d, dtype=torch.float32, device=dev)
+    _tensor(Y, "Y", dtype=torch.float32, shape=(B, d), device=dev)
+    _tensor(union_count, "union_count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    code = dtype_code(dt)
+    w, wb = _workspace(workspace_size(OP_BATCHED_UNION, B, d, f, 0, 0, code), dev, ws)
+    taken = ctypes.c_int(0)
+    _check(lib.csf_sparse_ffn_batched_union(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1),
+                                            _ptr(Wup), _ptr(W2T), _ptr(bitmaps), int(semantics),
+                                            int(path), _ptr(Y), _ptr(union_count),
+                                            ctypes.byref(taken), _ptr(w), wb, _stream(dev)))
+    return Y, taken.value

@@ -142,6 +142,34 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
     return w;
 }
 
+// Batches of at least this many tokens take the matrix-core path when it applies (the gather
+// path's vector ALU work grows with B per weight byte; the matrix cores' does not bind).
+constexpr int kMfmaMinBatch = 4;
+
+struct UnionWs {
+    size_t ulist, ucount, h, hlo, partials, total;
+};
+UnionWs union_ws(int B, int d, int f, int dtype)
+{
+    UnionWs w;
+    const size_t hs = csf::union_h_stride(f);
+    const size_t Bn = B > 0 ? (size_t)B : 1;
+    w.ulist = 0;
+    w.ucount = round_up((size_t)f * sizeof(int32_t));
+    w.h = w.ucount + kAlign;
+    // float32 h (gather path) or hi and lo 16-bit halves (matrix-core path) share this region
+    w.hlo = w.h + round_up(Bn * hs * sizeof(uint16_t));
+    const size_t h32_end = w.h + round_up(Bn * hs * sizeof(float));
+    const size_t hlo_end = w.hlo + round_up(Bn * hs * sizeof(uint16_t));
+    w.partials = h32_end > hlo_end ? h32_end : hlo_end;
+    int nch = csf::union_num_chunks(0, d, dtype, f);
+    const int nm = csf::union_num_chunks(1, d, dtype, f);
+    if (nm > nch)
+        nch = nm;
+    w.total = w.partials + round_up(Bn * (size_t)nch * d * sizeof(float));
+    return w;
+}
+
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 int check_ws(void *ws, size_t ws_bytes, size_t need)
@@ -231,6 +259,8 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
         return ffn_ws(B, d, dtype, f).total;
     case CSF_OP_LAYER:
         return r > 0 ? layer_ws(d, f, r, max_count, dtype).total : 0;
+    case CSF_OP_BATCHED_UNION:
+        return union_ws(B, d, f, dtype).total;
     default:
         return 0;
     }
@@ -377,6 +407,74 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     a.y = Y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "dense FFN launch");
+}
+
+int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, int dtype,
+                                 const void *W1, const float *b1, const void *Wup,
+                                 const void *W2T, const uint32_t *bitmaps, int semantics,
+                                 int path, float *Y, int32_t *union_count, int *path_taken,
+                                 void *ws, size_t ws_bytes, void *stream)
+{
+    int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    REQUIRE(B <= csf::kMaxUnionBatch, CSF_ERR_UNSUPPORTED,
+            "B = %d exceeds this build's limit of %d tokens per batched call", B,
+            csf::kMaxUnionBatch);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(semantics == CSF_SEM_PER_TOKEN || semantics == CSF_SEM_UNION, CSF_ERR_INVALID_ARG,
+            "unknown semantics %d", semantics);
+    REQUIRE(path == CSF_PATH_AUTO || path == CSF_PATH_GATHER || path == CSF_PATH_MFMA,
+            CSF_ERR_INVALID_ARG, "unknown path %d", path);
+    CHECK_PTR(bitmaps, B > 0);
+    CHECK_PTR(Y, B > 0);
+    CHECK_PTR(union_count, false);
+    const bool mfma_ok = csf::union_mfma_supported(dtype, d, B > 0 ? B : 1);
+    REQUIRE(path != CSF_PATH_MFMA || mfma_ok, CSF_ERR_UNSUPPORTED,
+            "the matrix-core path needs a 16-bit dtype and d %% 256 == 0 (dtype %d, d = %d)", dtype,
+            d);
+    const bool mfma = path == CSF_PATH_MFMA || (path == CSF_PATH_AUTO && mfma_ok && B >= kMfmaMinBatch);
+    if (B == 0) {
+        if (path_taken)
+            *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
+        return ok();
+    }
+    UnionWs w = union_ws(B, d, f, dtype);
+    CHECK_WS(ws, ws_bytes, w.total);
+    csf::UnionArgs a;
+    a.dtype = dtype;
+    a.act = act;
+    a.per_token = semantics == CSF_SEM_PER_TOKEN;
+    a.mfma = mfma;
+    a.X = X;
+    a.B = B;
+    a.d = d;
+    a.f = f;
+    a.W1 = W1;
+    a.Wup = Wup;
+    a.W2T = W2T;
+    a.b1 = b1;
+    a.bitmaps = bitmaps;
+    a.Y = Y;
+    a.ucount_out = union_count;
+    a.ulist = reinterpret_cast<int32_t *>(at(ws, w.ulist));
+    a.ucount = reinterpret_cast<int32_t *>(at(ws, w.ucount));
+    a.h32 = reinterpret_cast<float *>(at(ws, w.h));
+    a.hhi = reinterpret_cast<uint16_t *>(at(ws, w.h));
+    a.hlo = reinterpret_cast<uint16_t *>(at(ws, w.hlo));
+    a.hs = (int)csf::union_h_stride(f);
+    a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    csf::Trace tr;
+    if (g_trace_n > 0) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    s = hip_status(csf::launch_union_ffn(a, st, tr.ev ? &tr : nullptr), "batched union FFN launch");
+    if (s == CSF_OK && path_taken)
+        *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
+    return s;
 }
 
 int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,

@@ -15,6 +15,9 @@ namespace csf {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -74,6 +77,21 @@ struct F16T {
         p = as_f16x2(w.z); o[4] = (float)p.x; o[5] = (float)p.y;
         p = as_f16x2(w.w); o[6] = (float)p.x; o[7] = (float)p.y;
     }
+    // D += A B on one 16x16x32 matrix-core tile; A and B hold 8 binary16 values per lane
+    __device__ static __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    // round to nearest even (the conversion instruction's default mode)
+    __device__ static __forceinline__ uint16_t round_bits(float v)
+    {
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+    __device__ static __forceinline__ float widen_bits(uint16_t b)
+    {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
 };
 
 struct BF16T {
@@ -94,6 +112,18 @@ struct BF16T {
         o[4] = u2f(w.z << 16); o[5] = u2f(w.z & 0xffff0000u);
         o[6] = u2f(w.w << 16); o[7] = u2f(w.w & 0xffff0000u);
     }
+    __device__ static __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // round to nearest even on the bit pattern (finite inputs)
+    __device__ static __forceinline__ uint16_t round_bits(float v)
+    {
+        const uint32_t u = __float_as_uint(v);
+        return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    __device__ static __forceinline__ float widen_bits(uint16_t b) { return u2f((uint32_t)b << 16); }
 };
 
 // Sum over the 64 lanes of a wavefront; every lane receives the total.  The butterfly order is

@@ -273,8 +273,7 @@ hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
                a.max_count, a.f, C, nchunk, a.partials);
     if (e != hipSuccess)
         return e;
-    return launch(k_reduce_partials, dim3((a.d + 255) / 256, a.B), dim3(256), st, tr, a.partials,
-                  nchunk, a.d, a.y);
+    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.y, st, tr);
 }
 
 }  // namespace
@@ -300,6 +299,14 @@ int ffn_num_chunks(int d, int dtype, int max_count)
     if (want < 1)
         want = 1;
     return want;
+}
+
+hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, float *y,
+                                  hipStream_t st, Trace *tr)
+{
+    if (nchunk < 1 || nchunk > kMaxChunks)
+        return hipErrorInvalidValue;
+    return launch(k_reduce_partials, dim3((D + 255) / 256, B), dim3(256), st, tr, part, nchunk, D, y);
 }
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t st, Trace *tr)

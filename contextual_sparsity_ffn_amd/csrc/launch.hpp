@@ -82,5 +82,34 @@ struct FfnArgs {
 int ffn_num_slices(int d, int dtype);
 int ffn_num_chunks(int d, int dtype, int max_count);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
+// y[t][col] = sum over chunks q, in order, of part[t][q][col] (part is [B][nchunk][D] float32).
+hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, float *y,
+                                  hipStream_t stream, Trace *trace = nullptr);
+
+// ---- batched FFN over the union of the tokens' sets (union.hip) -------------------------------
+constexpr int kMaxUnionBatch = 32;   // tokens per call (two 16-token matrix-core tiles)
+struct UnionArgs {
+    int dtype, act;
+    int per_token;          // 1: token t keeps only its own rows; 0: every union row for all
+    int mfma;               // 1: matrix-core path (16-bit types, d % 256 == 0); 0: vector ALU
+    const void *X;          // [B][d]
+    int B, d, f;
+    const void *W1, *Wup, *W2T;
+    const float *b1;        // may be null
+    const uint32_t *bitmaps;  // [B][ceil(f / 32)]
+    float *Y;               // [B][d]
+    int32_t *ucount_out;    // optional device copy of the union size
+    // workspace
+    int32_t *ulist;         // [f]
+    int32_t *ucount;        // [1]
+    float *h32;             // [B][hs] (vector ALU path)
+    uint16_t *hhi, *hlo;    // [B][hs] each (matrix-core path)
+    int hs;                 // union_h_stride(f)
+    float *partials;        // [B][union_num_chunks][d]
+};
+bool union_mfma_supported(int dtype, int d, int B);
+int union_num_chunks(int mfma, int d, int dtype, int f);
+size_t union_h_stride(int f);
+hipError_t launch_union_ffn(const UnionArgs &a, hipStream_t stream, Trace *trace = nullptr);
 
 }  // namespace csf

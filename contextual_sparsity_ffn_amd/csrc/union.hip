@@ -1,0 +1,616 @@
+// union.hip -- the batched sparse FFN over the union of the tokens' active sets, on gfx950.
+//
+// [CP] "Contextual Sparsity and Activation Predictors", section "When it breaks": the tokens of a
+// batch have different active sets, so a batched layer has to read the union of them.
+// [DV] "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm", section
+// "Kernel-Level Implementation": each token keeps its own index list; section "Implications for
+// System Design": sparse batching has a crossover batch size.
+//
+// Semantics.  Every row of the union is read from HBM once per call and applied to all B tokens.
+// Per token (the default), token t keeps only its own neurons: h[t][n] is forced to 0 for a union
+// row that t did not select, so y_t is the sparse FFN of x_t over its own set.  Union semantics
+// apply every union row to every token.
+//
+// Kernels (all loops over the union are grid-stride loops that read the union size from device
+// memory, so nothing is sized from data the host does not have):
+//   k_union_list     one workgroup: OR of the B bitmaps, ascending union list and its size;
+//   gather path (vector ALU, for few tokens):
+//     k_union_up_valu    rows of the union in registers, one dot product per token; h in float32;
+//     k_union_down_valu  d-slices x union chunks x token groups, B accumulators per column;
+//   matrix-core path (MFMA 16x16x32, tokens padded to 16 or 32 as M):
+//     k_union_up_mfma    tile of 16 union rows: M = tokens, N = rows, K = d split over 4 waves;
+//                        h stored as a hi/lo pair of 16-bit values (hi = round(h),
+//                        lo = round(h - hi)), so the down product keeps about 22 bits of h;
+//     k_union_down_mfma  tile of 256 output columns x a chunk of the union: the rows of W2T are
+//                        staged through LDS and read back column-wise, because W2T is contiguous
+//                        along the output columns while the product contracts over rows;
+//   both paths end in the ordered partial-row reduction of the single-token FFN.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csf {
+
+namespace {
+
+constexpr int kUnionThreads = 1024;
+constexpr int kTileRows = 16;        // union rows per MFMA up tile (the N of the 16x16x32 shape)
+constexpr int kKStep = 32;           // K of one MFMA: 32 elements = 4 16-byte chunks
+constexpr int kDownCols = 256;       // output columns per MFMA down workgroup (512 bytes of a row)
+constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 bytes (8-byte aligned,
+                                     // rows 8 apart fall 16 banks apart)
+constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
+
+// Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
+template <int MX, bool GATED>
+struct UpRows {
+    static constexpr int loads = MX * (GATED ? 2 : 1);
+    static constexpr int value = loads >= 12 ? 1 : (loads >= 6 ? 2 : 4);
+};
+
+__device__ __forceinline__ int union_size(const int32_t *ucount, int f)
+{
+    const int u = *ucount;
+    return u < 0 ? 0 : (u > f ? f : u);
+}
+
+__device__ __forceinline__ bool token_has(const uint32_t *bitmaps, int words, int t, int j)
+{
+    return (bitmaps[(size_t)t * words + (j >> 5)] >> (j & 31)) & 1u;
+}
+
+// ---- union list --------------------------------------------------------------------------------
+__global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__restrict__ bitmaps,
+                                                              int B, int f,
+                                                              int32_t *__restrict__ ulist,
+                                                              int32_t *__restrict__ ucount,
+                                                              int32_t *__restrict__ ucount_out)
+{
+    __shared__ uint32_t scan_tmp[kUnionThreads / kWave];
+    const int t = threadIdx.x;
+    const int words = (f + 31) / 32;
+    const int wpt = (words + kUnionThreads - 1) / kUnionThreads;   // 1 or 2 (f <= 65536)
+    uint32_t orw[2] = {0u, 0u};
+    uint32_t n = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int w = t * wpt + q;
+        if (q < wpt && w < words) {
+            uint32_t o = 0u;
+            for (int b = 0; b < B; ++b)
+                o |= bitmaps[(size_t)b * words + w];
+            if (w == words - 1 && (f & 31))
+                o &= (1u << (f & 31)) - 1u;          // bits past f are not neurons
+            orw[q] = o;
+            n += __popc(o);
+        }
+    }
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kUnionThreads / kWave>(n, scan_tmp, &total);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t bits = orw[q];
+        const int w = t * wpt + q;
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            ulist[pos++] = w * 32 + b;
+        }
+    }
+    if (t == 0) {
+        *ucount = (int32_t)total;
+        if (ucount_out)
+            *ucount_out = (int32_t)total;
+    }
+}
+
+// ---- gather path -------------------------------------------------------------------------------
+// Workgroup of 256 threads per RPW union rows (grid-stride): the rows' chunks stay in registers
+// and each token's x is streamed past them (x is small and cache-resident).  Wave partial sums go
+// to LDS; after one barrier threads (token, row) finish h in a fixed order.
+template <class T, int MX, bool GATED, int RPW>
+__global__ __launch_bounds__(256) void k_union_up_valu(const u32x4 *__restrict__ X,
+                                                       const u32x4 *__restrict__ W1,
+                                                       const u32x4 *__restrict__ Wup,
+                                                       const float *__restrict__ b1,
+                                                       const int32_t *__restrict__ ulist,
+                                                       const int32_t *__restrict__ ucount,
+                                                       const uint32_t *__restrict__ bitmaps,
+                                                       int per_token, int B, int f, int C,
+                                                       float *__restrict__ h, int hs)
+{
+    constexpr int NV = GATED ? 2 : 1;
+    __shared__ float red[4][kMaxUnionBatch][RPW][NV];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int u = union_size(ucount, f);
+    const int words = (f + 31) / 32;
+
+    for (int n0 = blockIdx.x * RPW; n0 < u; n0 += gridDim.x * RPW) {
+        int jr[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+            jr[i] = n0 + i < u ? ulist[n0 + i] : -1;
+        u32x4 wv[RPW][MX];
+        u32x4 uv[GATED ? RPW : 1][GATED ? MX : 1];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const size_t rb = (size_t)(jr[i] < 0 ? 0 : jr[i]) * C;
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const int c = t + 256 * m;
+                const bool ok = jr[i] >= 0 && c < C;
+                wv[i][m] = ok ? ld_stream(W1 + rb + c) : u32x4{0u, 0u, 0u, 0u};
+                if constexpr (GATED)
+                    uv[i][m] = ok ? ld_stream(Wup + rb + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        for (int tok = 0; tok < B; ++tok) {
+            u32x4 xv[MX];
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const int c = t + 256 * m;
+                xv[m] = c < C ? X[(size_t)tok * C + c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int m = 0; m < MX; ++m)
+                    acc = T::dot(wv[i][m], xv[m], acc);
+                acc = wave_sum(acc);
+                if (lane == 0)
+                    red[w][tok][i][0] = acc;
+                if constexpr (GATED) {
+                    float au = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < MX; ++m)
+                        au = T::dot(uv[i][m], xv[m], au);
+                    au = wave_sum(au);
+                    if (lane == 0)
+                        red[w][tok][i][NV - 1] = au;
+                }
+            }
+        }
+        __syncthreads();
+        for (int e = t; e < B * RPW; e += 256) {
+            const int tok = e / RPW, i = e % RPW;
+            const int j = jr[i];
+            if (j < 0)
+                continue;
+            float p = (red[0][tok][i][0] + red[1][tok][i][0]) + (red[2][tok][i][0] + red[3][tok][i][0]);
+            if (b1)
+                p += b1[j];
+            float hv = p > 0.0f ? p : 0.0f;
+            if constexpr (GATED)
+                hv *= (red[0][tok][i][NV - 1] + red[1][tok][i][NV - 1]) +
+                      (red[2][tok][i][NV - 1] + red[3][tok][i][NV - 1]);
+            if (per_token && !token_has(bitmaps, words, tok, j))
+                hv = 0.0f;
+            h[(size_t)tok * hs + n0 + i] = hv;
+        }
+        __syncthreads();
+    }
+}
+
+// Grid (d-slice of 64 chunks, union chunk, token group of TB).  Each lane owns one 16-byte column
+// chunk of the slice and keeps TB x E float32 accumulators; the rows' h values are per token.
+template <class T, int TB, int UNR>
+__global__ __launch_bounds__(256) void k_union_down_valu(const u32x4 *__restrict__ W2T,
+                                                         const float *__restrict__ h, int hs,
+                                                         const int32_t *__restrict__ ulist,
+                                                         const int32_t *__restrict__ ucount,
+                                                         int B, int f, int C, int nchunk,
+                                                         float *__restrict__ part)
+{
+    constexpr int E = T::E;
+    __shared__ float red[3][TB][kWave * E];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int slice = blockIdx.x, chunk = blockIdx.y, tg = blockIdx.z * TB;
+    const int D = C * E;
+    const int c = slice * kWave + lane;
+    const int u = union_size(ucount, f);
+    const int per = (u + nchunk - 1) / nchunk;
+    const int nb = chunk * per;
+    const int ne = nb + per < u ? nb + per : u;
+
+    float acc[TB][E];
+#pragma unroll
+    for (int q = 0; q < TB; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[q][e] = 0.0f;
+
+    for (int n = nb + w; n < ne; n += 4 * UNR) {
+        u32x4 wv[UNR];
+        float hv[UNR][TB];
+#pragma unroll
+        for (int r = 0; r < UNR; ++r) {
+            const int nn = n + 4 * r;
+            const bool ok = nn < ne;
+            const int j = ok ? ulist[nn] : 0;
+            wv[r] = (ok && c < C) ? ld_stream(W2T + (size_t)j * C + c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < TB; ++q)
+                hv[r][q] = (ok && tg + q < B) ? h[(size_t)(tg + q) * hs + nn] : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < UNR; ++r) {
+            float wf[E];
+            T::unpack(wv[r], wf);
+#pragma unroll
+            for (int q = 0; q < TB; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc[q][e] = fmaf(hv[r][q], wf[e], acc[q][e]);
+        }
+    }
+    if (w > 0) {
+#pragma unroll
+        for (int q = 0; q < TB; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                red[w - 1][q][lane * E + e] = acc[q][e];
+    }
+    __syncthreads();
+    if (w == 0 && c < C) {
+#pragma unroll
+        for (int q = 0; q < TB; ++q) {
+            if (tg + q >= B)
+                break;
+            float *out = part + ((size_t)(tg + q) * nchunk + chunk) * (size_t)D + (size_t)c * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                out[e] = ((acc[q][e] + red[0][q][lane * E + e]) + red[1][q][lane * E + e]) +
+                         red[2][q][lane * E + e];
+        }
+    }
+}
+
+// ---- matrix-core path --------------------------------------------------------------------------
+// One 16x16x32 MFMA: lane l holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
+// e < 8, and receives D[4 (l / 16) + i][l % 16], i < 4.  A = tokens x K, B = K x union rows.
+// The 4 waves of a workgroup take consecutive quarters of the K steps and are summed in wave
+// order through LDS.  MT = 16-token tiles (1 for B <= 16, 2 for B <= 32).
+template <class T, int MT, bool GATED>
+__global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__ X,
+                                                       const u32x4 *__restrict__ W1,
+                                                       const u32x4 *__restrict__ Wup,
+                                                       const float *__restrict__ b1,
+                                                       const int32_t *__restrict__ ulist,
+                                                       const int32_t *__restrict__ ucount,
+                                                       const uint32_t *__restrict__ bitmaps,
+                                                       int per_token, int B, int f, int C,
+                                                       uint16_t *__restrict__ hhi,
+                                                       uint16_t *__restrict__ hlo, int hs)
+{
+    constexpr int NV = GATED ? 2 : 1;
+    constexpr int UNR = 4;                       // K steps whose loads are in flight together
+    __shared__ float red[4][NV][MT * 4][kWave];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int ln = lane & 15, g = lane >> 4;
+    const int u = union_size(ucount, f);
+    const int upad = (u + kKStep - 1) / kKStep * kKStep;   // h is written (zeros) up to here
+    const int words = (f + 31) / 32;
+    const int steps = C / 4;                     // K steps of 32 elements (C = 16-byte chunks)
+    const int s0 = w * steps / 4, s1 = (w + 1) * steps / 4;
+
+    for (int n0 = blockIdx.x * kTileRows; n0 < upad; n0 += gridDim.x * kTileRows) {
+        const int n = n0 + ln;
+        const int j = n < u ? ulist[n] : -1;
+        const size_t rb = (size_t)(j < 0 ? 0 : j) * C;
+        const u32x4 *xr[MT];
+        bool xok[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int tok = 16 * m + ln;
+            xok[m] = tok < B;
+            xr[m] = X + (size_t)(xok[m] ? tok : 0) * C;
+        }
+        f32x4 acc[NV][MT];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[v][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        for (int s = s0; s < s1; s += UNR) {
+            u32x4 bw[NV][UNR], ax[MT][UNR];
+#pragma unroll
+            for (int q = 0; q < UNR; ++q) {
+                const int c = 4 * (s + q) + g;
+                const bool ok = s + q < s1;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const u32x4 *Wm = v == 0 ? W1 : Wup;
+                    bw[v][q] = (ok && j >= 0) ? ld_stream(Wm + rb + c) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    ax[m][q] = (ok && xok[m]) ? xr[m][c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int q = 0; q < UNR; ++q)
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[v][m] = T::mfma(ax[m][q], bw[v][q], acc[v][m]);
+        }
+
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    red[w][v][m * 4 + i][lane] = acc[v][m][i];
+        __syncthreads();
+        // thread e covers D element (m, i, lane) = e: token 16 m + 4 (lane / 16) + i, row lane % 16
+        for (int e = t; e < MT * 4 * kWave; e += 256) {
+            const int mi = e / kWave, l = e % kWave;
+            const int m = mi / 4, i = mi % 4;
+            const int tok = 16 * m + 4 * (l >> 4) + i;
+            const int nn = n0 + (l & 15);
+            if (tok >= B || nn >= upad)
+                continue;
+            float hv = 0.0f;
+            if (nn < u) {
+                const int jj = ulist[nn];
+                float p = (red[0][0][mi][l] + red[1][0][mi][l]) + (red[2][0][mi][l] + red[3][0][mi][l]);
+                if (b1)
+                    p += b1[jj];
+                hv = p > 0.0f ? p : 0.0f;
+                if constexpr (GATED)
+                    hv *= (red[0][NV - 1][mi][l] + red[1][NV - 1][mi][l]) +
+                          (red[2][NV - 1][mi][l] + red[3][NV - 1][mi][l]);
+                if (per_token && !token_has(bitmaps, words, tok, jj))
+                    hv = 0.0f;
+            }
+            const uint16_t hi = T::round_bits(hv);
+            const uint16_t lo = T::round_bits(hv - T::widen_bits(hi));
+            hhi[(size_t)tok * hs + nn] = hi;
+            hlo[(size_t)tok * hs + nn] = lo;
+        }
+        __syncthreads();
+    }
+}
+
+// Grid (256-column tile, union chunk).  Per K step of 32 union rows the workgroup stages the
+// rows' 512-byte column segments in LDS (double-buffered, the next step's global loads in flight
+// during this step's products); wave w then multiplies columns 64 w .. 64 w + 63 as 4 tiles of 16:
+// A = h (tokens x 32 rows, hi and lo), B = staged rows read column-wise.
+template <class T, int MT>
+__global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict__ W2T,
+                                                         const uint16_t *__restrict__ hhi,
+                                                         const uint16_t *__restrict__ hlo,
+                                                         int hs,
+                                                         const int32_t *__restrict__ ulist,
+                                                         const int32_t *__restrict__ ucount,
+                                                         int B, int f, int C, int nchunk,
+                                                         float *__restrict__ part)
+{
+    constexpr int SEG = kDownCols / 8;            // 16-byte chunks per staged row segment: 32
+    constexpr int LPR = 256 / kKStep;             // loads per thread per step: 32 rows x 32 / 256
+    __shared__ __align__(16) uint16_t tile[2][kKStep][kDownLdsStride];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int ln = lane & 15, g = lane >> 4;
+    const int D = C * 8;
+    const int col0 = blockIdx.x * kDownCols;
+    const int chunk = blockIdx.y;
+    const int u = union_size(ucount, f);
+    const int steps = (u + kKStep - 1) / kKStep;
+    const int per = (steps + nchunk - 1) / nchunk;
+    const int sb = chunk * per;
+    const int se = sb + per < steps ? sb + per : steps;
+
+    // thread t stages rows (t / SEG) + 8 q, q < LPR / ... : 256 threads cover 8 rows x 32 chunks
+    const int srow = t / SEG, scol = t % SEG;
+    auto load_step = [&](int s, u32x4 *r) {
+#pragma unroll
+        for (int q = 0; q < kKStep / 8; ++q) {
+            const int nn = s * kKStep + srow + 8 * q;
+            const int j = nn < u ? ulist[nn] : 0;
+            r[q] = nn < u ? ld_stream(W2T + (size_t)j * C + (col0 / 8) + scol)
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_step = [&](int buf, const u32x4 *r) {
+#pragma unroll
+        for (int q = 0; q < kKStep / 8; ++q) {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[buf][srow + 8 * q][scol * 8]);
+            // two 8-byte stores: the staged row stride is 8-byte aligned only
+            *reinterpret_cast<uint2 *>(dst) = uint2{r[q].x, r[q].y};
+            *reinterpret_cast<uint2 *>(dst + 2) = uint2{r[q].z, r[q].w};
+        }
+    };
+    (void)LPR;
+
+    f32x4 acc[4][MT];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[q][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    u32x4 nxt[kKStep / 8];
+    if (sb < se) {
+        load_step(sb, nxt);
+        store_step(0, nxt);
+    }
+    __syncthreads();
+    for (int s = sb; s < se; ++s) {
+        const int buf = (s - sb) & 1;
+        if (s + 1 < se)
+            load_step(s + 1, nxt);
+        // A operands: h[token][32 s + 8 g .. + 8], hi and lo
+        u32x4 ahi[MT], alo[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int tok = 16 * m + ln;
+            const size_t off = (size_t)(tok < B ? tok : 0) * hs + (size_t)s * kKStep + 8 * g;
+            ahi[m] = tok < B ? *reinterpret_cast<const u32x4 *>(hhi + off) : u32x4{0u, 0u, 0u, 0u};
+            alo[m] = tok < B ? *reinterpret_cast<const u32x4 *>(hlo + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cc = 64 * w + 16 * q + ln;
+            uint32_t bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bv[e] = (uint32_t)tile[buf][8 * g + 2 * e][cc] |
+                        ((uint32_t)tile[buf][8 * g + 2 * e + 1][cc] << 16);
+            const u32x4 b = u32x4{bv[0], bv[1], bv[2], bv[3]};
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                acc[q][m] = T::mfma(ahi[m], b, acc[q][m]);
+                acc[q][m] = T::mfma(alo[m], b, acc[q][m]);
+            }
+        }
+        if (s + 1 < se)
+            store_step(buf ^ 1, nxt);
+        __syncthreads();
+    }
+
+    // D[4 g + i][ln] of tile (q, m): token 16 m + 4 g + i, column col0 + 64 w + 16 q + ln
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int col = col0 + 64 * w + 16 * q + ln;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * m + 4 * g + i;
+                if (tok < B && col < D)
+                    part[((size_t)tok * nchunk + chunk) * (size_t)D + col] = acc[q][m][i];
+            }
+    }
+}
+
+// ---- dispatch ----------------------------------------------------------------------------------
+template <class T, int MX, bool GATED>
+hipError_t up_valu(const UnionArgs &a, int C, hipStream_t st, Trace *tr)
+{
+    constexpr int RPW = UpRows<MX, GATED>::value;
+    const int blocks = (a.f + RPW - 1) / RPW < 4096 ? (a.f + RPW - 1) / RPW : 4096;
+    return launch(k_union_up_valu<T, MX, GATED, RPW>, dim3(blocks), dim3(256), st, tr,
+                  static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
+                  static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
+                  a.per_token, a.B, a.f, C, a.h32, a.hs);
+}
+
+template <class T, bool GATED>
+hipError_t up_valu_mx(const UnionArgs &a, int C, hipStream_t st, Trace *tr)
+{
+    const int mx = (C + 255) / 256;
+    if (mx <= 1) return up_valu<T, 1, GATED>(a, C, st, tr);
+    if (mx <= 2) return up_valu<T, 2, GATED>(a, C, st, tr);
+    if (mx <= 4) return up_valu<T, 4, GATED>(a, C, st, tr);
+    if (mx <= 6) return up_valu<T, 6, GATED>(a, C, st, tr);
+    if (mx <= 8) return up_valu<T, 8, GATED>(a, C, st, tr);
+    if (mx <= 12) return up_valu<T, 12, GATED>(a, C, st, tr);
+    if (mx <= 16) return up_valu<T, 16, GATED>(a, C, st, tr);
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
+{
+    const int C = a.d / T::E;
+    hipError_t e = a.act == 1 ? up_valu_mx<T, true>(a, C, st, tr) : up_valu_mx<T, false>(a, C, st, tr);
+    if (e != hipSuccess)
+        return e;
+    const int nchunk = union_num_chunks(0, a.d, a.dtype, a.f);
+    const dim3 grid(ffn_num_slices(a.d, a.dtype), nchunk, (a.B + kValuTokens - 1) / kValuTokens);
+    if (a.B <= 1)
+        e = launch(k_union_down_valu<T, 1, 4>, grid, dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.W2T), a.h32, a.hs, a.ulist, a.ucount, a.B, a.f, C,
+                   nchunk, a.partials);
+    else if (a.B <= 4)
+        e = launch(k_union_down_valu<T, 4, 2>, grid, dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.W2T), a.h32, a.hs, a.ulist, a.ucount, a.B, a.f, C,
+                   nchunk, a.partials);
+    else
+        e = launch(k_union_down_valu<T, kValuTokens, 2>, grid, dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.W2T), a.h32, a.hs, a.ulist, a.ucount, a.B, a.f, C,
+                   nchunk, a.partials);
+    if (e != hipSuccess)
+        return e;
+    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.Y, st, tr);
+}
+
+template <class T, int MT>
+hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
+{
+    const int C = a.d / 8;
+    const int tiles = (a.f + kKStep - 1) / kKStep * (kKStep / kTileRows);
+    const int blocks = tiles < 4096 ? tiles : 4096;
+    hipError_t e;
+    if (a.act == 1)
+        e = launch(k_union_up_mfma<T, MT, true>, dim3(blocks), dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
+                   static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
+                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
+    else
+        e = launch(k_union_up_mfma<T, MT, false>, dim3(blocks), dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
+                   static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
+                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
+    if (e != hipSuccess)
+        return e;
+    const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f);
+    e = launch(k_union_down_mfma<T, MT>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
+               static_cast<const u32x4 *>(a.W2T), a.hhi, a.hlo, a.hs, a.ulist, a.ucount, a.B, a.f,
+               C, nchunk, a.partials);
+    if (e != hipSuccess)
+        return e;
+    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.Y, st, tr);
+}
+
+template <class T>
+hipError_t union_mfma(const UnionArgs &a, hipStream_t st, Trace *tr)
+{
+    if (a.B <= 16)
+        return union_mfma_mt<T, 1>(a, st, tr);
+    return union_mfma_mt<T, 2>(a, st, tr);
+}
+
+}  // namespace
+
+bool union_mfma_supported(int dtype, int d, int B)
+{
+    return dtype != 0 && d % kDownCols == 0 && B >= 1 && B <= kMaxUnionBatch;
+}
+
+int union_num_chunks(int mfma, int d, int dtype, int f)
+{
+    if (!mfma)
+        return ffn_num_chunks(d, dtype, f);
+    // about 512 workgroups of 256 columns; the partial rows (B x chunks x d float32) stay a few
+    // percent of the weight bytes
+    const int tiles = d / kDownCols > 0 ? d / kDownCols : 1;
+    int n = (512 + tiles - 1) / tiles;
+    const int steps = (f + kKStep - 1) / kKStep;
+    if (n > steps)
+        n = steps;
+    if (n > 64)
+        n = 64;
+    return n < 1 ? 1 : n;
+}
+
+size_t union_h_stride(int f) { return (size_t)(f + kKStep - 1) / kKStep * kKStep; }
+
+hipError_t launch_union_ffn(const UnionArgs &a, hipStream_t st, Trace *tr)
+{
+    hipError_t e = launch(k_union_list, dim3(1), dim3(kUnionThreads), st, tr, a.bitmaps, a.B, a.f,
+                          a.ulist, a.ucount, a.ucount_out);
+    if (e != hipSuccess)
+        return e;
+    if (a.mfma) {
+        if (a.dtype == 1) return union_mfma<F16T>(a, st, tr);
+        return union_mfma<BF16T>(a, st, tr);
+    }
+    if (a.dtype == 0) return union_valu<F32T>(a, st, tr);
+    if (a.dtype == 1) return union_valu<F16T>(a, st, tr);
+    return union_valu<BF16T>(a, st, tr);
+}
+
+}  // namespace csf

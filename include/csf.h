@@ -72,6 +72,19 @@ typedef enum {
     CSF_OP_BATCHED_UNION = 6
 } csf_op;
 
+/* Which rows each token of a batched call uses (csf_sparse_ffn_batched_union). */
+typedef enum {
+    CSF_SEM_PER_TOKEN = 0,   /* token t keeps only its own active neurons (batch-invariant)    */
+    CSF_SEM_UNION = 1        /* every token uses every neuron of the batch's union              */
+} csf_union_sem;
+
+/* Kernel family of csf_sparse_ffn_batched_union. */
+typedef enum {
+    CSF_PATH_AUTO = 0,       /* chosen from the batch size and dtype                             */
+    CSF_PATH_GATHER = 1,     /* vector-ALU gather kernels, B accumulators per column             */
+    CSF_PATH_MFMA = 2        /* matrix-core (MFMA) kernels; 16-bit types, d % 256 == 0           */
+} csf_path;
+
 /* ABI version of this header (bumped on any incompatible change). */
 #define CSF_ABI_VERSION 1
 int csf_abi_version(void);
@@ -190,12 +203,43 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
                          void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer (per calling thread).
- * While n > 0 events are set, the i-th kernel a csf_sparse_ffn_layer call launches has the HIP
- * runtime record events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
+ * csf_sparse_ffn_batched_union -- the sparse FFN of B tokens reading the union of their active
+ * sets once.
+ * [CP] "When it breaks": the tokens of a batch select different neurons, so the layer reads the
+ *      union of their sets; [DV] "Kernel-Level Implementation": each token keeps its own list;
+ *      [DV] "Implications for System Design": sparse batching has a crossover batch size.
+ *
+ *   X         [B][d]  dtype       inputs, 1 <= B <= 32 (B = 0 is a no-op)
+ *   W1, b1, Wup, W2T, act, dtype  as csf_sparse_ffn
+ *   bitmaps   [B][(f+31)/32] uint32  each token's active set (the bitmap output of
+ *                                  csf_select_topk / csf_select_threshold); bits past f ignored
+ *   semantics CSF_SEM_PER_TOKEN: y_t = sparse FFN of x_t over its own set (rows of the union that
+ *             t did not select contribute exactly zero); CSF_SEM_UNION: over the whole union.
+ *   path      CSF_PATH_AUTO, CSF_PATH_GATHER or CSF_PATH_MFMA (CSF_ERR_UNSUPPORTED if the
+ *             matrix-core path is asked for float32 or d % 256 != 0).  The matrix-core path keeps
+ *             h as a pair of 16-bit values (hi + lo, about 22 significant bits) and needs
+ *             |h| < 65504 for binary16.
+ *   Y         [B][d]  float32     out
+ *   union_count [1] int32         out, optional device copy of the union size
+ *   path_taken  HOST int*         out, optional: CSF_PATH_GATHER or CSF_PATH_MFMA
+ * Each union row is read from HBM once per call for all B tokens.  f <= 65536.
+ * Workspace: csf_workspace_size(CSF_OP_BATCHED_UNION, B, d, f, 0, 0, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, int dtype,
+                                 const void *W1, const float *b1, const void *Wup,
+                                 const void *W2T, const uint32_t *bitmaps, int semantics,
+                                 int path, float *Y, int32_t *union_count, int *path_taken,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer and
+ * csf_sparse_ffn_batched_union (per calling thread).
+ * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record
+ * events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
  * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
- * order: predictor down-projection, predictor up-projection, selection, gathered up/gate rows,
- * gathered down rows (partial sums), reduction of the partial sums -- 12 events cover them all.
+ * order -- csf_sparse_ffn_layer: predictor down-projection, predictor up-projection, selection,
+ * gathered up/gate rows, gathered down rows (partial sums), reduction of the partial sums;
+ * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction.
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
  * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */

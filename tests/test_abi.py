@@ -122,6 +122,35 @@ def test_layer_validation():
     assert layer(wsb=100) == WS_SMALL
 
 
+def test_batched_union_validation():
+    taken = ctypes.c_int(-1)
+
+    def bu(X=P, B=4, d=256, f=100, act=csf.RELU, dt=csf.F16, W1=P, b1=NULL, Wup=NULL, W2T=P,
+           bm=P, sem=0, path=0, Y=P, uc=NULL, ws=P, wsb=1 << 26):
+        return L.csf_sparse_ffn_batched_union(X, B, d, f, act, dt, W1, b1, Wup, W2T, bm, sem, path,
+                                              Y, uc, ctypes.byref(taken), ws, wsb, NULL)
+    assert bu(B=33) == UNSUPPORTED                         # more tokens than one call takes
+    assert bu(B=-1) == INVALID
+    assert bu(f=70000) == UNSUPPORTED
+    assert bu(sem=2) == INVALID
+    assert bu(path=3) == INVALID
+    assert bu(bm=NULL) == INVALID
+    assert bu(bm=Q) == MISALIGNED
+    assert bu(Y=NULL) == INVALID
+    assert bu(uc=Q) == MISALIGNED
+    assert bu(dt=csf.F32, path=2) == UNSUPPORTED           # matrix cores: 16-bit types only
+    assert bu(d=264, path=2) == UNSUPPORTED                # ... and d % 256 == 0
+    assert b"d % 256" in L.csf_last_error()
+    assert bu(act=csf.REGLU) == INVALID
+    assert bu(wsb=1024) == WS_SMALL
+    # B = 0 enqueues nothing and reports the path the sizes would take
+    assert bu(B=0, X=NULL, bm=NULL, Y=NULL, dt=csf.F32) == OK and taken.value == 1
+    assert bu(B=0, X=NULL, bm=NULL, Y=NULL, path=2) == OK and taken.value == 2
+    need = csf.workspace_size(_lib.OP_BATCHED_UNION, 32, 7168, 28672, 0, 0, csf.F16)
+    # union list + h (float32, or hi/lo halves) + partial rows
+    assert need >= 28672 * 4 + 32 * 28672 * 4 + 32 * 7168 * 4
+
+
 def test_k_from_ratio_matches_the_printed_figures():
     figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     for case in figs["k_from_ratio"]:

@@ -1,0 +1,233 @@
+"""GPU parity of the batched union FFN (csf_sparse_ffn_batched_union) against the oracle.
+
+The oracle's batched form: token t over its own set (per-token semantics) or over the union of the
+batch's sets (union semantics), each a plain double-precision sparse FFN.  Both kernel families
+(vector-ALU gather, matrix-core MFMA) are compared at the FFN bars of csf_testutil; integer-valued
+inputs must match bit for bit on both.  The sets come from each token's bitmap, so every case also
+checks the union size the library reports.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import contextual_sparsity_ffn_amd as csf
+from contextual_sparsity_ffn_amd import workloads as wl
+from csf_testutil import announce, assert_ffn_close, layer_to_orc, to_orc
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _dev_layer(L):
+    d = lambda t: None if t is None else t.to(DEV)
+    return wl.Layer(L.cfg, d(L.V), d(L.U), d(L.W1), d(L.b1), d(L.Wup), d(L.W2T))
+
+
+def _bitmaps(sets, f):
+    words = np.stack([orc.to_bitmap(s, f) for s in sets])
+    return torch.from_numpy(words.view(np.int32)).to(DEV)
+
+
+def _random_sets(f, B, count, seed, shared=0.5):
+    """B ascending sets of `count` neurons: a `shared` fraction drawn from one common pool, so the
+    sets overlap the way clustered tokens do; the rest drawn per token."""
+    g = torch.Generator().manual_seed(seed)
+    pool = torch.randperm(f, generator=g)[: 2 * count]
+    sets = []
+    for _ in range(B):
+        n_sh = int(count * shared)
+        a = pool[torch.randperm(pool.numel(), generator=g)[:n_sh]]
+        rest = torch.randperm(f, generator=g)
+        rest = rest[~torch.isin(rest, a)][: count - n_sh]
+        sets.append(np.sort(torch.cat([a, rest]).numpy()).astype(np.int32))
+    return sets
+
+
+def _run(Ld, X, bm, semantics, path, uc=None):
+    Y, taken = csf.sparse_ffn_batched_union(X, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, bm, act=Ld.cfg.act,
+                                            semantics=semantics, path=path, union_count=uc)
+    torch.cuda.synchronize()
+    return Y, taken
+
+
+def _check(L, X, sets, Y, semantics, what):
+    o = layer_to_orc(L)
+    Yref = orc.batched_ffn(to_orc(X), sets, o["W1"], o["b1"], o["Wup"], o["W2T"], o["act"],
+                           o["dt"], union=semantics == csf.SEM_UNION)
+    for t in range(X.shape[0]):
+        assert_ffn_close(Y[t], Yref[t], L.cfg.dtype, f"{what} token {t}")
+
+
+# (name, config, B, active fraction): shapes span several tiles, f ends in a ragged word
+CASES = [
+    ("f16-B1", wl.CONFIGS[3].scaled(512, 1000, 64), 1, 0.2),
+    ("f16-B5", wl.CONFIGS[3].scaled(512, 1000, 64), 5, 0.2),
+    ("f16-B16", wl.CONFIGS[3].scaled(768, 2333, 64), 16, 0.2),
+    ("f16-B17", wl.CONFIGS[3].scaled(768, 2333, 64), 17, 0.1),
+    ("f16-B32", wl.CONFIGS[3].scaled(1024, 1601, 64), 32, 0.2),
+    ("bf16-reglu-B3", wl.CONFIGS[2].scaled(512, 1433, 64), 3, 0.3),
+    ("bf16-reglu-B20", wl.CONFIGS[2].scaled(512, 1433, 64), 20, 0.3),
+]
+PATHS = [("gather", csf.PATH_GATHER), ("mfma", csf.PATH_MFMA)]
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+@pytest.mark.parametrize("name,cfg,B,frac", CASES, ids=[c[0] for c in CASES])
+def test_batched_union_per_token(name, cfg, B, frac, pname, path):
+    announce(f"batched union {name} {pname}")
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    X = wl.make_clustered_tokens(cfg, B)
+    sets = _random_sets(cfg.f, B, max(1, int(cfg.f * frac)), seed=B * 1000 + cfg.d)
+    uc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    Y, taken = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, path, uc)
+    assert taken == path
+    assert int(uc.item()) == len(orc.union_of(sets, cfg.f))
+    _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"{name}/{pname}")
+    # the same call again gives the same bits
+    Y2, _ = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, path)
+    assert torch.equal(Y, Y2)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_batched_union_semantics_union(pname, path):
+    announce(f"batched union semantics=union {pname}")
+    cfg = wl.CONFIGS[3].scaled(512, 1200, 64)
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    B = 6
+    X = wl.make_clustered_tokens(cfg, B)
+    sets = _random_sets(cfg.f, B, 150, seed=11)
+    Y, _ = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_UNION, path)
+    _check(L, X, sets, Y, csf.SEM_UNION, f"union/{pname}")
+    # every neuron in every set: the union is the dense layer
+    full = [np.arange(cfg.f, dtype=np.int32)] * B
+    Yd, _ = _run(Ld, X.to(DEV), _bitmaps(full, cfg.f), csf.SEM_UNION, path)
+    o = layer_to_orc(L)
+    for t in range(B):
+        ref = orc.dense_ffn(to_orc(X[t]), o["W1"], o["b1"], None, o["W2T"], o["act"], o["dt"])[1]
+        assert_ffn_close(Yd[t], ref, cfg.dtype, f"dense/{pname} token {t}")
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+@pytest.mark.parametrize("act", [csf.RELU, csf.REGLU])
+def test_batched_union_integer_inputs_bit_exact(act, pname, path):
+    """Small integers: every h is an integer below 2^16, so hi + lo holds it exactly (hi rounds to
+    a multiple of the binary16 spacing, the integer remainder lo is exact), every product is exact
+    and every partial sum stays below 2^24: both kernel families must reproduce the oracle bit for
+    bit."""
+    announce(f"batched union integer act={act} {pname}")
+    g = torch.Generator().manual_seed(91 + act)
+    d, f, B = 768, 1111, 19
+    x = torch.randint(-1, 2, (B, d), generator=g).half()
+    W1 = torch.randint(-1, 2, (f, d), generator=g).half()
+    Wup = torch.randint(-1, 2, (f, d), generator=g).half() if act == csf.REGLU else None
+    W2T = torch.randint(-2, 3, (f, d), generator=g).half()
+    b1 = torch.randint(-3, 4, (f,), generator=g).float()
+    sets = _random_sets(f, B, 300, seed=3)
+    cfg = dataclasses.replace(wl.CONFIGS[3].scaled(d, f, 64), act=act)
+    Ld = wl.Layer(cfg, None, None, W1.to(DEV), b1.to(DEV), None if Wup is None else Wup.to(DEV),
+                  W2T.to(DEV))
+    Y, _ = _run(Ld, x.to(DEV), _bitmaps(sets, f), csf.SEM_PER_TOKEN, path)
+    Yref = orc.batched_ffn(to_orc(x), sets, to_orc(W1), to_orc(b1),
+                           None if Wup is None else to_orc(Wup), to_orc(W2T), act, orc.F16)
+    h_max = 0.0
+    for t in range(B):
+        h, _ = orc.sparse_ffn(to_orc(x[t]), to_orc(W1), to_orc(b1),
+                              None if Wup is None else to_orc(Wup), to_orc(W2T), sets[t], act,
+                              orc.F16)
+        h_max = max(h_max, float(np.abs(h).max()))
+    assert h_max < 65504 and np.abs(Yref).max() < 2 ** 24
+    assert np.array_equal(Y.cpu().double().numpy(), Yref)
+
+
+def test_batched_union_float32_and_auto_path():
+    announce("batched union float32 / auto path")
+    cfg = wl.CONFIGS[0]                                    # d = 256, f = 1024, float32
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    B = 7
+    X = wl.make_clustered_tokens(cfg, B)
+    sets = _random_sets(cfg.f, B, cfg.k, seed=4)
+    Y, taken = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, csf.PATH_AUTO)
+    assert taken == csf.PATH_GATHER                        # matrix cores take 16-bit types only
+    _check(L, X, sets, Y, csf.SEM_PER_TOKEN, "f32")
+    with pytest.raises(csf.CsfError):
+        _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, csf.PATH_MFMA)
+    # 16-bit: one token gathers, a batch of 8 takes the matrix cores
+    c16 = wl.CONFIGS[3].scaled(512, 1000, 64)
+    L16 = _dev_layer(wl.make_layer(c16))
+    X16 = wl.make_tokens(c16, 8).to(DEV)
+    s16 = _random_sets(c16.f, 8, 100, seed=5)
+    _, t1 = _run(L16, X16[:1].contiguous(), _bitmaps(s16[:1], c16.f), csf.SEM_PER_TOKEN, csf.PATH_AUTO)
+    _, t8 = _run(L16, X16, _bitmaps(s16, c16.f), csf.SEM_PER_TOKEN, csf.PATH_AUTO)
+    assert (t1, t8) == (csf.PATH_GATHER, csf.PATH_MFMA)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_batched_union_empty_and_one_token_sets(pname, path):
+    announce(f"batched union empty sets {pname}")
+    cfg = wl.CONFIGS[3].scaled(512, 999, 64)
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    B = 4
+    X = wl.make_tokens(cfg, B)
+    empty = [np.zeros(0, np.int32)] * B
+    uc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    Y, _ = _run(Ld, X.to(DEV), _bitmaps(empty, cfg.f), csf.SEM_PER_TOKEN, path, uc)
+    assert int(uc.item()) == 0 and not Y.any()
+    # only token 2 has neurons (including the last one, f - 1); the others must stay exactly 0
+    sets = [np.zeros(0, np.int32), np.zeros(0, np.int32),
+            np.array([0, 5, 31, 32, 500, cfg.f - 1], np.int32), np.zeros(0, np.int32)]
+    Y, _ = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, path, uc)
+    assert int(uc.item()) == 6
+    assert not Y[0].any() and not Y[1].any() and not Y[3].any()
+    _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"one-token/{pname}")
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_batched_union_matches_single_token_path(pname, path):
+    """Per-token semantics: each token's row equals the single-token sparse FFN of its own list
+    (to float32 rounding; the two sum in different orders)."""
+    announce(f"batched union vs single-token {pname}")
+    cfg = wl.CONFIGS[3].scaled(1024, 3000, 64)
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    B = 9
+    X = wl.make_clustered_tokens(cfg, B).to(DEV)
+    sets = _random_sets(cfg.f, B, 600, seed=8)
+    Y, _ = _run(Ld, X, _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, path)
+    for t in range(B):
+        y1 = csf.sparse_ffn(X[t], Ld.W1, Ld.b1, None, Ld.W2T, torch.from_numpy(sets[t]).to(DEV))
+        torch.cuda.synchronize()
+        err = float((Y[t] - y1).abs().max() / y1.abs().max())
+        assert err <= 1e-5, (t, err)
+
+
+@pytest.mark.parametrize("B,path", [(4, csf.PATH_GATHER), (32, csf.PATH_MFMA)],
+                         ids=["B4-gather", "B32-mfma"])
+def test_batched_union_full_size_opt30b_shape(B, path):
+    """The OPT-30B FFN shape (d 7168, f 28672, top-k 5734 per token) with sets chosen by the
+    library's own predictor and top-k on clustered tokens, as the benchmark runs it."""
+    announce(f"batched union full size B={B}")
+    cfg = wl.CONFIGS[3]
+    Ld = wl.make_layer(cfg, device=DEV)
+    X = wl.make_clustered_tokens(cfg, B, device=DEV)
+    scores = csf.predict_active(X, Ld.V, Ld.U)
+    words = (cfg.f + 31) // 32
+    bm = torch.zeros(B, words, dtype=torch.int32, device=DEV)
+    idx = csf.select_topk(scores, cfg.k, bitmap=bm)
+    uc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y, taken = _run(Ld, X, bm, csf.SEM_PER_TOKEN, path, uc)
+    assert taken == path
+    sets = [idx[t].cpu().numpy() for t in range(B)]
+    assert int(uc.item()) == len(orc.union_of(sets, cfg.f))
+    o = dict(W1=to_orc(Ld.W1), b1=to_orc(Ld.b1), W2T=to_orc(Ld.W2T))
+    for t in (0, B // 2, B - 1):                          # three tokens through the oracle
+        _, ref = orc.sparse_ffn(to_orc(X[t]), o["W1"], o["b1"], None, o["W2T"], sets[t],
+                                orc.RELU, orc.F16)
+        assert_ffn_close(Y[t], ref, cfg.dtype, f"full B={B} token {t}")
