@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--batched-steps", type=int, default=256,
+                    help="steps per (batch size, path) of the OPT-30B-shape batched leg (0: skip)")
+    ap.add_argument("--batched-layers", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -223,10 +226,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # ---- batched union leg (OPT-30B shape) --------------------------------------------------
+    batched = None
+    if args.batched_steps > 0:
+        del layers
+        torch.cuda.empty_cache()
+        batched = batched_union_leg(args, dev)
+
     # ---- CPU oracle baseline (rank 0, bounded sample) ----------------------------------------
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, layers[0], X, args.cpu_tokens, touched)
+        cpu = cpu_baseline(cfg, wl.make_layer(cfg, device=dev, layer=0), X, args.cpu_tokens,
+                           touched)
 
     dense_b = wl.dense_bytes(cfg)
     out = {
@@ -263,8 +274,133 @@ def main():
         "true_frac": round(sum(tfrac) / len(tfrac), 4) if tfrac else None,
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
+        "batched_union": batched,
     }
     print(json.dumps(out), flush=True)
+
+
+PEAK_MFMA_F16_TFLOPS = 2500.0
+UNION_KERNELS = ["pred_down", "pred_up", "select_topk", "union_list", "union_up", "union_down",
+                 "reduce_partials"]
+
+
+def batched_union_leg(args, dev):
+    """OPT-30B FFN shape (d 7168, f 28672, r 512, top-k 5734 = 20%), clustered tokens (8 centroids
+    + N(0, 0.3)), batches of B in {1, 4, 8, 16, 32}: one step is csf_sparse_ffn_batched_layer
+    (predict, top-k with bitmaps, union FFN, per-token semantics) on both kernel families, plus
+    the batched dense layer (every neuron, matrix-core path) at the same B."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    cfg = wl.CONFIGS[3]
+    d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
+    code = _lib.dtype_code(cfg.dtype)
+    nl = args.batched_layers
+    log(f"batched leg: {nl} layer instances of d={d} f={f} r={r}")
+    layers = [wl.make_layer(cfg, device=dev, layer=l) for l in range(nl)]
+    ntok = 256
+    X = wl.make_clustered_tokens(cfg, ntok, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+    fn = _lib.lib.csf_sparse_ffn_batched_layer
+    ufn = _lib.lib.csf_sparse_ffn_batched_union
+    words = (f + 31) // 32
+    full_bm = torch.full((32, words), -1, dtype=torch.int32, device=dev)
+    full_bm[:, -1] = (1 << (f % 32)) - 1 if f % 32 else -1
+    pred_bytes = 2 * (r * d + f * r)
+    out = []
+    for B in (1, 4, 8, 16, 32):
+        Y = torch.empty(B, d, dtype=torch.float32, device=dev)
+        uc = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws_b = csf.workspace_size(_lib.OP_BATCHED_LAYER, B, d, f, r, k, code)
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+        taken = ctypes.c_int(0)
+        nb = ntok // B
+
+        def args_for(s, path, ucount=None):
+            L = layers[s % nl]
+            Xb = X[(s % nb) * B:(s % nb) * B + B]
+            return (vp(Xb.data_ptr()), B, d, f, r, cfg.act, code, vp(L.V.data_ptr()),
+                    vp(L.U.data_ptr()), vp(L.W1.data_ptr()), vp(L.b1.data_ptr()), None,
+                    vp(L.W2T.data_ptr()), k, ctypes.c_float(0.0), 0, path, vp(Y.data_ptr()), None,
+                    None if ucount is None else vp(ucount.data_ptr()), ctypes.byref(taken),
+                    vp(ws.data_ptr()), ws_b, vp(stream.cuda_stream))
+
+        # union sizes of every (layer, batch) pair the timed loop visits
+        usum = 0
+        npairs = min(args.batched_steps, nl * nb)
+        for s in range(npairs):
+            fn(*args_for(s, _lib.PATH_GATHER, uc))
+            usum += int(uc.item())
+        u_mean = usum / npairs
+        step_bytes = pred_bytes + u_mean * 2 * d * 2 + B * d * 2
+        flops = 4.0 * B * u_mean * d
+        row = {"B": B, "union_mean": round(u_mean, 1), "union_frac": round(u_mean / f, 4),
+               "bytes_per_step": int(step_bytes)}
+        for pname, path in (("gather", _lib.PATH_GATHER), ("mfma", _lib.PATH_MFMA)):
+            plan = [args_for(s, path) for s in range(max(nl * nb, 1))]
+            for s in range(16):
+                rc = fn(*plan[s % len(plan)])
+                if rc:
+                    raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(args.batched_steps):
+                fn(*plan[s % len(plan)])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.batched_steps
+            # per-kernel times (runtime-recorded start/end events)
+            nev = 2 * len(UNION_KERNELS)
+            nt = min(64, args.batched_steps)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nt)]
+            for rowe in evs:
+                for e in rowe:
+                    e.record(stream)
+            torch.cuda.synchronize()
+            for s in range(nt):
+                csf.set_trace_events(evs[s])
+                fn(*plan[s % len(plan)])
+            csf.set_trace_events([])
+            torch.cuda.synchronize()
+            kern = {n: round(sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(nt))
+                             * 1e3 / nt, 2) for i, n in enumerate(UNION_KERNELS)}
+            row[pname] = {"us_per_batch": round(us, 2), "tokens_per_s": round(B / us * 1e6, 1),
+                          "GBps_touched": round(step_bytes / (us * 1e-6) / 1e9, 1),
+                          "mfma_util": round(flops / (us * 1e-6) / (PEAK_MFMA_F16_TFLOPS * 1e12), 5),
+                          "kernels_us": kern}
+        # batched dense: every neuron for every token (union semantics, all-ones bitmaps)
+        dws_b = csf.workspace_size(_lib.OP_BATCHED_UNION, B, d, f, 0, 0, code)
+        dws = torch.empty(dws_b, dtype=torch.uint8, device=dev)
+        dplan = [(vp(X[(s % nb) * B:(s % nb) * B + B].data_ptr()), B, d, f, cfg.act, code,
+                  vp(layers[s % nl].W1.data_ptr()), vp(layers[s % nl].b1.data_ptr()), None,
+                  vp(layers[s % nl].W2T.data_ptr()), vp(full_bm.data_ptr()), 1, _lib.PATH_MFMA,
+                  vp(Y.data_ptr()), None, ctypes.byref(taken), vp(dws.data_ptr()), dws_b,
+                  vp(stream.cuda_stream)) for s in range(nl)]
+        for s in range(4):
+            ufn(*dplan[s % nl])
+        torch.cuda.synchronize()
+        nd = max(8, args.batched_steps // 8)
+        e0.record(stream)
+        for s in range(nd):
+            ufn(*dplan[s % nl])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dus = e0.elapsed_time(e1) * 1e3 / nd
+        row["dense_mfma_us"] = round(dus, 2)
+        row["dense_GBps"] = round(2 * f * d * 2 / (dus * 1e-6) / 1e9, 1)
+        best = min(row["gather"]["us_per_batch"], row["mfma"]["us_per_batch"])
+        row["speedup_vs_dense"] = round(dus / best, 3)
+        log(f"B={B}: union {u_mean:.0f} ({u_mean / f:.2f}), gather {row['gather']['us_per_batch']} us, "
+            f"mfma {row['mfma']['us_per_batch']} us, dense {row['dense_mfma_us']} us")
+        out.append(row)
+        del ws, dws
+    return {"workload": "OPT-30B-shape sparse FFN layer, clustered tokens, per-token semantics: "
+                        "predict + top-k + union FFN",
+            "d": d, "f": f, "r": r, "k": k, "layers_rotated": nl, "steps": args.batched_steps,
+            "rows": out}
 
 
 def cpu_baseline(cfg, L, X, ntok, touched):

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libcsf.so")
 F32, F16, BF16 = 0, 1, 2
 RELU, REGLU = 0, 1
 OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
-    OP_BATCHED_UNION = range(7)
+    OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK = range(9)
+STACK_SYNC, STACK_LOOKAHEAD = 0, 1
 SEM_PER_TOKEN, SEM_UNION = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_MFMA = 0, 1, 2
 MAX_UNION_BATCH = 32
@@ -30,7 +31,13 @@ _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
            "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
            "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_batched_union",
-           "csf_set_trace_events")
+           "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_trace_events")
+
+
+class LayerWeights(ctypes.Structure):
+    """csf_layer_weights: one block's device pointers."""
+    _fields_ = [("V", ctypes.c_void_p), ("U", ctypes.c_void_p), ("W1", ctypes.c_void_p),
+                ("Wup", ctypes.c_void_p), ("W2T", ctypes.c_void_p), ("b1", ctypes.c_void_p)]
 
 
 class CsfError(RuntimeError):
@@ -65,6 +72,12 @@ def _load():
                                        flt, vp, vp, vp, vp, vp, sz, vp]
     L.csf_sparse_ffn_batched_union.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                i32, i32, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
+    L.csf_sparse_ffn_batched_layer.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                               vp, vp, i32, flt, i32, i32, vp, vp, vp,
+                                               ctypes.POINTER(i32), vp, sz, vp]
+    L.csf_stack_forward.argtypes = [ctypes.POINTER(LayerWeights), i32, i32, i32, i32, i32, i32,
+                                    vp, i32, i32, i32, flt, i32, flt, vp, vp, vp, vp, vp, sz, vp,
+                                    vp]
     for name in EXPORTS[4:]:
         getattr(L, name).restype = i32
     return L
@@ -337,3 +350,85 @@ def sparse_ffn_batched_union(X, W1, b1, Wup, W2T, bitmaps, act=RELU, semantics=S
                                             int(path), _ptr(Y), _ptr(union_count),
                                             ctypes.byref(taken), _ptr(w), wb, _stream(dev)))
     return Y, taken.value
+
+
+def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU,
+                             semantics=SEM_PER_TOKEN, path=PATH_AUTO, Y=None, bitmaps=None,
+                             union_count=None, ws=None):
+    """Predict, select (top-k if k is given, else threshold tau) and the batched union FFN for
+    the B tokens X [B, d].  Returns (Y [B, d] float32, path taken)."""
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k (top-k) or tau (threshold)")
+    _tensor(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be [B, d]")
+    dev, dt, f, d = _ffn_weights(X, W1, b1, Wup, W2T, act)
+    B = X.shape[0]
+    _tensor(X, "X", shape=(B, d))
+    r = V.shape[0]
+    _tensor(V, "V", dtype=dt, shape=(r, d), device=dev)
+    _tensor(U, "U", dtype=dt, shape=(f, r), device=dev)
+    kk = -1 if k is None else int(k)
+    if Y is None:
+        Y = torch.empty(B, d, dtype=torch.float32, device=dev)
+    _tensor(Y, "Y", dtype=torch.float32, shape=(B, d), device=dev)
+    _tensor(bitmaps, "bitmaps", dtype=torch.int32, shape=(B, (f + 31) // 32), device=dev,
+            optional=True)
+    _tensor(union_count, "union_count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    code = dtype_code(dt)
+    max_count = f if kk < 0 else kk
+    w, wb = _workspace(workspace_size(OP_BATCHED_LAYER, B, d, f, r, max_count, code), dev, ws)
+    taken = ctypes.c_int(0)
+    _check(lib.csf_sparse_ffn_batched_layer(
+        _ptr(X), B, d, f, r, act, code, _ptr(V), _ptr(U), _ptr(W1), _ptr(b1), _ptr(Wup), _ptr(W2T),
+        kk, float(tau if tau is not None else 0.0), int(semantics), int(path), _ptr(Y),
+        _ptr(bitmaps), _ptr(union_count), ctypes.byref(taken), _ptr(w), wb, _stream(dev)))
+    return Y, taken.value
+
+
+def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=True, eps=1e-6,
+                  x_log=None, xhat_log=None, idx_log=None, count_log=None, side_stream=None,
+                  ws=None):
+    """Run x [B, d] (float32, updated in place) through the residual blocks `layers` (objects with
+    V, U, W1, b1, Wup, W2T device tensors).  lookahead: each layer's set is predicted from the
+    previous layer's input on `side_stream` (a torch.cuda.Stream; required).  Returns x."""
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k (top-k) or tau (threshold)")
+    _tensor(x, "x", dtype=torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [B, d]")
+    B, d = x.shape
+    dev = x.device
+    nl = len(layers)
+    if nl == 0:
+        return x
+    L0 = layers[0]
+    dt = L0.W1.dtype
+    f, r = L0.W1.shape[0], L0.V.shape[0]
+    arr = (LayerWeights * nl)()
+    for i, Lw in enumerate(layers):
+        _ffn_weights(torch.empty(0, dtype=dt, device=dev), Lw.W1, Lw.b1, Lw.Wup, Lw.W2T, act)
+        _tensor(Lw.W1, "W1", shape=(f, d))
+        _tensor(Lw.V, "V", dtype=dt, shape=(r, d), device=dev)
+        _tensor(Lw.U, "U", dtype=dt, shape=(f, r), device=dev)
+        arr[i] = LayerWeights(Lw.V.data_ptr(), Lw.U.data_ptr(), Lw.W1.data_ptr(),
+                              None if Lw.Wup is None else Lw.Wup.data_ptr(), Lw.W2T.data_ptr(),
+                              None if Lw.b1 is None else Lw.b1.data_ptr())
+    kk = -1 if k is None else int(k)
+    stride = f if kk < 0 else max(kk, 1)
+    _tensor(x_log, "x_log", dtype=torch.float32, shape=(nl, B, d), device=dev, optional=True)
+    _tensor(xhat_log, "xhat_log", dtype=dt, shape=(nl, B, d), device=dev, optional=True)
+    _tensor(idx_log, "idx_log", dtype=torch.int32, shape=(nl, B, stride), device=dev, optional=True)
+    _tensor(count_log, "count_log", dtype=torch.int32, shape=(nl, B), device=dev, optional=True)
+    if lookahead and side_stream is None:
+        raise ValueError("look-ahead needs a side stream")
+    code = dtype_code(dt)
+    max_count = f if kk < 0 else kk
+    w, wb = _workspace(workspace_size(OP_STACK, B, d, f, r, max_count, code), dev, ws)
+    side = None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)
+    _check(lib.csf_stack_forward(arr, nl, d, f, r, act, code, _ptr(x), B,
+                                 STACK_LOOKAHEAD if lookahead else STACK_SYNC, kk,
+                                 float(tau if tau is not None else 0.0), 1 if norm else 0,
+                                 float(eps), _ptr(x_log), _ptr(xhat_log), _ptr(idx_log),
+                                 _ptr(count_log), _ptr(w), wb, _stream(dev), side))
+    return x

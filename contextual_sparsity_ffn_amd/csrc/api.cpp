@@ -170,6 +170,57 @@ UnionWs union_ws(int B, int d, int f, int dtype)
     return w;
 }
 
+struct BatchedLayerWs {
+    size_t a, scores, idx, count, bitmap, uni, total;
+};
+BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int dtype)
+{
+    BatchedLayerWs w;
+    const size_t Bn = B > 0 ? (size_t)B : 1;
+    w.a = 0;
+    w.scores = w.a + round_up((size_t)csf::kMaxPredSplit * Bn * r * sizeof(float));
+    w.idx = w.scores + round_up(Bn * f * sizeof(float));
+    w.count = w.idx + round_up(Bn * (max_count > 0 ? max_count : 1) * sizeof(int32_t));
+    w.bitmap = w.count + round_up(Bn * sizeof(int32_t));
+    w.uni = w.bitmap + round_up(Bn * ((f + 31) / 32) * sizeof(uint32_t));
+    w.total = w.uni + union_ws(B, d, f, dtype).total;
+    return w;
+}
+
+struct StackWs {
+    size_t xhat[2], a_main, s_main, a_side, s_side, idx[2], count[2], ffn, total;
+};
+StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
+{
+    StackWs w;
+    const size_t Bn = B > 0 ? (size_t)B : 1;
+    const size_t mc = max_count > 0 ? (size_t)max_count : 1;
+    size_t o = 0;
+    for (int i = 0; i < 2; ++i) {
+        w.xhat[i] = o;
+        o += round_up(Bn * d * elem_bytes(dtype));
+    }
+    const size_t pa = round_up((size_t)csf::kMaxPredSplit * Bn * r * sizeof(float));
+    const size_t ps = round_up(Bn * f * sizeof(float));
+    w.a_main = o;
+    o += pa;
+    w.s_main = o;
+    o += ps;
+    w.a_side = o;
+    o += pa;
+    w.s_side = o;
+    o += ps;
+    for (int i = 0; i < 2; ++i) {
+        w.idx[i] = o;
+        o += round_up(Bn * mc * sizeof(int32_t));
+        w.count[i] = o;
+        o += round_up(Bn * sizeof(int32_t));
+    }
+    w.ffn = o;
+    w.total = o + ffn_ws(B > 0 ? B : 1, d, dtype, max_count).total;
+    return w;
+}
+
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 int check_ws(void *ws, size_t ws_bytes, size_t need)
@@ -207,6 +258,98 @@ int validate_ffn(const void *x, int B, int d, int f, int act, int dtype, const v
     } else {
         REQUIRE(Wup == nullptr, CSF_ERR_INVALID_ARG, "Wup must be NULL for CSF_ACT_RELU");
     }
+    return CSF_OK;
+}
+
+int validate_union(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
+                   const float *b1, const void *Wup, const void *W2T, int semantics, int path,
+                   const float *Y, const int32_t *union_count)
+{
+    int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    REQUIRE(B <= csf::kMaxUnionBatch, CSF_ERR_UNSUPPORTED,
+            "B = %d exceeds this build's limit of %d tokens per batched call", B,
+            csf::kMaxUnionBatch);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(semantics == CSF_SEM_PER_TOKEN || semantics == CSF_SEM_UNION, CSF_ERR_INVALID_ARG,
+            "unknown semantics %d", semantics);
+    REQUIRE(path == CSF_PATH_AUTO || path == CSF_PATH_GATHER || path == CSF_PATH_MFMA,
+            CSF_ERR_INVALID_ARG, "unknown path %d", path);
+    CHECK_PTR(Y, B > 0);
+    CHECK_PTR(union_count, false);
+    REQUIRE(path != CSF_PATH_MFMA || csf::union_mfma_supported(dtype, d, B > 0 ? B : 1),
+            CSF_ERR_UNSUPPORTED,
+            "the matrix-core path needs a 16-bit dtype and d %% 256 == 0 (dtype %d, d = %d)", dtype,
+            d);
+    return CSF_OK;
+}
+
+bool choose_union_path(int path, int dtype, int d, int B)
+{
+    if (path == CSF_PATH_MFMA)
+        return true;
+    return path == CSF_PATH_AUTO && csf::union_mfma_supported(dtype, d, B > 0 ? B : 1) &&
+           B >= kMfmaMinBatch;
+}
+
+int enqueue_union(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
+                  const float *b1, const void *Wup, const void *W2T, const uint32_t *bitmaps,
+                  int semantics, bool mfma, float *Y, int32_t *union_count, void *ws,
+                  const UnionWs &w, hipStream_t st, csf::Trace *tr)
+{
+    csf::UnionArgs a;
+    a.dtype = dtype;
+    a.act = act;
+    a.per_token = semantics == CSF_SEM_PER_TOKEN;
+    a.mfma = mfma;
+    a.X = X;
+    a.B = B;
+    a.d = d;
+    a.f = f;
+    a.W1 = W1;
+    a.Wup = Wup;
+    a.W2T = W2T;
+    a.b1 = b1;
+    a.bitmaps = bitmaps;
+    a.Y = Y;
+    a.ucount_out = union_count;
+    a.ulist = reinterpret_cast<int32_t *>(at(ws, w.ulist));
+    a.ucount = reinterpret_cast<int32_t *>(at(ws, w.ucount));
+    a.h32 = reinterpret_cast<float *>(at(ws, w.h));
+    a.hhi = reinterpret_cast<uint16_t *>(at(ws, w.h));
+    a.hlo = reinterpret_cast<uint16_t *>(at(ws, w.hlo));
+    a.hs = (int)csf::union_h_stride(f);
+    a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    return hip_status(csf::launch_union_ffn(a, st, tr), "batched union FFN launch");
+}
+
+// Four events per device and calling thread for the look-ahead stack: "layer input ready" and
+// "selection ready", each double-buffered across consecutive layers.  Created once, on first use.
+int stack_events(hipEvent_t ev_x[2], hipEvent_t ev_s[2])
+{
+    constexpr int kMaxDevices = 64;
+    thread_local hipEvent_t cache[kMaxDevices][4] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond this build's limit", dev);
+    for (int i = 0; i < 4; ++i) {
+        if (!cache[dev][i]) {
+            e = hipEventCreateWithFlags(&cache[dev][i], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                cache[dev][i] = nullptr;
+                return hip_status(e, "hipEventCreateWithFlags");
+            }
+        }
+    }
+    ev_x[0] = cache[dev][0];
+    ev_x[1] = cache[dev][1];
+    ev_s[0] = cache[dev][2];
+    ev_s[1] = cache[dev][3];
     return CSF_OK;
 }
 
@@ -261,6 +404,10 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
         return r > 0 ? layer_ws(d, f, r, max_count, dtype).total : 0;
     case CSF_OP_BATCHED_UNION:
         return union_ws(B, d, f, dtype).total;
+    case CSF_OP_BATCHED_LAYER:
+        return r > 0 ? batched_layer_ws(B, d, f, r, max_count, dtype).total : 0;
+    case CSF_OP_STACK:
+        return r > 0 ? stack_ws(B, d, f, r, max_count, dtype).total : 0;
     default:
         return 0;
     }
@@ -415,26 +562,12 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
                                  int path, float *Y, int32_t *union_count, int *path_taken,
                                  void *ws, size_t ws_bytes, void *stream)
 {
-    int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
+    int s = validate_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, semantics, path, Y,
+                           union_count);
     if (s != CSF_OK)
         return s;
-    REQUIRE(B <= csf::kMaxUnionBatch, CSF_ERR_UNSUPPORTED,
-            "B = %d exceeds this build's limit of %d tokens per batched call", B,
-            csf::kMaxUnionBatch);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
-            f, csf::select_max_f());
-    REQUIRE(semantics == CSF_SEM_PER_TOKEN || semantics == CSF_SEM_UNION, CSF_ERR_INVALID_ARG,
-            "unknown semantics %d", semantics);
-    REQUIRE(path == CSF_PATH_AUTO || path == CSF_PATH_GATHER || path == CSF_PATH_MFMA,
-            CSF_ERR_INVALID_ARG, "unknown path %d", path);
     CHECK_PTR(bitmaps, B > 0);
-    CHECK_PTR(Y, B > 0);
-    CHECK_PTR(union_count, false);
-    const bool mfma_ok = csf::union_mfma_supported(dtype, d, B > 0 ? B : 1);
-    REQUIRE(path != CSF_PATH_MFMA || mfma_ok, CSF_ERR_UNSUPPORTED,
-            "the matrix-core path needs a 16-bit dtype and d %% 256 == 0 (dtype %d, d = %d)", dtype,
-            d);
-    const bool mfma = path == CSF_PATH_MFMA || (path == CSF_PATH_AUTO && mfma_ok && B >= kMfmaMinBatch);
+    const bool mfma = choose_union_path(path, dtype, d, B);
     if (B == 0) {
         if (path_taken)
             *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
@@ -442,36 +575,73 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
     }
     UnionWs w = union_ws(B, d, f, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
-    csf::UnionArgs a;
-    a.dtype = dtype;
-    a.act = act;
-    a.per_token = semantics == CSF_SEM_PER_TOKEN;
-    a.mfma = mfma;
-    a.X = X;
-    a.B = B;
-    a.d = d;
-    a.f = f;
-    a.W1 = W1;
-    a.Wup = Wup;
-    a.W2T = W2T;
-    a.b1 = b1;
-    a.bitmaps = bitmaps;
-    a.Y = Y;
-    a.ucount_out = union_count;
-    a.ulist = reinterpret_cast<int32_t *>(at(ws, w.ulist));
-    a.ucount = reinterpret_cast<int32_t *>(at(ws, w.ucount));
-    a.h32 = reinterpret_cast<float *>(at(ws, w.h));
-    a.hhi = reinterpret_cast<uint16_t *>(at(ws, w.h));
-    a.hlo = reinterpret_cast<uint16_t *>(at(ws, w.hlo));
-    a.hs = (int)csf::union_h_stride(f);
-    a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    csf::Trace tr;
+    if (g_trace_n > 0) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    s = enqueue_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, bitmaps, semantics, mfma, Y,
+                      union_count, ws, w, static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
+    if (s == CSF_OK && path_taken)
+        *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
+    return s;
+}
+
+int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int act, int dtype,
+                                 const void *V, const void *U, const void *W1, const float *b1,
+                                 const void *Wup, const void *W2T, int k, float tau,
+                                 int semantics, int path, float *Y, uint32_t *bitmaps_out,
+                                 int32_t *union_count, int *path_taken, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    int s = validate_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, semantics, path, Y,
+                           union_count);
+    if (s != CSF_OK)
+        return s;
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(V, true);
+    CHECK_PTR(U, true);
+    CHECK_PTR(bitmaps_out, false);
+    REQUIRE(k >= -1 && k <= f, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, f = %d]",
+            k, f);
+    REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    const bool mfma = choose_union_path(path, dtype, d, B);
+    if (B == 0) {
+        if (path_taken)
+            *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
+        return ok();
+    }
+    const int max_count = k >= 0 ? k : f;
+    BatchedLayerWs w = batched_layer_ws(B, d, f, r, max_count, dtype);
+    CHECK_WS(ws, ws_bytes, w.total);
     hipStream_t st = static_cast<hipStream_t>(stream);
     csf::Trace tr;
     if (g_trace_n > 0) {
         tr.ev = g_trace_events;
         tr.n = g_trace_n;
     }
-    s = hip_status(csf::launch_union_ffn(a, st, tr.ev ? &tr : nullptr), "batched union FFN launch");
+    csf::Trace *trp = tr.ev ? &tr : nullptr;
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    float *sc = reinterpret_cast<float *>(at(ws, w.scores));
+    int32_t *ix = reinterpret_cast<int32_t *>(at(ws, w.idx));
+    int32_t *cn = reinterpret_cast<int32_t *>(at(ws, w.count));
+    uint32_t *bm = bitmaps_out ? bitmaps_out : reinterpret_cast<uint32_t *>(at(ws, w.bitmap));
+    hipError_t e = csf::launch_pred_down(dtype, X, B, d, V, r, a, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor down-projection launch");
+    e = csf::launch_pred_up(dtype, a, B, d, r, U, f, sc, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor up-projection launch");
+    const int stride = max_count > 0 ? max_count : 1;
+    if (k >= 0)
+        e = csf::launch_select_topk(sc, B, f, k, ix, stride, cn, bm, st, trp);
+    else
+        e = csf::launch_select_threshold(sc, B, f, tau, ix, f, cn, bm, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "selection launch");
+    UnionWs uw = union_ws(B, d, f, dtype);
+    s = enqueue_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, bm, semantics, mfma, Y,
+                      union_count, at(ws, w.uni), uw, st, trp);
     if (s == CSF_OK && path_taken)
         *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
     return s;
@@ -549,6 +719,143 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
+}
+
+int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
+                      int dtype, float *x, int B, int mode, int k, float tau, int norm, float eps,
+                      float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
+                      void *ws, size_t ws_bytes, void *stream, void *side_stream)
+{
+    REQUIRE(L >= 0, CSF_ERR_INVALID_ARG, "L must be >= 0 (got %d)", L);
+    REQUIRE(L == 0 || layers, CSF_ERR_INVALID_ARG, "layers must not be NULL when L > 0");
+    REQUIRE(mode == CSF_STACK_SYNC || mode == CSF_STACK_LOOKAHEAD, CSF_ERR_INVALID_ARG,
+            "unknown stack mode %d", mode);
+    REQUIRE(norm == 0 || norm == 1, CSF_ERR_INVALID_ARG, "norm must be 0 or 1 (got %d)", norm);
+    REQUIRE(eps >= 0.0f && eps < 1e30f, CSF_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    REQUIRE(mode == CSF_STACK_SYNC || (side_stream && side_stream != stream), CSF_ERR_INVALID_ARG,
+            "look-ahead needs a side stream distinct from the main stream");
+    for (int l = 0; l < L; ++l) {
+        int s = validate_ffn(x, B, d, f, act, dtype, layers[l].W1, layers[l].b1, layers[l].Wup,
+                             layers[l].W2T);
+        if (s != CSF_OK)
+            return fail(s, "layer %d: %s", l, g_last_error.c_str());
+        s = check_ptr(layers[l].V, "V", true);
+        if (s == CSF_OK)
+            s = check_ptr(layers[l].U, "U", true);
+        if (s != CSF_OK)
+            return fail(s, "layer %d: %s", l, g_last_error.c_str());
+    }
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    REQUIRE(k >= -1 && k <= f, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, f = %d]",
+            k, f);
+    REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    REQUIRE(f > 0 && f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED,
+            "f = %d is outside this build's range [1, %d]", f, csf::select_max_f());
+    CHECK_PTR(x, B > 0 && L > 0);
+    CHECK_PTR(x_log, false);
+    CHECK_PTR(xhat_log, false);
+    CHECK_PTR(idx_log, false);
+    CHECK_PTR(count_log, false);
+    if (L == 0 || B == 0)
+        return ok();
+    const int max_count = k >= 0 ? k : f;
+    const int stride = max_count > 0 ? max_count : 1;
+    StackWs w = stack_ws(B, d, f, r, max_count, dtype);
+    CHECK_WS(ws, ws_bytes, w.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t side = static_cast<hipStream_t>(side_stream);
+    const bool ahead = mode == CSF_STACK_LOOKAHEAD;
+    hipEvent_t ev_x[2] = {nullptr, nullptr}, ev_s[2] = {nullptr, nullptr};
+    if (ahead) {
+        int s = stack_events(ev_x, ev_s);
+        if (s != CSF_OK)
+            return s;
+    }
+    const size_t es = elem_bytes(dtype);
+    FfnWs fw = ffn_ws(B, d, dtype, max_count);
+
+    auto sel_idx = [&](int l) {
+        return idx_log ? idx_log + (size_t)l * B * stride
+                       : reinterpret_cast<int32_t *>(at(ws, w.idx[l & 1]));
+    };
+    auto sel_count = [&](int l) {
+        return count_log ? count_log + (size_t)l * B
+                         : reinterpret_cast<int32_t *>(at(ws, w.count[l & 1]));
+    };
+    // predictor of layer `l` applied to `xh`, then the selection, on stream `q`
+    auto predict_select = [&](int l, const void *xh, hipStream_t q, bool on_side) -> int {
+        float *a = reinterpret_cast<float *>(at(ws, on_side ? w.a_side : w.a_main));
+        float *sc = reinterpret_cast<float *>(at(ws, on_side ? w.s_side : w.s_main));
+        hipError_t e = csf::launch_pred_down(dtype, xh, B, d, layers[l].V, r, a, q);
+        if (e == hipSuccess)
+            e = csf::launch_pred_up(dtype, a, B, d, r, layers[l].U, f, sc, q);
+        if (e == hipSuccess) {
+            if (k >= 0)
+                e = csf::launch_select_topk(sc, B, f, k, sel_idx(l), stride, sel_count(l), nullptr, q);
+            else
+                e = csf::launch_select_threshold(sc, B, f, tau, sel_idx(l), stride, sel_count(l),
+                                                 nullptr, q);
+        }
+        return hip_status(e, "stack predictor/selection launch");
+    };
+
+    for (int l = 0; l < L; ++l) {
+        void *xh = at(ws, w.xhat[l & 1]);
+        hipError_t e = csf::launch_rms_norm(
+            dtype, x, B, d, eps, norm, xh, x_log ? x_log + (size_t)l * B * d : nullptr,
+            xhat_log ? static_cast<char *>(xhat_log) + (size_t)l * B * d * es : nullptr, st);
+        if (e != hipSuccess)
+            return hip_status(e, "stack normalisation launch");
+        int s = CSF_OK;
+        if (!ahead || l == 0)
+            s = predict_select(l, xh, st, false);
+        if (s != CSF_OK)
+            return s;
+        if (ahead && l + 1 < L) {
+            // layer l+1's set from this layer's input, on the side stream, while this layer runs
+            e = hipEventRecord(ev_x[l & 1], st);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(side, ev_x[l & 1], 0);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+            s = predict_select(l + 1, xh, side, true);
+            if (s != CSF_OK)
+                return s;
+            e = hipEventRecord(ev_s[(l + 1) & 1], side);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+        }
+        if (ahead && l > 0) {
+            e = hipStreamWaitEvent(st, ev_s[l & 1], 0);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+        }
+        csf::FfnArgs fa;
+        fa.dtype = dtype;
+        fa.act = act;
+        fa.x = xh;
+        fa.B = B;
+        fa.d = d;
+        fa.f = f;
+        fa.W1 = layers[l].W1;
+        fa.Wup = layers[l].Wup;
+        fa.W2T = layers[l].W2T;
+        fa.b1 = layers[l].b1;
+        fa.idx = sel_idx(l);
+        fa.idx_stride = stride;
+        fa.count = k >= 0 ? nullptr : sel_count(l);
+        fa.max_count = max_count;
+        fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+        fa.h_stride = stride;
+        fa.y = x;
+        fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+        fa.accumulate = 1;
+        e = csf::launch_ffn(fa, st);
+        if (e != hipSuccess)
+            return hip_status(e, "stack FFN launch");
+    }
+    return ok();
 }
 
 }  // extern "C"

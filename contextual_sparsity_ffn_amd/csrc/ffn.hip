@@ -213,9 +213,11 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
 }
 
 // y[token][col] = sum over chunks q (in order) of part[token][q][col]; one thread per column with
-// every partial load issued before the first add.
+// every partial load issued before the first add.  accumulate: y += that sum (the residual add of a
+// stack of blocks).
 __global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict__ part, int nchunk,
-                                                         int D, float *__restrict__ y)
+                                                         int D, float *__restrict__ y,
+                                                         int accumulate)
 {
     const int col = blockIdx.x * 256 + threadIdx.x;
     const int token = blockIdx.y;
@@ -230,7 +232,8 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict
 #pragma unroll
     for (int q = 0; q < kMaxChunks; ++q)
         sum += pv[q];
-    y[(size_t)token * D + col] = sum;
+    float *out = y + (size_t)token * D + col;
+    *out = accumulate ? *out + sum : sum;
 }
 
 template <class T, int MX, bool GATED>
@@ -273,7 +276,7 @@ hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
                a.max_count, a.f, C, nchunk, a.partials);
     if (e != hipSuccess)
         return e;
-    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.y, st, tr);
+    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.y, st, tr, a.accumulate);
 }
 
 }  // namespace
@@ -302,11 +305,12 @@ int ffn_num_chunks(int d, int dtype, int max_count)
 }
 
 hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, float *y,
-                                  hipStream_t st, Trace *tr)
+                                  hipStream_t st, Trace *tr, int accumulate)
 {
     if (nchunk < 1 || nchunk > kMaxChunks)
         return hipErrorInvalidValue;
-    return launch(k_reduce_partials, dim3((D + 255) / 256, B), dim3(256), st, tr, part, nchunk, D, y);
+    return launch(k_reduce_partials, dim3((D + 255) / 256, B), dim3(256), st, tr, part, nchunk, D, y,
+                  accumulate);
 }
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t st, Trace *tr)

@@ -77,6 +77,7 @@ struct FfnArgs {
     int h_stride;
     float *y;               // [B][d]
     float *partials;        // [B][ffn_num_chunks][d] workspace
+    int accumulate = 0;     // 1: y += the FFN output (residual add)
 };
 // Shape of the down projection's two-phase reduction (sizes its workspace).
 int ffn_num_slices(int d, int dtype);
@@ -84,7 +85,13 @@ int ffn_num_chunks(int d, int dtype, int max_count);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 // y[t][col] = sum over chunks q, in order, of part[t][q][col] (part is [B][nchunk][D] float32).
 hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, float *y,
-                                  hipStream_t stream, Trace *trace = nullptr);
+                                  hipStream_t stream, Trace *trace = nullptr, int accumulate = 0);
+
+// ---- stack of blocks (stack.hip) -------------------------------------------------------------
+// xhat[t] = storage-type rounding of x[t] / sqrt(mean(x[t]^2) + eps) (norm = 1) or of x[t]
+// (norm = 0); x_log / xhat_log (optional) receive copies of x and xhat.
+hipError_t launch_rms_norm(int dtype, const float *x, int B, int d, float eps, int norm, void *xhat,
+                           float *x_log, void *xhat_log, hipStream_t stream);
 
 // ---- batched FFN over the union of the tokens' sets (union.hip) -------------------------------
 constexpr int kMaxUnionBatch = 32;   // tokens per call (two 16-token matrix-core tiles)

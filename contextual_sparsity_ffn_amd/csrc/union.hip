@@ -75,9 +75,15 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
     for (int q = 0; q < 2; ++q) {
         const int w = t * wpt + q;
         if (q < wpt && w < words) {
+            // every token's word is loaded before the first OR (one round of load latency)
+            uint32_t v[kMaxUnionBatch];
+#pragma unroll
+            for (int b = 0; b < kMaxUnionBatch; ++b)
+                v[b] = b < B ? bitmaps[(size_t)b * words + w] : 0u;
             uint32_t o = 0u;
-            for (int b = 0; b < B; ++b)
-                o |= bitmaps[(size_t)b * words + w];
+#pragma unroll
+            for (int b = 0; b < kMaxUnionBatch; ++b)
+                o |= v[b];
             if (w == words - 1 && (f & 31))
                 o &= (1u << (f & 31)) - 1u;          // bits past f are not neurons
             orw[q] = o;

@@ -69,8 +69,24 @@ typedef enum {
     CSF_OP_SPARSE_FFN = 3,
     CSF_OP_DENSE_FFN = 4,
     CSF_OP_LAYER = 5,
-    CSF_OP_BATCHED_UNION = 6
+    CSF_OP_BATCHED_UNION = 6,
+    CSF_OP_BATCHED_LAYER = 7,
+    CSF_OP_STACK = 8
 } csf_op;
+
+/* How csf_stack_forward schedules the predictor of each layer. */
+typedef enum {
+    CSF_STACK_SYNC = 0,      /* layer l's set is predicted from layer l's own input             */
+    CSF_STACK_LOOKAHEAD = 1  /* layer l's set is predicted from layer l-1's input, on the side
+                                stream while layer l-1 runs (layer 0: from its own input)       */
+} csf_stack_mode;
+
+/* One block of a stack: predictor and FFN weights, shapes and layouts as for
+ * csf_sparse_ffn_layer (Wup only for CSF_ACT_REGLU, b1 optional). */
+typedef struct {
+    const void *V, *U, *W1, *Wup, *W2T;
+    const float *b1;
+} csf_layer_weights;
 
 /* Which rows each token of a batched call uses (csf_sparse_ffn_batched_union). */
 typedef enum {
@@ -232,14 +248,62 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
                                  void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer and
- * csf_sparse_ffn_batched_union (per calling thread).
+ * csf_sparse_ffn_batched_layer -- predict, select and the batched union FFN for B tokens in one
+ * enqueue: csf_predict_active, csf_select_topk (k >= 0) or csf_select_threshold (k == -1, tau)
+ * with bitmap output, then csf_sparse_ffn_batched_union.  Sources as those three.
+ *
+ *   X [B][d] dtype (1 <= B <= 32), predictor V [r][d] / U [f][r], FFN weights as above.
+ *   semantics, path, Y, union_count, path_taken as csf_sparse_ffn_batched_union.
+ *   bitmaps_out [B][(f+31)/32] uint32, optional: each token's selected set.
+ * Workspace: csf_workspace_size(CSF_OP_BATCHED_LAYER, B, d, f, r, k >= 0 ? k : f, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int act, int dtype,
+                                 const void *V, const void *U, const void *W1, const float *b1,
+                                 const void *Wup, const void *W2T, int k, float tau,
+                                 int semantics, int path, float *Y, uint32_t *bitmaps_out,
+                                 int32_t *union_count, int *path_taken, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_stack_forward -- L residual blocks, each a contextual-sparsity FFN, on a float32 stream.
+ * [CP] "Contextual Sparsity and Activation Predictors", section "The predictor and its budget":
+ *      a sequential predict-then-compute pipeline puts the predictor on the critical path of
+ *      every layer; predicting layer l+1's set from layer l's input and running that prediction
+ *      asynchronously hides it, because the residual stream changes slowly between blocks;
+ *      section "When it breaks": early layers are where that look-ahead is weakest.
+ *
+ *   layers    HOST array [L] of per-layer weight pointers (device memory); shapes d, f, r shared.
+ *   x         [B][d] float32  in: the stream entering layer 0; out: the stream after layer L-1.
+ *             For l = 0..L-1:  xhat_l = round(x_l / sqrt(mean(x_l^2) + eps)) (norm = 1) or
+ *             round(x_l) (norm = 0), in the weight type;  A_l = top-k (k >= 0) or threshold (k =
+ *             -1, tau) selection of predictor_l(xhat_l) (CSF_STACK_SYNC) or of predictor_l(xhat_{l-1})
+ *             (CSF_STACK_LOOKAHEAD, l >= 1);  x_{l+1} = x_l + sparse FFN_l(xhat_l over A_l).
+ *   mode      CSF_STACK_SYNC or CSF_STACK_LOOKAHEAD.  Look-ahead needs a side stream distinct from
+ *             `stream`; the call orders it with events, and all of its work is ordered before the
+ *             end of `stream`'s work, so synchronising `stream` is enough.
+ *   x_log     [L][B][d] float32, optional: x_l at the input of each layer.
+ *   xhat_log  [L][B][d] dtype, optional: xhat_l.
+ *   idx_log   [L][B][k or f] int32, optional: each layer's ascending active list.
+ *   count_log [L][B] int32, optional: each layer's list length.
+ * B >= 0 tokens, each with its own sets.  The library keeps 4 HIP events per device and calling
+ * thread (created on first use, never device memory of its own).
+ * Workspace: csf_workspace_size(CSF_OP_STACK, B, d, f, r, k >= 0 ? k : f, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
+                      int dtype, float *x, int B, int mode, int k, float tau, int norm, float eps,
+                      float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
+                      void *ws, size_t ws_bytes, void *stream, void *side_stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer,
+ * csf_sparse_ffn_batched_union and csf_sparse_ffn_batched_layer (per calling thread).
  * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record
  * events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
  * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
  * order -- csf_sparse_ffn_layer: predictor down-projection, predictor up-projection, selection,
  * gathered up/gate rows, gathered down rows (partial sums), reduction of the partial sums;
- * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction.
+ * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction;
+ * csf_sparse_ffn_batched_layer: the predictor's two kernels, selection, then the union's four.
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
  * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */

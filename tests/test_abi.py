@@ -151,6 +151,58 @@ def test_batched_union_validation():
     assert need >= 28672 * 4 + 32 * 28672 * 4 + 32 * 7168 * 4
 
 
+def test_batched_layer_validation():
+    taken = ctypes.c_int(-1)
+
+    def bl(k=5, tau=0.5, r=16, B=4, V=P, bm=NULL, path=0, wsb=1 << 26):
+        return L.csf_sparse_ffn_batched_layer(P, B, 256, 100, r, csf.RELU, csf.F16, V, P, P, NULL,
+                                              NULL, P, k, ctypes.c_float(tau), 0, path, P, bm,
+                                              NULL, ctypes.byref(taken), P, wsb, NULL)
+    assert bl(k=-2) == INVALID
+    assert bl(k=101) == INVALID
+    assert bl(k=-1, tau=float("nan")) == INVALID
+    assert bl(r=10) == UNSUPPORTED
+    assert bl(V=NULL) == INVALID
+    assert bl(bm=Q) == MISALIGNED
+    assert bl(B=40) == UNSUPPORTED
+    assert bl(wsb=64) == WS_SMALL
+    assert bl(B=0) == OK
+    lay = csf.workspace_size(_lib.OP_BATCHED_LAYER, 8, 7168, 28672, 512, 5734, csf.F16)
+    assert lay > csf.workspace_size(_lib.OP_BATCHED_UNION, 8, 7168, 28672, 0, 0, csf.F16) + 8 * 28672 * 4
+
+
+def test_stack_validation():
+    lw = (_lib.LayerWeights * 2)(_lib.LayerWeights(P.value, P.value, P.value, None, P.value, None),
+                                 _lib.LayerWeights(P.value, P.value, P.value, None, P.value, None))
+    S1, S2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)   # stand-in stream handles
+
+    def st(layers=lw, L=2, k=5, tau=0.5, mode=0, norm=1, eps=1e-6, x=P, B=1, side=NULL, wsb=1 << 26,
+           r=16, stream=NULL):
+        return L_.csf_stack_forward(layers, L, 256, 100, r, csf.RELU, csf.F16, x, B, mode, k,
+                                    ctypes.c_float(tau), norm, ctypes.c_float(eps), NULL, NULL,
+                                    NULL, NULL, P, wsb, stream, side)
+    L_ = L
+    assert st(L=-1) == INVALID
+    assert st(layers=None) == INVALID
+    assert st(mode=2) == INVALID
+    assert st(norm=2) == INVALID
+    assert st(eps=-1.0) == INVALID
+    assert st(mode=1) == INVALID                            # look-ahead without a side stream
+    assert st(mode=1, side=S1, stream=S1) == INVALID        # ... or with the main stream as side
+    assert st(k=101) == INVALID
+    assert st(k=-1, tau=float("nan")) == INVALID
+    assert st(r=10) == UNSUPPORTED
+    assert st(x=Q) == MISALIGNED
+    assert st(wsb=64) == WS_SMALL
+    bad = (_lib.LayerWeights * 2)(lw[0], _lib.LayerWeights(P.value, None, P.value, None, P.value,
+                                                           None))
+    assert st(layers=bad) == INVALID
+    assert b"layer 1" in L.csf_last_error()
+    assert st(L=0) == OK and st(B=0) == OK                  # nothing to do
+    need = csf.workspace_size(_lib.OP_STACK, 1, 7168, 28672, 512, 5734, csf.F16)
+    assert need >= 2 * 7168 * 2 + 2 * 28672 * 4 + 2 * 5734 * 4
+
+
 def test_k_from_ratio_matches_the_printed_figures():
     figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     for case in figs["k_from_ratio"]:

@@ -231,3 +231,32 @@ def test_batched_union_full_size_opt30b_shape(B, path):
         _, ref = orc.sparse_ffn(to_orc(X[t]), o["W1"], o["b1"], None, o["W2T"], sets[t],
                                 orc.RELU, orc.F16)
         assert_ffn_close(Y[t], ref, cfg.dtype, f"full B={B} token {t}")
+
+
+@pytest.mark.parametrize("name,cfg,B", [
+    ("f16-topk-B6", wl.CONFIGS[3].scaled(768, 2333, 64), 6),
+    ("bf16-reglu-threshold-B5", wl.CONFIGS[2].scaled(512, 1433, 64), 5),
+], ids=["f16-topk-B6", "bf16-reglu-threshold-B5"])
+def test_batched_layer_end_to_end(name, cfg, B):
+    """Predict + select + union FFN in one call: the selected sets (bitmaps) equal the oracle's
+    selection from the library's own scores, and Y matches the oracle over those sets."""
+    announce(f"batched layer {name}")
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    X = wl.make_clustered_tokens(cfg, B)
+    words = (cfg.f + 31) // 32
+    bm = torch.zeros(B, words, dtype=torch.int32, device=DEV)
+    for path in (csf.PATH_GATHER, csf.PATH_MFMA):
+        Y, taken = csf.sparse_ffn_batched_layer(X.to(DEV), Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T,
+                                                k=cfg.k, tau=cfg.tau, act=cfg.act, path=path,
+                                                bitmaps=bm)
+        scores = csf.predict_active(X.to(DEV), Ld.V, Ld.U)
+        torch.cuda.synchronize()
+        assert taken == path
+        sets = []
+        for t in range(B):
+            s = scores[t].cpu().numpy()
+            sel = orc.select_topk(s, cfg.k) if cfg.k is not None else orc.select_threshold(s, cfg.tau)
+            assert np.array_equal(bm[t].cpu().numpy().view(np.uint32), orc.to_bitmap(sel, cfg.f))
+            sets.append(sel)
+        _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"{name} path {path}")
