@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--batched-steps", type=int, default=256,
                     help="steps per (batch size, path) of the OPT-30B-shape batched leg (0: skip)")
     ap.add_argument("--batched-layers", type=int, default=4)
+    ap.add_argument("--stack-tokens", type=int, default=16,
+                    help="tokens timed through the 48-layer OPT-30B-shape stack (0: skip)")
+    ap.add_argument("--stack-layers", type=int, default=48)
+    ap.add_argument("--stack-quality-tokens", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -233,6 +237,11 @@ def main():
         torch.cuda.empty_cache()
         batched = batched_union_leg(args, dev)
 
+    stack = None
+    if args.stack_tokens > 0:
+        torch.cuda.empty_cache()
+        stack = stack_leg(args, dev)
+
     # ---- CPU oracle baseline (rank 0, bounded sample) ----------------------------------------
     cpu = None
     if not args.no_cpu:
@@ -275,13 +284,21 @@ def main():
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
         "batched_union": batched,
+        "stack": stack,
     }
     print(json.dumps(out), flush=True)
 
 
 PEAK_MFMA_F16_TFLOPS = 2500.0
-UNION_KERNELS = ["pred_down", "pred_up", "select_topk", "union_list", "union_up", "union_down",
-                 "reduce_partials"]
+UNION_KERNELS = ["union_list", "union_up", "union_down", "reduce_partials"]
+
+
+def predictor_kernels(B, dtype_code, d, r):
+    """Kernels the library's predictor launches for B tokens: the matrix-core form for batches of
+    4 or more 16-bit tokens with d and r multiples of 128, else the vector-ALU pair."""
+    if B >= 4 and dtype_code != 0 and d % 128 == 0 and r % 128 == 0:
+        return ["pred_down", "pred_hidden", "pred_up"]
+    return ["pred_down", "pred_up"]
 
 
 def batched_union_leg(args, dev):
@@ -353,7 +370,8 @@ def batched_union_leg(args, dev):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.batched_steps
             # per-kernel times (runtime-recorded start/end events)
-            nev = 2 * len(UNION_KERNELS)
+            names = predictor_kernels(B, code, d, r) + ["select_topk"] + UNION_KERNELS
+            nev = 2 * len(names)
             nt = min(64, args.batched_steps)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nt)]
             for rowe in evs:
@@ -366,7 +384,7 @@ def batched_union_leg(args, dev):
             csf.set_trace_events([])
             torch.cuda.synchronize()
             kern = {n: round(sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(nt))
-                             * 1e3 / nt, 2) for i, n in enumerate(UNION_KERNELS)}
+                             * 1e3 / nt, 2) for i, n in enumerate(names)}
             row[pname] = {"us_per_batch": round(us, 2), "tokens_per_s": round(B / us * 1e6, 1),
                           "GBps_touched": round(step_bytes / (us * 1e-6) / 1e9, 1),
                           "mfma_util": round(flops / (us * 1e-6) / (PEAK_MFMA_F16_TFLOPS * 1e12), 5),
@@ -401,6 +419,84 @@ def batched_union_leg(args, dev):
                         "predict + top-k + union FFN",
             "d": d, "f": f, "r": r, "k": k, "layers_rotated": nl, "steps": args.batched_steps,
             "rows": out}
+
+
+def stack_leg(args, dev):
+    """48 residual blocks of the OPT-30B FFN shape (d 7168, f 28672, r 512, top-k 5734; about
+    41 GB of weights), batch 1: tokens per second through the whole stack, synchronous vs
+    look-ahead prediction, and each layer's recall of the true active set (the ReLU neurons that
+    fire on that layer's actual normalised input)."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    cfg = wl.CONFIGS[4]
+    d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
+    nl = args.stack_layers
+    log(f"stack leg: {nl} layers of d={d} f={f} r={r}")
+    t0 = time.perf_counter()
+    layers = [wl.make_layer(cfg, device=dev, layer=l) for l in range(nl)]
+    torch.cuda.synchronize()
+    log(f"  weights drawn in {time.perf_counter() - t0:.1f} s")
+    ntok = max(args.stack_tokens, args.stack_quality_tokens) + 2
+    X = wl.make_tokens(cfg, ntok, device=dev).float()
+    side = torch.cuda.Stream(device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = _lib.dtype_code(cfg.dtype)
+    ws = torch.empty(csf.workspace_size(_lib.OP_STACK, 1, d, f, r, k, code), dtype=torch.uint8,
+                     device=dev)
+    x = torch.empty(1, d, dtype=torch.float32, device=dev)
+    res = {"workload": "48-layer OPT-30B-shape residual stack (pre-RMSNorm blocks), batch 1",
+           "layers": nl, "d": d, "f": f, "r": r, "k": k,
+           "bytes_per_token": nl * wl.touched_bytes(cfg, k)}
+    for mode, ahead in (("sync", False), ("lookahead", True)):
+        for t in range(2):
+            x.copy_(X[t:t + 1])
+            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        host = 0.0
+        e0.record(stream)
+        for t in range(args.stack_tokens):
+            x.copy_(X[2 + t:3 + t])
+            h0 = time.perf_counter()
+            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws)
+            host += time.perf_counter() - h0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.stack_tokens
+        res[mode] = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 2),
+                     "GBps_touched": round(res["bytes_per_token"] / (ms * 1e-3) / 1e9, 1),
+                     "us_per_layer": round(ms * 1e3 / nl, 2),
+                     "host_enqueue_ms_per_token": round(host * 1e3 / args.stack_tokens, 3)}
+        log(f"  {mode}: {ms:.3f} ms/token ({1e3 / ms:.1f} tok/s), host {host * 1e3 / args.stack_tokens:.3f} ms")
+        # recall of each layer's set against the true set at that layer's actual input
+        nq = args.stack_quality_tokens
+        if nq > 0:
+            xhat_log = torch.empty(nl, 1, d, dtype=cfg.dtype, device=dev)
+            idx_log = torch.empty(nl, 1, k, dtype=torch.int32, device=dev)
+            H = torch.empty(1, f, dtype=torch.float32, device=dev)
+            rec = torch.zeros(nl, dtype=torch.float64)
+            for t in range(nq):
+                x.copy_(X[t:t + 1])
+                csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws,
+                                  xhat_log=xhat_log, idx_log=idx_log)
+                for l in range(nl):
+                    L = layers[l]
+                    csf.dense_ffn(xhat_log[l], L.W1, L.b1, None, L.W2T, h=H)
+                    true = H[0] > 0
+                    nt = int(true.sum())
+                    hit = int(true[idx_log[l, 0].long()].sum())
+                    rec[l] += hit / nt if nt else 1.0
+            rec /= nq
+            res[mode]["recall_per_layer"] = [round(float(v), 4) for v in rec]
+            res[mode]["recall_mean"] = round(float(rec.mean()), 4)
+    del layers
+    torch.cuda.empty_cache()
+    res["lookahead_speedup"] = round(res["sync"]["ms_per_token"] / res["lookahead"]["ms_per_token"], 4)
+    res["dense_bound_tokens_per_s"] = round(8e12 / (nl * wl.dense_bytes(cfg)), 1)
+    res["sparse_bound_tokens_per_s"] = round(8e12 / res["bytes_per_token"], 1)
+    return res
 
 
 def cpu_baseline(cfg, L, X, ntok, touched):

@@ -103,6 +103,16 @@ int check_row(int n, int dtype, const char *name, long max_chunks)
     } while (0)
 
 // ---- workspace layouts -------------------------------------------------------------------------
+// predictor scratch: split-K partial vectors (vector-ALU path) or partial sums and the 16-bit
+// terms of the hidden activation (matrix-core path for batches), whichever is larger
+size_t pred_ws_bytes(int B, int r)
+{
+    const size_t Bn = B > 0 ? (size_t)B : 1;
+    const size_t v = (size_t)csf::kMaxPredSplit * Bn * r;
+    const size_t m = csf::pred_mfma_ws_floats((int)Bn, r);
+    return round_up((v > m ? v : m) * sizeof(float));
+}
+
 struct PredictWs {
     size_t a, total;
 };
@@ -110,8 +120,21 @@ PredictWs predict_ws(int B, int r)
 {
     PredictWs w;
     w.a = 0;
-    w.total = round_up((size_t)csf::kMaxPredSplit * B * r * sizeof(float));
+    w.total = pred_ws_bytes(B, r);
     return w;
+}
+
+// the predictor for B tokens: matrix cores for batches of 16-bit weights, else vector ALU
+hipError_t enqueue_predict(int dtype, const void *x, int B, int d, const void *V, int r,
+                           const void *U, int f, float *scores, float *ws, hipStream_t st,
+                           csf::Trace *tr)
+{
+    if (csf::pred_mfma_supported(dtype, B, d, r))
+        return csf::launch_predict_mfma(dtype, x, B, d, V, r, U, f, scores, ws, st, tr);
+    hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, ws, st, tr);
+    if (e != hipSuccess)
+        return e;
+    return csf::launch_pred_up(dtype, ws, B, d, r, U, f, scores, st, tr);
 }
 
 struct FfnWs {
@@ -178,7 +201,7 @@ BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int d
     BatchedLayerWs w;
     const size_t Bn = B > 0 ? (size_t)B : 1;
     w.a = 0;
-    w.scores = w.a + round_up((size_t)csf::kMaxPredSplit * Bn * r * sizeof(float));
+    w.scores = w.a + pred_ws_bytes(B, r);
     w.idx = w.scores + round_up(Bn * f * sizeof(float));
     w.count = w.idx + round_up(Bn * (max_count > 0 ? max_count : 1) * sizeof(int32_t));
     w.bitmap = w.count + round_up(Bn * sizeof(int32_t));
@@ -200,7 +223,7 @@ StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
         w.xhat[i] = o;
         o += round_up(Bn * d * elem_bytes(dtype));
     }
-    const size_t pa = round_up((size_t)csf::kMaxPredSplit * Bn * r * sizeof(float));
+    const size_t pa = pred_ws_bytes(B, r);
     const size_t ps = round_up(Bn * f * sizeof(float));
     w.a_main = o;
     o += pa;
@@ -431,11 +454,8 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
     CHECK_WS(ws, ws_bytes, w.total);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *a = reinterpret_cast<float *>(at(ws, w.a));
-    hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, a, st);
-    if (e != hipSuccess)
-        return hip_status(e, "predictor down-projection launch");
-    return hip_status(csf::launch_pred_up(dtype, a, B, d, r, U, f, scores, st),
-                      "predictor up-projection launch");
+    return hip_status(enqueue_predict(dtype, x, B, d, V, r, U, f, scores, a, st, nullptr),
+                      "predictor launch");
 }
 
 int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
@@ -626,12 +646,9 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
     int32_t *ix = reinterpret_cast<int32_t *>(at(ws, w.idx));
     int32_t *cn = reinterpret_cast<int32_t *>(at(ws, w.count));
     uint32_t *bm = bitmaps_out ? bitmaps_out : reinterpret_cast<uint32_t *>(at(ws, w.bitmap));
-    hipError_t e = csf::launch_pred_down(dtype, X, B, d, V, r, a, st, trp);
+    hipError_t e = enqueue_predict(dtype, X, B, d, V, r, U, f, sc, a, st, trp);
     if (e != hipSuccess)
-        return hip_status(e, "predictor down-projection launch");
-    e = csf::launch_pred_up(dtype, a, B, d, r, U, f, sc, st, trp);
-    if (e != hipSuccess)
-        return hip_status(e, "predictor up-projection launch");
+        return hip_status(e, "predictor launch");
     const int stride = max_count > 0 ? max_count : 1;
     if (k >= 0)
         e = csf::launch_select_topk(sc, B, f, k, ix, stride, cn, bm, st, trp);
@@ -787,9 +804,8 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
     auto predict_select = [&](int l, const void *xh, hipStream_t q, bool on_side) -> int {
         float *a = reinterpret_cast<float *>(at(ws, on_side ? w.a_side : w.a_main));
         float *sc = reinterpret_cast<float *>(at(ws, on_side ? w.s_side : w.s_main));
-        hipError_t e = csf::launch_pred_down(dtype, xh, B, d, layers[l].V, r, a, q);
-        if (e == hipSuccess)
-            e = csf::launch_pred_up(dtype, a, B, d, r, layers[l].U, f, sc, q);
+        hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
+                                       nullptr);
         if (e == hipSuccess) {
             if (k >= 0)
                 e = csf::launch_select_topk(sc, B, f, k, sel_idx(l), stride, sel_count(l), nullptr, q);

@@ -177,4 +177,45 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     return before + incl - v;
 }
 
+// Ascending list of the set bits of an LDS bitmap: out[wpos[w] + rank of bit b in word w] =
+// 32 w + b, where wpos (LDS) holds the exclusive prefix of the words' popcounts and `total` the
+// number of set bits.  A sparse bitmap (at most 12 bits per word on average) is emitted by the
+// words' owners, thread t walking the bits of words t wpt .. t wpt + wpt - 1; a denser one by half
+// wavefronts, one word each with lane b taking bit b, so that a wavefront's stores go to
+// consecutive addresses.  Both give the same list.  Positions >= cap are dropped.  Every thread of
+// the NT-thread block calls.
+template <int NT>
+__device__ __forceinline__ void emit_bit_list(const uint32_t *words, const uint32_t *wpos, int nwords,
+                                              uint32_t total, int32_t *out, int cap)
+{
+    if (total <= 12u * (uint32_t)nwords) {
+        const int wpt = (nwords + NT - 1) / NT;
+        for (int q = 0; q < wpt; ++q) {
+            const int w = threadIdx.x * wpt + q;
+            if (w >= nwords)
+                break;
+            uint32_t bits = words[w];
+            uint32_t p = wpos[w];
+            while (bits) {
+                const int b = __ffs(bits) - 1;
+                bits &= bits - 1;
+                if (p < (uint32_t)cap)
+                    out[p] = 32 * w + b;
+                ++p;
+            }
+        }
+        return;
+    }
+    const int half = threadIdx.x >> 5, bit = threadIdx.x & 31;
+#pragma unroll 4
+    for (int w = half; w < nwords; w += NT / 32) {
+        const uint32_t v = words[w];
+        if ((v >> bit) & 1u) {
+            const uint32_t p = wpos[w] + __popc(v & ((1u << bit) - 1u));
+            if (p < (uint32_t)cap)
+                out[p] = 32 * w + bit;
+        }
+    }
+}
+
 }  // namespace csf

@@ -53,6 +53,18 @@ hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
                           float *s, hipStream_t stream, Trace *trace = nullptr);
 
+// ---- predictor for a batch on the matrix cores (predict_mfma.hip) --------------------------
+constexpr int kPredMfmaMinBatch = 4;      // tokens from which the batched predictor is used
+constexpr int kMaxPredMfmaTokens = 32;    // tokens per pass (two 16-token MFMA tiles)
+constexpr int kMaxPredMfmaSplit = 32;     // split of d over workgroups in the down projection
+bool pred_mfma_supported(int dtype, int B, int d, int r);
+int pred_mfma_split(int r, int d);
+size_t pred_mfma_ws_floats(int B, int r);   // workspace (floats) of launch_predict_mfma
+// s[B][f] = sigmoid(U relu(V x)) for 16-bit weights; ws: pred_mfma_ws_floats(B, r) floats.
+hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const void *V, int r,
+                               const void *U, int f, float *s, float *ws, hipStream_t stream,
+                               Trace *trace = nullptr);
+
 // ---- selection (select.hip) -----------------------------------------------------------------
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap,

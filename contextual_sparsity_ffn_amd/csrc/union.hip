@@ -39,6 +39,7 @@ constexpr int kDownCols = 256;       // output columns per MFMA down workgroup (
 constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 bytes (8-byte aligned,
                                      // rows 8 apart fall 16 banks apart)
 constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
+constexpr int kMaxDownSteps = 64;    // K steps (of 32 union rows) per matrix-core down chunk
 
 // Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
 template <int MX, bool GATED>
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
                                                               int32_t *__restrict__ ucount_out)
 {
     __shared__ uint32_t scan_tmp[kUnionThreads / kWave];
+    __shared__ uint32_t ow[2 * kUnionThreads], opos[2 * kUnionThreads];   // OR words, prefixes
     const int t = threadIdx.x;
     const int words = (f + 31) / 32;
     const int wpt = (words + kUnionThreads - 1) / kUnionThreads;   // 1 or 2 (f <= 65536)
@@ -79,11 +81,11 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
             uint32_t v[kMaxUnionBatch];
 #pragma unroll
             for (int b = 0; b < kMaxUnionBatch; ++b)
-                v[b] = b < B ? bitmaps[(size_t)b * words + w] : 0u;
+                v[b] = bitmaps[(size_t)(b < B ? b : 0) * words + w];
             uint32_t o = 0u;
 #pragma unroll
             for (int b = 0; b < kMaxUnionBatch; ++b)
-                o |= v[b];
+                o |= b < B ? v[b] : 0u;
             if (w == words - 1 && (f & 31))
                 o &= (1u << (f & 31)) - 1u;          // bits past f are not neurons
             orw[q] = o;
@@ -94,14 +96,15 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
     uint32_t pos = block_exclusive_scan<kUnionThreads / kWave>(n, scan_tmp, &total);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        uint32_t bits = orw[q];
         const int w = t * wpt + q;
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            ulist[pos++] = w * 32 + b;
+        if (q < wpt && w < words) {
+            ow[w] = orw[q];
+            opos[w] = pos;
+            pos += __popc(orw[q]);
         }
     }
+    __syncthreads();
+    emit_bit_list<kUnionThreads>(ow, opos, words, total, ulist, f);
     if (t == 0) {
         *ucount = (int32_t)total;
         if (ucount_out)
@@ -274,9 +277,13 @@ __global__ __launch_bounds__(256) void k_union_down_valu(const u32x4 *__restrict
 // ---- matrix-core path --------------------------------------------------------------------------
 // One 16x16x32 MFMA: lane l holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
 // e < 8, and receives D[4 (l / 16) + i][l % 16], i < 4.  A = tokens x K, B = K x union rows.
-// The 4 waves of a workgroup take consecutive quarters of the K steps and are summed in wave
-// order through LDS.  MT = 16-token tiles (1 for B <= 16, 2 for B <= 32).
-template <class T, int MT, bool GATED>
+//
+// Up projection: a workgroup takes 16 NT union rows (the NT row tiles of a wave share each token
+// operand); its 4 waves take consecutive quarters of the K steps and are summed in wave order
+// through LDS.  Each wave keeps P K steps of loads in flight in a ring of registers and refills a
+// slot as soon as its MFMAs are issued.  Loads past the wave's last step or past the union re-read
+// a valid address and are zeroed, so the loop has no branches and its wait counts stay exact.
+template <class T, int MT, int NT, bool GATED, int P>
 __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__ X,
                                                        const u32x4 *__restrict__ W1,
                                                        const u32x4 *__restrict__ Wup,
@@ -289,8 +296,8 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
                                                        uint16_t *__restrict__ hlo, int hs)
 {
     constexpr int NV = GATED ? 2 : 1;
-    constexpr int UNR = 4;                       // K steps whose loads are in flight together
-    __shared__ float red[4][NV][MT * 4][kWave];
+    constexpr int ROWS = 16 * NT;
+    __shared__ float red[4][NV * NT][MT * 4][kWave];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int ln = lane & 15, g = lane >> 4;
     const int u = union_size(ucount, f);
@@ -298,76 +305,105 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
     const int words = (f + 31) / 32;
     const int steps = C / 4;                     // K steps of 32 elements (C = 16-byte chunks)
     const int s0 = w * steps / 4, s1 = (w + 1) * steps / 4;
+    const int groups = (s1 - s0 + P - 1) / P;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
-    for (int n0 = blockIdx.x * kTileRows; n0 < upad; n0 += gridDim.x * kTileRows) {
-        const int n = n0 + ln;
-        const int j = n < u ? ulist[n] : -1;
-        const size_t rb = (size_t)(j < 0 ? 0 : j) * C;
-        const u32x4 *xr[MT];
-        bool xok[MT];
+    const u32x4 *xr[MT];
+    bool xok[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int tok = 16 * m + ln;
-            xok[m] = tok < B;
-            xr[m] = X + (size_t)(xok[m] ? tok : 0) * C;
+    for (int m = 0; m < MT; ++m) {
+        const int tok = 16 * m + ln;
+        xok[m] = tok < B;
+        xr[m] = X + (size_t)(xok[m] ? tok : 0) * C;
+    }
+
+    for (int n0 = blockIdx.x * ROWS; n0 < upad; n0 += gridDim.x * ROWS) {
+        // this lane's row of each tile; a row past the union reads the tile's first row, zeroed
+        const int jclamp = ulist[n0 < u ? n0 : u - 1];
+        const u32x4 *wr[NV][NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int n = n0 + 16 * q + ln;
+            const size_t rb = (size_t)(n < u ? ulist[n] : jclamp) * C;
+            wr[0][q] = W1 + rb;
+            if constexpr (GATED)
+                wr[NV - 1][q] = Wup + rb;
         }
-        f32x4 acc[NV][MT];
+        f32x4 acc[NV][NT][MT];
 #pragma unroll
         for (int v = 0; v < NV; ++v)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                acc[v][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-        for (int s = s0; s < s1; s += UNR) {
-            u32x4 bw[NV][UNR], ax[MT][UNR];
-#pragma unroll
-            for (int q = 0; q < UNR; ++q) {
-                const int c = 4 * (s + q) + g;
-                const bool ok = s + q < s1;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const u32x4 *Wm = v == 0 ? W1 : Wup;
-                    bw[v][q] = (ok && j >= 0) ? ld_stream(Wm + rb + c) : u32x4{0u, 0u, 0u, 0u};
-                }
+            for (int q = 0; q < NT; ++q)
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    ax[m][q] = (ok && xok[m]) ? xr[m][c] : u32x4{0u, 0u, 0u, 0u};
+                    acc[v][q][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        // The ring holds raw loads; nothing reads a slot until its MFMAs, so the P steps stay in
+        // flight.  A row past the union only fills D columns the epilogue discards; a step past
+        // the wave's range (a clamped re-read) is cancelled by zeroing its token operand at use.
+        u32x4 rw[P][NV][NT], rx[P][MT];
+        auto fill = [&](int p, int st) {
+            const int c = 4 * (st < s1 ? st : s1 - 1) + g;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int q = 0; q < NT; ++q)
+                    rw[p][v][q] = ld_stream(wr[v][q] + c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                rx[p][m] = xr[m][c];
+        };
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            fill(p, s0 + p);
+        for (int gi = 0; gi < groups; ++gi) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const bool ok = s0 + gi * P + p < s1;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const u32x4 a = (ok && xok[m]) ? rx[p][m] : zero;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int q = 0; q < NT; ++q)
+                            acc[v][q][m] = T::mfma(a, rw[p][v][q], acc[v][q][m]);
+                }
+                fill(p, s0 + (gi + 1) * P + p);
             }
-#pragma unroll
-            for (int q = 0; q < UNR; ++q)
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        acc[v][m] = T::mfma(ax[m][q], bw[v][q], acc[v][m]);
         }
 
 #pragma unroll
         for (int v = 0; v < NV; ++v)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int q = 0; q < NT; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[w][v][m * 4 + i][lane] = acc[v][m][i];
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[w][v * NT + q][m * 4 + i][lane] = acc[v][q][m][i];
         __syncthreads();
-        // thread e covers D element (m, i, lane) = e: token 16 m + 4 (lane / 16) + i, row lane % 16
-        for (int e = t; e < MT * 4 * kWave; e += 256) {
-            const int mi = e / kWave, l = e % kWave;
+        // thread e covers D element (tile q, m, i, lane): token 16 m + 4 (lane / 16) + i, row
+        // n0 + 16 q + lane % 16
+        for (int e = t; e < NT * MT * 4 * kWave; e += 256) {
+            const int q = e / (MT * 4 * kWave);
+            const int mi = (e / kWave) % (MT * 4), l = e % kWave;
             const int m = mi / 4, i = mi % 4;
             const int tok = 16 * m + 4 * (l >> 4) + i;
-            const int nn = n0 + (l & 15);
+            const int nn = n0 + 16 * q + (l & 15);
             if (tok >= B || nn >= upad)
                 continue;
             float hv = 0.0f;
             if (nn < u) {
                 const int jj = ulist[nn];
-                float p = (red[0][0][mi][l] + red[1][0][mi][l]) + (red[2][0][mi][l] + red[3][0][mi][l]);
+                float p = (red[0][q][mi][l] + red[1][q][mi][l]) + (red[2][q][mi][l] + red[3][q][mi][l]);
                 if (b1)
                     p += b1[jj];
                 hv = p > 0.0f ? p : 0.0f;
-                if constexpr (GATED)
-                    hv *= (red[0][NV - 1][mi][l] + red[1][NV - 1][mi][l]) +
-                          (red[2][NV - 1][mi][l] + red[3][NV - 1][mi][l]);
+                if constexpr (GATED) {
+                    const int qv = NT + q;
+                    hv *= (red[0][qv][mi][l] + red[1][qv][mi][l]) + (red[2][qv][mi][l] + red[3][qv][mi][l]);
+                }
                 if (per_token && !token_has(bitmaps, words, tok, jj))
                     hv = 0.0f;
             }
@@ -380,11 +416,13 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
     }
 }
 
-// Grid (256-column tile, union chunk).  Per K step of 32 union rows the workgroup stages the
-// rows' 512-byte column segments in LDS (double-buffered, the next step's global loads in flight
-// during this step's products); wave w then multiplies columns 64 w .. 64 w + 63 as 4 tiles of 16:
-// A = h (tokens x 32 rows, hi and lo), B = staged rows read column-wise.
-template <class T, int MT>
+// Down projection.  Grid (256-column tile, union chunk).  The chunk's union indices are staged in
+// LDS first.  Per K step of 32 union rows the workgroup stages the rows' 512-byte column segments
+// and the 32 rows' h values (hi and lo, every token) in LDS, double-buffered, with the global
+// loads of the next PD steps in flight in a register ring; wave w then multiplies columns
+// 64 w .. 64 w + 63 as 4 tiles of 16: A = h (tokens x 32 rows, hi then lo), B = the staged rows
+// read column-wise (W2T is contiguous along the output columns, the product contracts over rows).
+template <class T, int MT, int PD>
 __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict__ W2T,
                                                          const uint16_t *__restrict__ hhi,
                                                          const uint16_t *__restrict__ hlo,
@@ -395,8 +433,9 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
                                                          float *__restrict__ part)
 {
     constexpr int SEG = kDownCols / 8;            // 16-byte chunks per staged row segment: 32
-    constexpr int LPR = 256 / kKStep;             // loads per thread per step: 32 rows x 32 / 256
     __shared__ __align__(16) uint16_t tile[2][kKStep][kDownLdsStride];
+    __shared__ __align__(16) uint16_t hst[2][2][kMaxUnionBatch][kKStep];   // [buf][hi/lo][tok][row]
+    __shared__ int32_t rows[kMaxDownSteps * kKStep];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int ln = lane & 15, g = lane >> 4;
     const int D = C * 8;
@@ -407,28 +446,45 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
     const int per = (steps + nchunk - 1) / nchunk;
     const int sb = chunk * per;
     const int se = sb + per < steps ? sb + per : steps;
+    const int ns = se > sb ? se - sb : 0;         // <= kMaxDownSteps (the host sizes nchunk)
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
-    // thread t stages rows (t / SEG) + 8 q, q < LPR / ... : 256 threads cover 8 rows x 32 chunks
+    // union indices of this chunk (positions past the union read the last entry; their h is 0)
+    for (int i = t; i < ns * kKStep; i += 256) {
+        const int nn = sb * kKStep + i;
+        rows[i] = ulist[nn < u ? nn : u - 1];
+    }
+    __syncthreads();
+
+    // staging: thread t moves rows srow + 8 q (q < 4) of column chunk scol, and one 16-byte
+    // piece of h: token ht, rows 8 hg .. 8 hg + 7, hi (hl = 0) or lo (hl = 1)
     const int srow = t / SEG, scol = t % SEG;
-    auto load_step = [&](int s, u32x4 *r) {
+    const int hl = t >> 7, ht = (t >> 2) & 31, hg = t & 3;
+    const bool hok = ht < B;
+    const uint16_t *hsrc = (hl ? hlo : hhi) + (size_t)(hok ? ht : 0) * hs + 8 * hg;
+    // The ring holds raw loads (a step past the chunk re-reads its last step); they are only
+    // read when staged, PD - 1 steps later, where a step past the chunk stages h = 0 (so the
+    // re-read rows add nothing) and a token past B stages h = 0.
+    u32x4 rw[PD][kKStep / 8], rh[PD];
+    auto fill = [&](int p, int i) {            // i: step index within the chunk
+        const int ic = i < ns ? i : ns - 1;
 #pragma unroll
         for (int q = 0; q < kKStep / 8; ++q) {
-            const int nn = s * kKStep + srow + 8 * q;
-            const int j = nn < u ? ulist[nn] : 0;
-            r[q] = nn < u ? ld_stream(W2T + (size_t)j * C + (col0 / 8) + scol)
-                          : u32x4{0u, 0u, 0u, 0u};
+            const int r = ic * kKStep + srow + 8 * q;
+            rw[p][q] = ld_stream(W2T + (size_t)rows[r] * C + (col0 / 8) + scol);
         }
+        rh[p] = *reinterpret_cast<const u32x4 *>(hsrc + (size_t)(sb + ic) * kKStep);
     };
-    auto store_step = [&](int buf, const u32x4 *r) {
+    auto stage = [&](int p, int buf, int i) {
 #pragma unroll
         for (int q = 0; q < kKStep / 8; ++q) {
             uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[buf][srow + 8 * q][scol * 8]);
             // two 8-byte stores: the staged row stride is 8-byte aligned only
-            *reinterpret_cast<uint2 *>(dst) = uint2{r[q].x, r[q].y};
-            *reinterpret_cast<uint2 *>(dst + 2) = uint2{r[q].z, r[q].w};
+            *reinterpret_cast<uint2 *>(dst) = uint2{rw[p][q].x, rw[p][q].y};
+            *reinterpret_cast<uint2 *>(dst + 2) = uint2{rw[p][q].z, rw[p][q].w};
         }
+        *reinterpret_cast<u32x4 *>(&hst[buf][hl][ht][8 * hg]) = (i < ns && hok) ? rh[p] : zero;
     };
-    (void)LPR;
 
     f32x4 acc[4][MT];
 #pragma unroll
@@ -437,43 +493,47 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
         for (int m = 0; m < MT; ++m)
             acc[q][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    u32x4 nxt[kKStep / 8];
-    if (sb < se) {
-        load_step(sb, nxt);
-        store_step(0, nxt);
-    }
-    __syncthreads();
-    for (int s = sb; s < se; ++s) {
-        const int buf = (s - sb) & 1;
-        if (s + 1 < se)
-            load_step(s + 1, nxt);
-        // A operands: h[token][32 s + 8 g .. + 8], hi and lo
-        u32x4 ahi[MT], alo[MT];
+    if (ns > 0) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int tok = 16 * m + ln;
-            const size_t off = (size_t)(tok < B ? tok : 0) * hs + (size_t)s * kKStep + 8 * g;
-            ahi[m] = tok < B ? *reinterpret_cast<const u32x4 *>(hhi + off) : u32x4{0u, 0u, 0u, 0u};
-            alo[m] = tok < B ? *reinterpret_cast<const u32x4 *>(hlo + off) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int p = 0; p < PD; ++p)
+            fill(p, p);
+        stage(0, 0, 0);
+        __syncthreads();
+        const int groups = (ns + PD - 1) / PD;
+        for (int gi = 0; gi < groups; ++gi) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int cc = 64 * w + 16 * q + ln;
-            uint32_t bv[4];
+            for (int p = 0; p < PD; ++p) {
+                const int i = gi * PD + p;
+                const int buf = i & 1;
+                // slot p (step i) is already in LDS: refill it with step i + PD (the barrier keeps
+                // the scheduler from sinking these loads toward the staging)
+                fill(p, i + PD);
+                __builtin_amdgcn_sched_barrier(0);
+                u32x4 ahi[MT], alo[MT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                bv[e] = (uint32_t)tile[buf][8 * g + 2 * e][cc] |
-                        ((uint32_t)tile[buf][8 * g + 2 * e + 1][cc] << 16);
-            const u32x4 b = u32x4{bv[0], bv[1], bv[2], bv[3]};
+                for (int m = 0; m < MT; ++m) {
+                    ahi[m] = *reinterpret_cast<const u32x4 *>(&hst[buf][0][16 * m + ln][8 * g]);
+                    alo[m] = *reinterpret_cast<const u32x4 *>(&hst[buf][1][16 * m + ln][8 * g]);
+                }
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                acc[q][m] = T::mfma(ahi[m], b, acc[q][m]);
-                acc[q][m] = T::mfma(alo[m], b, acc[q][m]);
+                for (int q = 0; q < 4; ++q) {
+                    const int cc = 64 * w + 16 * q + ln;
+                    uint32_t bv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bv[e] = (uint32_t)tile[buf][8 * g + 2 * e][cc] |
+                                ((uint32_t)tile[buf][8 * g + 2 * e + 1][cc] << 16);
+                    const u32x4 b = u32x4{bv[0], bv[1], bv[2], bv[3]};
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        acc[q][m] = T::mfma(ahi[m], b, acc[q][m]);
+                        acc[q][m] = T::mfma(alo[m], b, acc[q][m]);
+                    }
+                }
+                stage((p + 1) % PD, buf ^ 1, i + 1);   // step i + 1
+                __syncthreads();
             }
         }
-        if (s + 1 < se)
-            store_step(buf ^ 1, nxt);
-        __syncthreads();
     }
 
     // D[4 g + i][ln] of tile (q, m): token 16 m + 4 g + i, column col0 + 64 w + 16 q + ln
@@ -543,27 +603,30 @@ hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
     return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.Y, st, tr);
 }
 
-template <class T, int MT>
+template <class T, int MT, int NT>
 hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / 8;
-    const int tiles = (a.f + kKStep - 1) / kKStep * (kKStep / kTileRows);
+    constexpr int ROWS = 16 * NT;
+    const int tiles = (a.f + kKStep - 1) / kKStep * kKStep / ROWS;
     const int blocks = tiles < 4096 ? tiles : 4096;
     hipError_t e;
     if (a.act == 1)
-        e = launch(k_union_up_mfma<T, MT, true>, dim3(blocks), dim3(256), st, tr,
-                   static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
-                   static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
-                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
+        e = launch(k_union_up_mfma<T, MT, 1, true, 4>, dim3((a.f + kKStep - 1) / kKStep * 2 < 4096
+                                                               ? (a.f + kKStep - 1) / kKStep * 2
+                                                               : 4096),
+                   dim3(256), st, tr, static_cast<const u32x4 *>(a.X),
+                   static_cast<const u32x4 *>(a.W1), static_cast<const u32x4 *>(a.Wup), a.b1,
+                   a.ulist, a.ucount, a.bitmaps, a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
     else
-        e = launch(k_union_up_mfma<T, MT, false>, dim3(blocks), dim3(256), st, tr,
+        e = launch(k_union_up_mfma<T, MT, NT, false, 4>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
                    a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
     if (e != hipSuccess)
         return e;
     const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f);
-    e = launch(k_union_down_mfma<T, MT>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
+    e = launch(k_union_down_mfma<T, MT, 3>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
                static_cast<const u32x4 *>(a.W2T), a.hhi, a.hlo, a.hs, a.ulist, a.ucount, a.B, a.f,
                C, nchunk, a.partials);
     if (e != hipSuccess)
@@ -574,9 +637,12 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
 template <class T>
 hipError_t union_mfma(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
+    // two row tiles per wave share each token operand once the union is large (B >= 8)
+    if (a.B <= 7)
+        return union_mfma_mt<T, 1, 1>(a, st, tr);
     if (a.B <= 16)
-        return union_mfma_mt<T, 1>(a, st, tr);
-    return union_mfma_mt<T, 2>(a, st, tr);
+        return union_mfma_mt<T, 1, 2>(a, st, tr);
+    return union_mfma_mt<T, 2, 2>(a, st, tr);
 }
 
 }  // namespace
@@ -590,15 +656,18 @@ int union_num_chunks(int mfma, int d, int dtype, int f)
 {
     if (!mfma)
         return ffn_num_chunks(d, dtype, f);
-    // about 512 workgroups of 256 columns; the partial rows (B x chunks x d float32) stay a few
-    // percent of the weight bytes
+    // about 768 workgroups of 256 columns (3 per CU); the partial rows (B x chunks x d float32)
+    // stay a few percent of the weight bytes; a chunk holds at most kMaxDownSteps K steps
     const int tiles = d / kDownCols > 0 ? d / kDownCols : 1;
-    int n = (512 + tiles - 1) / tiles;
     const int steps = (f + kKStep - 1) / kKStep;
+    int n = (768 + tiles - 1) / tiles;
+    const int least = (steps + kMaxDownSteps - 1) / kMaxDownSteps;
     if (n > steps)
         n = steps;
     if (n > 64)
         n = 64;
+    if (n < least)
+        n = least;
     return n < 1 ? 1 : n;
 }
 

@@ -37,6 +37,12 @@ PRED_CASES = [
     ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 2),
     ("bf16", wl.CONFIGS[2].scaled(4096, 1433, 256), 2),
     ("f16-r1024", wl.CONFIGS[1].scaled(1024, 2050, 1024), 1),
+    # batches of 4 or more 16-bit tokens with d, r multiples of 128 take the matrix-core predictor
+    ("f16-B8-mfma", wl.CONFIGS[3].scaled(1024, 2333, 128), 8),
+    ("bf16-B20-mfma", wl.CONFIGS[2].scaled(512, 1433, 256), 20),
+    ("f16-B37-mfma", wl.CONFIGS[1].scaled(1024, 1000, 256), 37),
+    ("f16-B5-r1024-mfma", wl.CONFIGS[1].scaled(2048, 3001, 1024), 5),
+    ("f16-B6-ragged-valu", wl.CONFIGS[1].scaled(2600, 3001, 136), 6),
 ]
 
 
