@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--batched-steps", type=int, default=256,
                     help="steps per (batch size, path) of the OPT-30B-shape batched leg (0: skip)")
     ap.add_argument("--batched-layers", type=int, default=4)
+    ap.add_argument("--batched-sizes", default="1,4,8,16,32",
+                    help="comma-separated batch sizes of the batched leg")
     ap.add_argument("--stack-tokens", type=int, default=16,
                     help="tokens timed through the 48-layer OPT-30B-shape stack (0: skip)")
     ap.add_argument("--stack-layers", type=int, default=48)
@@ -327,7 +329,7 @@ def batched_union_leg(args, dev):
     full_bm[:, -1] = (1 << (f % 32)) - 1 if f % 32 else -1
     pred_bytes = 2 * (r * d + f * r)
     out = []
-    for B in (1, 4, 8, 16, 32):
+    for B in [int(b) for b in args.batched_sizes.split(",") if b]:
         Y = torch.empty(B, d, dtype=torch.float32, device=dev)
         uc = torch.zeros(1, dtype=torch.int32, device=dev)
         ws_b = csf.workspace_size(_lib.OP_BATCHED_LAYER, B, d, f, r, k, code)

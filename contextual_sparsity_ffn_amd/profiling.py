@@ -14,7 +14,7 @@ Counter scaling: FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Ea
 the ratio of the known size of a plain device copy (the benchmark's --copy-calibration leg, a
 1 GiB copy) to what the same counter reads for that copy.
 
-    python -m contextual_sparsity_ffn_amd.profiling stats DIR/layer_kernel_stats.csv OUT.md "CMD"
+    python -m contextual_sparsity_ffn_amd.profiling stats DIR/layer_kernel_stats.csv OUT.md "CMD" ["TITLE"]
     python -m contextual_sparsity_ffn_amd.profiling counters FETCH.csv WRITE.csv OUT.json OUT.md "CMD"
 """
 from __future__ import annotations
@@ -34,7 +34,12 @@ COPY_BYTES = 1 << 30
 # kernel-name prefix -> label used by the benchmark
 LABELS = [("k_pred_down", "pred_down"), ("k_pred_up", "pred_up"), ("k_select_topk", "select_topk"),
           ("k_select_threshold", "select_threshold"), ("k_gather_up", "gather_up"),
-          ("k_gather_down", "gather_down"), ("k_reduce_partials", "reduce_partials")]
+          ("k_gather_down", "gather_down"), ("k_reduce_partials", "reduce_partials"),
+          ("k_pred_down_mfma", "pred_down_mfma"), ("k_pred_hidden", "pred_hidden"),
+          ("k_pred_up_mfma", "pred_up_mfma"), ("k_union_list", "union_list"),
+          ("k_union_up_valu", "union_up_valu"), ("k_union_down_valu", "union_down_valu"),
+          ("k_union_up_mfma", "union_up_mfma"), ("k_union_down_mfma", "union_down_mfma"),
+          ("k_rms_norm", "rms_norm")]
 
 
 def source_hash() -> str:
@@ -54,7 +59,8 @@ def label_of(name: str):
     return None
 
 
-def summarize_kernel_stats(stats_csv: str, out_md: str, command: str) -> None:
+def summarize_kernel_stats(stats_csv: str, out_md: str, command: str,
+                           title: str = "contextual-sparsity layer kernels") -> None:
     rows = []
     with open(stats_csv) as fh:
         for r in csv.DictReader(fh):
@@ -64,7 +70,7 @@ def summarize_kernel_stats(stats_csv: str, out_md: str, command: str) -> None:
                              float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Name"]))
     rows.sort(key=lambda t: -t[1] * t[2])
     with open(out_md, "w") as out:
-        out.write("# rocprofv3 kernel statistics: contextual-sparsity layer kernels\n\n")
+        out.write(f"# rocprofv3 kernel statistics: {title}\n\n")
         out.write(f"Command (repository root):\n\n    {command}\n\n")
         out.write(f"Kernel source sha256: `{source_hash()}`\n\n")
         out.write("| kernel | calls | avg us | min us | max us |\n|---|---:|---:|---:|---:|\n")
@@ -135,7 +141,7 @@ def load_counters(path: str):
 
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "stats":
-        summarize_kernel_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+        summarize_kernel_stats(sys.argv[2], sys.argv[3], sys.argv[4], *sys.argv[5:6])
     elif len(sys.argv) >= 2 and sys.argv[1] == "counters":
         summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
     else:
