@@ -451,10 +451,11 @@ def stack_leg(args, dev):
     res = {"workload": "48-layer OPT-30B-shape residual stack (pre-RMSNorm blocks), batch 1",
            "layers": nl, "d": d, "f": f, "r": r, "k": k,
            "bytes_per_token": nl * wl.touched_bytes(cfg, k)}
-    for mode, ahead in (("sync", False), ("lookahead", True)):
+    for mode, ahead, graph in (("sync", False, False), ("lookahead", True, False),
+                               ("sync_graph", False, True), ("lookahead_graph", True, True)):
         for t in range(2):
             x.copy_(X[t:t + 1])
-            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws)
+            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws, graph=graph)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         host = 0.0
@@ -462,7 +463,7 @@ def stack_leg(args, dev):
         for t in range(args.stack_tokens):
             x.copy_(X[2 + t:3 + t])
             h0 = time.perf_counter()
-            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws)
+            csf.stack_forward(x, layers, k=k, lookahead=ahead, side_stream=side, ws=ws, graph=graph)
             host += time.perf_counter() - h0
         e1.record(stream)
         torch.cuda.synchronize()
@@ -473,7 +474,7 @@ def stack_leg(args, dev):
                      "host_enqueue_ms_per_token": round(host * 1e3 / args.stack_tokens, 3)}
         log(f"  {mode}: {ms:.3f} ms/token ({1e3 / ms:.1f} tok/s), host {host * 1e3 / args.stack_tokens:.3f} ms")
         # recall of each layer's set against the true set at that layer's actual input
-        nq = args.stack_quality_tokens
+        nq = args.stack_quality_tokens if not graph else 0
         if nq > 0:
             xhat_log = torch.empty(nl, 1, d, dtype=cfg.dtype, device=dev)
             idx_log = torch.empty(nl, 1, k, dtype=torch.int32, device=dev)
@@ -496,6 +497,8 @@ def stack_leg(args, dev):
     del layers
     torch.cuda.empty_cache()
     res["lookahead_speedup"] = round(res["sync"]["ms_per_token"] / res["lookahead"]["ms_per_token"], 4)
+    res["lookahead_graph_speedup"] = round(res["sync_graph"]["ms_per_token"] /
+                                           res["lookahead_graph"]["ms_per_token"], 4)
     res["dense_bound_tokens_per_s"] = round(8e12 / (nl * wl.dense_bytes(cfg)), 1)
     res["sparse_bound_tokens_per_s"] = round(8e12 / res["bytes_per_token"], 1)
     return res

@@ -20,7 +20,7 @@ F32, F16, BF16 = 0, 1, 2
 RELU, REGLU = 0, 1
 OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
     OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK = range(9)
-STACK_SYNC, STACK_LOOKAHEAD = 0, 1
+STACK_SYNC, STACK_LOOKAHEAD, STACK_GRAPH = 0, 1, 0x100
 SEM_PER_TOKEN, SEM_UNION = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_MFMA = 0, 1, 2
 MAX_UNION_BATCH = 32
@@ -388,10 +388,12 @@ def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RE
 
 def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=True, eps=1e-6,
                   x_log=None, xhat_log=None, idx_log=None, count_log=None, side_stream=None,
-                  ws=None):
+                  ws=None, graph=False):
     """Run x [B, d] (float32, updated in place) through the residual blocks `layers` (objects with
     V, U, W1, b1, Wup, W2T device tensors).  lookahead: each layer's set is predicted from the
-    previous layer's input on `side_stream` (a torch.cuda.Stream; required).  Returns x."""
+    previous layer's input on `side_stream` (a torch.cuda.Stream; required).  graph: enqueue the
+    stack as one replayed HIP graph (captured when the arguments change; pass the same `ws` and
+    tensors to reuse it).  Returns x."""
     if (k is None) == (tau is None):
         raise ValueError("give exactly one of k (top-k) or tau (threshold)")
     _tensor(x, "x", dtype=torch.float32)
@@ -427,7 +429,8 @@ def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=T
     w, wb = _workspace(workspace_size(OP_STACK, B, d, f, r, max_count, code), dev, ws)
     side = None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)
     _check(lib.csf_stack_forward(arr, nl, d, f, r, act, code, _ptr(x), B,
-                                 STACK_LOOKAHEAD if lookahead else STACK_SYNC, kk,
+                                 (STACK_LOOKAHEAD if lookahead else STACK_SYNC) |
+                                 (STACK_GRAPH if graph else 0), kk,
                                  float(tau if tau is not None else 0.0), 1 if norm else 0,
                                  float(eps), _ptr(x_log), _ptr(xhat_log), _ptr(idx_log),
                                  _ptr(count_log), _ptr(w), wb, _stream(dev), side))

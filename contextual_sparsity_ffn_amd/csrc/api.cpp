@@ -376,6 +376,133 @@ int stack_events(hipEvent_t ev_x[2], hipEvent_t ev_s[2])
     return CSF_OK;
 }
 
+// One captured stack per calling thread, replayed while the arguments stay the same.  It is
+// captured on a stream of the library's own (one per device and thread; the caller's stream may
+// be the legacy default stream, which cannot be captured) and launched on the caller's stream.
+struct StackGraph {
+    uint64_t key = 0;
+    hipGraphExec_t exec = nullptr;
+};
+thread_local StackGraph g_stack_graph;
+
+int capture_stream(int dev, hipStream_t *out)
+{
+    constexpr int kMaxDevices = 64;
+    thread_local hipStream_t streams[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond this build's limit", dev);
+    if (!streams[dev]) {
+        hipError_t e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            streams[dev] = nullptr;
+            return hip_status(e, "hipStreamCreateWithFlags");
+        }
+    }
+    *out = streams[dev];
+    return CSF_OK;
+}
+
+int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
+                  int dtype, float *x, int B, int sched, int k, float tau, int norm, float eps,
+                  float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log, void *ws,
+                  hipStream_t st, hipStream_t side)
+{
+    const int max_count = k >= 0 ? k : f;
+    const int stride = max_count > 0 ? max_count : 1;
+    StackWs w = stack_ws(B, d, f, r, max_count, dtype);
+    const bool ahead = sched == CSF_STACK_LOOKAHEAD;
+    hipEvent_t ev_x[2] = {nullptr, nullptr}, ev_s[2] = {nullptr, nullptr};
+    if (ahead) {
+        int s = stack_events(ev_x, ev_s);
+        if (s != CSF_OK)
+            return s;
+    }
+    const size_t es = elem_bytes(dtype);
+    FfnWs fw = ffn_ws(B, d, dtype, max_count);
+
+    auto sel_idx = [&](int l) {
+        return idx_log ? idx_log + (size_t)l * B * stride
+                       : reinterpret_cast<int32_t *>(at(ws, w.idx[l & 1]));
+    };
+    auto sel_count = [&](int l) {
+        return count_log ? count_log + (size_t)l * B
+                         : reinterpret_cast<int32_t *>(at(ws, w.count[l & 1]));
+    };
+    // predictor of layer `l` applied to `xh`, then the selection, on stream `q`
+    auto predict_select = [&](int l, const void *xh, hipStream_t q, bool on_side) -> int {
+        float *a = reinterpret_cast<float *>(at(ws, on_side ? w.a_side : w.a_main));
+        float *sc = reinterpret_cast<float *>(at(ws, on_side ? w.s_side : w.s_main));
+        hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
+                                       nullptr);
+        if (e == hipSuccess) {
+            if (k >= 0)
+                e = csf::launch_select_topk(sc, B, f, k, sel_idx(l), stride, sel_count(l), nullptr, q);
+            else
+                e = csf::launch_select_threshold(sc, B, f, tau, sel_idx(l), stride, sel_count(l),
+                                                 nullptr, q);
+        }
+        return hip_status(e, "stack predictor/selection launch");
+    };
+
+    for (int l = 0; l < L; ++l) {
+        void *xh = at(ws, w.xhat[l & 1]);
+        hipError_t e = csf::launch_rms_norm(
+            dtype, x, B, d, eps, norm, xh, x_log ? x_log + (size_t)l * B * d : nullptr,
+            xhat_log ? static_cast<char *>(xhat_log) + (size_t)l * B * d * es : nullptr, st);
+        if (e != hipSuccess)
+            return hip_status(e, "stack normalisation launch");
+        int s = CSF_OK;
+        if (!ahead || l == 0)
+            s = predict_select(l, xh, st, false);
+        if (s != CSF_OK)
+            return s;
+        if (ahead && l + 1 < L) {
+            // layer l+1's set from this layer's input, on the side stream, while this layer runs
+            e = hipEventRecord(ev_x[l & 1], st);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(side, ev_x[l & 1], 0);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+            s = predict_select(l + 1, xh, side, true);
+            if (s != CSF_OK)
+                return s;
+            e = hipEventRecord(ev_s[(l + 1) & 1], side);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+        }
+        if (ahead && l > 0) {
+            e = hipStreamWaitEvent(st, ev_s[l & 1], 0);
+            if (e != hipSuccess)
+                return hip_status(e, "stack event");
+        }
+        csf::FfnArgs fa;
+        fa.dtype = dtype;
+        fa.act = act;
+        fa.x = xh;
+        fa.B = B;
+        fa.d = d;
+        fa.f = f;
+        fa.W1 = layers[l].W1;
+        fa.Wup = layers[l].Wup;
+        fa.W2T = layers[l].W2T;
+        fa.b1 = layers[l].b1;
+        fa.idx = sel_idx(l);
+        fa.idx_stride = stride;
+        fa.count = k >= 0 ? nullptr : sel_count(l);
+        fa.max_count = max_count;
+        fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+        fa.h_stride = stride;
+        fa.y = x;
+        fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+        fa.accumulate = 1;
+        e = csf::launch_ffn(fa, st);
+        if (e != hipSuccess)
+            return hip_status(e, "stack FFN launch");
+    }
+    return ok();
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -745,11 +872,12 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
 {
     REQUIRE(L >= 0, CSF_ERR_INVALID_ARG, "L must be >= 0 (got %d)", L);
     REQUIRE(L == 0 || layers, CSF_ERR_INVALID_ARG, "layers must not be NULL when L > 0");
-    REQUIRE(mode == CSF_STACK_SYNC || mode == CSF_STACK_LOOKAHEAD, CSF_ERR_INVALID_ARG,
+    const int sched = mode & ~CSF_STACK_GRAPH;
+    REQUIRE(sched == CSF_STACK_SYNC || sched == CSF_STACK_LOOKAHEAD, CSF_ERR_INVALID_ARG,
             "unknown stack mode %d", mode);
     REQUIRE(norm == 0 || norm == 1, CSF_ERR_INVALID_ARG, "norm must be 0 or 1 (got %d)", norm);
     REQUIRE(eps >= 0.0f && eps < 1e30f, CSF_ERR_INVALID_ARG, "eps must be finite and >= 0");
-    REQUIRE(mode == CSF_STACK_SYNC || (side_stream && side_stream != stream), CSF_ERR_INVALID_ARG,
+    REQUIRE(sched == CSF_STACK_SYNC || (side_stream && side_stream != stream), CSF_ERR_INVALID_ARG,
             "look-ahead needs a side stream distinct from the main stream");
     for (int l = 0; l < L; ++l) {
         int s = validate_ffn(x, B, d, f, act, dtype, layers[l].W1, layers[l].b1, layers[l].Wup,
@@ -777,101 +905,67 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
     if (L == 0 || B == 0)
         return ok();
     const int max_count = k >= 0 ? k : f;
-    const int stride = max_count > 0 ? max_count : 1;
-    StackWs w = stack_ws(B, d, f, r, max_count, dtype);
-    CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_WS(ws, ws_bytes, stack_ws(B, d, f, r, max_count, dtype).total);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipStream_t side = static_cast<hipStream_t>(side_stream);
-    const bool ahead = mode == CSF_STACK_LOOKAHEAD;
-    hipEvent_t ev_x[2] = {nullptr, nullptr}, ev_s[2] = {nullptr, nullptr};
-    if (ahead) {
-        int s = stack_events(ev_x, ev_s);
-        if (s != CSF_OK)
-            return s;
-    }
-    const size_t es = elem_bytes(dtype);
-    FfnWs fw = ffn_ws(B, d, dtype, max_count);
+    if (!(mode & CSF_STACK_GRAPH))
+        return enqueue_stack(layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps, x_log,
+                             xhat_log, idx_log, count_log, ws, st,
+                             static_cast<hipStream_t>(side_stream));
 
-    auto sel_idx = [&](int l) {
-        return idx_log ? idx_log + (size_t)l * B * stride
-                       : reinterpret_cast<int32_t *>(at(ws, w.idx[l & 1]));
+    // graph replay: the whole stack as one launch, captured on first use for these arguments
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    uint64_t key = 1469598103934665603ull;
+    auto mix = [&](const void *p, size_t n) {
+        const unsigned char *c = static_cast<const unsigned char *>(p);
+        for (size_t i = 0; i < n; ++i)
+            key = (key ^ c[i]) * 1099511628211ull;
     };
-    auto sel_count = [&](int l) {
-        return count_log ? count_log + (size_t)l * B
-                         : reinterpret_cast<int32_t *>(at(ws, w.count[l & 1]));
-    };
-    // predictor of layer `l` applied to `xh`, then the selection, on stream `q`
-    auto predict_select = [&](int l, const void *xh, hipStream_t q, bool on_side) -> int {
-        float *a = reinterpret_cast<float *>(at(ws, on_side ? w.a_side : w.a_main));
-        float *sc = reinterpret_cast<float *>(at(ws, on_side ? w.s_side : w.s_main));
-        hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
-                                       nullptr);
-        if (e == hipSuccess) {
-            if (k >= 0)
-                e = csf::launch_select_topk(sc, B, f, k, sel_idx(l), stride, sel_count(l), nullptr, q);
-            else
-                e = csf::launch_select_threshold(sc, B, f, tau, sel_idx(l), stride, sel_count(l),
-                                                 nullptr, q);
+    mix(layers, sizeof(csf_layer_weights) * (size_t)L);
+    const void *ptrs[] = {x, x_log, xhat_log, idx_log, count_log, ws, stream, side_stream};
+    mix(ptrs, sizeof ptrs);
+    const int ints[] = {L, d, f, r, act, dtype, B, mode, k, norm, dev};
+    mix(ints, sizeof ints);
+    mix(&tau, sizeof tau);
+    mix(&eps, sizeof eps);
+    mix(&ws_bytes, sizeof ws_bytes);
+    StackGraph &g = g_stack_graph;
+    if (!(g.exec && g.key == key)) {
+        if (g.exec) {
+            (void)hipGraphExecDestroy(g.exec);
+            g.exec = nullptr;
         }
-        return hip_status(e, "stack predictor/selection launch");
-    };
-
-    for (int l = 0; l < L; ++l) {
-        void *xh = at(ws, w.xhat[l & 1]);
-        hipError_t e = csf::launch_rms_norm(
-            dtype, x, B, d, eps, norm, xh, x_log ? x_log + (size_t)l * B * d : nullptr,
-            xhat_log ? static_cast<char *>(xhat_log) + (size_t)l * B * d * es : nullptr, st);
+        hipStream_t cap = nullptr;
+        int s1 = capture_stream(dev, &cap);
+        if (s1 != CSF_OK)
+            return s1;
+        e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess)
-            return hip_status(e, "stack normalisation launch");
-        int s = CSF_OK;
-        if (!ahead || l == 0)
-            s = predict_select(l, xh, st, false);
-        if (s != CSF_OK)
-            return s;
-        if (ahead && l + 1 < L) {
-            // layer l+1's set from this layer's input, on the side stream, while this layer runs
-            e = hipEventRecord(ev_x[l & 1], st);
-            if (e == hipSuccess)
-                e = hipStreamWaitEvent(side, ev_x[l & 1], 0);
-            if (e != hipSuccess)
-                return hip_status(e, "stack event");
-            s = predict_select(l + 1, xh, side, true);
-            if (s != CSF_OK)
-                return s;
-            e = hipEventRecord(ev_s[(l + 1) & 1], side);
-            if (e != hipSuccess)
-                return hip_status(e, "stack event");
+            return hip_status(e, "hipStreamBeginCapture");
+        const int s2 = enqueue_stack(layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps,
+                                     x_log, xhat_log, idx_log, count_log, ws, cap,
+                                     static_cast<hipStream_t>(side_stream));
+        const std::string msg = g_last_error;
+        hipGraph_t graph = nullptr;
+        e = hipStreamEndCapture(cap, &graph);
+        if (s2 != CSF_OK) {
+            if (graph)
+                (void)hipGraphDestroy(graph);
+            return fail(s2, "%s", msg.c_str());
         }
-        if (ahead && l > 0) {
-            e = hipStreamWaitEvent(st, ev_s[l & 1], 0);
-            if (e != hipSuccess)
-                return hip_status(e, "stack event");
-        }
-        csf::FfnArgs fa;
-        fa.dtype = dtype;
-        fa.act = act;
-        fa.x = xh;
-        fa.B = B;
-        fa.d = d;
-        fa.f = f;
-        fa.W1 = layers[l].W1;
-        fa.Wup = layers[l].Wup;
-        fa.W2T = layers[l].W2T;
-        fa.b1 = layers[l].b1;
-        fa.idx = sel_idx(l);
-        fa.idx_stride = stride;
-        fa.count = k >= 0 ? nullptr : sel_count(l);
-        fa.max_count = max_count;
-        fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
-        fa.h_stride = stride;
-        fa.y = x;
-        fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
-        fa.accumulate = 1;
-        e = csf::launch_ffn(fa, st);
         if (e != hipSuccess)
-            return hip_status(e, "stack FFN launch");
+            return hip_status(e, "hipStreamEndCapture");
+        e = hipGraphInstantiateWithFlags(&g.exec, graph, 0);
+        (void)hipGraphDestroy(graph);
+        if (e != hipSuccess) {
+            g.exec = nullptr;
+            return hip_status(e, "hipGraphInstantiateWithFlags");
+        }
+        g.key = key;
     }
-    return ok();
+    return hip_status(hipGraphLaunch(g.exec, st), "hipGraphLaunch");
 }
 
 }  // extern "C"

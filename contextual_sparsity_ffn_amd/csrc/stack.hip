@@ -6,15 +6,17 @@
 // xhat = x / sqrt(mean(x^2) + eps) (or x itself in literal mode), rounded once to the weight type;
 // the block's output is added back to the float32 stream by the FFN's partial-sum reduction.
 //
-//   k_rms_norm  one 256-thread workgroup per token: fixed-order sum of squares (so the result is
-//               deterministic), the scale, the rounding to the storage type; optional copies of
-//               the stream and of xhat for inspection.
+//   k_rms_norm  one 1024-thread workgroup per token, the row held in registers: fixed-order sum of
+//               squares (so the result is deterministic), the scale, the rounding to the storage
+//               type; optional copies of the stream and of xhat for inspection.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace csf {
 
 namespace {
+
+constexpr int kNormThreads = 1024;
 
 template <int DT>
 __device__ __forceinline__ void store_elem(void *p, size_t i, float v)
@@ -27,36 +29,82 @@ __device__ __forceinline__ void store_elem(void *p, size_t i, float v)
         static_cast<uint16_t *>(p)[i] = BF16T::round_bits(v);
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_rms_norm(const float *__restrict__ x, int d, float eps,
-                                                  int norm, void *__restrict__ xhat,
-                                                  float *__restrict__ x_log,
-                                                  void *__restrict__ xhat_log)
+// One 1024-thread workgroup per token.  Thread t holds float4 chunks t, t + 1024, ... (NPT of
+// them) in registers, all loaded before the first use; the sum of squares is reduced in a fixed
+// order (lanes, then waves), so the scale is deterministic.
+template <int DT, int NPT>
+__global__ __launch_bounds__(kNormThreads) void k_rms_norm(const float *__restrict__ x, int d,
+                                                           float eps, int norm,
+                                                           void *__restrict__ xhat,
+                                                           float *__restrict__ x_log,
+                                                           void *__restrict__ xhat_log)
 {
-    __shared__ float red[4];
+    __shared__ float red[kNormThreads / kWave];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const size_t base = (size_t)blockIdx.x * d;
-    const float *xt = x + base;
+    const float4 *xt = reinterpret_cast<const float4 *>(x + base);
+    const int n4 = d / 4;
+    float4 v[NPT];
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+        const int c = t + kNormThreads * q;
+        v[q] = c < n4 ? xt[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     float scale = 1.0f;
     if (norm) {
         float ss = 0.0f;
-        for (int c = t; c < d; c += 256)
-            ss = fmaf(xt[c], xt[c], ss);
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+            ss = fmaf(v[q].x, v[q].x, ss);
+            ss = fmaf(v[q].y, v[q].y, ss);
+            ss = fmaf(v[q].z, v[q].z, ss);
+            ss = fmaf(v[q].w, v[q].w, ss);
+        }
         ss = wave_sum(ss);
         if (lane == 0)
             red[w] = ss;
         __syncthreads();
-        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+        float tot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kNormThreads / kWave; ++i)
+            tot += red[i];
         scale = 1.0f / sqrtf(tot / (float)d + eps);
     }
-    for (int c = t; c < d; c += 256) {
-        const float v = xt[c];
-        store_elem<DT>(xhat, base + c, v * scale);
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+        const int c = t + kNormThreads * q;
+        if (c >= n4)
+            break;
+        const float e[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            store_elem<DT>(xhat, base + 4 * c + i, e[i] * scale);
+            if (xhat_log)
+                store_elem<DT>(xhat_log, base + 4 * c + i, e[i] * scale);
+        }
         if (x_log)
-            x_log[base + c] = v;
-        if (xhat_log)
-            store_elem<DT>(xhat_log, base + c, v * scale);
+            reinterpret_cast<float4 *>(x_log + base)[c] = v[q];
     }
+}
+
+template <int DT>
+hipError_t norm_dt(const float *x, int B, int d, float eps, int norm, void *xhat, float *x_log,
+                   void *xhat_log, hipStream_t st)
+{
+    const int npt = (d / 4 + kNormThreads - 1) / kNormThreads;
+    if (npt <= 1)
+        return launch(k_rms_norm<DT, 1>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
+                      xhat, x_log, xhat_log);
+    if (npt <= 2)
+        return launch(k_rms_norm<DT, 2>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
+                      xhat, x_log, xhat_log);
+    if (npt <= 4)
+        return launch(k_rms_norm<DT, 4>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
+                      xhat, x_log, xhat_log);
+    if (npt <= 8)
+        return launch(k_rms_norm<DT, 8>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
+                      xhat, x_log, xhat_log);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -66,14 +114,13 @@ hipError_t launch_rms_norm(int dtype, const float *x, int B, int d, float eps, i
 {
     if (B <= 0)
         return hipSuccess;
+    if (d % 4 != 0)
+        return hipErrorInvalidValue;
     if (dtype == 0)
-        return launch(k_rms_norm<0>, dim3(B), dim3(256), st, nullptr, x, d, eps, norm, xhat, x_log,
-                      xhat_log);
+        return norm_dt<0>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
     if (dtype == 1)
-        return launch(k_rms_norm<1>, dim3(B), dim3(256), st, nullptr, x, d, eps, norm, xhat, x_log,
-                      xhat_log);
-    return launch(k_rms_norm<2>, dim3(B), dim3(256), st, nullptr, x, d, eps, norm, xhat, x_log,
-                  xhat_log);
+        return norm_dt<1>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
+    return norm_dt<2>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
 }
 
 }  // namespace csf

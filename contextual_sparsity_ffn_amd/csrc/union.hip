@@ -33,7 +33,6 @@ namespace csf {
 namespace {
 
 constexpr int kUnionThreads = 1024;
-constexpr int kTileRows = 16;        // union rows per MFMA up tile (the N of the 16x16x32 shape)
 constexpr int kKStep = 32;           // K of one MFMA: 32 elements = 4 16-byte chunks
 constexpr int kDownCols = 256;       // output columns per MFMA down workgroup (512 bytes of a row)
 constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 bytes (8-byte aligned,

@@ -77,8 +77,12 @@ typedef enum {
 /* How csf_stack_forward schedules the predictor of each layer. */
 typedef enum {
     CSF_STACK_SYNC = 0,      /* layer l's set is predicted from layer l's own input             */
-    CSF_STACK_LOOKAHEAD = 1  /* layer l's set is predicted from layer l-1's input, on the side
+    CSF_STACK_LOOKAHEAD = 1, /* layer l's set is predicted from layer l-1's input, on the side
                                 stream while layer l-1 runs (layer 0: from its own input)       */
+    CSF_STACK_GRAPH = 0x100  /* flag, OR'd into the mode: enqueue the whole stack as one HIP
+                                graph launch.  The first call captures it (per calling thread);
+                                later calls with identical arguments (every pointer, size and
+                                value, the layers array's contents, the streams) replay it.     */
 } csf_stack_mode;
 
 /* One block of a stack: predictor and FFN weights, shapes and layouts as for
@@ -278,15 +282,19 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
  *             round(x_l) (norm = 0), in the weight type;  A_l = top-k (k >= 0) or threshold (k =
  *             -1, tau) selection of predictor_l(xhat_l) (CSF_STACK_SYNC) or of predictor_l(xhat_{l-1})
  *             (CSF_STACK_LOOKAHEAD, l >= 1);  x_{l+1} = x_l + sparse FFN_l(xhat_l over A_l).
- *   mode      CSF_STACK_SYNC or CSF_STACK_LOOKAHEAD.  Look-ahead needs a side stream distinct from
- *             `stream`; the call orders it with events, and all of its work is ordered before the
- *             end of `stream`'s work, so synchronising `stream` is enough.
+ *   mode      CSF_STACK_SYNC or CSF_STACK_LOOKAHEAD, optionally | CSF_STACK_GRAPH.  Look-ahead
+ *             needs a side stream distinct from `stream`; the call orders it with events, and all
+ *             of its work is ordered before the end of `stream`'s work, so synchronising `stream`
+ *             is enough.  With CSF_STACK_GRAPH the host enqueues one launch per call instead of
+ *             about 7 kernels and 4 event operations per layer; the captured graph (kept by the
+ *             runtime, one per calling thread) is replaced when the arguments change.
  *   x_log     [L][B][d] float32, optional: x_l at the input of each layer.
  *   xhat_log  [L][B][d] dtype, optional: xhat_l.
  *   idx_log   [L][B][k or f] int32, optional: each layer's ascending active list.
  *   count_log [L][B] int32, optional: each layer's list length.
  * B >= 0 tokens, each with its own sets.  The library keeps 4 HIP events per device and calling
- * thread (created on first use, never device memory of its own).
+ * thread, and for CSF_STACK_GRAPH one capture stream per device and thread and the instantiated
+ * graph (all created on first use; no device buffers of its own).
  * Workspace: csf_workspace_size(CSF_OP_STACK, B, d, f, r, k >= 0 ? k : f, dtype).
  * ------------------------------------------------------------------------------------------- */
 int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,

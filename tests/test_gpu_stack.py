@@ -181,3 +181,41 @@ def test_stack_full_size_opt30b_shape_lookahead():
                               idx_log[l, 0].cpu().numpy(), orc.RELU, orc.F16)
     y_gpu = torch.from_numpy(xL[0].cpu().double().numpy() - x_log[l, 0].cpu().double().numpy())
     assert_ffn_close(y_gpu, y_ref, cfg.dtype, "full-size layer 2")
+
+
+@pytest.mark.parametrize("lookahead", [False, True], ids=["sync", "lookahead"])
+def test_stack_graph_replay_matches_eager(lookahead):
+    """The captured-graph form gives the eager bits on every replay, with eager work (another
+    stack call on other buffers) between the replays, and recaptures when an argument changes."""
+    announce(f"stack graph lookahead={lookahead}")
+    cfg = wl.CONFIGS[4].scaled(1024, 2048, 128)
+    layers = _layers(cfg, 5)
+    X = wl.make_tokens(cfg, 4).float().to(DEV)
+    side = torch.cuda.Stream(device=DEV)
+    ws = torch.empty(csf.workspace_size(8, 1, cfg.d, cfg.f, cfg.r, cfg.k, csf.F16), dtype=torch.uint8,
+                     device=DEV)
+    ws2 = torch.empty_like(ws)
+
+    def eager(x0, w):
+        x = x0.clone()
+        csf.stack_forward(x, layers, k=cfg.k, lookahead=lookahead, side_stream=side, ws=w)
+        torch.cuda.synchronize()
+        return x
+
+    ref = [eager(X[t:t + 1], ws) for t in range(4)]
+    xg = torch.empty(1, cfg.d, dtype=torch.float32, device=DEV)
+    for rep in range(3):
+        for t in range(4):
+            xg.copy_(X[t:t + 1])
+            csf.stack_forward(xg, layers, k=cfg.k, lookahead=lookahead, side_stream=side, ws=ws,
+                              graph=True)
+            torch.cuda.synchronize()
+            assert torch.equal(xg, ref[t]), (rep, t)
+            other = eager(X[(t + 1) % 4:(t + 1) % 4 + 1], ws2)       # eager work in between
+            assert torch.equal(other, ref[(t + 1) % 4])
+    # a different output buffer is a different graph
+    xh = torch.empty_like(xg)
+    xh.copy_(X[2:3])
+    csf.stack_forward(xh, layers, k=cfg.k, lookahead=lookahead, side_stream=side, ws=ws, graph=True)
+    torch.cuda.synchronize()
+    assert torch.equal(xh, ref[2])
