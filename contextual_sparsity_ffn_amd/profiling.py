@@ -7,8 +7,9 @@ Used to turn the CSV files of
     rocprofv3 --pmc WRITE_SIZE -f csv -d DIR -o layer -- python bench.py ... --copy-calibration
 
 into the short text summaries kept with the project, and to read them back.  The counter summary
-records a hash of the kernel sources: the benchmark reports the measured HBM traffic only while
-the kernels are unchanged since the counters were taken.
+records a hash of the batch-1 layer kernels' sources (common.hpp, predict.hip, select.hip,
+ffn.hip): the benchmark reports the measured HBM traffic only while those are unchanged since the
+counters were taken.
 
 Counter scaling: FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by
 the ratio of the known size of a plain device copy (the benchmark's --copy-calibration leg, a
@@ -20,7 +21,6 @@ the ratio of the known size of a plain device copy (the benchmark's --copy-calib
 from __future__ import annotations
 
 import csv
-import glob
 import hashlib
 import json
 import os
@@ -42,11 +42,16 @@ LABELS = [("k_pred_down", "pred_down"), ("k_pred_up", "pred_up"), ("k_select_top
           ("k_rms_norm", "rms_norm")]
 
 
-def source_hash() -> str:
-    """SHA-256 over the kernel sources (csrc/*), in name order."""
+# the sources of the batch-1 layer kernels whose counters are kept (their code and launch shapes)
+LAYER_SOURCES = ("common.hpp", "predict.hip", "select.hip", "ffn.hip")
+
+
+def source_hash(names=LAYER_SOURCES) -> str:
+    """SHA-256 over the named kernel sources in csrc/, in name order."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
-        h.update(os.path.basename(path).encode())
+    for name in sorted(names):
+        path = os.path.join(PKG, "csrc", name)
+        h.update(name.encode())
         with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
