@@ -638,6 +638,8 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
         return s;
     REQUIRE(max_count >= 0 && max_count <= idx_stride, CSF_ERR_INVALID_ARG,
             "max_count = %d must be in [0, idx_stride = %d]", max_count, idx_stride);
+    REQUIRE(max_count <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED,
+            "max_count = %d exceeds this build's limit %d", max_count, csf::ffn_max_count());
     CHECK_PTR(idx, B > 0 && max_count > 0);
     CHECK_PTR(count, false);
     CHECK_PTR(h, false);
@@ -675,6 +677,8 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
         return s;
+    REQUIRE(f <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::ffn_max_count());
     CHECK_PTR(H, false);
     CHECK_PTR(Y, B > 0);
     if (B == 0)

@@ -23,7 +23,8 @@ namespace csf {
 
 namespace {
 
-constexpr int kDownUnroll = 4;    // list entries whose 16-byte chunks are in flight per lane
+constexpr int kDownUnroll = 12;   // list entries whose 16-byte chunks are in flight per lane
+constexpr int kMaxChunkRows = 1024; // list entries per down-projection chunk (staged in LDS)
 constexpr int kSliceChunks = 64;  // one 16-byte chunk per lane: a d-slice is 1 KiB of a row
 constexpr int kMaxChunks = 64;    // most neuron chunks (partial rows) per slice
 
@@ -140,14 +141,14 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
 }
 
 // Down projection.  Grid: (d-slice of 64 chunks, neuron chunk, token).  Each lane owns one
-// 16-byte chunk column of the slice, so a wavefront instruction reads 1 KiB of one row, contiguous;
-// the 4 wavefronts of a workgroup take every 4th list entry of the chunk, kDownUnroll rows in
-// flight each (few rows per wavefront and many workgroups measured faster than deep unrolling:
-// occupancy, not per-wavefront queue depth, sets the gather rate).  The wavefronts are summed in
-// a fixed order and the chunk's partial row is stored; k_reduce_partials then sums the partial
-// rows in chunk order.  Handing the partials to another workgroup inside this kernel would need a
-// device-coherent write-back of each XCD's L2 per workgroup, which costs more than the kernel
-// boundary.  No float atomics anywhere, so y is deterministic.
+// 16-byte chunk column of the slice, so a wavefront instruction reads 1 KiB of one row, contiguous.
+// The chunk's list entries and their h values are staged in LDS first (so no row load waits on an
+// index load), then the 4 wavefronts take every 4th entry with kDownUnroll rows in flight each.
+// The wavefronts are summed in a fixed order and the chunk's partial row is stored;
+// k_reduce_partials then sums the partial rows in chunk order.  Handing the partials to another
+// workgroup inside this kernel would need a device-coherent write-back of each XCD's L2 per
+// workgroup, which costs more than the kernel boundary.  No float atomics anywhere, so y is
+// deterministic.
 template <class T>
 __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W2T,
                                                      const float *__restrict__ h, int h_stride,
@@ -159,6 +160,8 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
 {
     constexpr int E = T::E;
     __shared__ float red[3][kSliceChunks * E];
+    __shared__ int32_t sj[kMaxChunkRows];
+    __shared__ float sh[kMaxChunkRows];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int slice = blockIdx.x, chunk = blockIdx.y, token = blockIdx.z;
     const int D = C * E;
@@ -167,25 +170,32 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
     const int per = (cnt + nchunk - 1) / nchunk;
     const int nb = chunk * per;
     const int ne = nb + per < cnt ? nb + per : cnt;
+    const int ns = ne > nb ? ne - nb : 0;          // <= kMaxChunkRows (the host sizes nchunk)
     const int32_t *it = idx ? idx + (size_t)token * idx_stride : nullptr;
     const float *ht = h + (size_t)token * h_stride;
+
+    // an entry outside [0, f) contributes nothing: row 0 with h = 0
+    for (int i = t; i < ns; i += 256) {
+        const int j = it ? it[nb + i] : nb + i;
+        const bool ok = j >= 0 && j < f;
+        sj[i] = ok ? j : 0;
+        sh[i] = ok ? ht[nb + i] : 0.0f;
+    }
+    __syncthreads();
 
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         acc[e] = 0.0f;
-
-    for (int n = nb + w; n < ne; n += 4 * kDownUnroll) {
+    for (int i0 = w; i0 < ns; i0 += 4 * kDownUnroll) {
         u32x4 wv[kDownUnroll];
         float hv[kDownUnroll];
 #pragma unroll
         for (int u = 0; u < kDownUnroll; ++u) {
-            const int nn = n + 4 * u;
-            int j = nn < ne ? (it ? it[nn] : nn) : 0;
-            const bool ok = nn < ne && j >= 0 && j < f;
-            j = ok ? j : 0;
-            hv[u] = ok ? ht[nn] : 0.0f;
-            wv[u] = (ok && c < C) ? ld_stream(W2T + (size_t)j * C + c) : u32x4{0u, 0u, 0u, 0u};
+            const int i = i0 + 4 * u;
+            const bool ok = i < ns && c < C;
+            hv[u] = i < ns ? sh[i] : 0.0f;
+            wv[u] = ok ? ld_stream(W2T + (size_t)sj[i] * C + c) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kDownUnroll; ++u) {
@@ -212,28 +222,36 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
     }
 }
 
-// y[token][col] = sum over chunks q (in order) of part[token][q][col]; one thread per column with
-// every partial load issued before the first add.  accumulate: y += that sum (the residual add of a
-// stack of blocks).
+// y[token][col] = sum over chunks q of part[token][q][col] in a fixed order; accumulate: y += that
+// sum (the residual add of a stack of blocks).  A workgroup covers 64 columns: wave w sums chunks
+// w, w + 4, ... for the lane's column (every load issued before the first add) and the 4 waves'
+// sums are added in wave order.
 __global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict__ part, int nchunk,
                                                          int D, float *__restrict__ y,
                                                          int accumulate)
 {
-    const int col = blockIdx.x * 256 + threadIdx.x;
+    __shared__ float red[4][kWave];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int col = blockIdx.x * kWave + lane;
     const int token = blockIdx.y;
-    if (col >= D)
-        return;
-    const float *p = part + (size_t)token * nchunk * (size_t)D + col;
-    float pv[kMaxChunks];
+    const float *p = part + (size_t)token * nchunk * (size_t)D + (col < D ? col : 0);
+    float pv[kMaxChunks / 4];
 #pragma unroll
-    for (int q = 0; q < kMaxChunks; ++q)
-        pv[q] = q < nchunk ? p[(size_t)q * D] : 0.0f;
+    for (int q = 0; q < kMaxChunks / 4; ++q) {
+        const int ch = w + 4 * q;
+        pv[q] = (ch < nchunk && col < D) ? p[(size_t)ch * D] : 0.0f;
+    }
     float sum = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxChunks; ++q)
+    for (int q = 0; q < kMaxChunks / 4; ++q)
         sum += pv[q];
-    float *out = y + (size_t)token * D + col;
-    *out = accumulate ? *out + sum : sum;
+    red[w][lane] = sum;
+    __syncthreads();
+    if (w == 0 && col < D) {
+        const float tot = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+        float *out = y + (size_t)token * D + col;
+        *out = accumulate ? *out + tot : tot;
+    }
 }
 
 template <class T, int MX, bool GATED>
@@ -281,6 +299,8 @@ hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
 
 }  // namespace
 
+int ffn_max_count() { return kMaxChunks * kMaxChunkRows; }
+
 int ffn_num_slices(int d, int dtype)
 {
     const int C = d / (dtype == 0 ? 4 : 8);
@@ -299,6 +319,10 @@ int ffn_num_chunks(int d, int dtype, int max_count)
         want = cap;
     if (want > kMaxChunks)
         want = kMaxChunks;
+    // a chunk holds at most kMaxChunkRows list entries
+    const int least = (max_count + kMaxChunkRows - 1) / kMaxChunkRows;
+    if (want < least)
+        want = least;
     if (want < 1)
         want = 1;
     return want;
@@ -309,8 +333,8 @@ hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, f
 {
     if (nchunk < 1 || nchunk > kMaxChunks)
         return hipErrorInvalidValue;
-    return launch(k_reduce_partials, dim3((D + 255) / 256, B), dim3(256), st, tr, part, nchunk, D, y,
-                  accumulate);
+    return launch(k_reduce_partials, dim3((D + kWave - 1) / kWave, B), dim3(256), st, tr, part, nchunk,
+                  D, y, accumulate);
 }
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t st, Trace *tr)

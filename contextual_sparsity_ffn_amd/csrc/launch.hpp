@@ -93,6 +93,7 @@ struct FfnArgs {
 };
 // Shape of the down projection's two-phase reduction (sizes its workspace).
 int ffn_num_slices(int d, int dtype);
+int ffn_max_count();   // longest active list (and widest dense layer) the FFN kernels take
 int ffn_num_chunks(int d, int dtype, int max_count);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 // y[t][col] = sum over chunks q, in order, of part[t][q][col] (part is [B][nchunk][D] float32).

@@ -104,6 +104,9 @@ def test_sparse_ffn_validation():
     assert sparse(d=12) == UNSUPPORTED
     assert sparse(d=64, dt=csf.F32, wsb=8) == WS_SMALL
     assert sparse(idx=NULL) == INVALID
+    assert sparse(maxc=70000, stride=70000) == UNSUPPORTED   # longer than a list the kernels take
+    assert L.csf_dense_ffn(P, 1, 64, 70000, csf.RELU, csf.F16, P, NULL, NULL, P, NULL, P, P,
+                           1 << 30, NULL) == UNSUPPORTED
 
 
 def test_layer_validation():
