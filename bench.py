@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--batched-layers", type=int, default=4)
     ap.add_argument("--batched-sizes", default="1,4,8,16,32",
                     help="comma-separated batch sizes of the batched leg")
+    ap.add_argument("--zero-skip-steps", type=int, default=500,
+                    help="steps of the post-gate zero-skip legs (0: skip them)")
     ap.add_argument("--stack-tokens", type=int, default=16,
                     help="tokens timed through the 48-layer OPT-30B-shape stack (0: skip)")
     ap.add_argument("--stack-layers", type=int, default=48)
@@ -208,7 +210,7 @@ def main():
 
     # ---- predictor quality: recall / precision against the true active set -------------------
     log(f"quality on {args.quality_tokens} tokens")
-    rec, prec, tfrac = [], [], []
+    rec, prec_list, tfrac = [], [], []
     for t in range(args.quality_tokens):
         l = t % args.layers
         rc = fn(*call_args(l, t, scores_out=scores, idx_out=idx))
@@ -221,8 +223,10 @@ def main():
         hit = torch.isin(pred, true).sum().item()
         nt = true.numel()
         rec.append(hit / nt if nt else 1.0)
-        prec.append(hit / k if k else 1.0)
+        prec_list.append(hit / k if k else 1.0)
         tfrac.append(nt / f)
+
+    prec = sum(prec_list) / len(prec_list) if prec_list else None
 
     # ---- optional plain copy for counter calibration -----------------------------------------
     if args.copy_calibration:
@@ -231,6 +235,13 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+    # ---- post-gate zero-skip on the same plan (an option, not the metric) ---------------------
+    zero_skip = None
+    if args.zero_skip_steps > 0:
+        zero_skip = {"opt175b_layer": zero_skip_same_plan(args, fn, plan, stream, us_layer, prec,
+                                                          cfg, k)}
+        zero_skip["llama_reglu_layer"] = zero_skip_gated_leg(args, dev)
 
     # ---- batched union leg (OPT-30B shape) --------------------------------------------------
     batched = None
@@ -281,10 +292,11 @@ def main():
         "speedup_bound_bytes": round(dense_b / touched, 3),
         "speedup_bound_active_frac": round(f / k, 3),
         "recall": round(sum(rec) / len(rec), 4) if rec else None,
-        "precision": round(sum(prec) / len(prec), 4) if prec else None,
+        "precision": round(prec, 4) if prec is not None else None,
         "true_frac": round(sum(tfrac) / len(tfrac), 4) if tfrac else None,
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
+        "zero_skip": zero_skip,
         "batched_union": batched,
         "stack": stack,
     }
@@ -301,6 +313,122 @@ def predictor_kernels(B, dtype_code, d, r):
     if B >= 4 and dtype_code != 0 and d % 128 == 0 and r % 128 == 0:
         return ["pred_down", "pred_hidden", "pred_up"]
     return ["pred_down", "pred_up"]
+
+
+def zero_skip_same_plan(args, fn, plan, stream, us_plain, prec, cfg, k):
+    """The headline step with CSF_FFN_SKIP_ZERO_H: rows whose h is 0 (the predictor's false
+    positives) skip their down row.  Bytes actually needed: V + U + k W1 rows + (precision k) W2T
+    rows + x."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib
+
+    n = args.zero_skip_steps
+    csf.set_ffn_flags(csf.FFN_SKIP_ZERO_H)
+    try:
+        for s in range(20):
+            fn(*plan[s % len(plan)])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(n):
+            rc = fn(*plan[(7 + s) % len(plan)])
+            if rc:
+                raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+        e1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        csf.set_ffn_flags(0)
+    us = e0.elapsed_time(e1) * 1e3 / n
+    es = 2
+    live = prec * k if prec is not None else None
+    need = None
+    if live is not None:
+        need = (cfg.r * cfg.d + cfg.f * cfg.r + k * cfg.d + cfg.d) * es + live * cfg.d * es
+    log(f"zero-skip OPT-175B layer: {us:.2f} us (plain {us_plain:.2f} us)")
+    return {"us_per_layer": round(us, 3), "plain_us_per_layer": round(us_plain, 3),
+            "speedup": round(us_plain / us, 4),
+            "down_rows_read_per_token": round(live, 1) if live is not None else None,
+            "bytes_needed": int(need) if need else None,
+            "GBps_on_bytes_needed": round(need / (us * 1e-6) / 1e9, 1) if need else None}
+
+
+def zero_skip_gated_leg(args, dev):
+    """LLaMA-class gated layer (d 4096, f 14336, r 256, bfloat16, ReGLU, sigmoid >= 0.5): the
+    recall-first predictor marks about half the neurons, a tenth fire.  Plain vs zero-skip (gate
+    rows always; up and down rows only for positive gates)."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    cfg = wl.CONFIGS[2]
+    d, f, r = cfg.d, cfg.f, cfg.r
+    code = _lib.dtype_code(cfg.dtype)
+    nl = 8
+    layers = [wl.make_layer(cfg, device=dev, layer=l) for l in range(nl)]
+    X = wl.make_tokens(cfg, 64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ws_b = csf.workspace_size(_lib.OP_LAYER, 1, d, f, r, f, code)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    idx = torch.empty(f, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    hd = torch.empty(f, dtype=torch.float32, device=dev)
+    vp = ctypes.c_void_p
+    fn = _lib.lib.csf_sparse_ffn_layer
+
+    def call(l, t, idx_out=None, cnt_out=None):
+        L = layers[l]
+        return fn(vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(L.V.data_ptr()), vp(L.U.data_ptr()),
+                  vp(L.W1.data_ptr()), vp(L.b1.data_ptr()), vp(L.Wup.data_ptr()), vp(L.W2T.data_ptr()),
+                  -1, ctypes.c_float(cfg.tau), vp(y.data_ptr()), None,
+                  None if idx_out is None else vp(idx_out.data_ptr()),
+                  None if cnt_out is None else vp(cnt_out.data_ptr()), vp(ws.data_ptr()), ws_b,
+                  vp(stream.cuda_stream))
+
+    # predicted and live (positive-gate) counts over a sample of (layer, token) pairs
+    counts, lives = [], []
+    for s in range(16):
+        l, t = s % nl, s % 64
+        call(l, t, idx, cnt)
+        L = layers[l]
+        csf.dense_ffn(X[t], L.W1, L.b1, L.Wup, L.W2T, act=cfg.act, h=hd)
+        torch.cuda.synchronize()
+        n = int(cnt.item())
+        counts.append(n)
+        # a listed neuron is live when its gate is positive; ReGLU h != 0 iff gate > 0 (and up != 0)
+        lives.append(int((hd[idx[:n].long()] != 0).sum()))
+    count, live = sum(counts) / len(counts), sum(lives) / len(lives)
+    res = {"workload": "LLaMA-class gated layer, batch 1: d 4096, f 14336, r 256, bfloat16, ReGLU, "
+                       "threshold sigmoid >= 0.5", "layers_rotated": nl,
+           "predicted_mean": round(count, 1), "live_mean": round(live, 1)}
+    es = 2
+    plain_bytes = (r * d + f * r + d) * es + count * 3 * d * es
+    skip_bytes = (r * d + f * r + d) * es + count * d * es + live * 2 * d * es
+    for mode, flags in (("plain", 0), ("zero_skip", csf.FFN_SKIP_ZERO_H)):
+        csf.set_ffn_flags(flags)
+        try:
+            for s in range(20):
+                call(s % nl, s % 64)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(args.zero_skip_steps):
+                call(s % nl, (s * 7) % 64)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            csf.set_ffn_flags(0)
+        us = e0.elapsed_time(e1) * 1e3 / args.zero_skip_steps
+        b = plain_bytes if mode == "plain" else skip_bytes
+        res[mode] = {"us_per_layer": round(us, 3), "bytes_needed": int(b),
+                     "GBps_on_bytes_needed": round(b / (us * 1e-6) / 1e9, 1)}
+    res["speedup"] = round(res["plain"]["us_per_layer"] / res["zero_skip"]["us_per_layer"], 4)
+    log(f"zero-skip gated layer: plain {res['plain']['us_per_layer']} us, skip "
+        f"{res['zero_skip']['us_per_layer']} us (predicted {count:.0f}, live {live:.0f})")
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def batched_union_leg(args, dev):

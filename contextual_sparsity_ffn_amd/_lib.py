@@ -21,6 +21,7 @@ RELU, REGLU = 0, 1
 OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
     OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK = range(9)
 STACK_SYNC, STACK_LOOKAHEAD, STACK_GRAPH = 0, 1, 0x100
+FFN_SKIP_ZERO_H = 1
 SEM_PER_TOKEN, SEM_UNION = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_MFMA = 0, 1, 2
 MAX_UNION_BATCH = 32
@@ -31,7 +32,8 @@ _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
            "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
            "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_batched_union",
-           "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_trace_events")
+           "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
+           "csf_set_trace_events")
 
 
 class LayerWeights(ctypes.Structure):
@@ -68,6 +70,7 @@ def _load():
                                  vp, vp, vp, sz, vp]
     L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csf_set_trace_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    L.csf_set_ffn_flags.argtypes = [i32]
     L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
                                        flt, vp, vp, vp, vp, vp, sz, vp]
     L.csf_sparse_ffn_batched_union.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
@@ -279,6 +282,11 @@ def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
     _check(lib.csf_dense_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
                              _ptr(W2T), _ptr(h), _ptr(y), _ptr(w), wb, _stream(dev)))
     return y.view(d) if squeeze else y.view(B, d)
+
+
+def set_ffn_flags(flags):
+    """Options of the gathered FFN for later calls on this thread (FFN_SKIP_ZERO_H or 0)."""
+    _check(lib.csf_set_ffn_flags(int(flags)))
 
 
 def set_trace_events(events):

@@ -19,6 +19,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_trace_events[16];
 thread_local int g_trace_n = 0;
+thread_local int g_ffn_flags = 0;
 
 int fail(int status, const char *fmt, ...)
 {
@@ -495,6 +496,7 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
         fa.y = x;
         fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
         fa.accumulate = 1;
+        fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
         e = csf::launch_ffn(fa, st);
         if (e != hipSuccess)
             return hip_status(e, "stack FFN launch");
@@ -523,6 +525,14 @@ const char *csf_status_string(int status)
 }
 
 const char *csf_last_error(void) { return g_last_error.c_str(); }
+
+int csf_set_ffn_flags(int flags)
+{
+    REQUIRE((flags & ~CSF_FFN_SKIP_ZERO_H) == 0, CSF_ERR_INVALID_ARG, "unknown FFN flags 0x%x",
+            flags);
+    g_ffn_flags = flags;
+    return ok();
+}
 
 int csf_set_trace_events(void *const *events, int n)
 {
@@ -667,6 +677,7 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
     a.h_stride = h ? idx_stride : (max_count > 0 ? max_count : 1);
     a.y = y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "sparse FFN launch");
 }
 
@@ -704,6 +715,7 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     a.h_stride = f;
     a.y = Y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
+    a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "dense FFN launch");
 }
 
@@ -866,6 +878,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     fa.h_stride = max_count > 0 ? max_count : 1;
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+    fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 
@@ -930,7 +943,7 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
     mix(layers, sizeof(csf_layer_weights) * (size_t)L);
     const void *ptrs[] = {x, x_log, xhat_log, idx_log, count_log, ws, stream, side_stream};
     mix(ptrs, sizeof ptrs);
-    const int ints[] = {L, d, f, r, act, dtype, B, mode, k, norm, dev};
+    const int ints[] = {L, d, f, r, act, dtype, B, mode, k, norm, dev, g_ffn_flags};
     mix(ints, sizeof ints);
     mix(&tau, sizeof tau);
     mix(&eps, sizeof eps);

@@ -44,7 +44,10 @@ struct UpShape {
     static constexpr int RPW = loads >= 12 ? 1 : (loads >= 6 ? 2 : 4);
 };
 
-template <class T, int MX, bool GATED, int RPW = UpShape<MX, GATED>::RPW>
+// SKIP (gated form only): the up rows are read only for neurons whose gate is positive (the
+// others have h = 0 whatever the up row holds): the gate dot products are finished first, then
+// the workgroup loads the up rows that are still needed.
+template <class T, int MX, bool GATED, bool SKIP = false, int RPW = UpShape<MX, GATED>::RPW>
 __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
                                                    const u32x4 *__restrict__ W1,
                                                    const u32x4 *__restrict__ Wup,
@@ -93,12 +96,40 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
             const int c = t + 256 * m;
             wv[i][m] = (jr[i] >= 0 && c < C) ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
         }
-        if constexpr (GATED) {
+        if constexpr (GATED && !SKIP) {
             const u32x4 *urow = Wup + (size_t)(jr[i] < 0 ? 0 : jr[i]) * C;
 #pragma unroll
             for (int m = 0; m < MX; ++m) {
                 const int c = t + 256 * m;
                 uv[i][m] = (jr[i] >= 0 && c < C) ? ld_stream(urow + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+    if constexpr (GATED && SKIP) {
+        // gates first; then the up rows of the rows whose gate (with bias) is positive
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MX; ++m)
+                acc = T::dot(wv[i][m], xv[m], acc);
+            acc = wave_sum(acc);
+            if (lane == 0)
+                red[w][i][0] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float p = (red[0][i][0] + red[1][i][0]) + (red[2][i][0] + red[3][i][0]);
+            if (b1 && jr[i] >= 0)
+                p += b1[jr[i]];
+            const bool live = jr[i] >= 0 && p > 0.0f;      // uniform across the workgroup
+            const u32x4 *urow = Wup + (size_t)(live ? jr[i] : 0) * C;
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const int c = t + 256 * m;
+                uv[i][m] = (live && c < C) ? ld_stream(urow + c) : u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
@@ -110,7 +141,7 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
         for (int m = 0; m < MX; ++m)
             acc = T::dot(wv[i][m], xv[m], acc);
         acc = wave_sum(acc);
-        if (lane == 0)
+        if (lane == 0 && !(GATED && SKIP))
             red[w][i][0] = acc;
         if constexpr (GATED) {
             float au = 0.0f;
@@ -156,7 +187,7 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
                                                      int idx_stride,
                                                      const int32_t *__restrict__ count,
                                                      int max_count, int f, int C, int nchunk,
-                                                     float *__restrict__ part)
+                                                     int skip_zero, float *__restrict__ part)
 {
     constexpr int E = T::E;
     __shared__ float red[3][kSliceChunks * E];
@@ -174,12 +205,37 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
     const int32_t *it = idx ? idx + (size_t)token * idx_stride : nullptr;
     const float *ht = h + (size_t)token * h_stride;
 
-    // an entry outside [0, f) contributes nothing: row 0 with h = 0
-    for (int i = t; i < ns; i += 256) {
-        const int j = it ? it[nb + i] : nb + i;
-        const bool ok = j >= 0 && j < f;
-        sj[i] = ok ? j : 0;
-        sh[i] = ok ? ht[nb + i] : 0.0f;
+    // an entry outside [0, f) contributes nothing: row 0 with h = 0.  skip_zero: entries with
+    // h = 0 are dropped (order kept), so their rows are not read at all.
+    int nk = ns;
+    if (!skip_zero) {
+        for (int i = t; i < ns; i += 256) {
+            const int j = it ? it[nb + i] : nb + i;
+            const bool ok = j >= 0 && j < f;
+            sj[i] = ok ? j : 0;
+            sh[i] = ok ? ht[nb + i] : 0.0f;
+        }
+    } else {
+        __shared__ uint32_t scan_tmp[4];
+        int base = 0;
+        for (int r0 = 0; r0 < ns; r0 += 256) {
+            const int i = r0 + t;
+            int j = 0;
+            float hv = 0.0f;
+            if (i < ns) {
+                j = it ? it[nb + i] : nb + i;
+                hv = (j >= 0 && j < f) ? ht[nb + i] : 0.0f;
+            }
+            const bool keep = hv != 0.0f;
+            uint32_t tot;
+            const uint32_t pos = block_exclusive_scan<4>(keep ? 1u : 0u, scan_tmp, &tot);
+            if (keep) {
+                sj[base + pos] = j;
+                sh[base + pos] = hv;
+            }
+            base += (int)tot;
+        }
+        nk = base;
     }
     __syncthreads();
 
@@ -187,14 +243,14 @@ __global__ __launch_bounds__(256) void k_gather_down(const u32x4 *__restrict__ W
 #pragma unroll
     for (int e = 0; e < E; ++e)
         acc[e] = 0.0f;
-    for (int i0 = w; i0 < ns; i0 += 4 * kDownUnroll) {
+    for (int i0 = w; i0 < nk; i0 += 4 * kDownUnroll) {
         u32x4 wv[kDownUnroll];
         float hv[kDownUnroll];
 #pragma unroll
         for (int u = 0; u < kDownUnroll; ++u) {
             const int i = i0 + 4 * u;
-            const bool ok = i < ns && c < C;
-            hv[u] = i < ns ? sh[i] : 0.0f;
+            const bool ok = i < nk && c < C;
+            hv[u] = i < nk ? sh[i] : 0.0f;
             wv[u] = ok ? ld_stream(W2T + (size_t)sj[i] * C + c) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
@@ -261,6 +317,11 @@ hipError_t up_launch(const FfnArgs &a, int C, hipStream_t st, Trace *tr)
     const int blocks = (a.max_count + RPW - 1) / RPW;
     if (blocks == 0)
         return hipSuccess;
+    if (GATED && a.skip_zero)
+        return launch(k_gather_up<T, MX, GATED, true>, dim3(blocks, a.B), dim3(256), st, tr,
+                      static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
+                      static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count,
+                      a.max_count, a.f, C, a.h, a.h_stride);
     return launch(k_gather_up<T, MX, GATED>, dim3(blocks, a.B), dim3(256), st, tr,
                   static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
                   static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count,
@@ -291,7 +352,7 @@ hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
     const int nchunk = ffn_num_chunks(a.d, a.dtype, a.max_count);
     e = launch(k_gather_down<T>, dim3(ffn_num_slices(a.d, a.dtype), nchunk, a.B), dim3(256), st,
                tr, static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride, a.idx, a.idx_stride, a.count,
-               a.max_count, a.f, C, nchunk, a.partials);
+               a.max_count, a.f, C, nchunk, a.skip_zero, a.partials);
     if (e != hipSuccess)
         return e;
     return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.y, st, tr, a.accumulate);

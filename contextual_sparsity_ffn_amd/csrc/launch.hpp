@@ -90,6 +90,8 @@ struct FfnArgs {
     float *y;               // [B][d]
     float *partials;        // [B][ffn_num_chunks][d] workspace
     int accumulate = 0;     // 1: y += the FFN output (residual add)
+    int skip_zero = 0;      // 1: rows with h = 0 are not read (down rows; up rows of the gated
+                            // form whose gate is not positive)
 };
 // Shape of the down projection's two-phase reduction (sizes its workspace).
 int ffn_num_slices(int d, int dtype);

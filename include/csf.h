@@ -303,6 +303,21 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
                       void *ws, size_t ws_bytes, void *stream, void *side_stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csf_set_ffn_flags -- options of the gathered FFN for later calls on the calling thread
+ * (csf_sparse_ffn, csf_dense_ffn, csf_sparse_ffn_layer, csf_stack_forward; not the batched union
+ * path).  0 (the default) restores the plain method.
+ *   CSF_FFN_SKIP_ZERO_H  post-gate zero-skip: a listed neuron whose activation h is exactly 0 is
+ *                        dropped before its down row is read, and in the gated form its up row
+ *                        is read only if its gate is positive.  The skipped terms are zero, so
+ *                        y is the same up to float32 summation order.  A predictor tuned for
+ *                        recall over-predicts ([CP] "Precision, recall, and which error hurts":
+ *                        a false positive costs bandwidth), so most of the skipped rows are its
+ *                        false positives.
+ * ------------------------------------------------------------------------------------------- */
+#define CSF_FFN_SKIP_ZERO_H 1
+int csf_set_ffn_flags(int flags);
+
+/* ---------------------------------------------------------------------------------------------
  * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer,
  * csf_sparse_ffn_batched_union and csf_sparse_ffn_batched_layer (per calling thread).
  * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record

@@ -206,6 +206,12 @@ def test_stack_validation():
     assert need >= 2 * 7168 * 2 + 2 * 28672 * 4 + 2 * 5734 * 4
 
 
+def test_ffn_flags_validation():
+    assert L.csf_set_ffn_flags(2) == INVALID
+    assert L.csf_set_ffn_flags(csf.FFN_SKIP_ZERO_H) == OK
+    assert L.csf_set_ffn_flags(0) == OK
+
+
 def test_k_from_ratio_matches_the_printed_figures():
     figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     for case in figs["k_from_ratio"]:

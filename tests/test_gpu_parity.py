@@ -306,3 +306,77 @@ def test_layer_full_size_opt175b_shape():
     o = layer_to_orc(Ld)
     ix = _check_layer_token(Ld, o, x, cfg.k, None, "c1 full")
     assert len(ix) == cfg.k
+
+
+# ---- post-gate zero-skip: rows with h = 0 are not read; y is the same up to summation order --------
+ZS_CASES = [
+    ("relu-f16", wl.CONFIGS[1].scaled(2048, 3001, 128)),
+    ("reglu-bf16-threshold", wl.CONFIGS[2].scaled(1024, 2500, 128)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", ZS_CASES, ids=[c[0] for c in ZS_CASES])
+def test_zero_skip_layer_and_ffn(name, cfg):
+    announce(f"zero-skip {name}")
+    L = _layer(cfg)
+    Ld = _to_dev_layer(L)
+    o = layer_to_orc(L)
+    X = wl.make_tokens(cfg, 3)
+    try:
+        for t in range(3):
+            x = _dev(X[t])
+            k = cfg.k
+            idx = torch.empty(k if k is not None else cfg.f, dtype=torch.int32, device=DEV)
+            cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+            csf.set_ffn_flags(0)
+            y0 = csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k, tau=cfg.tau,
+                                      act=cfg.act, idx=idx, count=cnt)
+            csf.set_ffn_flags(csf.FFN_SKIP_ZERO_H)
+            y1 = csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k, tau=cfg.tau,
+                                      act=cfg.act)
+            y1b = csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k, tau=cfg.tau,
+                                       act=cfg.act)
+            torch.cuda.synchronize()
+            n = int(cnt.item())
+            sel = idx[:n].cpu().numpy()
+            h_ref, y_ref = orc.sparse_ffn(to_orc(X[t]), o["W1"], o["b1"], o["Wup"], o["W2T"], sel,
+                                          o["act"], o["dt"])
+            assert (h_ref == 0).sum() > n // 4              # the skip has work to do
+            assert_ffn_close(y0, y_ref, cfg.dtype, f"{name} plain token {t}")
+            assert_ffn_close(y1, y_ref, cfg.dtype, f"{name} zero-skip token {t}")
+            assert torch.equal(y1, y1b)                     # deterministic
+        # the dense layer with the skip is the dense layer
+        hd = torch.empty(1, cfg.f, dtype=torch.float32, device=DEV)
+        yd = csf.dense_ffn(_dev(X[0]), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, act=cfg.act, h=hd)
+        torch.cuda.synchronize()
+        _, yd_ref = orc.dense_ffn(to_orc(X[0]), o["W1"], o["b1"], o["Wup"], o["W2T"], o["act"], o["dt"])
+        assert_ffn_close(yd, yd_ref, cfg.dtype, f"{name} dense zero-skip")
+    finally:
+        csf.set_ffn_flags(0)
+
+
+@pytest.mark.parametrize("act", [csf.RELU, csf.REGLU])
+def test_zero_skip_integer_inputs_bit_exact(act):
+    """Dropping exact zeros keeps integer arithmetic exact: bit-equal to the oracle."""
+    announce(f"zero-skip integer act={act}")
+    g = torch.Generator().manual_seed(123 + act)
+    d, f, count, B = 1024, 1300, 400, 2
+    x = torch.randint(-3, 4, (B, d), generator=g).half()
+    W1 = torch.randint(-2, 3, (f, d), generator=g).half()
+    Wup = torch.randint(-2, 3, (f, d), generator=g).half() if act == csf.REGLU else None
+    W2T = torch.randint(-2, 3, (f, d), generator=g).half()
+    b1 = torch.randint(-3, 4, (f,), generator=g).float()
+    idx = torch.stack([torch.sort(torch.randperm(f, generator=g)[:count]).values for _ in range(B)]).int()
+    try:
+        csf.set_ffn_flags(csf.FFN_SKIP_ZERO_H)
+        y = csf.sparse_ffn(_dev(x), _dev(W1), _dev(b1), None if Wup is None else _dev(Wup),
+                           _dev(W2T), _dev(idx), act=act)
+        torch.cuda.synchronize()
+    finally:
+        csf.set_ffn_flags(0)
+    for t in range(B):
+        h_ref, y_ref = orc.sparse_ffn(to_orc(x[t]), to_orc(W1), to_orc(b1),
+                                      None if Wup is None else to_orc(Wup), to_orc(W2T),
+                                      idx[t].numpy(), act, orc.F16)
+        assert (h_ref == 0).sum() > count // 4
+        assert np.array_equal(y[t].cpu().double().numpy(), y_ref)
