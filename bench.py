@@ -55,6 +55,8 @@ def parse():
                     help="comma-separated batch sizes of the batched leg")
     ap.add_argument("--zero-skip-steps", type=int, default=500,
                     help="steps of the post-gate zero-skip legs (0: skip them)")
+    ap.add_argument("--locality-steps", type=int, default=400,
+                    help="steps of the hot-block (static locality) leg (0: skip it)")
     ap.add_argument("--stack-tokens", type=int, default=16,
                     help="tokens timed through the 48-layer OPT-30B-shape stack (0: skip)")
     ap.add_argument("--stack-layers", type=int, default=48)
@@ -245,8 +247,13 @@ def main():
 
     # ---- batched union leg (OPT-30B shape) --------------------------------------------------
     batched = None
-    if args.batched_steps > 0:
+    locality_res = None
+    if args.batched_steps > 0 or args.locality_steps > 0:
         del layers
+        torch.cuda.empty_cache()
+    if args.locality_steps > 0:
+        locality_res = static_locality_leg(args, dev)
+    if args.batched_steps > 0:
         torch.cuda.empty_cache()
         batched = batched_union_leg(args, dev)
 
@@ -297,6 +304,7 @@ def main():
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
         "zero_skip": zero_skip,
+        "static_locality": locality_res,
         "batched_union": batched,
         "stack": stack,
     }
@@ -427,6 +435,92 @@ def zero_skip_gated_leg(args, dev):
     log(f"zero-skip gated layer: plain {res['plain']['us_per_layer']} us, skip "
         f"{res['zero_skip']['us_per_layer']} us (predicted {count:.0f}, live {live:.0f})")
     del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def static_locality_leg(args, dev):
+    """OPT-30B FFN shape with power-law firing (a few neurons fire for almost every token; the
+    bias-free predictor cannot see it): the plain layer (top-k 5734 over all neurons) against the
+    hot-first layer (profiled on 256 separately seeded tokens, reordered, neurons firing for at
+    least half of them always computed, the rest of the same 5734 budget chosen by the predictor
+    over the cold rows).  Time, recall of the true active set and predictor bytes for each."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, locality, workloads as wl
+
+    cfg = wl.CONFIGS[3]
+    d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
+    nl = 4
+    log(f"static-locality leg: {nl} power-law layers of d={d} f={f}")
+    plain, prepared = [], []
+    for l in range(nl):
+        L = wl.make_powerlaw_layer(cfg, device=dev, layer=l)
+        freq = locality.firing_frequency(L, wl.make_profile_tokens(cfg, 256, device=dev))
+        H = locality.reorder(L, locality.hot_first_order(freq))
+        hot = locality.hot_count(freq, 0.5, cap=k // 2)
+        plain.append(L)
+        prepared.append((H, hot, H.U[hot:].contiguous()))
+    X = wl.make_tokens(cfg, 64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = _lib.dtype_code(cfg.dtype)
+    ws_b = csf.workspace_size(_lib.OP_LAYER, 1, d, f, r, k, code)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    idx = torch.empty(f, dtype=torch.int32, device=dev)
+    H_all = torch.empty(1, f, dtype=torch.float32, device=dev)
+    vp = ctypes.c_void_p
+    fplain, fhot = _lib.lib.csf_sparse_ffn_layer, _lib.lib.csf_sparse_ffn_layer_hot
+
+    def call_plain(l, t, idx_out=None):
+        L = plain[l]
+        return fplain(vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(L.V.data_ptr()),
+                      vp(L.U.data_ptr()), vp(L.W1.data_ptr()), vp(L.b1.data_ptr()), None,
+                      vp(L.W2T.data_ptr()), k, ctypes.c_float(0.0), vp(y.data_ptr()), None,
+                      None if idx_out is None else vp(idx_out.data_ptr()), None, vp(ws.data_ptr()),
+                      ws_b, vp(stream.cuda_stream))
+
+    def call_hot(l, t, idx_out=None):
+        H, hot, Uc = prepared[l]
+        return fhot(vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(H.V.data_ptr()),
+                    vp(Uc.data_ptr()), vp(H.W1.data_ptr()), vp(H.b1.data_ptr()), None,
+                    vp(H.W2T.data_ptr()), hot, k - hot, ctypes.c_float(0.0), vp(y.data_ptr()), None,
+                    None if idx_out is None else vp(idx_out.data_ptr()), None, vp(ws.data_ptr()),
+                    ws_b, vp(stream.cuda_stream))
+
+    hots = [p[1] for p in prepared]
+    res = {"workload": "OPT-30B-shape layer with power-law firing (alpha 2, mean 0.2), batch 1, "
+                       "active budget 5734", "layers_rotated": nl, "hot_per_layer": hots}
+    for name, call, layers_of in (("plain", call_plain, lambda l: plain[l]),
+                                  ("hot_block", call_hot, lambda l: prepared[l][0])):
+        rec = []
+        for t in range(16):
+            l = t % nl
+            rc = call(l, t, idx)
+            if rc:
+                raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+            Lq = layers_of(l)
+            csf.dense_ffn(X[t:t + 1], Lq.W1, Lq.b1, None, Lq.W2T, h=H_all)
+            torch.cuda.synchronize()
+            true = H_all[0] > 0
+            nt = int(true.sum())
+            rec.append(int(true[idx[:k].long()].sum()) / nt if nt else 1.0)
+        for s in range(20):
+            call(s % nl, s % 64)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.locality_steps):
+            call(s % nl, (s * 7) % 64)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.locality_steps
+        hot_mean = sum(hots) / len(hots) if name == "hot_block" else 0
+        pred_bytes = 2 * (r * d + (f - hot_mean) * r)
+        res[name] = {"us_per_layer": round(us, 3), "recall": round(sum(rec) / len(rec), 4),
+                     "predictor_bytes": int(pred_bytes)}
+        log(f"  {name}: {us:.2f} us, recall {sum(rec) / len(rec):.3f}")
+    del plain, prepared
     torch.cuda.empty_cache()
     return res
 

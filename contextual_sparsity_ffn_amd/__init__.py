@@ -8,11 +8,11 @@ from ._lib import (BF16, F16, F32, FFN_SKIP_ZERO_H, PATH_AUTO, PATH_GATHER, PATH
                    SEM_UNION, CsfError, dense_ffn, k_from_ratio, lib, predict_active,
                    select_threshold, select_topk, set_ffn_flags, set_trace_events, sparse_ffn,
                    sparse_ffn_batched_layer, sparse_ffn_batched_union, sparse_ffn_layer,
-                   stack_forward, workspace_size)
+                   sparse_ffn_layer_hot, stack_forward, workspace_size)
 
 __all__ = ["BF16", "F16", "F32", "FFN_SKIP_ZERO_H", "PATH_AUTO", "PATH_GATHER", "PATH_MFMA", "REGLU", "RELU",
            "SEM_PER_TOKEN", "SEM_UNION", "CsfError", "dense_ffn", "k_from_ratio", "lib",
            "predict_active", "select_threshold", "select_topk", "set_ffn_flags", "set_trace_events",
            "sparse_ffn",
            "sparse_ffn_batched_layer", "sparse_ffn_batched_union", "sparse_ffn_layer",
-           "stack_forward", "workspace_size"]
+           "sparse_ffn_layer_hot", "stack_forward", "workspace_size"]

@@ -31,7 +31,8 @@ _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
 
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
            "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
-           "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_batched_union",
+           "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_layer_hot",
+           "csf_sparse_ffn_batched_union",
            "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
            "csf_set_trace_events")
 
@@ -73,6 +74,8 @@ def _load():
     L.csf_set_ffn_flags.argtypes = [i32]
     L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
                                        flt, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn_layer_hot.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
+                                           i32, flt, vp, vp, vp, vp, vp, sz, vp]
     L.csf_sparse_ffn_batched_union.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                i32, i32, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
     L.csf_sparse_ffn_batched_layer.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -443,3 +446,39 @@ def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=T
                                  float(eps), _ptr(x_log), _ptr(xhat_log), _ptr(idx_log),
                                  _ptr(count_log), _ptr(w), wb, _stream(dev), side))
     return x
+
+
+def sparse_ffn_layer_hot(x, V, U_cold, W1, b1, Wup, W2T, hot, k=None, tau=None, act=RELU, y=None,
+                         scores=None, idx=None, count=None, ws=None):
+    """One token through a hot-first layer: neurons 0 .. hot-1 always, plus the top-k (or >= tau)
+    of the cold neurons scored by the predictor with up rows U_cold [f - hot, r]."""
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k (top-k) or tau (threshold)")
+    _tensor(x, "x")
+    if x.dim() != 1:
+        raise ValueError("x must be one token, shape [d]")
+    dev, dt, f, d = _ffn_weights(x, W1, b1, Wup, W2T, act)
+    _tensor(x, "x", shape=(d,))
+    r = V.shape[0]
+    hot = int(hot)
+    _tensor(V, "V", dtype=dt, shape=(r, d), device=dev)
+    _tensor(U_cold, "U_cold", dtype=dt, shape=(f - hot, r), device=dev)
+    kk = -1 if k is None else int(k)
+    if y is None:
+        y = torch.empty(d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, shape=(d,), device=dev)
+    _tensor(scores, "scores", dtype=torch.float32, shape=(f - hot,), device=dev, optional=True)
+    max_count = hot + (f - hot if kk < 0 else kk)
+    if idx is not None:
+        _tensor(idx, "idx", dtype=torch.int32, device=dev)
+        if idx.numel() < max(max_count, 1):
+            raise ValueError("idx is too small")
+    _tensor(count, "count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    code = dtype_code(dt)
+    w, wb = _workspace(workspace_size(OP_LAYER, 1, d, f, r, max_count, code), dev, ws)
+    _check(lib.csf_sparse_ffn_layer_hot(_ptr(x), d, f, r, act, code, _ptr(V), _ptr(U_cold),
+                                        _ptr(W1), _ptr(b1), _ptr(Wup), _ptr(W2T), hot, kk,
+                                        float(tau if tau is not None else 0.0), _ptr(y),
+                                        _ptr(scores), _ptr(idx), _ptr(count), _ptr(w), wb,
+                                        _stream(dev)))
+    return y

@@ -807,6 +807,83 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
     return s;
 }
 
+int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dtype,
+                             const void *V, const void *U_cold, const void *W1, const float *b1,
+                             const void *Wup, const void *W2T, int hot, int k_cold, float tau,
+                             float *y, float *scores_out, int32_t *idx_out, int32_t *count_out,
+                             void *ws, size_t ws_bytes, void *stream)
+{
+    int s = validate_ffn(x, 1, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    REQUIRE(hot >= 0 && hot < f, CSF_ERR_INVALID_ARG,
+            "hot = %d must be in [0, f = %d) (a fully hot layer is csf_dense_ffn)", hot, f);
+    const int fc = f - hot;
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(V, true);
+    CHECK_PTR(U_cold, true);
+    CHECK_PTR(y, true);
+    CHECK_PTR(scores_out, false);
+    CHECK_PTR(idx_out, false);
+    CHECK_PTR(count_out, false);
+    REQUIRE(k_cold >= -1 && k_cold <= fc, CSF_ERR_INVALID_ARG,
+            "k_cold = %d must be -1 (threshold) or in [0, f - hot = %d]", k_cold, fc);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(k_cold >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    const int max_count = hot + (k_cold >= 0 ? k_cold : fc);
+    LayerWs w = layer_ws(d, f, r, max_count, dtype);
+    CHECK_WS(ws, ws_bytes, w.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    csf::Trace tr;
+    if (g_trace_n > 0) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    csf::Trace *trp = tr.ev ? &tr : nullptr;
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
+    int32_t *ix = idx_out ? idx_out : reinterpret_cast<int32_t *>(at(ws, w.idx));
+    int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
+    const int stride = max_count > 0 ? max_count : 1;
+
+    // the predictor scores the cold rows only; the list is the hot block, then the selection
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp);
+    if (e == hipSuccess)
+        e = csf::launch_pred_up(dtype, a, 1, d, r, U_cold, fc, sc, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor launch");
+    if (k_cold >= 0)
+        e = csf::launch_select_topk(sc, 1, fc, k_cold, ix, stride, cn, nullptr, st, trp, hot);
+    else
+        e = csf::launch_select_threshold(sc, 1, fc, tau, ix, stride, cn, nullptr, st, trp, hot);
+    if (e != hipSuccess)
+        return hip_status(e, "selection launch");
+
+    FfnWs fw = ffn_ws(1, d, dtype, max_count);
+    csf::FfnArgs fa;
+    fa.dtype = dtype;
+    fa.act = act;
+    fa.x = x;
+    fa.B = 1;
+    fa.d = d;
+    fa.f = f;
+    fa.W1 = W1;
+    fa.Wup = Wup;
+    fa.W2T = W2T;
+    fa.b1 = b1;
+    fa.idx = ix;
+    fa.idx_stride = stride;
+    fa.count = k_cold >= 0 ? nullptr : cn;
+    fa.max_count = max_count;
+    fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+    fa.h_stride = stride;
+    fa.y = y;
+    fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+    fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
+}
+
 int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,
                          const void *U, const void *W1, const float *b1, const void *Wup,
                          const void *W2T, int k, float tau, float *y, float *scores_out,

@@ -66,12 +66,15 @@ hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const voi
                                Trace *trace = nullptr);
 
 // ---- selection (select.hip) -----------------------------------------------------------------
+// prefix: the list of each token starts with the neurons 0 .. prefix-1 (a block that is always
+// computed) and the selected neurons follow as prefix + their index among the scores; counts
+// include the prefix, idx_stride must hold it.
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap,
-                              hipStream_t stream, Trace *trace = nullptr);
+                              hipStream_t stream, Trace *trace = nullptr, int prefix = 0);
 hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
-                                   hipStream_t stream, Trace *trace = nullptr);
+                                   hipStream_t stream, Trace *trace = nullptr, int prefix = 0);
 int select_max_f();   // largest f the selection kernels accept
 
 // ---- FFN (ffn.hip) --------------------------------------------------------------------------

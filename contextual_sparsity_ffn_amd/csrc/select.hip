@@ -80,8 +80,9 @@ __device__ __forceinline__ void store_nibbles(uint32_t nib, uint32_t *bm, int wo
     *dst = x;
 }
 
-// Compaction of an LDS bitmap into the ascending index list; also copies the bitmap out.
-__device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int out_cap,
+// Compaction of an LDS bitmap into the ascending index list (index + base); also copies the bitmap
+// out.
+__device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int out_cap, int base,
                                uint32_t *bitmap_out, uint32_t *scan_tmp, uint32_t *total_out)
 {
     const int t = threadIdx.x;
@@ -104,7 +105,7 @@ __device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int 
             const int b = __ffs(bits) - 1;
             bits &= bits - 1;
             if (pos < (uint32_t)out_cap)
-                out[pos] = w * 32 + b;
+                out[pos] = base + w * 32 + b;
             ++pos;
         }
     }
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
                                                              int32_t *__restrict__ idx,
                                                              int idx_stride,
                                                              int32_t *__restrict__ count,
-                                                             uint32_t *__restrict__ bitmap)
+                                                             uint32_t *__restrict__ bitmap,
+                                                             int prefix)
 {
     __shared__ uint32_t hist[NB];
     __shared__ uint32_t bm[kMaxWords];
@@ -136,10 +138,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
     int32_t *out = idx + (size_t)token * idx_stride;
     uint32_t *bm_out = bitmap ? bitmap + (size_t)token * words : nullptr;
 
+    // a leading block of `prefix` neurons always belongs to the list (they are not scored)
+    for (int i = t; i < prefix; i += kSelThreads)
+        out[i] = i;
     if (t == 0) {
         misc[2] = 0u;
         if (count)
-            count[token] = k;
+            count[token] = prefix + k;
     }
     if (k == 0) {                                     // uniform: nothing is selected
         if (bm_out)
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
         // many candidates (heavy ties or a concentrated distribution): radix select over the
         // 32-bit order keys of bucket B*, 8 bits per pass.  This rare path re-reads the scores
         // from memory so that the common path keeps its registers.
-        uint32_t prefix = 0u, pmask = 0u, krem = need;
+        uint32_t kpre = 0u, pmask = 0u, krem = need;
 #pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
             if (t < 256)
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
             for (int j = t; j < f; j += kSelThreads) {
                 const float x = s[j];
                 const uint32_t key = order_key(x);
-                if (score_bucket<NB>(x) == bstar && (key & pmask) == prefix)
+                if (score_bucket<NB>(x) == bstar && (key & pmask) == kpre)
                     atomicAdd(&rhist[(key >> shift) & 0xffu], 1u);
             }
             __syncthreads();
@@ -271,14 +276,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
                 }
             }
             __syncthreads();
-            prefix |= misc[3] << shift;
+            kpre |= misc[3] << shift;
             pmask |= 0xffu << shift;
             krem = misc[4];
             __syncthreads();
         }
         // keys above T are in; of the keys equal to T the krem lowest-indexed are in (blocks of
         // 1024 indices in ascending order, a block scan ranks the equal keys inside each block)
-        const uint32_t T = prefix;
+        const uint32_t T = kpre;
         uint32_t taken = 0;
 #pragma unroll 1
         for (int base = 0; base < f; base += kSelThreads) {
@@ -303,13 +308,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
     __syncthreads();
 
     // ---- 4. ascending list ------------------------------------------------------------------------
-    bitmap_to_list(bm, words, out, idx_stride, bm_out, scan_tmp, nullptr);
+    bitmap_to_list(bm, words, out + prefix, idx_stride - prefix, prefix, bm_out, scan_tmp, nullptr);
 }
 
 template <int J, bool VEC>
 __global__ __launch_bounds__(kSelThreads) void k_select_threshold(
     const float *__restrict__ scores, int f, float tau, int32_t *__restrict__ idx, int idx_stride,
-    int32_t *__restrict__ count, uint32_t *__restrict__ bitmap)
+    int32_t *__restrict__ count, uint32_t *__restrict__ bitmap, int prefix)
 {
     __shared__ uint32_t bm[kMaxWords];
     __shared__ uint32_t trash[kSelThreads];
@@ -331,33 +336,36 @@ __global__ __launch_bounds__(kSelThreads) void k_select_threshold(
     }
     __syncthreads();
     uint32_t total;
-    bitmap_to_list(bm, words, idx + (size_t)token * idx_stride, idx_stride,
+    int32_t *out = idx + (size_t)token * idx_stride;
+    for (int i = t; i < prefix; i += kSelThreads)
+        out[i] = i;
+    bitmap_to_list(bm, words, out + prefix, idx_stride - prefix, prefix,
                    bitmap ? bitmap + (size_t)token * words : nullptr, scan_tmp, &total);
     if (t == 0)
-        count[token] = (int32_t)total;
+        count[token] = prefix + (int32_t)total;
 }
 
 
 template <int J>
 hipError_t topk_j(const float *scores, int B, int f, int k, int32_t *idx, int idx_stride,
-                  int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr)
+                  int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr, int prefix)
 {
     if (f % 4 == 0)
         return launch(k_select_topk<kScoreBuckets, J, true>, dim3(B), dim3(kSelThreads), st, tr,
-                      scores, f, k, idx, idx_stride, count, bitmap);
+                      scores, f, k, idx, idx_stride, count, bitmap, prefix);
     return launch(k_select_topk<kScoreBuckets, J, false>, dim3(B), dim3(kSelThreads), st, tr,
-                  scores, f, k, idx, idx_stride, count, bitmap);
+                  scores, f, k, idx, idx_stride, count, bitmap, prefix);
 }
 
 template <int J>
 hipError_t threshold_j(const float *scores, int B, int f, float tau, int32_t *idx, int idx_stride,
-                       int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr)
+                       int32_t *count, uint32_t *bitmap, hipStream_t st, Trace *tr, int prefix)
 {
     if (f % 4 == 0)
         return launch(k_select_threshold<J, true>, dim3(B), dim3(kSelThreads), st, tr, scores, f,
-                      tau, idx, idx_stride, count, bitmap);
+                      tau, idx, idx_stride, count, bitmap, prefix);
     return launch(k_select_threshold<J, false>, dim3(B), dim3(kSelThreads), st, tr, scores, f,
-                  tau, idx, idx_stride, count, bitmap);
+                  tau, idx, idx_stride, count, bitmap, prefix);
 }
 
 }  // namespace
@@ -366,29 +374,29 @@ int select_max_f() { return 32 * kMaxWords; }
 
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap, hipStream_t st,
-                              Trace *tr)
+                              Trace *tr, int prefix)
 {
     const int J = (f + kQuad - 1) / kQuad;     // sweeps of 4096 scores
-    if (J <= 1) return topk_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 2) return topk_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 4) return topk_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 8) return topk_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 12) return topk_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 16) return topk_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 1) return topk_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 2) return topk_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 4) return topk_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 8) return topk_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 12) return topk_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 16) return topk_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, st, tr, prefix);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
-                                   hipStream_t st, Trace *tr)
+                                   hipStream_t st, Trace *tr, int prefix)
 {
     const int J = (f + kQuad - 1) / kQuad;
-    if (J <= 1) return threshold_j<1>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 2) return threshold_j<2>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 4) return threshold_j<4>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 8) return threshold_j<8>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 12) return threshold_j<12>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
-    if (J <= 16) return threshold_j<16>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr);
+    if (J <= 1) return threshold_j<1>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 2) return threshold_j<2>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 4) return threshold_j<4>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 8) return threshold_j<8>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 12) return threshold_j<12>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
+    if (J <= 16) return threshold_j<16>(scores, B, f, tau, idx, idx_stride, count, bitmap, st, tr, prefix);
     return hipErrorInvalidValue;
 }
 

@@ -8,7 +8,9 @@ are not available here; these stand-ins copy their shapes and the structure the 
     ("Contextual Sparsity and Activation Predictors": the set is predictable from the layer input
     by something far cheaper than the layer);
   * a bias calibrated so a chosen fraction of pre-activations is positive (the sparsity level);
-  * clustered tokens, so that the active sets of a batch overlap ("When it breaks").
+  * clustered tokens, so that the active sets of a batch overlap ("When it breaks");
+  * optionally, per-neuron biases that make firing frequency follow a power law, a few neurons
+    active for almost every token and a long rare tail ("Static locality: hot and cold neurons").
 
 Normal draws N(0, s) use s as the standard deviation.  Every tensor is drawn from its own
 torch.Generator seeded with seed(config, role, layer) = 1_000_000*config + 1_000*role + layer,
@@ -24,6 +26,7 @@ import torch
 
 ROLE_U, ROLE_V, ROLE_W1_NOISE, ROLE_W2T, ROLE_WUP, ROLE_TOKENS = 1, 2, 3, 4, 5, 6
 ROLE_CALIB, ROLE_CENTROIDS, ROLE_CLUSTER_IDS, ROLE_CLUSTER_NOISE = 7, 8, 9, 10
+ROLE_POWERLAW, ROLE_PROFILE = 11, 12
 
 RELU, REGLU = 0, 1
 
@@ -145,6 +148,43 @@ def calibrate_bias(cfg: Config, W1: torch.Tensor, device, c: int, layer: int,
     kth = min(max(kth, 1), P.numel())
     q = torch.kthvalue(P.cpu(), kth).values.item()
     return float(-q)
+
+
+def powerlaw_firing(f: int, mean: float, alpha: float, device, s: int) -> torch.Tensor:
+    """Target firing probability of each neuron: q = 0.99 / (1 + (rank / knee)^alpha) over a seeded
+    random ranking, the knee set (by bisection) so that the mean probability is `mean`."""
+    rank = torch.randperm(f, generator=_gen(device, s), device=device).to(torch.float64)
+
+    def q_of(knee):
+        return 0.99 / (1.0 + (rank / knee) ** alpha)
+
+    lo, hi = 1e-3, float(f)
+    for _ in range(80):
+        mid = math.sqrt(lo * hi)
+        if float(q_of(mid).mean()) < mean:
+            lo = mid
+        else:
+            hi = mid
+    return q_of(hi)
+
+
+def make_powerlaw_layer(cfg: Config, device="cpu", layer: int = 0, alpha: float = 2.0,
+                        config_id: Optional[int] = None) -> Layer:
+    """A layer of the same recipe whose per-neuron bias gives neuron j the firing probability q_j
+    of powerlaw_firing (mean cfg.positive_frac): for x ~ N(0, I), W1_j.x ~ N(0, |W1_j|^2), so
+    b1_j = |W1_j| * Phi^-1(q_j).  The predictor is bias-free, so it does not see this structure."""
+    c = cfg.index if config_id is None else config_id
+    L = make_layer(cfg, device=device, layer=layer, config_id=config_id)
+    sigma = L.W1.float().norm(dim=1).to(torch.float64)
+    q = powerlaw_firing(cfg.f, cfg.positive_frac, alpha, device, seed(c, ROLE_POWERLAW, layer))
+    b1 = (sigma * torch.special.ndtri(q)).to(torch.float32)
+    return Layer(cfg, L.V, L.U, L.W1, b1, L.Wup, L.W2T)
+
+
+def make_profile_tokens(cfg: Config, n: int, device="cpu", config_id: Optional[int] = None):
+    """n tokens for profiling firing frequencies, seeded apart from the measured tokens."""
+    c = cfg.index if config_id is None else config_id
+    return normal((n, cfg.d), 1.0, device, seed(c, ROLE_PROFILE)).to(cfg.dtype)
 
 
 def make_tokens(cfg: Config, n: int, device="cpu", config_id: Optional[int] = None) -> torch.Tensor:

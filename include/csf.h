@@ -223,6 +223,32 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
                          void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csf_sparse_ffn_layer_hot -- one token through a layer whose neurons are ordered hot first: the
+ * leading `hot` neurons are always computed (no prediction), the predictor scores only the cold
+ * remainder, and the top-k_cold (k_cold >= 0) or thresholded (k_cold == -1, tau) cold neurons
+ * are added.
+ * [CP] "Static locality: hot and cold neurons": activation frequency follows a power law, a small
+ *      set fires for almost every token; the static split decides where a neuron lives, the
+ *      predictor whether this token needs it.  [AS] "Hot and cold neuron split with per-layer
+ *      predictors": neurons ranked by firing frequency, the frequent ones kept resident, a
+ *      predictor per layer for the rest.
+ *
+ *   V [r][d]; U_cold [f - hot][r]: row i scores neuron hot + i (the predictor's up rows of the cold
+ *   neurons only, so its bytes shrink by hot / f).  W1, b1, Wup, W2T [f][...] as csf_sparse_ffn,
+ *   with the hot neurons in rows 0 .. hot-1 (see the reordering helpers of the Python package).
+ *   0 <= hot < f; 0 <= k_cold <= f - hot.
+ *   scores_out [f - hot], idx_out [hot + k_cold, or f in threshold mode], count_out [1]: optional;
+ *   the list is 0 .. hot-1 followed by the selected cold neurons, ascending.
+ * Workspace: csf_workspace_size(CSF_OP_LAYER, 1, d, f, r, hot + (k_cold >= 0 ? k_cold : f - hot),
+ * dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dtype,
+                             const void *V, const void *U_cold, const void *W1, const float *b1,
+                             const void *Wup, const void *W2T, int hot, int k_cold, float tau,
+                             float *y, float *scores_out, int32_t *idx_out, int32_t *count_out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csf_sparse_ffn_batched_union -- the sparse FFN of B tokens reading the union of their active
  * sets once.
  * [CP] "When it breaks": the tokens of a batch select different neurons, so the layer reads the

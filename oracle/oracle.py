@@ -248,6 +248,15 @@ def to_bitmap(idx, f):
     return words
 
 
+def hot_layer_set(x, V, U_cold, hot, dt, k=None, tau=None):
+    """[CP] "Static locality: hot and cold neurons": the neurons 0 .. hot-1 (ordered hot first) are
+    always active; the predictor (up rows U_cold: row i scores neuron hot + i) picks among the
+    rest by top-k or threshold.  Returns (ascending list, cold scores)."""
+    _, _, s = predict(x, V, U_cold, dt)
+    cold = select_topk(s, k) if k is not None else select_threshold(s, tau)
+    return np.concatenate([np.arange(hot, dtype=np.int32), cold.astype(np.int32) + hot]), s
+
+
 def round_to_storage(x, dt):
     """Round float values to storage type dt, nearest-even (bf16 as raw uint16 bits)."""
     x = np.asarray(x, dtype=np.float64).reshape(-1)

@@ -1,0 +1,79 @@
+"""Pins for the oracle's hot-block composition and for the static-locality inputs.
+
+"Contextual Sparsity and Activation Predictors", section "Static locality: hot and cold neurons":
+a hot-first layer always computes its leading neurons and lets the predictor choose among the
+rest.  The composition is pinned to library routines (argsort) and to the plain layer it must
+reduce to; reordering neurons must not change what the FFN computes; the power-law input
+generator must give the firing frequencies it promises.
+"""
+import numpy as np
+import torch
+
+from contextual_sparsity_ffn_amd import workloads as wl
+from oracle import oracle as orc
+
+
+def _rand_layer(rng, d=32, f=60, r=8):
+    V = rng.standard_normal((r, d)).astype(np.float32)
+    U = rng.standard_normal((f, r)).astype(np.float32)
+    W1 = rng.standard_normal((f, d)).astype(np.float32)
+    b1 = rng.standard_normal(f).astype(np.float32)
+    W2T = rng.standard_normal((f, d)).astype(np.float32)
+    return V, U, W1, b1, W2T
+
+
+def test_hot_block_of_zero_is_the_plain_selection():
+    rng = np.random.default_rng(1)
+    V, U, *_ = _rand_layer(rng)
+    x = rng.standard_normal(32).astype(np.float32)
+    A, s = orc.hot_layer_set(x, V, U, 0, orc.F32, k=13)
+    _, _, s_full = orc.predict(x, V, U, orc.F32)
+    assert np.array_equal(s, s_full)
+    assert np.array_equal(A, orc.select_topk(s_full, 13))
+
+
+def test_hot_block_then_top_k_of_the_cold_scores():
+    rng = np.random.default_rng(2)
+    V, U, *_ = _rand_layer(rng)
+    x = rng.standard_normal(32).astype(np.float32)
+    hot, k = 17, 9
+    A, s = orc.hot_layer_set(x, V, U[hot:], hot, orc.F32, k=k)
+    _, _, s_full = orc.predict(x, V, U, orc.F32)
+    assert np.array_equal(s, s_full[hot:])            # rows score independently
+    ref = np.concatenate([np.arange(hot), hot + np.sort(np.argsort(-s_full[hot:], kind="stable")[:k])])
+    assert np.array_equal(A, ref)
+    At, st = orc.hot_layer_set(x, V, U[hot:], hot, orc.F32, tau=0.5)
+    assert np.array_equal(At, np.concatenate([np.arange(hot), hot + np.nonzero(st >= 0.5)[0]]))
+
+
+def test_reordering_neurons_keeps_the_function():
+    rng = np.random.default_rng(3)
+    _, _, W1, b1, W2T = _rand_layer(rng)
+    x = rng.standard_normal(32).astype(np.float32)
+    perm = rng.permutation(60)
+    idx = np.sort(rng.choice(60, 25, replace=False)).astype(np.int32)
+    _, y = orc.sparse_ffn(x, W1, b1, None, W2T, idx, orc.RELU, orc.F32)
+    # the same neurons in the permuted layer: position p holds neuron perm[p]
+    inv = np.argsort(perm)
+    idx_p = np.sort(inv[idx]).astype(np.int32)
+    _, yp = orc.sparse_ffn(x, W1[perm], b1[perm], None, W2T[perm], idx_p, orc.RELU, orc.F32)
+    assert np.allclose(y, yp, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+    _, yd = orc.dense_ffn(x, W1, b1, None, W2T, orc.RELU, orc.F32)
+    _, ydp = orc.dense_ffn(x, W1[perm], b1[perm], None, W2T[perm], orc.RELU, orc.F32)
+    assert np.allclose(yd, ydp, rtol=1e-12, atol=1e-12 * np.abs(yd).max())
+
+
+def test_powerlaw_inputs_fire_as_promised():
+    """Mean firing fraction and per-neuron frequencies of the power-law layer (input generator)."""
+    cfg = wl.CONFIGS[3].scaled(256, 1500, 64)
+    q = wl.powerlaw_firing(1500, cfg.positive_frac, 2.0, "cpu", 7)
+    assert abs(float(q.mean()) - cfg.positive_frac) < 1e-6
+    assert float(q.max()) <= 0.99 and float((q > 0.5).float().mean()) > 0.05   # a hot head
+    assert float((q < 0.05).float().mean()) > 0.2                                # a rare tail
+    L = wl.make_powerlaw_layer(cfg)
+    X = wl.make_profile_tokens(cfg, 512).float()
+    freq = ((X @ L.W1.float().t() + L.b1) > 0).float().mean(0)
+    target = wl.powerlaw_firing(1500, cfg.positive_frac, 2.0, "cpu",
+                                wl.seed(cfg.index, wl.ROLE_POWERLAW, 0)).float()
+    assert abs(float(freq.mean()) - cfg.positive_frac) < 0.01
+    assert float(torch.corrcoef(torch.stack([freq, target]))[0, 1]) > 0.98
