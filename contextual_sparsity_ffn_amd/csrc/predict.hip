@@ -191,7 +191,7 @@ hipError_t up_rw(const float *a, int B, int S, int r, int C, const void *U, int 
                  hipStream_t st, Trace *tr)
 {
     constexpr int G = kWave / LPR;
-    int rw = 4;
+    int rw = MM >= 2 ? 2 : 4;   // rows of two 16-byte chunks per lane: 2 rows (measured fastest)
     while (rw > 1 && (long)f / (rw * G) < 4096)   // keep >= 1024 workgroups when f allows
         rw /= 2;
     if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st, tr);
