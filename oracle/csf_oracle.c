@@ -30,7 +30,7 @@
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
-enum { ORC_RELU = 0, ORC_REGLU = 1 };
+enum { ORC_RELU = 0, ORC_REGLU = 1, ORC_SILU = 2, ORC_SWIGLU = 3 };
 
 /* ------------------------------------------------------------------------------------------ */
 /* Storage types, from their IEEE / bfloat16 definitions.                                      */
@@ -222,6 +222,10 @@ int orc_select_threshold(const float *s, int f, float tau, int32_t *idx_out /* [
 /* dot product, fp32-or-better accumulation, then max(acc, 0).                                 */
 /* Readings: b1 is a per-neuron bias on the gate/up pre-activation (NULL = zero), no bias on   */
 /* W_up or on the output; h and y stay in full precision; the down projection is neuron-major. */
+/* SiLU forms ([DV] "The Prediction Problem": the sketch applies silu to the gathered gate      */
+/* product; "The SiLU/GELU Challenge": the LLaMA-style block is down(silu(gate x) * (up x))):   */
+/* silu(p) = p * sigmoid(p) = p / (1 + e^-p), never exactly zero, so a sparse step over a set   */
+/* that drops neurons is an approximation of the dense layer, not a rearrangement of it.        */
 /* ------------------------------------------------------------------------------------------ */
 
 /* Gate pre-activation p_j = W1[j].x + b1_j and, for the gated form, u_j = Wup[j].x. */
@@ -235,7 +239,7 @@ static void neuron_preact(const void *x, int d, int dt, const void *W1, const fl
         acc += (double)b1[j];
     *p = acc;
     *u = 1.0;
-    if (act == ORC_REGLU) {
+    if (act == ORC_REGLU || act == ORC_SWIGLU) {
         double au = 0.0;
         for (int c = 0; c < d; ++c)
             au += wid(Wup, (size_t)j * d + c, dt) * wid(x, c, dt);
@@ -243,19 +247,25 @@ static void neuron_preact(const void *x, int d, int dt, const void *W1, const fl
     }
 }
 
+static int gated_act(int act) { return act == ORC_REGLU || act == ORC_SWIGLU; }
+static int bad_act(int act) { return act < ORC_RELU || act > ORC_SWIGLU; }
+
+/* silu(p) = p / (1 + e^-p); for very negative p, e^-p overflows to +inf and the quotient is -0. */
+double orc_silu(double p) { return p / (1.0 + exp(-p)); }
+
 static double neuron_act(double p, double u, int act)
 {
-    double g = p > 0.0 ? p : 0.0;
-    return act == ORC_REGLU ? g * u : g;
+    double g = (act == ORC_SILU || act == ORC_SWIGLU) ? orc_silu(p) : (p > 0.0 ? p : 0.0);
+    return gated_act(act) ? g * u : g;
 }
 
 int orc_sparse_ffn(const void *x, int d, int f, int act, int dt, const void *W1, const float *b1,
                    const void *Wup, const void *W2T, const int32_t *idx, int count,
                    double *h_out /* [count] or NULL */, double *y_out /* [d] */)
 {
-    if (d <= 0 || f < 0 || count < 0 || bad_dtype(dt) || (act != ORC_RELU && act != ORC_REGLU))
+    if (d <= 0 || f < 0 || count < 0 || bad_dtype(dt) || bad_act(act))
         return -1;
-    if (!x || !W1 || !W2T || !y_out || (count > 0 && !idx) || (act == ORC_REGLU && !Wup))
+    if (!x || !W1 || !W2T || !y_out || (count > 0 && !idx) || (gated_act(act) && !Wup))
         return -1;
     for (int c = 0; c < d; ++c)
         y_out[c] = 0.0;
@@ -280,9 +290,9 @@ int orc_dense_ffn(const void *x, int d, int f, int act, int dt, const void *W1, 
                   const void *Wup, const void *W2T, double *h_out /* [f] or NULL */,
                   double *y_out /* [d] */)
 {
-    if (d <= 0 || f < 0 || bad_dtype(dt) || (act != ORC_RELU && act != ORC_REGLU))
+    if (d <= 0 || f < 0 || bad_dtype(dt) || bad_act(act))
         return -1;
-    if (!x || !W1 || !W2T || !y_out || (act == ORC_REGLU && !Wup))
+    if (!x || !W1 || !W2T || !y_out || (gated_act(act) && !Wup))
         return -1;
     for (int c = 0; c < d; ++c)
         y_out[c] = 0.0;

@@ -25,7 +25,7 @@ import subprocess
 import numpy as np
 
 F32, F16, BF16 = 0, 1, 2
-RELU, REGLU = 0, 1
+RELU, REGLU, SILU, SWIGLU = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csf_oracle.c")
@@ -61,6 +61,8 @@ def lib():
         L.orc_f64_to_f16.restype = ctypes.c_uint16
         L.orc_f64_to_bf16.argtypes = [dbl]
         L.orc_f64_to_bf16.restype = ctypes.c_uint16
+        L.orc_silu.argtypes = [dbl]
+        L.orc_silu.restype = dbl
         L.orc_predict.argtypes = [vp, i32, vp, i32, vp, i32, i32, vp, vp, vp]
         L.orc_select_topk.argtypes = [vp, i32, i32, vp]
         L.orc_select_threshold.argtypes = [vp, i32, flt, vp]
@@ -206,6 +208,19 @@ def rms_normalize(x, dt, eps=1e-6):
 def true_set(x, W1, b1, dt):
     """Neurons whose ReLU (or gate ReLU) output is non-zero: pre-activation strictly > 0."""
     return np.nonzero(preact(x, W1, b1, dt) > 0.0)[0].astype(np.int32)
+
+
+def silu(p: float) -> float:
+    """silu(p) = p / (1 + e^-p), as the C oracle computes it."""
+    return lib().orc_silu(float(p))
+
+
+def functional_set(x, W1, b1, dt, tau=0.1):
+    """[DV] "The Empirical Foundation" (measure_mlp_sparsity, SiLU form): the neurons whose gate
+    activation is large in magnitude, |silu(W1 x + b1)| > tau, in ascending order.  SiLU is never
+    exactly zero, so this is the set that matters to the output, not the set that is non-zero."""
+    p = preact(x, W1, b1, dt)
+    return np.array([j for j in range(p.shape[0]) if abs(silu(p[j])) > tau], dtype=np.int32)
 
 
 def recall_precision(pred, true):

@@ -1,0 +1,161 @@
+"""Pins for the oracle's SiLU forms and the functional active set.
+
+Sources: "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm" --
+"The Empirical Foundation" (measure_mlp_sparsity: a neuron counts as active when the magnitude of
+its activation exceeds a threshold, 0.1 by default; SiLU models show functional rather than exact
+sparsity), "The Prediction Problem" (the sketch applies silu to the gathered gate product),
+"The SiLU/GELU Challenge: TurboSparse" (the LLaMA-style block down(silu(gate x) * (up x)),
+about half of the neurons functionally sparse).
+
+Each pin is fixed by something other than the oracle's own formula: a closed form (the minimum of
+silu is -W(1/e), Lambert's W), an identity of the function (silu(p) - silu(-p) = p), a library
+routine (scipy's logistic function), hand-derived boundary cases, or an exact reduction to the
+ReLU forms.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import oracle as orc
+
+
+def _layer(rng, d, f, dt, gated, bias=0.0):
+    cast = {orc.F32: np.float32, orc.F16: np.float16}[dt]
+    x = rng.standard_normal(d).astype(cast)
+    W1 = (rng.standard_normal((f, d)) / math.sqrt(d)).astype(cast)
+    Wup = (rng.standard_normal((f, d)) / math.sqrt(d)).astype(cast) if gated else None
+    W2T = (rng.standard_normal((f, d)) / math.sqrt(f)).astype(cast)
+    b1 = (bias + 0.2 * rng.standard_normal(f)).astype(np.float32)
+    return x, W1, b1, Wup, W2T
+
+
+def test_silu_minimum_is_minus_lambert_w_of_inverse_e():
+    # d/dp p*sigmoid(p) = 0 gives q = 1 + e^-q for q = -p, so q = 1 + W(1/e) and the minimum
+    # value is -(q - 1) = -W(1/e).
+    w = float(special.lambertw(1.0 / math.e).real)
+    p_star = -(1.0 + w)
+    assert orc.silu(p_star) == pytest.approx(-w, rel=1e-14)
+    for dp in (1e-3, -1e-3, 0.1, -0.1):
+        assert orc.silu(p_star + dp) > orc.silu(p_star)
+
+
+def test_silu_odd_part_is_identity_and_matches_the_logistic_function():
+    for p in np.linspace(-30.0, 30.0, 241):
+        p = float(p)
+        assert orc.silu(p) - orc.silu(-p) == pytest.approx(p, rel=1e-14, abs=1e-14)
+        assert orc.silu(p) == pytest.approx(p * special.expit(p), rel=1e-14, abs=1e-300)
+
+
+def test_silu_limits_and_no_nan():
+    assert orc.silu(0.0) == 0.0
+    assert orc.silu(60.0) == pytest.approx(60.0, rel=1e-15)
+    assert orc.silu(-1000.0) == 0.0          # e^1000 overflows: the quotient is -0, not NaN
+    assert not math.isnan(orc.silu(-1e308))
+    assert 0.0 > orc.silu(-40.0) > -1e-15
+
+
+def test_functional_set_hand_derived_boundaries():
+    # d = 1, x = 1, so p_j = W1[j]; the values are exact in float32.  |silu| against 0.1:
+    #   0.25 -> 0.1406 in,  0.125 -> 0.0664 out,  -1 -> 0.2689 in,  -5 -> 0.0335 out,
+    #  -0.25 -> 0.1094 in,  3 -> 2.858 in,  -3 -> 0.1423 in,  -4 -> 0.0719 out,  0 -> 0 out.
+    # A ReLU reading would keep only {0, 1, 5}; dropping the magnitude would lose 2, 4, 6.
+    p = np.array([0.25, 0.125, -1.0, -5.0, -0.25, 3.0, -3.0, -4.0, 0.0], np.float32)
+    x = np.ones(1, np.float32)
+    got = orc.functional_set(x, p.reshape(-1, 1), None, orc.F32, tau=0.1)
+    assert got.tolist() == [0, 2, 4, 5, 6]
+    # tau = 0: every neuron with p != 0 has a non-zero activation
+    assert orc.functional_set(x, p.reshape(-1, 1), None, orc.F32, tau=0.0).tolist() == \
+        [0, 1, 2, 3, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("dt", [orc.F32, orc.F16])
+def test_silu_ffn_difference_under_negation_is_linear(dt):
+    # silu(p) - silu(-p) = p, so y(W1, b1) - y(-W1, -b1) = W2T^T (W1 x + b1): a plain matmul.
+    # Negation is exact in every storage type.
+    rng = np.random.default_rng(5)
+    d, f = 48, 200
+    x, W1, b1, _, W2T = _layer(rng, d, f, dt, gated=False, bias=-0.4)
+    _, y_pos = orc.dense_ffn(x, W1, b1, None, W2T, orc.SILU, dt)
+    _, y_neg = orc.dense_ffn(x, -W1, -b1, None, W2T, orc.SILU, dt)
+    p = W1.astype(np.float64) @ x.astype(np.float64) + b1.astype(np.float64)
+    ref = W2T.astype(np.float64).T @ p
+    assert np.allclose(y_pos - y_neg, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("act", [orc.SILU, orc.SWIGLU])
+def test_sparse_silu_matches_logistic_masked_dense(act):
+    rng = np.random.default_rng(17)
+    d, f = 40, 160
+    x, W1, b1, Wup, W2T = _layer(rng, d, f, orc.F32, gated=act == orc.SWIGLU)
+    idx = np.sort(rng.choice(f, 70, replace=False)).astype(np.int32)
+    mask = np.zeros(f)
+    mask[idx] = 1.0
+    x64 = x.astype(np.float64)
+    p = W1.astype(np.float64) @ x64 + b1.astype(np.float64)
+    h = p * special.expit(p)
+    if act == orc.SWIGLU:
+        h = h * (Wup.astype(np.float64) @ x64)
+    ref = W2T.astype(np.float64).T @ (mask * h)
+    hh, y = orc.sparse_ffn(x, W1, b1, Wup, W2T, idx, act, orc.F32)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    assert np.allclose(hh, h[idx], rtol=1e-13, atol=1e-300)
+
+
+def test_swiglu_with_unit_up_rows_is_silu_on_the_gate():
+    # x[0] = 1 and every up row e_0 make u_j = 1 exactly, so the gated form reduces to SiLU.
+    rng = np.random.default_rng(23)
+    d, f = 32, 96
+    x, W1, b1, _, W2T = _layer(rng, d, f, orc.F32, gated=False)
+    x = x.copy()
+    x[0] = 1.0
+    Wup = np.zeros((f, d), np.float32)
+    Wup[:, 0] = 1.0
+    _, y_g = orc.dense_ffn(x, W1, b1, Wup, W2T, orc.SWIGLU, orc.F32)
+    _, y_s = orc.dense_ffn(x, W1, b1, None, W2T, orc.SILU, orc.F32)
+    assert np.array_equal(y_g, y_s)
+
+
+@pytest.mark.parametrize("pair", [(orc.SILU, orc.RELU), (orc.SWIGLU, orc.REGLU)])
+def test_silu_forms_reduce_to_relu_forms_when_every_gate_is_large(pair):
+    # With every gate pre-activation >= 40, sigmoid(p) = 1 - O(e^-40): the SiLU forms equal the
+    # ReLU forms to far below float32 resolution.
+    silu_act, relu_act = pair
+    rng = np.random.default_rng(29)
+    d, f = 24, 64
+    x, W1, _, Wup, W2T = _layer(rng, d, f, orc.F32, gated=silu_act == orc.SWIGLU)
+    b1 = np.full(f, 60.0, np.float32)
+    _, y_s = orc.dense_ffn(x, W1, b1, Wup, W2T, silu_act, orc.F32)
+    _, y_r = orc.dense_ffn(x, W1, b1, Wup, W2T, relu_act, orc.F32)
+    assert np.allclose(y_s, y_r, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("act", [orc.SILU, orc.SWIGLU])
+def test_silu_all_neurons_equals_dense_and_partition_adds_up(act):
+    rng = np.random.default_rng(31)
+    d, f = 32, 120
+    x, W1, b1, Wup, W2T = _layer(rng, d, f, orc.F32, gated=act == orc.SWIGLU)
+    _, y_dense = orc.dense_ffn(x, W1, b1, Wup, W2T, act, orc.F32)
+    _, y_all = orc.sparse_ffn(x, W1, b1, Wup, W2T, np.arange(f, dtype=np.int32), act, orc.F32)
+    assert np.array_equal(y_all, y_dense)
+    A = np.sort(rng.choice(f, 50, replace=False)).astype(np.int32)
+    B = np.setdiff1d(np.arange(f), A).astype(np.int32)
+    _, ya = orc.sparse_ffn(x, W1, b1, Wup, W2T, A, act, orc.F32)
+    _, yb = orc.sparse_ffn(x, W1, b1, Wup, W2T, B, act, orc.F32)
+    assert np.allclose(ya + yb, y_dense, rtol=0, atol=1e-12 * np.abs(y_dense).max())
+
+
+def test_functional_set_drops_only_small_terms():
+    # Over the functional set the dropped neurons each have |silu(p)| <= tau, so the error of the
+    # sparse SiLU output is bounded by tau * sum over dropped j of |W2T[j]| (triangle inequality).
+    rng = np.random.default_rng(37)
+    d, f, tau = 32, 300, 0.1
+    x, W1, b1, _, W2T = _layer(rng, d, f, orc.F32, gated=False)
+    A = orc.functional_set(x, W1, b1, orc.F32, tau=tau)
+    assert 0 < A.shape[0] < f
+    _, y_dense = orc.dense_ffn(x, W1, b1, None, W2T, orc.SILU, orc.F32)
+    _, y_sp = orc.sparse_ffn(x, W1, b1, None, W2T, A, orc.SILU, orc.F32)
+    dropped = np.setdiff1d(np.arange(f), A)
+    bound = tau * np.abs(W2T[dropped].astype(np.float64)).sum(axis=0)
+    assert np.all(np.abs(y_dense - y_sp) <= bound + 1e-12)
