@@ -55,6 +55,8 @@ def parse():
                     help="comma-separated batch sizes of the batched leg")
     ap.add_argument("--zero-skip-steps", type=int, default=500,
                     help="steps of the post-gate zero-skip legs (0: skip them)")
+    ap.add_argument("--silu-steps", type=int, default=300,
+                    help="timed steps per variant of the SwiGLU functional-sparsity leg (0 = skip)")
     ap.add_argument("--locality-steps", type=int, default=400,
                     help="steps of the hot-block (static locality) leg (0: skip it)")
     ap.add_argument("--stack-tokens", type=int, default=16,
@@ -245,6 +247,10 @@ def main():
                                                           cfg, k)}
         zero_skip["llama_reglu_layer"] = zero_skip_gated_leg(args, dev)
 
+    silu = None
+    if args.silu_steps > 0:
+        silu = silu_functional_leg(args, dev)
+
     # ---- batched union leg (OPT-30B shape) --------------------------------------------------
     batched = None
     locality_res = None
@@ -304,6 +310,7 @@ def main():
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
         "zero_skip": zero_skip,
+        "silu_functional": silu,
         "static_locality": locality_res,
         "batched_union": batched,
         "stack": stack,
@@ -435,6 +442,190 @@ def zero_skip_gated_leg(args, dev):
     log(f"zero-skip gated layer: plain {res['plain']['us_per_layer']} us, skip "
         f"{res['zero_skip']['us_per_layer']} us (predicted {count:.0f}, live {live:.0f})")
     del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def silu_functional_leg(args, dev):
+    """LLaMA-class SwiGLU layer (d 4096, f 14336, r 256, bfloat16, no bias, gate spread set for
+    ~50% functional activity).  SiLU has no exact zeros, so every sparse variant approximates the
+    dense layer; each is reported with its time and its relative L2 error against the library's
+    dense SwiGLU FFN:
+      topk_K        predictor top-K (the plain method) at K = 25%, 50%, 75% of f;
+      topk_K+skip   the same list cut inside the FFN to |silu(gate)| > 0.1 (post-gate skip);
+      functional    the dense FFN cut to |silu(gate)| > 0.1 (the functional set itself, no
+                    predictor: the error floor of the 0.1 threshold);
+      best_K        the K neurons of largest |h| (known only after the dense layer: the error
+                    floor of any K-set).
+    Recall and precision of the predicted set are against the functional set."""
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    cfg = wl.CONFIGS[5]
+    d, f, r = cfg.d, cfg.f, cfg.r
+    code = _lib.dtype_code(cfg.dtype)
+    gate_tau = 0.1
+    nl, ntok, nq = 8, 64, 16
+    layers = [wl.make_layer(cfg, device=dev, layer=l) for l in range(nl)]
+    X = wl.make_tokens(cfg, ntok, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ws_b = csf.workspace_size(_lib.OP_LAYER, 1, d, f, r, f, code)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    vp = ctypes.c_void_p
+    fn = _lib.lib.csf_sparse_ffn_layer
+    ks = [f // 4, cfg.k, 3 * f // 4]
+
+    def call(l, t, k, y_out=y, idx_out=None):
+        L = layers[l]
+        return fn(vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(L.V.data_ptr()),
+                  vp(L.U.data_ptr()), vp(L.W1.data_ptr()), None, vp(L.Wup.data_ptr()),
+                  vp(L.W2T.data_ptr()), k, ctypes.c_float(0.0), vp(y_out.data_ptr()), None,
+                  None if idx_out is None else vp(idx_out.data_ptr()), None, vp(ws.data_ptr()),
+                  ws_b, vp(stream.cuda_stream))
+
+    def set_skip(on):
+        csf.set_ffn_flags(csf.FFN_SKIP_ZERO_H if on else 0)
+        csf.set_ffn_gate_threshold(gate_tau if on else 0.0)
+
+    def timed(fn_step):
+        for s in range(16):
+            fn_step(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.silu_steps):
+            fn_step(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.silu_steps
+
+    # ---- quality over nq (layer, token) pairs -------------------------------------------------
+    def rel(a, b):
+        return float((a - b).norm() / b.norm())
+
+    q = {f"topk_{k}": [] for k in ks}
+    q.update({f"topk_{k}+skip": [] for k in ks})
+    q.update({"functional": []})
+    q.update({f"best_{k}": [] for k in ks})
+    rec, prec, ffrac, live = [], [], [], {k: [] for k in ks}
+    idx = torch.empty(f, dtype=torch.int32, device=dev)
+    ys = torch.empty(d, dtype=torch.float32, device=dev)
+    hd = torch.empty(1, f, dtype=torch.float32, device=dev)
+    hg = torch.empty(1, f, dtype=torch.float32, device=dev)
+    hk = torch.empty(1, f, dtype=torch.float32, device=dev)
+    try:
+        for s in range(nq):
+            l, t = s % nl, (s * 5) % ntok
+            L = layers[l]
+            xt = X[t:t + 1]
+            set_skip(False)
+            yd = csf.dense_ffn(xt, L.W1, None, L.Wup, L.W2T, act=cfg.act, h=hd)[0].clone()
+            # the gate activation silu(W1 x) alone: the ungated SiLU form over the same W1
+            csf.dense_ffn(xt, L.W1, None, None, L.W2T, act=csf.SILU, h=hg)
+            fset = torch.nonzero(hg[0].abs() > gate_tau).flatten()
+            ffrac.append(fset.numel() / f)
+            set_skip(True)
+            yf = csf.dense_ffn(xt, L.W1, None, L.Wup, L.W2T, act=cfg.act)[0]
+            q["functional"].append(rel(yf, yd))
+            for k in ks:
+                set_skip(False)
+                rc = call(l, t, k, ys, idx)
+                if rc:
+                    raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+                torch.cuda.synchronize()
+                q[f"topk_{k}"].append(rel(ys, yd))
+                pred = idx[:k].long()
+                if k == cfg.k:
+                    hit = int(torch.isin(pred, fset).sum())
+                    rec.append(hit / max(fset.numel(), 1))
+                    prec.append(hit / k)
+                set_skip(True)
+                csf.sparse_ffn(xt, L.W1, None, L.Wup, L.W2T, idx[:k].unsqueeze(0), act=cfg.act,
+                               h=hk[:, :k])
+                rc = call(l, t, k, ys)
+                if rc:
+                    raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+                torch.cuda.synchronize()
+                q[f"topk_{k}+skip"].append(rel(ys, yd))
+                live[k].append(int((hk[0, :k] != 0).sum()))
+                set_skip(False)
+                best = torch.sort(torch.topk(hd[0].abs(), k).indices).values.int()
+                yb = csf.sparse_ffn(xt, L.W1, None, L.Wup, L.W2T, best.unsqueeze(0), act=cfg.act)[0]
+                torch.cuda.synchronize()
+                q[f"best_{k}"].append(rel(yb, yd))
+    finally:
+        set_skip(False)
+
+    mean = lambda v: sum(v) / len(v)
+    es = 2
+    pred_b = (r * d + f * r + d) * es
+    res = {"workload": "LLaMA-class SwiGLU layer, batch 1: d 4096, f 14336, r 256, bfloat16, no "
+                       "bias, std(W1 x) 0.3", "gate_tau": gate_tau, "layers_rotated": nl,
+           "quality_pairs": nq, "functional_frac": round(mean(ffrac), 4),
+           "recall_vs_functional": round(mean(rec), 4), "precision_vs_functional": round(mean(prec), 4),
+           "rel_l2_err": {n: round(mean(v), 4) for n, v in q.items()}}
+
+    # ---- timing ---------------------------------------------------------------------------------
+    L0 = layers[0]
+    dws_b = csf.workspace_size(_lib.OP_DENSE_FFN, 1, d, f, 0, f, code)
+    dws = torch.empty(dws_b, dtype=torch.uint8, device=dev)
+    dfn = _lib.lib.csf_dense_ffn
+
+    def dense_step(s):
+        L = layers[s % nl]
+        rc = dfn(vp(X[(s * 7) % ntok].data_ptr()), 1, d, f, cfg.act, code, vp(L.W1.data_ptr()),
+                 None, vp(L.Wup.data_ptr()), vp(L.W2T.data_ptr()), None, vp(y.data_ptr()),
+                 vp(dws.data_ptr()), dws_b, vp(stream.cuda_stream))
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+
+    us_dense = timed(dense_step)
+    timing = {"dense": {"us_per_layer": round(us_dense, 3), "bytes": 3 * f * d * es}}
+    try:
+        for k in ks:
+            for skip in (False, True):
+                set_skip(skip)
+                us = timed(lambda s: call(s % nl, (s * 7) % ntok, k))
+                nb = pred_b + (k * d * es + mean(live[k]) * 2 * d * es if skip else k * 3 * d * es)
+                timing[f"topk_{k}" + ("+skip" if skip else "")] = {
+                    "us_per_layer": round(us, 3), "bytes_needed": int(nb),
+                    "GBps_on_bytes_needed": round(nb / (us * 1e-6) / 1e9, 1),
+                    "speedup_vs_dense": round(us_dense / us, 3)}
+    finally:
+        set_skip(False)
+    # per-kernel times of the 50% layer, plain and with the skip (library trace hook)
+    kern = {}
+    try:
+        for skip in (False, True):
+            set_skip(skip)
+            n = 50
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
+                   for _ in range(n)]
+            for row in evs:
+                for e in row:
+                    e.record(stream)
+            torch.cuda.synchronize()
+            for s in range(n):
+                csf.set_trace_events(evs[s])
+                call(s % nl, (s * 7) % ntok, cfg.k)
+            csf.set_trace_events([])
+            torch.cuda.synchronize()
+            kern["skip" if skip else "plain"] = {
+                name: round(sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(n))
+                            * 1e3 / n, 3) for i, name in enumerate(KERNELS)}
+    finally:
+        csf.set_trace_events([])
+        set_skip(False)
+    res["live_after_skip_mean"] = {str(k): round(mean(live[k]), 1) for k in ks}
+    res["timing"] = timing
+    res[f"kernels_avg_us_topk_{cfg.k}"] = kern
+    log(f"SwiGLU functional: dense {us_dense:.1f} us; top-{cfg.k} "
+        f"{timing[f'topk_{cfg.k}']['us_per_layer']} us err {res['rel_l2_err'][f'topk_{cfg.k}']}; "
+        f"+skip {timing[f'topk_{cfg.k}+skip']['us_per_layer']} us err "
+        f"{res['rel_l2_err'][f'topk_{cfg.k}+skip']}; functional-set err {res['rel_l2_err']['functional']}")
+    del layers, L0
     torch.cuda.empty_cache()
     return res
 

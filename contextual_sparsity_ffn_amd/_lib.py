@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsf.so")
 
 F32, F16, BF16 = 0, 1, 2
-RELU, REGLU = 0, 1
+RELU, REGLU, SILU, SWIGLU = 0, 1, 2, 3
+GATED_ACTS = (REGLU, SWIGLU)
 OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
     OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK = range(9)
 STACK_SYNC, STACK_LOOKAHEAD, STACK_GRAPH = 0, 1, 0x100
@@ -34,7 +35,7 @@ EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_worksp
            "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_layer_hot",
            "csf_sparse_ffn_batched_union",
            "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
-           "csf_set_trace_events")
+           "csf_set_ffn_gate_threshold", "csf_set_trace_events")
 
 
 class LayerWeights(ctypes.Structure):
@@ -72,6 +73,7 @@ def _load():
     L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csf_set_trace_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     L.csf_set_ffn_flags.argtypes = [i32]
+    L.csf_set_ffn_gate_threshold.argtypes = [flt]
     L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
                                        flt, vp, vp, vp, vp, vp, sz, vp]
     L.csf_sparse_ffn_layer_hot.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
@@ -229,10 +231,10 @@ def _ffn_weights(x, W1, b1, Wup, W2T, act):
     _tensor(W1, "W1", dtype=dt, device=dev)
     _tensor(W2T, "W2T", dtype=dt, shape=(f, d), device=dev)
     _tensor(b1, "b1", dtype=torch.float32, shape=(f,), device=dev, optional=True)
-    if act == REGLU:
+    if act in GATED_ACTS:
         _tensor(Wup, "Wup", dtype=dt, shape=(f, d), device=dev)
     elif Wup is not None:
-        raise ValueError("Wup is only used with the gated (REGLU) activation")
+        raise ValueError("Wup is only used with the gated activations (REGLU, SWIGLU)")
     return dev, dt, f, d
 
 
@@ -290,6 +292,11 @@ def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
 def set_ffn_flags(flags):
     """Options of the gathered FFN for later calls on this thread (FFN_SKIP_ZERO_H or 0)."""
     _check(lib.csf_set_ffn_flags(int(flags)))
+
+
+def set_ffn_gate_threshold(tau):
+    """gate_tau of the post-gate skip for later calls on this thread (0 = exact zero-skip)."""
+    _check(lib.csf_set_ffn_gate_threshold(float(tau)))
 
 
 def set_trace_events(events):

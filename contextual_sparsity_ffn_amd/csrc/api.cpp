@@ -20,6 +20,7 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t g_trace_events[16];
 thread_local int g_trace_n = 0;
 thread_local int g_ffn_flags = 0;
+thread_local float g_gate_tau = 0.0f;
 
 int fail(int status, const char *fmt, ...)
 {
@@ -270,17 +271,17 @@ int validate_ffn(const void *x, int B, int d, int f, int act, int dtype, const v
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
     REQUIRE(valid_dtype(dtype), CSF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-    REQUIRE(act == CSF_ACT_RELU || act == CSF_ACT_REGLU, CSF_ERR_INVALID_ARG,
+    REQUIRE(act >= CSF_ACT_RELU && act <= CSF_ACT_SWIGLU, CSF_ERR_INVALID_ARG,
             "unknown activation %d", act);
     CHECK_ROW(d, dtype, kMaxRowChunks);
     CHECK_PTR(x, B > 0);
     CHECK_PTR(W1, true);
     CHECK_PTR(W2T, true);
     CHECK_PTR(b1, false);
-    if (act == CSF_ACT_REGLU) {
+    if (act == CSF_ACT_REGLU || act == CSF_ACT_SWIGLU) {
         CHECK_PTR(Wup, true);
     } else {
-        REQUIRE(Wup == nullptr, CSF_ERR_INVALID_ARG, "Wup must be NULL for CSF_ACT_RELU");
+        REQUIRE(Wup == nullptr, CSF_ERR_INVALID_ARG, "Wup must be NULL for the ungated forms");
     }
     return CSF_OK;
 }
@@ -497,6 +498,7 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
         fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
         fa.accumulate = 1;
         fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+        fa.gate_tau = g_gate_tau;
         e = csf::launch_ffn(fa, st);
         if (e != hipSuccess)
             return hip_status(e, "stack FFN launch");
@@ -531,6 +533,14 @@ int csf_set_ffn_flags(int flags)
     REQUIRE((flags & ~CSF_FFN_SKIP_ZERO_H) == 0, CSF_ERR_INVALID_ARG, "unknown FFN flags 0x%x",
             flags);
     g_ffn_flags = flags;
+    return ok();
+}
+
+int csf_set_ffn_gate_threshold(float tau)
+{
+    REQUIRE(tau >= 0.0f && tau <= 3.4e38f, CSF_ERR_INVALID_ARG,
+            "gate threshold %g must be finite and >= 0", (double)tau);
+    g_gate_tau = tau;
     return ok();
 }
 
@@ -678,6 +688,7 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
     a.y = y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
     a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    a.gate_tau = g_gate_tau;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "sparse FFN launch");
 }
 
@@ -716,6 +727,7 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     a.y = Y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
     a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    a.gate_tau = g_gate_tau;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "dense FFN launch");
 }
 
@@ -881,6 +893,7 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
     fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    fa.gate_tau = g_gate_tau;
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 
@@ -956,6 +969,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
     fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    fa.gate_tau = g_gate_tau;
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 
@@ -1024,6 +1038,7 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
     mix(ints, sizeof ints);
     mix(&tau, sizeof tau);
     mix(&eps, sizeof eps);
+    mix(&g_gate_tau, sizeof g_gate_tau);
     mix(&ws_bytes, sizeof ws_bytes);
     StackGraph &g = g_stack_graph;
     if (!(g.exec && g.key == key)) {

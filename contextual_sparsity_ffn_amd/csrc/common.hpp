@@ -126,6 +126,18 @@ struct BF16T {
     __device__ static __forceinline__ float widen_bits(uint16_t b) { return u2f((uint32_t)b << 16); }
 };
 
+// Activation codes (the csf_act values): 0 ReLU, 1 ReGLU, 2 SiLU, 3 SwiGLU.  The gated forms
+// multiply the gate activation by the up projection W_up x.
+__host__ __device__ constexpr bool act_gated(int act) { return act == 1 || act == 3; }
+__host__ __device__ constexpr int act_silu(int act) { return act == 2 || act == 3 ? 1 : 0; }
+
+// The gate nonlinearity of the FFN: ReLU (the ReLU and ReLU-fied gated forms) or SiLU,
+// silu(p) = p / (1 + exp(-p)) (the LLaMA-style forms, never exactly zero).
+__device__ __forceinline__ float gate_act(float p, int silu)
+{
+    return silu ? p / (1.0f + expf(-p)) : (p > 0.0f ? p : 0.0f);
+}
+
 // Sum over the 64 lanes of a wavefront; every lane receives the total.  The butterfly order is
 // fixed, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v)

@@ -44,9 +44,10 @@ struct UpShape {
     static constexpr int RPW = loads >= 12 ? 1 : (loads >= 6 ? 2 : 4);
 };
 
-// SKIP (gated form only): the up rows are read only for neurons whose gate is positive (the
-// others have h = 0 whatever the up row holds): the gate dot products are finished first, then
-// the workgroup loads the up rows that are still needed.
+// SKIP (post-gate skip): a neuron whose gate activation a = act(W1[j].x + b1_j) has
+// |a| <= gate_tau gets h = 0 (for the ReLU forms with gate_tau = 0: exactly the neurons whose h is
+// zero anyway).  In the gated forms the gate dot products are finished first and the workgroup
+// then loads only the up rows that are still needed.
 template <class T, int MX, bool GATED, bool SKIP = false, int RPW = UpShape<MX, GATED>::RPW>
 __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
                                                    const u32x4 *__restrict__ W1,
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
                                                    int idx_stride,
                                                    const int32_t *__restrict__ count,
                                                    int max_count, int f, int C,
-                                                   float *__restrict__ h, int h_stride)
+                                                   float *__restrict__ h, int h_stride, int silu,
+                                                   float gate_tau)
 {
     __shared__ float red[4][RPW][GATED ? 2 : 1];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
             float p = (red[0][i][0] + red[1][i][0]) + (red[2][i][0] + red[3][i][0]);
             if (b1 && jr[i] >= 0)
                 p += b1[jr[i]];
-            const bool live = jr[i] >= 0 && p > 0.0f;      // uniform across the workgroup
+            // uniform across the workgroup
+            const bool live = jr[i] >= 0 && fabsf(gate_act(p, silu)) > gate_tau;
             const u32x4 *urow = Wup + (size_t)(live ? jr[i] : 0) * C;
 #pragma unroll
             for (int m = 0; m < MX; ++m) {
@@ -161,13 +164,14 @@ __global__ __launch_bounds__(256) void k_gather_up(const u32x4 *__restrict__ x,
         float p = (red[0][i][0] + red[1][i][0]) + (red[2][i][0] + red[3][i][0]);
         if (b1)
             p += b1[jr[i]];
-        float hv = p > 0.0f ? p : 0.0f;
+        float hv = gate_act(p, silu);
+        const bool drop = SKIP && !(fabsf(hv) > gate_tau);
         if constexpr (GATED) {
             const int g = GATED ? 1 : 0;
             const float u = (red[0][i][g] + red[1][i][g]) + (red[2][i][g] + red[3][i][g]);
             hv *= u;
         }
-        h[(size_t)token * h_stride + n0 + i] = hv;
+        h[(size_t)token * h_stride + n0 + i] = drop ? 0.0f : hv;
     }
 }
 
@@ -317,15 +321,16 @@ hipError_t up_launch(const FfnArgs &a, int C, hipStream_t st, Trace *tr)
     const int blocks = (a.max_count + RPW - 1) / RPW;
     if (blocks == 0)
         return hipSuccess;
-    if (GATED && a.skip_zero)
+    const int silu = act_silu(a.act);
+    if (a.skip_zero)
         return launch(k_gather_up<T, MX, GATED, true>, dim3(blocks, a.B), dim3(256), st, tr,
                       static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
                       static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count,
-                      a.max_count, a.f, C, a.h, a.h_stride);
+                      a.max_count, a.f, C, a.h, a.h_stride, silu, a.gate_tau);
     return launch(k_gather_up<T, MX, GATED>, dim3(blocks, a.B), dim3(256), st, tr,
                   static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.W1),
                   static_cast<const u32x4 *>(a.Wup), a.b1, a.idx, a.idx_stride, a.count,
-                  a.max_count, a.f, C, a.h, a.h_stride);
+                  a.max_count, a.f, C, a.h, a.h_stride, silu, 0.0f);
 }
 
 template <class T, bool GATED>
@@ -346,7 +351,7 @@ template <class T>
 hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / T::E;
-    hipError_t e = a.act == 1 ? up_gated<T, true>(a, C, st, tr) : up_gated<T, false>(a, C, st, tr);
+    hipError_t e = act_gated(a.act) ? up_gated<T, true>(a, C, st, tr) : up_gated<T, false>(a, C, st, tr);
     if (e != hipSuccess)
         return e;
     const int nchunk = ffn_num_chunks(a.d, a.dtype, a.max_count);

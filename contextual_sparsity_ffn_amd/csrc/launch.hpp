@@ -93,8 +93,10 @@ struct FfnArgs {
     float *y;               // [B][d]
     float *partials;        // [B][ffn_num_chunks][d] workspace
     int accumulate = 0;     // 1: y += the FFN output (residual add)
-    int skip_zero = 0;      // 1: rows with h = 0 are not read (down rows; up rows of the gated
-                            // form whose gate is not positive)
+    int skip_zero = 0;      // 1: post-gate skip: a neuron whose |gate activation| <= gate_tau
+                            // gets h = 0, and rows with h = 0 are not read (down rows; up rows
+                            // of the gated forms)
+    float gate_tau = 0.0f;
 };
 // Shape of the down projection's two-phase reduction (sizes its workspace).
 int ffn_num_slices(int d, int dtype);

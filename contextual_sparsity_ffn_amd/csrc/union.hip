@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void k_union_up_valu(const u32x4 *__restrict__
                                                        const int32_t *__restrict__ ucount,
                                                        const uint32_t *__restrict__ bitmaps,
                                                        int per_token, int B, int f, int C,
-                                                       float *__restrict__ h, int hs)
+                                                       float *__restrict__ h, int hs, int silu)
 {
     constexpr int NV = GATED ? 2 : 1;
     __shared__ float red[4][kMaxUnionBatch][RPW][NV];
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void k_union_up_valu(const u32x4 *__restrict__
             float p = (red[0][tok][i][0] + red[1][tok][i][0]) + (red[2][tok][i][0] + red[3][tok][i][0]);
             if (b1)
                 p += b1[j];
-            float hv = p > 0.0f ? p : 0.0f;
+            float hv = gate_act(p, silu);
             if constexpr (GATED)
                 hv *= (red[0][tok][i][NV - 1] + red[1][tok][i][NV - 1]) +
                       (red[2][tok][i][NV - 1] + red[3][tok][i][NV - 1]);
@@ -292,7 +292,8 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
                                                        const uint32_t *__restrict__ bitmaps,
                                                        int per_token, int B, int f, int C,
                                                        uint16_t *__restrict__ hhi,
-                                                       uint16_t *__restrict__ hlo, int hs)
+                                                       uint16_t *__restrict__ hlo, int hs,
+                                                       int silu)
 {
     constexpr int NV = GATED ? 2 : 1;
     constexpr int ROWS = 16 * NT;
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
                 float p = (red[0][q][mi][l] + red[1][q][mi][l]) + (red[2][q][mi][l] + red[3][q][mi][l]);
                 if (b1)
                     p += b1[jj];
-                hv = p > 0.0f ? p : 0.0f;
+                hv = gate_act(p, silu);
                 if constexpr (GATED) {
                     const int qv = NT + q;
                     hv *= (red[0][qv][mi][l] + red[1][qv][mi][l]) + (red[2][qv][mi][l] + red[3][qv][mi][l]);
@@ -559,7 +560,7 @@ hipError_t up_valu(const UnionArgs &a, int C, hipStream_t st, Trace *tr)
     return launch(k_union_up_valu<T, MX, GATED, RPW>, dim3(blocks), dim3(256), st, tr,
                   static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                   static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
-                  a.per_token, a.B, a.f, C, a.h32, a.hs);
+                  a.per_token, a.B, a.f, C, a.h32, a.hs, act_silu(a.act));
 }
 
 template <class T, bool GATED>
@@ -580,7 +581,7 @@ template <class T>
 hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / T::E;
-    hipError_t e = a.act == 1 ? up_valu_mx<T, true>(a, C, st, tr) : up_valu_mx<T, false>(a, C, st, tr);
+    hipError_t e = act_gated(a.act) ? up_valu_mx<T, true>(a, C, st, tr) : up_valu_mx<T, false>(a, C, st, tr);
     if (e != hipSuccess)
         return e;
     const int nchunk = union_num_chunks(0, a.d, a.dtype, a.f);
@@ -610,18 +611,19 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
     const int tiles = (a.f + kKStep - 1) / kKStep * kKStep / ROWS;
     const int blocks = tiles < 4096 ? tiles : 4096;
     hipError_t e;
-    if (a.act == 1)
+    if (act_gated(a.act))
         e = launch(k_union_up_mfma<T, MT, 1, true, 4>, dim3((a.f + kKStep - 1) / kKStep * 2 < 4096
                                                                ? (a.f + kKStep - 1) / kKStep * 2
                                                                : 4096),
                    dim3(256), st, tr, static_cast<const u32x4 *>(a.X),
                    static_cast<const u32x4 *>(a.W1), static_cast<const u32x4 *>(a.Wup), a.b1,
-                   a.ulist, a.ucount, a.bitmaps, a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
+                   a.ulist, a.ucount, a.bitmaps, a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs,
+                   act_silu(a.act));
     else
         e = launch(k_union_up_mfma<T, MT, NT, false, 4>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
-                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs);
+                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
     if (e != hipSuccess)
         return e;
     const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f);

@@ -28,7 +28,8 @@ ROLE_U, ROLE_V, ROLE_W1_NOISE, ROLE_W2T, ROLE_WUP, ROLE_TOKENS = 1, 2, 3, 4, 5, 
 ROLE_CALIB, ROLE_CENTROIDS, ROLE_CLUSTER_IDS, ROLE_CLUSTER_NOISE = 7, 8, 9, 10
 ROLE_POWERLAW, ROLE_PROFILE = 11, 12
 
-RELU, REGLU = 0, 1
+RELU, REGLU, SILU, SWIGLU = 0, 1, 2, 3
+GATED = (REGLU, SWIGLU)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -55,16 +56,21 @@ class Config:
         """The same recipe at another shape (parity tests); k defaults to the same fraction of f."""
         if k is None and self.k is not None:
             k = int(math.floor(f * self.k / self.f + 0.5))
-        gated = self.act == REGLU
+        gated = self.act in GATED
+        # ReLU recipes: unit-scale factors (the bias sets the sparsity).  SiLU recipes keep the
+        # gate's spread, std(W1 x) = uv_std^2 sqrt(r d), which sets the functional sparsity.
+        uv = (1.0 / math.sqrt(r) if self.act in (RELU, REGLU)
+              else self.uv_std * (self.r * self.d / (r * d)) ** 0.25)
         return dataclasses.replace(self, d=d, f=f, r=r, k=k, tokens=tokens,
-                                   uv_std=1.0 / math.sqrt(r), noise_std=0.1 / d,
+                                   uv_std=uv, noise_std=0.1 / d,
                                    w2t_std=1.0 / math.sqrt(d if gated else f),
                                    wup_std=1.0 / math.sqrt(d) if gated else 0.0)
 
 
-# The five workloads: a tiny float32 layer; the OPT-175B FFN shape at 5% (the headline case); a
+# The workloads: a tiny float32 layer; the OPT-175B FFN shape at 5% (the headline case); a
 # LLaMA-class gated (ReGLU) layer in bfloat16 with a sigmoid >= 0.5 threshold; the OPT-30B FFN shape
-# at 20% for batch-union studies; and a 48-layer stack of that shape.
+# at 20% for batch-union studies; a 48-layer stack of that shape; and the SwiGLU form of the
+# LLaMA-class layer (functional sparsity).
 CONFIGS = {
     0: Config(0, "tiny-relu-f32", 256, 1024, 64, torch.float32, RELU, 102, None,
               uv_std=1 / 8, noise_std=0.1 / 256, w2t_std=1 / 32, wup_std=0.0, bias=-0.5,
@@ -81,6 +87,12 @@ CONFIGS = {
     4: Config(4, "opt30b-relu-f16-stack48", 7168, 28672, 512, torch.float16, RELU, 5734, None,
               uv_std=1 / math.sqrt(512), noise_std=0.1 / 7168, w2t_std=1 / math.sqrt(28672),
               wup_std=0.0, bias=None, positive_frac=0.20, tokens=128, layers=48),
+    # The LLaMA-class block before ReLU-fication: SwiGLU, no bias, the gate's spread chosen so
+    # that |silu(W1 x)| > 0.1 for about half of the neurons (std(W1 x) = 0.3), the ~50%
+    # functional sparsity the pages give for SiLU models; top-k keeps half of the neurons.
+    5: Config(5, "llama-swiglu-bf16", 4096, 14336, 256, torch.bfloat16, SWIGLU, 7168, None,
+              uv_std=(0.09 / (256 * 4096)) ** 0.25, noise_std=0.1 / 4096, w2t_std=1 / 64,
+              wup_std=1 / 64, bias=0.0, positive_frac=None, tokens=256),
 }
 
 
@@ -126,7 +138,7 @@ def make_layer(cfg: Config, device="cpu", layer: int = 0, config_id: Optional[in
     del W1_32
     W2T = normal((f, d), cfg.w2t_std, device, seed(c, ROLE_W2T, layer)).to(dt)
     Wup = None
-    if cfg.act == REGLU:
+    if cfg.act in GATED:
         Wup = normal((f, d), cfg.wup_std, device, seed(c, ROLE_WUP, layer)).to(dt)
     V, U = V32.to(dt), U32.to(dt)
     del U32, V32
@@ -208,11 +220,11 @@ def touched_bytes(cfg: Config, count: int) -> int:
     """Algorithmic bytes one batch-1 layer step reads: predictor V and U, `count` active rows of W1
     (and W_up) and W2T, and x."""
     es = torch.tensor([], dtype=cfg.dtype).element_size()
-    rows = 3 if cfg.act == REGLU else 2
+    rows = 3 if cfg.act in GATED else 2
     return es * (cfg.r * cfg.d + cfg.f * cfg.r + count * rows * cfg.d + cfg.d)
 
 
 def dense_bytes(cfg: Config) -> int:
     es = torch.tensor([], dtype=cfg.dtype).element_size()
-    rows = 3 if cfg.act == REGLU else 2
+    rows = 3 if cfg.act in GATED else 2
     return es * rows * cfg.f * cfg.d

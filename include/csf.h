@@ -55,11 +55,19 @@ typedef enum {
 
 typedef enum { CSF_F32 = 0, CSF_F16 = 1, CSF_BF16 = 2 } csf_dtype;
 
-/* CSF_ACT_RELU:  h_j = max(0, W1[j].x + b1_j)                       ([DV] "Kernel-Level
- *                Implementation": dot product then max(acc, 0)).
- * CSF_ACT_REGLU: h_j = max(0, W1[j].x + b1_j) * (Wup[j].x), with W1 the gate projection
- *                ([DV] "The SiLU/GELU Challenge: TurboSparse", the ReLU-fied gated form). */
-typedef enum { CSF_ACT_RELU = 0, CSF_ACT_REGLU = 1 } csf_act;
+/* CSF_ACT_RELU:   h_j = max(0, W1[j].x + b1_j)                      ([DV] "Kernel-Level
+ *                 Implementation": dot product then max(acc, 0)).
+ * CSF_ACT_REGLU:  h_j = max(0, W1[j].x + b1_j) * (Wup[j].x), with W1 the gate projection
+ *                 ([DV] "The SiLU/GELU Challenge: TurboSparse", the ReLU-fied gated form).
+ * CSF_ACT_SILU:   h_j = silu(W1[j].x + b1_j), silu(p) = p / (1 + e^-p)  ([DV] "The Prediction
+ *                 Problem": the sparse sketch's activation).
+ * CSF_ACT_SWIGLU: h_j = silu(W1[j].x + b1_j) * (Wup[j].x)  ([DV] "The SiLU/GELU Challenge":
+ *                 the LLaMA-style block before ReLU-fication).
+ * SiLU is never exactly zero: over a predicted set the SiLU forms approximate the dense layer
+ * (functional sparsity, [DV] "The Empirical Foundation"); the ReLU forms are exact over any set
+ * that holds every neuron with a positive gate.  The float32 exponential is the device
+ * library's expf. */
+typedef enum { CSF_ACT_RELU = 0, CSF_ACT_REGLU = 1, CSF_ACT_SILU = 2, CSF_ACT_SWIGLU = 3 } csf_act;
 
 /* Operation codes for csf_workspace_size. */
 typedef enum {
@@ -86,7 +94,7 @@ typedef enum {
 } csf_stack_mode;
 
 /* One block of a stack: predictor and FFN weights, shapes and layouts as for
- * csf_sparse_ffn_layer (Wup only for CSF_ACT_REGLU, b1 optional). */
+ * csf_sparse_ffn_layer (Wup only for the gated forms, b1 optional). */
 typedef struct {
     const void *V, *U, *W1, *Wup, *W2T;
     const float *b1;
@@ -174,7 +182,7 @@ int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *
  *   x        [B][d]  dtype
  *   W1       [f][d]  dtype     gate (ReLU: the up) projection
  *   b1       [f]     float32   optional (NULL = no bias)
- *   Wup      [f][d]  dtype     CSF_ACT_REGLU only, else NULL
+ *   Wup      [f][d]  dtype     gated forms (CSF_ACT_REGLU, CSF_ACT_SWIGLU) only, else NULL
  *   W2T      [f][d]  dtype     down projection, neuron-major
  *   idx      [B][idx_stride] int32  active lists (ascending, values in [0, f))
  *   count    [B]     int32     optional device lengths; NULL = every list has max_count entries
@@ -332,16 +340,32 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
  * csf_set_ffn_flags -- options of the gathered FFN for later calls on the calling thread
  * (csf_sparse_ffn, csf_dense_ffn, csf_sparse_ffn_layer, csf_stack_forward; not the batched union
  * path).  0 (the default) restores the plain method.
- *   CSF_FFN_SKIP_ZERO_H  post-gate zero-skip: a listed neuron whose activation h is exactly 0 is
- *                        dropped before its down row is read, and in the gated form its up row
- *                        is read only if its gate is positive.  The skipped terms are zero, so
- *                        y is the same up to float32 summation order.  A predictor tuned for
- *                        recall over-predicts ([CP] "Precision, recall, and which error hurts":
- *                        a false positive costs bandwidth), so most of the skipped rows are its
- *                        false positives.
+ *   CSF_FFN_SKIP_ZERO_H  post-gate skip: the gate activation a_j = act(W1[j].x + b1_j) of each
+ *                        listed neuron is computed first; a neuron with |a_j| <= gate_tau (see
+ *                        csf_set_ffn_gate_threshold; default 0) gets h_j = 0, its up row (gated
+ *                        forms) and its down row are not read, and any other neuron whose h_j
+ *                        is exactly 0 is dropped before its down row is read.  With gate_tau = 0
+ *                        the ReLU forms lose nothing (the skipped terms are zero), so y is the
+ *                        same up to float32 summation order.  A predictor tuned for recall
+ *                        over-predicts ([CP] "Precision, recall, and which error hurts": a false
+ *                        positive costs bandwidth), so most of the skipped rows are its false
+ *                        positives.
  * ------------------------------------------------------------------------------------------- */
 #define CSF_FFN_SKIP_ZERO_H 1
 int csf_set_ffn_flags(int flags);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_set_ffn_gate_threshold -- the gate_tau of CSF_FFN_SKIP_ZERO_H for later calls on the
+ * calling thread (0 by default).  tau > 0 applies the functional activity test of [DV] "The
+ * Empirical Foundation" (measure_mlp_sparsity: a neuron counts when the magnitude of its
+ * activation exceeds a threshold, 0.1 there) inside the FFN: a SiLU gate is never exactly zero
+ * ([DV] "The SiLU/GELU Challenge"), so the listed neurons are cut to those with |a_j| > tau
+ * before their up and down rows are read.  This approximates the layer: each dropped neuron
+ * changes y by at most tau * |Wup[j].x| * |W2T[j]| per element (without the Wup factor for the
+ * ungated forms).  The test is taken in float32 on the kernel's own a_j.
+ *   tau   >= 0 and finite, else CSF_ERR_INVALID_ARG (the previous value is kept).
+ * ------------------------------------------------------------------------------------------- */
+int csf_set_ffn_gate_threshold(float tau);
 
 /* ---------------------------------------------------------------------------------------------
  * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer,

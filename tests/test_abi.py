@@ -96,9 +96,12 @@ def sparse(x=P, B=1, d=64, f=100, act=csf.RELU, dt=csf.F16, W1=P, b1=NULL, Wup=N
 def test_sparse_ffn_validation():
     assert sparse(maxc=11) == INVALID                      # max_count > idx_stride
     assert sparse(maxc=-1) == INVALID
-    assert sparse(act=2) == INVALID
+    assert sparse(act=4) == INVALID
+    assert sparse(act=-1) == INVALID
     assert sparse(act=csf.REGLU) == INVALID                # gated form needs Wup
+    assert sparse(act=csf.SWIGLU) == INVALID               # gated form needs Wup
     assert sparse(Wup=P) == INVALID                        # ... and ReLU must not get one
+    assert sparse(act=csf.SILU, Wup=P) == INVALID          # ... nor SiLU
     assert sparse(W2T=NULL) == INVALID
     assert sparse(b1=Q) == MISALIGNED
     assert sparse(d=12) == UNSUPPORTED
@@ -210,6 +213,11 @@ def test_ffn_flags_validation():
     assert L.csf_set_ffn_flags(2) == INVALID
     assert L.csf_set_ffn_flags(csf.FFN_SKIP_ZERO_H) == OK
     assert L.csf_set_ffn_flags(0) == OK
+    assert L.csf_set_ffn_gate_threshold(-0.5) == INVALID
+    assert L.csf_set_ffn_gate_threshold(float("nan")) == INVALID
+    assert L.csf_set_ffn_gate_threshold(float("inf")) == INVALID
+    assert L.csf_set_ffn_gate_threshold(0.1) == OK
+    assert L.csf_set_ffn_gate_threshold(0.0) == OK
 
 
 def test_k_from_ratio_matches_the_printed_figures():

@@ -71,6 +71,9 @@ CASES = [
     ("f16-B32", wl.CONFIGS[3].scaled(1024, 1601, 64), 32, 0.2),
     ("bf16-reglu-B3", wl.CONFIGS[2].scaled(512, 1433, 64), 3, 0.3),
     ("bf16-reglu-B20", wl.CONFIGS[2].scaled(512, 1433, 64), 20, 0.3),
+    ("bf16-swiglu-B3", wl.CONFIGS[5].scaled(512, 1433, 64), 3, 0.5),
+    ("bf16-swiglu-B20", wl.CONFIGS[5].scaled(512, 1433, 64), 20, 0.5),
+    ("f16-silu-B8", dataclasses.replace(wl.CONFIGS[3].scaled(512, 1000, 64), act=csf.SILU), 8, 0.3),
 ]
 PATHS = [("gather", csf.PATH_GATHER), ("mfma", csf.PATH_MFMA)]
 

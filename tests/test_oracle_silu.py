@@ -159,3 +159,18 @@ def test_functional_set_drops_only_small_terms():
     dropped = np.setdiff1d(np.arange(f), A)
     bound = tau * np.abs(W2T[dropped].astype(np.float64)).sum(axis=0)
     assert np.all(np.abs(y_dense - y_sp) <= bound + 1e-12)
+
+
+def test_swiglu_workload_is_about_half_functionally_active():
+    # The SwiGLU recipe sets the gate's spread so that about half of the neurons pass the
+    # functional test, the ~50% the SiLU/GELU passage gives for SiLU models; scaled() keeps the
+    # spread at other shapes.
+    from contextual_sparsity_ffn_amd import workloads as wl
+    from csf_testutil import layer_to_orc, to_orc
+    cfg = wl.CONFIGS[5].scaled(1024, 4096, 64)
+    L = wl.make_layer(cfg)
+    o = layer_to_orc(L)
+    X = wl.make_tokens(cfg, 4)
+    for t in range(4):
+        frac = orc.functional_set(to_orc(X[t]), o["W1"], o["b1"], o["dt"], tau=0.1).shape[0] / cfg.f
+        assert 0.4 < frac < 0.6, frac
