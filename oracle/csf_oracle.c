@@ -349,3 +349,131 @@ int orc_rms_normalize(const float *x, int d, double eps, int dt, void *xhat_out 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* O9 -- attention-head sparsity: one decode step of multi-head attention over a set of heads. */
+/* [DV] opening section: for a given input a small set of attention heads (with the MLP        */
+/* neurons) approximates the dense layer; "The Empirical Foundation": only a fifth to a third  */
+/* of the heads matter per token; "Implications for System Design": selecting heads per token  */
+/* saves attention work and, above all, key/value cache traffic and memory.                    */
+/* The page gives no formulas; the step is standard multi-head attention for one new token:    */
+/*   q_h = Wq_h x + bq_h,  k_h = Wk_h x + bk_h,  v_h = Wv_h x + bv_h   (Wq_h: rows h*dh..+dh-1) */
+/*   the new k_h, v_h are rounded to the cache's storage type and appended at position len_h;  */
+/*   a_t = q_h . K_h[t] / sqrt(dh) for t = 0..len_h (the new token included), p = softmax(a),  */
+/*   o_h = sum_t p_t V_h[t];  y = sum over the computed heads of WoT_h^T o_h.                  */
+/* Readings: heads outside the set compute nothing for this token; with kv_all = 0 they also   */
+/* store nothing (their cache does not grow: the saving in cache memory the page points to),   */
+/* with kv_all = 1 every head appends its k, v (the cache stays complete, only q, the          */
+/* attention and the output projection are sparse).  No output bias (it does not depend on the  */
+/* selection).  Caches are [H][Tmax][dh] in the storage type, WoT [H*dh][d] (head-dimension   */
+/* major, the analogue of the neuron-major down projection).                                   */
+/* Returns 0, -1 for bad arguments, -4 for a head index outside [0, H), -5 for a full cache.   */
+/* ------------------------------------------------------------------------------------------ */
+static void store_elem(void *base, size_t i, int dt, double v)
+{
+    if (dt == ORC_F32)
+        ((float *)base)[i] = (float)v;
+    else if (dt == ORC_F16)
+        ((uint16_t *)base)[i] = orc_f64_to_f16(v);
+    else
+        ((uint16_t *)base)[i] = orc_f64_to_bf16(v);
+}
+
+/* One row of a head-major projection: W[row] . x + b[row]. */
+static double proj_row(const void *W, const float *b, const void *x, int d, int dt, size_t row)
+{
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c)
+        acc += wid(W, row * (size_t)d + c, dt) * wid(x, c, dt);
+    if (b)
+        acc += (double)b[row];
+    return acc;
+}
+
+int orc_attention_decode(const void *x, int d, int H, int dh, int dt, const void *Wq,
+                         const void *Wk, const void *Wv, const float *bq, const float *bk,
+                         const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
+                         int32_t *len, const int32_t *heads, int count, int kv_all,
+                         double *o_out /* [count][dh] or NULL */, double *y_out /* [d] */)
+{
+    if (d <= 0 || H <= 0 || dh <= 0 || Tmax <= 0 || count < 0 || count > H || bad_dtype(dt))
+        return -1;
+    if (!x || !Wq || !Wk || !Wv || !WoT || !Kc || !Vc || !len || !y_out || (count > 0 && !heads))
+        return -1;
+    char *store = (char *)calloc((size_t)H, 1);
+    double *q = (double *)malloc(sizeof(double) * (size_t)dh);
+    double *o = (double *)malloc(sizeof(double) * (size_t)dh);
+    double *a = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+    int rc = 0;
+    if (!store || !q || !o || !a) {
+        rc = -1;
+        goto done;
+    }
+    for (int n = 0; n < count; ++n) {
+        if (heads[n] < 0 || heads[n] >= H) {
+            rc = -4;
+            goto done;
+        }
+        store[heads[n]] = 1;
+    }
+    for (int h = 0; h < H; ++h) {
+        if (kv_all)
+            store[h] = 1;
+        if (store[h] && (len[h] < 0 || len[h] >= Tmax)) {
+            rc = -5;
+            goto done;
+        }
+    }
+    /* append the new token's key and value to every storing head's cache */
+    for (int h = 0; h < H; ++h) {
+        if (!store[h])
+            continue;
+        size_t pos = ((size_t)h * Tmax + (size_t)len[h]) * dh;
+        for (int i = 0; i < dh; ++i) {
+            size_t row = (size_t)h * dh + i;
+            store_elem(Kc, pos + i, dt, proj_row(Wk, bk, x, d, dt, row));
+            store_elem(Vc, pos + i, dt, proj_row(Wv, bv, x, d, dt, row));
+        }
+        len[h] += 1;
+    }
+    for (int c = 0; c < d; ++c)
+        y_out[c] = 0.0;
+    const double scale = 1.0 / sqrt((double)dh);
+    for (int n = 0; n < count; ++n) {
+        const int h = heads[n];
+        const int L = len[h];
+        for (int i = 0; i < dh; ++i)
+            q[i] = proj_row(Wq, bq, x, d, dt, (size_t)h * dh + i);
+        double amax = -INFINITY;
+        for (int t = 0; t < L; ++t) {
+            double s = 0.0;
+            for (int i = 0; i < dh; ++i)
+                s += q[i] * wid(Kc, ((size_t)h * Tmax + t) * dh + i, dt);
+            a[t] = s * scale;
+            if (a[t] > amax)
+                amax = a[t];
+        }
+        double z = 0.0;
+        for (int t = 0; t < L; ++t) {
+            a[t] = exp(a[t] - amax);
+            z += a[t];
+        }
+        for (int i = 0; i < dh; ++i)
+            o[i] = 0.0;
+        for (int t = 0; t < L; ++t)
+            for (int i = 0; i < dh; ++i)
+                o[i] += (a[t] / z) * wid(Vc, ((size_t)h * Tmax + t) * dh + i, dt);
+        if (o_out)
+            for (int i = 0; i < dh; ++i)
+                o_out[(size_t)n * dh + i] = o[i];
+        for (int i = 0; i < dh; ++i)
+            for (int c = 0; c < d; ++c)
+                y_out[c] += o[i] * wid(WoT, ((size_t)h * dh + i) * d + c, dt);
+    }
+done:
+    free(store);
+    free(q);
+    free(o);
+    free(a);
+    return rc;
+}

@@ -70,8 +70,10 @@ def lib():
         L.orc_dense_ffn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.orc_preact.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.orc_rms_normalize.argtypes = [vp, i32, dbl, i32, vp]
+        L.orc_attention_decode.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, i32, vp, vp, i32, i32, vp, vp]
         for name in ("orc_predict", "orc_select_topk", "orc_select_threshold", "orc_sparse_ffn",
-                     "orc_dense_ffn", "orc_preact", "orc_rms_normalize"):
+                     "orc_dense_ffn", "orc_preact", "orc_rms_normalize", "orc_attention_decode"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -307,3 +309,32 @@ def stack_forward(x0, layers, dt, k=None, tau=None, lookahead=False, eps=1e-6, n
         xhats.append(xhat)
         prev_xhat = xhat
     return x, sets, xhats
+
+
+# ---------------------------------------------------------------------------------------------
+# O9 attention-head sparsity: one decode step over a set of heads  (C primitive)
+# ---------------------------------------------------------------------------------------------
+def attention_decode(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, heads, dt, kv_all=False):
+    """[DV] (opening section; The Empirical Foundation; Implications for System Design): one new
+    token through the heads in `heads` (ascending): q, k, v projections, k and v appended to the
+    storing heads' caches (rounded to the storage type), softmax(q.K / sqrt(dh)) over the cache,
+    o_h = p.V, y = sum of WoT_h^T o_h.  Kc, Vc [H, Tmax, dh] (storage type) and lens [H] int32 are
+    updated in place.  Returns (o [count, dh], y [d]) in float64."""
+    x, Wq, Wk, Wv, WoT = (_storage(a, dt) for a in (x, Wq, Wk, Wv, WoT))
+    HD, d = Wq.shape
+    H, Tmax, dh = Kc.shape
+    assert HD == H * dh and Vc.shape == Kc.shape and lens.shape == (H,)
+    for a in (Kc, Vc):
+        assert a.dtype == _NP_STORAGE[dt] and a.flags.c_contiguous
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous
+    bq, bk, bv = (None if b is None else np.ascontiguousarray(b, dtype=np.float32)
+                  for b in (bq, bk, bv))
+    heads = np.ascontiguousarray(heads, dtype=np.int32)
+    n = heads.shape[0]
+    o = np.empty((max(n, 1), dh), np.float64)
+    y = np.empty(d, np.float64)
+    _check(lib().orc_attention_decode(_ptr(x), d, H, dh, dt, _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(bq),
+                                      _ptr(bk), _ptr(bv), _ptr(WoT), _ptr(Kc), _ptr(Vc), Tmax,
+                                      _ptr(lens), _ptr(heads), n, int(bool(kv_all)), _ptr(o), _ptr(y)),
+           "orc_attention_decode")
+    return o[:n].copy(), y

@@ -1,0 +1,165 @@
+"""Pins for the oracle's attention decode step (attention-head sparsity).
+
+Sources: "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm" -- the
+opening section (a small input-dependent set of attention heads approximates the dense layer),
+"The Empirical Foundation" (only a fifth to a third of the heads matter per token),
+"Implications for System Design" (selecting heads per token saves attention work and key/value
+cache traffic).  The step is standard multi-head attention for one new token; the pins fix it by
+a hand-derived two-position case, scipy's softmax, invariants of attention (permuting cached
+positions, a zero-valued sink that takes all the weight, a head alone on its own token) and the
+additivity of the output over a partition of the heads.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import oracle as orc
+
+CAST = {orc.F32: np.float32, orc.F16: np.float16}
+
+
+def _model(rng, d, H, dh, Tmax, dt, lens, bias=True):
+    c = CAST[dt]
+    HD = H * dh
+    W = lambda: (rng.standard_normal((HD, d)) / math.sqrt(d)).astype(c)
+    Wq, Wk, Wv, WoT = W(), W(), W(), (rng.standard_normal((HD, d)) / math.sqrt(HD)).astype(c)
+    b = (lambda: (0.1 * rng.standard_normal(HD)).astype(np.float32)) if bias else (lambda: None)
+    bq, bk, bv = b(), b(), b()
+    Kc = rng.standard_normal((H, Tmax, dh)).astype(c)
+    Vc = rng.standard_normal((H, Tmax, dh)).astype(c)
+    x = rng.standard_normal(d).astype(c)
+    return dict(x=x, Wq=Wq, Wk=Wk, Wv=Wv, bq=bq, bk=bk, bv=bv, WoT=WoT, Kc=Kc, Vc=Vc,
+                lens=np.array(lens, np.int32))
+
+
+def _run(m, heads, dt, kv_all=False):
+    return orc.attention_decode(m["x"], m["Wq"], m["Wk"], m["Wv"], m["bq"], m["bk"], m["bv"],
+                                m["WoT"], m["Kc"], m["Vc"], m["lens"], np.array(heads, np.int32),
+                                dt, kv_all)
+
+
+def _copy(m):
+    return {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in m.items()}
+
+
+def test_two_positions_hand_derived():
+    # d = dh = 4, one head; q = 2x, k = v = x, y = o.  Past position 0: key 0, value e_1.
+    # New token x = e_0: a_0 = 0, a_1 = (q . x) / sqrt(4) = 1, so p_1 = logistic(1).
+    # Without the 1/sqrt(dh) scale a_1 = 2; with 1/dh it is 0.5: both fail.
+    I = np.eye(4, dtype=np.float32)
+    m = dict(x=np.array([1, 0, 0, 0], np.float32), Wq=2 * I, Wk=I.copy(), Wv=I.copy(), bq=None,
+             bk=None, bv=None, WoT=I.copy(), Kc=np.zeros((1, 3, 4), np.float32),
+             Vc=np.zeros((1, 3, 4), np.float32), lens=np.array([1], np.int32))
+    m["Vc"][0, 0, 1] = 1.0
+    o, y = _run(m, [0], orc.F32)
+    p1 = special.expit(1.0)
+    assert np.allclose(o[0], [p1, 1.0 - p1, 0.0, 0.0], rtol=0, atol=1e-15)
+    assert np.allclose(y, o[0], rtol=0, atol=1e-15)
+    assert m["lens"].tolist() == [2]
+    assert m["Kc"][0, 1].tolist() == [1, 0, 0, 0] and m["Vc"][0, 1].tolist() == [1, 0, 0, 0]
+
+
+@pytest.mark.parametrize("dt", [orc.F32, orc.F16])
+@pytest.mark.parametrize("kv_all", [False, True])
+def test_matches_scipy_softmax_attention(dt, kv_all):
+    rng = np.random.default_rng(7)
+    d, H, dh, Tmax = 24, 5, 8, 12
+    lens = [3, 0, 7, 11 - 1, 5]
+    m = _model(rng, d, H, dh, Tmax, dt, lens)
+    ref = _copy(m)
+    heads = [0, 2, 3]
+    o, y = _run(m, heads, dt, kv_all)
+    x = ref["x"].astype(np.float64)
+    yref = np.zeros(d)
+    storing = range(H) if kv_all else heads
+    for h in range(H):
+        rows = slice(h * dh, (h + 1) * dh)
+        if h in storing:
+            k = ref["Wk"][rows].astype(np.float64) @ x + ref["bk"][rows]
+            v = ref["Wv"][rows].astype(np.float64) @ x + ref["bv"][rows]
+            L = ref["lens"][h]
+            # the appended entries are the projections rounded once to the storage type
+            assert np.array_equal(m["Kc"][h, L], k.astype(CAST[dt]))
+            assert np.array_equal(m["Vc"][h, L], v.astype(CAST[dt]))
+            assert m["lens"][h] == L + 1
+        else:
+            assert m["lens"][h] == ref["lens"][h]
+            assert np.array_equal(m["Kc"][h], ref["Kc"][h]) and np.array_equal(m["Vc"][h], ref["Vc"][h])
+    for n, h in enumerate(heads):
+        rows = slice(h * dh, (h + 1) * dh)
+        q = ref["Wq"][rows].astype(np.float64) @ x + ref["bq"][rows]
+        L = m["lens"][h]
+        K = m["Kc"][h, :L].astype(np.float64)
+        V = m["Vc"][h, :L].astype(np.float64)
+        p = special.softmax(K @ q / math.sqrt(dh))
+        oref = p @ V
+        assert np.allclose(o[n], oref, rtol=1e-12, atol=1e-13)
+        yref += ref["WoT"][rows].astype(np.float64).T @ oref
+    assert np.allclose(y, yref, rtol=1e-12, atol=1e-12 * np.abs(yref).max())
+
+
+def test_head_with_empty_cache_returns_its_own_value():
+    rng = np.random.default_rng(3)
+    d, H, dh, Tmax = 16, 2, 8, 4
+    m = _model(rng, d, H, dh, Tmax, orc.F16, [0, 2])
+    o, _ = _run(m, [0], orc.F16)
+    assert np.array_equal(o[0], m["Vc"][0, 0].astype(np.float64))
+
+
+def test_permuting_cached_positions_changes_nothing():
+    # attention is invariant to a joint permutation of the cached keys and values: a swapped
+    # K/V index or an off-by-one between them fails this
+    rng = np.random.default_rng(5)
+    d, H, dh, Tmax = 16, 3, 8, 9
+    m = _model(rng, d, H, dh, Tmax, orc.F32, [6, 6, 6])
+    m2 = _copy(m)
+    perm = np.array([4, 0, 5, 2, 1, 3])
+    m2["Kc"][:, :6] = m["Kc"][:, perm]
+    m2["Vc"][:, :6] = m["Vc"][:, perm]
+    o1, y1 = _run(m, [0, 1, 2], orc.F32)
+    o2, y2 = _run(m2, [0, 1, 2], orc.F32)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-13)
+
+
+def test_zero_valued_sink_silences_a_head():
+    # a cached key aligned with the query, far larger than any other logit, and a zero value:
+    # the head's output is (numerically) zero -- the synthetic form of a silent head
+    d, H, dh, Tmax = 8, 1, 8, 4
+    I = np.eye(8, dtype=np.float32)
+    x = np.zeros(8, np.float32)
+    x[0] = 1.0
+    m = dict(x=x, Wq=I.copy(), Wk=0.01 * I, Wv=I.copy(), bq=None, bk=None, bv=None, WoT=I.copy(),
+             Kc=np.zeros((1, Tmax, dh), np.float32), Vc=np.ones((1, Tmax, dh), np.float32),
+             lens=np.array([2], np.int32))
+    m["Kc"][0, 0, 0] = 400.0           # a_0 = 400 / sqrt(8) ~ 141
+    m["Vc"][0, 0] = 0.0
+    o, y = _run(m, [0], orc.F32)
+    assert np.abs(o).max() < 1e-50 and np.abs(y).max() < 1e-50
+
+
+def test_output_is_additive_over_a_partition_of_heads():
+    rng = np.random.default_rng(11)
+    d, H, dh, Tmax = 20, 6, 4, 8
+    m = _model(rng, d, H, dh, Tmax, orc.F32, [2, 5, 0, 7 - 1, 3, 4])
+    ma, mb, mall = _copy(m), _copy(m), _copy(m)
+    _, ya = _run(ma, [0, 3, 4], orc.F32, kv_all=True)
+    _, yb = _run(mb, [1, 2, 5], orc.F32, kv_all=True)
+    _, yall = _run(mall, list(range(H)), orc.F32, kv_all=True)
+    assert np.allclose(ya + yb, yall, rtol=0, atol=1e-12 * np.abs(yall).max())
+    for a, b in ((ma, mall), (mb, mall)):
+        assert np.array_equal(a["Kc"], b["Kc"]) and np.array_equal(a["lens"], b["lens"])
+
+
+def test_rejects_full_cache_and_bad_head():
+    rng = np.random.default_rng(1)
+    m = _model(rng, 8, 2, 4, 3, orc.F32, [3, 0])
+    with pytest.raises(ValueError):
+        _run(_copy(m), [0], orc.F32)                   # head 0's cache is full
+    _run(_copy(m), [1], orc.F32)                       # head 1 alone is fine
+    with pytest.raises(ValueError):
+        _run(_copy(m), [1], orc.F32, kv_all=True)      # ... unless every head must append
+    with pytest.raises(ValueError):
+        _run(_copy(m), [2], orc.F32)
