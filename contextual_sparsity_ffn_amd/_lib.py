@@ -20,7 +20,7 @@ F32, F16, BF16 = 0, 1, 2
 RELU, REGLU, SILU, SWIGLU = 0, 1, 2, 3
 GATED_ACTS = (REGLU, SWIGLU)
 OP_PREDICT, OP_SELECT_TOPK, OP_SELECT_THRESHOLD, OP_SPARSE_FFN, OP_DENSE_FFN, OP_LAYER, \
-    OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK = range(9)
+    OP_BATCHED_UNION, OP_BATCHED_LAYER, OP_STACK, OP_ATTN_DECODE, OP_ATTN_LAYER = range(11)
 STACK_SYNC, STACK_LOOKAHEAD, STACK_GRAPH = 0, 1, 0x100
 FFN_SKIP_ZERO_H = 1
 SEM_PER_TOKEN, SEM_UNION = 0, 1
@@ -35,7 +35,8 @@ EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_worksp
            "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_layer_hot",
            "csf_sparse_ffn_batched_union",
            "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
-           "csf_set_ffn_gate_threshold", "csf_set_trace_events")
+           "csf_set_ffn_gate_threshold", "csf_set_trace_events", "csf_sparse_attention_decode",
+           "csf_sparse_attention_layer", "csf_attention_workspace_size")
 
 
 class LayerWeights(ctypes.Structure):
@@ -86,8 +87,15 @@ def _load():
     L.csf_stack_forward.argtypes = [ctypes.POINTER(LayerWeights), i32, i32, i32, i32, i32, i32,
                                     vp, i32, i32, i32, flt, i32, flt, vp, vp, vp, vp, vp, sz, vp,
                                     vp]
+    L.csf_sparse_attention_decode.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.csf_sparse_attention_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, i32, vp, i32, flt, i32, vp, vp, vp, vp,
+                                             vp, vp, sz, vp]
+    L.csf_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     for name in EXPORTS[4:]:
         getattr(L, name).restype = i32
+    L.csf_attention_workspace_size.restype = sz
     return L
 
 
@@ -488,4 +496,92 @@ def sparse_ffn_layer_hot(x, V, U_cold, W1, b1, Wup, W2T, hot, k=None, tau=None, 
                                         float(tau if tau is not None else 0.0), _ptr(y),
                                         _ptr(scores), _ptr(idx), _ptr(count), _ptr(w), wb,
                                         _stream(dev)))
+    return y
+
+
+# ------------------------------------------------------------------------------------------------
+# attention-head sparsity
+# ------------------------------------------------------------------------------------------------
+def attention_workspace_size(op, d, H, dh, r, Tmax, max_heads, dtype=F16) -> int:
+    return int(lib.csf_attention_workspace_size(op, d, H, dh, r, Tmax, max_heads, dtype))
+
+
+def _attn_weights(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens):
+    _tensor(x, "x")
+    if x.dim() != 1:
+        raise ValueError("x must be one token, shape [d]")
+    dev, dt = x.device, x.dtype
+    H, Tmax, dh = Kc.shape
+    d = x.shape[0]
+    for name, W in (("Wq", Wq), ("Wk", Wk), ("Wv", Wv), ("WoT", WoT)):
+        _tensor(W, name, dtype=dt, shape=(H * dh, d), device=dev)
+    for name, b in (("bq", bq), ("bk", bk), ("bv", bv)):
+        _tensor(b, name, dtype=torch.float32, shape=(H * dh,), device=dev, optional=True)
+    _tensor(Kc, "Kc", dtype=dt, shape=(H, Tmax, dh), device=dev)
+    _tensor(Vc, "Vc", dtype=dt, shape=(H, Tmax, dh), device=dev)
+    _tensor(lens, "lens", dtype=torch.int32, shape=(H,), device=dev)
+    return dev, dt, d, H, dh, Tmax
+
+
+def sparse_attention_decode(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, heads=None, count=None,
+                            kv_all=False, o=None, y=None, ws=None):
+    """One decode step of multi-head attention over the heads in `heads` (int32 device list;
+    None = every head, the dense step).  Kc, Vc [H, Tmax, dh] and lens [H] are updated in place.
+    Returns y [d] float32."""
+    dev, dt, d, H, dh, Tmax = _attn_weights(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens)
+    if heads is None:
+        max_heads = H
+        if count is not None:
+            raise ValueError("count needs a head list")
+    else:
+        _tensor(heads, "heads", dtype=torch.int32, device=dev)
+        max_heads = heads.numel()
+    _tensor(count, "count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    _tensor(o, "o", dtype=torch.float32, shape=(max_heads, dh), device=dev, optional=True)
+    if y is None:
+        y = torch.empty(d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, shape=(d,), device=dev)
+    code = dtype_code(dt)
+    w, wb = _workspace(attention_workspace_size(OP_ATTN_DECODE, d, H, dh, 0, Tmax, max_heads, code),
+                       dev, ws)
+    _check(lib.csf_sparse_attention_decode(_ptr(x), d, H, dh, code, _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                           _ptr(bq), _ptr(bk), _ptr(bv), _ptr(WoT), _ptr(Kc),
+                                           _ptr(Vc), Tmax, _ptr(lens), _ptr(heads), _ptr(count),
+                                           max_heads, 1 if kv_all else 0, _ptr(o), _ptr(y), _ptr(w),
+                                           wb, _stream(dev)))
+    return y
+
+
+def sparse_attention_layer(x, Vp, Up, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, k=None, tau=None,
+                           kv_all=False, scores=None, heads=None, count=None, o=None, y=None,
+                           ws=None):
+    """Head predictor, top-k (or >= tau) head selection and the decode step over the selected
+    heads, for one token.  Returns y [d] float32."""
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k (top-k) or tau (threshold)")
+    dev, dt, d, H, dh, Tmax = _attn_weights(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens)
+    r = Vp.shape[0]
+    _tensor(Vp, "Vp", dtype=dt, shape=(r, d), device=dev)
+    _tensor(Up, "Up", dtype=dt, shape=(H, r), device=dev)
+    kk = -1 if k is None else int(k)
+    max_heads = H if kk < 0 else kk
+    _tensor(scores, "scores", dtype=torch.float32, shape=(H,), device=dev, optional=True)
+    if heads is not None:
+        _tensor(heads, "heads", dtype=torch.int32, device=dev)
+        if heads.numel() < max(max_heads, 1):
+            raise ValueError("heads is too small")
+    _tensor(count, "count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
+    _tensor(o, "o", dtype=torch.float32, shape=(max_heads, dh), device=dev, optional=True)
+    if y is None:
+        y = torch.empty(d, dtype=torch.float32, device=dev)
+    _tensor(y, "y", dtype=torch.float32, shape=(d,), device=dev)
+    code = dtype_code(dt)
+    w, wb = _workspace(attention_workspace_size(OP_ATTN_LAYER, d, H, dh, r, Tmax, max_heads, code),
+                       dev, ws)
+    _check(lib.csf_sparse_attention_layer(_ptr(x), d, H, dh, r, code, _ptr(Vp), _ptr(Up), _ptr(Wq),
+                                          _ptr(Wk), _ptr(Wv), _ptr(bq), _ptr(bk), _ptr(bv),
+                                          _ptr(WoT), _ptr(Kc), _ptr(Vc), Tmax, _ptr(lens), kk,
+                                          float(tau if tau is not None else 0.0),
+                                          1 if kv_all else 0, _ptr(scores), _ptr(heads),
+                                          _ptr(count), _ptr(o), _ptr(y), _ptr(w), wb, _stream(dev)))
     return y

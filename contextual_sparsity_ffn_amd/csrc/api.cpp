@@ -507,6 +507,116 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
 }
 
 
+
+// ---- attention-head sparsity ---------------------------------------------------------------------
+struct AttnWs {
+    size_t lens0, q, part, rows, hv, rcount, ffn, a, scores, heads, count, total;
+};
+AttnWs attn_ws(int d, int H, int dh, int r, int Tmax, int max_heads, int dtype, bool layer)
+{
+    AttnWs w{};
+    const size_t mh = max_heads > 0 ? (size_t)max_heads : 1;
+    const int max_rows = max_heads * dh;
+    size_t o = 0;
+    w.lens0 = o;
+    o += round_up((size_t)H * sizeof(int32_t));
+    w.q = o;
+    o += round_up(mh * dh * sizeof(float));
+    w.part = o;
+    o += round_up(mh * csf::attn_num_splits(Tmax) * (size_t)(dh + 2) * sizeof(float));
+    w.rows = o;
+    o += round_up(mh * dh * sizeof(int32_t));
+    w.hv = o;
+    o += round_up(mh * dh * sizeof(float));
+    w.rcount = o;
+    o += kAlign;
+    w.ffn = o;
+    o += round_up((size_t)csf::ffn_num_chunks(d, dtype, max_rows) * d * sizeof(float));
+    if (layer) {
+        w.a = o;
+        o += pred_ws_bytes(1, r);
+        w.scores = o;
+        o += round_up((size_t)H * sizeof(float));
+        w.heads = o;
+        o += round_up((size_t)H * sizeof(int32_t));
+        w.count = o;
+        o += kAlign;
+    }
+    w.total = o;
+    return w;
+}
+
+int validate_attention(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+                       const void *Wk, const void *Wv, const float *bq, const float *bk,
+                       const float *bv, const void *WoT, const void *Kc, const void *Vc, int Tmax,
+                       const int32_t *len, int kv_all, const float *o, const float *y)
+{
+    REQUIRE(valid_dtype(dtype), CSF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    CHECK_ROW(d, dtype, kMaxRowChunks);
+    REQUIRE(H > 0, CSF_ERR_INVALID_ARG, "H must be positive (got %d)", H);
+    REQUIRE(dh > 0, CSF_ERR_INVALID_ARG, "dh must be positive (got %d)", dh);
+    REQUIRE(csf::attn_head_dim_supported(dtype, dh), CSF_ERR_UNSUPPORTED,
+            "dh = %d: a cached row must be 32, 64, 128, 256 or 512 bytes", dh);
+    REQUIRE((long)H * dh <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED,
+            "H * dh = %ld exceeds this build's limit %d", (long)H * dh, csf::ffn_max_count());
+    REQUIRE(Tmax > 0, CSF_ERR_INVALID_ARG, "Tmax must be positive (got %d)", Tmax);
+    REQUIRE(kv_all == 0 || kv_all == 1, CSF_ERR_INVALID_ARG, "kv_all must be 0 or 1");
+    CHECK_PTR(x, true);
+    CHECK_PTR(Wq, true);
+    CHECK_PTR(Wk, true);
+    CHECK_PTR(Wv, true);
+    CHECK_PTR(WoT, true);
+    CHECK_PTR(bq, false);
+    CHECK_PTR(bk, false);
+    CHECK_PTR(bv, false);
+    CHECK_PTR(Kc, true);
+    CHECK_PTR(Vc, true);
+    CHECK_PTR(len, true);
+    CHECK_PTR(o, false);
+    CHECK_PTR(y, true);
+    return CSF_OK;
+}
+
+int enqueue_attention(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+                      const void *Wk, const void *Wv, const float *bq, const float *bk,
+                      const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
+                      int32_t *len, const int32_t *heads, const int32_t *count, int max_heads,
+                      int kv_all, float *o, float *y, void *ws, const AttnWs &w, hipStream_t st,
+                      csf::Trace *tr)
+{
+    csf::AttnArgs a;
+    a.dtype = dtype;
+    a.x = x;
+    a.d = d;
+    a.H = H;
+    a.dh = dh;
+    a.Wq = Wq;
+    a.Wk = Wk;
+    a.Wv = Wv;
+    a.WoT = WoT;
+    a.bq = bq;
+    a.bk = bk;
+    a.bv = bv;
+    a.Kc = Kc;
+    a.Vc = Vc;
+    a.Tmax = Tmax;
+    a.len = len;
+    a.heads = heads;
+    a.count = count;
+    a.max_heads = max_heads;
+    a.kv_all = kv_all;
+    a.o = o;
+    a.y = y;
+    a.lens0 = reinterpret_cast<int32_t *>(at(ws, w.lens0));
+    a.qbuf = reinterpret_cast<float *>(at(ws, w.q));
+    a.part = reinterpret_cast<float *>(at(ws, w.part));
+    a.rows = reinterpret_cast<int32_t *>(at(ws, w.rows));
+    a.hv = reinterpret_cast<float *>(at(ws, w.hv));
+    a.rows_count = reinterpret_cast<int32_t *>(at(ws, w.rcount));
+    a.ffn_partials = reinterpret_cast<float *>(at(ws, w.ffn));
+    return hip_status(csf::launch_attention_decode(a, st, tr), "attention decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,6 +664,19 @@ int csf_set_trace_events(void *const *events, int n)
         g_trace_events[i] = static_cast<hipEvent_t>(events[i]);
     g_trace_n = n;
     return ok();
+}
+
+size_t csf_attention_workspace_size(int op, int d, int H, int dh, int r, int Tmax, int max_heads,
+                                    int dtype)
+{
+    if (d <= 0 || H <= 0 || dh <= 0 || Tmax <= 0 || max_heads < 0 || max_heads > H ||
+        !valid_dtype(dtype))
+        return 0;
+    if (op == CSF_OP_ATTN_DECODE)
+        return attn_ws(d, H, dh, 0, Tmax, max_heads, dtype, false).total;
+    if (op == CSF_OP_ATTN_LAYER)
+        return r > 0 ? attn_ws(d, H, dh, r, Tmax, max_heads, dtype, true).total : 0;
+    return 0;
 }
 
 size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype)
@@ -1075,6 +1198,88 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
         g.key = key;
     }
     return hip_status(hipGraphLaunch(g.exec, st), "hipGraphLaunch");
+}
+
+int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+                                const void *Wk, const void *Wv, const float *bq, const float *bk,
+                                const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
+                                int32_t *len, const int32_t *heads, const int32_t *count,
+                                int max_heads, int kv_all, float *o, float *y, void *ws,
+                                size_t ws_bytes, void *stream)
+{
+    int s = validate_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len,
+                               kv_all, o, y);
+    if (s != CSF_OK)
+        return s;
+    CHECK_PTR(heads, false);
+    CHECK_PTR(count, false);
+    if (heads)
+        REQUIRE(max_heads >= 0 && max_heads <= H, CSF_ERR_INVALID_ARG,
+                "max_heads = %d must be in [0, H = %d]", max_heads, H);
+    else
+        REQUIRE(max_heads == H && !count, CSF_ERR_INVALID_ARG,
+                "without a head list every head is computed: max_heads must be H and count NULL");
+    AttnWs w = attn_ws(d, H, dh, 0, Tmax, max_heads, dtype, false);
+    CHECK_WS(ws, ws_bytes, w.total);
+    csf::Trace tr;
+    if (g_trace_n > 0) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    return enqueue_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len,
+                             heads, count, max_heads, kv_all, o, y, ws, w,
+                             static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
+}
+
+int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int dtype,
+                               const void *Vp, const void *Up, const void *Wq, const void *Wk,
+                               const void *Wv, const float *bq, const float *bk, const float *bv,
+                               const void *WoT, void *Kc, void *Vc, int Tmax, int32_t *len, int k,
+                               float tau, int kv_all, float *scores_out, int32_t *heads_out,
+                               int32_t *count_out, float *o, float *y, void *ws, size_t ws_bytes,
+                               void *stream)
+{
+    int s = validate_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len,
+                               kv_all, o, y);
+    if (s != CSF_OK)
+        return s;
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(Vp, true);
+    CHECK_PTR(Up, true);
+    CHECK_PTR(scores_out, false);
+    CHECK_PTR(heads_out, false);
+    CHECK_PTR(count_out, false);
+    REQUIRE(k >= -1 && k <= H, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, H = %d]",
+            k, H);
+    REQUIRE(H <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "H = %d exceeds this build's limit %d",
+            H, csf::select_max_f());
+    REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    const int max_heads = k >= 0 ? k : H;
+    AttnWs w = attn_ws(d, H, dh, r, Tmax, max_heads, dtype, true);
+    CHECK_WS(ws, ws_bytes, w.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    csf::Trace tr;
+    if (g_trace_n > 0) {
+        tr.ev = g_trace_events;
+        tr.n = g_trace_n;
+    }
+    csf::Trace *trp = tr.ev ? &tr : nullptr;
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
+    int32_t *hd = heads_out ? heads_out : reinterpret_cast<int32_t *>(at(ws, w.heads));
+    int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
+    hipError_t e = enqueue_predict(dtype, x, 1, d, Vp, r, Up, H, sc, a, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "head predictor launch");
+    if (k >= 0)
+        e = csf::launch_select_topk(sc, 1, H, k, hd, max_heads > 0 ? max_heads : 1, cn, nullptr, st,
+                                    trp);
+    else
+        e = csf::launch_select_threshold(sc, 1, H, tau, hd, H, cn, nullptr, st, trp);
+    if (e != hipSuccess)
+        return hip_status(e, "head selection launch");
+    return enqueue_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len, hd,
+                             cn, max_heads, kv_all, o, y, ws, w, st, trp);
 }
 
 }  // extern "C"

@@ -348,6 +348,20 @@ hipError_t up_gated(const FfnArgs &a, int C, hipStream_t st, Trace *tr)
 }
 
 template <class T>
+hipError_t down_t(const FfnArgs &a, hipStream_t st, Trace *tr)
+{
+    const int C = a.d / T::E;
+    const int nchunk = ffn_num_chunks(a.d, a.dtype, a.max_count);
+    hipError_t e = launch(k_gather_down<T>, dim3(ffn_num_slices(a.d, a.dtype), nchunk, a.B),
+                          dim3(256), st, tr, static_cast<const u32x4 *>(a.W2T), a.h, a.h_stride,
+                          a.idx, a.idx_stride, a.count, a.max_count, a.f, C, nchunk, a.skip_zero,
+                          a.partials);
+    if (e != hipSuccess)
+        return e;
+    return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.y, st, tr, a.accumulate);
+}
+
+template <class T>
 hipError_t ffn_t(const FfnArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / T::E;
@@ -401,6 +415,13 @@ hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, f
         return hipErrorInvalidValue;
     return launch(k_reduce_partials, dim3((D + kWave - 1) / kWave, B), dim3(256), st, tr, part, nchunk,
                   D, y, accumulate);
+}
+
+hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st, Trace *tr)
+{
+    if (a.dtype == 0) return down_t<F32T>(a, st, tr);
+    if (a.dtype == 1) return down_t<F16T>(a, st, tr);
+    return down_t<BF16T>(a, st, tr);
 }
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t st, Trace *tr)

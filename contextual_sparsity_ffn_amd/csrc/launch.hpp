@@ -103,9 +103,39 @@ int ffn_num_slices(int d, int dtype);
 int ffn_max_count();   // longest active list (and widest dense layer) the FFN kernels take
 int ffn_num_chunks(int d, int dtype, int max_count);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
+// The down projection and reduction alone, over a list whose h values are already in a.h.
+hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 // y[t][col] = sum over chunks q, in order, of part[t][q][col] (part is [B][nchunk][D] float32).
 hipError_t launch_reduce_partials(const float *part, int nchunk, int D, int B, float *y,
                                   hipStream_t stream, Trace *trace = nullptr, int accumulate = 0);
+
+// ---- attention-head sparsity (attention.hip) --------------------------------------------------
+struct AttnArgs {
+    int dtype;
+    const void *x;                  // [d]
+    int d, H, dh;
+    const void *Wq, *Wk, *Wv, *WoT; // [H*dh][d]
+    const float *bq, *bk, *bv;      // [H*dh] or null
+    void *Kc, *Vc;                  // [H][Tmax][dh]
+    int Tmax;
+    int32_t *len;                   // [H] device, advanced for the heads that store the token
+    const int32_t *heads;           // [max_heads] device, or null = every head (max_heads == H)
+    const int32_t *count;           // device, or null = max_heads
+    int max_heads, kv_all;
+    float *o;                       // [max_heads][dh] or null
+    float *y;                       // [d]
+    // workspace
+    int32_t *lens0;                 // [H] lengths at the start of the step
+    float *qbuf;                    // [max_heads][dh]
+    float *part;                    // [max_heads][attn_num_splits(Tmax)][dh + 2]
+    int32_t *rows;                  // [max_heads * dh]
+    float *hv;                      // [max_heads * dh]
+    int32_t *rows_count;            // [1]
+    float *ffn_partials;            // [ffn_num_chunks(d, dtype, max_heads * dh)][d]
+};
+int attn_num_splits(int Tmax);
+bool attn_head_dim_supported(int dtype, int dh);
+hipError_t launch_attention_decode(const AttnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 
 // ---- stack of blocks (stack.hip) -------------------------------------------------------------
 // xhat[t] = storage-type rounding of x[t] / sqrt(mean(x[t]^2) + eps) (norm = 1) or of x[t]

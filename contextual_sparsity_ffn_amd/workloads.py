@@ -228,3 +228,135 @@ def dense_bytes(cfg: Config) -> int:
     es = torch.tensor([], dtype=cfg.dtype).element_size()
     rows = 3 if cfg.act in GATED else 2
     return es * rows * cfg.f * cfg.d
+
+
+# ------------------------------------------------------------------------------------------------
+# Attention-head sparsity workload
+# ------------------------------------------------------------------------------------------------
+ROLE_A_U, ROLE_A_V, ROLE_A_DIR, ROLE_A_QNOISE, ROLE_A_WK, ROLE_A_WV, ROLE_A_WO = 21, 22, 23, 24, 25, 26, 27
+ROLE_A_KC, ROLE_A_VC, ROLE_A_CALIB, ROLE_A_TOKENS = 28, 29, 30, 31
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnConfig:
+    """A decode step of multi-head attention with a KV cache of `context` past tokens per head.
+
+    Head relevance is made input-dependent the way the pages describe silent heads: every head's
+    cache starts with a sink position whose value is zero.  A head's query has a component along
+    the sink key equal to beta * (theta - g_h(x)) + log(context) + q_std^2 / 2, with
+    g = U_a (V_a x) a low-rank projection of the input: where g_h(x) < theta the sink takes almost
+    all of the attention and the head's output is near zero; where g_h(x) > theta the head attends
+    to its content (the constant is the log of the content's total softmax weight, so the switch
+    sits at g_h = theta).  theta is set so that
+    `active_frac` of the (token, head) pairs have g_h > theta.  The predictor's factors are the
+    same U_a, V_a, so the active heads are predictable from x by a cheap low-rank network."""
+    index: int
+    name: str
+    d: int
+    H: int
+    dh: int
+    r: int
+    dtype: torch.dtype
+    k: int                  # heads kept by top-k
+    context: int            # cached past tokens per head (the sink included)
+    extra: int              # free cache positions beyond the context (Tmax = context + extra)
+    active_frac: float
+    beta: float = 16.0      # sink strength
+    q_std: float = 1.5      # spread of the content logits
+    tokens: int = 64
+
+    @property
+    def Tmax(self) -> int:
+        return self.context + self.extra
+
+    def scaled(self, d, H, dh, r, context, k=None, extra=8, tokens=4) -> "AttnConfig":
+        if k is None:
+            k = max(1, int(math.floor(H * self.k / self.H + 0.5)))
+        return dataclasses.replace(self, d=d, H=H, dh=dh, r=r, context=context, k=k, extra=extra,
+                                   tokens=tokens)
+
+
+# OPT-175B attention shape (d 12288 = 96 heads x 128), a 2048-token context, a fifth of the heads
+# active per token (the pages: a fifth to a third matter; over 80% can be silenced).
+ATTN_CONFIGS = {
+    0: AttnConfig(100, "tiny-attn-f32", 256, 8, 32, 32, torch.float32, 2, 64, 8, 0.25),
+    1: AttnConfig(101, "opt175b-attn-f16", 12288, 96, 128, 256, torch.float16, 19, 2048, 64, 0.20),
+}
+
+
+@dataclasses.dataclass
+class AttnLayer:
+    cfg: AttnConfig
+    Vp: torch.Tensor        # [r, d]      head predictor down projection (= V_a)
+    Up: torch.Tensor        # [H, r]      head predictor up projection (= U_a)
+    Wq: torch.Tensor        # [H*dh, d]
+    Wk: torch.Tensor
+    Wv: torch.Tensor
+    WoT: torch.Tensor       # [H*dh, d]  output projection, head-dimension major
+    bq: torch.Tensor        # [H*dh] float32
+    Kc: torch.Tensor        # [H, Tmax, dh]
+    Vc: torch.Tensor
+    lens: torch.Tensor      # [H] int32, all = context
+
+    @property
+    def weight_bytes(self) -> int:
+        return 4 * self.Wq.numel() * self.Wq.element_size()
+
+
+def make_attention_layer(cfg: AttnConfig, device="cpu", layer: int = 0) -> AttnLayer:
+    """Draw one attention layer and its filled caches (float32 draws, one rounding)."""
+    c = cfg.index
+    d, H, dh, r, dt, T = cfg.d, cfg.H, cfg.dh, cfg.r, cfg.dtype, cfg.context
+    HD = H * dh
+    uv = (1.0 / (r * d)) ** 0.25                       # g = U_a (V_a x) has unit spread
+    Ua = normal((H, r), uv, device, seed(c, ROLE_A_U, layer))
+    Va = normal((r, d), uv, device, seed(c, ROLE_A_V, layer))
+    e = normal((H, dh), 1.0, device, seed(c, ROLE_A_DIR, layer))
+    e = e / e.norm(dim=1, keepdim=True)                 # the sink direction of each head
+    theta = _attn_theta(cfg, Ua, Va, device, layer)
+    A = Ua @ Va                                         # [H, d]
+    Wq = normal((HD, d), cfg.q_std / math.sqrt(d), device, seed(c, ROLE_A_QNOISE, layer))
+    Wq.view(H, dh, d).add_(-cfg.beta * e[:, :, None] * A[:, None, :])
+    # at g_h = theta the sink logit equals the log of the content's total weight (context
+    # positions with logits of spread q_std), so the sink then holds about half of the attention
+    c0 = math.log(T) + 0.5 * cfg.q_std ** 2
+    bq = ((cfg.beta * theta + c0) * e).reshape(HD).to(torch.float32)
+    Wk = normal((HD, d), 1.0 / math.sqrt(d), device, seed(c, ROLE_A_WK, layer))
+    Wv = normal((HD, d), 1.0 / math.sqrt(d), device, seed(c, ROLE_A_WV, layer))
+    WoT = normal((HD, d), 1.0 / math.sqrt(HD), device, seed(c, ROLE_A_WO, layer))
+    Kc = normal((H, cfg.Tmax, dh), 1.0, device, seed(c, ROLE_A_KC, layer))
+    Vc = normal((H, cfg.Tmax, dh), 1.0, device, seed(c, ROLE_A_VC, layer))
+    Kc -= (Kc * e[:, None, :]).sum(-1, keepdim=True) * e[:, None, :]   # content keys avoid the sink
+    Kc[:, 0, :] = math.sqrt(dh) * e                     # the sink: key along e_h, value zero
+    Vc[:, 0, :] = 0.0
+    Kc[:, T:, :] = 0.0
+    Vc[:, T:, :] = 0.0
+    lens = torch.full((H,), T, dtype=torch.int32, device=device)
+    cast = lambda t: t.to(dt).contiguous()
+    return AttnLayer(cfg, cast(Va), cast(Ua), cast(Wq), cast(Wk), cast(Wv), cast(WoT), bq,
+                     cast(Kc), cast(Vc), lens)
+
+
+def _attn_theta(cfg: AttnConfig, Ua, Va, device, layer, n_tokens: int = 64) -> float:
+    """The (1 - active_frac) quantile of g = U_a (V_a x) over calibration tokens."""
+    X = normal((n_tokens, cfg.d), 1.0, device, seed(cfg.index, ROLE_A_CALIB, layer)).to(cfg.dtype)
+    G = (X.float() @ Va.to(cfg.dtype).float().t()) @ Ua.to(cfg.dtype).float().t()
+    G = G.reshape(-1).cpu()
+    kth = min(max(int(math.ceil((1.0 - cfg.active_frac) * G.numel())), 1), G.numel())
+    return float(torch.kthvalue(G, kth).values)
+
+
+def make_attn_tokens(cfg: AttnConfig, n: int, device="cpu") -> torch.Tensor:
+    """n tokens x ~ N(0, 1), rounded to the storage type: [n, d]."""
+    return normal((n, cfg.d), 1.0, device, seed(cfg.index, ROLE_A_TOKENS)).to(cfg.dtype)
+
+
+def attn_touched_bytes(cfg: AttnConfig, heads: int, lens: int) -> int:
+    """Algorithmic bytes of one decode step over `heads` heads with `lens` cached positions each
+    (before the step): predictor Vp, Up; Wq, Wk, Wv rows and WoT rows of the heads; their cached
+    keys and values (with the new token); x; the appended k, v."""
+    es = torch.tensor([], dtype=cfg.dtype).element_size()
+    pred = (cfg.r * cfg.d + cfg.H * cfg.r) * es
+    weights = 4 * heads * cfg.dh * cfg.d * es
+    cache = 2 * heads * (lens + 1) * cfg.dh * es
+    return pred + weights + cache + cfg.d * es

@@ -79,7 +79,9 @@ typedef enum {
     CSF_OP_LAYER = 5,
     CSF_OP_BATCHED_UNION = 6,
     CSF_OP_BATCHED_LAYER = 7,
-    CSF_OP_STACK = 8
+    CSF_OP_STACK = 8,
+    CSF_OP_ATTN_DECODE = 9,      /* csf_attention_workspace_size only */
+    CSF_OP_ATTN_LAYER = 10       /* csf_attention_workspace_size only */
 } csf_op;
 
 /* How csf_stack_forward schedules the predictor of each layer. */
@@ -369,18 +371,89 @@ int csf_set_ffn_gate_threshold(float tau);
 
 /* ---------------------------------------------------------------------------------------------
  * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer,
- * csf_sparse_ffn_batched_union and csf_sparse_ffn_batched_layer (per calling thread).
+ * csf_sparse_ffn_batched_union, csf_sparse_ffn_batched_layer and the attention calls (per
+ * calling thread).
  * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record
  * events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
  * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
  * order -- csf_sparse_ffn_layer: predictor down-projection, predictor up-projection, selection,
  * gathered up/gate rows, gathered down rows (partial sums), reduction of the partial sums;
  * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction;
- * csf_sparse_ffn_batched_layer: the predictor's two kernels, selection, then the union's four.
+ * csf_sparse_ffn_batched_layer: the predictor's two kernels, selection, then the union's four;
+ * csf_sparse_attention_decode: copy of the lengths, projections (q, k, v of the list; with kv_all
+ * q of the list then k, v of every head), attention blocks, combine, output-projection rows,
+ * reduction; csf_sparse_attention_layer: the predictor's two kernels and selection first.
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
  * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */
 int csf_set_trace_events(void *const *events, int n);
+
+/* ---------------------------------------------------------------------------------------------
+ * Attention-head sparsity: one decode step of multi-head attention for a set of heads.
+ * [DV] opening section: for a given input a small set of attention heads (with the MLP neurons)
+ *      approximates the dense layer; "The Empirical Foundation": a fifth to a third of the heads
+ *      matter per token; "Implications for System Design": choosing heads per token saves
+ *      attention work and key/value cache traffic and memory.
+ * For each listed head h and the new token x (standard multi-head attention, no positional
+ * rotation; the pages give no formulas):
+ *   q = Wq_h x + bq_h,  k = Wk_h x + bk_h,  v = Wv_h x + bv_h   (rows h*dh .. h*dh + dh - 1)
+ *   k and v are rounded to the storage type and written at position len[h] of the head's cache;
+ *   a_t = q . K_h[t] / sqrt(dh) for t = 0 .. len[h] (the new token included), p = softmax(a);
+ *   o_h = sum_t p_t V_h[t];   y = sum over the listed heads of sum_i o_h[i] * WoT[h*dh + i].
+ * A head outside the list computes nothing.  kv_all = 0: it stores nothing either (its cache
+ * and length stay as they are: the cache-memory saving of the pages); kv_all = 1: every head
+ * appends its k and v, so the caches stay complete and only q, the attention and the output
+ * projection are sparse.  Each head that stores the token has len[h] advanced by one.
+ *
+ *   x        [d]           dtype     the layer input of one token
+ *   Wq, Wk, Wv [H*dh][d]   dtype     head-major projections (head h owns rows h*dh .. h*dh+dh-1)
+ *   bq, bk, bv [H*dh]      float32   optional biases (NULL = none)
+ *   WoT      [H*dh][d]     dtype     output projection stored head-dimension major (row h*dh + i
+ *                                    holds the d output weights of dimension i of head h)
+ *   Kc, Vc   [H][Tmax][dh] dtype     key and value caches (in/out)
+ *   len      [H]           int32     device, in/out: cached positions per head
+ *   heads    [max_heads]   int32     device: distinct head indices (ascending gives the
+ *                                    documented summation order); NULL = every head, in order
+ *                                    (then max_heads must be H and count NULL: the dense step)
+ *   count    [1]           int32     device, optional: entries of `heads` to use (clamped to
+ *                                    [0, max_heads]); NULL = max_heads
+ *   o        [max_heads][dh] float32 out, optional: o_h of each list entry (0 for a skipped one)
+ *   y        [d]           float32   out
+ * Device-side rules: an entry outside [0, H), or a head whose cache is full (len[h] >= Tmax)
+ * or whose len is negative, is skipped (contributes nothing, stores nothing).
+ * Build limits (CSF_ERR_UNSUPPORTED): dh * element size in {32, 64, 128, 256, 512} bytes,
+ * H * dh <= 65536, d as for the FFN.  The score arithmetic is float32 (expf), o and y are float32
+ * and the summation orders are fixed, so results are deterministic.
+ * Workspace: csf_attention_workspace_size(CSF_OP_ATTN_DECODE, d, H, dh, 0, Tmax, max_heads,
+ * dtype).
+ * ------------------------------------------------------------------------------------------- */
+size_t csf_attention_workspace_size(int op, int d, int H, int dh, int r, int Tmax, int max_heads,
+                                    int dtype);
+int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+                                const void *Wk, const void *Wv, const float *bq, const float *bk,
+                                const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
+                                int32_t *len, const int32_t *heads, const int32_t *count,
+                                int max_heads, int kv_all, float *o, float *y, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csf_sparse_attention_layer -- the head predictor, the head selection and
+ * csf_sparse_attention_decode over the selected heads, for one token, in one enqueue.
+ * [DV] "The Prediction Problem": the same bias-free two-layer predictor, scoring heads instead of
+ * neurons: scores = sigmoid(Up relu(Vp x)) with Vp [r][d], Up [H][r]; the k best heads (ties to
+ * the lower index), or every head with score >= tau when k = -1, in ascending order.
+ *   scores_out [H] float32, heads_out [k, or H for a threshold] int32, count_out [1] int32:
+ *   optional copies (NULL = workspace).  Other arguments as csf_sparse_attention_decode.
+ * Workspace: csf_attention_workspace_size(CSF_OP_ATTN_LAYER, d, H, dh, r, Tmax,
+ * k >= 0 ? k : H, dtype).
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int dtype,
+                               const void *Vp, const void *Up, const void *Wq, const void *Wk,
+                               const void *Wv, const float *bq, const float *bk, const float *bv,
+                               const void *WoT, void *Kc, void *Vc, int Tmax, int32_t *len, int k,
+                               float tau, int kv_all, float *scores_out, int32_t *heads_out,
+                               int32_t *count_out, float *o, float *y, void *ws, size_t ws_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

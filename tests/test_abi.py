@@ -246,3 +246,46 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         csf.predict_active(x, torch.zeros(16, 64, dtype=torch.float16),
                            torch.zeros(100, 16, dtype=torch.float16))
+
+
+def attn(x=P, d=256, H=8, dh=32, dt=csf.F16, Wq=P, Wk=P, Wv=P, bq=NULL, bk=NULL, bv=NULL, WoT=P,
+         Kc=P, Vc=P, Tmax=64, lens=P, heads=P, count=NULL, maxh=4, kv_all=0, o=NULL, y=P, ws=P,
+         wsb=1 << 26):
+    return L.csf_sparse_attention_decode(x, d, H, dh, dt, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax,
+                                         lens, heads, count, maxh, kv_all, o, y, ws, wsb, NULL)
+
+
+def test_attention_validation():
+    assert attn(dh=12) == UNSUPPORTED                     # 24-byte cached rows
+    assert attn(dh=96) == UNSUPPORTED                     # 192 bytes: not a power of two
+    assert attn(dh=512) == UNSUPPORTED                    # 1 KiB rows
+    assert attn(dt=csf.F32, dh=4) == UNSUPPORTED          # 16-byte rows
+    assert attn(H=0) == INVALID
+    assert attn(Tmax=0) == INVALID
+    assert attn(kv_all=2) == INVALID
+    assert attn(Kc=NULL) == INVALID
+    assert attn(lens=NULL) == INVALID
+    assert attn(y=NULL) == INVALID
+    assert attn(bq=Q) == MISALIGNED
+    assert attn(maxh=9) == INVALID                        # more entries than heads
+    assert attn(heads=NULL) == INVALID                    # the dense step needs max_heads == H
+    assert attn(heads=NULL, maxh=8, count=P) == INVALID
+    assert attn(H=1024, dh=128) == UNSUPPORTED            # H * dh beyond the row-list limit
+    assert attn(d=12) == UNSUPPORTED
+    assert attn(wsb=8) == WS_SMALL
+    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
+                                        P, P, P, 64, P, 9, 0.0, 0, NULL, NULL, NULL, NULL, P, P,
+                                        1 << 26, NULL) == INVALID        # k > H
+    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
+                                        P, P, P, 64, P, -1, float("nan"), 0, NULL, NULL, NULL,
+                                        NULL, P, P, 1 << 26, NULL) == INVALID   # NaN threshold
+    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, NULL, P, P, P, P, NULL, NULL,
+                                        NULL, P, P, P, 64, P, 2, 0.0, 0, NULL, NULL, NULL, NULL, P,
+                                        P, 1 << 26, NULL) == INVALID     # no predictor
+    size = csf.attention_workspace_size
+    assert size(_lib.OP_ATTN_DECODE, 12288, 96, 128, 0, 2112, 19, csf.F16) > 19 * 128 * 4 * 3
+    assert size(_lib.OP_ATTN_LAYER, 12288, 96, 128, 256, 2112, 19, csf.F16) > \
+        size(_lib.OP_ATTN_DECODE, 12288, 96, 128, 0, 2112, 19, csf.F16)
+    assert size(_lib.OP_ATTN_DECODE, 12288, 96, 128, 0, 2112, 97, csf.F16) == 0
+    assert size(_lib.OP_ATTN_LAYER, 12288, 96, 128, 0, 2112, 19, csf.F16) == 0
+    assert size(_lib.OP_SPARSE_FFN, 12288, 96, 128, 0, 2112, 19, csf.F16) == 0

@@ -163,3 +163,28 @@ def test_rejects_full_cache_and_bad_head():
         _run(_copy(m), [1], orc.F32, kv_all=True)      # ... unless every head must append
     with pytest.raises(ValueError):
         _run(_copy(m), [2], orc.F32)
+
+
+def test_attention_workload_silences_most_heads():
+    # The synthetic layer's sink construction: per token about a fifth of the heads attend to
+    # their content (|o_h| well above 0.1) and the rest put almost all weight on the zero-valued
+    # sink (|o_h| far below 0.1), the split the pages describe (a fifth to a third of the heads
+    # matter).
+    import torch
+    from contextual_sparsity_ffn_amd import workloads as wl
+    from csf_testutil import to_orc
+    cfg = wl.ATTN_CONFIGS[1].scaled(1024, 16, 64, 64, 256)
+    L = wl.make_attention_layer(cfg)
+    X = wl.make_attn_tokens(cfg, 8)
+    fr, gap = [], []
+    for t in range(8):
+        Kc, Vc = to_orc(L.Kc).copy(), to_orc(L.Vc).copy()
+        o, _ = orc.attention_decode(to_orc(X[t]), to_orc(L.Wq), to_orc(L.Wk), to_orc(L.Wv),
+                                    L.bq.numpy(), None, None, to_orc(L.WoT), Kc, Vc,
+                                    L.lens.numpy().copy(), np.arange(cfg.H, dtype=np.int32),
+                                    orc.F16)
+        norms = np.linalg.norm(o, axis=1)
+        fr.append(np.mean(norms > 0.1))
+        gap.append(np.mean((norms > 0.02) & (norms < 0.1)))
+    assert 0.1 < np.mean(fr) < 0.35, fr
+    assert np.mean(gap) < 0.1, gap
