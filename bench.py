@@ -57,6 +57,8 @@ def parse():
                     help="steps of the post-gate zero-skip legs (0: skip them)")
     ap.add_argument("--silu-steps", type=int, default=300,
                     help="timed steps per variant of the SwiGLU functional-sparsity leg (0 = skip)")
+    ap.add_argument("--attn-steps", type=int, default=200,
+                    help="timed steps per variant of the attention-head sparsity leg (0 = skip)")
     ap.add_argument("--locality-steps", type=int, default=400,
                     help="steps of the hot-block (static locality) leg (0: skip it)")
     ap.add_argument("--stack-tokens", type=int, default=16,
@@ -251,6 +253,10 @@ def main():
     if args.silu_steps > 0:
         silu = silu_functional_leg(args, dev)
 
+    attn = None
+    if args.attn_steps > 0:
+        attn = attention_leg(args, dev)
+
     # ---- batched union leg (OPT-30B shape) --------------------------------------------------
     batched = None
     locality_res = None
@@ -311,6 +317,7 @@ def main():
         "cpu_baseline": cpu,
         "zero_skip": zero_skip,
         "silu_functional": silu,
+        "attention_heads": attn,
         "static_locality": locality_res,
         "batched_union": batched,
         "stack": stack,
@@ -626,6 +633,155 @@ def silu_functional_leg(args, dev):
         f"+skip {timing[f'topk_{cfg.k}+skip']['us_per_layer']} us err "
         f"{res['rel_l2_err'][f'topk_{cfg.k}+skip']}; functional-set err {res['rel_l2_err']['functional']}")
     del layers, L0
+    torch.cuda.empty_cache()
+    return res
+
+
+ATTN_KERNELS = ["pred_down", "pred_up", "select_topk", "head_proj", "head_attn", "head_combine",
+                "gather_down", "reduce_partials"]
+
+
+def attention_leg(args, dev):
+    """OPT-175B attention shape (d 12288, 96 heads of 128, 2048 cached tokens, f16): the head
+    predictor + top-19 heads + the decode step over them, against the dense decode step (every
+    head).  Each step appends the token's k, v to the computed heads' caches; the lengths are reset
+    to the context before each timed variant.  Quality over 16 (layer, token) pairs: a head is
+    active when its dense output has |o_h| > 0.1 (the silent heads sit at ~1e-3)."""
+    import dataclasses
+    import torch
+    import contextual_sparsity_ffn_amd as csf
+    from contextual_sparsity_ffn_amd import _lib, workloads as wl
+
+    cfg = dataclasses.replace(wl.ATTN_CONFIGS[1], extra=256)
+    d, H, dh, r, k, T = cfg.d, cfg.H, cfg.dh, cfg.r, cfg.k, cfg.context
+    code = _lib.dtype_code(cfg.dtype)
+    nl, ntok = 4, 64
+    steps = min(args.attn_steps, nl * (cfg.extra - 16))
+    layers = [wl.make_attention_layer(cfg, device=dev, layer=l) for l in range(nl)]
+    X = wl.make_attn_tokens(cfg, ntok, device=dev)
+    lens0 = layers[0].lens.clone()
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+    ws_b = csf.attention_workspace_size(_lib.OP_ATTN_LAYER, d, H, dh, r, cfg.Tmax, H, code)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    heads = torch.empty(H, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    lfn, dfn = _lib.lib.csf_sparse_attention_layer, _lib.lib.csf_sparse_attention_decode
+
+    def reset():
+        for L in layers:
+            L.lens.copy_(lens0)
+
+    def sparse_step(s, y_out=y, heads_out=None, count_out=None):
+        L = layers[s % nl]
+        rc = lfn(vp(X[(s * 7) % ntok].data_ptr()), d, H, dh, r, code, vp(L.Vp.data_ptr()),
+                 vp(L.Up.data_ptr()), vp(L.Wq.data_ptr()), vp(L.Wk.data_ptr()), vp(L.Wv.data_ptr()),
+                 vp(L.bq.data_ptr()), None, None, vp(L.WoT.data_ptr()), vp(L.Kc.data_ptr()),
+                 vp(L.Vc.data_ptr()), cfg.Tmax, vp(L.lens.data_ptr()), k, ctypes.c_float(0.0), 0,
+                 None, None if heads_out is None else vp(heads_out.data_ptr()),
+                 None if count_out is None else vp(count_out.data_ptr()), None,
+                 vp(y_out.data_ptr()), vp(ws.data_ptr()), ws_b, vp(stream.cuda_stream))
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+
+    def dense_step(s, y_out=y, o_out=None):
+        L = layers[s % nl]
+        rc = dfn(vp(X[(s * 7) % ntok].data_ptr()), d, H, dh, code, vp(L.Wq.data_ptr()),
+                 vp(L.Wk.data_ptr()), vp(L.Wv.data_ptr()), vp(L.bq.data_ptr()), None, None,
+                 vp(L.WoT.data_ptr()), vp(L.Kc.data_ptr()), vp(L.Vc.data_ptr()), cfg.Tmax,
+                 vp(L.lens.data_ptr()), None, None, H, 0,
+                 None if o_out is None else vp(o_out.data_ptr()), vp(y_out.data_ptr()),
+                 vp(ws.data_ptr()), ws_b, vp(stream.cuda_stream))
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+
+    def timed(step):
+        reset()
+        for s in range(8):
+            step(s)
+        reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            step(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us_sparse = timed(sparse_step)
+    us_dense = timed(dense_step)
+
+    # per-kernel times of the sparse layer (its eight kernels)
+    reset()
+    n = 40
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(16)] for _ in range(n)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for s in range(n):
+        csf.set_trace_events(evs[s])
+        sparse_step(s)
+    csf.set_trace_events([])
+    torch.cuda.synchronize()
+    kern = {name: round(sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(n))
+                        * 1e3 / n, 3) for i, name in enumerate(ATTN_KERNELS)}
+
+    # quality: predicted heads against the heads the dense step finds active
+    reset()
+    o = torch.empty(H, dh, dtype=torch.float32, device=dev)
+    yd = torch.empty(d, dtype=torch.float32, device=dev)
+    ys = torch.empty(d, dtype=torch.float32, device=dev)
+    yb = torch.empty(d, dtype=torch.float32, device=dev)
+    rec, prec, act, err, err_best, err_act = [], [], [], [], [], []
+    for q in range(16):
+        L = layers[q % nl]
+        xq = X[(q * 7) % ntok]
+        reset()
+        dense_step(q, y_out=yd, o_out=o)
+        reset()
+        sparse_step(q, y_out=ys, heads_out=heads, count_out=count)
+        torch.cuda.synchronize()
+        norms = o.norm(dim=1)
+        active = torch.nonzero(norms > 0.1).flatten()
+        pred = heads[:k].long()
+        hit = int(torch.isin(pred, active).sum())
+        rec.append(hit / max(active.numel(), 1))
+        prec.append(hit / k)
+        act.append(active.numel() / H)
+        err.append(float((ys - yd).norm() / yd.norm()))
+        for sel, acc in ((torch.sort(torch.topk(norms, k).indices).values, err_best),
+                         (active, err_act)):
+            reset()
+            csf.sparse_attention_decode(xq, L.Wq, L.Wk, L.Wv, L.bq, None, None, L.WoT, L.Kc, L.Vc,
+                                        L.lens, heads=sel.int().contiguous(), y=yb)
+            torch.cuda.synchronize()
+            acc.append(float((yb - yd).norm() / yd.norm()))
+    reset()
+    mean = lambda v: sum(v) / len(v)
+    touched = wl.attn_touched_bytes(cfg, k, T)
+    es = 2
+    dense_b = 4 * H * dh * d * es + 2 * H * (T + 1) * dh * es + d * es
+    res = {"workload": "OPT-175B attention decode step, batch 1: d 12288, 96 heads x 128, 2048 "
+                       "cached tokens, float16, predictor rank 256, top-19 heads",
+           "layers_rotated": nl, "steps": steps, "k_heads": k,
+           "us_per_step": round(us_sparse, 3), "touched_bytes": touched,
+           "GBps_on_touched": round(touched / (us_sparse * 1e-6) / 1e9, 1),
+           "dense_us_per_step": round(us_dense, 3), "dense_bytes": dense_b,
+           "dense_GBps": round(dense_b / (us_dense * 1e-6) / 1e9, 1),
+           "speedup_vs_dense": round(us_dense / us_sparse, 3),
+           "speedup_bound_bytes": round(dense_b / touched, 3),
+           "active_frac": round(mean(act), 4), "recall_vs_active": round(mean(rec), 4),
+           "precision_vs_active": round(mean(prec), 4),
+           "rel_l2_err": {"predicted_top19": round(mean(err), 4),
+                          "best_19_by_norm": round(mean(err_best), 4),
+                          "active_set": round(mean(err_act), 4)},
+           "kernels_avg_us": kern}
+    log(f"attention heads: sparse {us_sparse:.1f} us, dense {us_dense:.1f} us, "
+        f"recall {res['recall_vs_active']}, err {res['rel_l2_err']['predicted_top19']}")
+    del layers
     torch.cuda.empty_cache()
     return res
 

@@ -510,7 +510,7 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
 
 // ---- attention-head sparsity ---------------------------------------------------------------------
 struct AttnWs {
-    size_t lens0, q, part, rows, hv, rcount, ffn, a, scores, heads, count, total;
+    size_t lnew, q, part, rows, hv, rcount, ffn, a, scores, heads, count, total;
 };
 AttnWs attn_ws(int d, int H, int dh, int r, int Tmax, int max_heads, int dtype, bool layer)
 {
@@ -518,8 +518,8 @@ AttnWs attn_ws(int d, int H, int dh, int r, int Tmax, int max_heads, int dtype, 
     const size_t mh = max_heads > 0 ? (size_t)max_heads : 1;
     const int max_rows = max_heads * dh;
     size_t o = 0;
-    w.lens0 = o;
-    o += round_up((size_t)H * sizeof(int32_t));
+    w.lnew = o;
+    o += round_up(mh * sizeof(int32_t));
     w.q = o;
     o += round_up(mh * dh * sizeof(float));
     w.part = o;
@@ -560,6 +560,8 @@ int validate_attention(const void *x, int d, int H, int dh, int dtype, const voi
     REQUIRE((long)H * dh <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED,
             "H * dh = %ld exceeds this build's limit %d", (long)H * dh, csf::ffn_max_count());
     REQUIRE(Tmax > 0, CSF_ERR_INVALID_ARG, "Tmax must be positive (got %d)", Tmax);
+    REQUIRE(Tmax <= csf::attn_max_cache(), CSF_ERR_UNSUPPORTED,
+            "Tmax = %d exceeds this build's limit %d", Tmax, csf::attn_max_cache());
     REQUIRE(kv_all == 0 || kv_all == 1, CSF_ERR_INVALID_ARG, "kv_all must be 0 or 1");
     CHECK_PTR(x, true);
     CHECK_PTR(Wq, true);
@@ -607,7 +609,7 @@ int enqueue_attention(const void *x, int d, int H, int dh, int dtype, const void
     a.kv_all = kv_all;
     a.o = o;
     a.y = y;
-    a.lens0 = reinterpret_cast<int32_t *>(at(ws, w.lens0));
+    a.lnew = reinterpret_cast<int32_t *>(at(ws, w.lnew));
     a.qbuf = reinterpret_cast<float *>(at(ws, w.q));
     a.part = reinterpret_cast<float *>(at(ws, w.part));
     a.rows = reinterpret_cast<int32_t *>(at(ws, w.rows));

@@ -20,9 +20,9 @@
 //                   dh*es/16 lanes reads one cached row per 16-byte load, so a wavefront reads
 //                   whole 128-byte lines; the block's softmax numerator and partial o are kept
 //                   with the block maximum (the flash-decoding split);
-//   k_head_combine  one workgroup per listed head merges the blocks in order (deterministic),
-//                   turns o_h into the list of output-projection rows and their weights, and
-//                   advances the cache lengths;
+//   k_head_combine  one workgroup per listed head merges the blocks in a fixed order
+//                   (deterministic), turns o_h into the list of output-projection rows and their
+//                   weights, and advances the cache lengths;
 //   then the FFN's neuron-major down projection (k_gather_down + k_reduce_partials) reads the
 //   rows of WoT of the listed heads.
 #include "common.hpp"
@@ -33,6 +33,7 @@ namespace csf {
 namespace {
 
 constexpr int kAttnChunk = 128;   // cached positions per attention workgroup
+constexpr int kMaxAttnSplits = 1024;   // blocks per head: caches of up to 131072 positions
 
 template <class T>
 __device__ __forceinline__ void store_cache(void *base, size_t i, float v)
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(256) void k_head_attn(const float *__restrict__ qbu
                                                    const int32_t *__restrict__ count,
                                                    int max_heads, int H, int dh, int Tmax,
                                                    const int32_t *__restrict__ len, int nsplit,
-                                                   float scale, float *__restrict__ part)
+                                                   float scale, float *__restrict__ part,
+                                                   int32_t *__restrict__ lnew)
 {
     constexpr int E = T::E;
     constexpr int PPW = kWave / LPP;            // cached rows per wavefront load
@@ -173,6 +175,8 @@ __global__ __launch_bounds__(256) void k_head_attn(const float *__restrict__ qbu
     const int g = lane / LPP, li = lane % LPP;
     const int n = blockIdx.x, s = blockIdx.y;
     const int h = list_head(heads, count, max_heads, n, H, len, Tmax);
+    if (s == 0 && t == 0)
+        lnew[n] = h < 0 ? -1 : len[h] + 1;      // for the combine kernel, which advances len
     if (h < 0)
         return;
     const int L = len[h] + 1;                   // the new token was appended at len[h]
@@ -187,12 +191,17 @@ __global__ __launch_bounds__(256) void k_head_attn(const float *__restrict__ qbu
     for (int e = 0; e < E; ++e)
         qv[e] = qbuf[(size_t)n * dh + li * E + e];
 
-    // logits of the block: all key loads first
-    u32x4 kv[IT];
+    // every key and value load of the block is issued before the first use
+    u32x4 kv[IT], vv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int pos = p0 + it * PPI + w * PPW + g;
         kv[it] = pos < p1 ? Kc[(hrow + pos) * LPP + li] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int pos = p0 + it * PPI + w * PPW + g;
+        vv[it] = pos < p1 ? Vc[(hrow + pos) * LPP + li] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -231,12 +240,6 @@ __global__ __launch_bounds__(256) void k_head_attn(const float *__restrict__ qbu
     const float l = (wred[0] + wred[1]) + (wred[2] + wred[3]);
 
     // o = sum_t e_t V[t]: each lane group accumulates its rows, then the groups are summed
-    u32x4 vv[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int pos = p0 + it * PPI + w * PPW + g;
-        vv[it] = pos < p1 ? Vc[(hrow + pos) * LPP + li] : u32x4{0u, 0u, 0u, 0u};
-    }
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -267,24 +270,32 @@ __global__ __launch_bounds__(256) void k_head_attn(const float *__restrict__ qbu
     }
 }
 
-// One workgroup per list entry: merge the blocks of the head in order into o_h, write the output
-// projection's row list (rows h*dh + i with weights o_h[i]; -1 for a skipped entry), the optional
-// copy of o, and (workgroup 0) the row count and the new cache lengths.  Reads the lengths only
-// through `lens_in`, the values the earlier kernels used, so the update cannot race.
+// One workgroup per list entry: merge the blocks of the head into o_h (block weights
+// w_s = exp(m_s - M), M the largest block maximum; o_h = sum_s w_s o_s / sum_s w_s l_s, every sum
+// in a fixed order), write the output projection's row list (rows h*dh + i with weights o_h[i];
+// -1 for a skipped entry) and the optional copy of o.  Workgroup 0 also writes the row count and
+// advances the cache lengths; no workgroup of this kernel reads len, so the update cannot race
+// (the attention lengths come from lnew).  The G = 256 / dh thread groups take every G-th block.
 __global__ __launch_bounds__(256) void k_head_combine(const float *__restrict__ part,
                                                       const int32_t *__restrict__ heads,
                                                       const int32_t *__restrict__ count,
                                                       int max_heads, int H, int dh, int Tmax,
-                                                      const int32_t *__restrict__ lens_in,
+                                                      const int32_t *__restrict__ lnew,
                                                       int32_t *__restrict__ len, int kv_all,
                                                       int nsplit, int32_t *__restrict__ rows,
                                                       float *__restrict__ hv,
                                                       int32_t *__restrict__ rows_count,
                                                       float *__restrict__ o_out)
 {
-    const int t = threadIdx.x;
+    __shared__ float sw[kMaxAttnSplits];
+    __shared__ float red[4];
+    __shared__ float osum[256];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int n = blockIdx.x;
-    const int h = list_head(heads, count, max_heads, n, H, lens_in, Tmax);
+    int cnt = count ? *count : max_heads;
+    cnt = cnt < 0 ? 0 : (cnt > max_heads ? max_heads : cnt);
+    const int L = n < cnt ? lnew[n] : -1;
+    const int h = L > 0 ? (heads ? heads[n] : n) : -1;
     if (h < 0) {
         for (int i = t; i < dh; i += 256) {
             rows[(size_t)n * dh + i] = -1;
@@ -293,52 +304,78 @@ __global__ __launch_bounds__(256) void k_head_combine(const float *__restrict__ 
                 o_out[(size_t)n * dh + i] = 0.0f;
         }
     } else {
-        const int L = lens_in[h] + 1;
         const int ns = (L + kAttnChunk - 1) / kAttnChunk;
-        const float *pp = part + (size_t)n * nsplit * (dh + 2);
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s)
-            M = fmaxf(M, pp[(size_t)s * (dh + 2)]);
-        float lsum = 0.0f;
-        for (int s = 0; s < ns; ++s)
-            lsum += pp[(size_t)s * (dh + 2) + 1] * expf(pp[(size_t)s * (dh + 2)] - M);
-        const float inv = 1.0f / lsum;
-        for (int i = t; i < dh; i += 256) {
+        const int stride = dh + 2;
+        const float *pp = part + (size_t)n * nsplit * stride;
+        // M: every block maximum loaded at once (thread t owns blocks t, t + 256, ...)
+        float mv = -INFINITY;
+        for (int s = t; s < ns; s += 256)
+            mv = fmaxf(mv, pp[(size_t)s * stride]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            mv = fmaxf(mv, __shfl_xor(mv, o, kWave));
+        if (lane == 0)
+            red[w] = mv;
+        __syncthreads();
+        const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        float lv = 0.0f;
+        for (int s = t; s < ns; s += 256) {
+            const float ws = expf(pp[(size_t)s * stride] - M);
+            sw[s] = ws;
+            lv += ws * pp[(size_t)s * stride + 1];
+        }
+        lv = wave_sum(lv);
+        if (lane == 0)
+            red[w] = lv;
+        __syncthreads();
+        const float inv = 1.0f / ((red[0] + red[1]) + (red[2] + red[3]));
+        // o: thread t takes dimension t % dh over blocks t / dh, t / dh + G, ... (four loads in
+        // flight per step)
+        const int G = 256 / dh;
+        const int i = t % dh, g = t / dh;
+        float acc = 0.0f;
+        if (g < G) {
+            int s = g;
+            for (; s + 3 * G < ns; s += 4 * G) {
+                const float a0 = pp[(size_t)s * stride + 2 + i];
+                const float a1 = pp[(size_t)(s + G) * stride + 2 + i];
+                const float a2 = pp[(size_t)(s + 2 * G) * stride + 2 + i];
+                const float a3 = pp[(size_t)(s + 3 * G) * stride + 2 + i];
+                acc = fmaf(sw[s], a0, acc);
+                acc = fmaf(sw[s + G], a1, acc);
+                acc = fmaf(sw[s + 2 * G], a2, acc);
+                acc = fmaf(sw[s + 3 * G], a3, acc);
+            }
+            for (; s < ns; s += G)
+                acc = fmaf(sw[s], pp[(size_t)s * stride + 2 + i], acc);
+        }
+        osum[t] = acc;
+        __syncthreads();
+        if (t < dh) {
             float o = 0.0f;
-            for (int s = 0; s < ns; ++s)
-                o += pp[(size_t)s * (dh + 2) + 2 + i] * expf(pp[(size_t)s * (dh + 2)] - M);
+            for (int q = 0; q < G; ++q)
+                o += osum[q * dh + t];
             o *= inv;
-            rows[(size_t)n * dh + i] = h * dh + i;
-            hv[(size_t)n * dh + i] = o;
+            rows[(size_t)n * dh + t] = h * dh + t;
+            hv[(size_t)n * dh + t] = o;
             if (o_out)
-                o_out[(size_t)n * dh + i] = o;
+                o_out[(size_t)n * dh + t] = o;
         }
     }
     if (n == 0) {
-        int cnt = count ? *count : max_heads;
-        cnt = cnt < 0 ? 0 : (cnt > max_heads ? max_heads : cnt);
         if (t == 0)
             *rows_count = cnt * dh;
         if (kv_all) {
             for (int q = t; q < H; q += 256)
-                if (lens_in[q] >= 0 && lens_in[q] < Tmax)
-                    len[q] = lens_in[q] + 1;
+                if (len[q] >= 0 && len[q] < Tmax)
+                    len[q] += 1;
         } else {
-            for (int q = t; q < cnt; q += 256) {
-                const int hq = list_head(heads, count, max_heads, q, H, lens_in, Tmax);
-                if (hq >= 0)
-                    len[hq] = lens_in[hq] + 1;
-            }
+            for (int q = t; q < cnt; q += 256)
+                if (lnew[q] > 0)
+                    len[heads ? heads[q] : q] = lnew[q];
         }
     }
-}
-
-// The lengths the step starts from, copied so that the combine kernel can advance len in place.
-__global__ __launch_bounds__(256) void k_copy_lens(const int32_t *__restrict__ len, int H,
-                                                   int32_t *__restrict__ out)
-{
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < H; i += gridDim.x * 256)
-        out[i] = len[i];
 }
 
 template <class T, int MX>
@@ -356,7 +393,7 @@ hipError_t proj_launch(const AttnArgs &a, const int32_t *heads, const int32_t *c
                   static_cast<const u32x4 *>(a.x), static_cast<const u32x4 *>(a.Wq),
                   static_cast<const u32x4 *>(a.Wk), static_cast<const u32x4 *>(a.Wv), a.bq, a.bk,
                   a.bv, heads, count, nlist, a.H, a.dh, a.d / T::E, proj, np, a.qbuf, a.Kc, a.Vc,
-                  a.Tmax, a.lens0);
+                  a.Tmax, a.len);
 }
 
 template <class T>
@@ -380,8 +417,8 @@ hipError_t attn_launch(const AttnArgs &a, hipStream_t st, Trace *tr)
     const int nsplit = attn_num_splits(a.Tmax);
     return launch(k_head_attn<T, LPP>, dim3(a.max_heads, nsplit), dim3(256), st, tr, a.qbuf,
                   static_cast<const u32x4 *>(a.Kc), static_cast<const u32x4 *>(a.Vc), a.heads,
-                  a.count, a.max_heads, a.H, a.dh, a.Tmax, a.lens0, nsplit,
-                  1.0f / sqrtf((float)a.dh), a.part);
+                  a.count, a.max_heads, a.H, a.dh, a.Tmax, a.len, nsplit,
+                  1.0f / sqrtf((float)a.dh), a.part, a.lnew);
 }
 
 template <class T>
@@ -401,10 +438,7 @@ hipError_t attn_t(const AttnArgs &a, hipStream_t st, Trace *tr)
 template <class T>
 hipError_t decode_t(const AttnArgs &a, hipStream_t st, Trace *tr)
 {
-    hipError_t e = launch(k_copy_lens, dim3((a.H + 255) / 256), dim3(256), st, tr, a.len, a.H,
-                          a.lens0);
-    if (e != hipSuccess)
-        return e;
+    hipError_t e;
     if (a.kv_all) {
         e = proj_t<T>(a, a.heads, a.count, a.max_heads, 1, st, tr);              // q of the list
         if (e == hipSuccess)
@@ -420,7 +454,7 @@ hipError_t decode_t(const AttnArgs &a, hipStream_t st, Trace *tr)
             return e;
     }
     e = launch(k_head_combine, dim3(a.max_heads > 0 ? a.max_heads : 1), dim3(256), st, tr,
-               a.part, a.heads, a.count, a.max_heads, a.H, a.dh, a.Tmax, a.lens0, a.len, a.kv_all,
+               a.part, a.heads, a.count, a.max_heads, a.H, a.dh, a.Tmax, a.lnew, a.len, a.kv_all,
                attn_num_splits(a.Tmax), a.rows, a.hv, a.rows_count, a.o);
     if (e != hipSuccess)
         return e;
@@ -449,6 +483,8 @@ hipError_t decode_t(const AttnArgs &a, hipStream_t st, Trace *tr)
 }  // namespace
 
 int attn_num_splits(int Tmax) { return (Tmax + kAttnChunk - 1) / kAttnChunk; }
+
+int attn_max_cache() { return kMaxAttnSplits * kAttnChunk; }
 
 bool attn_head_dim_supported(int dtype, int dh)
 {

@@ -125,7 +125,7 @@ struct AttnArgs {
     float *o;                       // [max_heads][dh] or null
     float *y;                       // [d]
     // workspace
-    int32_t *lens0;                 // [H] lengths at the start of the step
+    int32_t *lnew;                  // [max_heads] attention length of each list entry (-1: skip)
     float *qbuf;                    // [max_heads][dh]
     float *part;                    // [max_heads][attn_num_splits(Tmax)][dh + 2]
     int32_t *rows;                  // [max_heads * dh]
@@ -134,6 +134,7 @@ struct AttnArgs {
     float *ffn_partials;            // [ffn_num_chunks(d, dtype, max_heads * dh)][d]
 };
 int attn_num_splits(int Tmax);
+int attn_max_cache();   // largest Tmax the attention kernels take
 bool attn_head_dim_supported(int dtype, int dh);
 hipError_t launch_attention_decode(const AttnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 

@@ -380,9 +380,8 @@ int csf_set_ffn_gate_threshold(float tau);
  * gathered up/gate rows, gathered down rows (partial sums), reduction of the partial sums;
  * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction;
  * csf_sparse_ffn_batched_layer: the predictor's two kernels, selection, then the union's four;
- * csf_sparse_attention_decode: copy of the lengths, projections (q, k, v of the list; with kv_all
- * q of the list then k, v of every head), attention blocks, combine, output-projection rows,
- * reduction; csf_sparse_attention_layer: the predictor's two kernels and selection first.
+ * csf_sparse_attention_decode: projections (q, k, v of the list; with kv_all q of the list then
+ * k, v of every head), attention blocks, combine, output-projection rows, reduction; csf_sparse_attention_layer: the predictor's two kernels and selection first.
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
  * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */
