@@ -28,7 +28,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-FFN µs/layer + HBM GB/s on touched bytes, batch 1, OPT-175B shape @5%"
 PEAK_HBM_GBS = 8000.0
-KERNELS = ["pred_down", "pred_up", "select_topk", "gather_up", "gather_down", "reduce_partials"]
+KERNELS = ["pred_down", "pred_up", "select_hist", "select_classify", "select_emit", "gather_up",
+           "gather_down", "reduce_partials"]
+
+
+def layer_kernels(f, k):
+    """Kernels of csf_sparse_ffn_layer for one token: top-k over 20000 or more scores runs as
+    three kernels (histogram, classify, emit), a smaller one as one."""
+    if k is not None and k > 0 and f >= 20000:
+        return KERNELS
+    return ["pred_down", "pred_up", "select_topk" if k is not None else "select_threshold",
+            "gather_up", "gather_down", "reduce_partials"]
 
 
 def log(msg):
@@ -163,7 +173,9 @@ def main():
     kernel_bytes = {
         "pred_down": r * d * es + d * es + r * 4,
         "pred_up": f * r * es + r * 4 + f * 4,
-        "select_topk": f * 4 + k * 4,
+        "select_hist": f * 4,
+        "select_classify": f * 4 + f // 8,
+        "select_emit": f // 8 + k * 4,
         "gather_up": k * d * es + d * es + k * 4 + k * 4,
         "gather_down": k * d * es + k * 8,
         "reduce_partials": 0,
@@ -608,7 +620,8 @@ def silu_functional_leg(args, dev):
         for skip in (False, True):
             set_skip(skip)
             n = 50
-            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
+            names = layer_kernels(f, cfg.k)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
                    for _ in range(n)]
             for row in evs:
                 for e in row:
@@ -621,7 +634,7 @@ def silu_functional_leg(args, dev):
             torch.cuda.synchronize()
             kern["skip" if skip else "plain"] = {
                 name: round(sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(n))
-                            * 1e3 / n, 3) for i, name in enumerate(KERNELS)}
+                            * 1e3 / n, 3) for i, name in enumerate(names)}
     finally:
         csf.set_trace_events([])
         set_skip(False)

@@ -208,7 +208,8 @@ def select_topk(scores, k, idx=None, count=None, bitmap=None):
         raise ValueError("idx is too small")
     _tensor(count, "count", dtype=torch.int32, device=dev, optional=True)
     _tensor(bitmap, "bitmap", dtype=torch.int32, device=dev, optional=True)
-    _check(lib.csf_select_topk(_ptr(S), B, f, k, _ptr(idx), _ptr(count), _ptr(bitmap), None, 0,
+    w, wb = _workspace(workspace_size(OP_SELECT_TOPK, B, 1, f, 0, k), dev)
+    _check(lib.csf_select_topk(_ptr(S), B, f, k, _ptr(idx), _ptr(count), _ptr(bitmap), _ptr(w), wb,
                                _stream(dev)))
     out = idx.view(B, -1)[:, :k]
     return out[0] if squeeze else out

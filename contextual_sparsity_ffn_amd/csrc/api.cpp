@@ -153,7 +153,7 @@ FfnWs ffn_ws(int B, int d, int dtype, int max_count)
 }
 
 struct LayerWs {
-    size_t a, scores, idx, count, ffn, total;
+    size_t a, scores, idx, count, sel, ffn, total;
 };
 LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
 {
@@ -162,7 +162,8 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
     w.scores = w.a + round_up((size_t)csf::kMaxPredSplit * r * sizeof(float));
     w.idx = w.scores + round_up((size_t)f * sizeof(float));
     w.count = w.idx + round_up((size_t)f * sizeof(int32_t));
-    w.ffn = w.count + round_up(sizeof(int32_t));
+    w.sel = w.count + round_up(sizeof(int32_t));
+    w.ffn = w.sel + round_up((size_t)csf::select_wide_ws_words(f) * sizeof(uint32_t));
     w.total = w.ffn + ffn_ws(1, d, dtype, max_count).total;
     return w;
 }
@@ -247,6 +248,14 @@ StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
 }
 
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+// top-k of a few tokens with many scores runs over many workgroups and needs a counter block
+size_t select_ws_bytes(int B, int f, int k)
+{
+    if (!csf::select_wide_used(B, f, k))
+        return 0;
+    return round_up((size_t)B * csf::select_wide_ws_words(f) * sizeof(uint32_t));
+}
 
 int check_ws(void *ws, size_t ws_bytes, size_t need)
 {
@@ -689,6 +698,7 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
     case CSF_OP_PREDICT:
         return r > 0 ? predict_ws(B, r).total : 0;
     case CSF_OP_SELECT_TOPK:
+        return select_ws_bytes(B, f, max_count);
     case CSF_OP_SELECT_THRESHOLD:
         return 0;
     case CSF_OP_SPARSE_FFN:
@@ -733,8 +743,6 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
 int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
                     uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
     REQUIRE(k >= 0 && k <= f, CSF_ERR_INVALID_ARG, "k = %d is outside [0, f = %d]", k, f);
@@ -746,6 +754,13 @@ int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int3
     CHECK_PTR(bitmap, false);
     if (B == 0)
         return ok();
+    if (csf::select_wide_used(B, f, k)) {
+        CHECK_WS(ws, ws_bytes, select_ws_bytes(B, f, k));
+        return hip_status(csf::launch_select_topk_wide(scores, B, f, k, idx, k, count, bitmap,
+                                                       static_cast<uint32_t *>(ws), false,
+                                                       static_cast<hipStream_t>(stream)),
+                          "top-k selection launch");
+    }
     return hip_status(csf::launch_select_topk(scores, B, f, k, idx, k > 0 ? k : 1, count, bitmap,
                                               static_cast<hipStream_t>(stream)),
                       "top-k selection launch");
@@ -1059,13 +1074,19 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
 
     csf::Trace *trp = tr.ev ? &tr : nullptr;
-    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp);
+    const bool wide = k >= 0 && csf::select_wide_used(1, f, k);
+    uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, w.sel));
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
+                                         wide ? csf::select_wide_zero_words() : 0);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
     e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "predictor up-projection launch");
-    if (k >= 0)
+    if (wide)
+        e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr,
+                                         selws, true, st, trp);
+    else if (k >= 0)
         e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st,
                                     trp);
     else

@@ -46,9 +46,11 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
 // Split-K factor of the predictor's down projection (rows of V split over S workgroups).
 constexpr int kMaxPredSplit = 4;
 int pred_split(int r, int d, int dtype);
-// part[S][B][r] = split-K partial sums of V x_t (float32), S = pred_split(r, d, dtype).
+// part[S][B][r] = split-K partial sums of V x_t (float32), S = pred_split(r, d, dtype).  zero
+// (optional): nzero words that the launch also clears, for a later kernel of the same call.
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *part, hipStream_t stream, Trace *trace = nullptr);
+                            float *part, hipStream_t stream, Trace *trace = nullptr,
+                            uint32_t *zero = nullptr, int nzero = 0);
 // s[B][f] = sigmoid(U relu(sum of the partials)) in float32.
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
                           float *s, hipStream_t stream, Trace *trace = nullptr);
@@ -76,6 +78,16 @@ hipError_t launch_select_threshold(const float *scores, int B, int f, float tau,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
                                    hipStream_t stream, Trace *trace = nullptr, int prefix = 0);
 int select_max_f();   // largest f the selection kernels accept
+// Top-k of a few tokens with many scores, spread over many workgroups (three kernels).  ws holds
+// select_wide_ws_words(f) 32-bit words per token; its first select_wide_zero_words() words of each
+// token must be zero at the start: pass zeroed = false to have this launch clear them.
+bool select_wide_used(int B, int f, int k);
+int select_wide_ws_words(int f);
+int select_wide_zero_words();
+hipError_t launch_select_topk_wide(const float *scores, int B, int f, int k, int32_t *idx,
+                                   int idx_stride, int32_t *count, uint32_t *bitmap, uint32_t *ws,
+                                   bool zeroed, hipStream_t stream, Trace *trace = nullptr,
+                                   int prefix = 0);
 
 // ---- FFN (ffn.hip) --------------------------------------------------------------------------
 struct FfnArgs {

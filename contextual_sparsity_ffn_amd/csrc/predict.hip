@@ -25,9 +25,14 @@ namespace {
 template <class T, int MX, int TG>
 __global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
                                                    const u32x4 *__restrict__ x, int C, int r,
-                                                   int B, int S, float *__restrict__ part)
+                                                   int B, int S, float *__restrict__ part,
+                                                   uint32_t *__restrict__ zero, int nzero)
 {
     __shared__ float red[4][TG];
+    // workgroup 0 also clears a caller's counter block for a later kernel of the same call
+    if (zero && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nzero; i += 256)
+            zero[i] = 0u;
     const int i = blockIdx.x / S, sp = blockIdx.x % S;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int cper = (C + S - 1) / S;
@@ -145,6 +150,8 @@ struct DownArgs {
     const void *V;
     int r, S;
     float *a;
+    uint32_t *zero;
+    int nzero;
 };
 
 template <class T, int MX>
@@ -153,9 +160,9 @@ hipError_t down_mx(const DownArgs &g, hipStream_t st, Trace *tr)
     const u32x4 *V = static_cast<const u32x4 *>(g.V), *x = static_cast<const u32x4 *>(g.x);
     if (g.B == 1)
         return launch(k_pred_down<T, MX, 1>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r,
-                      g.B, g.S, g.a);
+                      g.B, g.S, g.a, g.zero, g.nzero);
     return launch(k_pred_down<T, MX, 8>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r, g.B,
-                  g.S, g.a);
+                  g.S, g.a, g.zero, g.nzero);
 }
 
 template <class T>
@@ -229,9 +236,9 @@ int pred_split(int r, int d, int dtype)
 }
 
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *a, hipStream_t st, Trace *tr)
+                            float *a, hipStream_t st, Trace *tr, uint32_t *zero, int nzero)
 {
-    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a};
+    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a, zero, nzero};
     if (dtype == 0) return down_t<F32T>(g, st, tr);
     if (dtype == 1) return down_t<F16T>(g, st, tr);
     return down_t<BF16T>(g, st, tr);

@@ -114,14 +114,12 @@ __device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int 
             bitmap_out[w] = bm[w];
 }
 
+// The whole selection of one token by one 1024-thread workgroup (steps 1-4 above).
 template <int NB, int J, bool VEC>
-__global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__restrict__ scores,
-                                                             int f, int k,
-                                                             int32_t *__restrict__ idx,
-                                                             int idx_stride,
-                                                             int32_t *__restrict__ count,
-                                                             uint32_t *__restrict__ bitmap,
-                                                             int prefix)
+__device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ scores, int token,
+                                                   int f, int k, int32_t *__restrict__ idx,
+                                                   int idx_stride, int32_t *__restrict__ count,
+                                                   uint32_t *__restrict__ bitmap, int prefix)
 {
     __shared__ uint32_t hist[NB];
     __shared__ uint32_t bm[kMaxWords];
@@ -132,7 +130,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
     __shared__ uint32_t misc[8];   // 0: B*, 1: need, 2: candidate count, 3: digit, 4: krem
 
     const int t = threadIdx.x;
-    const int token = blockIdx.x;
     const float *s = scores + (size_t)token * f;
     const int words = (f + 31) / 32;
     int32_t *out = idx + (size_t)token * idx_stride;
@@ -311,6 +308,250 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
     bitmap_to_list(bm, words, out + prefix, idx_stride - prefix, prefix, bm_out, scan_tmp, nullptr);
 }
 
+template <int NB, int J, bool VEC>
+__global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__restrict__ scores,
+                                                             int f, int k,
+                                                             int32_t *__restrict__ idx,
+                                                             int idx_stride,
+                                                             int32_t *__restrict__ count,
+                                                             uint32_t *__restrict__ bitmap,
+                                                             int prefix)
+{
+    topk_one_workgroup<NB, J, VEC>(scores, blockIdx.x, f, k, idx, idx_stride, count, bitmap,
+                                   prefix);
+}
+
+// ---- top-k over many workgroups (one token, large f) -----------------------------------------
+// The same bucket select as topk_one_workgroup, spread over slices of kWideSlice scores so that
+// the work of one token runs on many compute units (a single workgroup retires about 64 lane
+// operations per cycle, so its passes over 49152 scores cost microseconds each):
+//   k_wide_hist      one workgroup per slice: LDS histogram of the slice, then one global atomic
+//                    add per non-empty bucket into the token's histogram (zeroed by the launch
+//                    before; integer adds, so the order does not matter);
+//   k_wide_classify  one workgroup per slice: every workgroup scans the finished histogram and
+//                    finds the same boundary bucket B* and `need`; the slice's certain members
+//                    (bucket above B*) go to the global bitmap words of the slice and their count
+//                    to slice_cnt; B*'s members are appended to a candidate list (capacity
+//                    kWideMaxCand; the count keeps growing past it);
+//   k_wide_emit      one 1024-thread workgroup per slice, thread t owning score t of the slice:
+//                    every workgroup ranks all candidates by (score desc, index asc) and keeps
+//                    the first `need`; a slice's output offset is the certain count of the
+//                    earlier slices plus the kept candidates below the slice; a block scan
+//                    places the slice's indices (ascending).  If the candidates overflowed,
+//                    workgroup 0 runs topk_one_workgroup instead (heavy ties) and the others exit.
+// Everything is integer arithmetic on the same bucket map and order keys, so the list equals
+// the one-workgroup result bit for bit.
+constexpr int kWideSlice = 1024;
+constexpr int kWideMaxCand = 512;
+constexpr int kWideMaxSlices = 64;
+
+template <int NB, bool VEC>
+__global__ __launch_bounds__(256) void k_wide_hist(const float *__restrict__ scores, int f,
+                                                   uint32_t *__restrict__ ws, int ws_stride)
+{
+    __shared__ uint32_t hist[NB];
+    const int t = threadIdx.x;
+    const int token = blockIdx.y;
+    const float *s = scores + (size_t)token * f;
+    uint32_t *ghist = ws + (size_t)token * ws_stride;
+    const int j0 = blockIdx.x * kWideSlice + 4 * t;
+    const float4 q = load_quad<VEC>(s, j0, f);
+    for (int b = t; b < NB; b += 256)
+        hist[b] = 0u;
+    __syncthreads();
+    const float e[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (e[i] == e[i])
+            atomicAdd(&hist[score_bucket<NB>(e[i])], 1u);
+    __syncthreads();
+    for (int b = t; b < NB; b += 256) {
+        const uint32_t c = hist[b];
+        if (c)
+            atomicAdd(&ghist[b], c);
+    }
+}
+
+// Workspace of one token (32-bit words): histogram [NB], candidate count, B*, need, slice
+// counts [kWideMaxSlices], candidates [kWideMaxCand] (64-bit), bitmap words [f / 32].
+constexpr int kWsNcand = kScoreBuckets, kWsBstar = kWsNcand + 1, kWsNeed = kWsNcand + 2;
+constexpr int kWsSliceCnt = kScoreBuckets + 64;
+constexpr int kWsCand = kWsSliceCnt + kWideMaxSlices;          // 64-bit aligned (even)
+constexpr int kWsWords = kWsCand + 2 * kWideMaxCand;
+
+template <int NB, bool VEC>
+__global__ __launch_bounds__(256) void k_wide_classify(const float *__restrict__ scores, int f,
+                                                       int k, uint32_t *__restrict__ ws,
+                                                       int ws_stride)
+{
+    __shared__ uint32_t scan_tmp[4];
+    __shared__ uint32_t misc[3];
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int token = blockIdx.y, slice = blockIdx.x;
+    const float *s = scores + (size_t)token * f;
+    uint32_t *W = ws + (size_t)token * ws_stride;
+    const int j0 = slice * kWideSlice + 4 * t;
+    const float4 q = load_quad<VEC>(s, j0, f);
+
+    // B* and need from the finished histogram: thread t owns buckets NB-1-BPT*t-q (top first)
+    constexpr int BPT = NB / 256;
+    if (t == 0) {
+        misc[0] = 0u;
+        misc[1] = 0u;
+        misc[2] = 0u;
+    }
+    uint32_t c[BPT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        c[i] = W[NB - 1 - (BPT * t + i)];
+        mine += c[i];
+    }
+    uint32_t total;
+    uint32_t above = block_exclusive_scan<4>(mine, scan_tmp, &total);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        if (above < (uint32_t)k && above + c[i] >= (uint32_t)k) {
+            misc[0] = (uint32_t)(NB - 1 - (BPT * t + i));
+            misc[1] = (uint32_t)k - above;
+            misc[2] = c[i];
+        }
+        above += c[i];
+    }
+    __syncthreads();
+    const int bstar = (int)misc[0];
+    // more candidates than the list holds (heavy ties): record the count, skip the appends
+    const bool overflow = misc[2] > (uint32_t)kWideMaxCand;
+    if (slice == 0 && t == 0) {
+        W[kWsBstar] = misc[0];
+        W[kWsNeed] = misc[1];
+        if (overflow)
+            W[kWsNcand] = misc[2];
+    }
+
+    // certain members into the slice's bitmap words, candidates into the global list
+    const float e[4] = {q.x, q.y, q.z, q.w};
+    uint32_t nib = 0u;
+    uint64_t *cand = reinterpret_cast<uint64_t *>(W + kWsCand);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = e[i] == e[i] ? score_bucket<NB>(e[i]) : -1;
+        nib |= (b > bstar ? 1u : 0u) << i;
+        if (b == bstar && !overflow) {
+            const uint32_t p = atomicAdd(&W[kWsNcand], 1u);
+            if (p < (uint32_t)kWideMaxCand)
+                cand[p] = composite(order_key(e[i]), j0 + i);
+        }
+    }
+    uint32_t x = nib << (4 * (lane & 7));
+    x |= __shfl_xor(x, 1, kWave);
+    x |= __shfl_xor(x, 2, kWave);
+    x |= __shfl_xor(x, 4, kWave);
+    const int words = (f + 31) / 32;
+    const int widx = slice * (kWideSlice / 32) + (t >> 3);
+    if ((lane & 7) == 0 && widx < words)
+        W[kWsWords + widx] = x;
+    uint32_t n = (uint32_t)__popc(nib);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        n += __shfl_xor(n, o, kWave);
+    if (lane == 0)
+        red[w] = n;
+    __syncthreads();
+    if (t == 0)
+        W[kWsSliceCnt + slice] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int NB, int J, bool VEC>
+__global__ __launch_bounds__(kSelThreads) void k_wide_emit(const float *__restrict__ scores,
+                                                           int f, int k,
+                                                           const uint32_t *__restrict__ ws,
+                                                           int ws_stride,
+                                                           int32_t *__restrict__ idx,
+                                                           int idx_stride,
+                                                           int32_t *__restrict__ count,
+                                                           uint32_t *__restrict__ bitmap,
+                                                           int prefix)
+{
+    __shared__ uint64_t cand[kWideMaxCand];
+    __shared__ uint32_t keep_bits[kWideSlice / 32];
+    __shared__ uint32_t before_part[kSelWaves];
+    __shared__ uint32_t scan_tmp[kSelWaves];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int token = blockIdx.y, slice = blockIdx.x;
+    const uint32_t *W = ws + (size_t)token * ws_stride;
+    const uint64_t *gc = reinterpret_cast<const uint64_t *>(W + kWsCand);
+    // every load of the kernel is issued up front: the candidate slots are read whether or not
+    // they were filled (the workspace holds all of them), the count decides which are used
+    const uint32_t nc = W[kWsNcand];
+    const uint32_t need = W[kWsNeed];
+    const uint64_t my_cand = t < kWideMaxCand ? gc[t] : 0ull;
+    const uint32_t my_slice_cnt = t < slice ? W[kWsSliceCnt + t] : 0u;
+    const int words = (f + 31) / 32;
+    const int wbase = slice * (kWideSlice / 32);
+    const uint32_t word = (wbase + (t >> 5)) < words ? W[kWsWords + wbase + (t >> 5)] : 0u;
+    const uint32_t my_word = (t < kWideSlice / 32 && wbase + t < words) ? W[kWsWords + wbase + t]
+                                                                        : 0u;
+    if (nc > (uint32_t)kWideMaxCand) {
+        // heavy ties in the boundary bucket: the one-workgroup selection (uniform branch)
+        if (slice == 0)
+            topk_one_workgroup<NB, J, VEC>(scores, token, f, k, idx, idx_stride, count, bitmap,
+                                           prefix);
+        return;
+    }
+    int32_t *out = idx + (size_t)token * idx_stride;
+    // this thread's score: certain member?
+    const int j = slice * kWideSlice + t;
+    bool sel = j < f && ((word >> (t & 31)) & 1u);
+    if ((uint32_t)t < nc)
+        cand[t] = my_cand;                            // nc <= kWideMaxCand <= kSelThreads
+    if (t < kWideSlice / 32)
+        keep_bits[t] = 0u;
+    __syncthreads();
+    // rank every candidate; count the kept ones below this slice and mark those inside it
+    uint32_t below = my_slice_cnt;                    // slices < 64 <= kSelThreads
+    for (uint32_t i = t; i < nc; i += kSelThreads) {
+        const uint64_t me = cand[i];
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (uint32_t q = 0; q < nc; ++q)
+            rank += cand[q] > me ? 1u : 0u;
+        if (rank < need) {
+            const int jc = (int)(0xffffffffu - (uint32_t)me);
+            if (jc < slice * kWideSlice)
+                ++below;
+            else if (jc < (slice + 1) * kWideSlice)
+                atomicOr(&keep_bits[(jc - slice * kWideSlice) >> 5], 1u << (jc & 31));
+        }
+    }
+    // block sum of `below` (fixed order: lanes, then waves)
+    uint32_t bsum = below;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        bsum += __shfl_xor(bsum, o, kWave);
+    if (lane == 0)
+        before_part[w] = bsum;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i)
+        before += before_part[i];
+    sel = sel || ((keep_bits[t >> 5] >> (t & 31)) & 1u);
+    uint32_t tot;
+    const uint32_t pos = before + block_exclusive_scan<kSelWaves>(sel ? 1u : 0u, scan_tmp, &tot);
+    if (sel && prefix + pos < (uint32_t)idx_stride)
+        out[prefix + pos] = prefix + j;
+    if (bitmap && t < kWideSlice / 32 && wbase + t < words)
+        bitmap[(size_t)token * words + wbase + t] = my_word | keep_bits[t];
+    if (slice == 0) {
+        for (int i = t; i < prefix; i += kSelThreads)
+            out[i] = i;
+        if (t == 0 && count)
+            count[token] = prefix + k;
+    }
+}
+
 template <int J, bool VEC>
 __global__ __launch_bounds__(kSelThreads) void k_select_threshold(
     const float *__restrict__ scores, int f, float tau, int32_t *__restrict__ idx, int idx_stride,
@@ -368,9 +609,73 @@ hipError_t threshold_j(const float *scores, int B, int f, float tau, int32_t *id
                   tau, idx, idx_stride, count, bitmap, prefix);
 }
 
+template <int J>
+hipError_t wide_j(const float *scores, int B, int f, int k, int32_t *idx, int idx_stride,
+                  int32_t *count, uint32_t *bitmap, uint32_t *ws, int ws_stride, hipStream_t st,
+                  Trace *tr, int prefix)
+{
+    const dim3 grid((f + kWideSlice - 1) / kWideSlice, B);
+    const bool vec = f % 4 == 0;
+    hipError_t e = vec ? launch(k_wide_hist<kScoreBuckets, true>, grid, dim3(256), st, tr, scores,
+                                f, ws, ws_stride)
+                       : launch(k_wide_hist<kScoreBuckets, false>, grid, dim3(256), st, tr,
+                                scores, f, ws, ws_stride);
+    if (e != hipSuccess)
+        return e;
+    e = vec ? launch(k_wide_classify<kScoreBuckets, true>, grid, dim3(256), st, tr, scores, f, k,
+                     ws, ws_stride)
+            : launch(k_wide_classify<kScoreBuckets, false>, grid, dim3(256), st, tr, scores, f, k,
+                     ws, ws_stride);
+    if (e != hipSuccess)
+        return e;
+    if (vec)
+        return launch(k_wide_emit<kScoreBuckets, J, true>, grid, dim3(kSelThreads), st, tr, scores,
+                      f, k, static_cast<const uint32_t *>(ws), ws_stride, idx, idx_stride, count,
+                      bitmap, prefix);
+    return launch(k_wide_emit<kScoreBuckets, J, false>, grid, dim3(kSelThreads), st, tr, scores,
+                  f, k, static_cast<const uint32_t *>(ws), ws_stride, idx, idx_stride, count,
+                  bitmap, prefix);
+}
+
+__global__ __launch_bounds__(256) void k_wide_zero(uint32_t *__restrict__ ws, int ws_stride, int n)
+{
+    uint32_t *W = ws + (size_t)blockIdx.x * ws_stride;
+    for (int i = threadIdx.x; i < n; i += 256)
+        W[i] = 0u;
+}
+
 }  // namespace
 
 int select_max_f() { return 32 * kMaxWords; }
+
+// measured: the three-kernel form pays off from about 20000 scores (at 14336 both take the same
+// time, at 49152 the layer is 3 us faster)
+bool select_wide_used(int B, int f, int k) { return B >= 1 && B <= 4 && f >= 20000 && k > 0; }
+
+int select_wide_ws_words(int f) { return (kWsWords + (f + 31) / 32 + 63) / 64 * 64; }
+
+int select_wide_zero_words() { return kWsNcand + 1; }
+
+hipError_t launch_select_topk_wide(const float *scores, int B, int f, int k, int32_t *idx,
+                                   int idx_stride, int32_t *count, uint32_t *bitmap, uint32_t *ws,
+                                   bool zeroed, hipStream_t st, Trace *tr, int prefix)
+{
+    const int stride = select_wide_ws_words(f);
+    if (!zeroed) {
+        hipError_t e = launch(k_wide_zero, dim3(B), dim3(256), st, nullptr, ws, stride,
+                              select_wide_zero_words());
+        if (e != hipSuccess)
+            return e;
+    }
+    const int J = (f + kQuad - 1) / kQuad;
+    if (J <= 1) return wide_j<1>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    if (J <= 2) return wide_j<2>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    if (J <= 4) return wide_j<4>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    if (J <= 8) return wide_j<8>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    if (J <= 12) return wide_j<12>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    if (J <= 16) return wide_j<16>(scores, B, f, k, idx, idx_stride, count, bitmap, ws, stride, st, tr, prefix);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_select_topk(const float *scores, int B, int f, int k, int32_t *idx,
                               int idx_stride, int32_t *count, uint32_t *bitmap, hipStream_t st,

@@ -157,7 +157,9 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
  *   idx     [B][k]       int32     out: ascending active list per token
  *   count   [B]          int32     out, optional (NULL): set to k
  *   bitmap  [B][(f+31)/32] uint32  out, optional (NULL): bit j%32 of word j/32 set iff j selected
- * Workspace: none (pass NULL, 0).
+ * Workspace: csf_workspace_size(CSF_OP_SELECT_TOPK, B, 1, f, 0, k, dtype) bytes; it is non-zero
+ * when a few tokens have many scores (then the selection of a token runs over many workgroups,
+ * with the same result) and 0 otherwise (pass NULL, 0).
  * ------------------------------------------------------------------------------------------- */
 int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
                     uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream);
