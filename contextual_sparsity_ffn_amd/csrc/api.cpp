@@ -126,14 +126,21 @@ PredictWs predict_ws(int B, int r)
     return w;
 }
 
-// the predictor for B tokens: matrix cores for batches of 16-bit weights, else vector ALU
+// the predictor for B tokens: matrix cores for batches of 16-bit weights, else vector ALU.
+// zero (optional): nzero words the vector-ALU path clears on the way (*zeroed tells whether it
+// did), for a later kernel of the same call.
 hipError_t enqueue_predict(int dtype, const void *x, int B, int d, const void *V, int r,
                            const void *U, int f, float *scores, float *ws, hipStream_t st,
-                           csf::Trace *tr)
+                           csf::Trace *tr, uint32_t *zero = nullptr, int nzero = 0,
+                           bool *zeroed = nullptr)
 {
+    if (zeroed)
+        *zeroed = false;
     if (csf::pred_mfma_supported(dtype, B, d, r))
         return csf::launch_predict_mfma(dtype, x, B, d, V, r, U, f, scores, ws, st, tr);
-    hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, ws, st, tr);
+    if (zeroed)
+        *zeroed = zero != nullptr;
+    hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, ws, st, tr, zero, nzero);
     if (e != hipSuccess)
         return e;
     return csf::launch_pred_up(dtype, ws, B, d, r, U, f, scores, st, tr);
@@ -214,7 +221,7 @@ BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int d
 }
 
 struct StackWs {
-    size_t xhat[2], a_main, s_main, a_side, s_side, idx[2], count[2], ffn, total;
+    size_t xhat[2], a_main, s_main, a_side, s_side, sel_main, sel_side, idx[2], count[2], ffn, total;
 };
 StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
 {
@@ -236,6 +243,11 @@ StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
     o += pa;
     w.s_side = o;
     o += ps;
+    const size_t psel = round_up(Bn * csf::select_wide_ws_words(f) * sizeof(uint32_t));
+    w.sel_main = o;
+    o += psel;
+    w.sel_side = o;
+    o += psel;
     for (int i = 0; i < 2; ++i) {
         w.idx[i] = o;
         o += round_up(Bn * mc * sizeof(int32_t));
@@ -443,10 +455,18 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
     auto predict_select = [&](int l, const void *xh, hipStream_t q, bool on_side) -> int {
         float *a = reinterpret_cast<float *>(at(ws, on_side ? w.a_side : w.a_main));
         float *sc = reinterpret_cast<float *>(at(ws, on_side ? w.s_side : w.s_main));
+        const bool wide = k >= 0 && csf::select_wide_used(B, f, k);
+        uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, on_side ? w.sel_side : w.sel_main));
+        bool zeroed = false;
+        // the clear covers token 0's counter block: only a single token can skip the clear kernel
         hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
-                                       nullptr);
+                                       nullptr, wide && B == 1 ? selws : nullptr,
+                                       wide && B == 1 ? csf::select_wide_zero_words() : 0, &zeroed);
         if (e == hipSuccess) {
-            if (k >= 0)
+            if (wide)
+                e = csf::launch_select_topk_wide(sc, B, f, k, sel_idx(l), stride, sel_count(l),
+                                                 nullptr, selws, zeroed, q);
+            else if (k >= 0)
                 e = csf::launch_select_topk(sc, B, f, k, sel_idx(l), stride, sel_count(l), nullptr, q);
             else
                 e = csf::launch_select_threshold(sc, B, f, tau, sel_idx(l), stride, sel_count(l),
@@ -1000,12 +1020,18 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     const int stride = max_count > 0 ? max_count : 1;
 
     // the predictor scores the cold rows only; the list is the hot block, then the selection
-    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp);
+    const bool wide = k_cold >= 0 && csf::select_wide_used(1, fc, k_cold);
+    uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, w.sel));
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
+                                         wide ? csf::select_wide_zero_words() : 0);
     if (e == hipSuccess)
         e = csf::launch_pred_up(dtype, a, 1, d, r, U_cold, fc, sc, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "predictor launch");
-    if (k_cold >= 0)
+    if (wide)
+        e = csf::launch_select_topk_wide(sc, 1, fc, k_cold, ix, stride, cn, nullptr, selws, true, st,
+                                         trp, hot);
+    else if (k_cold >= 0)
         e = csf::launch_select_topk(sc, 1, fc, k_cold, ix, stride, cn, nullptr, st, trp, hot);
     else
         e = csf::launch_select_threshold(sc, 1, fc, tau, ix, stride, cn, nullptr, st, trp, hot);
