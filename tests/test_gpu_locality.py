@@ -49,10 +49,11 @@ def test_firing_frequency_matches_oracle_signs():
     assert np.all(np.diff(f_sorted) <= 0)
 
 
-@pytest.mark.parametrize("mode", ["topk", "threshold"])
-def test_hot_layer_parity(mode):
-    announce(f"locality hot layer {mode}")
-    cfg = wl.CONFIGS[3].scaled(1024, 3000, 128)
+# f = 24576 leaves more than 20000 cold scores: the selection runs over many workgroups
+@pytest.mark.parametrize("mode,f", [("topk", 3000), ("threshold", 3000), ("topk", 24576)])
+def test_hot_layer_parity(mode, f):
+    announce(f"locality hot layer {mode} f={f}")
+    cfg = wl.CONFIGS[3].scaled(1024, f, 128)
     L, P, freq, order, H = _prepared(cfg)
     hot = locality.hot_count(freq, 0.5, cap=cfg.k // 2)
     assert 0 < hot < cfg.f
@@ -81,9 +82,10 @@ def test_hot_layer_parity(mode):
         assert_ffn_close(y, y_ref, cfg.dtype, f"hot layer {mode} token {t}")
 
 
-def test_hot_block_of_zero_is_the_plain_layer():
-    announce("locality hot = 0")
-    cfg = wl.CONFIGS[3].scaled(1024, 2000, 128)
+@pytest.mark.parametrize("f", [2000, 24576])
+def test_hot_block_of_zero_is_the_plain_layer(f):
+    announce(f"locality hot = 0, f={f}")
+    cfg = wl.CONFIGS[3].scaled(1024, f, 128)
     L = wl.make_powerlaw_layer(cfg, device=DEV)
     x = wl.make_tokens(cfg, 1, device=DEV)[0]
     y0 = csf.sparse_ffn_layer(x, L.V, L.U, L.W1, L.b1, None, L.W2T, k=cfg.k)
