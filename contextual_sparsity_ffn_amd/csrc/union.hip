@@ -18,7 +18,8 @@
 //     k_union_up_valu    rows of the union in registers, one dot product per token; h in float32;
 //     k_union_down_valu  d-slices x union chunks x token groups, B accumulators per column;
 //   matrix-core path (MFMA 16x16x32, tokens padded to 16 or 32 as M):
-//     k_union_up_mfma    tile of 16 union rows: M = tokens, N = rows, K = d split over 4 waves;
+//     k_union_up_lds     32 union rows x all tokens per workgroup: row and token segments staged
+//                        through LDS (whole 128-byte lines per load), M = tokens, N = rows;
 //                        h stored as a hi/lo pair of 16-bit values (hi = round(h),
 //                        lo = round(h - hi)), so the down product keeps about 22 bits of h;
 //     k_union_down_mfma  tile of 256 output columns x a chunk of the union: the rows of W2T are
@@ -39,6 +40,7 @@ constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 byte
                                      // rows 8 apart fall 16 banks apart)
 constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
 constexpr int kMaxDownSteps = 64;    // K steps (of 32 union rows) per matrix-core down chunk
+constexpr int kUpRows = 32;          // union rows per LDS-staged up-projection workgroup
 
 // Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
 template <int MX, bool GATED>
@@ -277,118 +279,148 @@ __global__ __launch_bounds__(256) void k_union_down_valu(const u32x4 *__restrict
 // One 16x16x32 MFMA: lane l holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
 // e < 8, and receives D[4 (l / 16) + i][l % 16], i < 4.  A = tokens x K, B = K x union rows.
 //
-// Up projection: a workgroup takes 16 NT union rows (the NT row tiles of a wave share each token
-// operand); its 4 waves take consecutive quarters of the K steps and are summed in wave order
-// through LDS.  Each wave keeps P K steps of loads in flight in a ring of registers and refills a
-// slot as soon as its MFMAs are issued.  Loads past the wave's last step or past the union re-read
-// a valid address and are zeroed, so the loop has no branches and its wait counts stay exact.
-template <class T, int MT, int NT, bool GATED, int P>
-__global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__ X,
-                                                       const u32x4 *__restrict__ W1,
-                                                       const u32x4 *__restrict__ Wup,
-                                                       const float *__restrict__ b1,
-                                                       const int32_t *__restrict__ ulist,
-                                                       const int32_t *__restrict__ ucount,
-                                                       const uint32_t *__restrict__ bitmaps,
-                                                       int per_token, int B, int f, int C,
-                                                       uint16_t *__restrict__ hhi,
-                                                       uint16_t *__restrict__ hlo, int hs,
-                                                       int silu)
+// Up projection through LDS.  A workgroup takes 32 union rows (two 16-row tiles) and all B tokens
+// over the whole of d, in segments of ST elements: per segment the 256 threads stage the
+// segment of every weight row (and, gated, of every up row) and of every token row in LDS -- each
+// wavefront load reads whole row segments, whole 128-byte lines -- with the loads of the
+// next PD - 1 segments in flight in a register ring.  The waves then take (gate or up, row tile,
+// token tile) pairs: four or more pairs give each wave its own (no reduction); two pairs split
+// each segment's K steps over two waves each, summed in a fixed order in the epilogue.
+template <class T, int MT, int NV, int PD, int ST>
+__global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ X,
+                                                      const u32x4 *__restrict__ W1,
+                                                      const u32x4 *__restrict__ Wup,
+                                                      const float *__restrict__ b1,
+                                                      const int32_t *__restrict__ ulist,
+                                                      const int32_t *__restrict__ ucount,
+                                                      const uint32_t *__restrict__ bitmaps,
+                                                      int per_token, int B, int f, int C,
+                                                      uint16_t *__restrict__ hhi,
+                                                      uint16_t *__restrict__ hlo, int hs,
+                                                      int silu)
 {
-    constexpr int NV = GATED ? 2 : 1;
-    constexpr int ROWS = 16 * NT;
-    __shared__ float red[4][NV * NT][MT * 4][kWave];
+    constexpr int WR = NV * kUpRows;             // staged weight rows
+    constexpr int SR = WR + 16 * MT;             // staged rows: weight rows, then token rows
+    constexpr int SEGC = ST / 8;                 // 16-byte chunks of a row segment
+    constexpr int RPP = 256 / SEGC;              // rows staged per pass of the workgroup
+    constexpr int LPT = SR / RPP;                // staged chunks per thread
+    constexpr int WPT = WR / RPP;                // ... of which weight rows
+    constexpr int TPR = kUpRows / RPP;           // chunks per thread per weight matrix
+    constexpr int STRIDE = ST + 8;               // staged row stride (16-bit elements)
+    constexpr int PAIRS = NV * 2 * MT;           // (gate/up, row tile, token tile) products
+    constexpr int KSPLIT = PAIRS >= 4 ? 1 : 4 / PAIRS;
+    constexpr int PPW = PAIRS >= 4 ? PAIRS / 4 : 1;
+    constexpr int SPW = ST / kKStep / KSPLIT;    // K steps per wave per segment
+    static_assert(SR % RPP == 0 && kUpRows % RPP == 0 && 256 % SEGC == 0 && SPW >= 1,
+                  "staging covers whole rows");
+    __shared__ __align__(16) uint16_t seg[2][SR][STRIDE];
+    __shared__ float red[KSPLIT][PAIRS][4][kWave];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int ln = lane & 15, g = lane >> 4;
     const int u = union_size(ucount, f);
     const int upad = (u + kKStep - 1) / kKStep * kKStep;   // h is written (zeros) up to here
     const int words = (f + 31) / 32;
-    const int steps = C / 4;                     // K steps of 32 elements (C = 16-byte chunks)
-    const int s0 = w * steps / 4, s1 = (w + 1) * steps / 4;
-    const int groups = (s1 - s0 + P - 1) / P;
+    const int nseg = C / SEGC;
+    const int srow = t / SEGC, scol = t % SEGC;   // thread t stages rows srow + 8 i, chunk scol
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
-    const u32x4 *xr[MT];
-    bool xok[MT];
+    // this wave's products: pair pi = (v, q, m) with v = pi / (2 MT), q = (pi / MT) % 2, m = pi % MT
+    const int kp = PAIRS >= 4 ? 0 : w / PAIRS;
+    int pv[PPW], pq[PPW], pm[PPW], pidx[PPW];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int tok = 16 * m + ln;
-        xok[m] = tok < B;
-        xr[m] = X + (size_t)(xok[m] ? tok : 0) * C;
+    for (int j = 0; j < PPW; ++j) {
+        const int pi = PAIRS >= 4 ? w + 4 * j : w % PAIRS;
+        pidx[j] = pi;
+        pv[j] = pi / (2 * MT);
+        pq[j] = (pi / MT) % 2;
+        pm[j] = pi % MT;
+    }
+    // token rows staged by this thread (chunks WPT .. LPT - 1); tokens past B stage zeros
+    const u32x4 *src[LPT];
+    bool tok_ok[LPT];
+#pragma unroll
+    for (int i = WPT; i < LPT; ++i) {
+        const int tok = srow + RPP * (i - WPT);
+        tok_ok[i] = tok < B;
+        src[i] = X + (size_t)(tok < B ? tok : 0) * C + scol;
     }
 
-    for (int n0 = blockIdx.x * ROWS; n0 < upad; n0 += gridDim.x * ROWS) {
-        // this lane's row of each tile; a row past the union reads the tile's first row, zeroed
-        const int jclamp = ulist[n0 < u ? n0 : u - 1];
-        const u32x4 *wr[NV][NT];
+    for (int n0 = blockIdx.x * kUpRows; n0 < upad; n0 += gridDim.x * kUpRows) {
+        // weight rows staged by this thread: matrix i / TPR, tile row srow + RPP (i % TPR); a
+        // row past the union re-reads the union's last row (its D columns are discarded)
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-            const int n = n0 + 16 * q + ln;
-            const size_t rb = (size_t)(n < u ? ulist[n] : jclamp) * C;
-            wr[0][q] = W1 + rb;
-            if constexpr (GATED)
-                wr[NV - 1][q] = Wup + rb;
+        for (int i = 0; i < WPT; ++i) {
+            const int n = n0 + srow + RPP * (i % TPR);
+            const size_t rb = (size_t)ulist[n < u ? n : u - 1] * C + scol;
+            src[i] = (i / TPR == 0 ? W1 : Wup) + rb;
+            tok_ok[i] = true;
         }
-        f32x4 acc[NV][NT][MT];
+        f32x4 acc[PPW];
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-            for (int q = 0; q < NT; ++q)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[v][q][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < PPW; ++j)
+            acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-        // The ring holds raw loads; nothing reads a slot until its MFMAs, so the P steps stay in
-        // flight.  A row past the union only fills D columns the epilogue discards; a step past
-        // the wave's range (a clamped re-read) is cancelled by zeroing its token operand at use.
-        u32x4 rw[P][NV][NT], rx[P][MT];
-        auto fill = [&](int p, int st) {
-            const int c = 4 * (st < s1 ? st : s1 - 1) + g;
+        u32x4 ring[PD][LPT];
+        auto fill = [&](int p, int sg) {         // a segment past the end re-reads the last one
+            const int c = (sg < nseg ? sg : nseg - 1) * SEGC;
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int q = 0; q < NT; ++q)
-                    rw[p][v][q] = ld_stream(wr[v][q] + c);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                rx[p][m] = xr[m][c];
+            for (int i = 0; i < LPT; ++i)
+                ring[p][i] = i < WPT ? ld_stream(src[i] + c) : src[i][c];
         };
+        auto stage = [&](int p, int buf) {
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-            fill(p, s0 + p);
+            for (int i = 0; i < LPT; ++i)
+                *reinterpret_cast<u32x4 *>(&seg[buf][srow + RPP * i][8 * scol]) =
+                    tok_ok[i] ? ring[p][i] : zero;
+        };
+        auto compute = [&](int buf) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                const int k0 = kKStep * (kp * SPW + s) + 8 * g;
+#pragma unroll
+                for (int j = 0; j < PPW; ++j) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(&seg[buf][WR + 16 * pm[j] + ln][k0]);
+                    const u32x4 b = *reinterpret_cast<const u32x4 *>(
+                        &seg[buf][kUpRows * pv[j] + 16 * pq[j] + ln][k0]);
+                    acc[j] = T::mfma(a, b, acc[j]);
+                }
+            }
+        };
+
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            fill(p, p);
+        stage(0, 0);
+        __syncthreads();
+        const int groups = (nseg + PD - 1) / PD;
         for (int gi = 0; gi < groups; ++gi) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const bool ok = s0 + gi * P + p < s1;
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const u32x4 a = (ok && xok[m]) ? rx[p][m] : zero;
-#pragma unroll
-                    for (int v = 0; v < NV; ++v)
-#pragma unroll
-                        for (int q = 0; q < NT; ++q)
-                            acc[v][q][m] = T::mfma(a, rw[p][v][q], acc[v][q][m]);
+            for (int p = 0; p < PD; ++p) {
+                const int i = gi * PD + p;
+                if (i < nseg) {                      // uniform across the workgroup
+                    // slot p (segment i) is already in LDS: refill it with segment i + PD
+                    fill(p, i + PD);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(i & 1);
+                    if (i + 1 < nseg)
+                        stage((p + 1) % PD, (i + 1) & 1);
+                    __syncthreads();
                 }
-                fill(p, s0 + (gi + 1) * P + p);
             }
         }
 
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
+        for (int j = 0; j < PPW; ++j)
 #pragma unroll
-            for (int q = 0; q < NT; ++q)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        red[w][v * NT + q][m * 4 + i][lane] = acc[v][q][m][i];
+            for (int i = 0; i < 4; ++i)
+                red[kp][pidx[j]][i][lane] = acc[j][i];
         __syncthreads();
-        // thread e covers D element (tile q, m, i, lane): token 16 m + 4 (lane / 16) + i, row
-        // n0 + 16 q + lane % 16
-        for (int e = t; e < NT * MT * 4 * kWave; e += 256) {
+        // element e: tile q, token tile m, D index i, lane l -> token 16 m + 4 (l / 16) + i,
+        // row n0 + 16 q + l % 16
+        for (int e = t; e < 2 * MT * 4 * kWave; e += 256) {
             const int q = e / (MT * 4 * kWave);
-            const int mi = (e / kWave) % (MT * 4), l = e % kWave;
-            const int m = mi / 4, i = mi % 4;
+            const int m = (e / (4 * kWave)) % MT;
+            const int i = (e / kWave) % 4, l = e % kWave;
             const int tok = 16 * m + 4 * (l >> 4) + i;
             const int nn = n0 + 16 * q + (l & 15);
             if (tok >= B || nn >= upad)
@@ -396,13 +428,21 @@ __global__ __launch_bounds__(256) void k_union_up_mfma(const u32x4 *__restrict__
             float hv = 0.0f;
             if (nn < u) {
                 const int jj = ulist[nn];
-                float p = (red[0][q][mi][l] + red[1][q][mi][l]) + (red[2][q][mi][l] + red[3][q][mi][l]);
+                const int p0 = q * MT + m;
+                float p = red[0][p0][i][l];
+#pragma unroll
+                for (int k = 1; k < KSPLIT; ++k)
+                    p += red[k][p0][i][l];
                 if (b1)
                     p += b1[jj];
                 hv = gate_act(p, silu);
-                if constexpr (GATED) {
-                    const int qv = NT + q;
-                    hv *= (red[0][qv][mi][l] + red[1][qv][mi][l]) + (red[2][qv][mi][l] + red[3][qv][mi][l]);
+                if constexpr (NV == 2) {
+                    const int p1 = 2 * MT + q * MT + m;
+                    float uv = red[0][p1][i][l];
+#pragma unroll
+                    for (int k = 1; k < KSPLIT; ++k)
+                        uv += red[k][p1][i][l];
+                    hv *= uv;
                 }
                 if (per_token && !token_has(bitmaps, words, tok, jj))
                     hv = 0.0f;
@@ -603,24 +643,20 @@ hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
     return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.Y, st, tr);
 }
 
-template <class T, int MT, int NT>
+template <class T, int MT, int ST>
 hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / 8;
-    constexpr int ROWS = 16 * NT;
-    const int tiles = (a.f + kKStep - 1) / kKStep * kKStep / ROWS;
+    const int tiles = (a.f + kUpRows - 1) / kUpRows;
     const int blocks = tiles < 4096 ? tiles : 4096;
     hipError_t e;
     if (act_gated(a.act))
-        e = launch(k_union_up_mfma<T, MT, 1, true, 4>, dim3((a.f + kKStep - 1) / kKStep * 2 < 4096
-                                                               ? (a.f + kKStep - 1) / kKStep * 2
-                                                               : 4096),
-                   dim3(256), st, tr, static_cast<const u32x4 *>(a.X),
-                   static_cast<const u32x4 *>(a.W1), static_cast<const u32x4 *>(a.Wup), a.b1,
-                   a.ulist, a.ucount, a.bitmaps, a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs,
-                   act_silu(a.act));
+        e = launch(k_union_up_lds<T, MT, 2, 3, ST>, dim3(blocks), dim3(256), st, tr,
+                   static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
+                   static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
+                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
     else
-        e = launch(k_union_up_mfma<T, MT, NT, false, 4>, dim3(blocks), dim3(256), st, tr,
+        e = launch(k_union_up_lds<T, MT, 1, 3, ST>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
                    a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
@@ -638,12 +674,14 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
 template <class T>
 hipError_t union_mfma(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
-    // two row tiles per wave share each token operand once the union is large (B >= 8)
+    // staged segment length (measured): 512-byte segments for one token tile of few tokens,
+    // 256-byte ones (less LDS and fewer registers per workgroup, so two workgroups per CU)
+    // from 8 tokens on
     if (a.B <= 7)
-        return union_mfma_mt<T, 1, 1>(a, st, tr);
+        return union_mfma_mt<T, 1, 256>(a, st, tr);
     if (a.B <= 16)
-        return union_mfma_mt<T, 1, 2>(a, st, tr);
-    return union_mfma_mt<T, 2, 2>(a, st, tr);
+        return union_mfma_mt<T, 1, 128>(a, st, tr);
+    return union_mfma_mt<T, 2, 128>(a, st, tr);
 }
 
 }  // namespace

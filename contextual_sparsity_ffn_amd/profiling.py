@@ -38,7 +38,7 @@ LABELS = [("k_pred_down", "pred_down"), ("k_pred_up", "pred_up"), ("k_select_top
           ("k_pred_down_mfma", "pred_down_mfma"), ("k_pred_hidden", "pred_hidden"),
           ("k_pred_up_mfma", "pred_up_mfma"), ("k_union_list", "union_list"),
           ("k_union_up_valu", "union_up_valu"), ("k_union_down_valu", "union_down_valu"),
-          ("k_union_up_mfma", "union_up_mfma"), ("k_union_down_mfma", "union_down_mfma"),
+          ("k_union_up_lds", "union_up_mfma"), ("k_union_down_mfma", "union_down_mfma"),
           ("k_rms_norm", "rms_norm"), ("k_head_proj", "head_proj"), ("k_head_attn", "head_attn"),
           ("k_head_combine", "head_combine"), ("k_wide_hist", "select_hist"),
           ("k_wide_classify", "select_classify"), ("k_wide_emit", "select_emit"),
