@@ -34,9 +34,12 @@ KERNELS = ["pred_down", "pred_up", "select_hist", "select_classify", "select_emi
 
 def layer_kernels(f, k):
     """Kernels of csf_sparse_ffn_layer for one token: top-k over 20000 or more scores runs as
-    three kernels (histogram, classify, emit), a smaller one as one."""
+    three kernels (histogram, classify, emit), a smaller one as one, and up to 1024 scores are
+    selected inside the predictor's up-projection kernel."""
     if k is not None and k > 0 and f >= 20000:
         return KERNELS
+    if f <= 1024:     # scores and selection in one kernel
+        return ["pred_down", "pred_up_select", "gather_up", "gather_down", "reduce_partials"]
     return ["pred_down", "pred_up", "select_topk" if k is not None else "select_threshold",
             "gather_up", "gather_down", "reduce_partials"]
 
@@ -650,7 +653,7 @@ def silu_functional_leg(args, dev):
     return res
 
 
-ATTN_KERNELS = ["pred_down", "pred_up", "select_topk", "head_proj", "head_attn", "head_combine",
+ATTN_KERNELS = ["pred_down", "pred_up_select", "head_proj", "head_attn", "head_combine",
                 "gather_down", "reduce_partials"]
 
 
@@ -726,7 +729,7 @@ def attention_leg(args, dev):
     us_sparse = timed(sparse_step)
     us_dense = timed(dense_step)
 
-    # per-kernel times of the sparse layer (its eight kernels)
+    # per-kernel times of the sparse layer (its seven kernels)
     reset()
     n = 40
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(16)] for _ in range(n)]

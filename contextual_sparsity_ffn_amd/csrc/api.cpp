@@ -1106,19 +1106,22 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
                                          wide ? csf::select_wide_zero_words() : 0);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
-    e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
+    if (f <= csf::kSmallF) {
+        // few neurons: the scores and their selection in one kernel
+        e = csf::launch_pred_up_select(dtype, a, d, r, U, f, sc, k, tau, ix, cn, st, trp);
+    } else {
+        e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
+        if (e == hipSuccess && wide)
+            e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn,
+                                             nullptr, selws, true, st, trp);
+        else if (e == hipSuccess && k >= 0)
+            e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr,
+                                        st, trp);
+        else if (e == hipSuccess)
+            e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st, trp);
+    }
     if (e != hipSuccess)
-        return hip_status(e, "predictor up-projection launch");
-    if (wide)
-        e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr,
-                                         selws, true, st, trp);
-    else if (k >= 0)
-        e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr, st,
-                                    trp);
-    else
-        e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st, trp);
-    if (e != hipSuccess)
-        return hip_status(e, "selection launch");
+        return hip_status(e, "predictor / selection launch");
 
     FfnWs fw = ffn_ws(1, d, dtype, max_count);
     csf::FfnArgs fa;
@@ -1317,16 +1320,26 @@ int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int d
     float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
     int32_t *hd = heads_out ? heads_out : reinterpret_cast<int32_t *>(at(ws, w.heads));
     int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
-    hipError_t e = enqueue_predict(dtype, x, 1, d, Vp, r, Up, H, sc, a, st, trp);
-    if (e != hipSuccess)
-        return hip_status(e, "head predictor launch");
-    if (k >= 0)
-        e = csf::launch_select_topk(sc, 1, H, k, hd, max_heads > 0 ? max_heads : 1, cn, nullptr, st,
-                                    trp);
-    else
-        e = csf::launch_select_threshold(sc, 1, H, tau, hd, H, cn, nullptr, st, trp);
-    if (e != hipSuccess)
-        return hip_status(e, "head selection launch");
+    hipError_t e;
+    if (H <= csf::kSmallF) {
+        // the usual case: the head scores and their selection in one kernel
+        e = csf::launch_pred_down(dtype, x, 1, d, Vp, r, a, st, trp);
+        if (e == hipSuccess)
+            e = csf::launch_pred_up_select(dtype, a, d, r, Up, H, sc, k, tau, hd, cn, st, trp);
+        if (e != hipSuccess)
+            return hip_status(e, "head predictor launch");
+    } else {
+        e = enqueue_predict(dtype, x, 1, d, Vp, r, Up, H, sc, a, st, trp);
+        if (e != hipSuccess)
+            return hip_status(e, "head predictor launch");
+        if (k >= 0)
+            e = csf::launch_select_topk(sc, 1, H, k, hd, max_heads > 0 ? max_heads : 1, cn, nullptr,
+                                        st, trp);
+        else
+            e = csf::launch_select_threshold(sc, 1, H, tau, hd, H, cn, nullptr, st, trp);
+        if (e != hipSuccess)
+            return hip_status(e, "head selection launch");
+    }
     return enqueue_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len, hd,
                              cn, max_heads, kv_all, o, y, ws, w, st, trp);
 }

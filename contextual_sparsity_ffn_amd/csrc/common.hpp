@@ -138,6 +138,21 @@ __device__ __forceinline__ float gate_act(float p, int silu)
     return silu ? p / (1.0f + expf(-p)) : (p > 0.0f ? p : 0.0f);
 }
 
+// Order of the top-k selection: a monotone 32-bit key of a float32 score (-0.0 ranks as +0.0),
+// and a (score, index) pair as one integer, larger first: score descending, index ascending.
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if ((u & 0x7fffffffu) == 0u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, int j)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
+}
+
 // Sum over the 64 lanes of a wavefront; every lane receives the total.  The butterfly order is
 // fixed, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v)

@@ -51,6 +51,13 @@ int pred_split(int r, int d, int dtype);
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
                             float *part, hipStream_t stream, Trace *trace = nullptr,
                             uint32_t *zero = nullptr, int nzero = 0);
+// One token with at most kSmallF scores: s[f] = sigmoid(U relu(sum of the partials)) and, in the
+// same kernel, the selection: top-k (k >= 0) or s >= tau (k == -1) into the ascending list idx
+// and count (k, or the threshold count).  The lists equal those of the selection kernels.
+constexpr int kSmallF = 1024;
+hipError_t launch_pred_up_select(int dtype, const float *part, int d, int r, const void *U, int f,
+                                 float *s, int k, float tau, int32_t *idx, int32_t *count,
+                                 hipStream_t stream, Trace *trace = nullptr);
 // s[B][f] = sigmoid(U relu(sum of the partials)) in float32.
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
                           float *s, hipStream_t stream, Trace *trace = nullptr);

@@ -144,6 +144,111 @@ __global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
     }
 }
 
+// Scores and selection of one token with few scores (f <= kSmallF), in one 1024-thread
+// workgroup: the up projection as in k_pred_up (LPR lanes per row of U, rows in passes of 16
+// waves), each score kept in LDS as well as written out; then the selection on the LDS copy --
+// top-k: a score's rank is the number of (score, index) pairs ordered before it (the order of the
+// one-workgroup bucket select, so the lists are the same), threshold: s >= tau -- and a block
+// scan of the selected flags writes the ascending list.  Saves the launch of a separate selection
+// kernel, which dominates when f is a few hundred (attention heads).
+template <class T, int LPR, int MM>
+__global__ __launch_bounds__(1024) void k_pred_up_select(const u32x4 *__restrict__ U,
+                                                         const float *__restrict__ a, int C, int r,
+                                                         int f, int S, float *__restrict__ s,
+                                                         int k, float tau,
+                                                         int32_t *__restrict__ idx,
+                                                         int32_t *__restrict__ count)
+{
+    constexpr int G = kWave / LPR;
+    constexpr int E = T::E;
+    __shared__ float ss[kSmallF];
+    __shared__ uint64_t key[kSmallF];
+    __shared__ uint32_t scan_tmp[16];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int g = lane / LPR, li = lane % LPR;
+    // hidden activation a = relu(sum of the S split-K partial sums, in order)
+    float av[MM][E];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            av[m][e] = 0.0f;
+    for (int sp = 0; sp < S; ++sp) {
+        const float *at = a + (size_t)sp * r;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int c = li + LPR * m;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                float4 v = c < C ? *reinterpret_cast<const float4 *>(at + c * E + e)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                av[m][e] += v.x; av[m][e + 1] += v.y; av[m][e + 2] += v.z; av[m][e + 3] += v.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            av[m][e] = av[m][e] > 0.0f ? av[m][e] : 0.0f;
+    // rows in groups of four passes of the 16 waves, every load of a group issued first
+    constexpr int NP = 4;
+    for (int row0 = 0; row0 < f; row0 += NP * 16 * G) {
+        u32x4 wv[NP][MM];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int j = row0 + q * 16 * G + w * G + g;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int c = li + LPR * m;
+                wv[q][m] = (j < f && c < C) ? ld_stream(U + (size_t)j * C + c)
+                                            : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int j = row0 + q * 16 * G + w * G + g;
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                float wf[E];
+                T::unpack(wv[q][m], wf);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc = fmaf(wf[e], av[m][e], acc);
+            }
+            acc = group_sum<LPR>(acc);
+            if (li == 0 && j < f) {
+                const float sc = 1.0f / (1.0f + expf(-acc));
+                s[j] = sc;
+                ss[j] = sc;
+            }
+        }
+    }
+    __syncthreads();
+    bool sel = false;
+    if (k >= 0) {
+        if (t < f)
+            key[t] = composite(order_key(ss[t]), t);
+        __syncthreads();
+        if (t < f) {
+            const uint64_t me = key[t];
+            int rank = 0;
+            for (int i = 0; i < f; ++i)
+                rank += key[i] > me ? 1 : 0;
+            sel = rank < k;
+        }
+    } else {
+        sel = t < f && ss[t] >= tau;
+    }
+    uint32_t total;
+    const uint32_t pos = block_exclusive_scan<16>(sel ? 1u : 0u, scan_tmp, &total);
+    if (sel)
+        idx[pos] = t;
+    if (t == 0 && count)
+        *count = k >= 0 ? k : (int32_t)total;
+}
+
 struct DownArgs {
     const void *x;
     int B, C;
@@ -219,7 +324,45 @@ hipError_t up_t(const float *a, int B, int S, int r, int C, const void *U, int f
     return hipErrorInvalidValue;
 }
 
+template <class T>
+hipError_t up_select_t(const float *a, int S, int r, int C, const void *U, int f, float *s, int k,
+                       float tau, int32_t *idx, int32_t *count, hipStream_t st, Trace *tr)
+{
+    const u32x4 *u = static_cast<const u32x4 *>(U);
+    if (C <= 16)
+        return launch(k_pred_up_select<T, 16, 1>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    if (C <= 32)
+        return launch(k_pred_up_select<T, 32, 1>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    if (C <= 64)
+        return launch(k_pred_up_select<T, 64, 1>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    if (C <= 128)
+        return launch(k_pred_up_select<T, 64, 2>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    if (C <= 256)
+        return launch(k_pred_up_select<T, 64, 4>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    if (C <= 512)
+        return launch(k_pred_up_select<T, 64, 8>, dim3(1), dim3(1024), st, tr, u, a, C, r, f, S, s,
+                      k, tau, idx, count);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_pred_up_select(int dtype, const float *a, int d, int r, const void *U, int f,
+                                 float *s, int k, float tau, int32_t *idx, int32_t *count,
+                                 hipStream_t st, Trace *tr)
+{
+    if (f < 1 || f > kSmallF)
+        return hipErrorInvalidValue;
+    const int S = pred_split(r, d, dtype);
+    if (dtype == 0) return up_select_t<F32T>(a, S, r, r / 4, U, f, s, k, tau, idx, count, st, tr);
+    if (dtype == 1) return up_select_t<F16T>(a, S, r, r / 8, U, f, s, k, tau, idx, count, st, tr);
+    return up_select_t<BF16T>(a, S, r, r / 8, U, f, s, k, tau, idx, count, st, tr);
+}
 
 int pred_split(int r, int d, int dtype)
 {

@@ -34,19 +34,6 @@ constexpr int kQuad = 4 * kSelThreads;     // scores per sweep: four consecutive
 constexpr int kMaxWords = 2048;            // bitmap words held in LDS: f <= 65536
 constexpr int kMaxDirect = 512;            // candidates ranked by direct counting
 
-__device__ __forceinline__ uint32_t order_key(float s)
-{
-    uint32_t u = __float_as_uint(s);
-    if ((u & 0x7fffffffu) == 0u)
-        u = 0u;                                   // -0.0 ranks as +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Rank of a (score, index) pair as one integer: larger ranks first (score desc, index asc).
-__device__ __forceinline__ uint64_t composite(uint32_t key, int j)
-{
-    return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
-}
 
 // Four consecutive scores j0..j0+3 of one row; positions past f read as NaN.  VEC: the row is
 // 16-byte aligned (f % 4 == 0), so a full quad is one 16-byte load.

@@ -256,6 +256,9 @@ LAYER_CASES = [
     ("c0", wl.CONFIGS[0], 6),
     ("f16-ragged-topk", wl.CONFIGS[1].scaled(2600, 3001, 136), 3),
     ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(4096, 1433, 256), 3),
+    # up to 1024 neurons: scores and selection in one kernel
+    ("bf16-reglu-small-threshold", wl.CONFIGS[2].scaled(1024, 700, 128), 3),
+    ("f16-small-topk-ragged", wl.CONFIGS[1].scaled(1000, 997, 72), 3),
 ]
 
 
@@ -294,6 +297,25 @@ def test_layer_end_to_end(name, cfg, ntok):
     for t in range(ntok):
         announce(f"layer {name} token {t}")
         _check_layer_token(Ld, o, X[t], cfg.k, cfg.tau if cfg.k is None else None, f"{name}/{t}")
+
+
+@pytest.mark.parametrize("f", [1024, 3000])
+def test_layer_selection_ties_go_to_the_lower_index(f):
+    """Predictor up rows in identical pairs give identical scores: the selection (inside the
+    predictor kernel for f <= 1024, the selection kernel above) must break the ties at the
+    boundary by the lower neuron index, as the oracle does."""
+    announce(f"layer ties f={f}")
+    cfg = wl.CONFIGS[0].scaled(256, f, 64, k=f // 10 + 1)
+    L = _layer(cfg)
+    U = L.U.clone()
+    U[1::2] = U[0::2][: U[1::2].shape[0]]
+    L = wl.Layer(cfg, L.V, U, L.W1, L.b1, L.Wup, L.W2T)
+    Ld = _to_dev_layer(L)
+    o = layer_to_orc(L)
+    X = wl.make_tokens(cfg, 3)
+    for t in range(3):
+        ix = _check_layer_token(Ld, o, X[t], cfg.k, None, f"ties f={f} token {t}")
+        assert len(ix) == cfg.k
 
 
 def test_layer_full_size_opt175b_shape():
