@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the HBM bandwidth probe (context for the metric)")
     ap.add_argument("--batched-steps", type=int, default=256,
                     help="steps per (batch size, path) of the OPT-30B-shape batched leg (0: skip)")
     ap.add_argument("--batched-layers", type=int, default=4)
@@ -151,6 +153,21 @@ def main():
     value = touched / (ms_per_step * 1e-3) / 1e9
     log(f"{us_layer:.2f} us/layer, {value:.1f} GB/s on touched bytes (wall {wall:.3f}s, "
         f"host enqueue {enqueue / args.steps * 1e6:.1f} us/step)")
+
+    # ---- per-step distribution: each of 256 steps bracketed by its own events ---------------
+    nd = min(256, len(plan))
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nd)]
+    for s_i in range(nd):
+        sev[s_i][0].record(stream)
+        rc = fn(*plan[(args.warmup + args.steps + s_i) % len(plan)])
+        if rc:
+            raise csf.CsfError(rc, _lib.lib.csf_last_error().decode())
+        sev[s_i][1].record(stream)
+    torch.cuda.synchronize()
+    st_us = sorted(a.elapsed_time(b) * 1e3 for a, b in sev)
+    step_dist = {"steps": nd, "p10_us": round(st_us[nd // 10], 3), "median_us": round(st_us[nd // 2], 3),
+                 "p90_us": round(st_us[(9 * nd) // 10], 3)}
 
     # ---- per-kernel times from the library's trace hook (a separate pass) -------------------
     log(f"timing each kernel over {args.trace_steps} steps")
@@ -289,6 +306,8 @@ def main():
         torch.cuda.empty_cache()
         stack = stack_leg(args, dev)
 
+    probe = None if args.no_probe else bandwidth_probe(dev)
+
     # ---- CPU oracle baseline (rank 0, bounded sample) ----------------------------------------
     cpu = None
     if not args.no_cpu:
@@ -314,6 +333,9 @@ def main():
                    "weights": "float16, float32 accumulation", "layers_rotated": args.layers,
                    "tokens": args.tokens, "parallelism": "single GPU"},
         "us_per_layer": round(us_layer, 3),
+        "us_per_step_distribution": step_dist,
+        "bandwidth_probe": probe,
+        "frac_of_dense_stream": round(value / (dense_b / (dense_us * 1e-6) / 1e9), 4) if dense_us else None,
         "host_enqueue_us_per_step": round(enqueue / args.steps * 1e6, 2),
         "tokens_per_s_per_layer": round(1e6 / us_layer, 1),
         "touched_bytes": touched,
@@ -1109,10 +1131,46 @@ def cpu_baseline(cfg, L, X, ntok, touched):
         orc.sparse_ffn(x, W1, b1, None, W2T, sel, orc.RELU, orc.F16)
     dt = time.perf_counter() - t0
     gbs = touched * ntok / dt / 1e9
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "us_per_layer": round(dt / ntok * 1e6, 1),
+            "host_cores_available": len(os.sched_getaffinity(0)), "host_cpu": model,
             "sample": f"{ntok} tokens of one layer of the same shape (predict + top-k + sparse FFN), "
                       f"single-threaded C oracle with double accumulation, {dt:.1f} s"}
+
+
+def bandwidth_probe(dev):
+    """HBM bandwidth of a plain 1 GiB device copy with PyTorch's own kernel (best of 5), for
+    context.  The library's dense FFN, a pure streaming read of W1 and W2T (1.2 GB), is the
+    read-side reference (dense_GBps)."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.float16, device=dev)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    t_copy = best(lambda: b.copy_(a))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * n / t_copy / 1e9, 1), "bytes_copied": n,
+            "how": "torch copy_ of 1 GiB (read + write counted)"}
 
 
 if __name__ == "__main__":
