@@ -177,7 +177,7 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
 
 // Batches of at least this many tokens take the matrix-core path when it applies (the gather
 // path's vector ALU work grows with B per weight byte; the matrix cores' does not bind).
-constexpr int kMfmaMinBatch = 4;
+constexpr int kMfmaMinBatch = 2;   // measured: from two tokens on the matrix-core path is faster
 
 struct UnionWs {
     size_t ulist, ucount, h, hlo, partials, total;

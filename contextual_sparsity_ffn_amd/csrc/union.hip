@@ -722,6 +722,30 @@ hipError_t launch_union_ffn(const UnionArgs &a, hipStream_t st, Trace *tr)
         if (a.dtype == 1) return union_mfma<F16T>(a, st, tr);
         return union_mfma<BF16T>(a, st, tr);
     }
+    if (a.B == 1) {
+        // one token: the union is its own list, so the single-token gathered FFN applies as it
+        // is (rows whole per workgroup, the list staged in LDS for the down projection)
+        FfnArgs fa;
+        fa.dtype = a.dtype;
+        fa.act = a.act;
+        fa.x = a.X;
+        fa.B = 1;
+        fa.d = a.d;
+        fa.f = a.f;
+        fa.W1 = a.W1;
+        fa.Wup = a.Wup;
+        fa.W2T = a.W2T;
+        fa.b1 = a.b1;
+        fa.idx = a.ulist;
+        fa.idx_stride = a.f;
+        fa.count = a.ucount;
+        fa.max_count = a.f;
+        fa.h = a.h32;
+        fa.h_stride = a.hs;
+        fa.y = a.Y;
+        fa.partials = a.partials;
+        return launch_ffn(fa, st, tr);
+    }
     if (a.dtype == 0) return union_valu<F32T>(a, st, tr);
     if (a.dtype == 1) return union_valu<F16T>(a, st, tr);
     return union_valu<BF16T>(a, st, tr);
