@@ -28,14 +28,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-FFN µs/layer + HBM GB/s on touched bytes, batch 1, OPT-175B shape @5%"
 PEAK_HBM_GBS = 8000.0
-KERNELS = ["pred_down", "pred_up", "select_hist", "select_classify", "select_emit", "gather_up",
+KERNELS = ["pred_down", "pred_up", "select_hist", "select_finish", "gather_up",
            "gather_down", "reduce_partials"]
 
 
 def layer_kernels(f, k):
     """Kernels of csf_sparse_ffn_layer for one token: top-k over 20000 or more scores runs as
-    three kernels (histogram, classify, emit), a smaller one as one, and up to 1024 scores are
-    selected inside the predictor's up-projection kernel."""
+    two kernels (histogram, then classify, rank and emit), a smaller one as one, and up to 1024
+    scores are selected inside the predictor's up-projection kernel."""
     if k is not None and k > 0 and f >= 20000:
         return KERNELS
     if f <= 1024:     # scores and selection in one kernel
@@ -194,8 +194,7 @@ def main():
         "pred_down": r * d * es + d * es + r * 4,
         "pred_up": f * r * es + r * 4 + f * 4,
         "select_hist": f * 4,
-        "select_classify": f * 4 + f // 8,
-        "select_emit": f // 8 + k * 4,
+        "select_finish": f * 4 + k * 4,
         "gather_up": k * d * es + d * es + k * 4 + k * 4,
         "gather_down": k * d * es + k * 8,
         "reduce_partials": 0,

@@ -312,91 +312,140 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
 // The same bucket select as topk_one_workgroup, spread over slices of kWideSlice scores so that
 // the work of one token runs on many compute units (a single workgroup retires about 64 lane
 // operations per cycle, so its passes over 49152 scores cost microseconds each):
-//   k_wide_hist      one workgroup per slice: LDS histogram of the slice, then one global atomic
-//                    add per non-empty bucket into the token's histogram (zeroed by the launch
-//                    before; integer adds, so the order does not matter);
-//   k_wide_classify  one workgroup per slice: every workgroup scans the finished histogram and
-//                    finds the same boundary bucket B* and `need`; the slice's certain members
-//                    (bucket above B*) go to the global bitmap words of the slice and their count
-//                    to slice_cnt; B*'s members are appended to a candidate list (capacity
-//                    kWideMaxCand; the count keeps growing past it);
-//   k_wide_emit      one 1024-thread workgroup per slice, thread t owning score t of the slice:
-//                    every workgroup ranks all candidates by (score desc, index asc) and keeps
-//                    the first `need`; a slice's output offset is the certain count of the
-//                    earlier slices plus the kept candidates below the slice; a block scan
-//                    places the slice's indices (ascending).  If the candidates overflowed,
-//                    workgroup 0 runs topk_one_workgroup instead (heavy ties) and the others exit.
-// Everything is integer arithmetic on the same bucket map and order keys, so the list equals
-// the one-workgroup result bit for bit.
+//   k_wide_hist      one workgroup per slice: LDS histogram of the slice, added into the token's
+//                    histogram with one global atomic per non-empty bucket (zeroed by the launch
+//                    before; integer adds, so the order does not matter); the slice is also
+//                    counting-sorted by bucket, top bucket first: above[b] (members in buckets
+//                    above b) and the members' (order key, index) composites in that order;
+//   k_wide_finish    one 1024-thread workgroup per slice, thread t owning score t of the slice:
+//                    every workgroup scans the finished histogram and finds the same boundary
+//                    bucket B* and `need`; two words of each slice's above[] give the slice's
+//                    certain members (bucket above B*) and the place of its B* members, which
+//                    are gathered from the sorted composites into LDS and ranked by (score desc,
+//                    index asc); the first `need` are kept.  The slice's output offset is the
+//                    certain members of the earlier slices plus the kept candidates below the
+//                    slice; a block scan places the slice's indices (ascending).  With more than
+//                    kWideMaxCand candidates (heavy ties) workgroup 0 runs topk_one_workgroup
+//                    instead and the others exit.
+// A score's own membership is tested on the score itself: with uniform buckets over [0, 1] and an
+// exact power-of-two scale, bucket(v) > B* exactly when v >= (B*+1)/NB.  Everything else is
+// integer arithmetic on the same bucket map and order keys, so the list equals the one-workgroup
+// result bit for bit.
 constexpr int kWideSlice = 1024;
 constexpr int kWideMaxCand = 512;
-constexpr int kWideMaxSlices = 64;
+// Workspace of one token (32-bit words): the histogram [NB], then per slice above[NB + 1]
+// (above[b + 1] for b = -1 .. NB-1), one pad word and the sorted composites [kWideSlice] (64-bit).
+constexpr int kWideAbove = kScoreBuckets + 2;
+constexpr int kWideSliceWords = kWideAbove + 2 * kWideSlice;
+
+__device__ __forceinline__ uint32_t *wide_slice(uint32_t *W, int slice)
+{
+    return W + kScoreBuckets + (size_t)slice * kWideSliceWords;
+}
 
 template <int NB, bool VEC>
 __global__ __launch_bounds__(256) void k_wide_hist(const float *__restrict__ scores, int f,
                                                    uint32_t *__restrict__ ws, int ws_stride)
 {
+    static_assert(NB == kScoreBuckets && NB % 256 == 0, "workspace layout");
+    constexpr int BPT = NB / 256;
     __shared__ uint32_t hist[NB];
+    __shared__ uint32_t start[NB];
+    __shared__ uint32_t scan_tmp[4];
     const int t = threadIdx.x;
-    const int token = blockIdx.y;
+    const int token = blockIdx.y, slice = blockIdx.x;
     const float *s = scores + (size_t)token * f;
-    uint32_t *ghist = ws + (size_t)token * ws_stride;
-    const int j0 = blockIdx.x * kWideSlice + 4 * t;
+    uint32_t *W = ws + (size_t)token * ws_stride;
+    uint32_t *above = wide_slice(W, slice);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(above + kWideAbove);
+    const int j0 = slice * kWideSlice + 4 * t;
     const float4 q = load_quad<VEC>(s, j0, f);
     for (int b = t; b < NB; b += 256)
         hist[b] = 0u;
     __syncthreads();
     const float e[4] = {q.x, q.y, q.z, q.w};
+    int bk[4];
+    uint32_t rk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bk[i] = e[i] == e[i] ? score_bucket<NB>(e[i]) : -1;     // NaN: past f
+        rk[i] = bk[i] >= 0 ? atomicAdd(&hist[bk[i]], 1u) : 0u;  // place inside the bucket
+    }
+    __syncthreads();
+    // thread t owns buckets NB-1-(BPT*t+i), top first; the scan gives the members above each
+    uint32_t c[BPT];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        c[i] = hist[NB - 1 - (BPT * t + i)];
+        sum += c[i];
+    }
+    uint32_t valid;
+    uint32_t run = block_exclusive_scan<4>(sum, scan_tmp, &valid);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        start[NB - 1 - (BPT * t + i)] = run;            // members above the bucket
+        run += c[i];
+    }
+    __syncthreads();
+    // global traffic with consecutive lanes on consecutive words
+    for (int b = t; b < NB; b += 256) {
+        above[b + 1] = start[b];
+        const uint32_t n = hist[b];
+        if (n)
+            atomicAdd(&W[b], n);
+    }
+    if (t == 0)
+        above[0] = valid;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (e[i] == e[i])
-            atomicAdd(&hist[score_bucket<NB>(e[i])], 1u);
-    __syncthreads();
-    for (int b = t; b < NB; b += 256) {
-        const uint32_t c = hist[b];
-        if (c)
-            atomicAdd(&ghist[b], c);
-    }
+        if (bk[i] >= 0)
+            keys[start[bk[i]] + rk[i]] = composite(order_key(e[i]), j0 + i);
 }
 
-// Workspace of one token (32-bit words): histogram [NB], candidate count, B*, need, slice
-// counts [kWideMaxSlices], candidates [kWideMaxCand] (64-bit), bitmap words [f / 32].
-constexpr int kWsNcand = kScoreBuckets, kWsBstar = kWsNcand + 1, kWsNeed = kWsNcand + 2;
-constexpr int kWsSliceCnt = kScoreBuckets + 64;
-constexpr int kWsCand = kWsSliceCnt + kWideMaxSlices;          // 64-bit aligned (even)
-constexpr int kWsWords = kWsCand + 2 * kWideMaxCand;
-
-template <int NB, bool VEC>
-__global__ __launch_bounds__(256) void k_wide_classify(const float *__restrict__ scores, int f,
-                                                       int k, uint32_t *__restrict__ ws,
-                                                       int ws_stride)
+template <int NB, int J, bool VEC>
+__global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__restrict__ scores,
+                                                             int f, int k,
+                                                             const uint32_t *__restrict__ ws,
+                                                             int ws_stride,
+                                                             int32_t *__restrict__ idx,
+                                                             int idx_stride,
+                                                             int32_t *__restrict__ count,
+                                                             uint32_t *__restrict__ bitmap,
+                                                             int prefix)
 {
-    __shared__ uint32_t scan_tmp[4];
-    __shared__ uint32_t misc[3];
-    __shared__ uint32_t red[4];
+    static_assert(NB % kSelThreads == 0, "whole buckets per thread");
+    constexpr int BPT = NB / kSelThreads;
+    __shared__ uint64_t cand[kWideMaxCand];
+    __shared__ uint32_t keep_bits[kWideSlice / 32];
+    __shared__ uint32_t scan_tmp[kSelWaves];
+    __shared__ uint32_t soff[kSelThreads];    // first candidate of each slice
+    __shared__ uint32_t sbeg[kSelThreads];    // its place among the slice's sorted composites
+    __shared__ uint32_t misc[3];              // B*, need, members of B*
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int token = blockIdx.y, slice = blockIdx.x;
+    const int nslices = (f + kWideSlice - 1) / kWideSlice;
     const float *s = scores + (size_t)token * f;
-    uint32_t *W = ws + (size_t)token * ws_stride;
-    const int j0 = slice * kWideSlice + 4 * t;
-    const float4 q = load_quad<VEC>(s, j0, f);
-
-    // B* and need from the finished histogram: thread t owns buckets NB-1-BPT*t-q (top first)
-    constexpr int BPT = NB / 256;
+    const uint32_t *W = ws + (size_t)token * ws_stride;
+    const int lim = slice * kWideSlice;
+    const int j = lim + t;
+    const float mine = j < f ? s[j] : __builtin_nanf("");
+    uint32_t c[BPT];
+    uint32_t csum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        c[i] = W[NB - 1 - (BPT * t + i)];
+        csum += c[i];
+    }
     if (t == 0) {
         misc[0] = 0u;
         misc[1] = 0u;
         misc[2] = 0u;
     }
-    uint32_t c[BPT];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        c[i] = W[NB - 1 - (BPT * t + i)];
-        mine += c[i];
-    }
+    if (t < kWideSlice / 32)
+        keep_bits[t] = 0u;
     uint32_t total;
-    uint32_t above = block_exclusive_scan<4>(mine, scan_tmp, &total);
+    uint32_t above = block_exclusive_scan<kSelWaves>(csum, scan_tmp, &total);
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
         if (above < (uint32_t)k && above + c[i] >= (uint32_t)k) {
@@ -408,129 +457,83 @@ __global__ __launch_bounds__(256) void k_wide_classify(const float *__restrict__
     }
     __syncthreads();
     const int bstar = (int)misc[0];
-    // more candidates than the list holds (heavy ties): record the count, skip the appends
-    const bool overflow = misc[2] > (uint32_t)kWideMaxCand;
-    if (slice == 0 && t == 0) {
-        W[kWsBstar] = misc[0];
-        W[kWsNeed] = misc[1];
-        if (overflow)
-            W[kWsNcand] = misc[2];
-    }
-
-    // certain members into the slice's bitmap words, candidates into the global list
-    const float e[4] = {q.x, q.y, q.z, q.w};
-    uint32_t nib = 0u;
-    uint64_t *cand = reinterpret_cast<uint64_t *>(W + kWsCand);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = e[i] == e[i] ? score_bucket<NB>(e[i]) : -1;
-        nib |= (b > bstar ? 1u : 0u) << i;
-        if (b == bstar && !overflow) {
-            const uint32_t p = atomicAdd(&W[kWsNcand], 1u);
-            if (p < (uint32_t)kWideMaxCand)
-                cand[p] = composite(order_key(e[i]), j0 + i);
-        }
-    }
-    uint32_t x = nib << (4 * (lane & 7));
-    x |= __shfl_xor(x, 1, kWave);
-    x |= __shfl_xor(x, 2, kWave);
-    x |= __shfl_xor(x, 4, kWave);
-    const int words = (f + 31) / 32;
-    const int widx = slice * (kWideSlice / 32) + (t >> 3);
-    if ((lane & 7) == 0 && widx < words)
-        W[kWsWords + widx] = x;
-    uint32_t n = (uint32_t)__popc(nib);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        n += __shfl_xor(n, o, kWave);
-    if (lane == 0)
-        red[w] = n;
-    __syncthreads();
-    if (t == 0)
-        W[kWsSliceCnt + slice] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-template <int NB, int J, bool VEC>
-__global__ __launch_bounds__(kSelThreads) void k_wide_emit(const float *__restrict__ scores,
-                                                           int f, int k,
-                                                           const uint32_t *__restrict__ ws,
-                                                           int ws_stride,
-                                                           int32_t *__restrict__ idx,
-                                                           int idx_stride,
-                                                           int32_t *__restrict__ count,
-                                                           uint32_t *__restrict__ bitmap,
-                                                           int prefix)
-{
-    __shared__ uint64_t cand[kWideMaxCand];
-    __shared__ uint32_t keep_bits[kWideSlice / 32];
-    __shared__ uint32_t before_part[kSelWaves];
-    __shared__ uint32_t scan_tmp[kSelWaves];
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int token = blockIdx.y, slice = blockIdx.x;
-    const uint32_t *W = ws + (size_t)token * ws_stride;
-    const uint64_t *gc = reinterpret_cast<const uint64_t *>(W + kWsCand);
-    // every load of the kernel is issued up front: the candidate slots are read whether or not
-    // they were filled (the workspace holds all of them), the count decides which are used
-    const uint32_t nc = W[kWsNcand];
-    const uint32_t need = W[kWsNeed];
-    const uint64_t my_cand = t < kWideMaxCand ? gc[t] : 0ull;
-    const uint32_t my_slice_cnt = t < slice ? W[kWsSliceCnt + t] : 0u;
-    const int words = (f + 31) / 32;
-    const int wbase = slice * (kWideSlice / 32);
-    const uint32_t word = (wbase + (t >> 5)) < words ? W[kWsWords + wbase + (t >> 5)] : 0u;
-    const uint32_t my_word = (t < kWideSlice / 32 && wbase + t < words) ? W[kWsWords + wbase + t]
-                                                                        : 0u;
-    if (nc > (uint32_t)kWideMaxCand) {
+    const uint32_t need = misc[1];
+    if (misc[2] > (uint32_t)kWideMaxCand) {
         // heavy ties in the boundary bucket: the one-workgroup selection (uniform branch)
         if (slice == 0)
             topk_one_workgroup<NB, J, VEC>(scores, token, f, k, idx, idx_stride, count, bitmap,
                                            prefix);
         return;
     }
-    int32_t *out = idx + (size_t)token * idx_stride;
-    // this thread's score: certain member?
-    const int j = slice * kWideSlice + t;
-    bool sel = j < f && ((word >> (t & 31)) & 1u);
-    if ((uint32_t)t < nc)
-        cand[t] = my_cand;                            // nc <= kWideMaxCand <= kSelThreads
-    if (t < kWideSlice / 32)
-        keep_bits[t] = 0u;
+    // slice t: members above B* (certain) and B*'s members, from its above[] words
+    uint32_t sab = 0, scnt = 0;
+    if (t < nslices) {
+        const uint32_t *ab = wide_slice(const_cast<uint32_t *>(W), t);
+        sab = ab[bstar + 1];
+        scnt = ab[bstar] - sab;
+    }
+    uint32_t nc;
+    const uint32_t off = block_exclusive_scan<kSelWaves>(scnt, scan_tmp, &nc);
+    soff[t] = off;
+    sbeg[t] = sab;
+    uint32_t before = t < slice ? sab : 0u;
     __syncthreads();
-    // rank every candidate; count the kept ones below this slice and mark those inside it
-    uint32_t below = my_slice_cnt;                    // slices < 64 <= kSelThreads
-    for (uint32_t i = t; i < nc; i += kSelThreads) {
-        const uint64_t me = cand[i];
+    if (nc > (uint32_t)kWideMaxCand) {
+        // only without a boundary bucket (fewer than k non-NaN scores), when B* = 0 stands in;
+        // the one-workgroup selection decides as above
+        if (slice == 0)
+            topk_one_workgroup<NB, J, VEC>(scores, token, f, k, idx, idx_stride, count, bitmap,
+                                           prefix);
+        return;
+    }
+    if ((uint32_t)t < nc) {
+        // candidate t lives in the last slice whose first candidate is at or before t
+        int lo = 0, hi = nslices - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (soff[mid] <= (uint32_t)t)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const uint64_t *keys =
+            reinterpret_cast<const uint64_t *>(wide_slice(const_cast<uint32_t *>(W), lo) + kWideAbove);
+        cand[t] = keys[sbeg[lo] + (uint32_t)t - soff[lo]];
+    }
+    __syncthreads();
+    // rank the candidates (at most one per thread); count the kept ones below this slice and mark
+    // those inside it
+    if ((uint32_t)t < nc) {
+        const uint64_t me = cand[t];
         uint32_t rank = 0;
 #pragma unroll 8
-        for (uint32_t q = 0; q < nc; ++q)
-            rank += cand[q] > me ? 1u : 0u;
+        for (uint32_t r = 0; r < nc; ++r)
+            rank += cand[r] > me ? 1u : 0u;
         if (rank < need) {
             const int jc = (int)(0xffffffffu - (uint32_t)me);
-            if (jc < slice * kWideSlice)
-                ++below;
-            else if (jc < (slice + 1) * kWideSlice)
-                atomicOr(&keep_bits[(jc - slice * kWideSlice) >> 5], 1u << (jc & 31));
+            if (jc < lim)
+                ++before;
+            else if (jc < lim + kWideSlice)
+                atomicOr(&keep_bits[(jc - lim) >> 5], 1u << (jc & 31));
         }
     }
-    // block sum of `below` (fixed order: lanes, then waves)
-    uint32_t bsum = below;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        bsum += __shfl_xor(bsum, o, kWave);
-    if (lane == 0)
-        before_part[w] = bsum;
-    __syncthreads();
-    uint32_t before = 0;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i)
-        before += before_part[i];
-    sel = sel || ((keep_bits[t >> 5] >> (t & 31)) & 1u);
+    uint32_t before_all;
+    block_exclusive_scan<kSelWaves>(before, scan_tmp, &before_all);   // also orders keep_bits
+    const float hi_v = bstar == NB - 1 ? __builtin_nanf("") : (float)(bstar + 1) / (float)NB;
+    const bool sel = mine >= hi_v || ((keep_bits[t >> 5] >> (t & 31)) & 1u);
     uint32_t tot;
-    const uint32_t pos = before + block_exclusive_scan<kSelWaves>(sel ? 1u : 0u, scan_tmp, &tot);
+    const uint32_t pos = before_all + block_exclusive_scan<kSelWaves>(sel ? 1u : 0u, scan_tmp, &tot);
+    int32_t *out = idx + (size_t)token * idx_stride;
     if (sel && prefix + pos < (uint32_t)idx_stride)
         out[prefix + pos] = prefix + j;
-    if (bitmap && t < kWideSlice / 32 && wbase + t < words)
-        bitmap[(size_t)token * words + wbase + t] = my_word | keep_bits[t];
+    if (bitmap) {
+        // words lim/32 + 2w and + 2w+1 from the wavefront's 64 bits (positions past f are clear)
+        const int words = (f + 31) / 32;
+        const uint64_t m = __ballot(sel);
+        const int wd = lim / 32 + 2 * w + (lane >> 5);
+        if ((lane & 31) == 0 && wd < words)
+            bitmap[(size_t)token * words + wd] = (uint32_t)(m >> (lane & 32));
+    }
     if (slice == 0) {
         for (int i = t; i < prefix; i += kSelThreads)
             out[i] = i;
@@ -609,17 +612,11 @@ hipError_t wide_j(const float *scores, int B, int f, int k, int32_t *idx, int id
                                 scores, f, ws, ws_stride);
     if (e != hipSuccess)
         return e;
-    e = vec ? launch(k_wide_classify<kScoreBuckets, true>, grid, dim3(256), st, tr, scores, f, k,
-                     ws, ws_stride)
-            : launch(k_wide_classify<kScoreBuckets, false>, grid, dim3(256), st, tr, scores, f, k,
-                     ws, ws_stride);
-    if (e != hipSuccess)
-        return e;
     if (vec)
-        return launch(k_wide_emit<kScoreBuckets, J, true>, grid, dim3(kSelThreads), st, tr, scores,
-                      f, k, static_cast<const uint32_t *>(ws), ws_stride, idx, idx_stride, count,
-                      bitmap, prefix);
-    return launch(k_wide_emit<kScoreBuckets, J, false>, grid, dim3(kSelThreads), st, tr, scores,
+        return launch(k_wide_finish<kScoreBuckets, J, true>, grid, dim3(kSelThreads), st, tr,
+                      scores, f, k, static_cast<const uint32_t *>(ws), ws_stride, idx, idx_stride,
+                      count, bitmap, prefix);
+    return launch(k_wide_finish<kScoreBuckets, J, false>, grid, dim3(kSelThreads), st, tr, scores,
                   f, k, static_cast<const uint32_t *>(ws), ws_stride, idx, idx_stride, count,
                   bitmap, prefix);
 }
@@ -639,9 +636,13 @@ int select_max_f() { return 32 * kMaxWords; }
 // time, at 49152 the layer is 3 us faster)
 bool select_wide_used(int B, int f, int k) { return B >= 1 && B <= 4 && f >= 20000 && k > 0; }
 
-int select_wide_ws_words(int f) { return (kWsWords + (f + 31) / 32 + 63) / 64 * 64; }
+int select_wide_ws_words(int f)
+{
+    const int slices = (f + kWideSlice - 1) / kWideSlice;
+    return (kScoreBuckets + slices * kWideSliceWords + 63) / 64 * 64;
+}
 
-int select_wide_zero_words() { return kWsNcand + 1; }
+int select_wide_zero_words() { return kScoreBuckets; }
 
 hipError_t launch_select_topk_wide(const float *scores, int B, int f, int k, int32_t *idx,
                                    int idx_stride, int32_t *count, uint32_t *bitmap, uint32_t *ws,

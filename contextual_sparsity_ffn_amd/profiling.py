@@ -41,7 +41,7 @@ LABELS = [("k_pred_down", "pred_down"), ("k_pred_up_select", "pred_up_select"), 
           ("k_union_up_lds", "union_up_mfma"), ("k_union_down_mfma", "union_down_mfma"),
           ("k_rms_norm", "rms_norm"), ("k_head_proj", "head_proj"), ("k_head_attn", "head_attn"),
           ("k_head_combine", "head_combine"), ("k_wide_hist", "select_hist"),
-          ("k_wide_classify", "select_classify"), ("k_wide_emit", "select_emit"),
+          ("k_wide_finish", "select_finish"),
           ("k_wide_zero", "select_zero")]
 
 

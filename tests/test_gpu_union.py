@@ -239,7 +239,8 @@ def test_batched_union_full_size_opt30b_shape(B, path):
 @pytest.mark.parametrize("name,cfg,B", [
     ("f16-topk-B6", wl.CONFIGS[3].scaled(768, 2333, 64), 6),
     ("bf16-reglu-threshold-B5", wl.CONFIGS[2].scaled(512, 1433, 64), 5),
-], ids=["f16-topk-B6", "bf16-reglu-threshold-B5"])
+    ("f16-topk-wide-B3", wl.CONFIGS[3].scaled(256, 24576, 64), 3),   # many-workgroup top-k
+], ids=["f16-topk-B6", "bf16-reglu-threshold-B5", "f16-topk-wide-B3"])
 def test_batched_layer_end_to_end(name, cfg, B):
     """Predict + select + union FFN in one call: the selected sets (bitmaps) equal the oracle's
     selection from the library's own scores, and Y matches the oracle over those sets."""
