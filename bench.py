@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--trace-steps", type=int, default=400)
     ap.add_argument("--quality-tokens", type=int, default=32)
     ap.add_argument("--dense-steps", type=int, default=64)
-    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM bandwidth probe (context for the metric)")
