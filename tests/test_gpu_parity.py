@@ -71,7 +71,7 @@ def _score_patterns(f, g):
             "sigmoid": sig}
 
 
-SELECT_F = [1, 7, 1000, 1024, 1025, 3001, 49152, 65536]
+SELECT_F = [1, 7, 1000, 1024, 1025, 3001, 30001, 49152, 65536]
 
 
 @pytest.mark.parametrize("f", SELECT_F)
