@@ -6,12 +6,13 @@
 //
 // Both halves are skinny GEMVs bound by HBM bandwidth (2 flops per weight element read), so they
 // are written as streaming dot-product kernels, not as MFMA tiles:
-//   k_pred_down  S 256-thread workgroups per row of V (split-K); each thread keeps its 16-byte
+//   k_pred_down  S 256-thread workgroups per R rows of V (split-K); each thread keeps its 16-byte
 //                chunks in registers and reuses them for every token; partial sums out.
 //   k_pred_up    groups of LPR lanes per row of U (LPR = 16/32/64 so short rows still use whole
-//                128-byte lines); the prologue adds the split-K partials and applies ReLU, and
-//                the hidden activation a (float32) of the lane's chunk positions sits in
-//                registers; sigmoid in the epilogue.
+//                128-byte lines); the weight loads are issued first, then the workgroup adds
+//                the split-K partials, applies ReLU and stages the hidden activation a (float32)
+//                in LDS once, and each lane takes its chunk positions from there (one read of a
+//                from L2 per workgroup rather than per wavefront); sigmoid in the epilogue.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,74 +20,94 @@ namespace csf {
 
 namespace {
 
-// Split-K down projection: S workgroups per row of V, each over a contiguous 1/S of the row's
-// 16-byte chunks (more, shorter workgroups keep more of HBM busy than one workgroup per row).  The
-// partial sums go to part[S][B][r]; the up-projection kernel adds them in order and applies ReLU.
-template <class T, int MX, int TG>
+// Split-K down projection: S workgroups per R rows of V, each over a contiguous 1/S of the rows'
+// 16-byte chunks (more, shorter workgroups keep more of HBM busy than one workgroup per row); the
+// x chunks a thread loads serve all R rows.  The partial sums go to part[S][B][r]; the
+// up-projection kernel adds them in order and applies ReLU.
+template <class T, int MX, int TG, int R>
 __global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
                                                    const u32x4 *__restrict__ x, int C, int r,
                                                    int B, int S, float *__restrict__ part,
                                                    uint32_t *__restrict__ zero, int nzero)
 {
-    __shared__ float red[4][TG];
+    __shared__ float red[4][R * TG];
     // workgroup 0 also clears a caller's counter block for a later kernel of the same call
     if (zero && blockIdx.x == 0)
         for (int i = threadIdx.x; i < nzero; i += 256)
             zero[i] = 0u;
-    const int i = blockIdx.x / S, sp = blockIdx.x % S;
+    const int i0 = (blockIdx.x / S) * R, sp = blockIdx.x % S;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int cper = (C + S - 1) / S;
     const int c0 = sp * cper;
     const int c1 = c0 + cper < C ? c0 + cper : C;
-    const u32x4 *row = V + (size_t)i * C;
-    u32x4 wv[MX];
+    u32x4 wv[R][MX];
 #pragma unroll
-    for (int m = 0; m < MX; ++m) {
-        const int c = c0 + t + 256 * m;
-        wv[m] = c < c1 ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < R; ++q) {
+        const u32x4 *row = V + (size_t)(i0 + q) * C;
+#pragma unroll
+        for (int m = 0; m < MX; ++m) {
+            const int c = c0 + t + 256 * m;
+            wv[q][m] = (c < c1 && i0 + q < r) ? ld_stream(row + c) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    // tokens in groups of TG (TG = 1 for a single token: one accumulator, one reduction)
+    // tokens in groups of TG (TG = 1 for a single token: one accumulator per row, one reduction)
     for (int t0 = 0; t0 < B; t0 += TG) {
-        float acc[TG];
+        float acc[R][TG];
 #pragma unroll
-        for (int q = 0; q < TG; ++q) {
-            acc[q] = 0.0f;
-            const int tok = t0 + q;
-            if (tok < B) {
-                const u32x4 *xt = x + (size_t)tok * C;
+        for (int p = 0; p < TG; ++p) {
+            const int tok = t0 + p;
+            u32x4 xv[MX];
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const int c = c0 + t + 256 * m;
+                xv[m] = (tok < B && c < c1) ? x[(size_t)tok * C + c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                acc[q][p] = 0.0f;
 #pragma unroll
                 for (int m = 0; m < MX; ++m) {
                     const int c = c0 + t + 256 * m;
-                    if (c < c1)
-                        acc[q] = T::dot(wv[m], xt[c], acc[q]);
+                    if (tok < B && c < c1)
+                        acc[q][p] = T::dot(wv[q][m], xv[m], acc[q][p]);
                 }
             }
         }
 #pragma unroll
-        for (int q = 0; q < TG; ++q)
-            acc[q] = wave_sum(acc[q]);
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+            for (int p = 0; p < TG; ++p)
+                acc[q][p] = wave_sum(acc[q][p]);
         if (lane == 0) {
 #pragma unroll
-            for (int q = 0; q < TG; ++q)
-                red[w][q] = acc[q];
+            for (int q = 0; q < R; ++q)
+#pragma unroll
+                for (int p = 0; p < TG; ++p)
+                    red[w][q * TG + p] = acc[q][p];
         }
         __syncthreads();
-        if (t < TG && t0 + t < B)
-            part[((size_t)sp * B + t0 + t) * r + i] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+        if (t < R * TG) {
+            const int q = t / TG, p = t % TG;
+            if (t0 + p < B && i0 + q < r)
+                part[((size_t)sp * B + t0 + p) * r + i0 + q] =
+                    (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+        }
         __syncthreads();
     }
 }
 
-template <class T, int LPR, int MM, int RW>
-__global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
+template <class T, int LPR, int MM, int RW, int NT = 256>
+__global__ __launch_bounds__(NT) void k_pred_up(const u32x4 *__restrict__ U,
                                                  const float *__restrict__ a, int C, int r, int f,
                                                  int B, int S, float *__restrict__ s)
 {
     constexpr int G = kWave / LPR;   // rows handled side by side by one wavefront
     constexpr int E = T::E;
-    const int lane = threadIdx.x & (kWave - 1);
+    __shared__ float4 sa[kWave * MM * E / 4];   // the token's hidden activation (C * E <= its size)
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
     const int g = lane / LPR, li = lane % LPR;
-    const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int wave = blockIdx.x * (NT / kWave) + t / kWave;
     const int row0 = wave * (RW * G);
     u32x4 wv[RW][MM];
 #pragma unroll
@@ -99,32 +120,35 @@ __global__ __launch_bounds__(256) void k_pred_up(const u32x4 *__restrict__ U,
                                          : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    const int n4 = C * E / 4;
     for (int tok = 0; tok < B; ++tok) {
-        // hidden activation a = relu(sum of the S split-K partial sums, in order)
+        // hidden activation a = relu(sum of the S split-K partial sums, in order), staged once per
+        // workgroup in LDS
+        if (tok > 0)
+            __syncthreads();
+        for (int i = t; i < n4; i += NT) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sp = 0; sp < S; ++sp) {
+                const float4 v = reinterpret_cast<const float4 *>(a + ((size_t)sp * B + tok) * r)[i];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            acc.x = acc.x > 0.0f ? acc.x : 0.0f;
+            acc.y = acc.y > 0.0f ? acc.y : 0.0f;
+            acc.z = acc.z > 0.0f ? acc.z : 0.0f;
+            acc.w = acc.w > 0.0f ? acc.w : 0.0f;
+            sa[i] = acc;
+        }
+        __syncthreads();
         float av[MM][E];
 #pragma unroll
-        for (int m = 0; m < MM; ++m)
+        for (int m = 0; m < MM; ++m) {
+            const int c = li + LPR * m;
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                av[m][e] = 0.0f;
-        for (int sp = 0; sp < S; ++sp) {
-            const float *at = a + ((size_t)sp * B + tok) * r;
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                const int c = li + LPR * m;
-#pragma unroll
-                for (int e = 0; e < E; e += 4) {
-                    float4 v = c < C ? *reinterpret_cast<const float4 *>(at + c * E + e)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-                    av[m][e] += v.x; av[m][e + 1] += v.y; av[m][e + 2] += v.z; av[m][e + 3] += v.w;
-                }
+            for (int e = 0; e < E; e += 4) {
+                const float4 v = c < C ? sa[(c * E + e) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                av[m][e] = v.x; av[m][e + 1] = v.y; av[m][e + 2] = v.z; av[m][e + 3] = v.w;
             }
         }
-#pragma unroll
-        for (int m = 0; m < MM; ++m)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                av[m][e] = av[m][e] > 0.0f ? av[m][e] : 0.0f;
 #pragma unroll
         for (int st = 0; st < RW; ++st) {
             float acc = 0.0f;
@@ -259,15 +283,25 @@ struct DownArgs {
     int nzero;
 };
 
+template <class T, int MX, int R>
+hipError_t down_r(const DownArgs &g, hipStream_t st, Trace *tr)
+{
+    const u32x4 *V = static_cast<const u32x4 *>(g.V), *x = static_cast<const u32x4 *>(g.x);
+    const dim3 grid((g.r + R - 1) / R * g.S);
+    if (g.B == 1)
+        return launch(k_pred_down<T, MX, 1, R>, grid, dim3(256), st, tr, V, x, g.C, g.r, g.B, g.S,
+                      g.a, g.zero, g.nzero);
+    return launch(k_pred_down<T, MX, 8, R>, grid, dim3(256), st, tr, V, x, g.C, g.r, g.B, g.S,
+                  g.a, g.zero, g.nzero);
+}
+
+// Two rows per workgroup halve the re-reads of x when that still leaves >= 512 workgroups.
 template <class T, int MX>
 hipError_t down_mx(const DownArgs &g, hipStream_t st, Trace *tr)
 {
-    const u32x4 *V = static_cast<const u32x4 *>(g.V), *x = static_cast<const u32x4 *>(g.x);
-    if (g.B == 1)
-        return launch(k_pred_down<T, MX, 1>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r,
-                      g.B, g.S, g.a, g.zero, g.nzero);
-    return launch(k_pred_down<T, MX, 8>, dim3(g.r * g.S), dim3(256), st, tr, V, x, g.C, g.r, g.B,
-                  g.S, g.a, g.zero, g.nzero);
+    if (MX <= 8 && (long)g.r * g.S >= 1024)
+        return down_r<T, MX, 2>(g, st, tr);
+    return down_r<T, MX, 1>(g, st, tr);
 }
 
 template <class T>
@@ -289,9 +323,10 @@ hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, 
                      hipStream_t st, Trace *tr)
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
+    constexpr int NT = 256;   // measured: 512-thread workgroups are slower (19.5 against 18.2 us)
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
-    const int blocks = (waves + 3) / 4;
-    return launch(k_pred_up<T, LPR, MM, RW>, dim3(blocks), dim3(256), st, tr,
+    const int blocks = (waves + NT / kWave - 1) / (NT / kWave);
+    return launch(k_pred_up<T, LPR, MM, RW, NT>, dim3(blocks), dim3(NT), st, tr,
                   static_cast<const u32x4 *>(U), a, C, r, f, B, S, s);
 }
 
