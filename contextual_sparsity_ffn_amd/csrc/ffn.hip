@@ -389,11 +389,13 @@ int ffn_num_slices(int d, int dtype)
 
 int ffn_num_chunks(int d, int dtype, int max_count)
 {
-    // about 1536 workgroups per token in the down projection, at least 16 list entries per chunk.
-    // The split depends on neither the batch size nor the data, so a token's summation order
-    // (and its bits) are the same in every batch.
+    // about 768 workgroups per token in the down projection, at least 16 list entries per chunk
+    // (measured at the OPT-175B shape: 768 is 0.5 us faster per layer than 1536, whose partial
+    // rows the reduction then reads twice over; 576 and 384 are slower again).  The split depends
+    // on neither the batch size nor the data, so a token's summation order (and its bits) are the
+    // same in every batch.
     const int slices = ffn_num_slices(d, dtype);
-    int want = (1536 + slices - 1) / slices;
+    int want = (768 + slices - 1) / slices;
     const int cap = max_count / 16;
     if (want > cap)
         want = cap;
