@@ -8,7 +8,8 @@
 // are written as streaming dot-product kernels, not as MFMA tiles:
 //   k_pred_down  S 256-thread workgroups per R rows of V (split-K); each thread keeps its 16-byte
 //                chunks in registers and reuses them for every token; partial sums out.
-//   k_pred_up    groups of LPR lanes per row of U (LPR = 16/32/64 so short rows still use whole
+//   k_pred_up    (batches; k_pred_up_loop is its persistent form for one token)
+//                groups of LPR lanes per row of U (LPR = 16/32/64 so short rows still use whole
 //                128-byte lines); the weight loads are issued first, then the workgroup adds
 //                the split-K partials, applies ReLU and stages the hidden activation a (float32)
 //                in LDS once, and each lane takes its chunk positions from there (one read of a
@@ -168,6 +169,100 @@ __global__ __launch_bounds__(NT) void k_pred_up(const u32x4 *__restrict__ U,
     }
 }
 
+// One token, persistent form of k_pred_up: a grid of about as many workgroups as the GPU holds at
+// once walks the row groups of U (workgroup b takes groups b, b + grid, ...).  The hidden
+// activation is staged once per workgroup and each lane keeps its chunk positions of it in
+// registers; the next group's weight loads are issued before the current group is reduced, so
+// every lane always has a group of loads in flight.  Same lane mapping, sums and rounding as
+// k_pred_up, so the scores are bit-identical.
+template <class T, int LPR, int MM, int RW>
+__global__ __launch_bounds__(256) void k_pred_up_loop(const u32x4 *__restrict__ U,
+                                                      const float *__restrict__ a, int C, int r,
+                                                      int f, int S, float *__restrict__ s)
+{
+    constexpr int G = kWave / LPR;
+    constexpr int E = T::E;
+    constexpr int NW = 4;
+    constexpr int RPG = NW * RW * G;             // rows per workgroup step
+    __shared__ float4 sa[kWave * MM * E / 4];
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1), w = t / kWave;
+    const int g = lane / LPR, li = lane % LPR;
+    const int ngroups = (f + RPG - 1) / RPG;
+    int grp = blockIdx.x;
+    u32x4 wv[RW][MM];
+#pragma unroll
+    for (int st = 0; st < RW; ++st) {
+        const int j = (grp * NW + w) * (RW * G) + st * G + g;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int c = li + LPR * m;
+            wv[st][m] = (j < f && c < C) ? ld_stream(U + (size_t)j * C + c)
+                                         : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const int n4 = C * E / 4;
+    for (int i = t; i < n4; i += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < S; ++sp) {
+            const float4 v = reinterpret_cast<const float4 *>(a + (size_t)sp * r)[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        acc.x = acc.x > 0.0f ? acc.x : 0.0f;
+        acc.y = acc.y > 0.0f ? acc.y : 0.0f;
+        acc.z = acc.z > 0.0f ? acc.z : 0.0f;
+        acc.w = acc.w > 0.0f ? acc.w : 0.0f;
+        sa[i] = acc;
+    }
+    __syncthreads();
+    float av[MM][E];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+        const int c = li + LPR * m;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            const float4 v = c < C ? sa[(c * E + e) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            av[m][e] = v.x; av[m][e + 1] = v.y; av[m][e + 2] = v.z; av[m][e + 3] = v.w;
+        }
+    }
+    while (grp < ngroups) {
+        const int nxt = grp + (int)gridDim.x;
+        u32x4 wn[RW][MM];
+#pragma unroll
+        for (int st = 0; st < RW; ++st) {
+            const int j = (nxt * NW + w) * (RW * G) + st * G + g;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int c = li + LPR * m;
+                wn[st][m] = (nxt < ngroups && j < f && c < C) ? ld_stream(U + (size_t)j * C + c)
+                                                              : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < RW; ++st) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                float wf[E];
+                T::unpack(wv[st][m], wf);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc = fmaf(wf[e], av[m][e], acc);
+            }
+            acc = group_sum<LPR>(acc);
+            const int j = (grp * NW + w) * (RW * G) + st * G + g;
+            if (li == 0 && j < f)
+                s[j] = 1.0f / (1.0f + expf(-acc));
+        }
+#pragma unroll
+        for (int st = 0; st < RW; ++st)
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+                wv[st][m] = wn[st][m];
+        grp = nxt;
+    }
+}
+
 // Scores and selection of one token with few scores (f <= kSmallF), in one 1024-thread
 // workgroup: the up projection as in k_pred_up (LPR lanes per row of U, rows in passes of 16
 // waves), each score kept in LDS as well as written out; then the selection on the LDS copy --
@@ -318,12 +413,31 @@ hipError_t down_t(const DownArgs &g, hipStream_t st, Trace *tr)
     return hipErrorInvalidValue;
 }
 
+// Workgroups of the persistent one-token up projection: 8 of 256 threads per CU on 256 CUs, the
+// most that are resident at once.  Measured at the OPT-175B / OPT-30B / LLaMA-class predictor
+// shapes: 17.4 / 8.1 / 4.2 us against 18.1 / 9.5 / 4.35 us for one short workgroup per 8 rows;
+// 1024 or 512 workgroups, or 2 and 4 rows per lane group, are slower.
+constexpr int kPredUpGrid = 2048;
+
+template <class T, int LPR, int MM, int RW>
+hipError_t up_loop_launch(const float *a, int S, int r, int C, const void *U, int f, float *s,
+                          hipStream_t st, Trace *tr, int grid)
+{
+    constexpr int RPG = 4 * RW * (kWave / LPR);
+    const int ngroups = (f + RPG - 1) / RPG;
+    const int blocks = grid < ngroups ? grid : ngroups;
+    return launch(k_pred_up_loop<T, LPR, MM, RW>, dim3(blocks), dim3(256), st, tr,
+                  static_cast<const u32x4 *>(U), a, C, r, f, S, s);
+}
+
 template <class T, int LPR, int MM, int RW>
 hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
                      hipStream_t st, Trace *tr)
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
     constexpr int NT = 256;   // measured: 512-thread workgroups are slower (19.5 against 18.2 us)
+    if (B == 1)
+        return up_loop_launch<T, LPR, MM, 1>(a, S, r, C, U, f, s, st, tr, kPredUpGrid);
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
     const int blocks = (waves + NT / kWave - 1) / (NT / kWave);
     return launch(k_pred_up<T, LPR, MM, RW, NT>, dim3(blocks), dim3(NT), st, tr,
