@@ -174,6 +174,23 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront, with DPP cross-lane moves (no LDS
+// round trips): inside each 16-lane row, adds of the value 1, 2, 4 and 8 lanes lower (lanes with
+// no such source add 0); then the row totals are carried across rows -- lane 15 of row 0 into row
+// 1 and of row 2 into row 3 (row_bcast:15 with rows 1 and 3 enabled), then lane 31 into rows 2
+// and 3 (row_bcast:31).  Disabled rows take the `old` operand, 0.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
+{
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return (uint32_t)x;
+}
+
 // Exclusive prefix sum over a workgroup of NW wavefronts (blockDim.x == 64 * NW).  `scratch` is
 // LDS of at least NW words; the call contains two barriers and must be reached by every thread.
 template <int NW>
@@ -182,13 +199,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t n = __shfl_up(incl, o, kWave);
-        if (lane >= o)
-            incl += n;
-    }
+    const uint32_t incl = wave_inclusive_scan(v);
     if (lane == kWave - 1)
         scratch[w] = incl;
     __syncthreads();

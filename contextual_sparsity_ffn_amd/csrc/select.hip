@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
     __shared__ uint32_t scan_tmp[kSelWaves];
     __shared__ uint32_t soff[kSelThreads];    // first candidate of each slice
     __shared__ uint32_t sbeg[kSelThreads];    // its place among the slice's sorted composites
-    __shared__ uint32_t misc[3];              // B*, need, members of B*
+    __shared__ uint32_t misc[4];              // B*, need, members of B*, candidates
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int token = blockIdx.y, slice = blockIdx.x;
     const int nslices = (f + kWideSlice - 1) / kWideSlice;
@@ -472,12 +472,17 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
         sab = ab[bstar + 1];
         scnt = ab[bstar] - sab;
     }
-    uint32_t nc;
-    const uint32_t off = block_exclusive_scan<kSelWaves>(scnt, scan_tmp, &nc);
-    soff[t] = off;
-    sbeg[t] = sab;
+    // at most 64 slices (f <= 65536): wavefront 0 places each slice's first candidate
+    if (w == 0) {
+        const uint32_t incl = wave_inclusive_scan(scnt);
+        soff[t] = incl - scnt;
+        sbeg[t] = sab;
+        if (lane == kWave - 1)
+            misc[3] = incl;
+    }
     uint32_t before = t < slice ? sab : 0u;
     __syncthreads();
+    const uint32_t nc = misc[3];
     if (nc > (uint32_t)kWideMaxCand) {
         // only without a boundary bucket (fewer than k non-NaN scores), when B* = 0 stands in;
         // the one-workgroup selection decides as above
@@ -501,28 +506,40 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
         cand[t] = keys[sbeg[lo] + (uint32_t)t - soff[lo]];
     }
     __syncthreads();
-    // rank the candidates (at most one per thread); count the kept ones below this slice and mark
-    // those inside it
-    if ((uint32_t)t < nc) {
-        const uint64_t me = cand[t];
-        uint32_t rank = 0;
-#pragma unroll 8
-        for (uint32_t r = 0; r < nc; ++r)
+    // rank the candidates by (score desc, index asc): L lanes per candidate (a power of two, at
+    // most 64, with nc * L <= 1024) each count the candidates ordered before it in every L-th
+    // place, and the group adds its counts.  Count the kept ones below this slice and mark those
+    // inside it.
+    uint32_t L = kWave;
+    while (L > 1 && nc * L > (uint32_t)kSelThreads)
+        L >>= 1;
+    const uint32_t ci = (uint32_t)t / L, sub = (uint32_t)t % L;
+    uint64_t me = 0;
+    uint32_t rank = 0;
+    if (ci < nc) {
+        me = cand[ci];
+        for (uint32_t r = sub; r < nc; r += L)
             rank += cand[r] > me ? 1u : 0u;
-        if (rank < need) {
-            const int jc = (int)(0xffffffffu - (uint32_t)me);
-            if (jc < lim)
-                ++before;
-            else if (jc < lim + kWideSlice)
-                atomicOr(&keep_bits[(jc - lim) >> 5], 1u << (jc & 31));
-        }
     }
-    uint32_t before_all;
-    block_exclusive_scan<kSelWaves>(before, scan_tmp, &before_all);   // also orders keep_bits
+    for (uint32_t o = 1; o < L; o <<= 1)
+        rank += __shfl_xor(rank, (int)o, kWave);
+    if (ci < nc && sub == 0 && rank < need) {
+        const int jc = (int)(0xffffffffu - (uint32_t)me);
+        if (jc < lim)
+            ++before;
+        else if (jc < lim + kWideSlice)
+            atomicOr(&keep_bits[(jc - lim) >> 5], 1u << (jc & 31));
+    }
+    __syncthreads();
     const float hi_v = bstar == NB - 1 ? __builtin_nanf("") : (float)(bstar + 1) / (float)NB;
     const bool sel = mine >= hi_v || ((keep_bits[t >> 5] >> (t & 31)) & 1u);
+    // one scan for both counts, packed as (before << 11) | sel: the low field's exclusive prefix
+    // (< 1024) is this thread's place among the slice's selected, the high field's block total
+    // the selected neurons of the earlier slices (<= 65536, so the word does not overflow)
     uint32_t tot;
-    const uint32_t pos = before_all + block_exclusive_scan<kSelWaves>(sel ? 1u : 0u, scan_tmp, &tot);
+    const uint32_t ex = block_exclusive_scan<kSelWaves>((before << 11) | (sel ? 1u : 0u), scan_tmp,
+                                                        &tot);
+    const uint32_t pos = (tot >> 11) + (ex & 0x7ffu);
     int32_t *out = idx + (size_t)token * idx_stride;
     if (sel && prefix + pos < (uint32_t)idx_stride)
         out[prefix + pos] = prefix + j;
