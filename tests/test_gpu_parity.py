@@ -67,8 +67,11 @@ def _score_patterns(f, g):
     z = torch.where(torch.rand(f, generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
     sat = torch.where(torch.rand(f, generator=g) < 0.3, torch.tensor(1.0), torch.rand(f, generator=g))
     sig = torch.sigmoid(torch.randn(f, generator=g) * 2.45)
+    # descending ramp: the k largest are the first k indices, so whole slices of a many-workgroup
+    # selection lie above the boundary bucket (more members than any per-slice prefix holds)
+    ramp = torch.linspace(1.0, 0.0, f)
     return {"uniform": u, "ties": q, "all-equal": eq, "signed-zero": z, "saturated": sat,
-            "sigmoid": sig}
+            "sigmoid": sig, "ramp": ramp}
 
 
 SELECT_F = [1, 7, 1000, 1024, 1025, 3001, 30001, 49152, 65536]
