@@ -978,7 +978,10 @@ def batched_union_leg(args, dev):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.batched_steps
             # per-kernel times (runtime-recorded start/end events)
-            names = predictor_kernels(B, code, d, r) + ["select_topk"] + UNION_KERNELS
+            if B == 1 and path == _lib.PATH_GATHER:
+                names = layer_kernels(f, k)      # a batch of one runs the single-token layer
+            else:
+                names = predictor_kernels(B, code, d, r) + ["select_topk"] + UNION_KERNELS
             nev = 2 * len(names)
             nt = min(64, args.batched_steps)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nt)]

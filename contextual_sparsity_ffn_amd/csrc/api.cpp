@@ -217,6 +217,12 @@ BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int d
     w.bitmap = w.count + round_up(Bn * sizeof(int32_t));
     w.uni = w.bitmap + round_up(Bn * ((f + 31) / 32) * sizeof(uint32_t));
     w.total = w.uni + union_ws(B, d, f, dtype).total;
+    if (B == 1) {
+        // a batch of one on the gather path runs the single-token layer in this workspace
+        const size_t one = layer_ws(d, f, r, max_count, dtype).total;
+        if (one > w.total)
+            w.total = one;
+    }
     return w;
 }
 
@@ -648,6 +654,70 @@ int enqueue_attention(const void *x, int d, int H, int dh, int dtype, const void
     return hip_status(csf::launch_attention_decode(a, st, tr), "attention decode launch");
 }
 
+// One token's layer (predict, select, gathered FFN) on validated arguments, in the LayerWs
+// layout of `ws`.  Optional outputs: scores, list, count, bitmap (NULL: kept in the workspace or
+// not written).
+int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const void *V,
+                   const void *U, const void *W1, const float *b1, const void *Wup,
+                   const void *W2T, int k, float tau, float *y, float *scores_out,
+                   int32_t *idx_out, int32_t *count_out, uint32_t *bitmap, void *ws,
+                   const LayerWs &w, int skip_zero, float gate_tau, hipStream_t st,
+                   csf::Trace *trp)
+{
+    const int max_count = k >= 0 ? k : f;
+    float *a = reinterpret_cast<float *>(at(ws, w.a));
+    float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
+    int32_t *ix = idx_out ? idx_out : reinterpret_cast<int32_t *>(at(ws, w.idx));
+    int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
+
+    const bool wide = k >= 0 && csf::select_wide_used(1, f, k);
+    uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, w.sel));
+    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
+                                         wide ? csf::select_wide_zero_words() : 0);
+    if (e != hipSuccess)
+        return hip_status(e, "predictor down-projection launch");
+    if (f <= csf::kSmallF && !bitmap) {
+        // few neurons: the scores and their selection in one kernel
+        e = csf::launch_pred_up_select(dtype, a, d, r, U, f, sc, k, tau, ix, cn, st, trp);
+    } else {
+        e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
+        if (e == hipSuccess && wide)
+            e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn,
+                                             bitmap, selws, true, st, trp);
+        else if (e == hipSuccess && k >= 0)
+            e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, bitmap,
+                                        st, trp);
+        else if (e == hipSuccess)
+            e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, bitmap, st, trp);
+    }
+    if (e != hipSuccess)
+        return hip_status(e, "predictor / selection launch");
+
+    FfnWs fw = ffn_ws(1, d, dtype, max_count);
+    csf::FfnArgs fa;
+    fa.dtype = dtype;
+    fa.act = act;
+    fa.x = x;
+    fa.B = 1;
+    fa.d = d;
+    fa.f = f;
+    fa.W1 = W1;
+    fa.Wup = Wup;
+    fa.W2T = W2T;
+    fa.b1 = b1;
+    fa.idx = ix;
+    fa.idx_stride = max_count > 0 ? max_count : 1;
+    fa.count = k >= 0 ? nullptr : cn;
+    fa.max_count = max_count;
+    fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+    fa.h_stride = max_count > 0 ? max_count : 1;
+    fa.y = y;
+    fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
+    fa.skip_zero = skip_zero;
+    fa.gate_tau = gate_tau;
+    return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -956,6 +1026,18 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
         tr.n = g_trace_n;
     }
     csf::Trace *trp = tr.ev ? &tr : nullptr;
+    if (B == 1 && !mfma) {
+        // One token on the gather path: its union is its own set, so the single-token layer
+        // (selection over many workgroups for large f, the gathered FFN over the token's list)
+        // computes the same thing without the union list.  No post-gate skip, as on the union
+        // path; the count is the union size.
+        s = enqueue_layer1(X, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, Y, nullptr,
+                           nullptr, union_count, bitmaps_out, ws, layer_ws(d, f, r, max_count, dtype),
+                           0, 0.0f, st, trp);
+        if (s == CSF_OK && path_taken)
+            *path_taken = CSF_PATH_GATHER;
+        return s;
+    }
     float *a = reinterpret_cast<float *>(at(ws, w.a));
     float *sc = reinterpret_cast<float *>(at(ws, w.scores));
     int32_t *ix = reinterpret_cast<int32_t *>(at(ws, w.idx));
@@ -1087,65 +1169,15 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     const int max_count = k >= 0 ? k : f;
     LayerWs w = layer_ws(d, f, r, max_count, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     csf::Trace tr;
     if (g_trace_n > 0) {
         tr.ev = g_trace_events;
         tr.n = g_trace_n;
     }
-
-    float *a = reinterpret_cast<float *>(at(ws, w.a));
-    float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
-    int32_t *ix = idx_out ? idx_out : reinterpret_cast<int32_t *>(at(ws, w.idx));
-    int32_t *cn = count_out ? count_out : reinterpret_cast<int32_t *>(at(ws, w.count));
-
-    csf::Trace *trp = tr.ev ? &tr : nullptr;
-    const bool wide = k >= 0 && csf::select_wide_used(1, f, k);
-    uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, w.sel));
-    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
-                                         wide ? csf::select_wide_zero_words() : 0);
-    if (e != hipSuccess)
-        return hip_status(e, "predictor down-projection launch");
-    if (f <= csf::kSmallF) {
-        // few neurons: the scores and their selection in one kernel
-        e = csf::launch_pred_up_select(dtype, a, d, r, U, f, sc, k, tau, ix, cn, st, trp);
-    } else {
-        e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
-        if (e == hipSuccess && wide)
-            e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn,
-                                             nullptr, selws, true, st, trp);
-        else if (e == hipSuccess && k >= 0)
-            e = csf::launch_select_topk(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn, nullptr,
-                                        st, trp);
-        else if (e == hipSuccess)
-            e = csf::launch_select_threshold(sc, 1, f, tau, ix, f, cn, nullptr, st, trp);
-    }
-    if (e != hipSuccess)
-        return hip_status(e, "predictor / selection launch");
-
-    FfnWs fw = ffn_ws(1, d, dtype, max_count);
-    csf::FfnArgs fa;
-    fa.dtype = dtype;
-    fa.act = act;
-    fa.x = x;
-    fa.B = 1;
-    fa.d = d;
-    fa.f = f;
-    fa.W1 = W1;
-    fa.Wup = Wup;
-    fa.W2T = W2T;
-    fa.b1 = b1;
-    fa.idx = ix;
-    fa.idx_stride = max_count > 0 ? max_count : 1;
-    fa.count = k >= 0 ? nullptr : cn;
-    fa.max_count = max_count;
-    fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
-    fa.h_stride = max_count > 0 ? max_count : 1;
-    fa.y = y;
-    fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
-    fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
-    fa.gate_tau = g_gate_tau;
-    return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
+    return enqueue_layer1(x, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, y, scores_out,
+                          idx_out, count_out, nullptr, ws, w,
+                          (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0, g_gate_tau,
+                          static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
 }
 
 int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,

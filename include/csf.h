@@ -297,6 +297,9 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
  *   X [B][d] dtype (1 <= B <= 32), predictor V [r][d] / U [f][r], FFN weights as above.
  *   semantics, path, Y, union_count, path_taken as csf_sparse_ffn_batched_union.
  *   bitmaps_out [B][(f+31)/32] uint32, optional: each token's selected set.
+ * A batch of one on the gather path (CSF_PATH_GATHER, or CSF_PATH_AUTO at B = 1) is the
+ * single-token layer: csf_sparse_ffn_layer's kernels and bits (without the post-gate skip), its
+ * count as the union size.
  * Workspace: csf_workspace_size(CSF_OP_BATCHED_LAYER, B, d, f, r, k >= 0 ? k : f, dtype).
  * ------------------------------------------------------------------------------------------- */
 int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int act, int dtype,

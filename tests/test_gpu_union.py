@@ -240,7 +240,12 @@ def test_batched_union_full_size_opt30b_shape(B, path):
     ("f16-topk-B6", wl.CONFIGS[3].scaled(768, 2333, 64), 6),
     ("bf16-reglu-threshold-B5", wl.CONFIGS[2].scaled(512, 1433, 64), 5),
     ("f16-topk-wide-B3", wl.CONFIGS[3].scaled(256, 24576, 64), 3),   # many-workgroup top-k
-], ids=["f16-topk-B6", "bf16-reglu-threshold-B5", "f16-topk-wide-B3"])
+    # a batch of one: the gather path runs the single-token layer (with the bitmap written)
+    ("f16-topk-wide-B1", wl.CONFIGS[3].scaled(256, 24576, 64), 1),
+    ("bf16-reglu-threshold-B1", wl.CONFIGS[2].scaled(512, 1433, 64), 1),
+    ("f16-topk-small-B1", wl.CONFIGS[3].scaled(256, 1000, 64), 1),
+], ids=["f16-topk-B6", "bf16-reglu-threshold-B5", "f16-topk-wide-B3", "f16-topk-wide-B1",
+        "bf16-reglu-threshold-B1", "f16-topk-small-B1"])
 def test_batched_layer_end_to_end(name, cfg, B):
     """Predict + select + union FFN in one call: the selected sets (bitmaps) equal the oracle's
     selection from the library's own scores, and Y matches the oracle over those sets."""
@@ -264,3 +269,35 @@ def test_batched_layer_end_to_end(name, cfg, B):
             assert np.array_equal(bm[t].cpu().numpy().view(np.uint32), orc.to_bitmap(sel, cfg.f))
             sets.append(sel)
         _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"{name} path {path}")
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("f16-topk-wide", wl.CONFIGS[3].scaled(256, 24576, 64)),
+    ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(512, 1433, 64)),
+], ids=["f16-topk-wide", "bf16-reglu-threshold"])
+def test_batched_layer_batch_of_one_is_the_single_token_layer(name, cfg):
+    """B = 1 on the gather path: the same bits as csf_sparse_ffn_layer for that token, the union
+    size is the token's count, and the bitmap is its list."""
+    announce(f"batched layer B=1 vs single-token layer {name}")
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    X = wl.make_tokens(cfg, 2)
+    for t in range(2):
+        x = X[t:t + 1].to(DEV).contiguous()
+        words = (cfg.f + 31) // 32
+        bm = torch.zeros(1, words, dtype=torch.int32, device=DEV)
+        uc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        Y, taken = csf.sparse_ffn_batched_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T,
+                                                k=cfg.k, tau=cfg.tau, act=cfg.act,
+                                                path=csf.PATH_AUTO, bitmaps=bm, union_count=uc)
+        cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+        idx = torch.empty(cfg.k if cfg.k is not None else cfg.f, dtype=torch.int32, device=DEV)
+        y1 = csf.sparse_ffn_layer(x[0], Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=cfg.k,
+                                  tau=cfg.tau, act=cfg.act, idx=idx, count=cnt)
+        torch.cuda.synchronize()
+        assert taken == csf.PATH_GATHER
+        assert torch.equal(Y[0], y1), (name, t)
+        n = int(cnt.item())
+        assert int(uc.item()) == n
+        sel = idx[:n].cpu().numpy()
+        assert np.array_equal(bm[0].cpu().numpy().view(np.uint32), orc.to_bitmap(sel, cfg.f))
