@@ -32,7 +32,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 
 # kernel-name prefix -> label used by the benchmark
-LABELS = [("k_pred_down", "pred_down"), ("k_pred_up_select", "pred_up_select"), ("k_pred_up", "pred_up"), ("k_select_topk", "select_topk"),
+LABELS = [("k_pred_down", "pred_down"), ("k_pred_up_select", "pred_up_select"),
+          ("k_pred_up_loop", "pred_up"), ("k_pred_up", "pred_up"), ("k_select_topk", "select_topk"),
           ("k_select_threshold", "select_threshold"), ("k_gather_up", "gather_up"),
           ("k_gather_down", "gather_down"), ("k_reduce_partials", "reduce_partials"),
           ("k_pred_down_mfma", "pred_down_mfma"), ("k_pred_hidden", "pred_hidden"),
