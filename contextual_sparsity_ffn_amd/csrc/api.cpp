@@ -132,7 +132,7 @@ PredictWs predict_ws(int B, int r)
 hipError_t enqueue_predict(int dtype, const void *x, int B, int d, const void *V, int r,
                            const void *U, int f, float *scores, float *ws, hipStream_t st,
                            csf::Trace *tr, uint32_t *zero = nullptr, int nzero = 0,
-                           bool *zeroed = nullptr)
+                           bool *zeroed = nullptr, int pu_grid = 0)
 {
     if (zeroed)
         *zeroed = false;
@@ -143,7 +143,7 @@ hipError_t enqueue_predict(int dtype, const void *x, int B, int d, const void *V
     hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, ws, st, tr, zero, nzero);
     if (e != hipSuccess)
         return e;
-    return csf::launch_pred_up(dtype, ws, B, d, r, U, f, scores, st, tr);
+    return csf::launch_pred_up(dtype, ws, B, d, r, U, f, scores, st, tr, pu_grid);
 }
 
 struct FfnWs {
@@ -467,7 +467,8 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
         // the clear covers token 0's counter block: only a single token can skip the clear kernel
         hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
                                        nullptr, wide && B == 1 ? selws : nullptr,
-                                       wide && B == 1 ? csf::select_wide_zero_words() : 0, &zeroed);
+                                       wide && B == 1 ? csf::select_wide_zero_words() : 0, &zeroed,
+                                       on_side ? csf::kPredUpSideGrid : 0);
         if (e == hipSuccess) {
             if (wide)
                 e = csf::launch_select_topk_wide(sc, B, f, k, sel_idx(l), stride, sel_count(l),

@@ -58,9 +58,15 @@ constexpr int kSmallF = 1024;
 hipError_t launch_pred_up_select(int dtype, const float *part, int d, int r, const void *U, int f,
                                  float *s, int k, float tau, int32_t *idx, int32_t *count,
                                  hipStream_t stream, Trace *trace = nullptr);
-// s[B][f] = sigmoid(U relu(sum of the partials)) in float32.
+// s[B][f] = sigmoid(U relu(sum of the partials)) in float32.  grid: workgroups of the persistent
+// one-token form (0: the default, the most resident at once; a predictor that runs beside other
+// work on a second stream takes kPredUpSideGrid).
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
-                          float *s, hipStream_t stream, Trace *trace = nullptr);
+                          float *s, hipStream_t stream, Trace *trace = nullptr, int grid = 0);
+// Measured on the 48-layer OPT-30B-shape look-ahead stack (graph replay): 2.35 ms/token with the
+// side stream's up projection on 1024 workgroups, 2.52 with 2048 (it then crowds out the FFN on
+// the main stream), 2.42 / 2.37 / 2.48 with 768 / 1280 / 1536.
+constexpr int kPredUpSideGrid = 1024;
 
 // ---- predictor for a batch on the matrix cores (predict_mfma.hip) --------------------------
 constexpr int kPredMfmaMinBatch = 4;      // tokens from which the batched predictor is used

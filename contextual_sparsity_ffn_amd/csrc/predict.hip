@@ -432,12 +432,13 @@ hipError_t up_loop_launch(const float *a, int S, int r, int C, const void *U, in
 
 template <class T, int LPR, int MM, int RW>
 hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                     hipStream_t st, Trace *tr)
+                     hipStream_t st, Trace *tr, int grid)
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
     constexpr int NT = 256;   // measured: 512-thread workgroups are slower (19.5 against 18.2 us)
     if (B == 1)
-        return up_loop_launch<T, LPR, MM, 1>(a, S, r, C, U, f, s, st, tr, kPredUpGrid);
+        return up_loop_launch<T, LPR, MM, 1>(a, S, r, C, U, f, s, st, tr,
+                                             grid > 0 ? grid : kPredUpGrid);
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
     const int blocks = (waves + NT / kWave - 1) / (NT / kWave);
     return launch(k_pred_up<T, LPR, MM, RW, NT>, dim3(blocks), dim3(NT), st, tr,
@@ -449,27 +450,27 @@ hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, 
 // every CU several workgroups.
 template <class T, int LPR, int MM>
 hipError_t up_rw(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                 hipStream_t st, Trace *tr)
+                 hipStream_t st, Trace *tr, int grid)
 {
     constexpr int G = kWave / LPR;
     int rw = MM >= 2 ? 2 : 4;   // rows of two 16-byte chunks per lane: 2 rows (measured fastest)
     while (rw > 1 && (long)f / (rw * G) < 4096)   // keep >= 1024 workgroups when f allows
         rw /= 2;
-    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st, tr);
-    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, S, r, C, U, f, s, st, tr);
-    return up_launch<T, LPR, MM, 1>(a, B, S, r, C, U, f, s, st, tr);
+    if (rw >= 4) return up_launch<T, LPR, MM, 4>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (rw >= 2) return up_launch<T, LPR, MM, 2>(a, B, S, r, C, U, f, s, st, tr, grid);
+    return up_launch<T, LPR, MM, 1>(a, B, S, r, C, U, f, s, st, tr, grid);
 }
 
 template <class T>
 hipError_t up_t(const float *a, int B, int S, int r, int C, const void *U, int f, float *s,
-                hipStream_t st, Trace *tr)
+                hipStream_t st, Trace *tr, int grid)
 {
-    if (C <= 16) return up_rw<T, 16, 1>(a, B, S, r, C, U, f, s, st, tr);
-    if (C <= 32) return up_rw<T, 32, 1>(a, B, S, r, C, U, f, s, st, tr);
-    if (C <= 64) return up_rw<T, 64, 1>(a, B, S, r, C, U, f, s, st, tr);
-    if (C <= 128) return up_rw<T, 64, 2>(a, B, S, r, C, U, f, s, st, tr);
-    if (C <= 256) return up_rw<T, 64, 4>(a, B, S, r, C, U, f, s, st, tr);
-    if (C <= 512) return up_rw<T, 64, 8>(a, B, S, r, C, U, f, s, st, tr);
+    if (C <= 16) return up_rw<T, 16, 1>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (C <= 32) return up_rw<T, 32, 1>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (C <= 64) return up_rw<T, 64, 1>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (C <= 128) return up_rw<T, 64, 2>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (C <= 256) return up_rw<T, 64, 4>(a, B, S, r, C, U, f, s, st, tr, grid);
+    if (C <= 512) return up_rw<T, 64, 8>(a, B, S, r, C, U, f, s, st, tr, grid);
     return hipErrorInvalidValue;
 }
 
@@ -537,12 +538,12 @@ hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *
 }
 
 hipError_t launch_pred_up(int dtype, const float *a, int B, int d, int r, const void *U, int f,
-                          float *s, hipStream_t st, Trace *tr)
+                          float *s, hipStream_t st, Trace *tr, int grid)
 {
     const int S = pred_split(r, d, dtype);
-    if (dtype == 0) return up_t<F32T>(a, B, S, r, r / 4, U, f, s, st, tr);
-    if (dtype == 1) return up_t<F16T>(a, B, S, r, r / 8, U, f, s, st, tr);
-    return up_t<BF16T>(a, B, S, r, r / 8, U, f, s, st, tr);
+    if (dtype == 0) return up_t<F32T>(a, B, S, r, r / 4, U, f, s, st, tr, grid);
+    if (dtype == 1) return up_t<F16T>(a, B, S, r, r / 8, U, f, s, st, tr, grid);
+    return up_t<BF16T>(a, B, S, r, r / 8, U, f, s, st, tr, grid);
 }
 
 }  // namespace csf
