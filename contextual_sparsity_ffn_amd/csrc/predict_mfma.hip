@@ -13,7 +13,9 @@
 //                     a = t0 + t1 (+ t2) (t0 = round(a), t1 = round(a - t0), ...): about 22 bits
 //                     of a for binary16 (NA = 2) and 24 for bfloat16 (NA = 3), so the products
 //                     with U (exact in float32) lose nothing the float32 scores would keep;
-//   k_pred_up_mfma    tile of 16 rows of U, the 4 waves split r; sigmoid epilogue.
+//   k_pred_up_mfma    tile of 16 rows of U, the 4 waves split r; sigmoid epilogue
+//                     (k_pred_up_mfma_res when r <= 512: the hidden terms held in registers
+//                     across the tiles of a 512-workgroup grid).
 // MFMA lane layout: lane l holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e < 8,
 // and receives D[4 (l / 16) + i][l % 16], i < 4 (A = tokens x K, B = K x rows).
 #include "common.hpp"
@@ -190,6 +192,82 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma(const u32x4 *__restrict__ 
     }
 }
 
+// The same product when each wave's share of r is at most KW K steps (r <= 512 for KW = 4): the
+// wave's 16-bit hidden terms are loaded once into registers and serve every tile the workgroup
+// takes (tiles b, b + grid, ...), so only U streams; the next tile's U chunks are loaded before the
+// current tile is multiplied.  k_pred_up_mfma instead re-reads the terms from L2 for every tile,
+// which at 32 tokens is about four times U's own bytes.  Same products and sums in the same order,
+// so the same scores.
+template <class T, int MT, int NA, int KW>
+__global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restrict__ U,
+                                                          const uint16_t *__restrict__ ahid, int B,
+                                                          int r, int f, float *__restrict__ s)
+{
+    __shared__ float red[4][MT * 4][kWave];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int ln = lane & 15, g = lane >> 4;
+    const int C = r / 8;
+    const int steps = C / 4;
+    const int s0 = w * steps / 4, s1 = (w + 1) * steps / 4;
+    const int ns = s1 - s0;                      // <= KW (checked by the launcher)
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    u32x4 ra[KW][NA][MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int tok = 16 * m + ln;
+        const bool ok = tok < B;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const u32x4 *ar = reinterpret_cast<const u32x4 *>(ahid + ((size_t)e * B + (ok ? tok : 0)) * r);
+#pragma unroll
+            for (int q = 0; q < KW; ++q)
+                ra[q][e][m] = (ok && q < ns) ? ar[4 * (s0 + q) + g] : zero;
+        }
+    }
+    auto load_tile = [&](int n0, u32x4 (&dst)[KW]) {
+        const int n = n0 + ln;
+        const u32x4 *wr = U + (size_t)(n < f ? n : f - 1) * C;   // a row past f is discarded
+#pragma unroll
+        for (int q = 0; q < KW; ++q)
+            dst[q] = (n0 < f && q < ns) ? ld_stream(wr + 4 * (s0 + q) + g) : zero;
+    };
+    u32x4 rw[KW];
+    load_tile(blockIdx.x * 16, rw);
+    for (int n0 = blockIdx.x * 16; n0 < f; n0 += gridDim.x * 16) {
+        u32x4 rn[KW];
+        load_tile(n0 + gridDim.x * 16, rn);
+        f32x4 acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < KW; ++q) {
+            if (q < ns) {
+#pragma unroll
+                for (int e = 0; e < NA; ++e)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m] = T::mfma(ra[q][e][m], rw[q], acc[m]);
+            }
+        }
+        sum_waves<MT>(red, acc, w, lane);
+        __syncthreads();
+        for (int e = t; e < MT * 4 * kWave; e += 256) {
+            const int mi = e / kWave, l = e % kWave;
+            const int tok = 16 * (mi / 4) + 4 * (l >> 4) + (mi % 4);
+            const int nn = n0 + (l & 15);
+            if (tok < B && nn < f) {
+                const float z = (red[0][mi][l] + red[1][mi][l]) + (red[2][mi][l] + red[3][mi][l]);
+                s[(size_t)tok * f + nn] = 1.0f / (1.0f + expf(-z));
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < KW; ++q)
+            rw[q] = rn[q];
+    }
+}
+
 template <class T, int MT, int NA>
 hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, const u32x4 *U,
                          int f, float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr)
@@ -205,6 +283,14 @@ hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, co
     if (e != hipSuccess)
         return e;
     const int tiles = (f + 15) / 16;
+    if ((r / 32 + 3) / 4 <= 4) {
+        // 512 workgroups (3.5 tiles each at the OPT-30B shape): 8.9 / 9.3 / 12.9 us at 8 / 16 / 32
+        // tokens, against 9.7 / 12.4 / 20.9 for k_pred_up_mfma; 256, 1024 and one workgroup per
+        // tile measured slower
+        constexpr int kResGrid = 512;
+        return launch(k_pred_up_mfma_res<T, MT, NA, 4>, dim3(tiles < kResGrid ? tiles : kResGrid),
+                      dim3(256), st, tr, U, ahid, B, r, f, s);
+    }
     return launch(k_pred_up_mfma<T, MT, NA>, dim3(tiles < 4096 ? tiles : 4096), dim3(256), st, tr,
                   U, ahid, B, r, f, s);
 }
