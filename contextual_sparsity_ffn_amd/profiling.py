@@ -37,7 +37,7 @@ LABELS = [("k_pred_down", "pred_down"), ("k_pred_up_select", "pred_up_select"),
           ("k_select_threshold", "select_threshold"), ("k_gather_up", "gather_up"),
           ("k_gather_down", "gather_down"), ("k_reduce_partials", "reduce_partials"),
           ("k_pred_down_mfma", "pred_down_mfma"), ("k_pred_hidden", "pred_hidden"),
-          ("k_pred_up_mfma", "pred_up_mfma"), ("k_union_list", "union_list"),
+          ("k_pred_up_mfma_res", "pred_up_mfma"), ("k_pred_up_mfma", "pred_up_mfma"), ("k_union_list", "union_list"),
           ("k_union_up_valu", "union_up_valu"), ("k_union_down_valu", "union_down_valu"),
           ("k_union_up_lds", "union_up_mfma"), ("k_union_down_mfma", "union_down_mfma"),
           ("k_rms_norm", "rms_norm"), ("k_head_proj", "head_proj"), ("k_head_attn", "head_attn"),
