@@ -37,6 +37,11 @@ PRED_CASES = [
     ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 2),
     ("bf16", wl.CONFIGS[2].scaled(4096, 1433, 256), 2),
     ("f16-r1024", wl.CONFIGS[1].scaled(1024, 2050, 1024), 1),
+    # one token: the persistent up projection (2048 workgroups over the row groups) with fewer
+    # rows than one group, and with more groups than workgroups and a ragged last group
+    ("f16-B1-tiny-f", wl.CONFIGS[1].scaled(512, 7, 64), 1),
+    ("f16-B1-many-groups-ragged", wl.CONFIGS[1].scaled(512, 40001, 64), 1),
+    ("f32-B1-many-groups-ragged", wl.CONFIGS[0].scaled(256, 33333, 64), 1),
     # batches of 4 or more 16-bit tokens with d, r multiples of 128 take the matrix-core predictor
     ("f16-B8-mfma", wl.CONFIGS[3].scaled(1024, 2333, 128), 8),
     ("bf16-B20-mfma", wl.CONFIGS[2].scaled(512, 1433, 256), 20),
