@@ -47,6 +47,9 @@ PRED_CASES = [
     ("bf16-B20-mfma", wl.CONFIGS[2].scaled(512, 1433, 256), 20),
     ("f16-B37-mfma", wl.CONFIGS[1].scaled(1024, 1000, 256), 37),
     ("f16-B5-r1024-mfma", wl.CONFIGS[1].scaled(2048, 3001, 1024), 5),
+    # r = 512: four K steps per wave, the most the register-resident up projection holds
+    ("f16-B12-r512-mfma", wl.CONFIGS[3].scaled(1024, 3001, 512), 12),
+    ("bf16-B32-r512-mfma", wl.CONFIGS[2].scaled(512, 2049, 512), 32),
     ("f16-B6-ragged-valu", wl.CONFIGS[1].scaled(2600, 3001, 136), 6),
 ]
 
