@@ -663,7 +663,9 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
     if (e != hipSuccess)
         return e;
     const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f);
-    e = launch(k_union_down_mfma<T, MT, 3>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
+    // two K steps of loads in flight ahead (measured at 8 / 16 / 32 tokens: 47.8 / 57.1 / 73.9 us
+    // against 49.2 / 59.7 / 75.2 with three and 51.4 / 61.6 / 79.6 with four)
+    e = launch(k_union_down_mfma<T, MT, 2>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
                static_cast<const u32x4 *>(a.W2T), a.hhi, a.hlo, a.hs, a.ulist, a.ucount, a.B, a.f,
                C, nchunk, a.partials);
     if (e != hipSuccess)
