@@ -381,10 +381,14 @@ int csf_set_ffn_gate_threshold(float tau);
  * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record
  * events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
  * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
- * order -- csf_sparse_ffn_layer: predictor down-projection, predictor up-projection, selection,
- * gathered up/gate rows, gathered down rows (partial sums), reduction of the partial sums;
+ * order -- csf_sparse_ffn_layer: predictor down-projection, predictor up-projection, selection
+ * (two kernels, histogram then finishing pass, for top-k over 20000 or more scores; none of its
+ * own for f <= 1024, where the up projection selects), gathered up/gate rows, gathered down rows
+ * (partial sums), reduction of the partial sums;
  * csf_sparse_ffn_batched_union: union list, up/gate rows, down rows, reduction;
- * csf_sparse_ffn_batched_layer: the predictor's two kernels, selection, then the union's four;
+ * csf_sparse_ffn_batched_layer: the predictor's kernels (two; three -- down projection, hidden
+ * terms, up projection -- on the matrix cores from 4 tokens), selection, then the union's four;
+ * a batch of one on the gather path: csf_sparse_ffn_layer's list;
  * csf_sparse_attention_decode: projections (q, k, v of the list; with kv_all q of the list then
  * k, v of every head), attention blocks, combine, output-projection rows, reduction; csf_sparse_attention_layer: the predictor's two kernels and selection first.
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
