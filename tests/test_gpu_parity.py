@@ -267,6 +267,8 @@ LAYER_CASES = [
     ("c0", wl.CONFIGS[0], 6),
     ("f16-ragged-topk", wl.CONFIGS[1].scaled(2600, 3001, 136), 3),
     ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(4096, 1433, 256), 3),
+    # threshold over 40001 scores (about 20000 entries)
+    ("bf16-reglu-threshold-many", wl.CONFIGS[2].scaled(512, 40001, 64), 2),
     # up to 1024 neurons: scores and selection in one kernel
     ("bf16-reglu-small-threshold", wl.CONFIGS[2].scaled(1024, 700, 128), 3),
     ("f16-small-topk-ragged", wl.CONFIGS[1].scaled(1000, 997, 72), 3),
