@@ -697,11 +697,14 @@ int union_num_chunks(int mfma, int d, int dtype, int f)
 {
     if (!mfma)
         return ffn_num_chunks(d, dtype, f);
-    // about 768 workgroups of 256 columns (3 per CU); the partial rows (B x chunks x d float32)
-    // stay a few percent of the weight bytes; a chunk holds at most kMaxDownSteps K steps
+    // about 384 workgroups of 256 columns (1.5 per CU; a chunk holds at most kMaxDownSteps K
+    // steps, which at the OPT-30B shape is the binding bound); the partial rows (B x chunks x d
+    // float32) stay a few percent of the weight bytes.  Measured at the OPT-30B shape: 185 against
+    // 193 us per batch of 32 tokens with about 768 workgroups (and 188 against 204 for the dense
+    // batched step), the same at 8 tokens; 1152 and 1536 are slower again
     const int tiles = d / kDownCols > 0 ? d / kDownCols : 1;
     const int steps = (f + kKStep - 1) / kKStep;
-    int n = (768 + tiles - 1) / tiles;
+    int n = (384 + tiles - 1) / tiles;
     const int least = (steps + kMaxDownSteps - 1) / kMaxDownSteps;
     if (n > steps)
         n = steps;
