@@ -40,7 +40,6 @@ constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 byte
                                      // rows 8 apart fall 16 banks apart)
 constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
 constexpr int kMaxDownSteps = 64;    // K steps (of 32 union rows) per matrix-core down chunk
-constexpr int kUpRows = 32;          // union rows per LDS-staged up-projection workgroup
 
 // Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
 template <int MX, bool GATED>
@@ -279,14 +278,14 @@ __global__ __launch_bounds__(256) void k_union_down_valu(const u32x4 *__restrict
 // One 16x16x32 MFMA: lane l holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
 // e < 8, and receives D[4 (l / 16) + i][l % 16], i < 4.  A = tokens x K, B = K x union rows.
 //
-// Up projection through LDS.  A workgroup takes 32 union rows (two 16-row tiles) and all B tokens
-// over the whole of d, in segments of ST elements: per segment the 256 threads stage the
+// Up projection through LDS.  A workgroup takes ROWS union rows (one or two 16-row tiles) and all B
+// tokens over the whole of d, in segments of ST elements: per segment the 256 threads stage the
 // segment of every weight row (and, gated, of every up row) and of every token row in LDS -- each
 // wavefront load reads whole row segments, whole 128-byte lines -- with the loads of the
 // next PD - 1 segments in flight in a register ring.  The waves then take (gate or up, row tile,
 // token tile) pairs: four or more pairs give each wave its own (no reduction); two pairs split
 // each segment's K steps over two waves each, summed in a fixed order in the epilogue.
-template <class T, int MT, int NV, int PD, int ST>
+template <class T, int MT, int NV, int PD, int ST, int ROWS>
 __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ X,
                                                       const u32x4 *__restrict__ W1,
                                                       const u32x4 *__restrict__ Wup,
@@ -299,19 +298,20 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
                                                       uint16_t *__restrict__ hlo, int hs,
                                                       int silu)
 {
-    constexpr int WR = NV * kUpRows;             // staged weight rows
+    constexpr int RT = ROWS / 16;                // 16-row tiles of union rows
+    constexpr int WR = NV * ROWS;                // staged weight rows
     constexpr int SR = WR + 16 * MT;             // staged rows: weight rows, then token rows
     constexpr int SEGC = ST / 8;                 // 16-byte chunks of a row segment
     constexpr int RPP = 256 / SEGC;              // rows staged per pass of the workgroup
     constexpr int LPT = SR / RPP;                // staged chunks per thread
     constexpr int WPT = WR / RPP;                // ... of which weight rows
-    constexpr int TPR = kUpRows / RPP;           // chunks per thread per weight matrix
+    constexpr int TPR = ROWS / RPP;              // chunks per thread per weight matrix
     constexpr int STRIDE = ST + 8;               // staged row stride (16-bit elements)
-    constexpr int PAIRS = NV * 2 * MT;           // (gate/up, row tile, token tile) products
+    constexpr int PAIRS = NV * RT * MT;          // (gate/up, row tile, token tile) products
     constexpr int KSPLIT = PAIRS >= 4 ? 1 : 4 / PAIRS;
     constexpr int PPW = PAIRS >= 4 ? PAIRS / 4 : 1;
     constexpr int SPW = ST / kKStep / KSPLIT;    // K steps per wave per segment
-    static_assert(SR % RPP == 0 && kUpRows % RPP == 0 && 256 % SEGC == 0 && SPW >= 1,
+    static_assert(SR % RPP == 0 && ROWS % RPP == 0 && 256 % SEGC == 0 && SPW >= 1 && RT >= 1,
                   "staging covers whole rows");
     __shared__ __align__(16) uint16_t seg[2][SR][STRIDE];
     __shared__ float red[KSPLIT][PAIRS][4][kWave];
@@ -324,15 +324,15 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
     const int srow = t / SEGC, scol = t % SEGC;   // thread t stages rows srow + 8 i, chunk scol
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
-    // this wave's products: pair pi = (v, q, m) with v = pi / (2 MT), q = (pi / MT) % 2, m = pi % MT
+    // this wave's products: pair pi = (v, q, m) with v = pi / (RT MT), q = (pi / MT) % RT, m = pi % MT
     const int kp = PAIRS >= 4 ? 0 : w / PAIRS;
     int pv[PPW], pq[PPW], pm[PPW], pidx[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
         const int pi = PAIRS >= 4 ? w + 4 * j : w % PAIRS;
         pidx[j] = pi;
-        pv[j] = pi / (2 * MT);
-        pq[j] = (pi / MT) % 2;
+        pv[j] = pi / (RT * MT);
+        pq[j] = (pi / MT) % RT;
         pm[j] = pi % MT;
     }
     // token rows staged by this thread (chunks WPT .. LPT - 1); tokens past B stage zeros
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
         src[i] = X + (size_t)(tok < B ? tok : 0) * C + scol;
     }
 
-    for (int n0 = blockIdx.x * kUpRows; n0 < upad; n0 += gridDim.x * kUpRows) {
+    for (int n0 = blockIdx.x * ROWS; n0 < upad; n0 += gridDim.x * ROWS) {
         // weight rows staged by this thread: matrix i / TPR, tile row srow + RPP (i % TPR); a
         // row past the union re-reads the union's last row (its D columns are discarded)
 #pragma unroll
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
                 for (int j = 0; j < PPW; ++j) {
                     const u32x4 a = *reinterpret_cast<const u32x4 *>(&seg[buf][WR + 16 * pm[j] + ln][k0]);
                     const u32x4 b = *reinterpret_cast<const u32x4 *>(
-                        &seg[buf][kUpRows * pv[j] + 16 * pq[j] + ln][k0]);
+                        &seg[buf][ROWS * pv[j] + 16 * pq[j] + ln][k0]);
                     acc[j] = T::mfma(a, b, acc[j]);
                 }
             }
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
         __syncthreads();
         // element e: tile q, token tile m, D index i, lane l -> token 16 m + 4 (l / 16) + i,
         // row n0 + 16 q + l % 16
-        for (int e = t; e < 2 * MT * 4 * kWave; e += 256) {
+        for (int e = t; e < RT * MT * 4 * kWave; e += 256) {
             const int q = e / (MT * 4 * kWave);
             const int m = (e / (4 * kWave)) % MT;
             const int i = (e / kWave) % 4, l = e % kWave;
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
                     p += b1[jj];
                 hv = gate_act(p, silu);
                 if constexpr (NV == 2) {
-                    const int p1 = 2 * MT + q * MT + m;
+                    const int p1 = RT * MT + q * MT + m;
                     float uv = red[0][p1][i][l];
 #pragma unroll
                     for (int k = 1; k < KSPLIT; ++k)
@@ -643,20 +643,20 @@ hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
     return launch_reduce_partials(a.partials, nchunk, a.d, a.B, a.Y, st, tr);
 }
 
-template <class T, int MT, int ST>
+template <class T, int MT, int ST, int ROWS>
 hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     const int C = a.d / 8;
-    const int tiles = (a.f + kUpRows - 1) / kUpRows;
+    const int tiles = (a.f + ROWS - 1) / ROWS;
     const int blocks = tiles < 4096 ? tiles : 4096;
     hipError_t e;
     if (act_gated(a.act))
-        e = launch(k_union_up_lds<T, MT, 2, 3, ST>, dim3(blocks), dim3(256), st, tr,
+        e = launch(k_union_up_lds<T, MT, 2, 3, ST, ROWS>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
                    a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
     else
-        e = launch(k_union_up_lds<T, MT, 1, 3, ST>, dim3(blocks), dim3(256), st, tr,
+        e = launch(k_union_up_lds<T, MT, 1, 3, ST, ROWS>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
                    a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
@@ -678,12 +678,17 @@ hipError_t union_mfma(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     // staged segment length (measured): 512-byte segments for one token tile of few tokens,
     // 256-byte ones (less LDS and fewer registers per workgroup, so two workgroups per CU)
-    // from 8 tokens on
+    // from 8 tokens on.  Up-projection rows per workgroup (measured on clustered OPT-30B-shape
+    // batches): 16 at two tokens (26.8 against 29.9 us: the small union gives twice as many
+    // workgroups); 32 from four on, where 16 measured 1-1.5 us slower at 4 and 16 tokens and
+    // 31 us slower at 32 (the token rows re-read from L2 per tile double)
+    if (a.B <= 2)
+        return union_mfma_mt<T, 1, 256, 16>(a, st, tr);
     if (a.B <= 7)
-        return union_mfma_mt<T, 1, 256>(a, st, tr);
+        return union_mfma_mt<T, 1, 256, 32>(a, st, tr);
     if (a.B <= 16)
-        return union_mfma_mt<T, 1, 128>(a, st, tr);
-    return union_mfma_mt<T, 2, 128>(a, st, tr);
+        return union_mfma_mt<T, 1, 128, 32>(a, st, tr);
+    return union_mfma_mt<T, 2, 128, 32>(a, st, tr);
 }
 
 }  // namespace

@@ -65,12 +65,14 @@ def _check(L, X, sets, Y, semantics, what):
 # (name, config, B, active fraction): shapes span several tiles, f ends in a ragged word
 CASES = [
     ("f16-B1", wl.CONFIGS[3].scaled(512, 1000, 64), 1, 0.2),
+    ("f16-B2", wl.CONFIGS[3].scaled(512, 1000, 64), 2, 0.2),
     ("f16-B5", wl.CONFIGS[3].scaled(512, 1000, 64), 5, 0.2),
     ("f16-B16", wl.CONFIGS[3].scaled(768, 2333, 64), 16, 0.2),
     ("f16-B17", wl.CONFIGS[3].scaled(768, 2333, 64), 17, 0.1),
     ("f16-B32", wl.CONFIGS[3].scaled(1024, 1601, 64), 32, 0.2),
     ("bf16-reglu-B3", wl.CONFIGS[2].scaled(512, 1433, 64), 3, 0.3),
     ("bf16-reglu-B20", wl.CONFIGS[2].scaled(512, 1433, 64), 20, 0.3),
+    ("bf16-swiglu-B2", wl.CONFIGS[5].scaled(512, 1433, 64), 2, 0.5),
     ("bf16-swiglu-B3", wl.CONFIGS[5].scaled(512, 1433, 64), 3, 0.5),
     ("bf16-swiglu-B20", wl.CONFIGS[5].scaled(512, 1433, 64), 20, 0.5),
     ("f16-silu-B8", dataclasses.replace(wl.CONFIGS[3].scaled(512, 1000, 64), act=csf.SILU), 8, 0.3),
