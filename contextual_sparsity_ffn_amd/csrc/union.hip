@@ -40,6 +40,7 @@ constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 byte
                                      // rows 8 apart fall 16 banks apart)
 constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
 constexpr int kMaxDownSteps = 64;    // K steps (of 32 union rows) per matrix-core down chunk
+constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs of 32 CUs
 
 // Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
 template <int MX, bool GATED>
@@ -702,14 +703,16 @@ int union_num_chunks(int mfma, int d, int dtype, int f)
 {
     if (!mfma)
         return ffn_num_chunks(d, dtype, f);
-    // about 384 workgroups of 256 columns (1.5 per CU; a chunk holds at most kMaxDownSteps K
-    // steps, which at the OPT-30B shape is the binding bound); the partial rows (B x chunks x d
-    // float32) stay a few percent of the weight bytes.  Measured at the OPT-30B shape: 185 against
-    // 193 us per batch of 32 tokens with about 768 workgroups (and 188 against 204 for the dense
-    // batched step), the same at 8 tokens; 1152 and 1536 are slower again
+    // as many chunks as keep the grid at two workgroups of 256 columns per CU or fewer (a chunk
+    // holds at most kMaxDownSteps K steps, which can force more); the partial rows (B x chunks x
+    // d float32) stay a few percent of the weight bytes.  Measured per batch of 32 tokens at the
+    // OPT-30B shape (28 column tiles): 18 chunks (504 workgroups) 179.2 us, 14 / 16 chunks 185.0 /
+    // 181.5 (CUs with one workgroup beside CUs with two), 19 chunks 192.3 (three workgroups on
+    // some CUs, two on the rest), three on every CU 192.5; the same order at 8 and 16 tokens and
+    // for the dense batched step
     const int tiles = d / kDownCols > 0 ? d / kDownCols : 1;
     const int steps = (f + kKStep - 1) / kKStep;
-    int n = (384 + tiles - 1) / tiles;
+    int n = 2 * kComputeUnits / tiles;
     const int least = (steps + kMaxDownSteps - 1) / kMaxDownSteps;
     if (n > steps)
         n = steps;
