@@ -213,8 +213,9 @@ def test_batched_union_matches_single_token_path(pname, path):
         assert err <= 1e-5, (t, err)
 
 
-@pytest.mark.parametrize("B,path", [(4, csf.PATH_GATHER), (32, csf.PATH_MFMA)],
-                         ids=["B4-gather", "B32-mfma"])
+@pytest.mark.parametrize("B,path", [(4, csf.PATH_GATHER), (2, csf.PATH_MFMA), (8, csf.PATH_MFMA),
+                                   (32, csf.PATH_MFMA)],
+                         ids=["B4-gather", "B2-mfma", "B8-mfma", "B32-mfma"])
 def test_batched_union_full_size_opt30b_shape(B, path):
     """The OPT-30B FFN shape (d 7168, f 28672, top-k 5734 per token) with sets chosen by the
     library's own predictor and top-k on clustered tokens, as the benchmark runs it."""
