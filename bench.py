@@ -88,7 +88,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU path only: this build has no multi-GPU mode "
+        print("bench.py measures the single-GPU path only: the library has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

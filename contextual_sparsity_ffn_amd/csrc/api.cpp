@@ -53,7 +53,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-// Limits of the kernels in this build (rows held in registers per thread).
+// Limits of the library's kernels (rows held in registers per thread).
 constexpr long kMaxRowChunks = 16 * 256;   // d: 16-byte chunks per row for the gathered kernels
 constexpr long kMaxPredChunks = 512;       // r: 16-byte chunks per row of U
 
@@ -92,7 +92,7 @@ int check_row(int n, int dtype, const char *name, long max_chunks)
                     "%s = %d: a row must be a multiple of 16 bytes (%s of 8 for 16-bit types, 4 for float32)",
                     name, n, name);
     if (bytes / 16 > max_chunks)
-        return fail(CSF_ERR_UNSUPPORTED, "%s = %d exceeds this build's limit of %ld elements", name,
+        return fail(CSF_ERR_UNSUPPORTED, "%s = %d exceeds the library's limit of %ld elements", name,
                     n, max_chunks * 16 / elem_bytes(dtype));
     return CSF_OK;
 }
@@ -321,9 +321,9 @@ int validate_union(const void *X, int B, int d, int f, int act, int dtype, const
     if (s != CSF_OK)
         return s;
     REQUIRE(B <= csf::kMaxUnionBatch, CSF_ERR_UNSUPPORTED,
-            "B = %d exceeds this build's limit of %d tokens per batched call", B,
+            "B = %d exceeds the library's limit of %d tokens per batched call", B,
             csf::kMaxUnionBatch);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::select_max_f());
     REQUIRE(semantics == CSF_SEM_PER_TOKEN || semantics == CSF_SEM_UNION, CSF_ERR_INVALID_ARG,
             "unknown semantics %d", semantics);
@@ -388,7 +388,7 @@ int stack_events(hipEvent_t ev_x[2], hipEvent_t ev_s[2])
     if (e != hipSuccess)
         return hip_status(e, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices)
-        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond this build's limit", dev);
+        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond the library's limit", dev);
     for (int i = 0; i < 4; ++i) {
         if (!cache[dev][i]) {
             e = hipEventCreateWithFlags(&cache[dev][i], hipEventDisableTiming);
@@ -419,7 +419,7 @@ int capture_stream(int dev, hipStream_t *out)
     constexpr int kMaxDevices = 64;
     thread_local hipStream_t streams[kMaxDevices] = {};
     if (dev < 0 || dev >= kMaxDevices)
-        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond this build's limit", dev);
+        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond the library's limit", dev);
     if (!streams[dev]) {
         hipError_t e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
         if (e != hipSuccess) {
@@ -594,10 +594,10 @@ int validate_attention(const void *x, int d, int H, int dh, int dtype, const voi
     REQUIRE(csf::attn_head_dim_supported(dtype, dh), CSF_ERR_UNSUPPORTED,
             "dh = %d: a cached row must be 32, 64, 128, 256 or 512 bytes", dh);
     REQUIRE((long)H * dh <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED,
-            "H * dh = %ld exceeds this build's limit %d", (long)H * dh, csf::ffn_max_count());
+            "H * dh = %ld exceeds the library's limit %d", (long)H * dh, csf::ffn_max_count());
     REQUIRE(Tmax > 0, CSF_ERR_INVALID_ARG, "Tmax must be positive (got %d)", Tmax);
     REQUIRE(Tmax <= csf::attn_max_cache(), CSF_ERR_UNSUPPORTED,
-            "Tmax = %d exceeds this build's limit %d", Tmax, csf::attn_max_cache());
+            "Tmax = %d exceeds the library's limit %d", Tmax, csf::attn_max_cache());
     REQUIRE(kv_all == 0 || kv_all == 1, CSF_ERR_INVALID_ARG, "kv_all must be 0 or 1");
     CHECK_PTR(x, true);
     CHECK_PTR(Wq, true);
@@ -837,7 +837,7 @@ int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int3
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
     REQUIRE(k >= 0 && k <= f, CSF_ERR_INVALID_ARG, "k = %d is outside [0, f = %d]", k, f);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::select_max_f());
     CHECK_PTR(scores, B > 0);
     CHECK_PTR(idx, B > 0 && k > 0);
@@ -865,7 +865,7 @@ int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *
     (void)ws_bytes;
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::select_max_f());
     REQUIRE(tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
     CHECK_PTR(scores, B > 0);
@@ -890,7 +890,7 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
     REQUIRE(max_count >= 0 && max_count <= idx_stride, CSF_ERR_INVALID_ARG,
             "max_count = %d must be in [0, idx_stride = %d]", max_count, idx_stride);
     REQUIRE(max_count <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED,
-            "max_count = %d exceeds this build's limit %d", max_count, csf::ffn_max_count());
+            "max_count = %d exceeds the library's limit %d", max_count, csf::ffn_max_count());
     CHECK_PTR(idx, B > 0 && max_count > 0);
     CHECK_PTR(count, false);
     CHECK_PTR(h, false);
@@ -930,7 +930,7 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
         return s;
-    REQUIRE(f <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::ffn_max_count(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::ffn_max_count());
     CHECK_PTR(H, false);
     CHECK_PTR(Y, B > 0);
@@ -1083,7 +1083,7 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     CHECK_PTR(count_out, false);
     REQUIRE(k_cold >= -1 && k_cold <= fc, CSF_ERR_INVALID_ARG,
             "k_cold = %d must be -1 (threshold) or in [0, f - hot = %d]", k_cold, fc);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::select_max_f());
     REQUIRE(k_cold >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
     const int max_count = hot + (k_cold >= 0 ? k_cold : fc);
@@ -1164,7 +1164,7 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     CHECK_PTR(count_out, false);
     REQUIRE(k >= -1 && k <= f, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, f = %d]",
             k, f);
-    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds this build's limit %d",
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
             f, csf::select_max_f());
     REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
     const int max_count = k >= 0 ? k : f;
@@ -1212,7 +1212,7 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
             k, f);
     REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
     REQUIRE(f > 0 && f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED,
-            "f = %d is outside this build's range [1, %d]", f, csf::select_max_f());
+            "f = %d is outside the library's range [1, %d]", f, csf::select_max_f());
     CHECK_PTR(x, B > 0 && L > 0);
     CHECK_PTR(x_log, false);
     CHECK_PTR(xhat_log, false);
@@ -1336,7 +1336,7 @@ int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int d
     CHECK_PTR(count_out, false);
     REQUIRE(k >= -1 && k <= H, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, H = %d]",
             k, H);
-    REQUIRE(H <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "H = %d exceeds this build's limit %d",
+    REQUIRE(H <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "H = %d exceeds the library's limit %d",
             H, csf::select_max_f());
     REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
     const int max_heads = k >= 0 ? k : H;

@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     CSF_OK = 0,
     CSF_ERR_INVALID_ARG = 1,          /* a size, k, pointer or enum value is out of range       */
-    CSF_ERR_UNSUPPORTED = 2,          /* a valid request this build does not implement           */
+    CSF_ERR_UNSUPPORTED = 2,          /* a valid request the library does not implement         */
     CSF_ERR_MISALIGNED = 3,           /* a pointer or a row length breaks the 16-byte rule       */
     CSF_ERR_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes < csf_workspace_size(...)                      */
     CSF_ERR_HIP = 5                   /* the HIP runtime reported an error at launch             */
@@ -153,7 +153,7 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
  * Ties go to the lower neuron index; -0.0 and +0.0 are equal; the list is ascending.
  *
  *   scores  [B][f]       float32   finite scores
- *   k       0 <= k <= f            (f <= 65536 in this build)
+ *   k       0 <= k <= f            (f <= 65536)
  *   idx     [B][k]       int32     out: ascending active list per token
  *   count   [B]          int32     out, optional (NULL): set to k
  *   bitmap  [B][(f+31)/32] uint32  out, optional (NULL): bit j%32 of word j/32 set iff j selected

@@ -2,7 +2,7 @@
 
 Top-k: "Contextual Sparsity: Activation-Aware LLM Inference and the Deja Vu Paradigm", section
 "The Prediction Problem" (the k best scores form the active set).  Ties go to the lower index
-and the set is listed in ascending order (the reading this build takes; the pages are silent).
+and the set is listed in ascending order (the reading taken here; the pages are silent).
 Threshold: "Activation sparsity", section "Implementation sketch" (scores >= threshold).
 """
 import itertools
