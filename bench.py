@@ -98,7 +98,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = wl.CONFIGS[1]
+    cfg = wl.OPT175B
     d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
     code = _lib.dtype_code(cfg.dtype)
     log(f"building {args.layers} layer instances of d={d} f={f} r={r} ({cfg.dtype})")
@@ -419,7 +419,7 @@ def zero_skip_gated_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, workloads as wl
 
-    cfg = wl.CONFIGS[2]
+    cfg = wl.LLAMA_REGLU
     d, f, r = cfg.d, cfg.f, cfg.r
     code = _lib.dtype_code(cfg.dtype)
     nl = 8
@@ -505,7 +505,7 @@ def silu_functional_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, workloads as wl
 
-    cfg = wl.CONFIGS[5]
+    cfg = wl.LLAMA_SWIGLU
     d, f, r = cfg.d, cfg.f, cfg.r
     code = _lib.dtype_code(cfg.dtype)
     gate_tau = 0.1
@@ -689,7 +689,7 @@ def attention_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, workloads as wl
 
-    cfg = dataclasses.replace(wl.ATTN_CONFIGS[1], extra=256)
+    cfg = dataclasses.replace(wl.ATTN_OPT175B, extra=256)
     d, H, dh, r, k, T = cfg.d, cfg.H, cfg.dh, cfg.r, cfg.k, cfg.context
     code = _lib.dtype_code(cfg.dtype)
     nl, ntok = 4, 64
@@ -833,7 +833,7 @@ def static_locality_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, locality, workloads as wl
 
-    cfg = wl.CONFIGS[3]
+    cfg = wl.OPT30B
     d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
     nl = 4
     log(f"static-locality leg: {nl} power-law layers of d={d} f={f}")
@@ -918,7 +918,7 @@ def batched_union_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, workloads as wl
 
-    cfg = wl.CONFIGS[3]
+    cfg = wl.OPT30B
     d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
     code = _lib.dtype_code(cfg.dtype)
     nl = args.batched_layers
@@ -1041,7 +1041,7 @@ def stack_leg(args, dev):
     import contextual_sparsity_ffn_amd as csf
     from contextual_sparsity_ffn_amd import _lib, workloads as wl
 
-    cfg = wl.CONFIGS[4]
+    cfg = wl.OPT30B_STACK48
     d, f, r, k = cfg.d, cfg.f, cfg.r, cfg.k
     nl = args.stack_layers
     log(f"stack leg: {nl} layers of d={d} f={f} r={r}")

@@ -95,6 +95,13 @@ CONFIGS = {
               wup_std=1 / 64, bias=0.0, positive_frac=None, tokens=256),
 }
 
+TINY_F32 = CONFIGS[0]          # d 256, f 1024, r 64, float32, top-k 102
+OPT175B = CONFIGS[1]           # d 12288, f 49152, r 1024, float16, top-k 2458 (5%)
+LLAMA_REGLU = CONFIGS[2]       # d 4096, f 14336, r 256, bfloat16, ReGLU, threshold 0.5
+OPT30B = CONFIGS[3]            # d 7168, f 28672, r 512, float16, top-k 5734 (20%)
+OPT30B_STACK48 = CONFIGS[4]    # 48 blocks of the OPT-30B shape
+LLAMA_SWIGLU = CONFIGS[5]      # the LLaMA-class shape with SwiGLU, top-k 7168
+
 
 def seed(config: int, role: int, layer: int = 0) -> int:
     return 1_000_000 * config + 1_000 * role + layer
@@ -282,6 +289,8 @@ ATTN_CONFIGS = {
     0: AttnConfig(100, "tiny-attn-f32", 256, 8, 32, 32, torch.float32, 2, 64, 8, 0.25),
     1: AttnConfig(101, "opt175b-attn-f16", 12288, 96, 128, 256, torch.float16, 19, 2048, 64, 0.20),
 }
+ATTN_TINY_F32 = ATTN_CONFIGS[0]
+ATTN_OPT175B = ATTN_CONFIGS[1]
 
 
 @dataclasses.dataclass

@@ -225,9 +225,9 @@ def test_k_from_ratio_matches_the_printed_figures():
     for case in figs["k_from_ratio"]:
         assert csf.k_from_ratio(case["f"], case["ratio"]) == case["k"]
     # the workload sizes: 10% of 1024, 5% of 49152, 20% of 28672
-    assert csf.k_from_ratio(1024, 0.10) == wl.CONFIGS[0].k == 102
-    assert csf.k_from_ratio(49152, 0.05) == wl.CONFIGS[1].k == 2458
-    assert csf.k_from_ratio(28672, 0.20) == wl.CONFIGS[3].k == 5734
+    assert csf.k_from_ratio(1024, 0.10) == wl.TINY_F32.k == 102
+    assert csf.k_from_ratio(49152, 0.05) == wl.OPT175B.k == 2458
+    assert csf.k_from_ratio(28672, 0.20) == wl.OPT30B.k == 5734
 
 
 def test_budget_figure_arithmetic():
@@ -235,7 +235,7 @@ def test_budget_figure_arithmetic():
     b = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))["predictor_budget"]
     assert abs(b["dense_bytes_GB"] * b["predicted_sparsity"] - b["headroom_GB_approx"]) < 0.15
     # the headline workload's predictor is far inside that budget: (V + U) < s * dense bytes
-    cfg = wl.CONFIGS[1]
+    cfg = wl.OPT175B
     pred = 2 * (cfg.r * cfg.d + cfg.f * cfg.r)
     assert pred < 0.95 * wl.dense_bytes(cfg)
 

@@ -66,15 +66,15 @@ def _check_caches(Ld, o, before_K, before_V, dtype, what):
 
 
 CASES = [
-    ("f32-tiny", wl.ATTN_CONFIGS[0], [0, 2, 5], [64, 3, 0, 71, 10, 64, 1, 2], False),
-    ("f16-ragged", wl.ATTN_CONFIGS[1].scaled(1000, 12, 64, 64, 300, extra=20),
+    ("f32-tiny", wl.ATTN_TINY_F32, [0, 2, 5], [64, 3, 0, 71, 10, 64, 1, 2], False),
+    ("f16-ragged", wl.ATTN_OPT175B.scaled(1000, 12, 64, 64, 300, extra=20),
      [0, 3, 4, 7, 11], [300, 0, 5, 318, 131, 128, 300, 2, 257, 1, 64, 129], False),
-    ("f16-ragged-kvall", wl.ATTN_CONFIGS[1].scaled(1000, 12, 64, 64, 300, extra=20),
+    ("f16-ragged-kvall", wl.ATTN_OPT175B.scaled(1000, 12, 64, 64, 300, extra=20),
      [1, 3, 10], [300, 0, 5, 318, 131, 128, 300, 2, 257, 1, 64, 129], True),
-    ("bf16-dh128", dataclasses.replace(wl.ATTN_CONFIGS[1].scaled(512, 6, 128, 64, 129, extra=8),
+    ("bf16-dh128", dataclasses.replace(wl.ATTN_OPT175B.scaled(512, 6, 128, 64, 129, extra=8),
                                        dtype=torch.bfloat16), [0, 1, 2, 3, 4, 5],
      [129, 130, 0, 1, 127, 128], False),
-    ("f32-dh64", dataclasses.replace(wl.ATTN_CONFIGS[0].scaled(512, 5, 64, 32, 200, extra=4),
+    ("f32-dh64", dataclasses.replace(wl.ATTN_TINY_F32.scaled(512, 5, 64, 32, 200, extra=4),
                                      dtype=torch.float32), [4, 1],
      [200, 100, 0, 50, 202], False),
 ]
@@ -108,7 +108,7 @@ def test_decode_parity(name, cfg, heads, lens, kv_all):
 
 
 def test_dense_step_and_determinism():
-    cfg = wl.ATTN_CONFIGS[1].scaled(1024, 8, 128, 64, 260, extra=4)
+    cfg = wl.ATTN_OPT175B.scaled(1024, 8, 128, 64, 260, extra=4)
     announce("attention dense")
     L = wl.make_attention_layer(cfg)
     x = wl.make_attn_tokens(cfg, 1)[0]
@@ -133,7 +133,7 @@ def test_dense_step_and_determinism():
 
 
 def test_empty_list_bad_entries_and_full_cache():
-    cfg = wl.ATTN_CONFIGS[1].scaled(512, 6, 64, 32, 40, extra=2)
+    cfg = wl.ATTN_OPT175B.scaled(512, 6, 64, 32, 40, extra=2)
     announce("attention edge cases")
     L = wl.make_attention_layer(cfg)
     L.lens = torch.tensor([40, 42, 41, 0, 40, 40], dtype=torch.int32)    # head 1's cache is full
@@ -166,8 +166,8 @@ def test_empty_list_bad_entries_and_full_cache():
 
 
 LAYER_CASES = [
-    ("f16-topk", wl.ATTN_CONFIGS[1].scaled(1024, 16, 64, 64, 300, extra=4), None),
-    ("f32-threshold", wl.ATTN_CONFIGS[0], 0.5),
+    ("f16-topk", wl.ATTN_OPT175B.scaled(1024, 16, 64, 64, 300, extra=4), None),
+    ("f32-threshold", wl.ATTN_TINY_F32, 0.5),
 ]
 
 
@@ -204,7 +204,7 @@ def test_layer_full_size_opt175b_attention():
     """The OPT-175B attention shape (d 12288, 96 heads of 128, 2048 cached tokens, f16, top-19
     heads), one token, in the launch configuration the benchmark times."""
     announce("attention layer full size")
-    cfg = wl.ATTN_CONFIGS[1]
+    cfg = wl.ATTN_OPT175B
     Ld = wl.make_attention_layer(cfg, device=DEV)
     o = _orc_state(Ld)
     x = wl.make_attn_tokens(cfg, 1, device=DEV)[0]

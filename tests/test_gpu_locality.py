@@ -31,7 +31,7 @@ def _prepared(cfg, n_profile=96):
 
 def test_firing_frequency_matches_oracle_signs():
     announce("locality firing frequency")
-    cfg = wl.CONFIGS[3].scaled(512, 1200, 64)
+    cfg = wl.OPT30B.scaled(512, 1200, 64)
     L, P, freq, order, _ = _prepared(cfg, n_profile=48)
     torch.cuda.synchronize()
     o = dict(W1=to_orc(L.W1), b1=to_orc(L.b1), dt=orc.F16)
@@ -53,7 +53,7 @@ def test_firing_frequency_matches_oracle_signs():
 @pytest.mark.parametrize("mode,f", [("topk", 3000), ("threshold", 3000), ("topk", 24576)])
 def test_hot_layer_parity(mode, f):
     announce(f"locality hot layer {mode} f={f}")
-    cfg = wl.CONFIGS[3].scaled(1024, f, 128)
+    cfg = wl.OPT30B.scaled(1024, f, 128)
     L, P, freq, order, H = _prepared(cfg)
     hot = locality.hot_count(freq, 0.5, cap=cfg.k // 2)
     assert 0 < hot < cfg.f
@@ -85,7 +85,7 @@ def test_hot_layer_parity(mode, f):
 @pytest.mark.parametrize("f", [2000, 24576])
 def test_hot_block_of_zero_is_the_plain_layer(f):
     announce(f"locality hot = 0, f={f}")
-    cfg = wl.CONFIGS[3].scaled(1024, f, 128)
+    cfg = wl.OPT30B.scaled(1024, f, 128)
     L = wl.make_powerlaw_layer(cfg, device=DEV)
     x = wl.make_tokens(cfg, 1, device=DEV)[0]
     y0 = csf.sparse_ffn_layer(x, L.V, L.U, L.W1, L.b1, None, L.W2T, k=cfg.k)
@@ -96,7 +96,7 @@ def test_hot_block_of_zero_is_the_plain_layer(f):
 
 def test_reordered_layer_computes_the_same_function():
     announce("locality reorder")
-    cfg = wl.CONFIGS[3].scaled(768, 1500, 64)
+    cfg = wl.OPT30B.scaled(768, 1500, 64)
     L, P, freq, order, H = _prepared(cfg, n_profile=32)
     X = wl.make_tokens(cfg, 2, device=DEV)
     y = csf.dense_ffn(X, L.W1, L.b1, None, L.W2T)

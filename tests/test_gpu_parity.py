@@ -33,24 +33,24 @@ def _to_dev_layer(L):
 
 # shapes that span several workgroup tiles and end in ragged tails
 PRED_CASES = [
-    ("c0", wl.CONFIGS[0], 3),
-    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 2),
-    ("bf16", wl.CONFIGS[2].scaled(4096, 1433, 256), 2),
-    ("f16-r1024", wl.CONFIGS[1].scaled(1024, 2050, 1024), 1),
+    ("c0", wl.TINY_F32, 3),
+    ("f16-ragged", wl.OPT175B.scaled(2600, 3001, 136), 2),
+    ("bf16", wl.LLAMA_REGLU.scaled(4096, 1433, 256), 2),
+    ("f16-r1024", wl.OPT175B.scaled(1024, 2050, 1024), 1),
     # one token: the persistent up projection (2048 workgroups over the row groups) with fewer
     # rows than one group, and with more groups than workgroups and a ragged last group
-    ("f16-B1-tiny-f", wl.CONFIGS[1].scaled(512, 7, 64), 1),
-    ("f16-B1-many-groups-ragged", wl.CONFIGS[1].scaled(512, 40001, 64), 1),
-    ("f32-B1-many-groups-ragged", wl.CONFIGS[0].scaled(256, 33333, 64), 1),
+    ("f16-B1-tiny-f", wl.OPT175B.scaled(512, 7, 64), 1),
+    ("f16-B1-many-groups-ragged", wl.OPT175B.scaled(512, 40001, 64), 1),
+    ("f32-B1-many-groups-ragged", wl.TINY_F32.scaled(256, 33333, 64), 1),
     # batches of 4 or more 16-bit tokens with d, r multiples of 128 take the matrix-core predictor
-    ("f16-B8-mfma", wl.CONFIGS[3].scaled(1024, 2333, 128), 8),
-    ("bf16-B20-mfma", wl.CONFIGS[2].scaled(512, 1433, 256), 20),
-    ("f16-B37-mfma", wl.CONFIGS[1].scaled(1024, 1000, 256), 37),
-    ("f16-B5-r1024-mfma", wl.CONFIGS[1].scaled(2048, 3001, 1024), 5),
+    ("f16-B8-mfma", wl.OPT30B.scaled(1024, 2333, 128), 8),
+    ("bf16-B20-mfma", wl.LLAMA_REGLU.scaled(512, 1433, 256), 20),
+    ("f16-B37-mfma", wl.OPT175B.scaled(1024, 1000, 256), 37),
+    ("f16-B5-r1024-mfma", wl.OPT175B.scaled(2048, 3001, 1024), 5),
     # r = 512: four K steps per wave, the most the register-resident up projection holds
-    ("f16-B12-r512-mfma", wl.CONFIGS[3].scaled(1024, 3001, 512), 12),
-    ("bf16-B32-r512-mfma", wl.CONFIGS[2].scaled(512, 2049, 512), 32),
-    ("f16-B6-ragged-valu", wl.CONFIGS[1].scaled(2600, 3001, 136), 6),
+    ("f16-B12-r512-mfma", wl.OPT30B.scaled(1024, 3001, 512), 12),
+    ("bf16-B32-r512-mfma", wl.LLAMA_REGLU.scaled(512, 2049, 512), 32),
+    ("f16-B6-ragged-valu", wl.OPT175B.scaled(2600, 3001, 136), 6),
 ]
 
 
@@ -130,11 +130,11 @@ def test_select_threshold_bit_exact(f):
 
 
 FFN_CASES = [
-    ("c0-f32", wl.CONFIGS[0], 102),
-    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136), 150),
-    ("f16-reglu", wl.dataclasses.replace(wl.CONFIGS[2].scaled(2600, 3001, 136), dtype=torch.float16), 301),
-    ("bf16-reglu", wl.CONFIGS[2].scaled(4096, 1433, 256), 400),
-    ("f16-wide", wl.CONFIGS[1].scaled(12288, 700, 64), 333),
+    ("c0-f32", wl.TINY_F32, 102),
+    ("f16-ragged", wl.OPT175B.scaled(2600, 3001, 136), 150),
+    ("f16-reglu", wl.dataclasses.replace(wl.LLAMA_REGLU.scaled(2600, 3001, 136), dtype=torch.float16), 301),
+    ("bf16-reglu", wl.LLAMA_REGLU.scaled(4096, 1433, 256), 400),
+    ("f16-wide", wl.OPT175B.scaled(12288, 700, 64), 333),
 ]
 
 
@@ -192,7 +192,7 @@ def test_sparse_ffn_integer_inputs_bit_exact(act):
 
 def test_sparse_ffn_device_counts_empty_and_bad_index():
     announce("sparse_ffn device counts / empty / bad index")
-    cfg = wl.CONFIGS[1].scaled(1024, 900, 64)
+    cfg = wl.OPT175B.scaled(1024, 900, 64)
     L = _to_dev_layer(_layer(cfg))
     B, stride = 3, 64
     X = _dev(wl.make_tokens(cfg, B))
@@ -223,9 +223,9 @@ def test_sparse_ffn_device_counts_empty_and_bad_index():
 
 
 DENSE_CASES = [
-    ("c0-f32", wl.CONFIGS[0]),
-    ("f16-ragged", wl.CONFIGS[1].scaled(2600, 3001, 136)),
-    ("bf16-reglu", wl.CONFIGS[2].scaled(4096, 1433, 256)),
+    ("c0-f32", wl.TINY_F32),
+    ("f16-ragged", wl.OPT175B.scaled(2600, 3001, 136)),
+    ("bf16-reglu", wl.LLAMA_REGLU.scaled(4096, 1433, 256)),
 ]
 
 
@@ -249,7 +249,7 @@ def test_dense_ffn_and_full_list(name, cfg):
 def test_relu_true_set_matches_dense():
     """For ReLU, the sparse step over the true active set gives the dense output (up to order)."""
     announce("true set vs dense")
-    cfg = wl.CONFIGS[1].scaled(2048, 4000, 128)
+    cfg = wl.OPT175B.scaled(2048, 4000, 128)
     L = _layer(cfg)
     Ld = _to_dev_layer(L)
     x = wl.make_tokens(cfg, 1)[0]
@@ -264,14 +264,14 @@ def test_relu_true_set_matches_dense():
 
 
 LAYER_CASES = [
-    ("c0", wl.CONFIGS[0], 6),
-    ("f16-ragged-topk", wl.CONFIGS[1].scaled(2600, 3001, 136), 3),
-    ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(4096, 1433, 256), 3),
+    ("c0", wl.TINY_F32, 6),
+    ("f16-ragged-topk", wl.OPT175B.scaled(2600, 3001, 136), 3),
+    ("bf16-reglu-threshold", wl.LLAMA_REGLU.scaled(4096, 1433, 256), 3),
     # threshold over 40001 scores (about 20000 entries)
-    ("bf16-reglu-threshold-many", wl.CONFIGS[2].scaled(512, 40001, 64), 2),
+    ("bf16-reglu-threshold-many", wl.LLAMA_REGLU.scaled(512, 40001, 64), 2),
     # up to 1024 neurons: scores and selection in one kernel
-    ("bf16-reglu-small-threshold", wl.CONFIGS[2].scaled(1024, 700, 128), 3),
-    ("f16-small-topk-ragged", wl.CONFIGS[1].scaled(1000, 997, 72), 3),
+    ("bf16-reglu-small-threshold", wl.LLAMA_REGLU.scaled(1024, 700, 128), 3),
+    ("f16-small-topk-ragged", wl.OPT175B.scaled(1000, 997, 72), 3),
 ]
 
 
@@ -318,7 +318,7 @@ def test_layer_selection_ties_go_to_the_lower_index(f):
     predictor kernel for f <= 1024, the selection kernel above) must break the ties at the
     boundary by the lower neuron index, as the oracle does."""
     announce(f"layer ties f={f}")
-    cfg = wl.CONFIGS[0].scaled(256, f, 64, k=f // 10 + 1)
+    cfg = wl.TINY_F32.scaled(256, f, 64, k=f // 10 + 1)
     L = _layer(cfg)
     U = L.U.clone()
     U[1::2] = U[0::2][: U[1::2].shape[0]]
@@ -335,7 +335,7 @@ def test_layer_full_size_opt175b_shape():
     """The headline workload at full size (d=12288, f=49152, r=1024, f16, k=2458), one token,
     in the same launch configuration the benchmark times."""
     announce("layer full size c1")
-    cfg = wl.CONFIGS[1]
+    cfg = wl.OPT175B
     Ld = wl.make_layer(cfg, device=DEV)
     x = wl.make_tokens(cfg, 1, device=DEV)[0]
     o = layer_to_orc(Ld)
@@ -345,8 +345,8 @@ def test_layer_full_size_opt175b_shape():
 
 # ---- post-gate zero-skip: rows with h = 0 are not read; y is the same up to summation order --------
 ZS_CASES = [
-    ("relu-f16", wl.CONFIGS[1].scaled(2048, 3001, 128)),
-    ("reglu-bf16-threshold", wl.CONFIGS[2].scaled(1024, 2500, 128)),
+    ("relu-f16", wl.OPT175B.scaled(2048, 3001, 128)),
+    ("reglu-bf16-threshold", wl.LLAMA_REGLU.scaled(1024, 2500, 128)),
 ]
 
 

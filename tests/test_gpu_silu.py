@@ -34,10 +34,10 @@ def _silu_cfg(cfg, act=csf.SILU):
 
 
 FFN_CASES = [
-    ("silu-f32", _silu_cfg(wl.CONFIGS[0]), 300),
-    ("silu-f16-ragged", _silu_cfg(wl.CONFIGS[1].scaled(2600, 3001, 136)), 777),
-    ("swiglu-bf16", wl.CONFIGS[5].scaled(4096, 1433, 256), 700),
-    ("swiglu-f16", dataclasses.replace(wl.CONFIGS[5].scaled(2600, 3001, 136), dtype=torch.float16),
+    ("silu-f32", _silu_cfg(wl.TINY_F32), 300),
+    ("silu-f16-ragged", _silu_cfg(wl.OPT175B.scaled(2600, 3001, 136)), 777),
+    ("swiglu-bf16", wl.LLAMA_SWIGLU.scaled(4096, 1433, 256), 700),
+    ("swiglu-f16", dataclasses.replace(wl.LLAMA_SWIGLU.scaled(2600, 3001, 136), dtype=torch.float16),
      1501),
 ]
 
@@ -73,8 +73,8 @@ def test_sparse_and_dense_ffn_silu(name, cfg, count):
 
 
 LAYER_CASES = [
-    ("swiglu-bf16-topk", wl.CONFIGS[5].scaled(4096, 1433, 256), None),
-    ("silu-f16-threshold", _silu_cfg(wl.CONFIGS[1].scaled(2048, 3001, 128)), 0.5),
+    ("swiglu-bf16-topk", wl.LLAMA_SWIGLU.scaled(4096, 1433, 256), None),
+    ("silu-f16-threshold", _silu_cfg(wl.OPT175B.scaled(2048, 3001, 128)), 0.5),
 ]
 
 
@@ -107,7 +107,7 @@ def test_layer_end_to_end_silu(name, cfg, tau):
 def test_layer_full_size_llama_swiglu():
     """The SwiGLU LLaMA-class layer at full size (d=4096, f=14336, r=256, bf16, k=7168)."""
     announce("silu layer full size swiglu")
-    cfg = wl.CONFIGS[5]
+    cfg = wl.LLAMA_SWIGLU
     Ld = wl.make_layer(cfg, device=DEV)
     o = layer_to_orc(Ld)
     x = wl.make_tokens(cfg, 1, device=DEV)[0]
@@ -143,8 +143,8 @@ def _resolved_functional(x, o, listed, h_gpu, tau):
 
 
 SKIP_CASES = [
-    ("swiglu-bf16", wl.CONFIGS[5].scaled(2048, 2500, 128)),
-    ("silu-f16", _silu_cfg(wl.CONFIGS[5].scaled(1024, 3001, 64), csf.SILU)),
+    ("swiglu-bf16", wl.LLAMA_SWIGLU.scaled(2048, 2500, 128)),
+    ("silu-f16", _silu_cfg(wl.LLAMA_SWIGLU.scaled(1024, 3001, 64), csf.SILU)),
 ]
 
 
@@ -215,7 +215,7 @@ def test_functional_skip_layer_and_dense(name, cfg):
 def test_relu_gate_threshold_drops_small_activations():
     """The threshold applies to the ReLU forms as well: ReGLU with gate_tau > 0 keeps the neurons
     whose relu(gate) exceeds it."""
-    cfg = wl.CONFIGS[2].scaled(1024, 2500, 128)
+    cfg = wl.LLAMA_REGLU.scaled(1024, 2500, 128)
     announce("relu gate threshold")
     L = wl.make_layer(cfg)
     Ld = _dev_layer(L)

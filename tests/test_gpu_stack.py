@@ -103,7 +103,7 @@ def _teacher_forced(layers, cfg, X, lookahead, norm=True, check_layers=None):
 @pytest.mark.parametrize("lookahead", [False, True], ids=["sync", "lookahead"])
 def test_stack_teacher_forced_topk(lookahead):
     announce(f"stack top-k lookahead={lookahead}")
-    cfg = wl.CONFIGS[4].scaled(512, 2048, 64)
+    cfg = wl.OPT30B_STACK48.scaled(512, 2048, 64)
     layers = _layers(cfg, 4)
     X = wl.make_tokens(cfg, 2)
     _teacher_forced(layers, cfg, X, lookahead)
@@ -111,7 +111,7 @@ def test_stack_teacher_forced_topk(lookahead):
 
 def test_stack_teacher_forced_threshold_reglu_literal():
     announce("stack threshold reglu literal")
-    cfg = wl.CONFIGS[2].scaled(512, 1433, 64)
+    cfg = wl.LLAMA_REGLU.scaled(512, 1433, 64)
     layers = _layers(cfg, 3)
     X = wl.make_tokens(cfg, 2)
     _teacher_forced(layers, cfg, X, lookahead=True, norm=False)
@@ -144,7 +144,7 @@ def _replay(layers, cfg, X, x_log, xhat_log, idx_log, count_log, xL, lookahead):
 @pytest.mark.parametrize("lookahead", [False, True], ids=["sync", "lookahead"])
 def test_stack_replays_bit_exact_from_single_layer_calls(lookahead):
     announce(f"stack replay lookahead={lookahead}")
-    cfg = wl.CONFIGS[4].scaled(1024, 3000, 128)
+    cfg = wl.OPT30B_STACK48.scaled(1024, 3000, 128)
     layers = _layers(cfg, 6)
     X = wl.make_tokens(cfg, 3)
     xL, x_log, xhat_log, idx_log, count_log = _run(layers, X, cfg, lookahead)
@@ -157,7 +157,7 @@ def test_stack_replays_bit_exact_from_single_layer_calls(lookahead):
 def test_stack_single_layer_and_modes_agree_at_layer_zero():
     """L = 1: look-ahead has nothing to look ahead to, so both modes equal one block."""
     announce("stack L=1")
-    cfg = wl.CONFIGS[4].scaled(512, 1024, 64)
+    cfg = wl.OPT30B_STACK48.scaled(512, 1024, 64)
     layers = _layers(cfg, 1)
     X = wl.make_tokens(cfg, 2)
     a = _run(layers, X, cfg, lookahead=False)[0]
@@ -169,7 +169,7 @@ def test_stack_full_size_opt30b_shape_lookahead():
     """Three blocks of the OPT-30B FFN shape (d 7168, f 28672, r 512, top-k 5734), batch 1,
     look-ahead: bitwise replay of all three, oracle check of the last one."""
     announce("stack full size")
-    cfg = wl.CONFIGS[4]
+    cfg = wl.OPT30B_STACK48
     layers = _layers(cfg, 3)
     X = wl.make_tokens(cfg, 1, device=DEV)
     xL, x_log, xhat_log, idx_log, count_log = _run(layers, X, cfg, lookahead=True)
@@ -189,7 +189,7 @@ def test_stack_full_size_graph_replay_matches_eager(lookahead):
     three blocks, batch 1 -- the launch configuration the benchmark times -- gives the eager bits
     on every replay."""
     announce(f"stack full size graph lookahead={lookahead}")
-    cfg = wl.CONFIGS[4]
+    cfg = wl.OPT30B_STACK48
     layers = _layers(cfg, 3)
     X = wl.make_tokens(cfg, 2).float().to(DEV)
     side = torch.cuda.Stream(device=DEV)
@@ -217,7 +217,7 @@ def test_stack_graph_replay_matches_eager(lookahead):
     """The captured-graph form gives the eager bits on every replay, with eager work (another
     stack call on other buffers) between the replays, and recaptures when an argument changes."""
     announce(f"stack graph lookahead={lookahead}")
-    cfg = wl.CONFIGS[4].scaled(1024, 2048, 128)
+    cfg = wl.OPT30B_STACK48.scaled(1024, 2048, 128)
     layers = _layers(cfg, 5)
     X = wl.make_tokens(cfg, 4).float().to(DEV)
     side = torch.cuda.Stream(device=DEV)

@@ -64,18 +64,18 @@ def _check(L, X, sets, Y, semantics, what):
 
 # (name, config, B, active fraction): shapes span several tiles, f ends in a ragged word
 CASES = [
-    ("f16-B1", wl.CONFIGS[3].scaled(512, 1000, 64), 1, 0.2),
-    ("f16-B2", wl.CONFIGS[3].scaled(512, 1000, 64), 2, 0.2),
-    ("f16-B5", wl.CONFIGS[3].scaled(512, 1000, 64), 5, 0.2),
-    ("f16-B16", wl.CONFIGS[3].scaled(768, 2333, 64), 16, 0.2),
-    ("f16-B17", wl.CONFIGS[3].scaled(768, 2333, 64), 17, 0.1),
-    ("f16-B32", wl.CONFIGS[3].scaled(1024, 1601, 64), 32, 0.2),
-    ("bf16-reglu-B3", wl.CONFIGS[2].scaled(512, 1433, 64), 3, 0.3),
-    ("bf16-reglu-B20", wl.CONFIGS[2].scaled(512, 1433, 64), 20, 0.3),
-    ("bf16-swiglu-B2", wl.CONFIGS[5].scaled(512, 1433, 64), 2, 0.5),
-    ("bf16-swiglu-B3", wl.CONFIGS[5].scaled(512, 1433, 64), 3, 0.5),
-    ("bf16-swiglu-B20", wl.CONFIGS[5].scaled(512, 1433, 64), 20, 0.5),
-    ("f16-silu-B8", dataclasses.replace(wl.CONFIGS[3].scaled(512, 1000, 64), act=csf.SILU), 8, 0.3),
+    ("f16-B1", wl.OPT30B.scaled(512, 1000, 64), 1, 0.2),
+    ("f16-B2", wl.OPT30B.scaled(512, 1000, 64), 2, 0.2),
+    ("f16-B5", wl.OPT30B.scaled(512, 1000, 64), 5, 0.2),
+    ("f16-B16", wl.OPT30B.scaled(768, 2333, 64), 16, 0.2),
+    ("f16-B17", wl.OPT30B.scaled(768, 2333, 64), 17, 0.1),
+    ("f16-B32", wl.OPT30B.scaled(1024, 1601, 64), 32, 0.2),
+    ("bf16-reglu-B3", wl.LLAMA_REGLU.scaled(512, 1433, 64), 3, 0.3),
+    ("bf16-reglu-B20", wl.LLAMA_REGLU.scaled(512, 1433, 64), 20, 0.3),
+    ("bf16-swiglu-B2", wl.LLAMA_SWIGLU.scaled(512, 1433, 64), 2, 0.5),
+    ("bf16-swiglu-B3", wl.LLAMA_SWIGLU.scaled(512, 1433, 64), 3, 0.5),
+    ("bf16-swiglu-B20", wl.LLAMA_SWIGLU.scaled(512, 1433, 64), 20, 0.5),
+    ("f16-silu-B8", dataclasses.replace(wl.OPT30B.scaled(512, 1000, 64), act=csf.SILU), 8, 0.3),
 ]
 PATHS = [("gather", csf.PATH_GATHER), ("mfma", csf.PATH_MFMA)]
 
@@ -101,7 +101,7 @@ def test_batched_union_per_token(name, cfg, B, frac, pname, path):
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
 def test_batched_union_semantics_union(pname, path):
     announce(f"batched union semantics=union {pname}")
-    cfg = wl.CONFIGS[3].scaled(512, 1200, 64)
+    cfg = wl.OPT30B.scaled(512, 1200, 64)
     L = wl.make_layer(cfg)
     Ld = _dev_layer(L)
     B = 6
@@ -134,7 +134,7 @@ def test_batched_union_integer_inputs_bit_exact(act, pname, path):
     W2T = torch.randint(-2, 3, (f, d), generator=g).half()
     b1 = torch.randint(-3, 4, (f,), generator=g).float()
     sets = _random_sets(f, B, 300, seed=3)
-    cfg = dataclasses.replace(wl.CONFIGS[3].scaled(d, f, 64), act=act)
+    cfg = dataclasses.replace(wl.OPT30B.scaled(d, f, 64), act=act)
     Ld = wl.Layer(cfg, None, None, W1.to(DEV), b1.to(DEV), None if Wup is None else Wup.to(DEV),
                   W2T.to(DEV))
     Y, _ = _run(Ld, x.to(DEV), _bitmaps(sets, f), csf.SEM_PER_TOKEN, path)
@@ -152,7 +152,7 @@ def test_batched_union_integer_inputs_bit_exact(act, pname, path):
 
 def test_batched_union_float32_and_auto_path():
     announce("batched union float32 / auto path")
-    cfg = wl.CONFIGS[0]                                    # d = 256, f = 1024, float32
+    cfg = wl.TINY_F32                                    # d = 256, f = 1024, float32
     L = wl.make_layer(cfg)
     Ld = _dev_layer(L)
     B = 7
@@ -164,7 +164,7 @@ def test_batched_union_float32_and_auto_path():
     with pytest.raises(csf.CsfError):
         _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, csf.PATH_MFMA)
     # 16-bit: one token gathers, a batch of 8 takes the matrix cores
-    c16 = wl.CONFIGS[3].scaled(512, 1000, 64)
+    c16 = wl.OPT30B.scaled(512, 1000, 64)
     L16 = _dev_layer(wl.make_layer(c16))
     X16 = wl.make_tokens(c16, 8).to(DEV)
     s16 = _random_sets(c16.f, 8, 100, seed=5)
@@ -176,7 +176,7 @@ def test_batched_union_float32_and_auto_path():
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
 def test_batched_union_empty_and_one_token_sets(pname, path):
     announce(f"batched union empty sets {pname}")
-    cfg = wl.CONFIGS[3].scaled(512, 999, 64)
+    cfg = wl.OPT30B.scaled(512, 999, 64)
     L = wl.make_layer(cfg)
     Ld = _dev_layer(L)
     B = 4
@@ -199,7 +199,7 @@ def test_batched_union_matches_single_token_path(pname, path):
     """Per-token semantics: each token's row equals the single-token sparse FFN of its own list
     (to float32 rounding; the two sum in different orders)."""
     announce(f"batched union vs single-token {pname}")
-    cfg = wl.CONFIGS[3].scaled(1024, 3000, 64)
+    cfg = wl.OPT30B.scaled(1024, 3000, 64)
     L = wl.make_layer(cfg)
     Ld = _dev_layer(L)
     B = 9
@@ -220,7 +220,7 @@ def test_batched_union_full_size_opt30b_shape(B, path):
     """The OPT-30B FFN shape (d 7168, f 28672, top-k 5734 per token) with sets chosen by the
     library's own predictor and top-k on clustered tokens, as the benchmark runs it."""
     announce(f"batched union full size B={B}")
-    cfg = wl.CONFIGS[3]
+    cfg = wl.OPT30B
     Ld = wl.make_layer(cfg, device=DEV)
     X = wl.make_clustered_tokens(cfg, B, device=DEV)
     scores = csf.predict_active(X, Ld.V, Ld.U)
@@ -240,13 +240,13 @@ def test_batched_union_full_size_opt30b_shape(B, path):
 
 
 @pytest.mark.parametrize("name,cfg,B", [
-    ("f16-topk-B6", wl.CONFIGS[3].scaled(768, 2333, 64), 6),
-    ("bf16-reglu-threshold-B5", wl.CONFIGS[2].scaled(512, 1433, 64), 5),
-    ("f16-topk-wide-B3", wl.CONFIGS[3].scaled(256, 24576, 64), 3),   # many-workgroup top-k
+    ("f16-topk-B6", wl.OPT30B.scaled(768, 2333, 64), 6),
+    ("bf16-reglu-threshold-B5", wl.LLAMA_REGLU.scaled(512, 1433, 64), 5),
+    ("f16-topk-wide-B3", wl.OPT30B.scaled(256, 24576, 64), 3),   # many-workgroup top-k
     # a batch of one: the gather path runs the single-token layer (with the bitmap written)
-    ("f16-topk-wide-B1", wl.CONFIGS[3].scaled(256, 24576, 64), 1),
-    ("bf16-reglu-threshold-B1", wl.CONFIGS[2].scaled(512, 1433, 64), 1),
-    ("f16-topk-small-B1", wl.CONFIGS[3].scaled(256, 1000, 64), 1),
+    ("f16-topk-wide-B1", wl.OPT30B.scaled(256, 24576, 64), 1),
+    ("bf16-reglu-threshold-B1", wl.LLAMA_REGLU.scaled(512, 1433, 64), 1),
+    ("f16-topk-small-B1", wl.OPT30B.scaled(256, 1000, 64), 1),
 ], ids=["f16-topk-B6", "bf16-reglu-threshold-B5", "f16-topk-wide-B3", "f16-topk-wide-B1",
         "bf16-reglu-threshold-B1", "f16-topk-small-B1"])
 def test_batched_layer_end_to_end(name, cfg, B):
@@ -275,8 +275,8 @@ def test_batched_layer_end_to_end(name, cfg, B):
 
 
 @pytest.mark.parametrize("name,cfg", [
-    ("f16-topk-wide", wl.CONFIGS[3].scaled(256, 24576, 64)),
-    ("bf16-reglu-threshold", wl.CONFIGS[2].scaled(512, 1433, 64)),
+    ("f16-topk-wide", wl.OPT30B.scaled(256, 24576, 64)),
+    ("bf16-reglu-threshold", wl.LLAMA_REGLU.scaled(512, 1433, 64)),
 ], ids=["f16-topk-wide", "bf16-reglu-threshold"])
 def test_batched_layer_batch_of_one_is_the_single_token_layer(name, cfg):
     """B = 1 on the gather path: the same bits as csf_sparse_ffn_layer for that token, the union

@@ -173,7 +173,7 @@ def test_attention_workload_silences_most_heads():
     import torch
     from contextual_sparsity_ffn_amd import workloads as wl
     from csf_testutil import to_orc
-    cfg = wl.ATTN_CONFIGS[1].scaled(1024, 16, 64, 64, 256)
+    cfg = wl.ATTN_OPT175B.scaled(1024, 16, 64, 64, 256)
     L = wl.make_attention_layer(cfg)
     X = wl.make_attn_tokens(cfg, 8)
     fr, gap = [], []

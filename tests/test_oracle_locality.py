@@ -65,7 +65,7 @@ def test_reordering_neurons_keeps_the_function():
 
 def test_powerlaw_inputs_fire_as_promised():
     """Mean firing fraction and per-neuron frequencies of the power-law layer (input generator)."""
-    cfg = wl.CONFIGS[3].scaled(256, 1500, 64)
+    cfg = wl.OPT30B.scaled(256, 1500, 64)
     q = wl.powerlaw_firing(1500, cfg.positive_frac, 2.0, "cpu", 7)
     assert abs(float(q.mean()) - cfg.positive_frac) < 1e-6
     assert float(q.max()) <= 0.99 and float((q > 0.5).float().mean()) > 0.05   # a hot head

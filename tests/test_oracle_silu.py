@@ -167,7 +167,7 @@ def test_swiglu_workload_is_about_half_functionally_active():
     # spread at other shapes.
     from contextual_sparsity_ffn_amd import workloads as wl
     from csf_testutil import layer_to_orc, to_orc
-    cfg = wl.CONFIGS[5].scaled(1024, 4096, 64)
+    cfg = wl.LLAMA_SWIGLU.scaled(1024, 4096, 64)
     L = wl.make_layer(cfg)
     o = layer_to_orc(L)
     X = wl.make_tokens(cfg, 4)
