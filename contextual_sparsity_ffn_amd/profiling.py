@@ -111,7 +111,8 @@ def _copy_scale(disp) -> float:
     return COPY_BYTES / (best * 1024.0)
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, out_json: str, out_md: str, command: str) -> dict:
+def summarize_counters(fetch_csv: str, write_csv: str, out_json: str, out_md: str, command: str,
+                       title: str = "layer kernels", sources=LAYER_SOURCES) -> dict:
     fetch, write = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
     fs, ws = _copy_scale(fetch), _copy_scale(write)
     kern = {}
@@ -122,16 +123,17 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_json: str, out_md: st
             kern[label] = {"dispatches": len(fv),
                            "fetch_bytes": statistics.median(fv) * 1024.0 * fs,
                            "write_bytes": statistics.median(wv) * 1024.0 * ws}
-    res = {"source_sha256": source_hash(), "fetch_scale": fs, "write_scale": ws,
+    res = {"source_sha256": source_hash(sources), "sources": sorted(sources),
+           "fetch_scale": fs, "write_scale": ws,
            "copy_bytes": COPY_BYTES, "command": command, "kernels": kern}
     with open(out_json, "w") as fh:
         json.dump(res, fh, indent=1)
     with open(out_md, "w") as out:
-        out.write("# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE), layer kernels\n\n")
+        out.write(f"# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE), {title}\n\n")
         out.write(f"Command (repository root), once per counter:\n\n    {command}\n\n")
         out.write(f"Scale factors from the {COPY_BYTES >> 20} MiB calibration copy: FETCH_SIZE x{fs:.4f}, "
                   f"WRITE_SIZE x{ws:.4f} (counter KiB -> bytes: KiB * 1024 * factor).\n\n")
-        out.write(f"Kernel source sha256: `{res['source_sha256']}`\n\n")
+        out.write(f"Kernel source sha256 ({', '.join(res['sources'])}): `{res['source_sha256']}`\n\n")
         out.write("| kernel | dispatches | fetch MB (median) | write MB (median) |\n|---|---:|---:|---:|\n")
         for lab, v in kern.items():
             out.write(f"| {lab} | {v['dispatches']} | {v['fetch_bytes'] / 1e6:.3f} | {v['write_bytes'] / 1e6:.3f} |\n")
@@ -152,7 +154,12 @@ if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "stats":
         summarize_kernel_stats(sys.argv[2], sys.argv[3], sys.argv[4], *sys.argv[5:6])
     elif len(sys.argv) >= 2 and sys.argv[1] == "counters":
-        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+        extra = {}
+        if len(sys.argv) >= 8:
+            extra["title"] = sys.argv[7]
+        if len(sys.argv) >= 9:
+            extra["sources"] = tuple(sys.argv[8].split(","))
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], **extra)
     else:
         print(__doc__)
         sys.exit(2)
