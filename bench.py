@@ -28,20 +28,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-FFN µs/layer + HBM GB/s on touched bytes, batch 1, OPT-175B shape @5%"
 PEAK_HBM_GBS = 8000.0
-KERNELS = ["pred_down", "pred_up", "select_hist", "select_finish", "gather_up",
-           "gather_down", "reduce_partials"]
+FFN_SEPARATE = ["gather_up", "gather_down", "reduce_partials"]
 
 
-def layer_kernels(f, k):
+def layer_kernels(f, k, skip=False):
     """Kernels of csf_sparse_ffn_layer for one token: top-k over 20000 or more scores runs as
     two kernels (histogram, then classify, rank and emit), a smaller one as one, and up to 1024
-    scores are selected inside the predictor's up-projection kernel."""
+    scores are selected inside the predictor's up-projection kernel.  The gathered FFN is one
+    kernel (up rows, down rows and the reduction handed over inside it), or three with the
+    post-gate skip."""
+    ffn = FFN_SEPARATE if skip else ["ffn_fused"]
     if k is not None and k > 0 and f >= 20000:
-        return KERNELS
+        return ["pred_down", "pred_up", "select_hist", "select_finish"] + ffn
     if f <= 1024:     # scores and selection in one kernel
-        return ["pred_down", "pred_up_select", "gather_up", "gather_down", "reduce_partials"]
-    return ["pred_down", "pred_up", "select_topk" if k is not None else "select_threshold",
-            "gather_up", "gather_down", "reduce_partials"]
+        return ["pred_down", "pred_up_select"] + ffn
+    return ["pred_down", "pred_up", "select_topk" if k is not None else "select_threshold"] + ffn
+
+
+KERNELS = layer_kernels(49152, 2458)
 
 
 def log(msg):
@@ -195,9 +199,7 @@ def main():
         "pred_up": f * r * es + r * 4 + f * 4,
         "select_hist": f * 4,
         "select_finish": f * 4 + k * 4,
-        "gather_up": k * d * es + d * es + k * 4 + k * 4,
-        "gather_down": k * d * es + k * 8,
-        "reduce_partials": 0,
+        "ffn_fused": 2 * k * d * es + d * es + k * 4 + d * 4,
     }
     dom = max(KERNELS, key=lambda n: per_kernel[n]["avg_us"])
     dom_gbs = kernel_bytes[dom] / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
@@ -644,7 +646,7 @@ def silu_functional_leg(args, dev):
         for skip in (False, True):
             set_skip(skip)
             n = 50
-            names = layer_kernels(f, cfg.k)
+            names = layer_kernels(f, cfg.k, skip)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
                    for _ in range(n)]
             for row in evs:

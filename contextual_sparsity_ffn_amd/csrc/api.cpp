@@ -159,8 +159,12 @@ FfnWs ffn_ws(int B, int d, int dtype, int max_count)
     return w;
 }
 
+// counters of the one-kernel gathered FFN, rounded so that the selection's counter block that
+// follows them starts 256-byte aligned: one clear covers both
+int fused_sync_words() { return (csf::ffn_fused_sync_words() + 63) / 64 * 64; }
+
 struct LayerWs {
-    size_t a, scores, idx, count, sel, ffn, total;
+    size_t a, scores, idx, count, sync, sel, ffn, total;
 };
 LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
 {
@@ -169,7 +173,8 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
     w.scores = w.a + round_up((size_t)csf::kMaxPredSplit * r * sizeof(float));
     w.idx = w.scores + round_up((size_t)f * sizeof(float));
     w.count = w.idx + round_up((size_t)f * sizeof(int32_t));
-    w.sel = w.count + round_up(sizeof(int32_t));
+    w.sync = w.count + round_up(sizeof(int32_t));
+    w.sel = w.sync + (size_t)fused_sync_words() * sizeof(uint32_t);
     w.ffn = w.sel + round_up((size_t)csf::select_wide_ws_words(f) * sizeof(uint32_t));
     w.total = w.ffn + ffn_ws(1, d, dtype, max_count).total;
     return w;
@@ -673,8 +678,15 @@ int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const
 
     const bool wide = k >= 0 && csf::select_wide_used(1, f, k);
     uint32_t *selws = reinterpret_cast<uint32_t *>(at(ws, w.sel));
-    hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
-                                         wide ? csf::select_wide_zero_words() : 0);
+    // the first kernel clears the gathered FFN's counters and, for the many-workgroup selection,
+    // its histogram (the two blocks are adjacent), and marks the FFN's h slots unwritten
+    uint32_t *sync = reinterpret_cast<uint32_t *>(at(ws, w.sync));
+    FfnWs fw = ffn_ws(1, d, dtype, max_count);
+    const bool fused = !skip_zero;
+    hipError_t e = csf::launch_pred_down(
+        dtype, x, 1, d, V, r, a, st, trp, sync,
+        fused_sync_words() + (wide ? csf::select_wide_zero_words() : 0),
+        fused ? reinterpret_cast<uint32_t *>(at(ws, w.ffn + fw.h)) : nullptr, max_count);
     if (e != hipSuccess)
         return hip_status(e, "predictor down-projection launch");
     if (f <= csf::kSmallF && !bitmap) {
@@ -694,7 +706,6 @@ int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const
     if (e != hipSuccess)
         return hip_status(e, "predictor / selection launch");
 
-    FfnWs fw = ffn_ws(1, d, dtype, max_count);
     csf::FfnArgs fa;
     fa.dtype = dtype;
     fa.act = act;
@@ -716,6 +727,8 @@ int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
     fa.skip_zero = skip_zero;
     fa.gate_tau = gate_tau;
+    if (fused)
+        return hip_status(csf::launch_ffn_fused(fa, sync, st, trp), "sparse FFN launch");
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 

@@ -24,8 +24,13 @@ constexpr int kWave = 64;
 // Buckets of the score histogram that top-k selection starts from.
 constexpr int kScoreBuckets = 2048;
 
+// Counters that workgroups of one kernel add to and poll each sit in a 128-byte line of their own
+// (a line that is polled while it takes many atomic adds serialises both).
+constexpr int kLineWords = 32;
+
 // Monotone, non-decreasing map of a score to a bucket in [0, NB): uniform buckets over [0, 1]
-// (the range of a sigmoid); values below 0 (and NaN) land in bucket 0, values >= 1 in NB - 1.
+// (the range of a sigmoid); values below 0 (and NaN, the lowest in the selection's order) land in
+// bucket 0, values >= 1 in NB - 1.
 // Scaling by NB is exact (a power of two) and truncation of a non-negative float is its floor.
 template <int NB>
 __device__ __forceinline__ int score_bucket(float s)
@@ -126,6 +131,57 @@ struct BF16T {
     __device__ static __forceinline__ float widen_bits(uint16_t b) { return u2f((uint32_t)b << 16); }
 };
 
+// ---- hand-over between workgroups of one kernel -------------------------------------------------
+// Each XCD has its own L2, and the L2s are not coherent with one another.  Values that one
+// workgroup hands to another inside the same kernel therefore travel with the device-coherent
+// policy (agent-scope relaxed atomics: the store is written through to, and the load is served
+// from, the level all XCDs share), and a counter says when they are complete.  The producer
+// waits until its own coherent stores are acknowledged before it adds to the counter, so a
+// consumer that sees the count and then issues coherent loads reads the new values.  This costs
+// no L2 write-back or invalidate (which a release/acquire fence at agent scope would add).
+__device__ __forceinline__ void st_coherent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coherent_u32(const uint32_t *p)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed (stores acknowledged).
+__device__ __forceinline__ void wait_own_memory()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void count_add(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Polls of a hand-over counter before a waiting workgroup gives up (about 2^15 round trips of a
+// microsecond or less).  A consumer only ever waits for workgroups with lower indices, which the
+// hardware dispatches first, so the count always arrives; the bound only guarantees that a
+// kernel ends even if that did not hold: the waiter then records the failure in *err (read by
+// the tests) and goes on.
+constexpr uint32_t kSpinLimit = 1u << 15;
+// A value that marks "not written yet" in a buffer of float32 results handed over inside a kernel:
+// a NaN bit pattern (all ones) that float32 arithmetic on finite inputs never produces.
+constexpr uint32_t kHSentinel = 0xffffffffu;
+__device__ __forceinline__ void wait_count(const uint32_t *p, uint32_t target, uint32_t *err)
+{
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        if (ld_coherent_u32(p) >= target)
+            return;
+        __builtin_amdgcn_s_sleep(4);
+    }
+    count_add(err, 1u);
+}
+
 // Activation codes (the csf_act values): 0 ReLU, 1 ReGLU, 2 SiLU, 3 SwiGLU.  The gated forms
 // multiply the gate activation by the up projection W_up x.
 __host__ __device__ constexpr bool act_gated(int act) { return act == 1 || act == 3; }
@@ -138,13 +194,16 @@ __device__ __forceinline__ float gate_act(float p, int silu)
     return silu ? p / (1.0f + expf(-p)) : (p > 0.0f ? p : 0.0f);
 }
 
-// Order of the top-k selection: a monotone 32-bit key of a float32 score (-0.0 ranks as +0.0),
-// and a (score, index) pair as one integer, larger first: score descending, index ascending.
+// Order of the top-k selection: a monotone 32-bit key of a float32 score (-0.0 ranks as +0.0; a
+// NaN ranks below every number, -inf included), and a (score, index) pair as one integer, larger
+// first: score descending, index ascending.
 __device__ __forceinline__ uint32_t order_key(float s)
 {
     uint32_t u = __float_as_uint(s);
     if ((u & 0x7fffffffu) == 0u)
         u = 0u;
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -47,10 +47,12 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
 constexpr int kMaxPredSplit = 4;
 int pred_split(int r, int d, int dtype);
 // part[S][B][r] = split-K partial sums of V x_t (float32), S = pred_split(r, d, dtype).  zero
-// (optional): nzero words that the launch also clears, for a later kernel of the same call.
+// (optional): nzero words that the launch also clears, and fill: nfill words it sets to
+// kHSentinel, for a later kernel of the same call.
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
                             float *part, hipStream_t stream, Trace *trace = nullptr,
-                            uint32_t *zero = nullptr, int nzero = 0);
+                            uint32_t *zero = nullptr, int nzero = 0, uint32_t *fill = nullptr,
+                            int nfill = 0);
 // One token with at most kSmallF scores: s[f] = sigmoid(U relu(sum of the partials)) and, in the
 // same kernel, the selection: top-k (k >= 0) or s >= tau (k == -1) into the ascending list idx
 // and count (k, or the threshold count).  The lists equal those of the selection kernels.
@@ -91,7 +93,7 @@ hipError_t launch_select_threshold(const float *scores, int B, int f, float tau,
                                    int idx_stride, int32_t *count, uint32_t *bitmap,
                                    hipStream_t stream, Trace *trace = nullptr, int prefix = 0);
 int select_max_f();   // largest f the selection kernels accept
-// Top-k of a few tokens with many scores, spread over many workgroups (three kernels).  ws holds
+// Top-k of a few tokens with many scores, spread over many workgroups (two kernels).  ws holds
 // select_wide_ws_words(f) 32-bit words per token; its first select_wide_zero_words() words of each
 // token must be zero at the start: pass zeroed = false to have this launch clear them.
 bool select_wide_used(int B, int f, int k);
@@ -128,6 +130,14 @@ int ffn_num_slices(int d, int dtype);
 int ffn_max_count();   // longest active list (and widest dense layer) the FFN kernels take
 int ffn_num_chunks(int d, int dtype, int max_count);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
+// One token (B == 1, no skip) in one kernel: the up rows, the down rows and the reduction as
+// roles of one launch, handing h and the partial rows over inside it (bit-identical y).  When
+// the kernel starts, a.h[0, max_count) must hold kHSentinel and sync (ffn_fused_sync_words()
+// words) must be zero: an earlier kernel of the same call writes them.  The last counter line
+// counts waits that gave up (0 in a correct run).
+int ffn_fused_sync_words();
+hipError_t launch_ffn_fused(const FfnArgs &a, uint32_t *sync, hipStream_t stream,
+                            Trace *trace = nullptr);
 // The down projection and reduction alone, over a list whose h values are already in a.h.
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 // y[t][col] = sum over chunks q, in order, of part[t][q][col] (part is [B][nchunk][D] float32).

@@ -29,13 +29,16 @@ template <class T, int MX, int TG, int R>
 __global__ __launch_bounds__(256) void k_pred_down(const u32x4 *__restrict__ V,
                                                    const u32x4 *__restrict__ x, int C, int r,
                                                    int B, int S, float *__restrict__ part,
-                                                   uint32_t *__restrict__ zero, int nzero)
+                                                   uint32_t *__restrict__ zero, int nzero,
+                                                   uint32_t *__restrict__ fill, int nfill)
 {
     __shared__ float red[4][R * TG];
-    // workgroup 0 also clears a caller's counter block for a later kernel of the same call
-    if (zero && blockIdx.x == 0)
-        for (int i = threadIdx.x; i < nzero; i += 256)
-            zero[i] = 0u;
+    // the workgroups also prepare blocks of a caller's workspace for a later kernel of the same
+    // call: counters cleared, hand-over slots marked unwritten
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nzero; i += gridDim.x * 256)
+        zero[i] = 0u;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nfill; i += gridDim.x * 256)
+        fill[i] = kHSentinel;
     const int i0 = (blockIdx.x / S) * R, sp = blockIdx.x % S;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int cper = (C + S - 1) / S;
@@ -376,6 +379,8 @@ struct DownArgs {
     float *a;
     uint32_t *zero;
     int nzero;
+    uint32_t *fill;
+    int nfill;
 };
 
 template <class T, int MX, int R>
@@ -385,9 +390,9 @@ hipError_t down_r(const DownArgs &g, hipStream_t st, Trace *tr)
     const dim3 grid((g.r + R - 1) / R * g.S);
     if (g.B == 1)
         return launch(k_pred_down<T, MX, 1, R>, grid, dim3(256), st, tr, V, x, g.C, g.r, g.B, g.S,
-                      g.a, g.zero, g.nzero);
+                      g.a, g.zero, g.nzero, g.fill, g.nfill);
     return launch(k_pred_down<T, MX, 8, R>, grid, dim3(256), st, tr, V, x, g.C, g.r, g.B, g.S,
-                  g.a, g.zero, g.nzero);
+                  g.a, g.zero, g.nzero, g.fill, g.nfill);
 }
 
 // Two rows per workgroup halve the re-reads of x when that still leaves >= 512 workgroups.
@@ -529,9 +534,11 @@ int pred_split(int r, int d, int dtype)
 }
 
 hipError_t launch_pred_down(int dtype, const void *x, int B, int d, const void *V, int r,
-                            float *a, hipStream_t st, Trace *tr, uint32_t *zero, int nzero)
+                            float *a, hipStream_t st, Trace *tr, uint32_t *zero, int nzero,
+                            uint32_t *fill, int nfill)
 {
-    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a, zero, nzero};
+    DownArgs g{x, B, d / (dtype == 0 ? 4 : 8), V, r, pred_split(r, d, dtype), a,
+               zero, zero ? nzero : 0, fill, fill ? nfill : 0};
     if (dtype == 0) return down_t<F32T>(g, st, tr);
     if (dtype == 1) return down_t<F16T>(g, st, tr);
     return down_t<BF16T>(g, st, tr);

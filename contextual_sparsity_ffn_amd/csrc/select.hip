@@ -35,8 +35,9 @@ constexpr int kMaxWords = 2048;            // bitmap words held in LDS: f <= 655
 constexpr int kMaxDirect = 512;            // candidates ranked by direct counting
 
 
-// Four consecutive scores j0..j0+3 of one row; positions past f read as NaN.  VEC: the row is
-// 16-byte aligned (f % 4 == 0), so a full quad is one 16-byte load.
+// Four consecutive scores j0..j0+3 of one row; positions past f read as NaN (callers test the
+// position, since a score may itself be NaN).  VEC: the row is 16-byte aligned (f % 4 == 0), so a
+// full quad is one 16-byte load.
 template <bool VEC>
 __device__ __forceinline__ float4 load_quad(const float *s, int j0, int f)
 {
@@ -117,6 +118,10 @@ __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ sco
     __shared__ uint32_t misc[8];   // 0: B*, 1: need, 2: candidate count, 3: digit, 4: krem
 
     const int t = threadIdx.x;
+    if (t == 0) {
+        misc[0] = 0u;
+        misc[1] = 0u;
+    }
     const float *s = scores + (size_t)token * f;
     const int words = (f + 31) / 32;
     int32_t *out = idx + (size_t)token * idx_stride;
@@ -152,7 +157,7 @@ __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ sco
         const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (e[q] == e[q])
+            if (i * kQuad + 4 * t + q < f)
                 atomicAdd(&hist[score_bucket<NB>(e[q])], 1u);
     }
     __syncthreads();
@@ -187,7 +192,7 @@ __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ sco
         uint32_t nib = 0u, cmask = 0u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int b = e[q] == e[q] ? score_bucket<NB>(e[q]) : -1;
+            const int b = i * kQuad + 4 * t + q < f ? score_bucket<NB>(e[q]) : -1;
             nib |= (b > bstar ? 1u : 0u) << q;
             cmask |= (b == bstar ? 1u : 0u) << q;
         }
@@ -327,10 +332,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(const float *__rest
 //                    slice; a block scan places the slice's indices (ascending).  With more than
 //                    kWideMaxCand candidates (heavy ties) workgroup 0 runs topk_one_workgroup
 //                    instead and the others exit.
-// A score's own membership is tested on the score itself: with uniform buckets over [0, 1] and an
-// exact power-of-two scale, bucket(v) > B* exactly when v >= (B*+1)/NB.  Everything else is
-// integer arithmetic on the same bucket map and order keys, so the list equals the one-workgroup
-// result bit for bit.
+// Everything is integer arithmetic on the same bucket map and order keys (a NaN score sits in
+// bucket 0 with the lowest key), so the list equals the one-workgroup result bit for bit.
 constexpr int kWideSlice = 1024;
 constexpr int kWideMaxCand = 512;
 // Workspace of one token (32-bit words): the histogram [NB], then per slice above[NB + 1]
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256) void k_wide_hist(const float *__restrict__ sco
     uint32_t rk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        bk[i] = e[i] == e[i] ? score_bucket<NB>(e[i]) : -1;     // NaN: past f
+        bk[i] = j0 + i < f ? score_bucket<NB>(e[i]) : -1;        // -1: past f
         rk[i] = bk[i] >= 0 ? atomicAdd(&hist[bk[i]], 1u) : 0u;  // place inside the bucket
     }
     __syncthreads();
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
     const uint32_t *W = ws + (size_t)token * ws_stride;
     const int lim = slice * kWideSlice;
     const int j = lim + t;
-    const float mine = j < f ? s[j] : __builtin_nanf("");
+    const float mine = j < f ? s[j] : 0.0f;
     uint32_t c[BPT];
     uint32_t csum = 0;
 #pragma unroll
@@ -531,8 +534,8 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
             atomicOr(&keep_bits[(jc - lim) >> 5], 1u << (jc & 31));
     }
     __syncthreads();
-    const float hi_v = bstar == NB - 1 ? __builtin_nanf("") : (float)(bstar + 1) / (float)NB;
-    const bool sel = mine >= hi_v || ((keep_bits[t >> 5] >> (t & 31)) & 1u);
+    const bool sel = (j < f && score_bucket<NB>(mine) > bstar) ||
+                     ((keep_bits[t >> 5] >> (t & 31)) & 1u);
     // one scan for both counts, packed as (before << 11) | sel: the low field's exclusive prefix
     // (< 1024) is this thread's place among the slice's selected, the high field's block total
     // the selected neurons of the earlier slices (<= 65536, so the word does not overflow)

@@ -129,6 +129,46 @@ def test_select_threshold_bit_exact(f):
                 assert np.array_equal(bm[t].cpu().numpy(), orc.to_bitmap(ref, f).view(np.int32))
 
 
+def _topk_nan_last(s, k):
+    """Top-k with the library's documented order for non-finite scores: a NaN ranks below every
+    number (-inf included); otherwise score descending, -0.0 equal to +0.0, lower index first."""
+    v = s.astype(np.float64)
+    order = sorted(range(len(v)), key=lambda j: (1, 0.0, j) if np.isnan(v[j]) else (0, -v[j] + 0.0, j))
+    return np.sort(np.array(order[:k], dtype=np.int64))
+
+
+@pytest.mark.parametrize("f", [3001, 49152])
+def test_select_topk_with_nan_scores(f):
+    """NaN scores (e.g. from non-finite inputs) never leave the list short or stale: both the
+    one-workgroup and the many-workgroup selections return exactly k neurons, NaN ranked last."""
+    g = torch.Generator().manual_seed(77 + f)
+    base = torch.rand(f, generator=g)
+    few = base.clone()
+    few[torch.rand(f, generator=g) < 0.1] = float("nan")
+    most = torch.full((f,), float("nan"))
+    keep = torch.randperm(f, generator=g)[: f // 50]
+    most[keep] = base[keep]
+    most[keep[:3]] = float("-inf")
+    for pname, sc in (("some-nan", few), ("mostly-nan", most)):
+        for k in (1, f // 20, f // 10, f // 2):
+            announce(f"select_topk NaN f={f} k={k} pattern={pname}")
+            S = torch.stack([sc, sc.flip(0)]).float().contiguous()
+            cnt = torch.empty(2, dtype=torch.int32, device=DEV)
+            idx = csf.select_topk(_dev(S), k, count=cnt)
+            torch.cuda.synchronize()
+            for t in range(2):
+                ref = _topk_nan_last(S[t].numpy(), k)
+                assert cnt[t].item() == k
+                assert np.array_equal(idx[t].cpu().numpy(), ref), (f, k, pname, t)
+            idx2, cnt2 = csf.select_threshold(_dev(S), 0.5)
+            torch.cuda.synchronize()
+            for t in range(2):
+                v = S[t].numpy()
+                ref = np.nonzero(v >= 0.5)[0]           # NaN compares false: never selected
+                n = cnt2[t].item()
+                assert n == len(ref) and np.array_equal(idx2[t, :n].cpu().numpy(), ref)
+
+
 FFN_CASES = [
     ("c0-f32", wl.TINY_F32, 102),
     ("f16-ragged", wl.OPT175B.scaled(2600, 3001, 136), 150),
@@ -341,6 +381,56 @@ def test_layer_full_size_opt175b_shape():
     o = layer_to_orc(Ld)
     ix = _check_layer_token(Ld, o, x, cfg.k, None, "c1 full")
     assert len(ix) == cfg.k
+
+
+FUSED_CASES = [
+    ("c0", wl.TINY_F32, 3),
+    ("f16-ragged-topk", wl.OPT175B.scaled(2600, 3001, 136), 3),
+    ("bf16-reglu-threshold", wl.LLAMA_REGLU.scaled(4096, 1433, 256), 3),
+    ("f32-many-slices", wl.TINY_F32.scaled(8192, 5000, 64, k=1200), 2),
+]
+
+
+def _fused_vs_separate(Ld, x, k, tau, act, what):
+    """The layer's gathered FFN runs as one kernel that hands h and the partial rows from one
+    workgroup to another inside the launch; y must equal, bit for bit, the three-kernel
+    csf_sparse_ffn over the same list (same sums in the same order)."""
+    f = Ld.cfg.f
+    idx = torch.empty(f, dtype=torch.int32, device=DEV)
+    count = torch.empty(1, dtype=torch.int32, device=DEV)
+    y = csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k, tau=tau, act=act,
+                             idx=idx, count=count)
+    # the same list length bound (k, or f for a threshold with the count on the device), so the
+    # same split of the down projection into chunks
+    mc = k if k is not None else f
+    lst = idx[:mc].reshape(1, mc)
+    ys = csf.sparse_ffn(x.reshape(1, -1), Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, lst, act=act,
+                        count=None if k is not None else count, max_count=mc)
+    torch.cuda.synchronize()
+    assert int(count.item()) > 0, what
+    assert torch.equal(y, ys.reshape(-1)), what
+
+
+@pytest.mark.parametrize("name,cfg,ntok", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_layer_one_kernel_ffn_is_bit_identical(name, cfg, ntok):
+    Ld = _to_dev_layer(_layer(cfg))
+    X = wl.make_tokens(cfg, ntok)
+    for t in range(ntok):
+        announce(f"one-kernel FFN {name} token {t}")
+        _fused_vs_separate(Ld, _dev(X[t]), cfg.k, cfg.tau if cfg.k is None else None, cfg.act,
+                           f"{name}/{t}")
+
+
+def test_layer_one_kernel_ffn_full_size_repeated():
+    """The headline shape, many calls back to back (the counters are cleared by each call's
+    first kernel): every y bit-identical to the three-kernel form."""
+    cfg = wl.OPT175B
+    Ld = wl.make_layer(cfg, device=DEV)
+    X = wl.make_tokens(cfg, 4, device=DEV)
+    for rep in range(3):
+        for t in range(4):
+            announce(f"one-kernel FFN c1 rep {rep} token {t}")
+            _fused_vs_separate(Ld, X[t], cfg.k, None, cfg.act, f"c1 {rep}/{t}")
 
 
 # ---- post-gate zero-skip: rows with h = 0 are not read; y is the same up to summation order --------
