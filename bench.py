@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cp
 """
 import argparse
 import ctypes
+import functools
 import json
 import math
 import os
@@ -46,6 +47,13 @@ def layer_kernels(f, k, skip=False):
 
 
 KERNELS = layer_kernels(49152, 2458)
+
+
+def _entry(name):
+    """A C entry point with the default handle of the current device bound as its first
+    argument (every step of the path runs in the library; this only marshals)."""
+    from contextual_sparsity_ffn_amd import _lib
+    return functools.partial(getattr(_lib.lib, name), _lib.context().handle)
 
 
 def log(msg):
@@ -128,7 +136,7 @@ def main():
                 vp(ws.data_ptr()), ws_bytes, vp(stream.cuda_stream))
 
     plan = [call_args(s % args.layers, (s * 7) % args.tokens) for s in range(args.layers * args.tokens)]
-    fn = _lib.lib.csf_sparse_ffn_layer
+    fn = _entry("csf_sparse_ffn_layer")
 
     def run(n, offset=0):
         for s in range(n):
@@ -226,7 +234,7 @@ def main():
     dws_bytes = csf.workspace_size(_lib.OP_DENSE_FFN, 1, d, f, 0, f, code)
     dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
     hd = torch.empty(f, dtype=torch.float32, device=dev)
-    dfn = _lib.lib.csf_dense_ffn
+    dfn = _entry("csf_dense_ffn")
 
     def dense_call(l, t, h_out=None):
         L = layers[l]
@@ -435,7 +443,7 @@ def zero_skip_gated_leg(args, dev):
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
     hd = torch.empty(f, dtype=torch.float32, device=dev)
     vp = ctypes.c_void_p
-    fn = _lib.lib.csf_sparse_ffn_layer
+    fn = _entry("csf_sparse_ffn_layer")
 
     def call(l, t, idx_out=None, cnt_out=None):
         L = layers[l]
@@ -519,7 +527,7 @@ def silu_functional_leg(args, dev):
     ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
     y = torch.empty(d, dtype=torch.float32, device=dev)
     vp = ctypes.c_void_p
-    fn = _lib.lib.csf_sparse_ffn_layer
+    fn = _entry("csf_sparse_ffn_layer")
     ks = [f // 4, cfg.k, 3 * f // 4]
 
     def call(l, t, k, y_out=y, idx_out=None):
@@ -616,7 +624,7 @@ def silu_functional_leg(args, dev):
     L0 = layers[0]
     dws_b = csf.workspace_size(_lib.OP_DENSE_FFN, 1, d, f, 0, f, code)
     dws = torch.empty(dws_b, dtype=torch.uint8, device=dev)
-    dfn = _lib.lib.csf_dense_ffn
+    dfn = _entry("csf_dense_ffn")
 
     def dense_step(s):
         L = layers[s % nl]
@@ -706,7 +714,7 @@ def attention_leg(args, dev):
     y = torch.empty(d, dtype=torch.float32, device=dev)
     heads = torch.empty(H, dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int32, device=dev)
-    lfn, dfn = _lib.lib.csf_sparse_attention_layer, _lib.lib.csf_sparse_attention_decode
+    lfn, dfn = _entry("csf_sparse_attention_layer"), _entry("csf_sparse_attention_decode")
 
     def reset():
         for L in layers:
@@ -856,7 +864,7 @@ def static_locality_leg(args, dev):
     idx = torch.empty(f, dtype=torch.int32, device=dev)
     H_all = torch.empty(1, f, dtype=torch.float32, device=dev)
     vp = ctypes.c_void_p
-    fplain, fhot = _lib.lib.csf_sparse_ffn_layer, _lib.lib.csf_sparse_ffn_layer_hot
+    fplain, fhot = _entry("csf_sparse_ffn_layer"), _entry("csf_sparse_ffn_layer_hot")
 
     def call_plain(l, t, idx_out=None):
         L = plain[l]
@@ -930,8 +938,8 @@ def batched_union_leg(args, dev):
     X = wl.make_clustered_tokens(cfg, ntok, device=dev)
     stream = torch.cuda.current_stream(dev)
     vp = ctypes.c_void_p
-    fn = _lib.lib.csf_sparse_ffn_batched_layer
-    ufn = _lib.lib.csf_sparse_ffn_batched_union
+    fn = _entry("csf_sparse_ffn_batched_layer")
+    ufn = _entry("csf_sparse_ffn_batched_union")
     words = (f + 31) // 32
     full_bm = torch.full((32, words), -1, dtype=torch.int32, device=dev)
     full_bm[:, -1] = (1 << (f % 32)) - 1 if f % 32 else -1

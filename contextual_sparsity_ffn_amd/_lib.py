@@ -31,7 +31,7 @@ _STATUS = {0: "CSF_OK", 1: "CSF_ERR_INVALID_ARG", 2: "CSF_ERR_UNSUPPORTED",
            3: "CSF_ERR_MISALIGNED", 4: "CSF_ERR_WORKSPACE_TOO_SMALL", 5: "CSF_ERR_HIP"}
 
 EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_workspace_size",
-           "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
+           "csf_create", "csf_destroy", "csf_get_device_info", "csf_predict_active", "csf_select_topk", "csf_select_threshold", "csf_sparse_ffn",
            "csf_dense_ffn", "csf_sparse_ffn_layer", "csf_sparse_ffn_layer_hot",
            "csf_sparse_ffn_batched_union",
            "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
@@ -65,33 +65,40 @@ def _load():
     L.csf_last_error.restype = ctypes.c_char_p
     L.csf_last_error.argtypes = []
     L.csf_workspace_size.restype = sz
-    L.csf_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
-    L.csf_predict_active.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
-    L.csf_select_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
-    L.csf_select_threshold.argtypes = [vp, i32, i32, flt, vp, vp, vp, vp, sz, vp]
-    L.csf_sparse_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32,
+    L.csf_workspace_size.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
+    L.csf_create.argtypes = [ctypes.POINTER(vp), i32]
+    L.csf_destroy.argtypes = [vp]
+    L.csf_get_device_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    # every entry point below takes the handle first
+    L.csf_predict_active.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
+    L.csf_select_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.csf_select_threshold.argtypes = [vp, vp, i32, i32, flt, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32,
                                  vp, vp, vp, sz, vp]
-    L.csf_dense_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.csf_set_trace_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
-    L.csf_set_ffn_flags.argtypes = [i32]
-    L.csf_set_ffn_gate_threshold.argtypes = [flt]
-    L.csf_sparse_ffn_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
-                                       flt, vp, vp, vp, vp, vp, sz, vp]
-    L.csf_sparse_ffn_layer_hot.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
-                                           i32, flt, vp, vp, vp, vp, vp, sz, vp]
-    L.csf_sparse_ffn_batched_union.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
-                                               i32, i32, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
-    L.csf_sparse_ffn_batched_layer.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
-                                               vp, vp, i32, flt, i32, i32, vp, vp, vp,
+    L.csf_dense_ffn.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                vp]
+    L.csf_set_trace_events.argtypes = [vp, ctypes.POINTER(ctypes.c_void_p), i32]
+    L.csf_set_ffn_flags.argtypes = [vp, i32]
+    L.csf_set_ffn_gate_threshold.argtypes = [vp, flt]
+    L.csf_sparse_ffn_layer.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       i32, flt, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn_layer_hot.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                           i32, i32, flt, vp, vp, vp, vp, vp, sz, vp]
+    L.csf_sparse_ffn_batched_union.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                               vp, i32, i32, vp, vp, ctypes.POINTER(i32), vp, sz,
+                                               vp]
+    L.csf_sparse_ffn_batched_layer.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                               vp, vp, vp, i32, flt, i32, i32, vp, vp, vp,
                                                ctypes.POINTER(i32), vp, sz, vp]
-    L.csf_stack_forward.argtypes = [ctypes.POINTER(LayerWeights), i32, i32, i32, i32, i32, i32,
-                                    vp, i32, i32, i32, flt, i32, flt, vp, vp, vp, vp, vp, sz, vp,
-                                    vp]
-    L.csf_sparse_attention_decode.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
-                                              vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
-    L.csf_sparse_attention_layer.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
-                                             vp, vp, vp, vp, i32, vp, i32, flt, i32, vp, vp, vp, vp,
-                                             vp, vp, sz, vp]
+    L.csf_stack_forward.argtypes = [vp, ctypes.POINTER(LayerWeights), i32, i32, i32, i32, i32,
+                                    i32, vp, i32, i32, i32, flt, i32, flt, vp, vp, vp, vp, vp, sz,
+                                    vp, vp]
+    L.csf_sparse_attention_decode.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp,
+                                              sz, vp]
+    L.csf_sparse_attention_layer.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, i32, vp, i32, flt, i32, vp,
+                                             vp, vp, vp, vp, vp, sz, vp]
     L.csf_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     for name in EXPORTS[4:]:
         getattr(L, name).restype = i32
@@ -100,6 +107,77 @@ def _load():
 
 
 lib = _load()
+
+
+# ------------------------------------------------------------------------------------------------
+# handles
+# ------------------------------------------------------------------------------------------------
+class Context:
+    """A library handle (csf_create) for one HIP device: it holds the device's facts, the
+    gathered FFN's options, the per-kernel timing hook and the stack's events and graph.  Use it
+    from one thread at a time; `close()` (or garbage collection) destroys it."""
+
+    def __init__(self, device=0):
+        index = device.index if isinstance(device, torch.device) else int(device)
+        if index is None:
+            index = torch.cuda.current_device()
+        h = ctypes.c_void_p()
+        with torch.cuda.device(index):
+            _check(lib.csf_create(ctypes.byref(h), index))
+        self.handle = h
+        self.device = torch.device("cuda", index)
+        cus = ctypes.c_int(0)
+        _check(lib.csf_get_device_info(h, None, ctypes.byref(cus)))
+        self.compute_units = cus.value
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            lib.csf_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_ffn_flags(self, flags):
+        _check(lib.csf_set_ffn_flags(self.handle, int(flags)))
+
+    def set_ffn_gate_threshold(self, tau):
+        _check(lib.csf_set_ffn_gate_threshold(self.handle, float(tau)))
+
+    def set_trace_events(self, events):
+        n = len(events)
+        arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check(lib.csf_set_trace_events(self.handle, arr, n))
+
+
+_default_contexts = {}
+
+
+def context(device=None) -> Context:
+    """The default handle of a device (created on first use): the one the functions below use
+    when no ctx is given."""
+    if device is None:
+        index = torch.cuda.current_device()
+    elif isinstance(device, torch.device):
+        index = device.index if device.index is not None else torch.cuda.current_device()
+    else:
+        index = int(device)
+    ctx = _default_contexts.get(index)
+    if ctx is None:
+        ctx = Context(index)
+        _default_contexts[index] = ctx
+    return ctx
+
+
+def _h(ctx, dev):
+    """The handle for a call on device `dev`; that device is made current if it is not."""
+    c = ctx if ctx is not None else context(dev)
+    if torch.cuda.current_device() != c.device.index:
+        torch.cuda.set_device(c.device)
+    return c.handle
 
 
 # ------------------------------------------------------------------------------------------------
@@ -145,8 +223,13 @@ def _tensor(t, name, dtype=None, shape=None, device=None, optional=False):
     return t
 
 
-def workspace_size(op, B, d, f, r=0, max_count=0, dtype=F16) -> int:
-    return int(lib.csf_workspace_size(op, B, d, f, r, max_count, dtype))
+def workspace_size(op, B, d, f, r=0, max_count=0, dtype=F16, ctx=None) -> int:
+    """Workspace bytes of an operation; with ctx (a Context, or a device for its default
+    context) sized for that handle's device, else for any device."""
+    if ctx is not None and not isinstance(ctx, Context):
+        ctx = context(ctx)
+    return int(lib.csf_workspace_size(ctx.handle if ctx is not None else None, op, B, d, f, r,
+                                      max_count, dtype))
 
 
 def _workspace(nbytes, device, ws=None):
@@ -169,7 +252,7 @@ def k_from_ratio(f: int, ratio: float) -> int:
 # ------------------------------------------------------------------------------------------------
 # entry points (same names as the C ABI without the csf_ prefix)
 # ------------------------------------------------------------------------------------------------
-def predict_active(x, V, U, scores=None, ws=None):
+def predict_active(x, V, U, scores=None, ws=None, ctx=None):
     """Sigmoid scores [B, f] (float32) of the low-rank predictor for x [B, d] (or [d])."""
     squeeze = x.dim() == 1
     X = x.unsqueeze(0) if squeeze else x
@@ -188,12 +271,12 @@ def predict_active(x, V, U, scores=None, ws=None):
         raise ValueError(f"scores must hold {B}x{f} values")
     code = dtype_code(dt)
     w, wb = _workspace(workspace_size(OP_PREDICT, B, d, f, r, 0, code), dev, ws)
-    _check(lib.csf_predict_active(_ptr(X), B, d, _ptr(V), r, _ptr(U), f, code, _ptr(scores),
-                                  _ptr(w), wb, _stream(dev)))
+    _check(lib.csf_predict_active(_h(ctx, dev), _ptr(X), B, d, _ptr(V), r, _ptr(U), f, code,
+                                  _ptr(scores), _ptr(w), wb, _stream(dev)))
     return scores.view(f) if squeeze else scores.view(B, f)
 
 
-def select_topk(scores, k, idx=None, count=None, bitmap=None):
+def select_topk(scores, k, idx=None, count=None, bitmap=None, ctx=None):
     """Ascending top-k neuron lists [B, k] (int32); lower index wins ties."""
     squeeze = scores.dim() == 1
     S = scores.unsqueeze(0) if squeeze else scores
@@ -209,13 +292,13 @@ def select_topk(scores, k, idx=None, count=None, bitmap=None):
     _tensor(count, "count", dtype=torch.int32, device=dev, optional=True)
     _tensor(bitmap, "bitmap", dtype=torch.int32, device=dev, optional=True)
     w, wb = _workspace(workspace_size(OP_SELECT_TOPK, B, 1, f, 0, k), dev)
-    _check(lib.csf_select_topk(_ptr(S), B, f, k, _ptr(idx), _ptr(count), _ptr(bitmap), _ptr(w), wb,
-                               _stream(dev)))
+    _check(lib.csf_select_topk(_h(ctx, dev), _ptr(S), B, f, k, _ptr(idx), _ptr(count),
+                               _ptr(bitmap), _ptr(w), wb, _stream(dev)))
     out = idx.view(B, -1)[:, :k]
     return out[0] if squeeze else out
 
 
-def select_threshold(scores, tau, idx=None, count=None, bitmap=None):
+def select_threshold(scores, tau, idx=None, count=None, bitmap=None, ctx=None):
     """Every neuron with score >= tau: returns (idx [B, f] int32, count [B] int32), both on device."""
     squeeze = scores.dim() == 1
     S = scores.unsqueeze(0) if squeeze else scores
@@ -229,8 +312,8 @@ def select_threshold(scores, tau, idx=None, count=None, bitmap=None):
     _tensor(idx, "idx", dtype=torch.int32, shape=(B, f), device=dev)
     _tensor(count, "count", dtype=torch.int32, shape=(B,), device=dev)
     _tensor(bitmap, "bitmap", dtype=torch.int32, device=dev, optional=True)
-    _check(lib.csf_select_threshold(_ptr(S), B, f, float(tau), _ptr(idx), _ptr(count),
-                                    _ptr(bitmap), None, 0, _stream(dev)))
+    _check(lib.csf_select_threshold(_h(ctx, dev), _ptr(S), B, f, float(tau), _ptr(idx),
+                                    _ptr(count), _ptr(bitmap), None, 0, _stream(dev)))
     return (idx[0], count[0:1]) if squeeze else (idx, count)
 
 
@@ -248,7 +331,7 @@ def _ffn_weights(x, W1, b1, Wup, W2T, act):
 
 
 def sparse_ffn(x, W1, b1, Wup, W2T, idx, act=RELU, count=None, max_count=None, h=None, y=None,
-               ws=None):
+               ws=None, ctx=None):
     """y [B, d] float32 over each token's active list idx [B, stride] (int32, ascending)."""
     squeeze = x.dim() == 1
     X = x.unsqueeze(0) if squeeze else x
@@ -270,13 +353,13 @@ def sparse_ffn(x, W1, b1, Wup, W2T, idx, act=RELU, count=None, max_count=None, h
     _tensor(y, "y", dtype=torch.float32, device=dev)
     code = dtype_code(dt)
     w, wb = _workspace(workspace_size(OP_SPARSE_FFN, B, d, f, 0, max_count, code), dev, ws)
-    _check(lib.csf_sparse_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
-                              _ptr(W2T), _ptr(I), stride, _ptr(count), max_count, _ptr(h), _ptr(y),
-                              _ptr(w), wb, _stream(dev)))
+    _check(lib.csf_sparse_ffn(_h(ctx, dev), _ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1),
+                              _ptr(Wup), _ptr(W2T), _ptr(I), stride, _ptr(count), max_count,
+                              _ptr(h), _ptr(y), _ptr(w), wb, _stream(dev)))
     return y.view(d) if squeeze else y.view(B, d)
 
 
-def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
+def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None, ctx=None):
     """y [B, d] float32 over every neuron; h [B, f] (optional) receives every activation."""
     squeeze = x.dim() == 1
     X = x.unsqueeze(0) if squeeze else x
@@ -293,33 +376,32 @@ def dense_ffn(x, W1, b1, Wup, W2T, act=RELU, y=None, h=None, ws=None):
             raise ValueError(f"h must hold {B}x{f} values")
     code = dtype_code(dt)
     w, wb = _workspace(workspace_size(OP_DENSE_FFN, B, d, f, 0, f, code), dev, ws)
-    _check(lib.csf_dense_ffn(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1), _ptr(Wup),
-                             _ptr(W2T), _ptr(h), _ptr(y), _ptr(w), wb, _stream(dev)))
+    _check(lib.csf_dense_ffn(_h(ctx, dev), _ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1),
+                             _ptr(Wup), _ptr(W2T), _ptr(h), _ptr(y), _ptr(w), wb, _stream(dev)))
     return y.view(d) if squeeze else y.view(B, d)
 
 
-def set_ffn_flags(flags):
-    """Options of the gathered FFN for later calls on this thread (FFN_SKIP_ZERO_H or 0)."""
-    _check(lib.csf_set_ffn_flags(int(flags)))
+def set_ffn_flags(flags, ctx=None):
+    """Options of the gathered FFN for later calls with the handle (default: the current device's
+    default context): FFN_SKIP_ZERO_H or 0."""
+    (ctx or context()).set_ffn_flags(flags)
 
 
-def set_ffn_gate_threshold(tau):
-    """gate_tau of the post-gate skip for later calls on this thread (0 = exact zero-skip)."""
-    _check(lib.csf_set_ffn_gate_threshold(float(tau)))
+def set_ffn_gate_threshold(tau, ctx=None):
+    """gate_tau of the post-gate skip for later calls with the handle (0 = exact zero-skip)."""
+    (ctx or context()).set_ffn_gate_threshold(tau)
 
 
-def set_trace_events(events):
-    """Per-kernel timing hook: a list of up to 16 torch.cuda.Event(enable_timing=True) (or [] to
-    switch off); the i-th kernel of csf_sparse_ffn_layer gets events 2i (start) and 2i+1 (end),
-    recorded by the runtime at the kernel's own start and end.  torch creates the underlying HIP
-    event on its first record(), so record each event once beforehand."""
-    n = len(events)
-    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(e.cuda_event) for e in events])
-    _check(lib.csf_set_trace_events(arr, n))
+def set_trace_events(events, ctx=None):
+    """Per-kernel timing hook of a handle: a list of up to 16 torch.cuda.Event(enable_timing=True)
+    (or [] to switch off); the i-th kernel of csf_sparse_ffn_layer gets events 2i (start) and
+    2i+1 (end), recorded by the runtime at the kernel's own start and end.  torch creates the
+    underlying HIP event on its first record(), so record each event once beforehand."""
+    (ctx or context()).set_trace_events(events)
 
 
 def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=None, scores=None,
-                     idx=None, count=None, ws=None):
+                     idx=None, count=None, ws=None, ctx=None):
     """Predict, select (top-k if k is given, else threshold tau) and the sparse FFN for one token."""
     if (k is None) == (tau is None):
         raise ValueError("give exactly one of k (top-k) or tau (threshold)")
@@ -344,7 +426,8 @@ def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=No
     code = dtype_code(dt)
     max_count = f if kk < 0 else kk
     w, wb = _workspace(workspace_size(OP_LAYER, 1, d, f, r, max_count, code), dev, ws)
-    _check(lib.csf_sparse_ffn_layer(_ptr(x), d, f, r, act, code, _ptr(V), _ptr(U), _ptr(W1),
+    _check(lib.csf_sparse_ffn_layer(_h(ctx, dev), _ptr(x), d, f, r, act, code, _ptr(V), _ptr(U),
+                                    _ptr(W1),
                                     _ptr(b1), _ptr(Wup), _ptr(W2T), kk,
                                     float(tau if tau is not None else 0.0), _ptr(y), _ptr(scores),
                                     _ptr(idx), _ptr(count), _ptr(w), wb, _stream(dev)))
@@ -352,7 +435,7 @@ def sparse_ffn_layer(x, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU, y=No
 
 
 def sparse_ffn_batched_union(X, W1, b1, Wup, W2T, bitmaps, act=RELU, semantics=SEM_PER_TOKEN,
-                             path=PATH_AUTO, Y=None, union_count=None, ws=None):
+                             path=PATH_AUTO, Y=None, union_count=None, ws=None, ctx=None):
     """Sparse FFN of the B tokens X [B, d] reading the union of their sets once.
 
     bitmaps [B, ceil(f/32)] int32 (the bit patterns of csf_select_*'s bitmap output).  Returns
@@ -370,9 +453,11 @@ def sparse_ffn_batched_union(X, W1, b1, Wup, W2T, bitmaps, act=RELU, semantics=S
     _tensor(Y, "Y", dtype=torch.float32, shape=(B, d), device=dev)
     _tensor(union_count, "union_count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
     code = dtype_code(dt)
-    w, wb = _workspace(workspace_size(OP_BATCHED_UNION, B, d, f, 0, 0, code), dev, ws)
+    c = ctx if ctx is not None else context(dev)
+    w, wb = _workspace(workspace_size(OP_BATCHED_UNION, B, d, f, 0, 0, code, ctx=c), dev, ws)
     taken = ctypes.c_int(0)
-    _check(lib.csf_sparse_ffn_batched_union(_ptr(X), B, d, f, act, code, _ptr(W1), _ptr(b1),
+    _check(lib.csf_sparse_ffn_batched_union(_h(c, dev), _ptr(X), B, d, f, act, code, _ptr(W1),
+                                            _ptr(b1),
                                             _ptr(Wup), _ptr(W2T), _ptr(bitmaps), int(semantics),
                                             int(path), _ptr(Y), _ptr(union_count),
                                             ctypes.byref(taken), _ptr(w), wb, _stream(dev)))
@@ -381,7 +466,7 @@ def sparse_ffn_batched_union(X, W1, b1, Wup, W2T, bitmaps, act=RELU, semantics=S
 
 def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RELU,
                              semantics=SEM_PER_TOKEN, path=PATH_AUTO, Y=None, bitmaps=None,
-                             union_count=None, ws=None):
+                             union_count=None, ws=None, ctx=None):
     """Predict, select (top-k if k is given, else threshold tau) and the batched union FFN for
     the B tokens X [B, d].  Returns (Y [B, d] float32, path taken)."""
     if (k is None) == (tau is None):
@@ -404,10 +489,12 @@ def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RE
     _tensor(union_count, "union_count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
     code = dtype_code(dt)
     max_count = f if kk < 0 else kk
-    w, wb = _workspace(workspace_size(OP_BATCHED_LAYER, B, d, f, r, max_count, code), dev, ws)
+    c = ctx if ctx is not None else context(dev)
+    w, wb = _workspace(workspace_size(OP_BATCHED_LAYER, B, d, f, r, max_count, code, ctx=c), dev,
+                       ws)
     taken = ctypes.c_int(0)
     _check(lib.csf_sparse_ffn_batched_layer(
-        _ptr(X), B, d, f, r, act, code, _ptr(V), _ptr(U), _ptr(W1), _ptr(b1), _ptr(Wup), _ptr(W2T),
+        _h(c, dev), _ptr(X), B, d, f, r, act, code, _ptr(V), _ptr(U), _ptr(W1), _ptr(b1), _ptr(Wup), _ptr(W2T),
         kk, float(tau if tau is not None else 0.0), int(semantics), int(path), _ptr(Y),
         _ptr(bitmaps), _ptr(union_count), ctypes.byref(taken), _ptr(w), wb, _stream(dev)))
     return Y, taken.value
@@ -415,7 +502,7 @@ def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RE
 
 def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=True, eps=1e-6,
                   x_log=None, xhat_log=None, idx_log=None, count_log=None, side_stream=None,
-                  ws=None, graph=False):
+                  ws=None, graph=False, ctx=None):
     """Run x [B, d] (float32, updated in place) through the residual blocks `layers` (objects with
     V, U, W1, b1, Wup, W2T device tensors).  lookahead: each layer's set is predicted from the
     previous layer's input on `side_stream` (a torch.cuda.Stream; required).  graph: enqueue the
@@ -455,7 +542,7 @@ def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=T
     max_count = f if kk < 0 else kk
     w, wb = _workspace(workspace_size(OP_STACK, B, d, f, r, max_count, code), dev, ws)
     side = None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)
-    _check(lib.csf_stack_forward(arr, nl, d, f, r, act, code, _ptr(x), B,
+    _check(lib.csf_stack_forward(_h(ctx, dev), arr, nl, d, f, r, act, code, _ptr(x), B,
                                  (STACK_LOOKAHEAD if lookahead else STACK_SYNC) |
                                  (STACK_GRAPH if graph else 0), kk,
                                  float(tau if tau is not None else 0.0), 1 if norm else 0,
@@ -465,7 +552,7 @@ def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=T
 
 
 def sparse_ffn_layer_hot(x, V, U_cold, W1, b1, Wup, W2T, hot, k=None, tau=None, act=RELU, y=None,
-                         scores=None, idx=None, count=None, ws=None):
+                         scores=None, idx=None, count=None, ws=None, ctx=None):
     """One token through a hot-first layer: neurons 0 .. hot-1 always, plus the top-k (or >= tau)
     of the cold neurons scored by the predictor with up rows U_cold [f - hot, r]."""
     if (k is None) == (tau is None):
@@ -492,7 +579,8 @@ def sparse_ffn_layer_hot(x, V, U_cold, W1, b1, Wup, W2T, hot, k=None, tau=None, 
     _tensor(count, "count", dtype=torch.int32, shape=(1,), device=dev, optional=True)
     code = dtype_code(dt)
     w, wb = _workspace(workspace_size(OP_LAYER, 1, d, f, r, max_count, code), dev, ws)
-    _check(lib.csf_sparse_ffn_layer_hot(_ptr(x), d, f, r, act, code, _ptr(V), _ptr(U_cold),
+    _check(lib.csf_sparse_ffn_layer_hot(_h(ctx, dev), _ptr(x), d, f, r, act, code, _ptr(V),
+                                        _ptr(U_cold),
                                         _ptr(W1), _ptr(b1), _ptr(Wup), _ptr(W2T), hot, kk,
                                         float(tau if tau is not None else 0.0), _ptr(y),
                                         _ptr(scores), _ptr(idx), _ptr(count), _ptr(w), wb,
@@ -525,7 +613,7 @@ def _attn_weights(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens):
 
 
 def sparse_attention_decode(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, heads=None, count=None,
-                            kv_all=False, o=None, y=None, ws=None):
+                            kv_all=False, o=None, y=None, ws=None, ctx=None):
     """One decode step of multi-head attention over the heads in `heads` (int32 device list;
     None = every head, the dense step).  Kc, Vc [H, Tmax, dh] and lens [H] are updated in place.
     Returns y [d] float32."""
@@ -545,7 +633,8 @@ def sparse_attention_decode(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, heads=
     code = dtype_code(dt)
     w, wb = _workspace(attention_workspace_size(OP_ATTN_DECODE, d, H, dh, 0, Tmax, max_heads, code),
                        dev, ws)
-    _check(lib.csf_sparse_attention_decode(_ptr(x), d, H, dh, code, _ptr(Wq), _ptr(Wk), _ptr(Wv),
+    _check(lib.csf_sparse_attention_decode(_h(ctx, dev), _ptr(x), d, H, dh, code, _ptr(Wq),
+                                           _ptr(Wk), _ptr(Wv),
                                            _ptr(bq), _ptr(bk), _ptr(bv), _ptr(WoT), _ptr(Kc),
                                            _ptr(Vc), Tmax, _ptr(lens), _ptr(heads), _ptr(count),
                                            max_heads, 1 if kv_all else 0, _ptr(o), _ptr(y), _ptr(w),
@@ -555,7 +644,7 @@ def sparse_attention_decode(x, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, heads=
 
 def sparse_attention_layer(x, Vp, Up, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens, k=None, tau=None,
                            kv_all=False, scores=None, heads=None, count=None, o=None, y=None,
-                           ws=None):
+                           ws=None, ctx=None):
     """Head predictor, top-k (or >= tau) head selection and the decode step over the selected
     heads, for one token.  Returns y [d] float32."""
     if (k is None) == (tau is None):
@@ -579,7 +668,8 @@ def sparse_attention_layer(x, Vp, Up, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, lens,
     code = dtype_code(dt)
     w, wb = _workspace(attention_workspace_size(OP_ATTN_LAYER, d, H, dh, r, Tmax, max_heads, code),
                        dev, ws)
-    _check(lib.csf_sparse_attention_layer(_ptr(x), d, H, dh, r, code, _ptr(Vp), _ptr(Up), _ptr(Wq),
+    _check(lib.csf_sparse_attention_layer(_h(ctx, dev), _ptr(x), d, H, dh, r, code, _ptr(Vp),
+                                          _ptr(Up), _ptr(Wq),
                                           _ptr(Wk), _ptr(Wv), _ptr(bq), _ptr(bk), _ptr(bv),
                                           _ptr(WoT), _ptr(Kc), _ptr(Vc), Tmax, _ptr(lens), kk,
                                           float(tau if tau is not None else 0.0),

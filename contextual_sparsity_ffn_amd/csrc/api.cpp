@@ -8,19 +8,48 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
 #include <string>
 
 #include "../../include/csf.h"
 #include "common.hpp"
 #include "launch.hpp"
 
+// The state a handle owns: facts of its device (queried once), the gathered FFN's options, the
+// per-kernel timing hook, and what the stack keeps between calls (events, a capture stream, the
+// captured graph).  No tensor and no device memory.
+struct csf_context {
+    int device = 0;
+    int cus = 0;                  // compute units
+    int pred_up_grid = 0;         // persistent one-token up projection: 8 workgroups per CU
+    int pred_up_side_grid = 0;    // the look-ahead stack's side-stream copy: 4 per CU
+    int ffn_flags = 0;
+    float gate_tau = 0.0f;
+    hipEvent_t trace[16] = {};
+    int trace_n = 0;
+    hipEvent_t stack_ev[4] = {};  // look-ahead stack: input ready x2, selection ready x2
+    hipStream_t capture = nullptr;
+    uint64_t graph_key = 0;
+    hipGraphExec_t graph = nullptr;
+};
+
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_trace_events[16];
-thread_local int g_trace_n = 0;
-thread_local int g_ffn_flags = 0;
-thread_local float g_gate_tau = 0.0f;
+
+// Live handles: a destroyed handle (or any other pointer) is recognised as not a handle.
+std::mutex g_handles_mu;
+std::unordered_set<const csf_context *> g_handles;
+
+bool is_live(const csf_context *h)
+{
+    if (!h)
+        return false;
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    return g_handles.count(h) != 0;
+}
 
 int fail(int status, const char *fmt, ...)
 {
@@ -62,6 +91,43 @@ constexpr long kMaxPredChunks = 512;       // r: 16-byte chunks per row of U
         if (!(cond))                               \
             return fail(status, __VA_ARGS__);      \
     } while (0)
+
+// A handle is checked after every other argument (so host-side argument checks need none) and
+// before anything is enqueued: it must be live and belong to the current device.
+int check_handle(csf_handle h)
+{
+    if (!is_live(h))
+        return fail(CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle (csf_create)");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(CSF_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev != h->device)
+        return fail(CSF_ERR_INVALID_ARG, "the handle belongs to device %d but device %d is current",
+                    h->device, dev);
+    return CSF_OK;
+}
+
+#define CHECK_HANDLE(h)                                    \
+    do {                                                   \
+        int _s = check_handle(h);                          \
+        if (_s != CSF_OK)                                  \
+            return _s;                                     \
+    } while (0)
+
+// the timing hook of a handle (empty when off)
+csf::Trace make_trace(csf_handle h)
+{
+    csf::Trace tr;
+    if (h && h->trace_n > 0) {
+        tr.ev = h->trace;
+        tr.n = h->trace_n;
+    }
+    return tr;
+}
+
+// compute units a workspace is sized for: a live handle's device, or (no handle) any device
+int sizing_cus(csf_handle h) { return is_live(h) ? h->cus : 1 << 20; }
 
 int check_ptr(const void *p, const char *name, bool required)
 {
@@ -129,15 +195,18 @@ PredictWs predict_ws(int B, int r)
 // the predictor for B tokens: matrix cores for batches of 16-bit weights, else vector ALU.
 // zero (optional): nzero words the vector-ALU path clears on the way (*zeroed tells whether it
 // did), for a later kernel of the same call.
+// side: the look-ahead stack's second-stream copy (a smaller persistent grid).
 hipError_t enqueue_predict(int dtype, const void *x, int B, int d, const void *V, int r,
                            const void *U, int f, float *scores, float *ws, hipStream_t st,
-                           csf::Trace *tr, uint32_t *zero = nullptr, int nzero = 0,
-                           bool *zeroed = nullptr, int pu_grid = 0)
+                           csf::Trace *tr, const csf_context *h, bool side = false,
+                           uint32_t *zero = nullptr, int nzero = 0, bool *zeroed = nullptr)
 {
     if (zeroed)
         *zeroed = false;
     if (csf::pred_mfma_supported(dtype, B, d, r))
-        return csf::launch_predict_mfma(dtype, x, B, d, V, r, U, f, scores, ws, st, tr);
+        return csf::launch_predict_mfma(dtype, x, B, d, V, r, U, f, scores, ws, st, tr,
+                                        2 * h->cus);
+    const int pu_grid = side ? h->pred_up_side_grid : h->pred_up_grid;
     if (zeroed)
         *zeroed = zero != nullptr;
     hipError_t e = csf::launch_pred_down(dtype, x, B, d, V, r, ws, st, tr, zero, nzero);
@@ -187,7 +256,7 @@ constexpr int kMfmaMinBatch = 2;   // measured: from two tokens on the matrix-co
 struct UnionWs {
     size_t ulist, ucount, h, hlo, partials, total;
 };
-UnionWs union_ws(int B, int d, int f, int dtype)
+UnionWs union_ws(int B, int d, int f, int dtype, int cus)
 {
     UnionWs w;
     const size_t hs = csf::union_h_stride(f);
@@ -200,8 +269,8 @@ UnionWs union_ws(int B, int d, int f, int dtype)
     const size_t h32_end = w.h + round_up(Bn * hs * sizeof(float));
     const size_t hlo_end = w.hlo + round_up(Bn * hs * sizeof(uint16_t));
     w.partials = h32_end > hlo_end ? h32_end : hlo_end;
-    int nch = csf::union_num_chunks(0, d, dtype, f);
-    const int nm = csf::union_num_chunks(1, d, dtype, f);
+    int nch = csf::union_num_chunks(0, d, dtype, f, cus);
+    const int nm = csf::union_num_chunks(1, d, dtype, f, cus);
     if (nm > nch)
         nch = nm;
     w.total = w.partials + round_up(Bn * (size_t)nch * d * sizeof(float));
@@ -211,7 +280,7 @@ UnionWs union_ws(int B, int d, int f, int dtype)
 struct BatchedLayerWs {
     size_t a, scores, idx, count, bitmap, uni, total;
 };
-BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int dtype)
+BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int dtype, int cus)
 {
     BatchedLayerWs w;
     const size_t Bn = B > 0 ? (size_t)B : 1;
@@ -221,7 +290,7 @@ BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int d
     w.count = w.idx + round_up(Bn * (max_count > 0 ? max_count : 1) * sizeof(int32_t));
     w.bitmap = w.count + round_up(Bn * sizeof(int32_t));
     w.uni = w.bitmap + round_up(Bn * ((f + 31) / 32) * sizeof(uint32_t));
-    w.total = w.uni + union_ws(B, d, f, dtype).total;
+    w.total = w.uni + union_ws(B, d, f, dtype, cus).total;
     if (B == 1) {
         // a batch of one on the gather path runs the single-token layer in this workspace
         const size_t one = layer_ws(d, f, r, max_count, dtype).total;
@@ -354,9 +423,10 @@ bool choose_union_path(int path, int dtype, int d, int B)
 int enqueue_union(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
                   const float *b1, const void *Wup, const void *W2T, const uint32_t *bitmaps,
                   int semantics, bool mfma, float *Y, int32_t *union_count, void *ws,
-                  const UnionWs &w, hipStream_t st, csf::Trace *tr)
+                  const UnionWs &w, int cus, hipStream_t st, csf::Trace *tr)
 {
     csf::UnionArgs a;
+    a.cus = cus;
     a.dtype = dtype;
     a.act = act;
     a.per_token = semantics == CSF_SEM_PER_TOKEN;
@@ -382,64 +452,45 @@ int enqueue_union(const void *X, int B, int d, int f, int act, int dtype, const 
     return hip_status(csf::launch_union_ffn(a, st, tr), "batched union FFN launch");
 }
 
-// Four events per device and calling thread for the look-ahead stack: "layer input ready" and
-// "selection ready", each double-buffered across consecutive layers.  Created once, on first use.
-int stack_events(hipEvent_t ev_x[2], hipEvent_t ev_s[2])
+// The look-ahead stack's four events ("layer input ready" and "selection ready", each
+// double-buffered across consecutive layers), created on the handle's first use of them.
+int stack_events(csf_handle h, hipEvent_t ev_x[2], hipEvent_t ev_s[2])
 {
-    constexpr int kMaxDevices = 64;
-    thread_local hipEvent_t cache[kMaxDevices][4] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return hip_status(e, "hipGetDevice");
-    if (dev < 0 || dev >= kMaxDevices)
-        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond the library's limit", dev);
     for (int i = 0; i < 4; ++i) {
-        if (!cache[dev][i]) {
-            e = hipEventCreateWithFlags(&cache[dev][i], hipEventDisableTiming);
+        if (!h->stack_ev[i]) {
+            hipError_t e = hipEventCreateWithFlags(&h->stack_ev[i], hipEventDisableTiming);
             if (e != hipSuccess) {
-                cache[dev][i] = nullptr;
+                h->stack_ev[i] = nullptr;
                 return hip_status(e, "hipEventCreateWithFlags");
             }
         }
     }
-    ev_x[0] = cache[dev][0];
-    ev_x[1] = cache[dev][1];
-    ev_s[0] = cache[dev][2];
-    ev_s[1] = cache[dev][3];
+    ev_x[0] = h->stack_ev[0];
+    ev_x[1] = h->stack_ev[1];
+    ev_s[0] = h->stack_ev[2];
+    ev_s[1] = h->stack_ev[3];
     return CSF_OK;
 }
 
-// One captured stack per calling thread, replayed while the arguments stay the same.  It is
-// captured on a stream of the library's own (one per device and thread; the caller's stream may
-// be the legacy default stream, which cannot be captured) and launched on the caller's stream.
-struct StackGraph {
-    uint64_t key = 0;
-    hipGraphExec_t exec = nullptr;
-};
-thread_local StackGraph g_stack_graph;
-
-int capture_stream(int dev, hipStream_t *out)
+// The stack's graph form is captured on a stream of the handle's own (the caller's stream may be
+// the legacy default stream, which cannot be captured) and launched on the caller's stream.
+int capture_stream(csf_handle h, hipStream_t *out)
 {
-    constexpr int kMaxDevices = 64;
-    thread_local hipStream_t streams[kMaxDevices] = {};
-    if (dev < 0 || dev >= kMaxDevices)
-        return fail(CSF_ERR_UNSUPPORTED, "device %d is beyond the library's limit", dev);
-    if (!streams[dev]) {
-        hipError_t e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (!h->capture) {
+        hipError_t e = hipStreamCreateWithFlags(&h->capture, hipStreamNonBlocking);
         if (e != hipSuccess) {
-            streams[dev] = nullptr;
+            h->capture = nullptr;
             return hip_status(e, "hipStreamCreateWithFlags");
         }
     }
-    *out = streams[dev];
+    *out = h->capture;
     return CSF_OK;
 }
 
-int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
-                  int dtype, float *x, int B, int sched, int k, float tau, int norm, float eps,
-                  float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log, void *ws,
-                  hipStream_t st, hipStream_t side)
+int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, int f, int r,
+                  int act, int dtype, float *x, int B, int sched, int k, float tau, int norm,
+                  float eps, float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
+                  void *ws, hipStream_t st, hipStream_t side)
 {
     const int max_count = k >= 0 ? k : f;
     const int stride = max_count > 0 ? max_count : 1;
@@ -447,7 +498,7 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
     const bool ahead = sched == CSF_STACK_LOOKAHEAD;
     hipEvent_t ev_x[2] = {nullptr, nullptr}, ev_s[2] = {nullptr, nullptr};
     if (ahead) {
-        int s = stack_events(ev_x, ev_s);
+        int s = stack_events(h, ev_x, ev_s);
         if (s != CSF_OK)
             return s;
     }
@@ -471,9 +522,8 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
         bool zeroed = false;
         // the clear covers token 0's counter block: only a single token can skip the clear kernel
         hipError_t e = enqueue_predict(dtype, xh, B, d, layers[l].V, r, layers[l].U, f, sc, a, q,
-                                       nullptr, wide && B == 1 ? selws : nullptr,
-                                       wide && B == 1 ? csf::select_wide_zero_words() : 0, &zeroed,
-                                       on_side ? csf::kPredUpSideGrid : 0);
+                                       nullptr, h, on_side, wide && B == 1 ? selws : nullptr,
+                                       wide && B == 1 ? csf::select_wide_zero_words() : 0, &zeroed);
         if (e == hipSuccess) {
             if (wide)
                 e = csf::launch_select_topk_wide(sc, B, f, k, sel_idx(l), stride, sel_count(l),
@@ -538,8 +588,8 @@ int enqueue_stack(const csf_layer_weights *layers, int L, int d, int f, int r, i
         fa.y = x;
         fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
         fa.accumulate = 1;
-        fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
-        fa.gate_tau = g_gate_tau;
+        fa.skip_zero = (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+        fa.gate_tau = h->gate_tau;
         e = csf::launch_ffn(fa, st);
         if (e != hipSuccess)
             return hip_status(e, "stack FFN launch");
@@ -663,7 +713,7 @@ int enqueue_attention(const void *x, int d, int H, int dh, int dtype, const void
 // One token's layer (predict, select, gathered FFN) on validated arguments, in the LayerWs
 // layout of `ws`.  Optional outputs: scores, list, count, bitmap (NULL: kept in the workspace or
 // not written).
-int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const void *V,
+int enqueue_layer1(csf_handle h, const void *x, int d, int f, int r, int act, int dtype, const void *V,
                    const void *U, const void *W1, const float *b1, const void *Wup,
                    const void *W2T, int k, float tau, float *y, float *scores_out,
                    int32_t *idx_out, int32_t *count_out, uint32_t *bitmap, void *ws,
@@ -693,7 +743,7 @@ int enqueue_layer1(const void *x, int d, int f, int r, int act, int dtype, const
         // few neurons: the scores and their selection in one kernel
         e = csf::launch_pred_up_select(dtype, a, d, r, U, f, sc, k, tau, ix, cn, st, trp);
     } else {
-        e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp);
+        e = csf::launch_pred_up(dtype, a, 1, d, r, U, f, sc, st, trp, h->pred_up_grid);
         if (e == hipSuccess && wide)
             e = csf::launch_select_topk_wide(sc, 1, f, k, ix, max_count > 0 ? max_count : 1, cn,
                                              bitmap, selws, true, st, trp);
@@ -753,31 +803,102 @@ const char *csf_status_string(int status)
 
 const char *csf_last_error(void) { return g_last_error.c_str(); }
 
-int csf_set_ffn_flags(int flags)
+int csf_create(csf_handle *out, int device)
 {
+    REQUIRE(out, CSF_ERR_INVALID_ARG, "out must not be NULL");
+    *out = nullptr;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDeviceCount");
+    REQUIRE(device >= 0 && device < n, CSF_ERR_INVALID_ARG, "device %d is not in [0, %d)", device,
+            n);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess)
+        return hip_status(e, "hipDeviceGetAttribute");
+    REQUIRE(cus > 0, CSF_ERR_UNSUPPORTED, "device %d reports %d compute units", device, cus);
+    csf_context *h = new (std::nothrow) csf_context;
+    REQUIRE(h, CSF_ERR_INVALID_ARG, "out of host memory");
+    h->device = device;
+    h->cus = cus;
+    // measured on MI355X (256 CUs): the persistent one-token up projection is fastest with the
+    // most workgroups resident at once, 8 of 256 threads per CU (2048; 1024 / 512 slower).  On the
+    // look-ahead stack's second stream, beside the FFN, 4 per CU: 2.35 ms/token for the 48-layer
+    // OPT-30B-shape stack (graph replay) against 2.52 with 8 per CU (it then crowds out the FFN)
+    // and 2.42 / 2.37 / 2.48 with 3 / 5 / 6 per CU
+    h->pred_up_grid = 8 * cus;
+    h->pred_up_side_grid = 4 * cus;
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        g_handles.insert(h);
+    }
+    *out = h;
+    return ok();
+}
+
+int csf_destroy(csf_handle h)
+{
+    if (!h)
+        return ok();
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        REQUIRE(g_handles.erase(h) == 1, CSF_ERR_INVALID_ARG, "not a live handle");
+    }
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    if (h->graph)
+        (void)hipGraphExecDestroy(h->graph);
+    for (hipEvent_t ev : h->stack_ev)
+        if (ev)
+            (void)hipEventDestroy(ev);
+    if (h->capture)
+        (void)hipStreamDestroy(h->capture);
+    if (prev >= 0)
+        (void)hipSetDevice(prev);
+    delete h;
+    return ok();
+}
+
+int csf_get_device_info(csf_handle h, int *device, int *compute_units)
+{
+    REQUIRE(is_live(h), CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle");
+    if (device)
+        *device = h->device;
+    if (compute_units)
+        *compute_units = h->cus;
+    return ok();
+}
+
+int csf_set_ffn_flags(csf_handle h, int flags)
+{
+    REQUIRE(is_live(h), CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle");
     REQUIRE((flags & ~CSF_FFN_SKIP_ZERO_H) == 0, CSF_ERR_INVALID_ARG, "unknown FFN flags 0x%x",
             flags);
-    g_ffn_flags = flags;
+    h->ffn_flags = flags;
     return ok();
 }
 
-int csf_set_ffn_gate_threshold(float tau)
+int csf_set_ffn_gate_threshold(csf_handle h, float tau)
 {
+    REQUIRE(is_live(h), CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle");
     REQUIRE(tau >= 0.0f && tau <= 3.4e38f, CSF_ERR_INVALID_ARG,
             "gate threshold %g must be finite and >= 0", (double)tau);
-    g_gate_tau = tau;
+    h->gate_tau = tau;
     return ok();
 }
 
-int csf_set_trace_events(void *const *events, int n)
+int csf_set_trace_events(csf_handle h, void *const *events, int n)
 {
+    REQUIRE(is_live(h), CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle");
     REQUIRE(n >= 0 && n <= 16, CSF_ERR_INVALID_ARG, "n = %d must be in [0, 16]", n);
     REQUIRE(n == 0 || events, CSF_ERR_INVALID_ARG, "events must not be NULL when n > 0");
     for (int i = 0; i < n; ++i)
         REQUIRE(events[i], CSF_ERR_INVALID_ARG, "events[%d] is NULL", i);
     for (int i = 0; i < n; ++i)
-        g_trace_events[i] = static_cast<hipEvent_t>(events[i]);
-    g_trace_n = n;
+        h->trace[i] = static_cast<hipEvent_t>(events[i]);
+    h->trace_n = n;
     return ok();
 }
 
@@ -794,8 +915,10 @@ size_t csf_attention_workspace_size(int op, int d, int H, int dh, int r, int Tma
     return 0;
 }
 
-size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype)
+size_t csf_workspace_size(csf_handle h, int op, int B, int d, int f, int r, int max_count,
+                          int dtype)
 {
+    const int cus = sizing_cus(h);
     if (B < 0 || d <= 0 || f <= 0 || !valid_dtype(dtype) || max_count < 0)
         return 0;
     switch (op) {
@@ -812,9 +935,9 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
     case CSF_OP_LAYER:
         return r > 0 ? layer_ws(d, f, r, max_count, dtype).total : 0;
     case CSF_OP_BATCHED_UNION:
-        return union_ws(B, d, f, dtype).total;
+        return union_ws(B, d, f, dtype, cus).total;
     case CSF_OP_BATCHED_LAYER:
-        return r > 0 ? batched_layer_ws(B, d, f, r, max_count, dtype).total : 0;
+        return r > 0 ? batched_layer_ws(B, d, f, r, max_count, dtype, cus).total : 0;
     case CSF_OP_STACK:
         return r > 0 ? stack_ws(B, d, f, r, max_count, dtype).total : 0;
     default:
@@ -822,8 +945,9 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
     }
 }
 
-int csf_predict_active(const void *x, int B, int d, const void *V, int r, const void *U, int f,
-                       int dtype, float *scores, void *ws, size_t ws_bytes, void *stream)
+int csf_predict_active(csf_handle h, const void *x, int B, int d, const void *V, int r,
+                       const void *U, int f, int dtype, float *scores, void *ws, size_t ws_bytes,
+                       void *stream)
 {
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
@@ -838,14 +962,15 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
         return ok();
     PredictWs w = predict_ws(B, r);
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(h);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *a = reinterpret_cast<float *>(at(ws, w.a));
-    return hip_status(enqueue_predict(dtype, x, B, d, V, r, U, f, scores, a, st, nullptr),
+    return hip_status(enqueue_predict(dtype, x, B, d, V, r, U, f, scores, a, st, nullptr, h),
                       "predictor launch");
 }
 
-int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
-                    uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream)
+int csf_select_topk(csf_handle h, const float *scores, int B, int f, int k, int32_t *idx,
+                    int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream)
 {
     REQUIRE(B >= 0, CSF_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
     REQUIRE(f > 0, CSF_ERR_INVALID_ARG, "f must be positive (got %d)", f);
@@ -860,18 +985,20 @@ int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int3
         return ok();
     if (csf::select_wide_used(B, f, k)) {
         CHECK_WS(ws, ws_bytes, select_ws_bytes(B, f, k));
+        CHECK_HANDLE(h);
         return hip_status(csf::launch_select_topk_wide(scores, B, f, k, idx, k, count, bitmap,
                                                        static_cast<uint32_t *>(ws), false,
                                                        static_cast<hipStream_t>(stream)),
                           "top-k selection launch");
     }
+    CHECK_HANDLE(h);
     return hip_status(csf::launch_select_topk(scores, B, f, k, idx, k > 0 ? k : 1, count, bitmap,
                                               static_cast<hipStream_t>(stream)),
                       "top-k selection launch");
 }
 
-int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
-                         int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes,
+int csf_select_threshold(csf_handle h, const float *scores, int B, int f, float tau,
+                         int32_t *idx, int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes,
                          void *stream)
 {
     (void)ws;
@@ -887,15 +1014,16 @@ int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *
     CHECK_PTR(bitmap, false);
     if (B == 0)
         return ok();
+    CHECK_HANDLE(h);
     return hip_status(csf::launch_select_threshold(scores, B, f, tau, idx, f, count, bitmap,
                                                    static_cast<hipStream_t>(stream)),
                       "threshold selection launch");
 }
 
-int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const void *W1,
-                   const float *b1, const void *Wup, const void *W2T, const int32_t *idx,
-                   int idx_stride, const int32_t *count, int max_count, float *h, float *y,
-                   void *ws, size_t ws_bytes, void *stream)
+int csf_sparse_ffn(csf_handle hd, const void *x, int B, int d, int f, int act, int dtype,
+                   const void *W1, const float *b1, const void *Wup, const void *W2T,
+                   const int32_t *idx, int idx_stride, const int32_t *count, int max_count,
+                   float *h, float *y, void *ws, size_t ws_bytes, void *stream)
 {
     int s = validate_ffn(x, B, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
@@ -912,6 +1040,7 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
         return ok();
     FfnWs w = ffn_ws(B, d, dtype, max_count);
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(hd);
     csf::FfnArgs a;
     a.dtype = dtype;
     a.act = act;
@@ -931,14 +1060,14 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
     a.h_stride = h ? idx_stride : (max_count > 0 ? max_count : 1);
     a.y = y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
-    a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
-    a.gate_tau = g_gate_tau;
+    a.skip_zero = (hd->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    a.gate_tau = hd->gate_tau;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "sparse FFN launch");
 }
 
-int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
-                  const float *b1, const void *Wup, const void *W2T, float *H, float *Y, void *ws,
-                  size_t ws_bytes, void *stream)
+int csf_dense_ffn(csf_handle h, const void *X, int B, int d, int f, int act, int dtype,
+                  const void *W1, const float *b1, const void *Wup, const void *W2T, float *H,
+                  float *Y, void *ws, size_t ws_bytes, void *stream)
 {
     int s = validate_ffn(X, B, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
@@ -951,6 +1080,7 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
         return ok();
     FfnWs w = ffn_ws(B, d, dtype, f);
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(h);
     csf::FfnArgs a;
     a.dtype = dtype;
     a.act = act;
@@ -970,12 +1100,12 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
     a.h_stride = f;
     a.y = Y;
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
-    a.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
-    a.gate_tau = g_gate_tau;
+    a.skip_zero = (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    a.gate_tau = h->gate_tau;
     return hip_status(csf::launch_ffn(a, static_cast<hipStream_t>(stream)), "dense FFN launch");
 }
 
-int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, int dtype,
+int csf_sparse_ffn_batched_union(csf_handle h, const void *X, int B, int d, int f, int act, int dtype,
                                  const void *W1, const float *b1, const void *Wup,
                                  const void *W2T, const uint32_t *bitmaps, int semantics,
                                  int path, float *Y, int32_t *union_count, int *path_taken,
@@ -992,21 +1122,20 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
             *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
         return ok();
     }
-    UnionWs w = union_ws(B, d, f, dtype);
+    UnionWs w = union_ws(B, d, f, dtype, sizing_cus(h));
     CHECK_WS(ws, ws_bytes, w.total);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
+    CHECK_HANDLE(h);
+    csf::Trace tr = make_trace(h);
     s = enqueue_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, bitmaps, semantics, mfma, Y,
-                      union_count, ws, w, static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
+                      union_count, ws, w, h->cus, static_cast<hipStream_t>(stream),
+                      tr.ev ? &tr : nullptr);
     if (s == CSF_OK && path_taken)
         *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
     return s;
 }
 
-int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int act, int dtype,
+int csf_sparse_ffn_batched_layer(csf_handle h, const void *X, int B, int d, int f, int r, int act,
+                                 int dtype,
                                  const void *V, const void *U, const void *W1, const float *b1,
                                  const void *Wup, const void *W2T, int k, float tau,
                                  int semantics, int path, float *Y, uint32_t *bitmaps_out,
@@ -1031,21 +1160,18 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
         return ok();
     }
     const int max_count = k >= 0 ? k : f;
-    BatchedLayerWs w = batched_layer_ws(B, d, f, r, max_count, dtype);
+    BatchedLayerWs w = batched_layer_ws(B, d, f, r, max_count, dtype, sizing_cus(h));
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(h);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
+    csf::Trace tr = make_trace(h);
     csf::Trace *trp = tr.ev ? &tr : nullptr;
     if (B == 1 && !mfma) {
         // One token on the gather path: its union is its own set, so the single-token layer
         // (selection over many workgroups for large f, the gathered FFN over the token's list)
         // computes the same thing without the union list.  No post-gate skip, as on the union
         // path; the count is the union size.
-        s = enqueue_layer1(X, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, Y, nullptr,
+        s = enqueue_layer1(h, X, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, Y, nullptr,
                            nullptr, union_count, bitmaps_out, ws, layer_ws(d, f, r, max_count, dtype),
                            0, 0.0f, st, trp);
         if (s == CSF_OK && path_taken)
@@ -1057,7 +1183,7 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
     int32_t *ix = reinterpret_cast<int32_t *>(at(ws, w.idx));
     int32_t *cn = reinterpret_cast<int32_t *>(at(ws, w.count));
     uint32_t *bm = bitmaps_out ? bitmaps_out : reinterpret_cast<uint32_t *>(at(ws, w.bitmap));
-    hipError_t e = enqueue_predict(dtype, X, B, d, V, r, U, f, sc, a, st, trp);
+    hipError_t e = enqueue_predict(dtype, X, B, d, V, r, U, f, sc, a, st, trp, h);
     if (e != hipSuccess)
         return hip_status(e, "predictor launch");
     const int stride = max_count > 0 ? max_count : 1;
@@ -1067,15 +1193,15 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
         e = csf::launch_select_threshold(sc, B, f, tau, ix, f, cn, bm, st, trp);
     if (e != hipSuccess)
         return hip_status(e, "selection launch");
-    UnionWs uw = union_ws(B, d, f, dtype);
+    UnionWs uw = union_ws(B, d, f, dtype, h->cus);
     s = enqueue_union(X, B, d, f, act, dtype, W1, b1, Wup, W2T, bm, semantics, mfma, Y,
-                      union_count, at(ws, w.uni), uw, st, trp);
+                      union_count, at(ws, w.uni), uw, h->cus, st, trp);
     if (s == CSF_OK && path_taken)
         *path_taken = mfma ? CSF_PATH_MFMA : CSF_PATH_GATHER;
     return s;
 }
 
-int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dtype,
+int csf_sparse_ffn_layer_hot(csf_handle h, const void *x, int d, int f, int r, int act, int dtype,
                              const void *V, const void *U_cold, const void *W1, const float *b1,
                              const void *Wup, const void *W2T, int hot, int k_cold, float tau,
                              float *y, float *scores_out, int32_t *idx_out, int32_t *count_out,
@@ -1102,12 +1228,9 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     const int max_count = hot + (k_cold >= 0 ? k_cold : fc);
     LayerWs w = layer_ws(d, f, r, max_count, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(h);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
+    csf::Trace tr = make_trace(h);
     csf::Trace *trp = tr.ev ? &tr : nullptr;
     float *a = reinterpret_cast<float *>(at(ws, w.a));
     float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
@@ -1121,7 +1244,7 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     hipError_t e = csf::launch_pred_down(dtype, x, 1, d, V, r, a, st, trp, wide ? selws : nullptr,
                                          wide ? csf::select_wide_zero_words() : 0);
     if (e == hipSuccess)
-        e = csf::launch_pred_up(dtype, a, 1, d, r, U_cold, fc, sc, st, trp);
+        e = csf::launch_pred_up(dtype, a, 1, d, r, U_cold, fc, sc, st, trp, h->pred_up_grid);
     if (e != hipSuccess)
         return hip_status(e, "predictor launch");
     if (wide)
@@ -1154,16 +1277,16 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
     fa.h_stride = stride;
     fa.y = y;
     fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
-    fa.skip_zero = (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
-    fa.gate_tau = g_gate_tau;
+    fa.skip_zero = (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
+    fa.gate_tau = h->gate_tau;
     return hip_status(csf::launch_ffn(fa, st, trp), "sparse FFN launch");
 }
 
-int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,
-                         const void *U, const void *W1, const float *b1, const void *Wup,
-                         const void *W2T, int k, float tau, float *y, float *scores_out,
-                         int32_t *idx_out, int32_t *count_out, void *ws, size_t ws_bytes,
-                         void *stream)
+int csf_sparse_ffn_layer(csf_handle h, const void *x, int d, int f, int r, int act, int dtype,
+                         const void *V, const void *U, const void *W1, const float *b1,
+                         const void *Wup, const void *W2T, int k, float tau, float *y,
+                         float *scores_out, int32_t *idx_out, int32_t *count_out, void *ws,
+                         size_t ws_bytes, void *stream)
 {
     int s = validate_ffn(x, 1, d, f, act, dtype, W1, b1, Wup, W2T);
     if (s != CSF_OK)
@@ -1183,18 +1306,16 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
     const int max_count = k >= 0 ? k : f;
     LayerWs w = layer_ws(d, f, r, max_count, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
-    return enqueue_layer1(x, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, y, scores_out,
-                          idx_out, count_out, nullptr, ws, w,
-                          (g_ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0, g_gate_tau,
+    CHECK_HANDLE(h);
+    csf::Trace tr = make_trace(h);
+    return enqueue_layer1(h, x, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, y,
+                          scores_out, idx_out, count_out, nullptr, ws, w,
+                          (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0, h->gate_tau,
                           static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
 }
 
-int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
+int csf_stack_forward(csf_handle h, const csf_layer_weights *layers, int L, int d, int f, int r,
+                      int act,
                       int dtype, float *x, int B, int mode, int k, float tau, int norm, float eps,
                       float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
                       void *ws, size_t ws_bytes, void *stream, void *side_stream)
@@ -1235,17 +1356,15 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
         return ok();
     const int max_count = k >= 0 ? k : f;
     CHECK_WS(ws, ws_bytes, stack_ws(B, d, f, r, max_count, dtype).total);
+    CHECK_HANDLE(h);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!(mode & CSF_STACK_GRAPH))
-        return enqueue_stack(layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps, x_log,
-                             xhat_log, idx_log, count_log, ws, st,
+        return enqueue_stack(h, layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps,
+                             x_log, xhat_log, idx_log, count_log, ws, st,
                              static_cast<hipStream_t>(side_stream));
 
     // graph replay: the whole stack as one launch, captured on first use for these arguments
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return hip_status(e, "hipGetDevice");
+    hipError_t e = hipSuccess;
     uint64_t key = 1469598103934665603ull;
     auto mix = [&](const void *p, size_t n) {
         const unsigned char *c = static_cast<const unsigned char *>(p);
@@ -1255,27 +1374,26 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
     mix(layers, sizeof(csf_layer_weights) * (size_t)L);
     const void *ptrs[] = {x, x_log, xhat_log, idx_log, count_log, ws, stream, side_stream};
     mix(ptrs, sizeof ptrs);
-    const int ints[] = {L, d, f, r, act, dtype, B, mode, k, norm, dev, g_ffn_flags};
+    const int ints[] = {L, d, f, r, act, dtype, B, mode, k, norm, h->ffn_flags};
     mix(ints, sizeof ints);
     mix(&tau, sizeof tau);
     mix(&eps, sizeof eps);
-    mix(&g_gate_tau, sizeof g_gate_tau);
+    mix(&h->gate_tau, sizeof h->gate_tau);
     mix(&ws_bytes, sizeof ws_bytes);
-    StackGraph &g = g_stack_graph;
-    if (!(g.exec && g.key == key)) {
-        if (g.exec) {
-            (void)hipGraphExecDestroy(g.exec);
-            g.exec = nullptr;
+    if (!(h->graph && h->graph_key == key)) {
+        if (h->graph) {
+            (void)hipGraphExecDestroy(h->graph);
+            h->graph = nullptr;
         }
         hipStream_t cap = nullptr;
-        int s1 = capture_stream(dev, &cap);
+        int s1 = capture_stream(h, &cap);
         if (s1 != CSF_OK)
             return s1;
         e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess)
             return hip_status(e, "hipStreamBeginCapture");
-        const int s2 = enqueue_stack(layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps,
-                                     x_log, xhat_log, idx_log, count_log, ws, cap,
+        const int s2 = enqueue_stack(h, layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm,
+                                     eps, x_log, xhat_log, idx_log, count_log, ws, cap,
                                      static_cast<hipStream_t>(side_stream));
         const std::string msg = g_last_error;
         hipGraph_t graph = nullptr;
@@ -1287,18 +1405,19 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
         }
         if (e != hipSuccess)
             return hip_status(e, "hipStreamEndCapture");
-        e = hipGraphInstantiateWithFlags(&g.exec, graph, 0);
+        e = hipGraphInstantiateWithFlags(&h->graph, graph, 0);
         (void)hipGraphDestroy(graph);
         if (e != hipSuccess) {
-            g.exec = nullptr;
+            h->graph = nullptr;
             return hip_status(e, "hipGraphInstantiateWithFlags");
         }
-        g.key = key;
+        h->graph_key = key;
     }
-    return hip_status(hipGraphLaunch(g.exec, st), "hipGraphLaunch");
+    return hip_status(hipGraphLaunch(h->graph, st), "hipGraphLaunch");
 }
 
-int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+int csf_sparse_attention_decode(csf_handle h, const void *x, int d, int H, int dh, int dtype,
+                                const void *Wq,
                                 const void *Wk, const void *Wv, const float *bq, const float *bk,
                                 const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
                                 int32_t *len, const int32_t *heads, const int32_t *count,
@@ -1319,17 +1438,15 @@ int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, 
                 "without a head list every head is computed: max_heads must be H and count NULL");
     AttnWs w = attn_ws(d, H, dh, 0, Tmax, max_heads, dtype, false);
     CHECK_WS(ws, ws_bytes, w.total);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
+    CHECK_HANDLE(h);
+    csf::Trace tr = make_trace(h);
     return enqueue_attention(x, d, H, dh, dtype, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax, len,
                              heads, count, max_heads, kv_all, o, y, ws, w,
                              static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
 }
 
-int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int dtype,
+int csf_sparse_attention_layer(csf_handle h, const void *x, int d, int H, int dh, int r,
+                               int dtype,
                                const void *Vp, const void *Up, const void *Wq, const void *Wk,
                                const void *Wv, const float *bq, const float *bk, const float *bv,
                                const void *WoT, void *Kc, void *Vc, int Tmax, int32_t *len, int k,
@@ -1355,12 +1472,9 @@ int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int d
     const int max_heads = k >= 0 ? k : H;
     AttnWs w = attn_ws(d, H, dh, r, Tmax, max_heads, dtype, true);
     CHECK_WS(ws, ws_bytes, w.total);
+    CHECK_HANDLE(h);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    csf::Trace tr;
-    if (g_trace_n > 0) {
-        tr.ev = g_trace_events;
-        tr.n = g_trace_n;
-    }
+    csf::Trace tr = make_trace(h);
     csf::Trace *trp = tr.ev ? &tr : nullptr;
     float *a = reinterpret_cast<float *>(at(ws, w.a));
     float *sc = scores_out ? scores_out : reinterpret_cast<float *>(at(ws, w.scores));
@@ -1375,7 +1489,7 @@ int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int d
         if (e != hipSuccess)
             return hip_status(e, "head predictor launch");
     } else {
-        e = enqueue_predict(dtype, x, 1, d, Vp, r, Up, H, sc, a, st, trp);
+        e = enqueue_predict(dtype, x, 1, d, Vp, r, Up, H, sc, a, st, trp, h);
         if (e != hipSuccess)
             return hip_status(e, "head predictor launch");
         if (k >= 0)

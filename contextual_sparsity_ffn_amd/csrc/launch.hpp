@@ -61,14 +61,10 @@ hipError_t launch_pred_up_select(int dtype, const float *part, int d, int r, con
                                  float *s, int k, float tau, int32_t *idx, int32_t *count,
                                  hipStream_t stream, Trace *trace = nullptr);
 // s[B][f] = sigmoid(U relu(sum of the partials)) in float32.  grid: workgroups of the persistent
-// one-token form (0: the default, the most resident at once; a predictor that runs beside other
-// work on a second stream takes kPredUpSideGrid).
+// one-token form (the caller's choice from the device's compute units: the most resident at once,
+// or fewer for a predictor that runs beside other work on a second stream); unused for batches.
 hipError_t launch_pred_up(int dtype, const float *part, int B, int d, int r, const void *U, int f,
-                          float *s, hipStream_t stream, Trace *trace = nullptr, int grid = 0);
-// Measured on the 48-layer OPT-30B-shape look-ahead stack (graph replay): 2.35 ms/token with the
-// side stream's up projection on 1024 workgroups, 2.52 with 2048 (it then crowds out the FFN on
-// the main stream), 2.42 / 2.37 / 2.48 with 768 / 1280 / 1536.
-constexpr int kPredUpSideGrid = 1024;
+                          float *s, hipStream_t stream, Trace *trace, int grid);
 
 // ---- predictor for a batch on the matrix cores (predict_mfma.hip) --------------------------
 constexpr int kPredMfmaMinBatch = 4;      // tokens from which the batched predictor is used
@@ -78,9 +74,10 @@ bool pred_mfma_supported(int dtype, int B, int d, int r);
 int pred_mfma_split(int r, int d);
 size_t pred_mfma_ws_floats(int B, int r);   // workspace (floats) of launch_predict_mfma
 // s[B][f] = sigmoid(U relu(V x)) for 16-bit weights; ws: pred_mfma_ws_floats(B, r) floats.
+// res_grid: workgroups of the register-resident up projection (two per compute unit).
 hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const void *V, int r,
                                const void *U, int f, float *s, float *ws, hipStream_t stream,
-                               Trace *trace = nullptr);
+                               Trace *trace, int res_grid);
 
 // ---- selection (select.hip) -----------------------------------------------------------------
 // prefix: the list of each token starts with the neurons 0 .. prefix-1 (a block that is always
@@ -182,6 +179,7 @@ hipError_t launch_rms_norm(int dtype, const float *x, int B, int d, float eps, i
 // ---- batched FFN over the union of the tokens' sets (union.hip) -------------------------------
 constexpr int kMaxUnionBatch = 32;   // tokens per call (two 16-token matrix-core tiles)
 struct UnionArgs {
+    int cus = 0;            // compute units of the device
     int dtype, act;
     int per_token;          // 1: token t keeps only its own rows; 0: every union row for all
     int mfma;               // 1: matrix-core path (16-bit types, d % 256 == 0); 0: vector ALU
@@ -201,7 +199,8 @@ struct UnionArgs {
     float *partials;        // [B][union_num_chunks][d]
 };
 bool union_mfma_supported(int dtype, int d, int B);
-int union_num_chunks(int mfma, int d, int dtype, int f);
+// chunks of the union's down projection (sizes its workspace); cus: the device's compute units
+int union_num_chunks(int mfma, int d, int dtype, int f, int cus);
 size_t union_h_stride(int f);
 hipError_t launch_union_ffn(const UnionArgs &a, hipStream_t stream, Trace *trace = nullptr);
 

@@ -418,12 +418,6 @@ hipError_t down_t(const DownArgs &g, hipStream_t st, Trace *tr)
     return hipErrorInvalidValue;
 }
 
-// Workgroups of the persistent one-token up projection: 8 of 256 threads per CU on 256 CUs, the
-// most that are resident at once.  Measured at the OPT-175B / OPT-30B / LLaMA-class predictor
-// shapes: 17.4 / 8.1 / 4.2 us against 18.1 / 9.5 / 4.35 us for one short workgroup per 8 rows;
-// 1024 or 512 workgroups, or 2 and 4 rows per lane group, are slower.
-constexpr int kPredUpGrid = 2048;
-
 template <class T, int LPR, int MM, int RW>
 hipError_t up_loop_launch(const float *a, int S, int r, int C, const void *U, int f, float *s,
                           hipStream_t st, Trace *tr, int grid)
@@ -441,9 +435,13 @@ hipError_t up_launch(const float *a, int B, int S, int r, int C, const void *U, 
 {
     constexpr int rows_per_wave = RW * (kWave / LPR);
     constexpr int NT = 256;   // measured: 512-thread workgroups are slower (19.5 against 18.2 us)
+    // one token: the persistent form on the caller's grid (measured at the OPT-175B / OPT-30B /
+    // LLaMA-class predictor shapes with 8 workgroups per CU: 17.4 / 8.1 / 4.2 us against 18.1 / 9.5
+    // / 4.35 us for one short workgroup per 8 rows; 4 or 2 per CU, or 2 and 4 rows per lane
+    // group, are slower)
     if (B == 1)
-        return up_loop_launch<T, LPR, MM, 1>(a, S, r, C, U, f, s, st, tr,
-                                             grid > 0 ? grid : kPredUpGrid);
+        return grid > 0 ? up_loop_launch<T, LPR, MM, 1>(a, S, r, C, U, f, s, st, tr, grid)
+                        : hipErrorInvalidValue;
     const int waves = (f + rows_per_wave - 1) / rows_per_wave;
     const int blocks = (waves + NT / kWave - 1) / (NT / kWave);
     return launch(k_pred_up<T, LPR, MM, RW, NT>, dim3(blocks), dim3(NT), st, tr,

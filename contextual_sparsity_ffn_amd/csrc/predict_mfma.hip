@@ -270,7 +270,8 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restric
 
 template <class T, int MT, int NA>
 hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, const u32x4 *U,
-                         int f, float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr)
+                         int f, float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr,
+                         int res_grid)
 {
     const int C = d / 8;
     const int ks_n = pred_mfma_split(r, d);
@@ -284,11 +285,10 @@ hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, co
         return e;
     const int tiles = (f + 15) / 16;
     if ((r / 32 + 3) / 4 <= 4) {
-        // 512 workgroups (3.5 tiles each at the OPT-30B shape): 8.9 / 9.3 / 12.9 us at 8 / 16 / 32
-        // tokens, against 9.7 / 12.4 / 20.9 for k_pred_up_mfma; 256, 1024 and one workgroup per
-        // tile measured slower
-        constexpr int kResGrid = 512;
-        return launch(k_pred_up_mfma_res<T, MT, NA, 4>, dim3(tiles < kResGrid ? tiles : kResGrid),
+        // two workgroups per CU (512 on MI355X, 3.5 tiles each at the OPT-30B shape): 8.9 / 9.3 /
+        // 12.9 us at 8 / 16 / 32 tokens, against 9.7 / 12.4 / 20.9 for k_pred_up_mfma; one or four
+        // per CU and one workgroup per tile measured slower
+        return launch(k_pred_up_mfma_res<T, MT, NA, 4>, dim3(tiles < res_grid ? tiles : res_grid),
                       dim3(256), st, tr, U, ahid, B, r, f, s);
     }
     return launch(k_pred_up_mfma<T, MT, NA>, dim3(tiles < 4096 ? tiles : 4096), dim3(256), st, tr,
@@ -297,7 +297,7 @@ hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, co
 
 template <class T, int NA>
 hipError_t predict_t(const void *x, int B, int d, const void *V, int r, const void *U, int f,
-                     float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr)
+                     float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr, int res_grid)
 {
     for (int b0 = 0; b0 < B; b0 += kMaxPredMfmaTokens) {
         const int nb = B - b0 < kMaxPredMfmaTokens ? B - b0 : kMaxPredMfmaTokens;
@@ -305,9 +305,9 @@ hipError_t predict_t(const void *x, int B, int d, const void *V, int r, const vo
         float *sb = s + (size_t)b0 * f;
         hipError_t e = nb <= 16
             ? predict_group<T, 1, NA>(xb, nb, d, static_cast<const u32x4 *>(V), r,
-                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr)
+                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr, res_grid)
             : predict_group<T, 2, NA>(xb, nb, d, static_cast<const u32x4 *>(V), r,
-                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr);
+                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr, res_grid);
         if (e != hipSuccess)
             return e;
     }
@@ -343,16 +343,18 @@ size_t pred_mfma_ws_floats(int B, int r)
 
 hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const void *V, int r,
                                const void *U, int f, float *s, float *ws, hipStream_t st,
-                               Trace *tr)
+                               Trace *tr, int res_grid)
 {
+    if (res_grid < 1)
+        return hipErrorInvalidValue;
     const int nb = B < kMaxPredMfmaTokens ? B : kMaxPredMfmaTokens;
     float *part = ws;
     // 16-byte aligned start for the 16-bit terms
     size_t off = ((size_t)kMaxPredMfmaSplit * nb * r + 3) / 4 * 4;
     uint16_t *ahid = reinterpret_cast<uint16_t *>(ws + off);
     if (dtype == 1)
-        return predict_t<F16T, 2>(x, B, d, V, r, U, f, s, part, ahid, st, tr);
-    return predict_t<BF16T, 3>(x, B, d, V, r, U, f, s, part, ahid, st, tr);
+        return predict_t<F16T, 2>(x, B, d, V, r, U, f, s, part, ahid, st, tr, res_grid);
+    return predict_t<BF16T, 3>(x, B, d, V, r, U, f, s, part, ahid, st, tr, res_grid);
 }
 
 }  // namespace csf

@@ -40,7 +40,6 @@ constexpr int kDownLdsStride = 260;  // 16-bit elements per staged row: 520 byte
                                      // rows 8 apart fall 16 banks apart)
 constexpr int kValuTokens = 8;       // tokens per vector-ALU down-projection workgroup
 constexpr int kMaxDownSteps = 64;    // K steps (of 32 union rows) per matrix-core down chunk
-constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs of 32 CUs
 
 // Union rows per gather-path workgroup: about 12 chunk loads in flight per thread, at most 4 rows.
 template <int MX, bool GATED>
@@ -625,7 +624,7 @@ hipError_t union_valu(const UnionArgs &a, hipStream_t st, Trace *tr)
     hipError_t e = act_gated(a.act) ? up_valu_mx<T, true>(a, C, st, tr) : up_valu_mx<T, false>(a, C, st, tr);
     if (e != hipSuccess)
         return e;
-    const int nchunk = union_num_chunks(0, a.d, a.dtype, a.f);
+    const int nchunk = union_num_chunks(0, a.d, a.dtype, a.f, a.cus);
     const dim3 grid(ffn_num_slices(a.d, a.dtype), nchunk, (a.B + kValuTokens - 1) / kValuTokens);
     if (a.B <= 1)
         e = launch(k_union_down_valu<T, 1, 4>, grid, dim3(256), st, tr,
@@ -663,7 +662,7 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
                    a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
     if (e != hipSuccess)
         return e;
-    const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f);
+    const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f, a.cus);
     // two K steps of loads in flight ahead (measured at 8 / 16 / 32 tokens: 47.8 / 57.1 / 73.9 us
     // against 49.2 / 59.7 / 75.2 with three and 51.4 / 61.6 / 79.6 with four)
     e = launch(k_union_down_mfma<T, MT, 2>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
@@ -699,7 +698,7 @@ bool union_mfma_supported(int dtype, int d, int B)
     return dtype != 0 && d % kDownCols == 0 && B >= 1 && B <= kMaxUnionBatch;
 }
 
-int union_num_chunks(int mfma, int d, int dtype, int f)
+int union_num_chunks(int mfma, int d, int dtype, int f, int cus)
 {
     if (!mfma)
         return ffn_num_chunks(d, dtype, f);
@@ -712,7 +711,7 @@ int union_num_chunks(int mfma, int d, int dtype, int f)
     // for the dense batched step
     const int tiles = d / kDownCols > 0 ? d / kDownCols : 1;
     const int steps = (f + kKStep - 1) / kKStep;
-    int n = 2 * kComputeUnits / tiles;
+    int n = (int)(2L * cus / tiles);
     const int least = (steps + kMaxDownSteps - 1) / kMaxDownSteps;
     if (n > steps)
         n = steps;

@@ -12,6 +12,16 @@
  *   [AS] "Activation sparsity" (wiki page)
  *
  * Conventions shared by every entry point
+ *   Handle        Every call that enqueues work takes a csf_handle (csf_create) as its first
+ *                 argument.  A handle belongs to one device, which must be the current device
+ *                 when it is used; it holds that device's facts (queried once: the compute-unit
+ *                 count the persistent grids and the batched chunking are sized from), the
+ *                 gathered FFN's options, the per-kernel timing hook and the stack's events,
+ *                 capture stream and captured graph.  It holds no tensor.  A handle may be used
+ *                 by one thread at a time; calls on different handles are independent.  A call
+ *                 that enqueues nothing (B == 0, L == 0) does not look at the handle; otherwise
+ *                 the handle is checked after every other argument, and a NULL, destroyed or
+ *                 other-device handle gives CSF_ERR_INVALID_ARG with nothing enqueued.
  *   Pointers      All tensor pointers are DEVICE pointers (hipMalloc or equivalent) unless a
  *                 comment says "host".  The caller allocates and frees every buffer, including
  *                 the workspace; the library never allocates device memory.
@@ -30,7 +40,8 @@
  *                 enqueues anything: a non-zero status means nothing was enqueued, except
  *                 CSF_ERR_HIP, which reports a failed launch.  Device faults surface at the
  *                 caller's next synchronisation.  csf_last_error() gives a message (per thread).
- *                 Inputs must be finite; NaN/Inf are not checked.
+ *                 Inputs must be finite; NaN/Inf are not checked (a NaN score ranks below every
+ *                 number in the top-k selections and never passes a threshold).
  *   Determinism   The same inputs give bitwise-identical outputs: no floating-point atomics, every
  *                 reduction runs in a fixed order.
  */
@@ -90,7 +101,7 @@ typedef enum {
     CSF_STACK_LOOKAHEAD = 1, /* layer l's set is predicted from layer l-1's input, on the side
                                 stream while layer l-1 runs (layer 0: from its own input)       */
     CSF_STACK_GRAPH = 0x100  /* flag, OR'd into the mode: enqueue the whole stack as one HIP
-                                graph launch.  The first call captures it (per calling thread);
+                                graph launch.  The first call captures it (kept by the handle);
                                 later calls with identical arguments (every pointer, size and
                                 value, the layers array's contents, the streams) replay it.     */
 } csf_stack_mode;
@@ -116,8 +127,26 @@ typedef enum {
 } csf_path;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define CSF_ABI_VERSION 1
+#define CSF_ABI_VERSION 2
 int csf_abi_version(void);
+
+/* An opaque library handle (see "Handle" above). */
+typedef struct csf_context *csf_handle;
+
+/* csf_create -- a handle for HIP device `device` (0 <= device < the device count).  Queries the
+ * device's compute-unit count; creates no stream, event or device buffer (the stack creates its
+ * events and capture stream on first use, owned by the handle).
+ *   out     HOST, out: the new handle (NULL on failure)
+ * CSF_ERR_INVALID_ARG for a bad device index or NULL out; CSF_ERR_HIP when the runtime fails. */
+int csf_create(csf_handle *out, int device);
+
+/* csf_destroy -- releases a handle and whatever it created (events, capture stream, graph).  NULL
+ * is accepted (no-op).  The caller must have finished (synchronised) the work the handle
+ * enqueued that could still use its events or graph. */
+int csf_destroy(csf_handle h);
+
+/* The device of a handle and the compute units it reports (either pointer may be NULL). */
+int csf_get_device_info(csf_handle h, int *device, int *compute_units);
 
 /* Static text for a status code (never NULL). */
 const char *csf_status_string(int status);
@@ -128,8 +157,10 @@ const char *csf_last_error(void);
 
 /* Bytes of device workspace the operation needs for these sizes (0 if none).  `d`, `f`, `r`, `B`
  * are the sizes passed to the entry point; `max_count` is the longest active list (k for top-k,
- * f for threshold or dense).  Returns 0 for invalid sizes. */
-size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int dtype);
+ * f for threshold or dense).  Returns 0 for invalid sizes.  h: the handle the calls will use (the
+ * batched union's chunking follows its device), or NULL for a size that fits any device. */
+size_t csf_workspace_size(csf_handle h, int op, int B, int d, int f, int r, int max_count,
+                          int dtype);
 
 /* ---------------------------------------------------------------------------------------------
  * csf_predict_active -- predictor scores for every neuron of every token.
@@ -142,9 +173,9 @@ size_t csf_workspace_size(int op, int B, int d, int f, int r, int max_count, int
  *   U       [f][r]  dtype      predictor up projection
  *   scores  [B][f]  float32    out: sigmoid scores in [0, 1]
  * The hidden activation relu(V x) is kept in float32; all sums accumulate in float32.
- * Workspace: csf_workspace_size(CSF_OP_PREDICT, B, d, f, r, 0, dtype) bytes.
+ * Workspace: csf_workspace_size(h, CSF_OP_PREDICT, B, d, f, r, 0, dtype) bytes.
  * ------------------------------------------------------------------------------------------- */
-int csf_predict_active(const void *x, int B, int d, const void *V, int r, const void *U, int f,
+int csf_predict_active(csf_handle h, const void *x, int B, int d, const void *V, int r, const void *U, int f,
                        int dtype, float *scores, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
@@ -157,11 +188,11 @@ int csf_predict_active(const void *x, int B, int d, const void *V, int r, const 
  *   idx     [B][k]       int32     out: ascending active list per token
  *   count   [B]          int32     out, optional (NULL): set to k
  *   bitmap  [B][(f+31)/32] uint32  out, optional (NULL): bit j%32 of word j/32 set iff j selected
- * Workspace: csf_workspace_size(CSF_OP_SELECT_TOPK, B, 1, f, 0, k, dtype) bytes; it is non-zero
+ * Workspace: csf_workspace_size(h, CSF_OP_SELECT_TOPK, B, 1, f, 0, k, dtype) bytes; it is non-zero
  * when a few tokens have many scores (then the selection of a token runs over many workgroups,
  * with the same result) and 0 otherwise (pass NULL, 0).
  * ------------------------------------------------------------------------------------------- */
-int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
+int csf_select_topk(csf_handle h, const float *scores, int B, int f, int k, int32_t *idx, int32_t *count,
                     uint32_t *bitmap, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
@@ -173,7 +204,7 @@ int csf_select_topk(const float *scores, int B, int f, int k, int32_t *idx, int3
  *   bitmap  optional, as for csf_select_topk
  * Workspace: none.
  * ------------------------------------------------------------------------------------------- */
-int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *idx,
+int csf_select_threshold(csf_handle h, const float *scores, int B, int f, float tau, int32_t *idx,
                          int32_t *count, uint32_t *bitmap, void *ws, size_t ws_bytes,
                          void *stream);
 
@@ -195,9 +226,9 @@ int csf_select_threshold(const float *scores, int B, int f, float tau, int32_t *
  *   y        [B][d]  float32   out: y_t = sum over the list of h_j * W2T[j]
  * Tokens are independent (each reads its own rows).  For one read of shared rows across a
  * batch use csf_sparse_ffn_batched_union.
- * Workspace: csf_workspace_size(CSF_OP_SPARSE_FFN, B, d, f, 0, max_count, dtype).
+ * Workspace: csf_workspace_size(h, CSF_OP_SPARSE_FFN, B, d, f, 0, max_count, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const void *W1,
+int csf_sparse_ffn(csf_handle hd, const void *x, int B, int d, int f, int act, int dtype, const void *W1,
                    const float *b1, const void *Wup, const void *W2T, const int32_t *idx,
                    int idx_stride, const int32_t *count, int max_count, float *h, float *y,
                    void *ws, size_t ws_bytes, void *stream);
@@ -210,9 +241,9 @@ int csf_sparse_ffn(const void *x, int B, int d, int f, int act, int dtype, const
  *   the true active set ([DV] "The Empirical Foundation": a ReLU neuron is either exactly zero
  *   or contributes), against which a predicted set's recall and precision are measured
  *   ([CP] "Precision, recall, and which error hurts").
- * Workspace: csf_workspace_size(CSF_OP_DENSE_FFN, B, d, f, 0, f, dtype).
+ * Workspace: csf_workspace_size(h, CSF_OP_DENSE_FFN, B, d, f, 0, f, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const void *W1,
+int csf_dense_ffn(csf_handle h, const void *X, int B, int d, int f, int act, int dtype, const void *W1,
                   const float *b1, const void *Wup, const void *W2T, float *H, float *Y, void *ws,
                   size_t ws_bytes, void *stream);
 
@@ -226,9 +257,9 @@ int csf_dense_ffn(const void *X, int B, int d, int f, int act, int dtype, const 
  *   y [d] float32 out
  *   scores_out [f] float32, idx_out [k or f] int32, count_out [1] int32: optional outputs (NULL =
  *   kept in the workspace only).
- * Workspace: csf_workspace_size(CSF_OP_LAYER, 1, d, f, r, k >= 0 ? k : f, dtype).
+ * Workspace: csf_workspace_size(h, CSF_OP_LAYER, 1, d, f, r, k >= 0 ? k : f, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype, const void *V,
+int csf_sparse_ffn_layer(csf_handle h, const void *x, int d, int f, int r, int act, int dtype, const void *V,
                          const void *U, const void *W1, const float *b1, const void *Wup,
                          const void *W2T, int k, float tau, float *y, float *scores_out,
                          int32_t *idx_out, int32_t *count_out, void *ws, size_t ws_bytes,
@@ -251,10 +282,10 @@ int csf_sparse_ffn_layer(const void *x, int d, int f, int r, int act, int dtype,
  *   0 <= hot < f; 0 <= k_cold <= f - hot.
  *   scores_out [f - hot], idx_out [hot + k_cold, or f in threshold mode], count_out [1]: optional;
  *   the list is 0 .. hot-1 followed by the selected cold neurons, ascending.
- * Workspace: csf_workspace_size(CSF_OP_LAYER, 1, d, f, r, hot + (k_cold >= 0 ? k_cold : f - hot),
+ * Workspace: csf_workspace_size(h, CSF_OP_LAYER, 1, d, f, r, hot + (k_cold >= 0 ? k_cold : f - hot),
  * dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dtype,
+int csf_sparse_ffn_layer_hot(csf_handle h, const void *x, int d, int f, int r, int act, int dtype,
                              const void *V, const void *U_cold, const void *W1, const float *b1,
                              const void *Wup, const void *W2T, int hot, int k_cold, float tau,
                              float *y, float *scores_out, int32_t *idx_out, int32_t *count_out,
@@ -281,9 +312,9 @@ int csf_sparse_ffn_layer_hot(const void *x, int d, int f, int r, int act, int dt
  *   union_count [1] int32         out, optional device copy of the union size
  *   path_taken  HOST int*         out, optional: CSF_PATH_GATHER or CSF_PATH_MFMA
  * Each union row is read from HBM once per call for all B tokens.  f <= 65536.
- * Workspace: csf_workspace_size(CSF_OP_BATCHED_UNION, B, d, f, 0, 0, dtype).
+ * Workspace: csf_workspace_size(h, CSF_OP_BATCHED_UNION, B, d, f, 0, 0, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, int dtype,
+int csf_sparse_ffn_batched_union(csf_handle h, const void *X, int B, int d, int f, int act, int dtype,
                                  const void *W1, const float *b1, const void *Wup,
                                  const void *W2T, const uint32_t *bitmaps, int semantics,
                                  int path, float *Y, int32_t *union_count, int *path_taken,
@@ -300,9 +331,9 @@ int csf_sparse_ffn_batched_union(const void *X, int B, int d, int f, int act, in
  * A batch of one on the gather path (CSF_PATH_GATHER, or CSF_PATH_AUTO at B = 1) is the
  * single-token layer: csf_sparse_ffn_layer's kernels and bits (without the post-gate skip), its
  * count as the union size.
- * Workspace: csf_workspace_size(CSF_OP_BATCHED_LAYER, B, d, f, r, k >= 0 ? k : f, dtype).
+ * Workspace: csf_workspace_size(h, CSF_OP_BATCHED_LAYER, B, d, f, r, k >= 0 ? k : f, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int act, int dtype,
+int csf_sparse_ffn_batched_layer(csf_handle h, const void *X, int B, int d, int f, int r, int act, int dtype,
                                  const void *V, const void *U, const void *W1, const float *b1,
                                  const void *Wup, const void *W2T, int k, float tau,
                                  int semantics, int path, float *Y, uint32_t *bitmaps_out,
@@ -328,25 +359,25 @@ int csf_sparse_ffn_batched_layer(const void *X, int B, int d, int f, int r, int 
  *             of its work is ordered before the end of `stream`'s work, so synchronising `stream`
  *             is enough.  With CSF_STACK_GRAPH the host enqueues one launch per call instead of
  *             about 7 kernels and 4 event operations per layer; the captured graph (kept by the
- *             runtime, one per calling thread) is replaced when the arguments change.
+ *             runtime, one per handle) is replaced when the arguments change.
  *   x_log     [L][B][d] float32, optional: x_l at the input of each layer.
  *   xhat_log  [L][B][d] dtype, optional: xhat_l.
  *   idx_log   [L][B][k or f] int32, optional: each layer's ascending active list.
  *   count_log [L][B] int32, optional: each layer's list length.
- * B >= 0 tokens, each with its own sets.  The library keeps 4 HIP events per device and calling
- * thread, and for CSF_STACK_GRAPH one capture stream per device and thread and the instantiated
- * graph (all created on first use; no device buffers of its own).
- * Workspace: csf_workspace_size(CSF_OP_STACK, B, d, f, r, k >= 0 ? k : f, dtype).
+ * B >= 0 tokens, each with its own sets.  The handle keeps 4 HIP events, and for
+ * CSF_STACK_GRAPH a capture stream and the instantiated graph (all created on first use; no device
+ * buffers of its own).
+ * Workspace: csf_workspace_size(h, CSF_OP_STACK, B, d, f, r, k >= 0 ? k : f, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int r, int act,
+int csf_stack_forward(csf_handle h, const csf_layer_weights *layers, int L, int d, int f, int r, int act,
                       int dtype, float *x, int B, int mode, int k, float tau, int norm, float eps,
                       float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
                       void *ws, size_t ws_bytes, void *stream, void *side_stream);
 
 /* ---------------------------------------------------------------------------------------------
- * csf_set_ffn_flags -- options of the gathered FFN for later calls on the calling thread
- * (csf_sparse_ffn, csf_dense_ffn, csf_sparse_ffn_layer, csf_stack_forward; not the batched union
- * path).  0 (the default) restores the plain method.
+ * csf_set_ffn_flags -- options of the gathered FFN for later calls with this handle
+ * (csf_sparse_ffn, csf_dense_ffn, csf_sparse_ffn_layer, csf_sparse_ffn_layer_hot,
+ * csf_stack_forward; not the batched union path).  0 (the default) restores the plain method.
  *   CSF_FFN_SKIP_ZERO_H  post-gate skip: the gate activation a_j = act(W1[j].x + b1_j) of each
  *                        listed neuron is computed first; a neuron with |a_j| <= gate_tau (see
  *                        csf_set_ffn_gate_threshold; default 0) gets h_j = 0, its up row (gated
@@ -359,11 +390,11 @@ int csf_stack_forward(const csf_layer_weights *layers, int L, int d, int f, int 
  *                        positives.
  * ------------------------------------------------------------------------------------------- */
 #define CSF_FFN_SKIP_ZERO_H 1
-int csf_set_ffn_flags(int flags);
+int csf_set_ffn_flags(csf_handle h, int flags);
 
 /* ---------------------------------------------------------------------------------------------
- * csf_set_ffn_gate_threshold -- the gate_tau of CSF_FFN_SKIP_ZERO_H for later calls on the
- * calling thread (0 by default).  tau > 0 applies the functional activity test of [DV] "The
+ * csf_set_ffn_gate_threshold -- the gate_tau of CSF_FFN_SKIP_ZERO_H for later calls with this
+ * handle (0 by default).  tau > 0 applies the functional activity test of [DV] "The
  * Empirical Foundation" (measure_mlp_sparsity: a neuron counts when the magnitude of its
  * activation exceeds a threshold, 0.1 there) inside the FFN: a SiLU gate is never exactly zero
  * ([DV] "The SiLU/GELU Challenge"), so the listed neurons are cut to those with |a_j| > tau
@@ -372,12 +403,12 @@ int csf_set_ffn_flags(int flags);
  * ungated forms).  The test is taken in float32 on the kernel's own a_j.
  *   tau   >= 0 and finite, else CSF_ERR_INVALID_ARG (the previous value is kept).
  * ------------------------------------------------------------------------------------------- */
-int csf_set_ffn_gate_threshold(float tau);
+int csf_set_ffn_gate_threshold(csf_handle h, float tau);
 
 /* ---------------------------------------------------------------------------------------------
  * csf_set_trace_events -- per-kernel timing hook for csf_sparse_ffn_layer,
- * csf_sparse_ffn_batched_union, csf_sparse_ffn_batched_layer and the attention calls (per
- * calling thread).
+ * csf_sparse_ffn_batched_union, csf_sparse_ffn_batched_layer and the attention calls made with
+ * this handle.
  * While n > 0 events are set, the i-th kernel such a call launches has the HIP runtime record
  * events[2i] when it starts and events[2i+1] when it ends (while 2i+1 < n), so
  * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's own duration.  The kernels, in
@@ -394,7 +425,7 @@ int csf_set_ffn_gate_threshold(float tau);
  * The events are hipEvent_t handles (as void*) created and owned by the caller, at most 16;
  * n = 0 switches timing off.
  * ------------------------------------------------------------------------------------------- */
-int csf_set_trace_events(void *const *events, int n);
+int csf_set_trace_events(csf_handle h, void *const *events, int n);
 
 /* ---------------------------------------------------------------------------------------------
  * Attention-head sparsity: one decode step of multi-head attention for a set of heads.
@@ -437,7 +468,7 @@ int csf_set_trace_events(void *const *events, int n);
  * ------------------------------------------------------------------------------------------- */
 size_t csf_attention_workspace_size(int op, int d, int H, int dh, int r, int Tmax, int max_heads,
                                     int dtype);
-int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, const void *Wq,
+int csf_sparse_attention_decode(csf_handle h, const void *x, int d, int H, int dh, int dtype, const void *Wq,
                                 const void *Wk, const void *Wv, const float *bq, const float *bk,
                                 const float *bv, const void *WoT, void *Kc, void *Vc, int Tmax,
                                 int32_t *len, const int32_t *heads, const int32_t *count,
@@ -455,7 +486,7 @@ int csf_sparse_attention_decode(const void *x, int d, int H, int dh, int dtype, 
  * Workspace: csf_attention_workspace_size(CSF_OP_ATTN_LAYER, d, H, dh, r, Tmax,
  * k >= 0 ? k : H, dtype).
  * ------------------------------------------------------------------------------------------- */
-int csf_sparse_attention_layer(const void *x, int d, int H, int dh, int r, int dtype,
+int csf_sparse_attention_layer(csf_handle h, const void *x, int d, int H, int dh, int r, int dtype,
                                const void *Vp, const void *Up, const void *Wq, const void *Wk,
                                const void *Wv, const float *bq, const float *bk, const float *bv,
                                const void *WoT, void *Kc, void *Vc, int Tmax, int32_t *len, int k,

@@ -1,8 +1,10 @@
 """CPU-side checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
 arguments on the host with the documented status before anything is enqueued.
 
-No call here passes validation, so no kernel is launched and no GPU is needed.  Device pointers
-are stand-in addresses that the host code never dereferences.
+No call here passes validation, so no kernel is launched and no GPU is needed: the handle is
+checked after every other argument, so argument errors are reported with a NULL handle, and a call
+whose arguments are all valid stops at the NULL handle.  Device pointers are stand-in addresses
+that the host code never dereferences.
 """
 import ctypes
 import json
@@ -36,10 +38,35 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert L.csf_abi_version() == 1
+    assert L.csf_abi_version() == 2
     assert L.csf_status_string(0) == b"CSF_OK"
     assert L.csf_status_string(4) == b"CSF_ERR_WORKSPACE_TOO_SMALL"
     assert L.csf_status_string(99) == b"CSF_ERR_UNKNOWN"
+
+
+def test_handle_lifecycle_on_the_host():
+    h = ctypes.c_void_p()
+    assert L.csf_create(None, 0) == INVALID
+    assert L.csf_destroy(None) == OK                       # NULL is accepted
+    assert L.csf_get_device_info(None, None, None) == INVALID
+    assert L.csf_set_ffn_flags(None, 0) == INVALID
+    assert L.csf_set_ffn_gate_threshold(None, ctypes.c_float(0.0)) == INVALID
+    assert L.csf_set_trace_events(None, None, 0) == INVALID
+    rc = L.csf_create(ctypes.byref(h), -1)
+    assert rc in (INVALID, HIP) and not h.value            # a bad index (or no runtime): no handle
+    rc = L.csf_create(ctypes.byref(h), 0)
+    assert rc in (OK, HIP)                                 # HIP: no device in this container
+    if rc == OK:
+        assert h.value
+        assert L.csf_destroy(h) == OK
+
+
+def test_valid_arguments_stop_at_a_missing_handle():
+    assert L.csf_select_topk(NULL, P, 1, 100, 5, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert b"handle" in L.csf_last_error()
+    assert L.csf_sparse_ffn(NULL, P, 1, 64, 100, csf.RELU, csf.F16, P, NULL, NULL, P, P, 10, NULL,
+                            10, NULL, P, P, 1 << 24, NULL) == INVALID
+    assert b"handle" in L.csf_last_error()
 
 
 def test_workspace_sizes():
@@ -54,7 +81,7 @@ def test_workspace_sizes():
 
 
 def predict(x=P, B=1, d=64, V=P, r=16, U=P, f=100, dt=csf.F16, s=P, ws=P, wsb=1 << 20):
-    return L.csf_predict_active(x, B, d, V, r, U, f, dt, s, ws, wsb, NULL)
+    return L.csf_predict_active(NULL, x, B, d, V, r, U, f, dt, s, ws, wsb, NULL)
 
 
 def test_predict_validation():
@@ -75,22 +102,22 @@ def test_predict_validation():
 
 
 def test_select_validation():
-    assert L.csf_select_topk(P, 1, 100, 101, P, NULL, NULL, NULL, 0, NULL) == INVALID
-    assert L.csf_select_topk(P, 1, 100, -1, P, NULL, NULL, NULL, 0, NULL) == INVALID
-    assert L.csf_select_topk(P, 1, 70000, 5, P, NULL, NULL, NULL, 0, NULL) == UNSUPPORTED
-    assert L.csf_select_topk(P, 1, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == INVALID
-    assert L.csf_select_topk(P, 1, 100, 5, P, Q, NULL, NULL, 0, NULL) == MISALIGNED
-    assert L.csf_select_threshold(P, 1, 100, ctypes.c_float(float("nan")), P, P, NULL, NULL, 0,
+    assert L.csf_select_topk(NULL, P, 1, 100, 101, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(NULL, P, 1, 100, -1, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(NULL, P, 1, 70000, 5, P, NULL, NULL, NULL, 0, NULL) == UNSUPPORTED
+    assert L.csf_select_topk(NULL, P, 1, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert L.csf_select_topk(NULL, P, 1, 100, 5, P, Q, NULL, NULL, 0, NULL) == MISALIGNED
+    assert L.csf_select_threshold(NULL, P, 1, 100, ctypes.c_float(float("nan")), P, P, NULL, NULL, 0,
                                   NULL) == INVALID
-    assert L.csf_select_threshold(P, 1, 100, ctypes.c_float(0.5), P, NULL, NULL, NULL, 0,
+    assert L.csf_select_threshold(NULL, P, 1, 100, ctypes.c_float(0.5), P, NULL, NULL, NULL, 0,
                                   NULL) == INVALID                       # count is required
-    assert L.csf_select_topk(NULL, 0, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == OK
+    assert L.csf_select_topk(NULL, NULL, 0, 100, 5, NULL, NULL, NULL, NULL, 0, NULL) == OK
 
 
 def sparse(x=P, B=1, d=64, f=100, act=csf.RELU, dt=csf.F16, W1=P, b1=NULL, Wup=NULL, W2T=P,
            idx=P, stride=10, count=NULL, maxc=10, h=NULL, y=P, ws=P, wsb=1 << 24):
-    return L.csf_sparse_ffn(x, B, d, f, act, dt, W1, b1, Wup, W2T, idx, stride, count, maxc, h,
-                            y, ws, wsb, NULL)
+    return L.csf_sparse_ffn(NULL, x, B, d, f, act, dt, W1, b1, Wup, W2T, idx, stride, count, maxc,
+                            h, y, ws, wsb, NULL)
 
 
 def test_sparse_ffn_validation():
@@ -108,7 +135,7 @@ def test_sparse_ffn_validation():
     assert sparse(d=64, dt=csf.F32, wsb=8) == WS_SMALL
     assert sparse(idx=NULL) == INVALID
     assert sparse(maxc=70000, stride=70000) == UNSUPPORTED   # longer than a list the kernels take
-    assert L.csf_dense_ffn(P, 1, 64, 70000, csf.RELU, csf.F16, P, NULL, NULL, P, NULL, P, P,
+    assert L.csf_dense_ffn(NULL, P, 1, 64, 70000, csf.RELU, csf.F16, P, NULL, NULL, P, NULL, P, P,
                            1 << 30, NULL) == UNSUPPORTED
 
 
@@ -117,7 +144,7 @@ def test_layer_validation():
         a = dict(x=P, d=64, f=100, act=csf.RELU, dt=csf.F16, V=P, U=P, W1=P, b1=NULL, Wup=NULL,
                  W2T=P, y=P, ws=P, wsb=1 << 24)
         a.update(kw)
-        return L.csf_sparse_ffn_layer(a["x"], a["d"], a["f"], r, a["act"], a["dt"], a["V"], a["U"],
+        return L.csf_sparse_ffn_layer(NULL, a["x"], a["d"], a["f"], r, a["act"], a["dt"], a["V"], a["U"],
                                       a["W1"], a["b1"], a["Wup"], a["W2T"], k, ctypes.c_float(tau),
                                       a["y"], NULL, NULL, NULL, a["ws"], a["wsb"], NULL)
     assert layer(k=-2) == INVALID
@@ -133,7 +160,7 @@ def test_batched_union_validation():
 
     def bu(X=P, B=4, d=256, f=100, act=csf.RELU, dt=csf.F16, W1=P, b1=NULL, Wup=NULL, W2T=P,
            bm=P, sem=0, path=0, Y=P, uc=NULL, ws=P, wsb=1 << 26):
-        return L.csf_sparse_ffn_batched_union(X, B, d, f, act, dt, W1, b1, Wup, W2T, bm, sem, path,
+        return L.csf_sparse_ffn_batched_union(NULL, X, B, d, f, act, dt, W1, b1, Wup, W2T, bm, sem, path,
                                               Y, uc, ctypes.byref(taken), ws, wsb, NULL)
     assert bu(B=33) == UNSUPPORTED                         # more tokens than one call takes
     assert bu(B=-1) == INVALID
@@ -161,7 +188,7 @@ def test_batched_layer_validation():
     taken = ctypes.c_int(-1)
 
     def bl(k=5, tau=0.5, r=16, B=4, V=P, bm=NULL, path=0, wsb=1 << 26):
-        return L.csf_sparse_ffn_batched_layer(P, B, 256, 100, r, csf.RELU, csf.F16, V, P, P, NULL,
+        return L.csf_sparse_ffn_batched_layer(NULL, P, B, 256, 100, r, csf.RELU, csf.F16, V, P, P, NULL,
                                               NULL, P, k, ctypes.c_float(tau), 0, path, P, bm,
                                               NULL, ctypes.byref(taken), P, wsb, NULL)
     assert bl(k=-2) == INVALID
@@ -184,7 +211,7 @@ def test_stack_validation():
 
     def st(layers=lw, L=2, k=5, tau=0.5, mode=0, norm=1, eps=1e-6, x=P, B=1, side=NULL, wsb=1 << 26,
            r=16, stream=NULL):
-        return L_.csf_stack_forward(layers, L, 256, 100, r, csf.RELU, csf.F16, x, B, mode, k,
+        return L_.csf_stack_forward(NULL, layers, L, 256, 100, r, csf.RELU, csf.F16, x, B, mode, k,
                                     ctypes.c_float(tau), norm, ctypes.c_float(eps), NULL, NULL,
                                     NULL, NULL, P, wsb, stream, side)
     L_ = L
@@ -209,15 +236,12 @@ def test_stack_validation():
     assert need >= 2 * 7168 * 2 + 2 * 28672 * 4 + 2 * 5734 * 4
 
 
-def test_ffn_flags_validation():
-    assert L.csf_set_ffn_flags(2) == INVALID
-    assert L.csf_set_ffn_flags(csf.FFN_SKIP_ZERO_H) == OK
-    assert L.csf_set_ffn_flags(0) == OK
-    assert L.csf_set_ffn_gate_threshold(-0.5) == INVALID
-    assert L.csf_set_ffn_gate_threshold(float("nan")) == INVALID
-    assert L.csf_set_ffn_gate_threshold(float("inf")) == INVALID
-    assert L.csf_set_ffn_gate_threshold(0.1) == OK
-    assert L.csf_set_ffn_gate_threshold(0.0) == OK
+def test_ffn_options_need_a_live_handle():
+    """The gathered FFN's options are state of a handle, not of the calling thread: without a
+    handle they are rejected (the values themselves are checked in the GPU handle tests)."""
+    assert L.csf_set_ffn_flags(NULL, csf.FFN_SKIP_ZERO_H) == INVALID
+    assert L.csf_set_ffn_gate_threshold(NULL, ctypes.c_float(0.1)) == INVALID
+    assert b"handle" in L.csf_last_error()
 
 
 def test_k_from_ratio_matches_the_printed_figures():
@@ -251,7 +275,7 @@ def test_binding_rejects_host_tensors():
 def attn(x=P, d=256, H=8, dh=32, dt=csf.F16, Wq=P, Wk=P, Wv=P, bq=NULL, bk=NULL, bv=NULL, WoT=P,
          Kc=P, Vc=P, Tmax=64, lens=P, heads=P, count=NULL, maxh=4, kv_all=0, o=NULL, y=P, ws=P,
          wsb=1 << 26):
-    return L.csf_sparse_attention_decode(x, d, H, dh, dt, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax,
+    return L.csf_sparse_attention_decode(NULL, x, d, H, dh, dt, Wq, Wk, Wv, bq, bk, bv, WoT, Kc, Vc, Tmax,
                                          lens, heads, count, maxh, kv_all, o, y, ws, wsb, NULL)
 
 
@@ -273,13 +297,13 @@ def test_attention_validation():
     assert attn(H=1024, dh=128) == UNSUPPORTED            # H * dh beyond the row-list limit
     assert attn(d=12) == UNSUPPORTED
     assert attn(wsb=8) == WS_SMALL
-    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
+    assert L.csf_sparse_attention_layer(NULL, P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
                                         P, P, P, 64, P, 9, 0.0, 0, NULL, NULL, NULL, NULL, P, P,
                                         1 << 26, NULL) == INVALID        # k > H
-    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
+    assert L.csf_sparse_attention_layer(NULL, P, 256, 8, 32, 64, csf.F16, P, P, P, P, P, NULL, NULL, NULL,
                                         P, P, P, 64, P, -1, float("nan"), 0, NULL, NULL, NULL,
                                         NULL, P, P, 1 << 26, NULL) == INVALID   # NaN threshold
-    assert L.csf_sparse_attention_layer(P, 256, 8, 32, 64, csf.F16, NULL, P, P, P, P, NULL, NULL,
+    assert L.csf_sparse_attention_layer(NULL, P, 256, 8, 32, 64, csf.F16, NULL, P, P, P, P, NULL, NULL,
                                         NULL, P, P, P, 64, P, 2, 0.0, 0, NULL, NULL, NULL, NULL, P,
                                         P, 1 << 26, NULL) == INVALID     # no predictor
     size = csf.attention_workspace_size
