@@ -36,7 +36,8 @@ EXPORTS = ("csf_abi_version", "csf_status_string", "csf_last_error", "csf_worksp
            "csf_sparse_ffn_batched_union",
            "csf_sparse_ffn_batched_layer", "csf_stack_forward", "csf_set_ffn_flags",
            "csf_set_ffn_gate_threshold", "csf_set_trace_events", "csf_sparse_attention_decode",
-           "csf_sparse_attention_layer", "csf_attention_workspace_size")
+           "csf_sparse_attention_layer", "csf_attention_workspace_size",
+           "csf_sparse_ffn_layer_noalloc")
 
 
 class LayerWeights(ctypes.Structure):
@@ -100,6 +101,8 @@ def _load():
                                              vp, vp, vp, vp, vp, vp, i32, vp, i32, flt, i32, vp,
                                              vp, vp, vp, vp, vp, sz, vp]
     L.csf_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.csf_sparse_ffn_layer_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                               vp, vp, i32, flt, vp, vp, vp, vp, vp]
     for name in EXPORTS[4:]:
         getattr(L, name).restype = i32
     L.csf_attention_workspace_size.restype = sz

@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsf.so")
 
 ARCH = "gfx950"
-SOURCES = ["predict.hip", "predict_mfma.hip", "select.hip", "ffn.hip", "union.hip", "stack.hip", "attention.hip", "api.cpp"]
+SOURCES = ["predict.hip", "predict_mfma.hip", "select.hip", "ffn.hip", "union.hip", "stack.hip",
+           "attention.hip", "scratch.hip", "api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed float32 arithmetic.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

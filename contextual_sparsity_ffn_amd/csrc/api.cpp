@@ -818,6 +818,18 @@ int csf_create(csf_handle *out, int device)
     if (e != hipSuccess)
         return hip_status(e, "hipDeviceGetAttribute");
     REQUIRE(cus > 0, CSF_ERR_UNSUPPORTED, "device %d reports %d compute units", device, cus);
+    // the static scratch's address on this device, read with the device current
+    int prev = -1;
+    e = hipGetDevice(&prev);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    if (prev != device && (e = hipSetDevice(device)) != hipSuccess)
+        return hip_status(e, "hipSetDevice");
+    const hipError_t es = csf::scratch_init(device);
+    if (prev != device && (e = hipSetDevice(prev)) != hipSuccess)
+        return hip_status(e, "hipSetDevice");
+    if (es != hipSuccess)
+        return hip_status(es, "static scratch address (hipGetSymbolAddress)");
     csf_context *h = new (std::nothrow) csf_context;
     REQUIRE(h, CSF_ERR_INVALID_ARG, "out of host memory");
     h->device = device;
@@ -1307,6 +1319,43 @@ int csf_sparse_ffn_layer(csf_handle h, const void *x, int d, int f, int r, int a
     LayerWs w = layer_ws(d, f, r, max_count, dtype);
     CHECK_WS(ws, ws_bytes, w.total);
     CHECK_HANDLE(h);
+    csf::Trace tr = make_trace(h);
+    return enqueue_layer1(h, x, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, y,
+                          scores_out, idx_out, count_out, nullptr, ws, w,
+                          (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0, h->gate_tau,
+                          static_cast<hipStream_t>(stream), tr.ev ? &tr : nullptr);
+}
+
+int csf_sparse_ffn_layer_noalloc(csf_handle h, const void *x, int d, int f, int r, int act,
+                                 int dtype, const void *V, const void *U, const void *W1,
+                                 const float *b1, const void *Wup, const void *W2T, int k,
+                                 float tau, float *y, float *scores_out, int32_t *idx_out,
+                                 int32_t *count_out, void *stream)
+{
+    int s = validate_ffn(x, 1, d, f, act, dtype, W1, b1, Wup, W2T);
+    if (s != CSF_OK)
+        return s;
+    CHECK_ROW(r, dtype, kMaxPredChunks);
+    CHECK_PTR(V, true);
+    CHECK_PTR(U, true);
+    CHECK_PTR(y, true);
+    CHECK_PTR(scores_out, false);
+    CHECK_PTR(idx_out, false);
+    CHECK_PTR(count_out, false);
+    REQUIRE(k >= -1 && k <= f, CSF_ERR_INVALID_ARG, "k = %d must be -1 (threshold) or in [0, f = %d]",
+            k, f);
+    REQUIRE(f <= csf::select_max_f(), CSF_ERR_UNSUPPORTED, "f = %d exceeds the library's limit %d",
+            f, csf::select_max_f());
+    REQUIRE(k >= 0 || tau == tau, CSF_ERR_INVALID_ARG, "tau must not be NaN");
+    const int max_count = k >= 0 ? k : f;
+    LayerWs w = layer_ws(d, f, r, max_count, dtype);
+    REQUIRE(w.total <= csf::scratch_bytes(), CSF_ERR_UNSUPPORTED,
+            "this layer needs %zu bytes of scratch; the library's static scratch holds %zu "
+            "(csf_sparse_ffn_layer takes a caller workspace of any size)",
+            w.total, csf::scratch_bytes());
+    CHECK_HANDLE(h);
+    void *ws = csf::scratch_ptr(h->device);
+    REQUIRE(ws, CSF_ERR_INVALID_ARG, "the static scratch of device %d has no address", h->device);
     csf::Trace tr = make_trace(h);
     return enqueue_layer1(h, x, d, f, r, act, dtype, V, U, W1, b1, Wup, W2T, k, tau, y,
                           scores_out, idx_out, count_out, nullptr, ws, w,

@@ -170,6 +170,14 @@ int attn_max_cache();   // largest Tmax the attention kernels take
 bool attn_head_dim_supported(int dtype, int dh);
 hipError_t launch_attention_decode(const AttnArgs &a, hipStream_t stream, Trace *trace = nullptr);
 
+// ---- static scratch (scratch.hip) -------------------------------------------------------------
+// Bytes of the library's static device scratch; scratch_init reads its device address on
+// `device` (which must be current; once per device, later calls return at once) and scratch_ptr
+// returns that address (NULL before scratch_init succeeded).
+size_t scratch_bytes();
+hipError_t scratch_init(int device);
+void *scratch_ptr(int device);
+
 // ---- stack of blocks (stack.hip) -------------------------------------------------------------
 // xhat[t] = storage-type rounding of x[t] / sqrt(mean(x[t]^2) + eps) (norm = 1) or of x[t]
 // (norm = 0); x_log / xhat_log (optional) receive copies of x and xhat.

@@ -266,6 +266,26 @@ int csf_sparse_ffn_layer(csf_handle h, const void *x, int d, int f, int r, int a
                          void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csf_sparse_ffn_layer_noalloc -- csf_sparse_ffn_layer without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same kernels and bits as csf_sparse_ffn_layer, with the
+ * library's static device scratch (8 MiB per GPU, created when the library is loaded on the GPU
+ * and held until the process ends) as the workspace.  The call allocates nothing.
+ *   Arguments as csf_sparse_ffn_layer, without ws / ws_bytes.
+ *   A layer whose workspace (csf_workspace_size(h, CSF_OP_LAYER, 1, d, f, r, k >= 0 ? k : f,
+ *   dtype)) exceeds the scratch is refused with CSF_ERR_UNSUPPORTED before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch (through every handle of the GPU): calls whose
+ * work overlaps on one GPU -- on different streams, or from different threads -- race and give
+ * undefined results.  Calls ordered on one stream are safe: each call's first kernel writes
+ * every scratch word a later kernel of the call reads before it is read.
+ * ------------------------------------------------------------------------------------------- */
+int csf_sparse_ffn_layer_noalloc(csf_handle h, const void *x, int d, int f, int r, int act,
+                                 int dtype, const void *V, const void *U, const void *W1,
+                                 const float *b1, const void *Wup, const void *W2T, int k,
+                                 float tau, float *y, float *scores_out, int32_t *idx_out,
+                                 int32_t *count_out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csf_sparse_ffn_layer_hot -- one token through a layer whose neurons are ordered hot first: the
  * leading `hot` neurons are always computed (no prediction), the predictor scores only the cold
  * remainder, and the top-k_cold (k_cold >= 0) or thresholded (k_cold == -1, tau) cold neurons
