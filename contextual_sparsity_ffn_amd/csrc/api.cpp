@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -92,10 +93,36 @@ constexpr long kMaxPredChunks = 512;       // r: 16-byte chunks per row of U
             return fail(status, __VA_ARGS__);      \
     } while (0)
 
-// A handle is checked after every other argument (so host-side argument checks need none) and
-// before anything is enqueued: it must be live and belong to the current device.
-int check_handle(csf_handle h)
+// Test hook: the environment variable CSF_FAULT_INJECT names entry points (comma-separated, or
+// "all") whose dispatch fails with CSF_ERR_HIP once their arguments have passed every check and
+// before anything is enqueued, so a caller can exercise its handling of a HIP failure without a
+// failing device (and without a device at all).  Read on every call; unset or empty: off.
+bool fault_injected(const char *op)
 {
+    const char *v = getenv("CSF_FAULT_INJECT");
+    if (!v || !*v)
+        return false;
+    if (!strcmp(v, "all"))
+        return true;
+    const size_t n = strlen(op);
+    for (const char *p = v;;) {
+        const char *c = strchr(p, ',');
+        const size_t len = c ? (size_t)(c - p) : strlen(p);
+        if (len == n && !strncmp(p, op, n))
+            return true;
+        if (!c)
+            return false;
+        p = c + 1;
+    }
+}
+
+// A handle is checked after every other argument (so host-side argument checks need none) and
+// before anything is enqueued: it must be live and belong to the current device.  The fault
+// injection hook comes first, so it also answers for a call without a live handle.
+int check_handle(csf_handle h, const char *op)
+{
+    if (fault_injected(op))
+        return fail(CSF_ERR_HIP, "%s: failure injected by CSF_FAULT_INJECT (nothing enqueued)", op);
     if (!is_live(h))
         return fail(CSF_ERR_INVALID_ARG, "handle is NULL or not a live handle (csf_create)");
     int dev = -1;
@@ -110,7 +137,7 @@ int check_handle(csf_handle h)
 
 #define CHECK_HANDLE(h)                                    \
     do {                                                   \
-        int _s = check_handle(h);                          \
+        int _s = check_handle(h, __func__);                \
         if (_s != CSF_OK)                                  \
             return _s;                                     \
     } while (0)
@@ -254,7 +281,7 @@ LayerWs layer_ws(int d, int f, int r, int max_count, int dtype)
 constexpr int kMfmaMinBatch = 2;   // measured: from two tokens on the matrix-core path is faster
 
 struct UnionWs {
-    size_t ulist, ucount, h, hlo, partials, total;
+    size_t ulist, ucount, hmax, h, partials, total;
 };
 UnionWs union_ws(int B, int d, int f, int dtype, int cus)
 {
@@ -263,12 +290,10 @@ UnionWs union_ws(int B, int d, int f, int dtype, int cus)
     const size_t Bn = B > 0 ? (size_t)B : 1;
     w.ulist = 0;
     w.ucount = round_up((size_t)f * sizeof(int32_t));
+    w.hmax = w.ucount + kAlign / 2;   // the union size, then the per-token |h| maxima
+    static_assert(csf::kMaxUnionBatch * sizeof(uint32_t) <= kAlign / 2, "maxima fit the line");
     w.h = w.ucount + kAlign;
-    // float32 h (gather path) or hi and lo 16-bit halves (matrix-core path) share this region
-    w.hlo = w.h + round_up(Bn * hs * sizeof(uint16_t));
-    const size_t h32_end = w.h + round_up(Bn * hs * sizeof(float));
-    const size_t hlo_end = w.hlo + round_up(Bn * hs * sizeof(uint16_t));
-    w.partials = h32_end > hlo_end ? h32_end : hlo_end;
+    w.partials = w.h + round_up(Bn * hs * sizeof(float));
     int nch = csf::union_num_chunks(0, d, dtype, f, cus);
     const int nm = csf::union_num_chunks(1, d, dtype, f, cus);
     if (nm > nch)
@@ -445,8 +470,7 @@ int enqueue_union(const void *X, int B, int d, int f, int act, int dtype, const 
     a.ulist = reinterpret_cast<int32_t *>(at(ws, w.ulist));
     a.ucount = reinterpret_cast<int32_t *>(at(ws, w.ucount));
     a.h32 = reinterpret_cast<float *>(at(ws, w.h));
-    a.hhi = reinterpret_cast<uint16_t *>(at(ws, w.h));
-    a.hlo = reinterpret_cast<uint16_t *>(at(ws, w.hlo));
+    a.hmax = reinterpret_cast<uint32_t *>(at(ws, w.hmax));
     a.hs = (int)csf::union_h_stride(f);
     a.partials = reinterpret_cast<float *>(at(ws, w.partials));
     return hip_status(csf::launch_union_ffn(a, st, tr), "batched union FFN launch");

@@ -88,6 +88,9 @@ struct F16T {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                        __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    // largest power of two a value split into 16-bit terms may reach unscaled: binary16 holds
+    // magnitudes up to 65504, so |v| >= 2^15 is scaled down first (split_shift below)
+    static constexpr int kSplitExp = 15;
     // round to nearest even (the conversion instruction's default mode)
     __device__ static __forceinline__ uint16_t round_bits(float v)
     {
@@ -122,6 +125,8 @@ struct BF16T {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                         __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
+    // bfloat16 has binary32's exponent range: only |v| >= 2^127 (next to overflow) is scaled
+    static constexpr int kSplitExp = 127;
     // round to nearest even on the bit pattern (finite inputs)
     __device__ static __forceinline__ uint16_t round_bits(float v)
     {
@@ -130,6 +135,29 @@ struct BF16T {
     }
     __device__ static __forceinline__ float widen_bits(uint16_t b) { return u2f((uint32_t)b << 16); }
 };
+
+// ---- scaled split of float32 values into 16-bit terms ------------------------------------------
+// A float32 vector v that feeds a 16-bit matrix-core product is written as v = t0 + t1 (+ t2),
+// t0 = round(v), t1 = round(v - t0), ...  For binary16 that overflows once |v| reaches 65520, so
+// the split is taken of v 2^k instead, with k <= 0 chosen from the largest |v| of the vector (its
+// float32 bits with the sign cleared, `maxbits`) so that the largest scaled value lies in
+// [2^(E-1), 2^E), E = T::kSplitExp; the product is multiplied by 2^-k afterwards.  Powers of
+// two scale exactly, so k = 0 (every |v| < 2^E, the common case) leaves the bits unchanged, and
+// a non-finite maximum gets k = 0 (nothing to rescale: the outputs are non-finite).
+template <class T>
+__device__ __forceinline__ bool split_needs_scale(uint32_t absbits)
+{
+    return absbits >= (uint32_t)(127 + T::kSplitExp) << 23;
+}
+template <class T>
+__device__ __forceinline__ int split_shift(uint32_t maxbits)
+{
+    if (!split_needs_scale<T>(maxbits) || maxbits >= 0x7f800000u)
+        return 0;
+    return T::kSplitExp - 1 - ((int)(maxbits >> 23) - 127);   // in [kSplitExp - 128, -1]
+}
+// 2^k for k in [-126, 127]
+__device__ __forceinline__ float pow2_exact(int k) { return u2f((uint32_t)(127 + k) << 23); }
 
 // ---- hand-over between workgroups of one kernel -------------------------------------------------
 // Each XCD has its own L2, and the L2s are not coherent with one another.  Values that one

@@ -750,8 +750,8 @@ hipError_t launch_ffn_fused(const FfnArgs &a, uint32_t *sync, hipStream_t st, Tr
 {
     if (a.B != 1 || a.skip_zero)
         return hipErrorInvalidValue;
-    if (a.max_count == 0)
-        return hipSuccess;
+    if (a.max_count == 0)   // an empty list still writes y = 0 (or leaves y for accumulate)
+        return launch_ffn(a, st, tr);
     if (a.dtype == 0) return fused_t<F32T>(a, sync, st, tr);
     if (a.dtype == 1) return fused_t<F16T>(a, sync, st, tr);
     return fused_t<BF16T>(a, sync, st, tr);

@@ -201,8 +201,8 @@ struct UnionArgs {
     // workspace
     int32_t *ulist;         // [f]
     int32_t *ucount;        // [1]
-    float *h32;             // [B][hs] (vector ALU path)
-    uint16_t *hhi, *hlo;    // [B][hs] each (matrix-core path)
+    float *h32;             // [B][hs]
+    uint32_t *hmax;         // [kMaxUnionBatch] per-token largest |h| past the 16-bit split limit
     int hs;                 // union_h_stride(f)
     float *partials;        // [B][union_num_chunks][d]
 };

@@ -9,10 +9,13 @@
 // 16 or 32), so every weight row is read once for the whole batch:
 //   k_pred_down_mfma  tile of 16 rows of V x (a range of the d steps); the 4 waves of a workgroup
 //                     split that range and are summed in order; float32 partial sums out;
-//   k_pred_hidden     a = relu(sum of the partials, in order), written as NA 16-bit terms
-//                     a = t0 + t1 (+ t2) (t0 = round(a), t1 = round(a - t0), ...): about 22 bits
-//                     of a for binary16 (NA = 2) and 24 for bfloat16 (NA = 3), so the products
-//                     with U (exact in float32) lose nothing the float32 scores would keep;
+//   k_pred_hidden     one workgroup per token: a = relu(sum of the partials, in order), written
+//                     as NA 16-bit terms of a 2^k, a 2^k = t0 + t1 (+ t2) (t0 = round(a 2^k),
+//                     t1 = round(a 2^k - t0), ...): about 22 bits of a for binary16 (NA = 2) and
+//                     24 for bfloat16 (NA = 3), so the products with U (exact in float32) lose
+//                     nothing the float32 scores would keep.  k = 0 unless the token's largest a
+//                     reaches the 16-bit split limit (2^15 for binary16); the up projection
+//                     multiplies the token's sums by 2^-k before the sigmoid;
 //   k_pred_up_mfma    tile of 16 rows of U, the 4 waves split r; sigmoid epilogue
 //                     (k_pred_up_mfma_res when r <= 512: the hidden terms held in registers
 //                     across the tiles of a 512-workgroup grid).
@@ -101,28 +104,74 @@ __global__ __launch_bounds__(256) void k_pred_down_mfma(const u32x4 *__restrict_
     }
 }
 
+constexpr int kHiddenThreads = 1024;
+constexpr int kHiddenKeep = 4;     // hidden values per thread kept in registers between the passes
+
 template <class T, int NA>
-__global__ __launch_bounds__(256) void k_pred_hidden(const float *__restrict__ part, int ks_n,
-                                                     int B, int r, uint16_t *__restrict__ ahid)
+__global__ __launch_bounds__(kHiddenThreads) void k_pred_hidden(const float *__restrict__ part,
+                                                                int ks_n, int B, int r,
+                                                                uint16_t *__restrict__ ahid,
+                                                                float *__restrict__ hinv)
 {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= B * r)
-        return;
-    float a = 0.0f;
-    for (int ks = 0; ks < ks_n; ++ks)
-        a += part[(size_t)ks * B * r + i];
-    a = a > 0.0f ? a : 0.0f;
+    __shared__ uint32_t wmax[kHiddenThreads / kWave];
+    const int tok = blockIdx.x, t = threadIdx.x;
+    const float *pt = part + (size_t)tok * r;
+    const size_t kstride = (size_t)B * r;
+    auto hidden = [&](int j) {
+        float a = 0.0f;
+#pragma unroll 8
+        for (int ks = 0; ks < ks_n; ++ks)
+            a += pt[ks * kstride + j];
+        return a > 0.0f ? a : 0.0f;
+    };
+    // pass 1: the token's largest a (a >= 0, so its float32 bits order like its value)
+    float keep[kHiddenKeep];
+    uint32_t mx = 0u;
 #pragma unroll
-    for (int e = 0; e < NA; ++e) {
-        const uint16_t b = T::round_bits(a);
-        ahid[(size_t)e * B * r + i] = b;
-        a -= T::widen_bits(b);
+    for (int q = 0; q < kHiddenKeep; ++q) {
+        const int j = t + kHiddenThreads * q;
+        keep[q] = j < r ? hidden(j) : 0.0f;
+        mx = max(mx, __float_as_uint(keep[q]));
     }
+    for (int j = t + kHiddenThreads * kHiddenKeep; j < r; j += kHiddenThreads)
+        mx = max(mx, __float_as_uint(hidden(j)));
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if ((t & (kWave - 1)) == 0)
+        wmax[t / kWave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kHiddenThreads / kWave; ++i)
+        mx = max(mx, wmax[i]);
+    // pass 2: the terms of a 2^k (values past the kept ones are recomputed in the same order)
+    const int k = split_shift<T>(mx);
+    const float sc = pow2_exact(k);
+    if (t == 0)
+        hinv[tok] = pow2_exact(-k);
+    auto put = [&](int j, float a) {
+        a *= sc;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const uint16_t b = T::round_bits(a);
+            ahid[((size_t)e * B + tok) * r + j] = b;
+            a -= T::widen_bits(b);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < kHiddenKeep; ++q) {
+        const int j = t + kHiddenThreads * q;
+        if (j < r)
+            put(j, keep[q]);
+    }
+    for (int j = t + kHiddenThreads * kHiddenKeep; j < r; j += kHiddenThreads)
+        put(j, hidden(j));
 }
 
 template <class T, int MT, int NA>
 __global__ __launch_bounds__(256) void k_pred_up_mfma(const u32x4 *__restrict__ U,
-                                                      const uint16_t *__restrict__ ahid, int B,
+                                                      const uint16_t *__restrict__ ahid,
+                                                      const float *__restrict__ hinv, int B,
                                                       int r, int f, float *__restrict__ s)
 {
     __shared__ float red[4][MT * 4][kWave];
@@ -141,6 +190,15 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma(const u32x4 *__restrict__ 
 #pragma unroll
         for (int e = 0; e < NA; ++e)
             ar[e][m] = reinterpret_cast<const u32x4 *>(ahid + ((size_t)e * B + (aok[m] ? tok : 0)) * r);
+    }
+    // the token scales of the epilogue elements this thread writes (the same in every tile;
+    // MT * 4 * kWave = 256 MT elements, element t + 256 q for thread t)
+    float tinv[MT];
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+        const int e = t + 256 * q, mi = e / kWave, l = e % kWave;
+        const int tok = 16 * (mi / 4) + 4 * (l >> 4) + (mi % 4);
+        tinv[q] = tok < B ? hinv[tok] : 1.0f;
     }
     for (int n0 = blockIdx.x * 16; n0 < f; n0 += gridDim.x * 16) {
         const int n = n0 + ln;
@@ -179,12 +237,14 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma(const u32x4 *__restrict__ 
         }
         sum_waves<MT>(red, acc, w, lane);
         __syncthreads();
-        for (int e = t; e < MT * 4 * kWave; e += 256) {
-            const int mi = e / kWave, l = e % kWave;
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+            const int e = t + 256 * q, mi = e / kWave, l = e % kWave;
             const int tok = 16 * (mi / 4) + 4 * (l >> 4) + (mi % 4);
             const int nn = n0 + (l & 15);
             if (tok < B && nn < f) {
-                const float z = (red[0][mi][l] + red[1][mi][l]) + (red[2][mi][l] + red[3][mi][l]);
+                const float z = ((red[0][mi][l] + red[1][mi][l]) + (red[2][mi][l] + red[3][mi][l])) *
+                                tinv[q];
                 s[(size_t)tok * f + nn] = 1.0f / (1.0f + expf(-z));
             }
         }
@@ -200,7 +260,8 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma(const u32x4 *__restrict__ 
 // so the same scores.
 template <class T, int MT, int NA, int KW>
 __global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restrict__ U,
-                                                          const uint16_t *__restrict__ ahid, int B,
+                                                          const uint16_t *__restrict__ ahid,
+                                                          const float *__restrict__ hinv, int B,
                                                           int r, int f, float *__restrict__ s)
 {
     __shared__ float red[4][MT * 4][kWave];
@@ -231,6 +292,15 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restric
         for (int q = 0; q < KW; ++q)
             dst[q] = (n0 < f && q < ns) ? ld_stream(wr + 4 * (s0 + q) + g) : zero;
     };
+    // the token scales of the epilogue elements this thread writes (the same in every tile;
+    // MT * 4 * kWave = 256 MT elements, element t + 256 q for thread t)
+    float tinv[MT];
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+        const int e = t + 256 * q, mi = e / kWave, l = e % kWave;
+        const int tok = 16 * (mi / 4) + 4 * (l >> 4) + (mi % 4);
+        tinv[q] = tok < B ? hinv[tok] : 1.0f;
+    }
     u32x4 rw[KW];
     load_tile(blockIdx.x * 16, rw);
     for (int n0 = blockIdx.x * 16; n0 < f; n0 += gridDim.x * 16) {
@@ -252,12 +322,14 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restric
         }
         sum_waves<MT>(red, acc, w, lane);
         __syncthreads();
-        for (int e = t; e < MT * 4 * kWave; e += 256) {
-            const int mi = e / kWave, l = e % kWave;
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+            const int e = t + 256 * q, mi = e / kWave, l = e % kWave;
             const int tok = 16 * (mi / 4) + 4 * (l >> 4) + (mi % 4);
             const int nn = n0 + (l & 15);
             if (tok < B && nn < f) {
-                const float z = (red[0][mi][l] + red[1][mi][l]) + (red[2][mi][l] + red[3][mi][l]);
+                const float z = ((red[0][mi][l] + red[1][mi][l]) + (red[2][mi][l] + red[3][mi][l])) *
+                                tinv[q];
                 s[(size_t)tok * f + nn] = 1.0f / (1.0f + expf(-z));
             }
         }
@@ -270,8 +342,8 @@ __global__ __launch_bounds__(256) void k_pred_up_mfma_res(const u32x4 *__restric
 
 template <class T, int MT, int NA>
 hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, const u32x4 *U,
-                         int f, float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr,
-                         int res_grid)
+                         int f, float *s, float *part, uint16_t *ahid, float *hinv, hipStream_t st,
+                         Trace *tr, int res_grid)
 {
     const int C = d / 8;
     const int ks_n = pred_mfma_split(r, d);
@@ -279,8 +351,8 @@ hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, co
                           C, r, ks_n, part);
     if (e != hipSuccess)
         return e;
-    e = launch(k_pred_hidden<T, NA>, dim3((B * r + 255) / 256), dim3(256), st, tr, part, ks_n, B, r,
-               ahid);
+    e = launch(k_pred_hidden<T, NA>, dim3(B), dim3(kHiddenThreads), st, tr, part, ks_n, B, r, ahid,
+               hinv);
     if (e != hipSuccess)
         return e;
     const int tiles = (f + 15) / 16;
@@ -289,15 +361,16 @@ hipError_t predict_group(const u32x4 *x, int B, int d, const u32x4 *V, int r, co
         // 12.9 us at 8 / 16 / 32 tokens, against 9.7 / 12.4 / 20.9 for k_pred_up_mfma; one or four
         // per CU and one workgroup per tile measured slower
         return launch(k_pred_up_mfma_res<T, MT, NA, 4>, dim3(tiles < res_grid ? tiles : res_grid),
-                      dim3(256), st, tr, U, ahid, B, r, f, s);
+                      dim3(256), st, tr, U, ahid, hinv, B, r, f, s);
     }
     return launch(k_pred_up_mfma<T, MT, NA>, dim3(tiles < 4096 ? tiles : 4096), dim3(256), st, tr,
-                  U, ahid, B, r, f, s);
+                  U, ahid, hinv, B, r, f, s);
 }
 
 template <class T, int NA>
 hipError_t predict_t(const void *x, int B, int d, const void *V, int r, const void *U, int f,
-                     float *s, float *part, uint16_t *ahid, hipStream_t st, Trace *tr, int res_grid)
+                     float *s, float *part, uint16_t *ahid, float *hinv, hipStream_t st, Trace *tr,
+                     int res_grid)
 {
     for (int b0 = 0; b0 < B; b0 += kMaxPredMfmaTokens) {
         const int nb = B - b0 < kMaxPredMfmaTokens ? B - b0 : kMaxPredMfmaTokens;
@@ -305,9 +378,11 @@ hipError_t predict_t(const void *x, int B, int d, const void *V, int r, const vo
         float *sb = s + (size_t)b0 * f;
         hipError_t e = nb <= 16
             ? predict_group<T, 1, NA>(xb, nb, d, static_cast<const u32x4 *>(V), r,
-                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr, res_grid)
+                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, hinv, st, tr,
+                                      res_grid)
             : predict_group<T, 2, NA>(xb, nb, d, static_cast<const u32x4 *>(V), r,
-                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, st, tr, res_grid);
+                                      static_cast<const u32x4 *>(U), f, sb, part, ahid, hinv, st, tr,
+                                      res_grid);
         if (e != hipSuccess)
             return e;
     }
@@ -337,8 +412,9 @@ bool pred_mfma_supported(int dtype, int B, int d, int r)
 size_t pred_mfma_ws_floats(int B, int r)
 {
     const int nb = B < kMaxPredMfmaTokens ? B : kMaxPredMfmaTokens;
-    // partial sums [split][nb][r] float32, then NA <= 3 16-bit terms [3][nb][r] (as floats: / 2)
-    return (size_t)kMaxPredMfmaSplit * nb * r + ((size_t)3 * nb * r + 1) / 2 + 64;
+    // partial sums [split][nb][r] float32, then NA <= 3 16-bit terms [3][nb][r] (as floats: / 2),
+    // then the per-token scales [nb] float32 (plus alignment)
+    return (size_t)kMaxPredMfmaSplit * nb * r + ((size_t)3 * nb * r + 1) / 2 + kMaxPredMfmaTokens + 64;
 }
 
 hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const void *V, int r,
@@ -352,9 +428,10 @@ hipError_t launch_predict_mfma(int dtype, const void *x, int B, int d, const voi
     // 16-byte aligned start for the 16-bit terms
     size_t off = ((size_t)kMaxPredMfmaSplit * nb * r + 3) / 4 * 4;
     uint16_t *ahid = reinterpret_cast<uint16_t *>(ws + off);
+    float *hinv = ws + off + ((size_t)3 * nb * r + 1) / 2;
     if (dtype == 1)
-        return predict_t<F16T, 2>(x, B, d, V, r, U, f, s, part, ahid, st, tr, res_grid);
-    return predict_t<BF16T, 3>(x, B, d, V, r, U, f, s, part, ahid, st, tr, res_grid);
+        return predict_t<F16T, 2>(x, B, d, V, r, U, f, s, part, ahid, hinv, st, tr, res_grid);
+    return predict_t<BF16T, 3>(x, B, d, V, r, U, f, s, part, ahid, hinv, st, tr, res_grid);
 }
 
 }  // namespace csf

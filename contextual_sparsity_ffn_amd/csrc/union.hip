@@ -20,11 +20,16 @@
 //   matrix-core path (MFMA 16x16x32, tokens padded to 16 or 32 as M):
 //     k_union_up_lds     32 union rows x all tokens per workgroup: row and token segments staged
 //                        through LDS (whole 128-byte lines per load), M = tokens, N = rows;
-//                        h stored as a hi/lo pair of 16-bit values (hi = round(h),
-//                        lo = round(h - hi)), so the down product keeps about 22 bits of h;
+//                        h stored in float32, and each token's largest |h| past the 16-bit
+//                        split limit recorded (an atomic max, taken only on that rare path);
 //     k_union_down_mfma  tile of 256 output columns x a chunk of the union: the rows of W2T are
 //                        staged through LDS and read back column-wise, because W2T is contiguous
-//                        along the output columns while the product contracts over rows;
+//                        along the output columns while the product contracts over rows; h
+//                        enters the matrix cores as a hi/lo pair of 16-bit values of h 2^k
+//                        (hi = round(h 2^k), lo = round(h 2^k - hi); k = 0 unless the token's
+//                        |h| reaches the split limit), which keeps about 22 bits of h for
+//                        binary16 and 16 for bfloat16, and the token's outputs are scaled by
+//                        2^-k;
 //   both paths end in the ordered partial-row reduction of the single-token FFN.
 #include "common.hpp"
 #include "launch.hpp"
@@ -64,7 +69,8 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
                                                               int B, int f,
                                                               int32_t *__restrict__ ulist,
                                                               int32_t *__restrict__ ucount,
-                                                              int32_t *__restrict__ ucount_out)
+                                                              int32_t *__restrict__ ucount_out,
+                                                              uint32_t *__restrict__ hmax)
 {
     __shared__ uint32_t scan_tmp[kUnionThreads / kWave];
     __shared__ uint32_t ow[2 * kUnionThreads], opos[2 * kUnionThreads];   // OR words, prefixes
@@ -105,6 +111,8 @@ __global__ __launch_bounds__(kUnionThreads) void k_union_list(const uint32_t *__
     }
     __syncthreads();
     emit_bit_list<kUnionThreads>(ow, opos, words, total, ulist, f);
+    if (hmax && t < kMaxUnionBatch)
+        hmax[t] = 0u;                                  // per-token |h| maxima of this call
     if (t == 0) {
         *ucount = (int32_t)total;
         if (ucount_out)
@@ -294,8 +302,8 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
                                                       const int32_t *__restrict__ ucount,
                                                       const uint32_t *__restrict__ bitmaps,
                                                       int per_token, int B, int f, int C,
-                                                      uint16_t *__restrict__ hhi,
-                                                      uint16_t *__restrict__ hlo, int hs,
+                                                      float *__restrict__ h32,
+                                                      uint32_t *__restrict__ hmax, int hs,
                                                       int silu)
 {
     constexpr int RT = ROWS / 16;                // 16-row tiles of union rows
@@ -447,10 +455,10 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
                 if (per_token && !token_has(bitmaps, words, tok, jj))
                     hv = 0.0f;
             }
-            const uint16_t hi = T::round_bits(hv);
-            const uint16_t lo = T::round_bits(hv - T::widen_bits(hi));
-            hhi[(size_t)tok * hs + nn] = hi;
-            hlo[(size_t)tok * hs + nn] = lo;
+            h32[(size_t)tok * hs + nn] = hv;
+            const uint32_t hb = __float_as_uint(hv) & 0x7fffffffu;
+            if (split_needs_scale<T>(hb))
+                atomicMax(hmax + tok, hb);
         }
         __syncthreads();
     }
@@ -458,14 +466,15 @@ __global__ __launch_bounds__(256) void k_union_up_lds(const u32x4 *__restrict__ 
 
 // Down projection.  Grid (256-column tile, union chunk).  The chunk's union indices are staged in
 // LDS first.  Per K step of 32 union rows the workgroup stages the rows' 512-byte column segments
-// and the 32 rows' h values (hi and lo, every token) in LDS, double-buffered, with the global
-// loads of the next PD steps in flight in a register ring; wave w then multiplies columns
-// 64 w .. 64 w + 63 as 4 tiles of 16: A = h (tokens x 32 rows, hi then lo), B = the staged rows
-// read column-wise (W2T is contiguous along the output columns, the product contracts over rows).
+// and the 32 rows' h values of every token (split into hi and lo while they are staged) in LDS,
+// double-buffered, with the global loads of the next PD steps in flight in a register ring; wave
+// w then multiplies columns 64 w .. 64 w + 63 as 4 tiles of 16: A = h (tokens x 32 rows, hi then
+// lo), B = the staged rows read column-wise (W2T is contiguous along the output columns, the
+// product contracts over rows).
 template <class T, int MT, int PD>
 __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict__ W2T,
-                                                         const uint16_t *__restrict__ hhi,
-                                                         const uint16_t *__restrict__ hlo,
+                                                         const float *__restrict__ h32,
+                                                         const uint32_t *__restrict__ hmax,
                                                          int hs,
                                                          const int32_t *__restrict__ ulist,
                                                          const int32_t *__restrict__ ucount,
@@ -487,7 +496,6 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
     const int sb = chunk * per;
     const int se = sb + per < steps ? sb + per : steps;
     const int ns = se > sb ? se - sb : 0;         // <= kMaxDownSteps (the host sizes nchunk)
-    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
     // union indices of this chunk (positions past the union read the last entry; their h is 0)
     for (int i = t; i < ns * kKStep; i += 256) {
@@ -496,12 +504,13 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
     }
     __syncthreads();
 
-    // staging: thread t moves rows srow + 8 q (q < 4) of column chunk scol, and one 16-byte
-    // piece of h: token ht, rows 8 hg .. 8 hg + 7, hi (hl = 0) or lo (hl = 1)
+    // staging: thread t moves rows srow + 8 q (q < 4) of column chunk scol, and 4 h values:
+    // token ht, rows 4 hq .. 4 hq + 3, scaled by the token's 2^k and split into hi and lo
     const int srow = t / SEG, scol = t % SEG;
-    const int hl = t >> 7, ht = (t >> 2) & 31, hg = t & 3;
+    const int ht = t >> 3, hq = t & 7;
     const bool hok = ht < B;
-    const uint16_t *hsrc = (hl ? hlo : hhi) + (size_t)(hok ? ht : 0) * hs + 8 * hg;
+    const float *hsrc = h32 + (size_t)(hok ? ht : 0) * hs + 4 * hq;
+    const float hsc = pow2_exact(hok ? split_shift<T>(hmax[ht]) : 0);
     // The ring holds raw loads (a step past the chunk re-reads its last step); they are only
     // read when staged, PD - 1 steps later, where a step past the chunk stages h = 0 (so the
     // re-read rows add nothing) and a token past B stages h = 0.
@@ -515,6 +524,14 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
         }
         rh[p] = *reinterpret_cast<const u32x4 *>(hsrc + (size_t)(sb + ic) * kKStep);
     };
+    auto split2 = [&](uint32_t a, uint32_t b, uint32_t &hi, uint32_t &lo) {
+        const float va = u2f(a) * hsc, vb = u2f(b) * hsc;
+        const uint16_t ha = T::round_bits(va), hb = T::round_bits(vb);
+        const uint16_t la = T::round_bits(va - T::widen_bits(ha));
+        const uint16_t lb = T::round_bits(vb - T::widen_bits(hb));
+        hi = (uint32_t)ha | ((uint32_t)hb << 16);
+        lo = (uint32_t)la | ((uint32_t)lb << 16);
+    };
     auto stage = [&](int p, int buf, int i) {
 #pragma unroll
         for (int q = 0; q < kKStep / 8; ++q) {
@@ -523,7 +540,13 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
             *reinterpret_cast<uint2 *>(dst) = uint2{rw[p][q].x, rw[p][q].y};
             *reinterpret_cast<uint2 *>(dst + 2) = uint2{rw[p][q].z, rw[p][q].w};
         }
-        *reinterpret_cast<u32x4 *>(&hst[buf][hl][ht][8 * hg]) = (i < ns && hok) ? rh[p] : zero;
+        uint2 hi = uint2{0u, 0u}, lo = uint2{0u, 0u};
+        if (i < ns && hok) {
+            split2(rh[p].x, rh[p].y, hi.x, lo.x);
+            split2(rh[p].z, rh[p].w, hi.y, lo.y);
+        }
+        *reinterpret_cast<uint2 *>(&hst[buf][0][ht][4 * hq]) = hi;
+        *reinterpret_cast<uint2 *>(&hst[buf][1][ht][4 * hq]) = lo;
     };
 
     f32x4 acc[4][MT];
@@ -576,7 +599,16 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
         }
     }
 
-    // D[4 g + i][ln] of tile (q, m): token 16 m + 4 g + i, column col0 + 64 w + 16 q + ln
+    // D[4 g + i][ln] of tile (q, m): token 16 m + 4 g + i, column col0 + 64 w + 16 q + ln; the
+    // token's 2^-k undoes the scale of its h (exactly: a power of two)
+    float unsc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * m + 4 * g + i;
+            unsc[m][i] = pow2_exact(tok < B ? -split_shift<T>(hmax[tok]) : 0);
+        }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int col = col0 + 64 * w + 16 * q + ln;
@@ -586,7 +618,7 @@ __global__ __launch_bounds__(256) void k_union_down_mfma(const u32x4 *__restrict
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * m + 4 * g + i;
                 if (tok < B && col < D)
-                    part[((size_t)tok * nchunk + chunk) * (size_t)D + col] = acc[q][m][i];
+                    part[((size_t)tok * nchunk + chunk) * (size_t)D + col] = acc[q][m][i] * unsc[m][i];
             }
     }
 }
@@ -654,19 +686,19 @@ hipError_t union_mfma_mt(const UnionArgs &a, hipStream_t st, Trace *tr)
         e = launch(k_union_up_lds<T, MT, 2, 3, ST, ROWS>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
-                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
+                   a.per_token, a.B, a.f, C, a.h32, a.hmax, a.hs, act_silu(a.act));
     else
         e = launch(k_union_up_lds<T, MT, 1, 3, ST, ROWS>, dim3(blocks), dim3(256), st, tr,
                    static_cast<const u32x4 *>(a.X), static_cast<const u32x4 *>(a.W1),
                    static_cast<const u32x4 *>(a.Wup), a.b1, a.ulist, a.ucount, a.bitmaps,
-                   a.per_token, a.B, a.f, C, a.hhi, a.hlo, a.hs, act_silu(a.act));
+                   a.per_token, a.B, a.f, C, a.h32, a.hmax, a.hs, act_silu(a.act));
     if (e != hipSuccess)
         return e;
     const int nchunk = union_num_chunks(1, a.d, a.dtype, a.f, a.cus);
     // two K steps of loads in flight ahead (measured at 8 / 16 / 32 tokens: 47.8 / 57.1 / 73.9 us
     // against 49.2 / 59.7 / 75.2 with three and 51.4 / 61.6 / 79.6 with four)
     e = launch(k_union_down_mfma<T, MT, 2>, dim3(a.d / kDownCols, nchunk), dim3(256), st, tr,
-               static_cast<const u32x4 *>(a.W2T), a.hhi, a.hlo, a.hs, a.ulist, a.ucount, a.B, a.f,
+               static_cast<const u32x4 *>(a.W2T), a.h32, a.hmax, a.hs, a.ulist, a.ucount, a.B, a.f,
                C, nchunk, a.partials);
     if (e != hipSuccess)
         return e;
@@ -727,7 +759,7 @@ size_t union_h_stride(int f) { return (size_t)(f + kKStep - 1) / kKStep * kKStep
 hipError_t launch_union_ffn(const UnionArgs &a, hipStream_t st, Trace *tr)
 {
     hipError_t e = launch(k_union_list, dim3(1), dim3(kUnionThreads), st, tr, a.bitmaps, a.B, a.f,
-                          a.ulist, a.ucount, a.ucount_out);
+                          a.ulist, a.ucount, a.ucount_out, a.hmax);
     if (e != hipSuccess)
         return e;
     if (a.mfma) {

@@ -40,6 +40,10 @@
  *                 enqueues anything: a non-zero status means nothing was enqueued, except
  *                 CSF_ERR_HIP, which reports a failed launch.  Device faults surface at the
  *                 caller's next synchronisation.  csf_last_error() gives a message (per thread).
+ *                 Test hook: while the environment variable CSF_FAULT_INJECT holds "all" or a
+ *                 comma-separated list of entry-point names (read on every call), those entry
+ *                 points return CSF_ERR_HIP once their arguments pass the host checks, before the
+ *                 handle check and before anything is enqueued (no device needed).
  *                 Inputs must be finite; NaN/Inf are not checked (a NaN score ranks below every
  *                 number in the top-k selections and never passes a threshold).
  *   Determinism   The same inputs give bitwise-identical outputs: no floating-point atomics, every
@@ -172,7 +176,12 @@ size_t csf_workspace_size(csf_handle h, int op, int B, int d, int f, int r, int 
  *   V       [r][d]  dtype      predictor down projection
  *   U       [f][r]  dtype      predictor up projection
  *   scores  [B][f]  float32    out: sigmoid scores in [0, 1]
- * The hidden activation relu(V x) is kept in float32; all sums accumulate in float32.
+ * The hidden activation relu(V x) is kept in float32; all sums accumulate in float32.  From 4
+ * tokens on, 16-bit weights with d and r multiples of 128 take the matrix cores, where the hidden
+ * activation enters the product with U as 16-bit terms: two for binary16 (about 22 significant
+ * bits) and three for bfloat16 (24).  A token whose largest hidden value reaches 2^15 (binary16;
+ * 2^127 for bfloat16) is scaled by a power of two 2^k before the split and its sums by 2^-k
+ * before the sigmoid (exact), so large values stay finite.
  * Workspace: csf_workspace_size(h, CSF_OP_PREDICT, B, d, f, r, 0, dtype) bytes.
  * ------------------------------------------------------------------------------------------- */
 int csf_predict_active(csf_handle h, const void *x, int B, int d, const void *V, int r, const void *U, int f,
@@ -325,9 +334,12 @@ int csf_sparse_ffn_layer_hot(csf_handle h, const void *x, int d, int f, int r, i
  *   semantics CSF_SEM_PER_TOKEN: y_t = sparse FFN of x_t over its own set (rows of the union that
  *             t did not select contribute exactly zero); CSF_SEM_UNION: over the whole union.
  *   path      CSF_PATH_AUTO, CSF_PATH_GATHER or CSF_PATH_MFMA (CSF_ERR_UNSUPPORTED if the
- *             matrix-core path is asked for float32 or d % 256 != 0).  The matrix-core path keeps
- *             h as a pair of 16-bit values (hi + lo, about 22 significant bits) and needs
- *             |h| < 65504 for binary16.
+ *             matrix-core path is asked for float32 or d % 256 != 0).  The matrix-core path
+ *             multiplies h as a pair of 16-bit values (hi + lo): about 22 significant bits of h
+ *             for binary16 and 16 for bfloat16.  A token whose largest |h| reaches 2^15
+ *             (binary16; 2^127 for bfloat16) has its h scaled by a power of two 2^k before the
+ *             split and its outputs by 2^-k after it (exact), so any finite h gives finite,
+ *             accurate outputs; a binary16 value under 2^-24 2^-k rounds to zero in the split.
  *   Y         [B][d]  float32     out
  *   union_count [1] int32         out, optional device copy of the union size
  *   path_taken  HOST int*         out, optional: CSF_PATH_GATHER or CSF_PATH_MFMA

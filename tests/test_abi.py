@@ -155,6 +155,38 @@ def test_layer_validation():
     assert layer(wsb=100) == WS_SMALL
 
 
+def test_fault_injection_hook(monkeypatch):
+    """CSF_FAULT_INJECT makes the named entry points fail with CSF_ERR_HIP once their arguments
+    pass the host checks, before the handle check and before any launch; the binding turns the
+    status into a CsfError that carries it."""
+    monkeypatch.setenv("CSF_FAULT_INJECT", "csf_sparse_ffn")
+    assert sparse() == HIP
+    assert b"CSF_FAULT_INJECT" in L.csf_last_error() and b"nothing enqueued" in L.csf_last_error()
+    assert sparse(maxc=11) == INVALID                      # argument checks still come first
+    assert L.csf_select_topk(NULL, P, 1, 100, 5, P, NULL, NULL, NULL, 0, NULL) == INVALID
+    assert b"handle" in L.csf_last_error()                 # an entry point not named: no hook
+    monkeypatch.setenv("CSF_FAULT_INJECT", "csf_predict_active,csf_select_topk")
+    assert predict() == HIP
+    assert L.csf_select_topk(NULL, P, 1, 100, 5, P, NULL, NULL, NULL, 0, NULL) == HIP
+    assert sparse() == INVALID
+    assert predict(B=0, x=NULL, s=NULL) == OK              # nothing to dispatch: no failure
+    monkeypatch.setenv("CSF_FAULT_INJECT", "csf_sparse_ffn_layer_")   # names match whole
+    assert L.csf_sparse_ffn_layer(NULL, P, 64, 100, 16, csf.RELU, csf.F16, P, P, P, NULL, NULL, P,
+                                  5, ctypes.c_float(0.5), P, NULL, NULL, NULL, P, 1 << 24,
+                                  NULL) == INVALID
+    monkeypatch.setenv("CSF_FAULT_INJECT", "all")
+    assert L.csf_sparse_ffn_layer(NULL, P, 64, 100, 16, csf.RELU, csf.F16, P, P, P, NULL, NULL, P,
+                                  5, ctypes.c_float(0.5), P, NULL, NULL, NULL, P, 1 << 24,
+                                  NULL) == HIP
+    with pytest.raises(csf.CsfError) as err:
+        _lib._check(sparse())
+    assert err.value.status == HIP and "CSF_FAULT_INJECT" in str(err.value)
+    monkeypatch.setenv("CSF_FAULT_INJECT", "")
+    assert sparse() == INVALID
+    monkeypatch.delenv("CSF_FAULT_INJECT")
+    assert sparse() == INVALID
+
+
 def test_batched_union_validation():
     taken = ctypes.c_int(-1)
 

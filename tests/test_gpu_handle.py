@@ -77,3 +77,28 @@ def test_destroyed_handle_is_refused():
     torch.cuda.synchronize()
     assert (idx == -7).all()                           # nothing ran
     assert _lib.lib.csf_destroy(h) == 1
+
+
+def test_injected_failure_reaches_the_caller_and_launches_nothing(monkeypatch):
+    """With CSF_FAULT_INJECT naming an entry point, the binding's call raises CsfError with
+    CSF_ERR_HIP and the outputs keep their old contents (nothing ran); other entry points and,
+    once the variable is cleared, the same one work as before."""
+    announce("fault injection through the binding")
+    cfg = wl.OPT175B.scaled(1024, 2000, 64)
+    L = wl.make_layer(cfg, device=DEV)
+    x = wl.make_tokens(cfg, 1, device=DEV)[0]
+    idx = torch.arange(0, cfg.f, 7, dtype=torch.int32, device=DEV)
+    y = torch.full((cfg.d,), 1234.5, dtype=torch.float32, device=DEV)
+    monkeypatch.setenv("CSF_FAULT_INJECT", "csf_sparse_ffn")
+    with pytest.raises(csf.CsfError) as err:
+        csf.sparse_ffn(x, L.W1, L.b1, None, L.W2T, idx, y=y)
+    torch.cuda.synchronize()
+    assert err.value.status == 5 and "CSF_FAULT_INJECT" in str(err.value)
+    assert bool((y == 1234.5).all())
+    s = csf.predict_active(x.reshape(1, -1), L.V, L.U)       # not named: runs
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(s).all())
+    monkeypatch.delenv("CSF_FAULT_INJECT")
+    y2 = csf.sparse_ffn(x, L.W1, L.b1, None, L.W2T, idx, y=y)
+    torch.cuda.synchronize()
+    assert y2.data_ptr() == y.data_ptr() and not bool((y == 1234.5).any())

@@ -4,6 +4,8 @@ Bars: predictor scores within 1e-5 absolute; selection bit-exact when the oracle
 scores; FFN outputs within the normwise bars of csf_testutil (1e-5 float32, 2e-2 16-bit, plus the
 tighter 1e-4 accumulation bound); integer-valued inputs bit-exact.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -66,6 +68,38 @@ def test_predict_scores(name, cfg, B):
         _, _, s_ref = orc.predict(to_orc(X[t]), o["V"], o["U"], o["dt"])
         diff = np.abs(s[t].cpu().numpy().astype(np.float64) - s_ref.astype(np.float64)).max()
         assert diff <= 1e-5, (name, t, diff)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_predict_large_hidden_keeps_its_range(dtype):
+    """The batched matrix-core predictor multiplies relu(V x) with U as 16-bit terms; binary16
+    holds magnitudes up to 65504, so a token whose hidden values reach 2^15 is split after a
+    power-of-two scale.  Half the tokens get x scaled by 2^6 and V by 2^8 (largest hidden value
+    well past 65504, checked on the oracle), with U scaled by 2^-14 so that their scores stay
+    away from 0 and 1; exact powers of two, so the oracle sees the same stored values."""
+    announce(f"predict large hidden {dtype}")
+    cfg = wl.OPT30B.scaled(1024, 2333, 128)
+    cfg = dataclasses.replace(cfg, dtype=dtype)
+    L = _layer(cfg)
+    B = 8
+    X = wl.make_tokens(cfg, B).float()
+    X[: B // 2] *= 2.0 ** 6
+    X = X.to(dtype)
+    V = (L.V.float() * 2.0 ** 8).to(dtype)
+    U = (L.U.float() * 2.0 ** -14).to(dtype)
+    s = csf.predict_active(_dev(X), _dev(V), _dev(U))
+    torch.cuda.synchronize()
+    assert torch.isfinite(s).all()
+    dt = ORC_DT[dtype]
+    mid = 0
+    for t in range(B):
+        a, _, s_ref = orc.predict(to_orc(X[t]), to_orc(V), to_orc(U), dt)
+        if t < B // 2:
+            assert a.max() > 65504, "the scaled tokens must need the wide range"
+        mid += int(((s_ref > 0.05) & (s_ref < 0.95)).sum())
+        diff = np.abs(s[t].cpu().numpy().astype(np.float64) - s_ref.astype(np.float64)).max()
+        assert diff <= 1e-5, (t, diff)
+    assert mid > B * cfg.f // 10, "scores must not all saturate"
 
 
 def _score_patterns(f, g):
@@ -381,6 +415,37 @@ def test_layer_full_size_opt175b_shape():
     o = layer_to_orc(Ld)
     ix = _check_layer_token(Ld, o, x, cfg.k, None, "c1 full")
     assert len(ix) == cfg.k
+
+
+def test_layer_empty_selection_writes_zero():
+    """k = 0, and a threshold above every score: the layer writes y = 0 (an empty list must not
+    leave y as it was)."""
+    cfg = wl.OPT175B.scaled(2048, 3001, 128)
+    Ld = _to_dev_layer(_layer(cfg))
+    x = _dev(wl.make_tokens(cfg, 1)[0])
+    for k, tau in ((0, None), (None, 1.5)):
+        announce(f"layer empty selection k={k} tau={tau}")
+        y = torch.full((cfg.d,), 7.0, dtype=torch.float32, device=DEV)
+        count = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k, tau=tau,
+                             act=cfg.act, y=y, count=count)
+        torch.cuda.synchronize()
+        assert int(count.item()) == 0 and not y.any(), (k, tau)
+
+
+def test_layer_full_size_llama_reglu_threshold():
+    """The LLaMA-class ReGLU layer at full size (d 4096, f 14336, r 256, bfloat16) in threshold
+    mode (score >= 0.5), two tokens, in the launch configuration the benchmark uses; its
+    one-kernel FFN equals the three-kernel form bit for bit."""
+    cfg = wl.LLAMA_REGLU
+    Ld = wl.make_layer(cfg, device=DEV)
+    X = wl.make_tokens(cfg, 2, device=DEV)
+    o = layer_to_orc(Ld)
+    for t in range(2):
+        announce(f"layer full size c2 token {t}")
+        ix = _check_layer_token(Ld, o, X[t], None, cfg.tau, f"c2 full token {t}")
+        assert 0 < len(ix) < cfg.f
+        _fused_vs_separate(Ld, X[t], None, cfg.tau, cfg.act, f"c2 full one-kernel {t}")
 
 
 FUSED_CASES = [

@@ -304,3 +304,44 @@ def test_batched_layer_batch_of_one_is_the_single_token_layer(name, cfg):
         assert int(uc.item()) == n
         sel = idx[:n].cpu().numpy()
         assert np.array_equal(bm[0].cpu().numpy().view(np.uint32), orc.to_bitmap(sel, cfg.f))
+
+
+@pytest.mark.parametrize("act", [csf.RELU, csf.SILU])
+def test_batched_union_large_h_keeps_its_range(act):
+    """binary16 holds magnitudes up to 65504, so the matrix-core path's 16-bit hi/lo split of h
+    must not see h itself once a token's |h| reaches 2^15: that token's h is split after a
+    power-of-two scale, and its outputs are scaled back.  W1 and b1 are scaled by 2^10 (every
+    |h| in the thousands) and two tokens' inputs by a further 2^5, which takes their largest |h|
+    past 2^16 (checked on the oracle's h); the others stay under 2^15.  Every output must be
+    finite and meet the usual bars."""
+    announce(f"batched union large h act={act}")
+    cfg = dataclasses.replace(wl.OPT30B.scaled(512, 1000, 64), act=act)
+    L0 = wl.make_layer(cfg)
+    L = wl.Layer(cfg, L0.V, L0.U, (L0.W1.float() * 2.0 ** 10).to(cfg.dtype), L0.b1 * 2.0 ** 10,
+                 L0.Wup, L0.W2T)
+    Ld = _dev_layer(L)
+    B = 6
+    X = wl.make_clustered_tokens(cfg, B)
+    sets = _random_sets(cfg.f, B, 300, seed=77)
+    o = layer_to_orc(L)
+
+    def h_max(x, t):
+        h, _ = orc.sparse_ffn(to_orc(x), o["W1"], o["b1"], o["Wup"], o["W2T"], sets[t],
+                              o["act"], o["dt"])
+        return float(np.abs(h).max())
+
+    for t in (1, 4):
+        X[t] = (X[t].float() * 2.0 ** 5).to(cfg.dtype)
+        assert h_max(X[t], t) >= 2.0 ** 16, "the scaled token must need the wide range"
+    for t in (0, 2, 3, 5):
+        assert h_max(X[t], t) < 2.0 ** 15
+    Y, taken = _run(Ld, X.to(DEV), _bitmaps(sets, cfg.f), csf.SEM_PER_TOKEN, csf.PATH_MFMA)
+    assert taken == csf.PATH_MFMA
+    assert torch.isfinite(Y).all()
+    _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"large-h act={act}")
+    # the unscaled tokens' rows do not depend on the scaled ones: the same bits without them
+    keep = [0, 2, 3, 5]
+    Y2, _ = _run(Ld, X[keep].to(DEV), _bitmaps([sets[t] for t in keep], cfg.f),
+                 csf.SEM_PER_TOKEN, csf.PATH_MFMA)
+    err = float((Y[keep] - Y2).abs().max() / Y2.abs().max())
+    assert err <= 1e-5, err
