@@ -71,7 +71,12 @@ def parse():
     ap.add_argument("--trace-steps", type=int, default=400)
     ap.add_argument("--quality-tokens", type=int, default=32)
     ap.add_argument("--dense-steps", type=int, default=64)
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=12,
+                    help="tokens of the single-thread oracle leg")
+    ap.add_argument("--cpu-tokens-mt", type=int, default=64,
+                    help="tokens of the multi-thread oracle leg")
+    ap.add_argument("--no-hash", action="store_true",
+                    help="skip the SHA-256 of the headline workload's tensors")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM bandwidth probe (context for the metric)")
@@ -88,10 +93,10 @@ def parse():
                     help="timed steps per variant of the attention-head sparsity leg (0 = skip)")
     ap.add_argument("--locality-steps", type=int, default=400,
                     help="steps of the hot-block (static locality) leg (0: skip it)")
-    ap.add_argument("--stack-tokens", type=int, default=16,
+    ap.add_argument("--stack-tokens", type=int, default=128,
                     help="tokens timed through the 48-layer OPT-30B-shape stack (0: skip)")
     ap.add_argument("--stack-layers", type=int, default=48)
-    ap.add_argument("--stack-quality-tokens", type=int, default=4)
+    ap.add_argument("--stack-quality-tokens", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -283,6 +288,27 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # ---- provenance: seeds and digests of the headline workload's tensors ---------------------
+    seeds = {"rule": "seed(config, role, layer) = 1000000 config + 1000 role + layer; each tensor "
+                     "drawn from its own torch.Generator on the GPU, float32, rounded once",
+             "headline": {"config": cfg.index,
+                          "roles": {"U": wl.ROLE_U, "V": wl.ROLE_V, "W1_noise": wl.ROLE_W1_NOISE,
+                                    "W2T": wl.ROLE_W2T, "tokens": wl.ROLE_TOKENS,
+                                    "bias_calibration": wl.ROLE_CALIB},
+                          "layers": list(range(args.layers))},
+             "other_legs": {name: c.index for name, c in (
+                 ("zero_skip_gated", wl.LLAMA_REGLU), ("silu_functional", wl.LLAMA_SWIGLU),
+                 ("batched_union", wl.OPT30B), ("static_locality", wl.OPT30B),
+                 ("attention_heads", wl.ATTN_OPT175B), ("stack", wl.OPT30B_STACK48))}}
+    digests = None
+    if not args.no_hash:
+        log("SHA-256 of the headline tensors")
+        named = [("X", X)]
+        for l, L in enumerate(layers):
+            named += [(f"layer{l}.{n}", t) for n, t in (("V", L.V), ("U", L.U), ("W1", L.W1),
+                                                        ("b1", L.b1), ("W2T", L.W2T))]
+        digests = tensor_sha256(named)
+
     # ---- post-gate zero-skip on the same plan (an option, not the metric) ---------------------
     zero_skip = None
     if args.zero_skip_steps > 0:
@@ -301,6 +327,7 @@ def main():
     # ---- batched union leg (OPT-30B shape) --------------------------------------------------
     batched = None
     locality_res = None
+    layer0 = layers[0]          # kept for the CPU baseline
     if args.batched_steps > 0 or args.locality_steps > 0:
         del layers
         torch.cuda.empty_cache()
@@ -320,8 +347,8 @@ def main():
     # ---- CPU oracle baseline (rank 0, bounded sample) ----------------------------------------
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, wl.make_layer(cfg, device=dev, layer=0), X, args.cpu_tokens,
-                           touched)
+        cpu = cpu_baseline(cfg, layer0, X, args.cpu_tokens, args.cpu_tokens_mt, touched)
+
 
     dense_b = wl.dense_bytes(cfg)
     out = {
@@ -361,6 +388,8 @@ def main():
         "true_frac": round(sum(tfrac) / len(tfrac), 4) if tfrac else None,
         "pred_frac": round(k / f, 4),
         "cpu_baseline": cpu,
+        "seeds": seeds,
+        "tensor_sha256": digests,
         "zero_skip": zero_skip,
         "silu_functional": silu,
         "attention_heads": attn,
@@ -454,22 +483,39 @@ def zero_skip_gated_leg(args, dev):
                   None if cnt_out is None else vp(cnt_out.data_ptr()), vp(ws.data_ptr()), ws_b,
                   vp(stream.cuda_stream))
 
-    # predicted and live (positive-gate) counts over a sample of (layer, token) pairs
-    counts, lives = [], []
-    for s in range(16):
-        l, t = s % nl, s % 64
+    # predicted and live (positive-gate) counts over a sample of (layer, token) pairs; the true
+    # set of a token is its positive-gate neurons (ReGLU h != 0 iff gate > 0 and up != 0), read
+    # from the library's dense FFN; the scores give the sets of the other thresholds
+    taus = (0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9)
+    counts, lives, trues = [], [], []
+    sweep = {tau: [0, 0, 0] for tau in taus}          # predicted, hits, true (summed)
+    nq = 32
+    for s in range(nq):
+        l, t = s % nl, (5 * s) % 64
         call(l, t, idx, cnt)
         L = layers[l]
         csf.dense_ffn(X[t], L.W1, L.b1, L.Wup, L.W2T, act=cfg.act, h=hd)
+        sc = csf.predict_active(X[t].reshape(1, -1), L.V, L.U)[0]
         torch.cuda.synchronize()
         n = int(cnt.item())
+        true = hd != 0
         counts.append(n)
-        # a listed neuron is live when its gate is positive; ReGLU h != 0 iff gate > 0 (and up != 0)
-        lives.append(int((hd[idx[:n].long()] != 0).sum()))
+        lives.append(int(true[idx[:n].long()].sum()))
+        trues.append(int(true.sum()))
+        for tau in taus:
+            sel = sc >= tau
+            sweep[tau][0] += int(sel.sum())
+            sweep[tau][1] += int((sel & true).sum())
+            sweep[tau][2] += int(true.sum())
     count, live = sum(counts) / len(counts), sum(lives) / len(lives)
+    ntrue = sum(trues) / len(trues)
     res = {"workload": "LLaMA-class gated layer, batch 1: d 4096, f 14336, r 256, bfloat16, ReGLU, "
                        "threshold sigmoid >= 0.5", "layers_rotated": nl,
-           "predicted_mean": round(count, 1), "live_mean": round(live, 1)}
+           "predicted_mean": round(count, 1), "live_mean": round(live, 1),
+           "quality": {"samples": nq, "recall": round(sum(lives) / max(sum(trues), 1), 4),
+                       "precision": round(sum(lives) / max(sum(counts), 1), 4),
+                       "true_frac": round(ntrue / f, 4), "pred_frac": round(count / f, 4),
+                       "true_set": "neurons with a positive gate (h != 0) on the token's input"}}
     es = 2
     plain_bytes = (r * d + f * r + d) * es + count * 3 * d * es
     skip_bytes = (r * d + f * r + d) * es + count * d * es + live * 2 * d * es
@@ -494,6 +540,38 @@ def zero_skip_gated_leg(args, dev):
     res["speedup"] = round(res["plain"]["us_per_layer"] / res["zero_skip"]["us_per_layer"], 4)
     log(f"zero-skip gated layer: plain {res['plain']['us_per_layer']} us, skip "
         f"{res['zero_skip']['us_per_layer']} us (predicted {count:.0f}, live {live:.0f})")
+
+    # threshold sweep on the predictor's own score scale: set size, recall, precision and the
+    # plain layer's time at each tau (0.5 is the configured one)
+    rows = []
+    steps = max(50, args.zero_skip_steps // 4)
+    for tau in taus:
+        def call_tau(l, t):
+            L = layers[l]
+            return fn(vp(X[t].data_ptr()), d, f, r, cfg.act, code, vp(L.V.data_ptr()),
+                      vp(L.U.data_ptr()), vp(L.W1.data_ptr()), vp(L.b1.data_ptr()),
+                      vp(L.Wup.data_ptr()), vp(L.W2T.data_ptr()), -1, ctypes.c_float(tau),
+                      vp(y.data_ptr()), None, None, None, vp(ws.data_ptr()), ws_b,
+                      vp(stream.cuda_stream))
+        for s in range(10):
+            call_tau(s % nl, s % 64)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            call_tau(s % nl, (s * 7) % 64)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        npred, hits, ntr = sweep[tau]
+        rows.append({"tau": tau, "pred_frac": round(npred / (nq * f), 4),
+                     "recall": round(hits / max(ntr, 1), 4),
+                     "precision": round(hits / max(npred, 1), 4),
+                     "us_per_layer": round(e0.elapsed_time(e1) * 1e3 / steps, 3)})
+    res["tau_sweep"] = {"samples": nq, "rows": rows,
+                        "note": "sigmoid score >= tau over the same (layer, token) pairs as "
+                                "quality; the layer timed without zero-skip"}
+    log("tau sweep: " + ", ".join(f"{w['tau']}: frac {w['pred_frac']} rec {w['recall']} "
+                                  f"prec {w['precision']} {w['us_per_layer']} us" for w in rows))
     del layers
     torch.cuda.empty_cache()
     return res
@@ -1113,6 +1191,27 @@ def stack_leg(args, dev):
             rec /= nq
             res[mode]["recall_per_layer"] = [round(float(v), 4) for v in rec]
             res[mode]["recall_mean"] = round(float(rec.mean()), 4)
+    # the recurrence as written (no normalisation): the stream's growth and the first layer
+    # whose input no longer fits the 16-bit storage type
+    x_log = torch.empty(nl, 1, d, dtype=torch.float32, device=dev)
+    xhat_log = torch.empty(nl, 1, d, dtype=cfg.dtype, device=dev)
+    lit = {}
+    for norm in (True, False):
+        x.copy_(X[0:1])
+        csf.stack_forward(x, layers, k=k, norm=norm, ws=ws, x_log=x_log, xhat_log=xhat_log)
+        torch.cuda.synchronize()
+        rms = x_log[:, 0].double().pow(2).mean(dim=1).sqrt()
+        bad = [l for l in range(nl) if not bool(torch.isfinite(xhat_log[l, 0]).all())]
+        lit["normalised" if norm else "literal"] = {
+            "rms_per_layer": [float(f"{v:.4g}") for v in rms.tolist()],
+            "first_layer_input_overflowing_f16": bad[0] if bad else None,
+            "final_finite": bool(torch.isfinite(x).all())}
+    lit["note"] = ("one token through the stack: x_{l+1} = x_l + FFN_l(xhat_l), xhat_l = "
+                   "dtype(x_l / rms(x_l)) (normalised, the default) or dtype(x_l) (literal); "
+                   "rms of x_l per layer, and the first layer whose rounded input holds inf")
+    res["literal_recurrence"] = lit
+    log(f"  literal recurrence: first f16 overflow at layer "
+        f"{lit['literal']['first_layer_input_overflowing_f16']}")
     del layers
     torch.cuda.empty_cache()
     res["lookahead_speedup"] = round(res["sync"]["ms_per_token"] / res["lookahead"]["ms_per_token"], 4)
@@ -1123,37 +1222,92 @@ def stack_leg(args, dev):
     return res
 
 
-def cpu_baseline(cfg, L, X, ntok, touched):
-    """The oracle as it stands, single-threaded on the host, on `ntok` tokens of layer 0."""
+def cpu_threads():
+    """Host threads for the N-core oracle leg: the cores this process may run on, at most 16 (the
+    host share that goes with one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(cfg, L, X, ntok, ntok_mt, touched):
+    """The oracle as it stands (predict + top-k + sparse FFN per token, then the dense FFN) on the
+    host: one thread on `ntok` tokens, then all of the host share's cores (OpenMP over rows and
+    column blocks, the same sums in the same order) on `ntok_mt` tokens."""
     import numpy as np
     from oracle import oracle as orc
-
-    log(f"CPU oracle baseline on {ntok} tokens")
 
     def host(t):
         return t.detach().cpu().numpy()
 
     V, U, W1, W2T, b1 = host(L.V), host(L.U), host(L.W1), host(L.W2T), host(L.b1)
-    xs = [host(X[t]) for t in range(ntok)]
+    n_mt = cpu_threads()
+    xs = [host(X[t]) for t in range(max(ntok, ntok_mt))]
     orc.lib()
-    t0 = time.perf_counter()
-    for x in xs:
-        _, _, s = orc.predict(x, V, U, orc.F16)
-        sel = orc.select_topk(s, cfg.k)
-        orc.sparse_ffn(x, W1, b1, None, W2T, sel, orc.RELU, orc.F16)
-    dt = time.perf_counter() - t0
-    gbs = touched * ntok / dt / 1e9
     model = None
     try:
         with open("/proc/cpuinfo") as fh:
             model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_layer": round(dt / ntok * 1e6, 1),
-            "host_cores_available": len(os.sched_getaffinity(0)), "host_cpu": model,
-            "sample": f"{ntok} tokens of one layer of the same shape (predict + top-k + sparse FFN), "
-                      f"single-threaded C oracle with double accumulation, {dt:.1f} s"}
+    dense_b = (2 * cfg.f * cfg.d) * 2 + cfg.d * 2
+
+    def sparse_leg(threads, n):
+        orc.set_threads(threads)
+        t0 = time.perf_counter()
+        for x in xs[:n]:
+            _, _, s = orc.predict(x, V, U, orc.F16)
+            sel = orc.select_topk(s, cfg.k)
+            orc.sparse_ffn(x, W1, b1, None, W2T, sel, orc.RELU, orc.F16)
+        return time.perf_counter() - t0
+
+    def dense_leg(threads, n):
+        orc.set_threads(threads)
+        t0 = time.perf_counter()
+        for x in xs[:n]:
+            orc.dense_ffn(x, W1, b1, None, W2T, orc.RELU, orc.F16)
+        return time.perf_counter() - t0
+
+    try:
+        log(f"CPU oracle baseline: {ntok} tokens on 1 thread, {ntok_mt} on {n_mt} threads")
+        t1 = sparse_leg(1, ntok)
+        tn = sparse_leg(n_mt, ntok_mt)
+        log("CPU oracle dense FFN: 1 token on 1 thread, 2 on all threads")
+        td1 = dense_leg(1, 1)
+        tdn = dense_leg(n_mt, 2)
+    finally:
+        orc.set_threads(1)
+
+    def leg(dt, n, threads, nbytes):
+        return {"value": round(nbytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+                "us_per_layer": round(dt / n * 1e6, 1), "tokens": n, "seconds": round(dt, 2)}
+
+    single = leg(t1, ntok, 1, touched)
+    multi = leg(tn, ntok_mt, n_mt, touched)
+    return {"value": multi["value"], "unit": "GB/s", "cores": n_mt, "kind": "oracle",
+            "us_per_layer": multi["us_per_layer"],
+            "sample": f"{ntok_mt} tokens of one layer of the same shape (predict + top-k + sparse "
+                      f"FFN) through the C oracle with double accumulation on {n_mt} OpenMP "
+                      f"threads (whole rows and column blocks per thread, each sum in ascending "
+                      f"order: bitwise the single-thread result), {tn:.1f} s",
+            "single_thread": dict(single, sample=f"{ntok} tokens, one thread, {t1:.1f} s"),
+            "dense": {"single_thread": leg(td1, 1, 1, dense_b), "multi_thread": leg(tdn, 2, n_mt, dense_b),
+                      "sample": "the oracle's dense FFN (every neuron) on the first tokens"},
+            "multi_thread_speedup": round(t1 / ntok / (tn / ntok_mt), 2),
+            "host_cores_available": len(os.sched_getaffinity(0)), "host_cpu": model}
+
+
+def tensor_sha256(named):
+    """SHA-256 of each tensor's bytes (as stored: row-major, storage type), read back in chunks."""
+    import hashlib
+    import torch
+    out = {}
+    for name, t in named:
+        h = hashlib.sha256()
+        flat = t.detach().contiguous().reshape(-1).view(torch.uint8)
+        step = 1 << 28
+        for i in range(0, flat.numel(), step):
+            h.update(flat[i:i + step].cpu().numpy().tobytes())
+        out[name] = h.hexdigest()
+    return out
 
 
 def bandwidth_probe(dev):

@@ -32,6 +32,22 @@
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
 enum { ORC_RELU = 0, ORC_REGLU = 1, ORC_SILU = 2, ORC_SWIGLU = 3 };
 
+/* Threads for the loops over independent outputs (OpenMP; 1 = plain serial loops).  Every output
+ * element is still one sum in ascending index order, formed by one thread, so the thread count
+ * never changes a bit of any result: it only shares out whole rows (predictor, activations) and
+ * whole column blocks (the FFN output). */
+static int g_threads = 1;
+
+int orc_set_threads(int n)
+{
+    if (n < 1)
+        return -1;
+    g_threads = n;
+    return 0;
+}
+
+int orc_get_threads(void) { return g_threads; }
+
 /* ------------------------------------------------------------------------------------------ */
 /* Storage types, from their IEEE / bfloat16 definitions.                                      */
 /* ------------------------------------------------------------------------------------------ */
@@ -134,6 +150,7 @@ int orc_predict(const void *x, int d, const void *V, int r, const void *U, int f
     double *a = (double *)malloc(sizeof(double) * (size_t)r);
     if (!a)
         return -2;
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int i = 0; i < r; ++i) {                  /* a = relu(V x) */
         double acc = 0.0;
         for (int c = 0; c < d; ++c)
@@ -142,6 +159,7 @@ int orc_predict(const void *x, int d, const void *V, int r, const void *U, int f
         if (a_out)
             a_out[i] = a[i];
     }
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int j = 0; j < f; ++j) {                  /* z = U a ; s = sigmoid(z) */
         double acc = 0.0;
         for (int i = 0; i < r; ++i)
@@ -259,6 +277,26 @@ static double neuron_act(double p, double u, int act)
     return gated_act(act) ? g * u : g;
 }
 
+/* y[c] = sum over list entries n (ascending) of h[n] W2T[rows[n]][c], each y[c] starting from 0
+ * and adding the terms in list order; the columns go in blocks to the threads. */
+enum { ORC_COL_BLOCK = 256 };
+
+static void down_rows(const double *h, const int32_t *rows, int count, const void *W2T, int d,
+                      int dt, double *y_out)
+{
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
+    for (int cb = 0; cb < d; cb += ORC_COL_BLOCK) {
+        const int ce = cb + ORC_COL_BLOCK < d ? cb + ORC_COL_BLOCK : d;
+        for (int c = cb; c < ce; ++c)
+            y_out[c] = 0.0;
+        for (int n = 0; n < count; ++n) {
+            const size_t row = (size_t)(rows ? rows[n] : n) * d;
+            for (int c = cb; c < ce; ++c)
+                y_out[c] += h[n] * wid(W2T, row + c, dt);
+        }
+    }
+}
+
 int orc_sparse_ffn(const void *x, int d, int f, int act, int dt, const void *W1, const float *b1,
                    const void *Wup, const void *W2T, const int32_t *idx, int count,
                    double *h_out /* [count] or NULL */, double *y_out /* [d] */)
@@ -267,20 +305,23 @@ int orc_sparse_ffn(const void *x, int d, int f, int act, int dt, const void *W1,
         return -1;
     if (!x || !W1 || !W2T || !y_out || (count > 0 && !idx) || (gated_act(act) && !Wup))
         return -1;
-    for (int c = 0; c < d; ++c)
-        y_out[c] = 0.0;
-    for (int n = 0; n < count; ++n) {
-        int j = idx[n];
-        if (j < 0 || j >= f)
+    for (int n = 0; n < count; ++n)
+        if (idx[n] < 0 || idx[n] >= f)
             return -4;
+    double *h = (double *)malloc(sizeof(double) * (size_t)(count > 0 ? count : 1));
+    if (!h)
+        return -2;
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
+    for (int n = 0; n < count; ++n) {           /* the active neurons' activations */
         double p, u;
-        neuron_preact(x, d, dt, W1, b1, Wup, act, j, &p, &u);
-        double h = neuron_act(p, u, act);
-        if (h_out)
-            h_out[n] = h;
-        for (int c = 0; c < d; ++c)
-            y_out[c] += h * wid(W2T, (size_t)j * d + c, dt);
+        neuron_preact(x, d, dt, W1, b1, Wup, act, idx[n], &p, &u);
+        h[n] = neuron_act(p, u, act);
     }
+    if (h_out)
+        for (int n = 0; n < count; ++n)
+            h_out[n] = h[n];
+    down_rows(h, idx, count, W2T, d, dt, y_out);   /* y = sum of h_n W2T[idx[n]] */
+    free(h);
     return 0;
 }
 
@@ -294,17 +335,20 @@ int orc_dense_ffn(const void *x, int d, int f, int act, int dt, const void *W1, 
         return -1;
     if (!x || !W1 || !W2T || !y_out || (gated_act(act) && !Wup))
         return -1;
-    for (int c = 0; c < d; ++c)
-        y_out[c] = 0.0;
+    double *h = (double *)malloc(sizeof(double) * (size_t)(f > 0 ? f : 1));
+    if (!h)
+        return -2;
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int j = 0; j < f; ++j) {
         double p, u;
         neuron_preact(x, d, dt, W1, b1, Wup, act, j, &p, &u);
-        double h = neuron_act(p, u, act);
-        if (h_out)
-            h_out[j] = h;
-        for (int c = 0; c < d; ++c)
-            y_out[c] += h * wid(W2T, (size_t)j * d + c, dt);
+        h[j] = neuron_act(p, u, act);
     }
+    if (h_out)
+        for (int j = 0; j < f; ++j)
+            h_out[j] = h[j];
+    down_rows(h, NULL, f, W2T, d, dt, y_out);
+    free(h);
     return 0;
 }
 

@@ -39,7 +39,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-                               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+                               "-ffp-contract=off", "-fopenmp", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -63,6 +63,10 @@ def lib():
         L.orc_f64_to_bf16.restype = ctypes.c_uint16
         L.orc_silu.argtypes = [dbl]
         L.orc_silu.restype = dbl
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = i32
+        L.orc_get_threads.argtypes = []
+        L.orc_get_threads.restype = i32
         L.orc_predict.argtypes = [vp, i32, vp, i32, vp, i32, i32, vp, vp, vp]
         L.orc_select_topk.argtypes = [vp, i32, i32, vp]
         L.orc_select_threshold.argtypes = [vp, i32, flt, vp]
@@ -77,6 +81,17 @@ def lib():
             getattr(L, name).restype = i32
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's loops over independent outputs (1: serial).  Each output element
+    is one sum in ascending index order whatever n is, so results do not depend on n."""
+    if lib().orc_set_threads(int(n)) != 0:
+        raise ValueError(f"thread count must be >= 1, got {n}")
+
+
+def get_threads() -> int:
+    return lib().orc_get_threads()
 
 
 def _ptr(a):
