@@ -326,7 +326,8 @@ BatchedLayerWs batched_layer_ws(int B, int d, int f, int r, int max_count, int d
 }
 
 struct StackWs {
-    size_t xhat[2], a_main, s_main, a_side, s_side, sel_main, sel_side, idx[2], count[2], ffn, total;
+    size_t xhat[2], a_main, s_main, a_side, s_side, sel_main, sel_side, idx[2], count[2], sync, ffn,
+        total;
 };
 StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
 {
@@ -359,6 +360,8 @@ StackWs stack_ws(int B, int d, int f, int r, int max_count, int dtype)
         w.count[i] = o;
         o += round_up(Bn * sizeof(int32_t));
     }
+    w.sync = o;   // counters of the one-kernel FFN (single token)
+    o += round_up((size_t)fused_sync_words() * sizeof(uint32_t));
     w.ffn = o;
     w.total = o + ffn_ws(B > 0 ? B : 1, d, dtype, max_count).total;
     return w;
@@ -514,7 +517,7 @@ int capture_stream(csf_handle h, hipStream_t *out)
 int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, int f, int r,
                   int act, int dtype, float *x, int B, int sched, int k, float tau, int norm,
                   float eps, float *x_log, void *xhat_log, int32_t *idx_log, int32_t *count_log,
-                  void *ws, hipStream_t st, hipStream_t side)
+                  void *ws, hipStream_t st, hipStream_t side, bool captured)
 {
     const int max_count = k >= 0 ? k : f;
     const int stride = max_count > 0 ? max_count : 1;
@@ -528,6 +531,16 @@ int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, i
     }
     const size_t es = elem_bytes(dtype);
     FfnWs fw = ffn_ws(B, d, dtype, max_count);
+    // one token without the post-gate skip: each block's FFN is the one-kernel form, whose
+    // hand-over state the block's normalisation kernel prepares -- except in a captured look-ahead
+    // schedule, where the next block's predictor runs beside the FFN: there the one-kernel form's
+    // waiting workgroups share the CUs with the predictor and it gains nothing (measured at the
+    // OPT-30B shape, 48 blocks: 2.34-2.49 ms per token against 2.32-2.37 with the three-kernel
+    // FFN), while the synchronous schedule gains about 0.1 ms (2.73 against 2.83) and the eager
+    // look-ahead schedule, bound by the host's enqueue, two launches per block
+    const bool fused = B == 1 && !(h->ffn_flags & CSF_FFN_SKIP_ZERO_H) && !(ahead && captured);
+    uint32_t *sync = reinterpret_cast<uint32_t *>(at(ws, w.sync));
+    float *hbuf = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
 
     auto sel_idx = [&](int l) {
         return idx_log ? idx_log + (size_t)l * B * stride
@@ -565,7 +578,9 @@ int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, i
         void *xh = at(ws, w.xhat[l & 1]);
         hipError_t e = csf::launch_rms_norm(
             dtype, x, B, d, eps, norm, xh, x_log ? x_log + (size_t)l * B * d : nullptr,
-            xhat_log ? static_cast<char *>(xhat_log) + (size_t)l * B * d * es : nullptr, st);
+            xhat_log ? static_cast<char *>(xhat_log) + (size_t)l * B * d * es : nullptr, st,
+            fused ? sync : nullptr, fused_sync_words(),
+            fused ? reinterpret_cast<uint32_t *>(hbuf) : nullptr, max_count);
         if (e != hipSuccess)
             return hip_status(e, "stack normalisation launch");
         int s = CSF_OK;
@@ -607,14 +622,14 @@ int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, i
         fa.idx_stride = stride;
         fa.count = k >= 0 ? nullptr : sel_count(l);
         fa.max_count = max_count;
-        fa.h = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));
+        fa.h = hbuf;
         fa.h_stride = stride;
         fa.y = x;
         fa.partials = reinterpret_cast<float *>(at(ws, w.ffn + fw.partials));
         fa.accumulate = 1;
         fa.skip_zero = (h->ffn_flags & CSF_FFN_SKIP_ZERO_H) ? 1 : 0;
         fa.gate_tau = h->gate_tau;
-        e = csf::launch_ffn(fa, st);
+        e = fused ? csf::launch_ffn_fused(fa, sync, st) : csf::launch_ffn(fa, st);
         if (e != hipSuccess)
             return hip_status(e, "stack FFN launch");
     }
@@ -1434,7 +1449,7 @@ int csf_stack_forward(csf_handle h, const csf_layer_weights *layers, int L, int 
     if (!(mode & CSF_STACK_GRAPH))
         return enqueue_stack(h, layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm, eps,
                              x_log, xhat_log, idx_log, count_log, ws, st,
-                             static_cast<hipStream_t>(side_stream));
+                             static_cast<hipStream_t>(side_stream), false);
 
     // graph replay: the whole stack as one launch, captured on first use for these arguments
     hipError_t e = hipSuccess;
@@ -1467,7 +1482,7 @@ int csf_stack_forward(csf_handle h, const csf_layer_weights *layers, int L, int 
             return hip_status(e, "hipStreamBeginCapture");
         const int s2 = enqueue_stack(h, layers, L, d, f, r, act, dtype, x, B, sched, k, tau, norm,
                                      eps, x_log, xhat_log, idx_log, count_log, ws, cap,
-                                     static_cast<hipStream_t>(side_stream));
+                                     static_cast<hipStream_t>(side_stream), true);
         const std::string msg = g_last_error;
         hipGraph_t graph = nullptr;
         e = hipStreamEndCapture(cap, &graph);

@@ -180,9 +180,13 @@ void *scratch_ptr(int device);
 
 // ---- stack of blocks (stack.hip) -------------------------------------------------------------
 // xhat[t] = storage-type rounding of x[t] / sqrt(mean(x[t]^2) + eps) (norm = 1) or of x[t]
-// (norm = 0); x_log / xhat_log (optional) receive copies of x and xhat.
+// (norm = 0); x_log / xhat_log (optional) receive copies of x and xhat.  zero (optional): nzero
+// words the launch also clears, and fill: nfill words it sets to kHSentinel (the hand-over state
+// of a one-kernel FFN that follows on the same stream).
 hipError_t launch_rms_norm(int dtype, const float *x, int B, int d, float eps, int norm, void *xhat,
-                           float *x_log, void *xhat_log, hipStream_t stream);
+                           float *x_log, void *xhat_log, hipStream_t stream,
+                           uint32_t *zero = nullptr, int nzero = 0, uint32_t *fill = nullptr,
+                           int nfill = 0);
 
 // ---- batched FFN over the union of the tokens' sets (union.hip) -------------------------------
 constexpr int kMaxUnionBatch = 32;   // tokens per call (two 16-token matrix-core tiles)

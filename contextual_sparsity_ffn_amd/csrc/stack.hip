@@ -8,7 +8,10 @@
 //
 //   k_rms_norm  one 1024-thread workgroup per token, the row held in registers: fixed-order sum of
 //               squares (so the result is deterministic), the scale, the rounding to the storage
-//               type; optional copies of the stream and of xhat for inspection.
+//               type; optional copies of the stream and of xhat for inspection.  It also prepares
+//               the hand-over state of the block's one-kernel FFN (counters cleared, h slots
+//               marked unwritten): it runs after the previous block's FFN and before this one's,
+//               on the same stream.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -37,9 +40,15 @@ __global__ __launch_bounds__(kNormThreads) void k_rms_norm(const float *__restri
                                                            float eps, int norm,
                                                            void *__restrict__ xhat,
                                                            float *__restrict__ x_log,
-                                                           void *__restrict__ xhat_log)
+                                                           void *__restrict__ xhat_log,
+                                                           uint32_t *__restrict__ zero, int nzero,
+                                                           uint32_t *__restrict__ fill, int nfill)
 {
     __shared__ float red[kNormThreads / kWave];
+    for (int i = blockIdx.x * kNormThreads + threadIdx.x; i < nzero; i += gridDim.x * kNormThreads)
+        zero[i] = 0u;
+    for (int i = blockIdx.x * kNormThreads + threadIdx.x; i < nfill; i += gridDim.x * kNormThreads)
+        fill[i] = kHSentinel;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const size_t base = (size_t)blockIdx.x * d;
     const float4 *xt = reinterpret_cast<const float4 *>(x + base);
@@ -89,38 +98,44 @@ __global__ __launch_bounds__(kNormThreads) void k_rms_norm(const float *__restri
 
 template <int DT>
 hipError_t norm_dt(const float *x, int B, int d, float eps, int norm, void *xhat, float *x_log,
-                   void *xhat_log, hipStream_t st)
+                   void *xhat_log, uint32_t *zero, int nzero, uint32_t *fill, int nfill,
+                   hipStream_t st)
 {
     const int npt = (d / 4 + kNormThreads - 1) / kNormThreads;
     if (npt <= 1)
         return launch(k_rms_norm<DT, 1>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
-                      xhat, x_log, xhat_log);
+                      xhat, x_log, xhat_log, zero, nzero, fill, nfill);
     if (npt <= 2)
         return launch(k_rms_norm<DT, 2>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
-                      xhat, x_log, xhat_log);
+                      xhat, x_log, xhat_log, zero, nzero, fill, nfill);
     if (npt <= 4)
         return launch(k_rms_norm<DT, 4>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
-                      xhat, x_log, xhat_log);
+                      xhat, x_log, xhat_log, zero, nzero, fill, nfill);
     if (npt <= 8)
         return launch(k_rms_norm<DT, 8>, dim3(B), dim3(kNormThreads), st, nullptr, x, d, eps, norm,
-                      xhat, x_log, xhat_log);
+                      xhat, x_log, xhat_log, zero, nzero, fill, nfill);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_rms_norm(int dtype, const float *x, int B, int d, float eps, int norm, void *xhat,
-                           float *x_log, void *xhat_log, hipStream_t st)
+                           float *x_log, void *xhat_log, hipStream_t st, uint32_t *zero,
+                           int nzero, uint32_t *fill, int nfill)
 {
+    if (!zero)
+        nzero = 0;
+    if (!fill)
+        nfill = 0;
     if (B <= 0)
         return hipSuccess;
     if (d % 4 != 0)
         return hipErrorInvalidValue;
     if (dtype == 0)
-        return norm_dt<0>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
+        return norm_dt<0>(x, B, d, eps, norm, xhat, x_log, xhat_log, zero, nzero, fill, nfill, st);
     if (dtype == 1)
-        return norm_dt<1>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
-    return norm_dt<2>(x, B, d, eps, norm, xhat, x_log, xhat_log, st);
+        return norm_dt<1>(x, B, d, eps, norm, xhat, x_log, xhat_log, zero, nzero, fill, nfill, st);
+    return norm_dt<2>(x, B, d, eps, norm, xhat, x_log, xhat_log, zero, nzero, fill, nfill, st);
 }
 
 }  // namespace csf

@@ -100,20 +100,24 @@ def _teacher_forced(layers, cfg, X, lookahead, norm=True, check_layers=None):
     return xL, x_log, xhat_log, idx_log, count_log
 
 
+# B = 1 takes the one-kernel FFN (its hand-over state prepared by each block's normalisation
+# kernel); B = 2 the three-kernel form
+@pytest.mark.parametrize("B", [1, 2])
 @pytest.mark.parametrize("lookahead", [False, True], ids=["sync", "lookahead"])
-def test_stack_teacher_forced_topk(lookahead):
-    announce(f"stack top-k lookahead={lookahead}")
+def test_stack_teacher_forced_topk(lookahead, B):
+    announce(f"stack top-k lookahead={lookahead} B={B}")
     cfg = wl.OPT30B_STACK48.scaled(512, 2048, 64)
     layers = _layers(cfg, 4)
-    X = wl.make_tokens(cfg, 2)
+    X = wl.make_tokens(cfg, B)
     _teacher_forced(layers, cfg, X, lookahead)
 
 
-def test_stack_teacher_forced_threshold_reglu_literal():
-    announce("stack threshold reglu literal")
+@pytest.mark.parametrize("B", [1, 2])
+def test_stack_teacher_forced_threshold_reglu_literal(B):
+    announce(f"stack threshold reglu literal B={B}")
     cfg = wl.LLAMA_REGLU.scaled(512, 1433, 64)
     layers = _layers(cfg, 3)
-    X = wl.make_tokens(cfg, 2)
+    X = wl.make_tokens(cfg, B)
     _teacher_forced(layers, cfg, X, lookahead=True, norm=False)
 
 
@@ -141,12 +145,13 @@ def _replay(layers, cfg, X, x_log, xhat_log, idx_log, count_log, xL, lookahead):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("B", [1, 3])
 @pytest.mark.parametrize("lookahead", [False, True], ids=["sync", "lookahead"])
-def test_stack_replays_bit_exact_from_single_layer_calls(lookahead):
-    announce(f"stack replay lookahead={lookahead}")
+def test_stack_replays_bit_exact_from_single_layer_calls(lookahead, B):
+    announce(f"stack replay lookahead={lookahead} B={B}")
     cfg = wl.OPT30B_STACK48.scaled(1024, 3000, 128)
     layers = _layers(cfg, 6)
-    X = wl.make_tokens(cfg, 3)
+    X = wl.make_tokens(cfg, B)
     xL, x_log, xhat_log, idx_log, count_log = _run(layers, X, cfg, lookahead)
     _replay(layers, cfg, X, x_log, xhat_log, idx_log, count_log, xL, lookahead)
     # the same run again gives the same bits
