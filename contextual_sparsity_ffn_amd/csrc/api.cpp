@@ -537,7 +537,7 @@ int enqueue_stack(csf_handle h, const csf_layer_weights *layers, int L, int d, i
     // waiting workgroups share the CUs with the predictor and it gains nothing (measured at the
     // OPT-30B shape, 48 blocks: 2.34-2.49 ms per token against 2.32-2.37 with the three-kernel
     // FFN), while the synchronous schedule gains about 0.1 ms (2.73 against 2.83) and the eager
-    // look-ahead schedule, bound by the host's enqueue, two launches per block
+    // look-ahead schedule, bound by the host's enqueue, saves two launches per block
     const bool fused = B == 1 && !(h->ffn_flags & CSF_FFN_SKIP_ZERO_H) && !(ahead && captured);
     uint32_t *sync = reinterpret_cast<uint32_t *>(at(ws, w.sync));
     float *hbuf = reinterpret_cast<float *>(at(ws, w.ffn + fw.h));

@@ -36,6 +36,7 @@ LABELS = [("k_pred_down", "pred_down"), ("k_pred_up_select", "pred_up_select"),
           ("k_pred_up_loop", "pred_up"), ("k_pred_up", "pred_up"), ("k_select_topk", "select_topk"),
           ("k_select_threshold", "select_threshold"), ("k_gather_up", "gather_up"),
           ("k_gather_down", "gather_down"), ("k_reduce_partials", "reduce_partials"),
+          ("k_ffn_fused", "ffn_fused"),
           ("k_pred_down_mfma", "pred_down_mfma"), ("k_pred_hidden", "pred_hidden"),
           ("k_pred_up_mfma_res", "pred_up_mfma"), ("k_pred_up_mfma", "pred_up_mfma"), ("k_union_list", "union_list"),
           ("k_union_up_valu", "union_up_valu"), ("k_union_down_valu", "union_down_valu"),
