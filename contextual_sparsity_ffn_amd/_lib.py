@@ -503,14 +503,50 @@ def sparse_ffn_batched_layer(X, V, U, W1, b1, Wup, W2T, k=None, tau=None, act=RE
     return Y, taken.value
 
 
+class StackLayers:
+    """The blocks of a stack (objects with V, U, W1, b1, Wup, W2T device tensors), checked once and
+    packed into the C ABI's array of weight pointers, for repeated stack_forward calls: checking
+    and packing every block's tensors on each call costs the host about as much as enqueueing the
+    stack.  Keeps references to the tensors; they must not be resized or moved while it is used."""
+
+    def __init__(self, layers, act=RELU):
+        self.layers = list(layers)
+        self.act = act
+        nl = len(self.layers)
+        self.n = nl
+        self.arr = (LayerWeights * max(nl, 1))()
+        if nl == 0:
+            self.device = self.dtype = None
+            self.d = self.f = self.r = 0
+            return
+        L0 = self.layers[0]
+        _tensor(L0.W1, "W1")
+        dev, dt = L0.W1.device, L0.W1.dtype
+        f, d = L0.W1.shape
+        r = L0.V.shape[0]
+        for i, Lw in enumerate(self.layers):
+            _ffn_weights(torch.empty(0, dtype=dt, device=dev), Lw.W1, Lw.b1, Lw.Wup, Lw.W2T, act)
+            _tensor(Lw.W1, "W1", shape=(f, d))
+            _tensor(Lw.V, "V", dtype=dt, shape=(r, d), device=dev)
+            _tensor(Lw.U, "U", dtype=dt, shape=(f, r), device=dev)
+            self.arr[i] = LayerWeights(Lw.V.data_ptr(), Lw.U.data_ptr(), Lw.W1.data_ptr(),
+                                       None if Lw.Wup is None else Lw.Wup.data_ptr(),
+                                       Lw.W2T.data_ptr(), None if Lw.b1 is None else Lw.b1.data_ptr())
+        self.device, self.dtype, self.d, self.f, self.r = dev, dt, d, f, r
+
+    def __len__(self):
+        return self.n
+
+
 def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=True, eps=1e-6,
                   x_log=None, xhat_log=None, idx_log=None, count_log=None, side_stream=None,
                   ws=None, graph=False, ctx=None):
-    """Run x [B, d] (float32, updated in place) through the residual blocks `layers` (objects with
-    V, U, W1, b1, Wup, W2T device tensors).  lookahead: each layer's set is predicted from the
-    previous layer's input on `side_stream` (a torch.cuda.Stream; required).  graph: enqueue the
-    stack as one replayed HIP graph (captured when the arguments change; pass the same `ws` and
-    tensors to reuse it).  Returns x."""
+    """Run x [B, d] (float32, updated in place) through the residual blocks `layers` (a list of
+    objects with V, U, W1, b1, Wup, W2T device tensors, or a StackLayers made from one with the
+    same act).  lookahead: each layer's set is predicted from the previous layer's input on
+    `side_stream` (a torch.cuda.Stream; required).  graph: enqueue the stack as one replayed HIP
+    graph (captured when the arguments change; pass the same `ws` and tensors to reuse it).
+    Returns x."""
     if (k is None) == (tau is None):
         raise ValueError("give exactly one of k (top-k) or tau (threshold)")
     _tensor(x, "x", dtype=torch.float32)
@@ -518,21 +554,17 @@ def stack_forward(x, layers, k=None, tau=None, act=RELU, lookahead=False, norm=T
         raise ValueError("x must be [B, d]")
     B, d = x.shape
     dev = x.device
+    if not isinstance(layers, StackLayers):
+        layers = StackLayers(layers, act)
+    elif layers.act != act:
+        raise ValueError("the StackLayers were checked for another activation")
     nl = len(layers)
     if nl == 0:
         return x
-    L0 = layers[0]
-    dt = L0.W1.dtype
-    f, r = L0.W1.shape[0], L0.V.shape[0]
-    arr = (LayerWeights * nl)()
-    for i, Lw in enumerate(layers):
-        _ffn_weights(torch.empty(0, dtype=dt, device=dev), Lw.W1, Lw.b1, Lw.Wup, Lw.W2T, act)
-        _tensor(Lw.W1, "W1", shape=(f, d))
-        _tensor(Lw.V, "V", dtype=dt, shape=(r, d), device=dev)
-        _tensor(Lw.U, "U", dtype=dt, shape=(f, r), device=dev)
-        arr[i] = LayerWeights(Lw.V.data_ptr(), Lw.U.data_ptr(), Lw.W1.data_ptr(),
-                              None if Lw.Wup is None else Lw.Wup.data_ptr(), Lw.W2T.data_ptr(),
-                              None if Lw.b1 is None else Lw.b1.data_ptr())
+    if layers.device != dev or layers.d != d:
+        raise ValueError(f"the layers ({layers.device}, d = {layers.d}) do not match x "
+                         f"({dev}, d = {d})")
+    dt, f, r, arr = layers.dtype, layers.f, layers.r, layers.arr
     kk = -1 if k is None else int(k)
     stride = f if kk < 0 else max(kk, 1)
     _tensor(x_log, "x_log", dtype=torch.float32, shape=(nl, B, d), device=dev, optional=True)

@@ -253,3 +253,26 @@ def test_stack_graph_replay_matches_eager(lookahead):
     csf.stack_forward(xh, layers, k=cfg.k, lookahead=lookahead, side_stream=side, ws=ws, graph=True)
     torch.cuda.synchronize()
     assert torch.equal(xh, ref[2])
+
+
+def test_stack_layers_packed_once_give_the_same_bits():
+    """StackLayers checks and packs the blocks once; stack_forward over it gives the bits of the
+    list form, and refuses blocks checked for another activation or made for another d."""
+    announce("stack StackLayers")
+    cfg = wl.OPT30B_STACK48.scaled(1024, 2048, 128)
+    layers = _layers(cfg, 4)
+    X = wl.make_tokens(cfg, 1).float().to(DEV)
+    side = torch.cuda.Stream(device=DEV)
+    blocks = csf.StackLayers(layers)
+    assert len(blocks) == 4
+    for lookahead in (False, True):
+        a = X.clone()
+        b = X.clone()
+        csf.stack_forward(a, layers, k=cfg.k, lookahead=lookahead, side_stream=side)
+        csf.stack_forward(b, blocks, k=cfg.k, lookahead=lookahead, side_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), lookahead
+    with pytest.raises(ValueError):
+        csf.stack_forward(X.clone(), blocks, k=cfg.k, act=csf.SILU)
+    with pytest.raises(ValueError):
+        csf.stack_forward(torch.zeros(1, 512, dtype=torch.float32, device=DEV), blocks, k=cfg.k)
