@@ -259,9 +259,10 @@ def test_batched_layer_end_to_end(name, cfg, B):
     words = (cfg.f + 31) // 32
     bm = torch.zeros(B, words, dtype=torch.int32, device=DEV)
     for path in (csf.PATH_GATHER, csf.PATH_MFMA):
+        uc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
         Y, taken = csf.sparse_ffn_batched_layer(X.to(DEV), Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T,
                                                 k=cfg.k, tau=cfg.tau, act=cfg.act, path=path,
-                                                bitmaps=bm)
+                                                bitmaps=bm, union_count=uc)
         scores = csf.predict_active(X.to(DEV), Ld.V, Ld.U)
         torch.cuda.synchronize()
         assert taken == path
@@ -271,7 +272,42 @@ def test_batched_layer_end_to_end(name, cfg, B):
             sel = orc.select_topk(s, cfg.k) if cfg.k is not None else orc.select_threshold(s, cfg.tau)
             assert np.array_equal(bm[t].cpu().numpy().view(np.uint32), orc.to_bitmap(sel, cfg.f))
             sets.append(sel)
+        assert int(uc.item()) == len(orc.union_of(sets, cfg.f))
         _check(L, X, sets, Y, csf.SEM_PER_TOKEN, f"{name} path {path}")
+
+
+@pytest.mark.parametrize("B", [2, 5, 32])
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_batched_layer_equals_the_composed_calls(B, pname, path):
+    """The batched layer in one enqueue against predict, select and the batched union FFN called
+    one after another: the same bits, the same bitmaps and the same union size, for top-k, a
+    threshold and an empty selection."""
+    cfg = wl.OPT30B.scaled(1024, 3001, 128)
+    L = wl.make_layer(cfg)
+    Ld = _dev_layer(L)
+    X = wl.make_clustered_tokens(cfg, B).to(DEV)
+    words = (cfg.f + 31) // 32
+    for k, tau in ((cfg.k, None), (None, 0.5), (0, None)):
+        announce(f"batched layer vs composed B={B} {pname} k={k} tau={tau}")
+        bm = torch.zeros(B, words, dtype=torch.int32, device=DEV)
+        uc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        Y, _ = csf.sparse_ffn_batched_layer(X, Ld.V, Ld.U, Ld.W1, Ld.b1, Ld.Wup, Ld.W2T, k=k,
+                                            tau=tau, act=cfg.act, path=path, bitmaps=bm,
+                                            union_count=uc)
+        s = csf.predict_active(X, Ld.V, Ld.U)
+        bm2 = torch.zeros(B, words, dtype=torch.int32, device=DEV)
+        if k is not None:
+            csf.select_topk(s, k, bitmap=bm2)
+        else:
+            csf.select_threshold(s, tau, bitmap=bm2)
+        uc2 = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        Y2, _ = _run(Ld, X, bm2, csf.SEM_PER_TOKEN, path, uc2)
+        torch.cuda.synchronize()
+        assert torch.equal(bm, bm2)
+        assert int(uc.item()) == int(uc2.item())
+        assert torch.equal(Y, Y2)
+        if k == 0:
+            assert int(uc.item()) == 0 and not Y.any()
 
 
 @pytest.mark.parametrize("name,cfg", [
