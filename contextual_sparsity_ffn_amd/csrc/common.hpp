@@ -198,7 +198,8 @@ __device__ __forceinline__ void count_add(uint32_t *p, uint32_t v)
 // the tests) and goes on.
 constexpr uint32_t kSpinLimit = 1u << 15;
 // A value that marks "not written yet" in a buffer of float32 results handed over inside a kernel:
-// a NaN bit pattern (all ones) that float32 arithmetic on finite inputs never produces.
+// a NaN bit pattern (all ones) that float32 arithmetic on finite inputs never produces; a producer
+// whose inputs may carry NaN payloads stores every NaN as the default quiet NaN 0x7fc00000.
 constexpr uint32_t kHSentinel = 0xffffffffu;
 __device__ __forceinline__ void wait_count(const uint32_t *p, uint32_t target, uint32_t *err)
 {

@@ -319,7 +319,8 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float *__restrict
 //   nup     "up" workgroups, RPW list entries each with every row load issued at once, as
 //           k_gather_up computes them (the up rows are the critical path, so they are all
 //           requested first).  Each h is stored coherently over a sentinel the call's first
-//           kernel wrote there (kHSentinel, a NaN pattern no arithmetic result has), so no
+//           kernel wrote there (kHSentinel, a NaN pattern; a NaN h, which a float32 input's NaN
+//           payload could carry through, is stored as the default quiet NaN instead), so no
 //           counter and no wait for the store is needed;
 //   nitems  "down" workgroups, one (chunk, d-slice) item of k_gather_down each, chunk-major: each
 //           wavefront's first kDownUnroll rows of the item are requested first, then the
@@ -424,6 +425,8 @@ __device__ __forceinline__ void fused_up(const FusedFfnArgs &a, int blk)
                 hv *= u;
             }
         }
+        if ((__float_as_uint(hv) & 0x7fffffffu) > 0x7f800000u)
+            hv = __uint_as_float(0x7fc00000u);
         st_coherent(a.h + n0 + i, hv);
     }
 }

@@ -486,6 +486,25 @@ def test_layer_one_kernel_ffn_is_bit_identical(name, cfg, ntok):
                            f"{name}/{t}")
 
 
+@pytest.mark.parametrize("act", [csf.REGLU, csf.SILU, csf.SWIGLU], ids=["reglu", "silu", "swiglu"])
+def test_layer_one_kernel_ffn_nan_payload_is_not_the_sentinel(act):
+    """A float32 token holding the NaN whose bits are all ones (the one-kernel FFN's mark for an
+    unwritten h) carries it into h in the gated and SiLU forms (0 * NaN and NaN arithmetic keep
+    the payload).  The up role stores such an h as the default NaN, so every column of y is NaN,
+    as in the three-kernel form, instead of a wait running out and h being read as zero."""
+    cfg = wl.TINY_F32
+    Ld = _to_dev_layer(_layer(cfg))
+    gated = act in (csf.REGLU, csf.SWIGLU)
+    g = torch.Generator().manual_seed(77)
+    Wup = _dev((torch.randn(cfg.f, cfg.d, generator=g) * 0.05).contiguous()) if gated else None
+    x = _dev(wl.make_tokens(cfg, 1)[0]).clone()
+    x.view(torch.int32)[3] = -1
+    announce(f"one-kernel FFN NaN payload act={act}")
+    y = csf.sparse_ffn_layer(x, Ld.V, Ld.U, Ld.W1, Ld.b1, Wup, Ld.W2T, k=cfg.k, act=act)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+
+
 def test_layer_one_kernel_ffn_full_size_repeated():
     """The headline shape, many calls back to back (the counters are cleared by each call's
     first kernel): every y bit-identical to the three-kernel form."""
