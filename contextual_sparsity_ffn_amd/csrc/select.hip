@@ -68,6 +68,25 @@ __device__ __forceinline__ void store_nibbles(uint32_t nib, uint32_t *bm, int wo
     *dst = x;
 }
 
+// Add one to rhist[dig] for every lane with `hit`.  When all the wavefront's hitting lanes share
+// a digit (equal scores, the case this serves), one lane adds their count: the lanes would
+// otherwise serialize on one LDS word.
+__device__ __forceinline__ void add_digit(uint32_t *rhist, bool hit, uint32_t dig)
+{
+    if (hit) {
+        const uint64_t act = __ballot(1);                       // the hitting lanes
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(dig);
+        if (__ballot(dig == d0) == act) {
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
+            if (below == 0)
+                atomicAdd(&rhist[d0], (uint32_t)__popcll(act));
+        } else {
+            atomicAdd(&rhist[dig], 1u);
+        }
+    }
+}
+
 // Compaction of an LDS bitmap into the ascending index list (index + base); also copies the bitmap
 // out.
 __device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int out_cap, int base,
@@ -228,69 +247,110 @@ __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ sco
     } else {
         // many candidates (heavy ties or a concentrated distribution): radix select over the
         // 32-bit order keys of bucket B*, 8 bits per pass.  This rare path re-reads the scores
-        // from memory so that the common path keeps its registers.
-        uint32_t kpre = 0u, pmask = 0u, krem = need;
-#pragma unroll 1
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (t < 256)
-                rhist[t] = 0u;
-            __syncthreads();
-            for (int j = t; j < f; j += kSelThreads) {
-                const float x = s[j];
+        // from memory so that the common path keeps its registers.  Shortcut first: when the
+        // candidates holding the bucket's largest key are at least `need` (equal scores at the top
+        // of the bucket, the usual cause of this path), that key is the k-th and no radix pass is
+        // needed.
+        uint32_t kmax = 0u, kcnt = 0u;
+        for (int j = t; j < f; j += kSelThreads) {
+            const float x = s[j];
+            if (score_bucket<NB>(x) == bstar) {
                 const uint32_t key = order_key(x);
-                if (score_bucket<NB>(x) == bstar && (key & pmask) == kpre)
-                    atomicAdd(&rhist[(key >> shift) & 0xffu], 1u);
+                kcnt = key > kmax ? 1u : kcnt + (key == kmax ? 1u : 0u);
+                kmax = key > kmax ? key : kmax;
             }
-            __syncthreads();
-            if (t < kWave) {
-                const uint32_t c0 = rhist[4 * t], c1 = rhist[4 * t + 1];
-                const uint32_t c2 = rhist[4 * t + 2], c3 = rhist[4 * t + 3];
-                const uint32_t local = c0 + c1 + c2 + c3;
-                uint32_t suffix = local;
+        }
+        uint32_t wmax = kmax;
 #pragma unroll
-                for (int o = 1; o < kWave; o <<= 1) {
-                    const uint32_t n = __shfl_down(suffix, o, kWave);
-                    if (t + o < kWave)
-                        suffix += n;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)wmax, o, kWave);
+            wmax = other > wmax ? other : wmax;
+        }
+        if ((t & (kWave - 1)) == 0)
+            rhist[t / kWave] = wmax;
+        __syncthreads();
+        uint32_t gmax = 0u;
+#pragma unroll
+        for (int w2 = 0; w2 < kSelWaves; ++w2)
+            gmax = rhist[w2] > gmax ? rhist[w2] : gmax;
+        uint32_t at_max;
+        // (its barriers also keep the reads of rhist above before a radix pass clears it)
+        (void)block_exclusive_scan<kSelWaves>(kmax == gmax ? kcnt : 0u, scan_tmp, &at_max);
+        uint32_t kpre = gmax, pmask = 0u, krem = need;
+        if (at_max < need) {
+            kpre = 0u;
+#pragma unroll 1
+            for (int shift = 24; shift >= 0; shift -= 8) {
+                if (t < 256)
+                    rhist[t] = 0u;
+                __syncthreads();
+                for (int j = t; j < f; j += kSelThreads) {
+                    const float x = s[j];
+                    const uint32_t key = order_key(x);
+                    add_digit(rhist, score_bucket<NB>(x) == bstar && (key & pmask) == kpre,
+                              (key >> shift) & 0xffu);
                 }
-                uint32_t ab = suffix - local;
-                const uint32_t cs[4] = {c0, c1, c2, c3};
+                __syncthreads();
+                if (t < kWave) {
+                    const uint32_t c0 = rhist[4 * t], c1 = rhist[4 * t + 1];
+                    const uint32_t c2 = rhist[4 * t + 2], c3 = rhist[4 * t + 3];
+                    const uint32_t local = c0 + c1 + c2 + c3;
+                    uint32_t suffix = local;
 #pragma unroll
-                for (int b = 3; b >= 0; --b) {
-                    if (ab < krem && ab + cs[b] >= krem) {
-                        misc[3] = (uint32_t)(4 * t + b);
-                        misc[4] = krem - ab;
+                    for (int o = 1; o < kWave; o <<= 1) {
+                        const uint32_t n = __shfl_down(suffix, o, kWave);
+                        if (t + o < kWave)
+                            suffix += n;
                     }
-                    ab += cs[b];
+                    uint32_t ab = suffix - local;
+                    const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+                    for (int b = 3; b >= 0; --b) {
+                        if (ab < krem && ab + cs[b] >= krem) {
+                            misc[3] = (uint32_t)(4 * t + b);
+                            misc[4] = krem - ab;
+                        }
+                        ab += cs[b];
+                    }
                 }
+                __syncthreads();
+                kpre |= misc[3] << shift;
+                pmask |= 0xffu << shift;
+                krem = misc[4];
+                __syncthreads();
             }
-            __syncthreads();
-            kpre |= misc[3] << shift;
-            pmask |= 0xffu << shift;
-            krem = misc[4];
-            __syncthreads();
         }
         // keys above T are in; of the keys equal to T the krem lowest-indexed are in (blocks of
-        // 1024 indices in ascending order, a block scan ranks the equal keys inside each block)
+        // 4096 indices in ascending order, four consecutive per thread; a block scan of the
+        // threads' equal-key counts ranks them inside each block)
         const uint32_t T = kpre;
         uint32_t taken = 0;
 #pragma unroll 1
-        for (int base = 0; base < f; base += kSelThreads) {
-            const int j = base + t;
-            bool gt = false, eq = false;
-            if (j < f) {
-                const float x = s[j];
-                if (score_bucket<NB>(x) == bstar) {
-                    const uint32_t key = order_key(x);
-                    gt = key > T;
-                    eq = key == T;
+        for (int base = 0; base < f; base += kQuad) {
+            const int j0 = base + 4 * t;
+            const float4 xq = load_quad<VEC>(s, j0, f);
+            const float e[4] = {xq.x, xq.y, xq.z, xq.w};
+            uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (j0 + q < f && score_bucket<NB>(e[q]) == bstar) {
+                    const uint32_t key = order_key(e[q]);
+                    gtm |= (key > T ? 1u : 0u) << q;
+                    eqm |= (key == T ? 1u : 0u) << q;
                 }
             }
             uint32_t eq_total;
-            const uint32_t eq_before =
-                block_exclusive_scan<kSelWaves>(eq ? 1u : 0u, scan_tmp, &eq_total);
-            if (gt || (eq && taken + eq_before < krem))
-                atomicOr(&bm[j >> 5], 1u << (j & 31));
+            uint32_t rank = taken + block_exclusive_scan<kSelWaves>(
+                                        (uint32_t)__builtin_popcount(eqm), scan_tmp, &eq_total);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                bool in = (gtm >> q) & 1u;
+                if ((eqm >> q) & 1u)
+                    in = rank++ < krem;
+                if (in)
+                    atomicOr(&bm[j >> 5], 1u << (j & 31));
+            }
             taken += eq_total;
         }
     }

@@ -112,8 +112,14 @@ def _score_patterns(f, g):
     # descending ramp: the k largest are the first k indices, so whole slices of a many-workgroup
     # selection lie above the boundary bucket (more members than any per-slice prefix holds)
     ramp = torch.linspace(1.0, 0.0, f)
+    # a band narrower than one bucket (1/2048): more candidates than the direct ranking takes.
+    # Distinct values, and the same band on a grid of 2^-22 (duplicates, but no one value
+    # holding the k-th place alone), go through the radix passes; the tie patterns above take
+    # the shortcut (the bucket's largest value fills the k-th place).
+    band = 0.5 + torch.rand(f, generator=g) * 4e-4
+    grid = torch.round(band * 2.0 ** 22) / 2.0 ** 22
     return {"uniform": u, "ties": q, "all-equal": eq, "signed-zero": z, "saturated": sat,
-            "sigmoid": sig, "ramp": ramp}
+            "sigmoid": sig, "ramp": ramp, "band": band, "band-grid": grid}
 
 
 SELECT_F = [1, 7, 1000, 1024, 1025, 3001, 30001, 49152, 65536]
