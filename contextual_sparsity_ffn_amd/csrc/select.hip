@@ -121,12 +121,14 @@ __device__ void bitmap_to_list(const uint32_t *bm, int words, int32_t *out, int 
             bitmap_out[w] = bm[w];
 }
 
-// The whole selection of one token by one 1024-thread workgroup (steps 1-4 above).
+// The whole selection of one token by one 1024-thread workgroup (steps 1-4 above).  ghist
+// (optional): the token's finished bucket histogram, which step 1 then reads instead of counting.
 template <int NB, int J, bool VEC>
 __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ scores, int token,
                                                    int f, int k, int32_t *__restrict__ idx,
                                                    int idx_stride, int32_t *__restrict__ count,
-                                                   uint32_t *__restrict__ bitmap, int prefix)
+                                                   uint32_t *__restrict__ bitmap, int prefix,
+                                                   const uint32_t *__restrict__ ghist = nullptr)
 {
     __shared__ uint32_t hist[NB];
     __shared__ uint32_t bm[kMaxWords];
@@ -168,16 +170,21 @@ __device__ __forceinline__ void topk_one_workgroup(const float *__restrict__ sco
         v[i] = load_quad<VEC>(s, i * kQuad + 4 * t, f);
 
     // ---- 1. the bucket histogram and the boundary bucket B* ------------------------------------
-    for (int b = t; b < NB; b += kSelThreads)
-        hist[b] = 0u;
-    __syncthreads();
+    if (ghist) {
+        for (int b = t; b < NB; b += kSelThreads)
+            hist[b] = ghist[b];
+    } else {
+        for (int b = t; b < NB; b += kSelThreads)
+            hist[b] = 0u;
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < J; ++i) {
-        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        for (int i = 0; i < J; ++i) {
+            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (i * kQuad + 4 * t + q < f)
-                atomicAdd(&hist[score_bucket<NB>(e[q])], 1u);
+            for (int q = 0; q < 4; ++q)
+                if (i * kQuad + 4 * t + q < f)
+                    atomicAdd(&hist[score_bucket<NB>(e[q])], 1u);
+        }
     }
     __syncthreads();
 
@@ -525,7 +532,7 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
         // heavy ties in the boundary bucket: the one-workgroup selection (uniform branch)
         if (slice == 0)
             topk_one_workgroup<NB, J, VEC>(scores, token, f, k, idx, idx_stride, count, bitmap,
-                                           prefix);
+                                           prefix, W);
         return;
     }
     // slice t: members above B* (certain) and B*'s members, from its above[] words
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(kSelThreads) void k_wide_finish(const float *__rest
         // the one-workgroup selection decides as above
         if (slice == 0)
             topk_one_workgroup<NB, J, VEC>(scores, token, f, k, idx, idx_stride, count, bitmap,
-                                           prefix);
+                                           prefix, W);
         return;
     }
     if ((uint32_t)t < nc) {
